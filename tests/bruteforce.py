@@ -1,0 +1,66 @@
+"""Pure-Python enumeration for tiny catalogs: an implementation independent of ``oracle/``.
+
+It shares nothing with the oracle: prefixes are Python tuples kept in sets and
+dicts, the log-softmax uses ``math``, and ordering uses Python's ``sorted``.
+
+* ``all_scores`` scores every distinct catalog SID by its summed per-level
+  log-probabilities (SPRINT summary, inference paragraph: the token
+  log-probability sum over valid SIDs of a prefix trie). A beam at least as wide
+  as the number of distinct prefixes at every depth never prunes, so its final
+  beams must equal this list.
+* ``beam_replay`` replays the constrained beam search by listing every
+  (row, child) candidate of a step explicitly and sorting the list.
+"""
+from __future__ import annotations
+
+import math
+
+CHILDREN, LEVEL = 0, 1
+
+
+def _children_map(catalog):
+    kids = {}
+    for sid in catalog:
+        for d in range(len(sid)):
+            kids.setdefault(tuple(sid[:d]), set()).add(sid[d])
+    return {p: sorted(s) for p, s in kids.items()}
+
+
+def _logp(row, support, code):
+    m = max(row[c] for c in support)
+    lse = m + math.log(math.fsum(math.exp(row[c] - m) for c in support))
+    return row[code] - lse
+
+
+def all_scores(catalog, V, logit_fn, norm=CHILDREN):
+    """[(score, sid)] for every distinct SID, best first (ties: smaller SID first)."""
+    kids = _children_map(catalog)
+    out = []
+    for sid in sorted(set(tuple(s) for s in catalog)):
+        total = 0.0
+        for d in range(len(sid)):
+            p = tuple(sid[:d])
+            row = logit_fn(d, p)
+            support = kids[p] if norm == CHILDREN else range(V)
+            total += _logp(row, support, sid[d])
+        out.append((total, sid))
+    out.sort(key=lambda t: (-t[0], t[1]))
+    return out
+
+
+def beam_replay(catalog, V, width, logit_fn, norm=CHILDREN, steps=None):
+    """Constrained beam search by explicit candidate lists; returns [(score, sid)] ranked."""
+    kids = _children_map(catalog)
+    L = len(catalog[0])
+    steps = L if steps is None else steps
+    beams = [(0.0, ())]
+    for d in range(steps):
+        cands = []
+        for r, (s, p) in enumerate(beams):
+            row = logit_fn(d, p)
+            support = kids[p] if norm == CHILDREN else range(V)
+            for c in kids[p]:
+                cands.append((s + _logp(row, support, c), r * V + c, p + (c,)))
+        cands.sort(key=lambda t: (-t[0], t[1]))
+        beams = [(s, p) for s, _, p in cands[:width]]
+    return beams

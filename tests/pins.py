@@ -1,0 +1,360 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Every check takes ``orc``, a namespace with the oracle's functions, so that
+``test_oracle_mutations.py`` can run the same checks against copies of the oracle
+with a planted mistake and require that some check fails.
+
+None of these checks re-types the oracle's formula: they compare it with a
+hand-derived example, closed forms, library routines on special cases
+(torch.log_softmax / torch.sort, exact rational arithmetic) and with the
+independent pure-Python enumerator in ``tests/bruteforce.py``.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# --------------------------------------------------------------------------- helpers
+def pack(t):
+    k = 0
+    for c in t:
+        k = k * 256 + int(c)
+    return k
+
+
+def unpack(k, depth):
+    return tuple((int(k) >> (8 * (depth - 1 - j))) & 255 for j in range(depth))
+
+
+def run_decode(orc, trie, width, logit_fn, norm=0, steps=None):
+    """Decode one request with ``orc.expand_request`` step by step.
+
+    ``logit_fn(depth, prefix_tuple)`` returns a float64 row of V logits."""
+    steps = trie.L if steps is None else steps
+    prefixes = np.zeros(1, dtype=np.uint64)
+    scores = np.zeros(1, dtype=np.float64)
+    hist = []
+    for d in range(steps):
+        x = np.stack([np.asarray(logit_fn(d, unpack(p, d)), dtype=np.float64) for p in prefixes])
+        res = orc.expand_request(trie, d, prefixes, scores, x, width, norm)
+        hist.append(res)
+        prefixes, scores = res["prefix"], res["score"]
+    return [unpack(p, steps) for p in prefixes], list(scores), hist
+
+
+def random_catalog(rng, V, L, n):
+    tuples = list(itertools.product(range(V), repeat=L))
+    idx = rng.choice(len(tuples), size=min(n, len(tuples)), replace=False)
+    return [tuples[i] for i in idx]
+
+
+def gaussian_logit_fn(seed, V, sigma=2.0):
+    cache = {}
+
+    def f(d, p):
+        key = (d, p)
+        if key not in cache:
+            r = np.random.default_rng([seed, d, pack(p), len(p)])
+            cache[key] = r.normal(0.0, sigma, V)
+        return cache[key]
+    return f
+
+
+# --------------------------------------------------------------------------- pins
+def pin_handworked(orc):
+    """Hand-derived example of tests/golden/handworked_v3_l2.json (closed forms)."""
+    with open(os.path.join(GOLDEN, "handworked_v3_l2.json")) as fh:
+        g = json.load(fh)
+    V, L = g["V"], g["L"]
+    trie = orc.OracleTrie(np.asarray(g["catalog"], dtype=np.int64), V=V)
+    assert list(trie.nodes_per_depth) == g["expected_trie"]["nodes_per_depth"]
+    for key, nid in g["expected_trie"]["node_of_prefix"].items():
+        t = tuple(int(c) for c in key.split(",")) if key else ()
+        assert trie.node_id(len(t), pack(t)) == nid, key
+    for key, item in g["expected_trie"]["item_of_sid"].items():
+        t = tuple(int(c) for c in key.split(","))
+        assert trie.item_of(pack(t)) == item, key
+    weights = {k: v for k, v in g["logit_weights_by_prefix"].items()}
+
+    def logit_fn(d, p):
+        w = weights[",".join(str(c) for c in p)]
+        return [math.log(x) for x in w]
+    for case in g["cases"]:
+        norm = 0 if case["norm"] == "children" else 1
+        sids, scores, _ = run_decode(orc, trie, case["width"], logit_fn, norm)
+        exp = case["beams"]
+        assert [tuple(b["sid"]) for b in exp] == sids, (case, sids)
+        for b, s in zip(exp, scores):
+            assert abs(s - math.log(b["p"][0] / b["p"][1])) < 1e-12
+            assert trie.item_of(pack(b["sid"])) == b["item"]
+
+
+def pin_trie_numbering(orc, seed=0):
+    """Depth-major lexicographic node ids and child lists, against explicit enumeration."""
+    rng = np.random.default_rng(seed)
+    for V, L, n in [(3, 3, 12), (5, 2, 9), (4, 4, 40), (256, 3, 300)]:
+        cat = [tuple(int(c) for c in rng.integers(0, V, L)) for _ in range(n)]
+        trie = orc.OracleTrie(np.asarray(cat, dtype=np.int64), V=V)
+        nid = 0
+        for d in range(L + 1):
+            prefs = sorted(set(c[:d] for c in cat))
+            for p in prefs:
+                assert trie.node_id(d, pack(p)) == nid
+                nid += 1
+            if d < L:
+                for p in prefs:
+                    codes, nodes = trie.children(d, pack(p))
+                    kids = sorted(set(c[d] for c in cat if c[:d] == p))
+                    assert list(codes) == kids
+                    assert list(nodes) == [trie.node_id(d + 1, pack(p + (k,))) for k in kids]
+        assert nid == sum(trie.nodes_per_depth)
+
+
+def pin_dedupe_lowest_row(orc):
+    cat = np.asarray([[1, 2], [0, 0], [1, 2], [0, 0], [3, 1], [1, 2]], dtype=np.int64)
+    trie = orc.OracleTrie(cat, V=4)
+    assert trie.n_distinct == 3
+    assert trie.item_of(pack((1, 2))) == 0
+    assert trie.item_of(pack((0, 0))) == 1
+    assert trie.item_of(pack((3, 1))) == 4
+
+
+def pin_masked_log_softmax_vs_torch(orc, seed=1):
+    """Masked log-softmax equals torch.log_softmax of the masked row (library routine)."""
+    rng = np.random.default_rng(seed)
+    for V in (2, 7, 256):
+        for _ in range(20):
+            x = rng.normal(0, 3, V)
+            f = int(rng.integers(1, V + 1))
+            codes = np.sort(rng.choice(V, f, replace=False))
+            mask = torch.zeros(V, dtype=torch.bool)
+            mask[torch.from_numpy(codes)] = True
+            xt = torch.from_numpy(x)
+            ref_c = torch.log_softmax(xt.masked_fill(~mask, float("-inf")), 0)[mask].numpy()
+            ref_l = torch.log_softmax(xt, 0)[mask].numpy()
+            got_c = orc.masked_log_softmax(x, codes, 0)
+            got_l = orc.masked_log_softmax(x, codes, 1)
+            assert np.max(np.abs(got_c - ref_c)) < 1e-12
+            assert np.max(np.abs(got_l - ref_l)) < 1e-12
+            assert abs(math.fsum(np.exp(got_c)) - 1.0) < 1e-12
+
+
+def pin_single_child_and_constant(orc):
+    """Closed forms: a single child gets logp = 0 exactly; constant logits give -ln(fanout)."""
+    # prefix 0 has one child per level; prefix 1 fans out 1 -> 3
+    cat = [(0, 5, 7), (1, 2, 0), (1, 2, 1), (1, 2, 2), (1, 3, 3)]
+    trie = orc.OracleTrie(np.asarray(cat), V=8)
+    zero = lambda d, p: [0.0] * 8
+    sids, scores, hist = run_decode(orc, trie, 8, zero)
+    expect = {}
+    kids = bf._children_map(cat)
+    for sid in cat:
+        expect[sid] = -sum(math.log(len(kids[sid[:d]])) for d in range(3))
+    for sid, s in zip(sids, scores):
+        assert abs(s - expect[sid]) < 1e-12, (sid, s, expect[sid])
+    # ranking: descending closed-form score; exact ties by flat index (parent rank, then code)
+    got = [expect[s] for s in sids]
+    assert got == sorted(got, reverse=True)
+    assert sids[0] == (0, 5, 7)                   # -ln 2 beats every path through prefix 1
+    # after step 1 the single-child rows keep their score exactly
+    h1 = hist[1]
+    for par, sc in zip(h1["parent"], h1["score"]):
+        if hist[0]["code"][par] == 0:
+            assert sc == hist[0]["score"][par]
+
+
+def pin_ties_lower_flat(orc):
+    """Equal candidates: the better-ranked parent first, then the lower code."""
+    cat = [(a, b) for a in range(4) for b in range(4)]
+    trie = orc.OracleTrie(np.asarray(cat), V=4)
+    zero = lambda d, p: [0.0] * 4
+    sids, scores, _ = run_decode(orc, trie, 16, zero)
+    assert sids == cat                            # all tied: flat order == lexicographic
+    sids5, _, _ = run_decode(orc, trie, 5, zero)
+    # step 0 keeps codes 0..3; step 1: 16 equal candidates, flat order keeps the first five
+    assert sids5 == cat[:5]
+
+
+def pin_full_catalog_unconstrained(orc, seed=2):
+    """With every V^L tuple in the catalog the mask is a no-op, so the step is
+    torch.log_softmax of each row plus a stable descending torch.sort of the flattened
+    [rows*V] scores (library routines)."""
+    for V, L, width in [(5, 3, 7), (16, 2, 20), (3, 4, 5)]:
+        cat = list(itertools.product(range(V), repeat=L))
+        trie = orc.OracleTrie(np.asarray(cat), V=V)
+        fn = gaussian_logit_fn(seed, V)
+        for norm in (0, 1):
+            sids, scores, _ = run_decode(orc, trie, width, fn, norm)
+            beams = [()]
+            sc = torch.zeros(1, dtype=torch.float64)
+            for d in range(L):
+                x = torch.tensor(np.stack([fn(d, p) for p in beams]), dtype=torch.float64)
+                cand = (sc[:, None] + torch.log_softmax(x, dim=1)).reshape(-1)
+                s_sorted, idx = torch.sort(cand, descending=True, stable=True)
+                k = min(width, cand.numel())
+                idx = idx[:k].tolist()
+                beams = [beams[i // V] + (i % V,) for i in idx]
+                sc = s_sorted[:k]
+            assert beams == sids
+            assert np.max(np.abs(sc.numpy() - np.asarray(scores))) < 1e-12
+
+
+def pin_width_one_greedy(orc, seed=3):
+    """Width 1 is the greedy constrained argmax over children (closed form)."""
+    rng = np.random.default_rng(seed)
+    for V, L in [(6, 3), (256, 4)]:
+        cat = random_catalog(rng, V, L, 60) if V < 10 else \
+            [tuple(int(c) for c in rng.integers(0, V, L)) for _ in range(500)]
+        trie = orc.OracleTrie(np.asarray(cat), V=V)
+        fn = gaussian_logit_fn(seed + V, V)
+        kids = bf._children_map(cat)
+        p, total = (), 0.0
+        for d in range(L):
+            row = np.asarray(fn(d, p))
+            ks = kids[p]
+            best = max(ks, key=lambda c: (row[c], -c))
+            m = max(row[k] for k in ks)
+            total += row[best] - (m + math.log(sum(math.exp(row[k] - m) for k in ks)))
+            p = p + (best,)
+        sids, scores, _ = run_decode(orc, trie, 1, fn)
+        assert sids == [p]
+        assert abs(scores[0] - total) < 1e-12
+
+
+def pin_wide_equals_bruteforce(orc, seed=4):
+    """A beam at least as wide as every level's distinct-prefix count prunes nothing, so
+    the final beams are every catalog SID ranked by summed log-probabilities."""
+    rng = np.random.default_rng(seed)
+    for V, L, n in [(4, 3, 30), (256, 3, 120), (7, 2, 49)]:
+        cat = random_catalog(rng, V, L, n) if V ** L < 10 ** 6 else \
+            [tuple(int(c) for c in rng.integers(0, V, L)) for _ in range(n)]
+        trie = orc.OracleTrie(np.asarray(cat), V=V)
+        width = max(trie.nodes_per_depth)
+        fn = gaussian_logit_fn(seed + n, V)
+        for norm in (0, 1):
+            sids, scores, _ = run_decode(orc, trie, width, fn, norm)
+            ref = bf.all_scores(cat, V, fn, norm)
+            assert len(sids) == len(ref) == trie.n_distinct
+            assert set(sids) == set(s for _, s in ref)
+            d = dict((s, v) for v, s in ref)
+            for s, v in zip(sids, scores):
+                assert abs(v - d[s]) < 1e-12
+            assert all(scores[i] >= scores[i + 1] for i in range(len(scores) - 1))
+
+
+def pin_tiny_vs_replay(orc, seed=5, n_cases=150):
+    """Tiny catalogs, any width, both normalisers: equal to the explicit-list replay."""
+    rng = np.random.default_rng(seed)
+    for case in range(n_cases):
+        V = int(rng.integers(2, 6))
+        L = int(rng.integers(1, 4))
+        n = int(rng.integers(1, V ** L + 1))
+        cat = random_catalog(rng, V, L, n)
+        width = int(rng.integers(1, 9))
+        norm = int(rng.integers(0, 2))
+        fn = gaussian_logit_fn(seed * 1000 + case, V)
+        trie = orc.OracleTrie(np.asarray(cat), V=V)
+        sids, scores, _ = run_decode(orc, trie, width, fn, norm)
+        ref = bf.beam_replay(cat, V, width, fn, norm)
+        assert sids == [p for _, p in ref], (case, V, L, n, width, norm)
+        assert np.max(np.abs(np.asarray(scores) - np.asarray([s for s, _ in ref]))) < 1e-12
+
+
+def pin_legality(orc, seed=6):
+    """Every emitted SID is in the catalog (illegal rate exactly 0, flashrec 0.1.0,
+    Features > Decoding), no request holds a SID twice, and every survivor's node is a
+    child of its parent's node."""
+    rng = np.random.default_rng(seed)
+    V, L = 256, 4
+    cat = [tuple(int(c) for c in rng.integers(0, 8, L)) for _ in range(3000)]
+    catset = set(cat)
+    prefset = set(c[:d] for c in cat for d in range(L + 1))
+    trie = orc.OracleTrie(np.asarray(cat), V=V)
+    fn = gaussian_logit_fn(seed, V)
+    sids, scores, hist = run_decode(orc, trie, 50, fn)
+    assert len(sids) == 50 and len(set(sids)) == 50
+    assert all(s in catset for s in sids)
+    prev = [()]
+    for d, h in enumerate(hist):
+        cur = []
+        for par, code, node in zip(h["parent"], h["code"], h["node"]):
+            p = prev[par] + (int(code),)
+            assert p in prefset
+            assert trie.node_id(d + 1, pack(p)) == node
+            pd, pp = trie.prefix_of(int(node))
+            assert pd == d + 1 and pp == pack(p)
+            cur.append(p)
+        prev = cur
+
+
+def pin_lmhead_exact(orc, seed=7):
+    """fp64 H W^T from bf16 inputs equals the exact rational result; the operands have
+    few significant bits, so every product and partial sum is exact in float64."""
+    rng = np.random.default_rng(seed)
+
+    # bf16 values: sign, 7 stored mantissa bits, exponent in [-8, 7]. A product has at most
+    # 16 significant bits spread over 2**-16..2**15; a sum of up to 64 of them fits in 53 bits
+    # (exact in float64) but not in float32's 24.
+    def rand_bf16(shape):
+        sign = rng.integers(0, 2, shape)
+        e = rng.integers(-8, 8, shape)
+        mant = rng.integers(0, 128, shape)
+        val = (1 + mant / 128.0) * (2.0 ** e) * np.where(sign == 1, -1.0, 1.0)
+        bits = (np.asarray(val, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        return bits, val
+    # the 4x4x4 case is square on purpose: a transposed operand still runs
+    for R, V, H in [(4, 4, 4), (3, 5, 64)]:
+        hb, hv = rand_bf16((R, H))
+        wb, wv = rand_bf16((V, H))
+        got = orc.lmhead_logits(hb, wb)
+        assert got.shape == (R, V)
+        for r in range(R):
+            for c in range(V):
+                exact = sum(Fraction(float(hv[r, k])) * Fraction(float(wv[c, k]))
+                            for k in range(H))
+                assert Fraction(float(got[r, c])) == exact
+
+
+def pin_bf16_widening(orc):
+    bits = np.asarray([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x4049], dtype=np.uint16)
+    want = [1.0, -2.0, 1.0078125, 0.0, -0.0, 3.140625]
+    got = orc.widen_logits(bits, "bf16")
+    assert list(got) == want
+    f = np.asarray([1.5, -0.25], dtype=np.float32)
+    assert list(orc.widen_logits(f, "f32")) == [1.5, -0.25]
+
+
+def pin_decode_api(orc, seed=8):
+    """``orc.decode`` agrees with the step-by-step loop and reports catalog items."""
+    rng = np.random.default_rng(seed)
+    cat = [tuple(int(c) for c in rng.integers(0, 5, 3)) for _ in range(40)]
+    trie = orc.OracleTrie(np.asarray(cat), V=256)
+    fn = gaussian_logit_fn(seed, 256)
+    sids, scores, _ = run_decode(orc, trie, 6, fn)
+
+    def logits_for(t, prefixes):
+        return np.stack([np.asarray(fn(t, unpack(p, t))) for p in prefixes])
+    out = orc.decode(trie, 6, logits_for)
+    assert [unpack(p, 3) for p in out["sids"]] == sids
+    assert np.max(np.abs(out["scores"] - np.asarray(scores))) < 1e-12
+    for p, item in zip(out["sids"], out["items"]):
+        assert tuple(cat[item]) == unpack(p, 3)
+        assert all(tuple(cat[j]) != unpack(p, 3) for j in range(item))
+
+
+ALL_PINS = [pin_handworked, pin_trie_numbering, pin_dedupe_lowest_row,
+            pin_masked_log_softmax_vs_torch, pin_single_child_and_constant, pin_ties_lower_flat,
+            pin_full_catalog_unconstrained, pin_width_one_greedy, pin_wide_equals_bruteforce,
+            pin_tiny_vs_replay, pin_legality, pin_lmhead_exact, pin_bf16_widening,
+            pin_decode_api]

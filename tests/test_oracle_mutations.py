@@ -1,0 +1,173 @@
+"""Plant plausible mistakes in copies of the oracle and require that some pin fails.
+
+Each mutant changes one thing (a dropped term, a wrong sign, a wrong index, a
+transposed operand, a flipped tie-break...). A mutant that every pin accepts would
+mean the pins cannot tell that mistake from the method. CPU only; nothing here
+touches the HIP path.
+"""
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import beam as ob
+from oracle.trie import OracleTrie
+import pins
+
+
+def _expand(trie, depth, prefixes, scores, logits64, beam_width, norm=0, *, lsm=None,
+            use_score=True, flat_sign=1, extra=0, score_shift=0, parent_from_code=False):
+    lsm = lsm or ob.masked_log_softmax
+    V = trie.V
+    cs, cf, cp, cc, cn = [], [], [], [], []
+    for r in range(len(prefixes)):
+        codes, nodes = trie.children(depth, prefixes[r])
+        logp = lsm(logits64[r], codes, norm)
+        s = float(scores[(r + score_shift) % len(scores)]) if use_score else 0.0
+        cs.append(s + logp)
+        cf.append(r * V + codes)
+        cp.append(np.full(codes.size, r))
+        cc.append(codes)
+        cn.append(nodes)
+    score, flat = np.concatenate(cs), np.concatenate(cf)
+    order = np.lexsort((flat_sign * flat, -score))
+    out = {"cand_score": score[order], "cand_flat": flat[order],
+           "cand_parent": np.concatenate(cp)[order], "cand_code": np.concatenate(cc)[order],
+           "cand_node": np.concatenate(cn)[order]}
+    k = min(beam_width + extra, score.size)
+    for key in ("parent", "code", "node", "score"):
+        out[key] = out["cand_" + key][:k]
+    pref = np.asarray([int(p) for p in prefixes], dtype=np.uint64)
+    par = out["code"] % len(pref) if parent_from_code else out["parent"]
+    out["prefix"] = pref[par] * np.uint64(256) + out["code"].astype(np.uint64)
+    return out
+
+
+def _lsm_always(norm_forced):
+    def f(x, codes, norm=0):
+        return ob.masked_log_softmax(x, codes, norm_forced)
+    return f
+
+
+def _lsm_sign(x, codes, norm=0):
+    return -ob.masked_log_softmax(x, codes, norm)
+
+
+def _lsm_drop_max(x, codes, norm=0):
+    support = x[codes] if norm == 0 else x
+    m = support.max()
+    return x[codes] - np.log(np.sum(np.exp(support - m)))
+
+
+class _TrieNodeOffByOne(OracleTrie):
+    def children(self, depth, prefix):
+        codes, nodes = super().children(depth, prefix)
+        return codes, nodes + 1
+
+
+class _TrieLastRow(OracleTrie):
+    def __init__(self, sids, V=256):
+        super().__init__(sids, V)
+        sids = np.asarray(sids)
+        keys = np.zeros(sids.shape[0], dtype=np.uint64)
+        for j in range(self.L):
+            keys = keys * np.uint64(256) + sids[:, j].astype(np.uint64)
+        rev = keys[::-1]
+        _, idx = np.unique(rev, return_index=True)
+        self.leaf_item = (len(keys) - 1 - idx).astype(np.int64)
+
+
+class _TrieNoMask(OracleTrie):
+    def children(self, depth, prefix):
+        codes, nodes = super().children(depth, prefix)
+        allc = np.arange(self.V, dtype=np.int64)
+        fake = np.full(self.V, nodes[0] if nodes.size else 0, dtype=np.int64)
+        fake[codes] = nodes
+        return allc, fake
+
+
+class _TrieDfsNumbering(OracleTrie):
+    """Node ids in depth-first (pre-order) order instead of depth-major."""
+    def __init__(self, sids, V=256):
+        super().__init__(sids, V)
+        order = []
+
+        def visit(d, p):
+            order.append((d, p))
+            if d < self.L:
+                for c in OracleTrie.children(self, d, p)[0]:
+                    visit(d + 1, p * 256 + int(c))
+        visit(0, 0)
+        self._dfs = {dp: i for i, dp in enumerate(order)}
+
+    def node_id(self, depth, prefix):
+        return self._dfs[(depth, int(prefix))]
+
+    def children(self, depth, prefix):
+        codes, _ = super().children(depth, prefix)
+        return codes, np.asarray([self._dfs[(depth + 1, int(prefix) * 256 + int(c))]
+                                  for c in codes], dtype=np.int64)
+
+
+def _widen_shift8(x, dtype):
+    if dtype == "bf16":
+        bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(8)
+        return bits.view(np.float32).astype(np.float64)
+    return ob.widen_logits(x, dtype)
+
+
+def _lmhead_transposed(h, w):
+    return ob.widen_logits(h, "bf16") @ ob.widen_logits(w, "bf16")
+
+
+def _lmhead_f32(h, w):
+    return (ob.widen_logits(h, "bf16").astype(np.float32) @
+            ob.widen_logits(w, "bf16").astype(np.float32).T).astype(np.float64)
+
+
+def _ns(**over):
+    ns = dict(OracleTrie=oracle.OracleTrie, expand_request=oracle.expand_request,
+              masked_log_softmax=oracle.masked_log_softmax, decode=oracle.decode,
+              lmhead_logits=oracle.lmhead_logits, widen_logits=oracle.widen_logits)
+    ns.update(over)
+    return types.SimpleNamespace(**ns)
+
+
+def _exp(**kw):
+    return lambda *a, **k: _expand(*a, **kw)
+
+
+MUTANTS = {
+    "normaliser_always_level": dict(masked_log_softmax=_lsm_always(1),
+                                    expand_request=_exp(lsm=_lsm_always(1))),
+    "normaliser_always_children": dict(masked_log_softmax=_lsm_always(0),
+                                       expand_request=_exp(lsm=_lsm_always(0))),
+    "logp_sign_flipped": dict(masked_log_softmax=_lsm_sign, expand_request=_exp(lsm=_lsm_sign)),
+    "lse_dropped_max_term": dict(masked_log_softmax=_lsm_drop_max,
+                                 expand_request=_exp(lsm=_lsm_drop_max)),
+    "parent_score_dropped": dict(expand_request=_exp(use_score=False)),
+    "parent_score_wrong_row": dict(expand_request=_exp(score_shift=1)),
+    "tie_break_flat_descending": dict(expand_request=_exp(flat_sign=-1)),
+    "keeps_one_extra_beam": dict(expand_request=_exp(extra=1)),
+    "survivor_parent_wrong_index": dict(expand_request=_exp(parent_from_code=True)),
+    "child_node_off_by_one": dict(OracleTrie=_TrieNodeOffByOne),
+    "duplicate_sid_maps_to_last_row": dict(OracleTrie=_TrieLastRow),
+    "children_not_masked": dict(OracleTrie=_TrieNoMask),
+    "node_numbering_depth_first": dict(OracleTrie=_TrieDfsNumbering),
+    "bf16_widened_wrong_shift": dict(widen_logits=_widen_shift8),
+    "lmhead_operand_transposed": dict(lmhead_logits=_lmhead_transposed),
+    "lmhead_fp32_accumulate": dict(lmhead_logits=_lmhead_f32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_some_pin_rejects_mutant(name):
+    ns = _ns(**MUTANTS[name])
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(ns)
+        except Exception as e:          # an assertion, or the mutant breaking an invariant
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin rejects mutant {name}"
