@@ -1,0 +1,229 @@
+/*
+ * tcb.h -- catalog-constrained wide-beam expansion on MI355X (gfx950).
+ *
+ * C ABI of libtcb.so. The operation is one step of generative-recommendation
+ * decoding over semantic IDs (SIDs): every live beam row's logits over its level's
+ * code range are masked to the children of the row's node in a prefix trie of
+ * valid catalog SIDs, log-softmaxed and added to the beam score; each request then
+ * keeps its best n (beam width) (row, child) candidates, ranked best-first, and the
+ * survivors are re-indexed by parent row and trie node.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [FR]  flashrec 0.1.0 (PyPI project page): Features > Decoding ("SID
+ *         constraint": dense or CSR-sparse trie, illegal SIDs never candidates,
+ *         lm_head only over the SID token range; "Scheduling": requests admitted
+ *         into decode waves between steps under a beam-row slot budget),
+ *         Features > Serving ("API": deterministic top-k at temperature 0, Gumbel
+ *         top-k without replacement above it), Quickstart (beam width n, ranked
+ *         choices with a sequence score, --batch-slots).
+ *   [OLA] OneLA summary: section 2.1 (candidates globally selected across the
+ *         beam), sections 2.4 / 3.3 (children keep an index to their parent;
+ *         records are append-only and never moved).
+ *   [SP]  SPRINT summary, inference paragraph (valid SIDs of a prefix trie scored
+ *         by their token log-probability sum).
+ *
+ * Conventions
+ *   - Every call returns tcb_status: TCB_OK (0) or a negative error code. On error
+ *     tcb_last_error() returns a thread-local message. Argument errors are found on
+ *     the host before any device work, so they leave every object unchanged.
+ *   - Device pointers ("d_") are HIP device addresses owned by the caller; they
+ *     must stay valid until the work enqueued on the stream has completed. The
+ *     library never allocates device memory. Host pointers ("h_" or plain) are
+ *     read or written before the call returns unless stated otherwise.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the default stream).
+ *   - A tcb_trie is immutable after tcb_trie_upload and may be shared by several
+ *     tcb_beams. A tcb_beams object is used from one host thread and one stream.
+ *   - Only tcb_beam_check and tcb_beam_finalize synchronise the stream.
+ */
+#ifndef TCB_H
+#define TCB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tcb_status;
+
+enum {
+    TCB_OK = 0,
+    TCB_E_ARG = -1,        /* null pointer, bad size, bad enum value             */
+    TCB_E_RANGE = -2,      /* a SID code >= V, L or V out of range               */
+    TCB_E_BUDGET = -3,     /* beam widths exceed the free slots or request ids   */
+    TCB_E_STATE = -4,      /* call not valid in the current state                */
+    TCB_E_WORKSPACE = -5,  /* device buffer too small or misaligned              */
+    TCB_E_HIP = -6,        /* a HIP runtime call failed                          */
+    TCB_E_NONFINITE = -7,  /* a non-finite logit was seen (validation on)        */
+    TCB_E_DEVICE = -8      /* the device found corrupt state; destroy the wave   */
+};
+
+enum { TCB_F32 = 0, TCB_BF16 = 1 };                 /* logits element type           */
+enum { TCB_NORM_CHILDREN = 0, TCB_NORM_LEVEL = 1 }; /* log-softmax normaliser        */
+
+#define TCB_MAX_L 8
+#define TCB_MAX_V 256
+#define TCB_MAX_WIDTH 4096
+
+typedef struct tcb_trie tcb_trie;
+typedef struct tcb_beams tcb_beams;
+
+const char *tcb_last_error(void);
+const char *tcb_version(void);
+
+/* ------------------------------------------------------------------------ trie */
+
+/* Build the prefix trie of a SID catalog on the host ([FR] Decoding, "SID
+ * constraint"; [SP] inference).
+ *   sids        host [n_items][L] uint8, row i = SID of catalog item i
+ *   n_items     > 0
+ *   L           SID depth, 1..TCB_MAX_L
+ *   V           codes per level, 2..256; every code must be < V
+ *   mask_depths depths 0..mask_depths-1 also get a 256-bit child mask per node
+ *               ("dense" trie); deeper nodes use only the CSR child list. 0..L.
+ * Duplicated SIDs collapse onto one leaf whose item is the lowest catalog row.
+ * Nodes are numbered depth-major and lexicographically: the root is 0, depth d
+ * holds ids [off_d, off_{d+1}) in ascending prefix order, so the children of a node
+ * are a contiguous id range in ascending code order.
+ * Errors: TCB_E_ARG (null, n_items <= 0, mask_depths out of range),
+ *         TCB_E_RANGE (L or V out of range, a code >= V). */
+tcb_status tcb_build_trie(const uint8_t *sids, int64_t n_items, int32_t L, int32_t V,
+                          int32_t mask_depths, tcb_trie **out);
+
+typedef struct {
+    int32_t L, V, mask_depths;
+    int64_t n_items;                       /* catalog rows given                      */
+    int64_t n_distinct;                    /* distinct SIDs = leaves                  */
+    int64_t nodes_per_depth[TCB_MAX_L + 1];
+    int64_t node_offset[TCB_MAX_L + 2];    /* off_d; node_offset[L+1] = total nodes   */
+    size_t device_bytes;                   /* size of the device image                */
+} tcb_trie_info_t;
+
+tcb_status tcb_trie_info(const tcb_trie *t, tcb_trie_info_t *out);
+
+/* Host views of the CSR arrays (valid until tcb_trie_destroy), for inspection:
+ *   child_begin [node_offset[L] + 1]  children of internal node n are node ids
+ *                                      child_begin[n] .. child_begin[n+1]-1
+ *   child_code  [total nodes]         code on the edge into node k (0 for the root)
+ *   leaf_item   [n_distinct]          catalog row of leaf node_offset[L] + j       */
+tcb_status tcb_trie_host_arrays(const tcb_trie *t, const uint32_t **child_begin,
+                                const uint8_t **child_code, const int32_t **leaf_item);
+
+/* Copy the trie image into caller-owned device memory of at least
+ * tcb_trie_info().device_bytes bytes (256-byte aligned). Asynchronous on stream;
+ * the host image stays owned by the trie. A later upload replaces the previous one
+ * for every wave created afterwards. Errors: TCB_E_ARG, TCB_E_WORKSPACE, TCB_E_HIP. */
+tcb_status tcb_trie_upload(tcb_trie *t, void *d_buf, size_t bytes, void *stream);
+
+void tcb_trie_destroy(tcb_trie *t);
+
+/* ------------------------------------------------------------------------ wave */
+
+/* Device workspace needed by a wave (tcb_beams) with at most max_slots beam rows
+ * in flight, max_requests requests in flight and beams at most max_width wide. */
+tcb_status tcb_beams_workspace_bytes(const tcb_trie *t, int32_t max_slots,
+                                     int32_t max_requests, int32_t max_width, size_t *bytes);
+
+/* Create a decode wave over an uploaded trie ([FR] Decoding, "Scheduling": rows of
+ * different requests share a step under a beam-row slot budget).
+ *   norm   TCB_NORM_CHILDREN (log-softmax over the node's children) or
+ *          TCB_NORM_LEVEL (over all V codes of the level, then masked)
+ *   d_ws   caller-owned device workspace of ws_bytes >= tcb_beams_workspace_bytes,
+ *          256-byte aligned; the wave initialises it on `stream`.
+ * Errors: TCB_E_ARG, TCB_E_STATE (trie not uploaded), TCB_E_WORKSPACE, TCB_E_HIP. */
+tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_requests,
+                            int32_t max_width, int32_t norm, void *d_ws, size_t ws_bytes,
+                            void *stream, tcb_beams **out);
+
+/* Admit n requests at the root (one row, score 0) before the next step.
+ *   widths         host [n], beam width n_i of each request, 1..max_width
+ *   out_req_ids    host [n] (may be NULL): request id of each admitted request
+ *   out_slot_base  host [n] (may be NULL): request i owns slots
+ *                  [base_i, base_i + n_i); its live rows are the first rows_i of
+ *                  them, best first. Logits / hidden rows are indexed by slot.
+ * All or nothing: if the requests do not all fit in the free slots / ids the call
+ * returns TCB_E_BUDGET and admits none. */
+tcb_status tcb_beam_init(tcb_beams *b, int32_t n, const int32_t *widths,
+                         int32_t *out_req_ids, int32_t *out_slot_base, void *stream);
+
+/* One constrained beam step for every admitted, unfinished request ([FR] Decoding;
+ * [OLA] 2.1; [SP] inference).
+ *   d_logits  device [max_slots][ld] of dtype TCB_F32 or TCB_BF16; row `slot` holds
+ *             the V logits of that slot's row at its request's current level. Only
+ *             live rows are read. ld >= V (elements).
+ * Per request: candidates (r, c) for every live row r and child code c of its node,
+ * scored s_r + logp(c); the best min(n_i, #candidates) by (score desc, r*V+c asc)
+ * become the new rows in rank order, with parent slot base_i + r and a
+ * back-pointer (r, c) appended for this level. Requests never compete.
+ * Errors: TCB_E_ARG, TCB_E_STATE (no unfinished request), TCB_E_HIP. */
+tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t dtype,
+                         void *stream);
+
+/* Same step with the logits computed on chip by the SID-range lm_head ([FR]
+ * Decoding: lm_head only over the SID token range):
+ *   x[slot][c] = sum_h hidden[slot][h] * W[level][c][h], fp32 accumulate, no bias.
+ *   d_hidden  device bf16 [max_slots][ld_hidden], ld_hidden >= H, H % 64 == 0
+ *   d_weight  device bf16 [L][V][H] contiguous (one [V][H] matrix per level)
+ * Errors as tcb_beam_step. */
+tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_hidden,
+                                int32_t H, const void *d_weight, void *stream);
+
+/* Copy the current wave state into caller device buffers (any may be NULL):
+ *   d_node, d_score       [max_slots]  node id and score of each slot's row
+ *   d_parent_slot         [max_slots]  slot of each row's parent at the last step
+ *   d_hist                [L][max_slots] back-pointer of level t: (r << 8) | c
+ *   d_rows, d_level       [max_requests] live rows and levels per request id
+ * Rows beyond a request's live count hold stale values. Asynchronous. */
+tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score,
+                           int32_t *d_parent_slot, uint32_t *d_hist, int32_t *d_rows,
+                           int32_t *d_level, void *stream);
+
+/* Host-side status (no device access): steps taken, requests admitted and
+ * finished, free slots. */
+typedef struct {
+    int64_t steps;
+    int32_t active;          /* admitted and not yet at depth L */
+    int32_t finished;        /* at depth L, awaiting finalize   */
+    int32_t free_slots;
+    int32_t free_requests;
+} tcb_beams_status_t;
+tcb_status tcb_beams_status(const tcb_beams *b, tcb_beams_status_t *out);
+
+/* Level of a request (host-side; levels advance by one per step). */
+tcb_status tcb_request_level(const tcb_beams *b, int32_t req_id, int32_t *level);
+
+/* Turn on non-finite checks of every logit read (sticky TCB_E_NONFINITE). */
+tcb_status tcb_beams_set_validate(tcb_beams *b, int32_t on);
+
+/* Synchronise `stream` and report a sticky device error, if any. */
+tcb_status tcb_beam_check(tcb_beams *b, void *stream);
+
+/* Finished requests' beams, ranked best-first with their scores ([FR] Quickstart:
+ * ranked choices with a sequence score), then release their slots and ids.
+ *   req_ids    host [n], requests at depth L
+ *   h_sids     host [n][max_width][L] uint8   codes, walked back from the
+ *                                             per-level back-pointers
+ *   h_scores   host [n][max_width] float      summed log-probabilities
+ *   h_items    host [n][max_width] int64      catalog row of the SID
+ *   h_counts   host [n] int32                 number of beams of each request
+ * Entries past a request's count are zero / -inf / -1. Synchronises `stream`.
+ * Errors: TCB_E_ARG, TCB_E_STATE (a request not finished), TCB_E_NONFINITE,
+ *         TCB_E_DEVICE, TCB_E_HIP. */
+tcb_status tcb_beam_finalize(tcb_beams *b, int32_t n, const int32_t *req_ids,
+                             uint8_t *h_sids, float *h_scores, int64_t *h_items,
+                             int32_t *h_counts, void *stream);
+
+/* As tcb_beam_finalize, but writes caller device buffers of the same layouts and
+ * does not synchronise; the ids and slots are reusable by the next tcb_beam_init
+ * (stream order keeps the gather ahead of any reuse). */
+tcb_status tcb_beam_finalize_device(tcb_beams *b, int32_t n, const int32_t *req_ids,
+                                    uint8_t *d_sids, float *d_scores, int64_t *d_items,
+                                    int32_t *d_counts, void *stream);
+
+void tcb_beams_destroy(tcb_beams *b);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TCB_H */

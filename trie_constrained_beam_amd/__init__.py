@@ -1,0 +1,11 @@
+"""Catalog-constrained wide-beam expansion on MI355X (gfx950).
+
+The beam step runs in libtcb.so (hand-written HIP kernels behind the C ABI of
+include/tcb.h); this package is its Python binding (``Trie``, ``Beams``) plus the
+seeded workload generators in ``synth``.
+"""
+from . import _lib
+from .api import Beams, Trie
+from ._lib import TcbError
+
+__all__ = ["Beams", "Trie", "TcbError"]

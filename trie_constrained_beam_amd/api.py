@@ -1,0 +1,199 @@
+"""Python face of libtcb: the same calls as include/tcb.h, with torch for device memory
+and streams. Every step of the beam path runs in the HIP library; this module only
+marshals arguments.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from ._lib import check, lib
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
+
+
+class Trie:
+    """Prefix trie of a SID catalog (host build, optional device upload)."""
+
+    def __init__(self, sids, V: int = 256, mask_depths=None, device=None):
+        sids = np.ascontiguousarray(sids, dtype=np.uint8)
+        if sids.ndim != 2:
+            raise ValueError("sids must be [n_items, L]")
+        n, depth = sids.shape
+        mask_depths = min(3, depth) if mask_depths is None else int(mask_depths)
+        h = C.c_void_p()
+        check(lib().tcb_build_trie(sids.ctypes.data, n, depth, V, mask_depths, C.byref(h)))
+        self._h = h
+        self.info = L.TrieInfo()
+        check(lib().tcb_trie_info(h, C.byref(self.info)))
+        self.L, self.V = int(self.info.L), int(self.info.V)
+        self.d_image = None
+        if device is not None:
+            self.upload(device)
+
+    def __del__(self):
+        if getattr(self, "_h", None) and lib is not None:
+            lib().tcb_trie_destroy(self._h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def n_distinct(self):
+        return int(self.info.n_distinct)
+
+    @property
+    def nodes_per_depth(self):
+        return [int(self.info.nodes_per_depth[d]) for d in range(self.L + 1)]
+
+    @property
+    def node_offset(self):
+        return [int(self.info.node_offset[d]) for d in range(self.L + 2)]
+
+    def host_arrays(self):
+        """Copies of (child_begin, child_code, leaf_item) as numpy arrays."""
+        cb, cc, li = C.c_void_p(), C.c_void_p(), C.c_void_p()
+        check(lib().tcb_trie_host_arrays(self._h, C.byref(cb), C.byref(cc), C.byref(li)))
+        off = self.node_offset
+        n_int, n_all = off[self.L], off[self.L + 1]
+        a = np.ctypeslib.as_array(C.cast(cb, C.POINTER(C.c_uint32)), shape=(n_int + 1,)).copy()
+        b = np.ctypeslib.as_array(C.cast(cc, C.POINTER(C.c_uint8)), shape=(n_all,)).copy()
+        c = np.ctypeslib.as_array(C.cast(li, C.POINTER(C.c_int32)), shape=(self.n_distinct,)).copy()
+        return a, b, c
+
+    def upload(self, device="cuda"):
+        nbytes = int(self.info.device_bytes)
+        self.d_image = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        check(lib().tcb_trie_upload(self._h, _ptr(self.d_image), nbytes, _stream()))
+        return self
+
+
+class Beams:
+    """A decode wave: slot budget, requests, and the per-slot beam state on the GPU."""
+
+    def __init__(self, trie: Trie, max_slots: int, max_requests: int, max_width: int,
+                 norm: str = "children", device="cuda"):
+        if trie.d_image is None:
+            trie.upload(device)
+        self.trie = trie
+        self.max_slots, self.max_requests, self.max_width = max_slots, max_requests, max_width
+        nb = C.c_size_t()
+        check(lib().tcb_beams_workspace_bytes(trie.handle, max_slots, max_requests, max_width,
+                                              C.byref(nb)))
+        self.ws = torch.empty(int(nb.value), dtype=torch.uint8, device=device)
+        n = {"children": L.TCB_NORM_CHILDREN, "level": L.TCB_NORM_LEVEL}[norm]
+        h = C.c_void_p()
+        check(lib().tcb_beams_create(trie.handle, max_slots, max_requests, max_width, n,
+                                     _ptr(self.ws), int(nb.value), _stream(), C.byref(h)))
+        self._h = h
+        self.device = device
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            lib().tcb_beams_destroy(self._h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def init(self, widths):
+        w = np.ascontiguousarray(widths, dtype=np.int32)
+        ids = np.zeros(w.size, dtype=np.int32)
+        bases = np.zeros(w.size, dtype=np.int32)
+        check(lib().tcb_beam_init(self._h, w.size, w.ctypes.data, ids.ctypes.data,
+                                  bases.ctypes.data, _stream()))
+        return ids, bases
+
+    def step(self, logits: torch.Tensor):
+        if logits.dtype == torch.float32:
+            dt = L.TCB_F32
+        elif logits.dtype == torch.bfloat16:
+            dt = L.TCB_BF16
+        else:
+            raise TypeError("logits must be float32 or bfloat16")
+        if logits.dim() != 2 or logits.stride(1) != 1 or not logits.is_cuda:
+            raise ValueError("logits must be a row-major [max_slots, ld] CUDA tensor")
+        if logits.shape[0] < self.max_slots:
+            raise ValueError("logits must have max_slots rows")
+        check(lib().tcb_beam_step(self._h, _ptr(logits), logits.stride(0), dt, _stream()))
+
+    def step_lmhead(self, hidden: torch.Tensor, weight: torch.Tensor):
+        if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+            raise TypeError("hidden and weight must be bfloat16")
+        if hidden.dim() != 2 or hidden.stride(1) != 1 or hidden.shape[0] < self.max_slots:
+            raise ValueError("hidden must be a row-major [max_slots, ld] CUDA tensor")
+        if not weight.is_contiguous() or weight.shape[0] != self.trie.L or weight.shape[1] != self.trie.V:
+            raise ValueError("weight must be a contiguous [L, V, H] tensor")
+        H = int(weight.shape[2])
+        check(lib().tcb_beam_step_lmhead(self._h, _ptr(hidden), hidden.stride(0), H,
+                                         _ptr(weight), _stream()))
+
+    def export(self):
+        S, R, Lv = self.max_slots, self.max_requests, self.trie.L
+        dev = self.device
+        out = {"node": torch.empty(S, dtype=torch.int32, device=dev),
+               "score": torch.empty(S, dtype=torch.float32, device=dev),
+               "parent_slot": torch.empty(S, dtype=torch.int32, device=dev),
+               "hist": torch.empty((Lv, S), dtype=torch.int32, device=dev),
+               "rows": torch.empty(R, dtype=torch.int32, device=dev),
+               "level": torch.empty(R, dtype=torch.int32, device=dev)}
+        check(lib().tcb_beam_export(self._h, _ptr(out["node"]), _ptr(out["score"]),
+                                    _ptr(out["parent_slot"]), _ptr(out["hist"]),
+                                    _ptr(out["rows"]), _ptr(out["level"]), _stream()))
+        return out
+
+    def set_validate(self, on: bool = True):
+        check(lib().tcb_beams_set_validate(self._h, 1 if on else 0))
+
+    def check(self):
+        check(lib().tcb_beam_check(self._h, _stream()))
+
+    def status(self):
+        st = L.BeamsStatus()
+        check(lib().tcb_beams_status(self._h, C.byref(st)))
+        return {k: int(getattr(st, k)) for k, _ in L.BeamsStatus._fields_}
+
+    def level(self, req_id: int) -> int:
+        v = C.c_int32()
+        check(lib().tcb_request_level(self._h, int(req_id), C.byref(v)))
+        return int(v.value)
+
+    def finalize(self, req_ids):
+        """Ranked beams of finished requests (host arrays); releases their slots."""
+        ids = np.ascontiguousarray(req_ids, dtype=np.int32)
+        n, B, Lv = ids.size, self.max_width, self.trie.L
+        sids = np.zeros((n, B, Lv), dtype=np.uint8)
+        scores = np.zeros((n, B), dtype=np.float32)
+        items = np.zeros((n, B), dtype=np.int64)
+        counts = np.zeros(n, dtype=np.int32)
+        check(lib().tcb_beam_finalize(self._h, n, ids.ctypes.data, sids.ctypes.data,
+                                      scores.ctypes.data, items.ctypes.data, counts.ctypes.data,
+                                      _stream()))
+        return {"sids": sids, "scores": scores, "items": items, "counts": counts}
+
+    def finalize_device(self, req_ids, out=None):
+        """As finalize, into device tensors, without synchronising."""
+        ids = np.ascontiguousarray(req_ids, dtype=np.int32)
+        n, B, Lv = ids.size, self.max_width, self.trie.L
+        if out is None:
+            dev = self.device
+            out = {"sids": torch.empty((n, B, Lv), dtype=torch.uint8, device=dev),
+                   "scores": torch.empty((n, B), dtype=torch.float32, device=dev),
+                   "items": torch.empty((n, B), dtype=torch.int64, device=dev),
+                   "counts": torch.empty(n, dtype=torch.int32, device=dev)}
+        check(lib().tcb_beam_finalize_device(self._h, n, ids.ctypes.data, _ptr(out["sids"]),
+                                             _ptr(out["scores"]), _ptr(out["items"]),
+                                             _ptr(out["counts"]), _stream()))
+        return out

@@ -1,0 +1,473 @@
+// libtcb host ABI: argument validation, workspace carving, slot and request-id
+// allocation, and kernel launches on the caller's stream.
+//
+// Scheduling follows flashrec 0.1.0, Features > Decoding ("Scheduling"): requests are
+// admitted between steps under a beam-row slot budget, and the rows of every admitted
+// request share each step. Requests never compete for survivors.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "tcb_host.h"
+
+namespace tcb_host {
+thread_local std::string g_last_error;
+
+tcb_status set_error(tcb_status code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+}  // namespace tcb_host
+
+using tcb_host::set_error;
+
+namespace {
+
+tcb_status hip_fail(hipError_t e, const char *what) {
+    return set_error(TCB_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+    int32_t MT = 0, CAPT = 0;
+    size_t node[2]{}, score[2]{}, parent_slot = 0, hist = 0, rec = 0;
+    size_t cand = 0, tile_count = 0, tile_thr = 0, err = 0;
+    size_t fin_sids = 0, fin_scores = 0, fin_items = 0, fin_counts = 0, total = 0;
+};
+
+Layout make_layout(int L, int S, int R, int Bmax) {
+    Layout l;
+    l.MT = (Bmax + tcb::kTileRows - 1) / tcb::kTileRows;
+    l.CAPT = std::min(Bmax, tcb::kTileRows * TCB_MAX_V);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    const size_t s = (size_t)S, r = (size_t)R;
+    l.node[0] = take(s * 4);
+    l.node[1] = take(s * 4);
+    l.score[0] = take(s * 4);
+    l.score[1] = take(s * 4);
+    l.parent_slot = take(s * 4);
+    l.hist = take((size_t)L * s * 4);
+    l.rec = take(r * sizeof(tcb::ReqRec));
+    const size_t ncand = r * (size_t)l.MT * (size_t)l.CAPT;
+    l.cand = take(ncand * 16);
+    l.tile_count = take(r * (size_t)l.MT * 4);
+    l.tile_thr = take(r * (size_t)l.MT * 4);
+    l.err = take(256);
+    l.fin_sids = take(r * (size_t)Bmax * (size_t)L);
+    l.fin_scores = take(r * (size_t)Bmax * 4);
+    l.fin_items = take(r * (size_t)Bmax * 8);
+    l.fin_counts = take(r * 4);
+    l.total = o;
+    return l;
+}
+
+int n_req_hw(const tcb_beams *b) {
+    int n = 0;
+    for (int i = 0; i < (int)b->reqs.size(); ++i)
+        if (b->reqs[(size_t)i].used) n = i + 1;
+    return n;
+}
+
+bool take_slots(std::vector<std::pair<int32_t, int32_t>> &fr, int32_t width, int32_t *base) {
+    for (size_t i = 0; i < fr.size(); ++i) {
+        if (fr[i].second >= width) {
+            *base = fr[i].first;
+            fr[i].first += width;
+            fr[i].second -= width;
+            if (fr[i].second == 0) fr.erase(fr.begin() + (long)i);
+            return true;
+        }
+    }
+    return false;
+}
+
+void give_slots(std::vector<std::pair<int32_t, int32_t>> &fr, int32_t base, int32_t width) {
+    auto it = std::lower_bound(fr.begin(), fr.end(), std::make_pair(base, 0));
+    it = fr.insert(it, {base, width});
+    size_t i = (size_t)(it - fr.begin());
+    if (i + 1 < fr.size() && fr[i].first + fr[i].second == fr[i + 1].first) {
+        fr[i].second += fr[i + 1].second;
+        fr.erase(fr.begin() + (long)i + 1);
+    }
+    if (i > 0 && fr[i - 1].first + fr[i - 1].second == fr[i].first) {
+        fr[i - 1].second += fr[i].second;
+        fr.erase(fr.begin() + (long)i);
+    }
+}
+
+tcb_status read_err(tcb_beams *b, hipStream_t s, uint32_t *err) {
+    hipError_t e = hipMemcpyAsync(err, b->w.err, 4, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "read error flags");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    return TCB_OK;
+}
+
+tcb_status err_status(uint32_t err) {
+    if (err & tcb::kErrNonFinite) return set_error(TCB_E_NONFINITE, "a non-finite logit was read");
+    if (err & tcb::kErrBadNode) return set_error(TCB_E_DEVICE, "a row held a node outside its depth");
+    if (err & tcb::kErrInternal) return set_error(TCB_E_DEVICE, "internal invariant violated on device");
+    return TCB_OK;
+}
+
+tcb_status check_finalize_args(tcb_beams *b, int32_t n, const int32_t *req_ids) {
+    if (!b || !req_ids || n <= 0) return set_error(TCB_E_ARG, "finalize: bad arguments");
+    if (n > b->w.R) return set_error(TCB_E_ARG, "finalize: n exceeds max_requests");
+    std::vector<char> seen(b->reqs.size(), 0);
+    for (int i = 0; i < n; ++i) {
+        const int r = req_ids[i];
+        if (r < 0 || r >= (int)b->reqs.size() || !b->reqs[(size_t)r].used)
+            return set_error(TCB_E_ARG, "finalize: unknown request id " + std::to_string(r));
+        if (seen[(size_t)r]) return set_error(TCB_E_ARG, "finalize: request id repeated");
+        seen[(size_t)r] = 1;
+        if (b->reqs[(size_t)r].level < b->L)
+            return set_error(TCB_E_STATE, "finalize: request " + std::to_string(r) + " is at level " +
+                                              std::to_string(b->reqs[(size_t)r].level) + " < L");
+    }
+    return TCB_OK;
+}
+
+tcb_status run_finalize(tcb_beams *b, int32_t n, const int32_t *req_ids, uint8_t *sids,
+                        float *scores, int64_t *items, int32_t *counts, hipStream_t s) {
+    for (int i0 = 0; i0 < n; i0 += tcb::FinBatch::kMax) {
+        tcb::FinBatch fb{};
+        fb.n = std::min(n - i0, tcb::FinBatch::kMax);
+        for (int j = 0; j < fb.n; ++j) {
+            fb.req[j] = req_ids[i0 + j];
+            fb.out_row[j] = i0 + j;
+        }
+        hipError_t e = tcb::launch_finalize(b->tdev, b->w, b->par, fb, sids, scores, items, counts, s);
+        if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    }
+    return TCB_OK;
+}
+
+void release(tcb_beams *b, int32_t n, const int32_t *req_ids) {
+    for (int i = 0; i < n; ++i) {
+        auto &q = b->reqs[(size_t)req_ids[i]];
+        give_slots(b->free_ranges, q.base, q.width);
+        q = tcb_beams::Req{};
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tcb_last_error(void) { return tcb_host::g_last_error.c_str(); }
+
+const char *tcb_version(void) { return "tcb 0.1.0 gfx950"; }
+
+// --------------------------------------------------------------------------- trie
+tcb_status tcb_build_trie(const uint8_t *sids, int64_t n_items, int32_t L, int32_t V,
+                          int32_t mask_depths, tcb_trie **out) {
+    if (n_items >= (int64_t)0x7FFFFFFF) return set_error(TCB_E_ARG, "build_trie: n_items >= 2^31");
+    return tcb_trie_build_impl(sids, n_items, L, V, mask_depths, out);
+}
+
+tcb_status tcb_trie_info(const tcb_trie *t, tcb_trie_info_t *out) {
+    if (!t || !out) return set_error(TCB_E_ARG, "trie_info: null pointer");
+    std::memset(out, 0, sizeof(*out));
+    out->L = t->L;
+    out->V = t->V;
+    out->mask_depths = t->mask_depths;
+    out->n_items = t->n_items;
+    out->n_distinct = t->n_distinct;
+    for (int d = 0; d <= t->L; ++d) out->nodes_per_depth[d] = t->nodes_per_depth[(size_t)d];
+    for (int d = 0; d <= t->L + 1; ++d) out->node_offset[d] = t->off[(size_t)d];
+    out->device_bytes = t->image_bytes;
+    return TCB_OK;
+}
+
+tcb_status tcb_trie_host_arrays(const tcb_trie *t, const uint32_t **child_begin,
+                                const uint8_t **child_code, const int32_t **leaf_item) {
+    if (!t) return set_error(TCB_E_ARG, "trie_host_arrays: null trie");
+    if (child_begin) *child_begin = t->child_begin.data();
+    if (child_code) *child_code = t->child_code.data();
+    if (leaf_item) *leaf_item = t->leaf_item.data();
+    return TCB_OK;
+}
+
+tcb_status tcb_trie_upload(tcb_trie *t, void *d_buf, size_t bytes, void *stream) {
+    if (!t || !d_buf) return set_error(TCB_E_ARG, "trie_upload: null pointer");
+    if (bytes < t->image_bytes) return set_error(TCB_E_WORKSPACE, "trie_upload: buffer too small");
+    if (((uintptr_t)d_buf & 255) != 0) return set_error(TCB_E_WORKSPACE, "trie_upload: buffer not 256-byte aligned");
+    hipError_t e = hipMemcpyAsync(d_buf, t->image.data(), t->image_bytes, hipMemcpyHostToDevice,
+                                  (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "trie_upload copy");
+    t->d_image = d_buf;
+    return TCB_OK;
+}
+
+void tcb_trie_destroy(tcb_trie *t) { delete t; }
+
+// --------------------------------------------------------------------------- wave
+tcb_status tcb_beams_workspace_bytes(const tcb_trie *t, int32_t max_slots, int32_t max_requests,
+                                     int32_t max_width, size_t *bytes) {
+    if (!t || !bytes) return set_error(TCB_E_ARG, "workspace_bytes: null pointer");
+    if (max_slots <= 0 || max_requests <= 0 || max_width <= 0 || max_width > TCB_MAX_WIDTH)
+        return set_error(TCB_E_ARG, "workspace_bytes: sizes out of range");
+    if (max_slots >= (1 << 24)) return set_error(TCB_E_ARG, "workspace_bytes: max_slots >= 2^24");
+    *bytes = make_layout(t->L, max_slots, max_requests, max_width).total;
+    return TCB_OK;
+}
+
+tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_requests,
+                            int32_t max_width, int32_t norm, void *d_ws, size_t ws_bytes,
+                            void *stream, tcb_beams **out) {
+    if (!t || !d_ws || !out) return set_error(TCB_E_ARG, "beams_create: null pointer");
+    if (!t->d_image) return set_error(TCB_E_STATE, "beams_create: trie not uploaded");
+    if (norm != TCB_NORM_CHILDREN && norm != TCB_NORM_LEVEL)
+        return set_error(TCB_E_ARG, "beams_create: bad norm");
+    size_t need = 0;
+    tcb_status st = tcb_beams_workspace_bytes(t, max_slots, max_requests, max_width, &need);
+    if (st) return st;
+    if (ws_bytes < need) return set_error(TCB_E_WORKSPACE, "beams_create: workspace too small");
+    if (((uintptr_t)d_ws & 255) != 0) return set_error(TCB_E_WORKSPACE, "beams_create: workspace not 256-byte aligned");
+    *out = nullptr;
+    tcb_beams *b = new (std::nothrow) tcb_beams();
+    if (!b) return set_error(TCB_E_ARG, "beams_create: out of host memory");
+    b->L = t->L;
+    b->V = t->V;
+    const uint8_t *img = (const uint8_t *)t->d_image;
+    b->tdev.child_begin = (const uint32_t *)(img + t->o_child_begin);
+    b->tdev.child_code = img + t->o_child_code;
+    b->tdev.leaf_item = (const int32_t *)(img + t->o_leaf);
+    b->tdev.mask = (const uint32_t *)(img + t->o_mask);
+    b->tdev.L = t->L;
+    b->tdev.V = t->V;
+    b->tdev.mask_depths = t->mask_depths;
+    for (int d = 0; d <= t->L + 1; ++d) b->tdev.off[d] = (uint32_t)t->off[(size_t)d];
+
+    const Layout l = make_layout(t->L, max_slots, max_requests, max_width);
+    uint8_t *ws = (uint8_t *)d_ws;
+    auto &w = b->w;
+    for (int p = 0; p < 2; ++p) {
+        w.node[p] = (int32_t *)(ws + l.node[p]);
+        w.score[p] = (float *)(ws + l.score[p]);
+    }
+    w.parent_slot = (int32_t *)(ws + l.parent_slot);
+    w.hist = (uint32_t *)(ws + l.hist);
+    w.rec = (tcb::ReqRec *)(ws + l.rec);
+    w.cand = (void *)(ws + l.cand);
+    w.tile_count = (int32_t *)(ws + l.tile_count);
+    w.tile_thr = (uint32_t *)(ws + l.tile_thr);
+    w.err = (uint32_t *)(ws + l.err);
+    w.S = max_slots;
+    w.R = max_requests;
+    w.MT = l.MT;
+    w.CAPT = l.CAPT;
+    w.Bmax = max_width;
+    w.norm = norm;
+    w.validate = 0;
+    b->d_fin_sids = ws + l.fin_sids;
+    b->d_fin_scores = (float *)(ws + l.fin_scores);
+    b->d_fin_items = (int64_t *)(ws + l.fin_items);
+    b->d_fin_counts = (int32_t *)(ws + l.fin_counts);
+    b->reqs.assign((size_t)max_requests, tcb_beams::Req{});
+    b->free_ranges.push_back({0, max_slots});
+    hipError_t e = tcb::launch_clear_wave(w, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        delete b;
+        return hip_fail(e, "beams_create clear");
+    }
+    *out = b;
+    return TCB_OK;
+}
+
+tcb_status tcb_beam_init(tcb_beams *b, int32_t n, const int32_t *widths, int32_t *out_req_ids,
+                         int32_t *out_slot_base, void *stream) {
+    if (!b || !widths || n <= 0) return set_error(TCB_E_ARG, "beam_init: bad arguments");
+    for (int i = 0; i < n; ++i)
+        if (widths[i] < 1 || widths[i] > b->w.Bmax)
+            return set_error(TCB_E_ARG, "beam_init: width " + std::to_string(widths[i]) +
+                                            " outside 1..max_width");
+    // all-or-nothing: plan on copies, commit only if everything fits
+    auto fr = b->free_ranges;
+    std::vector<int32_t> ids, bases;
+    int next = 0;
+    for (int i = 0; i < n; ++i) {
+        while (next < (int)b->reqs.size() && b->reqs[(size_t)next].used) ++next;
+        if (next >= (int)b->reqs.size())
+            return set_error(TCB_E_BUDGET, "beam_init: no free request id");
+        int32_t base = 0;
+        if (!take_slots(fr, widths[i], &base))
+            return set_error(TCB_E_BUDGET, "beam_init: slot budget exhausted");
+        ids.push_back(next);
+        bases.push_back(base);
+        ++next;
+    }
+    for (int i0 = 0; i0 < n; i0 += tcb::InitBatch::kMax) {
+        tcb::InitBatch ib{};
+        ib.n = std::min(n - i0, tcb::InitBatch::kMax);
+        for (int j = 0; j < ib.n; ++j) {
+            ib.req[j] = ids[(size_t)(i0 + j)];
+            ib.base[j] = bases[(size_t)(i0 + j)];
+            ib.width[j] = widths[i0 + j];
+        }
+        hipError_t e = tcb::launch_init(b->w, b->par, ib, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "beam_init launch");
+    }
+    b->free_ranges = fr;
+    for (int i = 0; i < n; ++i) {
+        auto &q = b->reqs[(size_t)ids[(size_t)i]];
+        q.used = true;
+        q.base = bases[(size_t)i];
+        q.width = widths[i];
+        q.level = 0;
+        if (out_req_ids) out_req_ids[i] = ids[(size_t)i];
+        if (out_slot_base) out_slot_base[i] = bases[(size_t)i];
+    }
+    return TCB_OK;
+}
+
+static tcb_status step_common(tcb_beams *b) {
+    for (const auto &q : b->reqs)
+        if (q.used && q.level < b->L) return TCB_OK;
+    return set_error(TCB_E_STATE, "beam_step: no admitted request is unfinished");
+}
+
+static void step_done(tcb_beams *b) {
+    b->par ^= 1;
+    b->steps++;
+    for (auto &q : b->reqs)
+        if (q.used && q.level < b->L) q.level++;
+}
+
+tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t dtype, void *stream) {
+    if (!b || !d_logits) return set_error(TCB_E_ARG, "beam_step: null pointer");
+    if (dtype != TCB_F32 && dtype != TCB_BF16) return set_error(TCB_E_ARG, "beam_step: bad dtype");
+    if (ld < b->V) return set_error(TCB_E_ARG, "beam_step: ld < V");
+    tcb_status st = step_common(b);
+    if (st) return st;
+    const int nr = n_req_hw(b);
+    hipError_t e = tcb::launch_expand(b->tdev, b->w, b->par, nr, d_logits, ld, dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "expand launch");
+    e = tcb::launch_merge(b->tdev, b->w, b->par, nr, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    step_done(b);
+    return TCB_OK;
+}
+
+tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_hidden, int32_t H,
+                                const void *d_weight, void *stream) {
+    if (!b || !d_hidden || !d_weight) return set_error(TCB_E_ARG, "beam_step_lmhead: null pointer");
+    if (H <= 0 || H % 64 != 0) return set_error(TCB_E_ARG, "beam_step_lmhead: H must be a positive multiple of 64");
+    if (ld_hidden < H) return set_error(TCB_E_ARG, "beam_step_lmhead: ld_hidden < H");
+    if (((uintptr_t)d_hidden & 15) || ((uintptr_t)d_weight & 15) || (ld_hidden % 8))
+        return set_error(TCB_E_ARG, "beam_step_lmhead: hidden/weight must be 16-byte aligned, ld % 8 == 0");
+    tcb_status st = step_common(b);
+    if (st) return st;
+    const int nr = n_req_hw(b);
+    hipError_t e = tcb::launch_expand_lmhead(b->tdev, b->w, b->par, nr, d_hidden, ld_hidden, H,
+                                             d_weight, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "expand_lmhead launch");
+    e = tcb::launch_merge(b->tdev, b->w, b->par, nr, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    step_done(b);
+    return TCB_OK;
+}
+
+tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, int32_t *d_parent_slot,
+                           uint32_t *d_hist, int32_t *d_rows, int32_t *d_level, void *stream) {
+    if (!b) return set_error(TCB_E_ARG, "beam_export: null wave");
+    hipStream_t s = (hipStream_t)stream;
+    const size_t S = (size_t)b->w.S;
+    hipError_t e = hipSuccess;
+    if (d_node && e == hipSuccess)
+        e = hipMemcpyAsync(d_node, b->w.node[b->par], S * 4, hipMemcpyDeviceToDevice, s);
+    if (d_score && e == hipSuccess)
+        e = hipMemcpyAsync(d_score, b->w.score[b->par], S * 4, hipMemcpyDeviceToDevice, s);
+    if (d_parent_slot && e == hipSuccess)
+        e = hipMemcpyAsync(d_parent_slot, b->w.parent_slot, S * 4, hipMemcpyDeviceToDevice, s);
+    if (d_hist && e == hipSuccess)
+        e = hipMemcpyAsync(d_hist, b->w.hist, (size_t)b->L * S * 4, hipMemcpyDeviceToDevice, s);
+    if ((d_rows || d_level) && e == hipSuccess) e = tcb::launch_export_req(b->w, d_rows, d_level, s);
+    if (e != hipSuccess) return hip_fail(e, "beam_export");
+    return TCB_OK;
+}
+
+tcb_status tcb_beams_status(const tcb_beams *b, tcb_beams_status_t *out) {
+    if (!b || !out) return set_error(TCB_E_ARG, "beams_status: null pointer");
+    std::memset(out, 0, sizeof(*out));
+    out->steps = b->steps;
+    for (const auto &q : b->reqs) {
+        if (!q.used) {
+            out->free_requests++;
+            continue;
+        }
+        if (q.level < b->L) out->active++;
+        else out->finished++;
+    }
+    for (const auto &r : b->free_ranges) out->free_slots += r.second;
+    return TCB_OK;
+}
+
+tcb_status tcb_request_level(const tcb_beams *b, int32_t req_id, int32_t *level) {
+    if (!b || !level) return set_error(TCB_E_ARG, "request_level: null pointer");
+    if (req_id < 0 || req_id >= (int)b->reqs.size() || !b->reqs[(size_t)req_id].used)
+        return set_error(TCB_E_ARG, "request_level: unknown request id");
+    *level = b->reqs[(size_t)req_id].level;
+    return TCB_OK;
+}
+
+tcb_status tcb_beams_set_validate(tcb_beams *b, int32_t on) {
+    if (!b) return set_error(TCB_E_ARG, "set_validate: null wave");
+    b->w.validate = on ? 1 : 0;
+    return TCB_OK;
+}
+
+tcb_status tcb_beam_check(tcb_beams *b, void *stream) {
+    if (!b) return set_error(TCB_E_ARG, "beam_check: null wave");
+    uint32_t err = 0;
+    tcb_status st = read_err(b, (hipStream_t)stream, &err);
+    if (st) return st;
+    return err_status(err);
+}
+
+tcb_status tcb_beam_finalize(tcb_beams *b, int32_t n, const int32_t *req_ids, uint8_t *h_sids,
+                             float *h_scores, int64_t *h_items, int32_t *h_counts, void *stream) {
+    tcb_status st = check_finalize_args(b, n, req_ids);
+    if (st) return st;
+    if (!h_sids || !h_scores || !h_items || !h_counts)
+        return set_error(TCB_E_ARG, "finalize: null output pointer");
+    hipStream_t s = (hipStream_t)stream;
+    st = run_finalize(b, n, req_ids, b->d_fin_sids, b->d_fin_scores, b->d_fin_items, b->d_fin_counts, s);
+    if (st) return st;
+    const size_t rowsz = (size_t)b->w.Bmax;
+    hipError_t e = hipMemcpyAsync(h_sids, b->d_fin_sids, (size_t)n * rowsz * (size_t)b->L, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h_scores, b->d_fin_scores, (size_t)n * rowsz * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h_items, b->d_fin_items, (size_t)n * rowsz * 8, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h_counts, b->d_fin_counts, (size_t)n * 4, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "finalize copy");
+    uint32_t err = 0;
+    st = read_err(b, s, &err);
+    if (st) return st;
+    release(b, n, req_ids);
+    return err_status(err);
+}
+
+tcb_status tcb_beam_finalize_device(tcb_beams *b, int32_t n, const int32_t *req_ids, uint8_t *d_sids,
+                                    float *d_scores, int64_t *d_items, int32_t *d_counts, void *stream) {
+    tcb_status st = check_finalize_args(b, n, req_ids);
+    if (st) return st;
+    if (!d_sids || !d_scores || !d_items || !d_counts)
+        return set_error(TCB_E_ARG, "finalize_device: null output pointer");
+    st = run_finalize(b, n, req_ids, d_sids, d_scores, d_items, d_counts, (hipStream_t)stream);
+    if (st) return st;
+    release(b, n, req_ids);
+    return TCB_OK;
+}
+
+void tcb_beams_destroy(tcb_beams *b) { delete b; }
+
+}  // extern "C"

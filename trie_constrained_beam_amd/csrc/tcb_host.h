@@ -1,0 +1,48 @@
+// Host-side object layouts of libtcb.
+#pragma once
+
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "tcb_internal.h"
+
+struct tcb_trie {
+    int32_t L = 0, V = 0, mask_depths = 0;
+    int64_t n_items = 0, n_distinct = 0;
+    std::vector<int64_t> nodes_per_depth;  // [L+1]
+    std::vector<int64_t> off;              // [L+2]
+    std::vector<uint32_t> child_begin;     // [off[L] + 1]
+    std::vector<uint8_t> child_code;       // [total nodes]
+    std::vector<int32_t> leaf_item;        // [n_distinct]
+    std::vector<uint32_t> mask;            // [off[mask_depths] * 8]
+    std::vector<uint8_t> image;            // device image, uploaded as one copy
+    size_t o_child_begin = 0, o_child_code = 0, o_leaf = 0, o_mask = 0, image_bytes = 0;
+    void *d_image = nullptr;               // caller-owned, set by tcb_trie_upload
+};
+
+struct tcb_beams {
+    struct Req {
+        bool used = false;
+        int32_t base = 0, width = 0, level = 0;
+    };
+    tcb::TrieDev tdev{};
+    tcb::WaveDev w{};
+    int32_t L = 0, V = 0;
+    int par = 0;
+    int64_t steps = 0;
+    std::vector<Req> reqs;
+    std::vector<std::pair<int32_t, int32_t>> free_ranges;  // (start, length), sorted
+    // finalize staging inside the workspace
+    uint8_t *d_fin_sids = nullptr;
+    float *d_fin_scores = nullptr;
+    int64_t *d_fin_items = nullptr;
+    int32_t *d_fin_counts = nullptr;
+};
+
+namespace tcb_host {
+tcb_status set_error(tcb_status code, const std::string &msg);
+}
+
+tcb_status tcb_trie_build_impl(const uint8_t *sids, int64_t n_items, int32_t L, int32_t V,
+                               int32_t mask_depths, tcb_trie **out);
