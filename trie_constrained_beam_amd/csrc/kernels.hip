@@ -14,13 +14,16 @@
 //           (fp32) or 512 B (bf16) load. The row's child set is a 256-bit mask, read
 //           from the dense per-node mask at shallow depths or built in wave-private LDS
 //           from the CSR child list deeper down; both give bit-identical results.
-//           The masked log-softmax is two wave reductions. The tile then keeps its own
-//           best n candidates (exact, by histogram refinement) and records the n-th
-//           score, so the merge can discard what no tile-local top-n contains.
-//   merge   one workgroup per request: prunes against the largest tile threshold,
-//           stages the rest in LDS, finds the exact n-th candidate, orders the
-//           survivors by bucketing plus exact in-bucket ranking, and writes the new
-//           rows (parent-gather / trie-advance) plus the per-level back-pointers.
+//           The masked log-softmax is two wave reductions. Candidates are counted in
+//           request-wide score bins (distance below the request's best row score,
+//           which no candidate can exceed); the tile keeps the bins down to the one
+//           holding its own n-th best, a superset of its top-n, and writes the bin
+//           counts of what it kept.
+//   merge   one workgroup per request: sums the tiles' bin counts to find the bin
+//           b* of the request's n-th candidate before reading any candidate, stages
+//           only bins <= b* in LDS grouped by bin, ranks each by counting the better
+//           members of its bin, and writes the new rows (parent-gather / trie-advance)
+//           plus the per-level back-pointers.
 // All selection keys are unique (flat index breaks ties) and all float reductions
 // have a fixed order, so results are deterministic run to run.
 #include "tcb_internal.h"
@@ -319,40 +322,23 @@ __device__ __forceinline__ void load_row(const void *logits, int64_t ld, int slo
     }
 }
 
-// Child set of node n as a 256-bit mask (8 wave-uniform words) plus the first child id.
-// Returns false if n is not a node of depth `level` (corrupt state).
-__device__ __forceinline__ bool row_children(const TrieDev &T, uint32_t n, int level, int lane,
-                                             uint32_t *wmask, uint32_t m[8], uint32_t &cb) {
-    if (n < T.off[level] || n >= T.off[level + 1]) return false;
-    cb = T.child_begin[n];
-    if (level < T.mask_depths) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) m[w] = T.mask[(size_t)n * 8 + w];
-    } else {
-        const uint32_t ce = T.child_begin[n + 1];
-        if (lane < 8) wmask[lane] = 0u;
-        wave_lds_sync();
-        for (uint32_t p = cb + lane; p < ce; p += 64) {
-            const uint32_t c = T.child_code[p];
-            atomicOr(&wmask[c >> 5], 1u << (c & 31));
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int w = 0; w < 8; ++w) m[w] = __builtin_amdgcn_readfirstlane(wmask[w]);
-        wave_lds_sync();
-    }
-    return true;
-}
-
 // ---------------------------------------------------------------------- expand
 // Per-thread candidate store: kRowsPerWave rows x 4 codes.
 constexpr int kE = kRowsPerWave * 4;
 
+__device__ __forceinline__ uint32_t score_bin(float sref, float s) {
+    const float d = (sref - s) * kHistRes;
+    return d < (float)(kHistBins - 1) ? (uint32_t)d : (uint32_t)(kHistBins - 1);
+}
+
 template <int DT, int NORM, bool VEC>
 __global__ __launch_bounds__(kExpandThreads) void k_expand(TrieDev T, WaveDev W, int par,
                                                            const void *__restrict__ logits, int64_t ld) {
-    __shared__ uint32_t s_wmask[kTileWaves][8];
+    static_assert(kExpandThreads == kHistBins, "one histogram bin per thread");
+    __shared__ uint32_t s_wmask[kTileWaves][kRowsPerWave][8];
+    __shared__ uint32_t s_hist[kHistBins];
     __shared__ SelSmem S;
+    __shared__ uint32_t s_bstar;
 
     const int req = blockIdx.x / W.MT;
     const int lt = blockIdx.x - req * W.MT;
@@ -361,58 +347,114 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand(TrieDev T, WaveDev W,
     const int r0 = lt * kTileRows;
     if (r0 >= rec.rows) return;
     const int level = rec.level;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int V = T.V;
+    const float sref = W.score[par][rec.base];      // best row of the request (rank order)
+    s_hist[tid] = 0u;
+    if (tid == 0) s_bstar = kHistBins - 1;
 
-    // issue every row's state and logits loads first
+    // 1. state and logits of this wave's rows, all issued before any use
     int rr[kRowsPerWave];
+    bool live[kRowsPerWave];
     int32_t nd[kRowsPerWave];
     float sr[kRowsPerWave];
     float x[kRowsPerWave][4];
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j) {
         rr[j] = r0 + j * kTileWaves + wave;
+        live[j] = rr[j] < rec.rows;
         nd[j] = -1;
         sr[j] = 0.0f;
         x[j][0] = x[j][1] = x[j][2] = x[j][3] = 0.0f;
-        if (rr[j] < rec.rows) {
+        if (live[j]) {
             const int slot = rec.base + rr[j];
             nd[j] = W.node[par][slot];
             sr[j] = W.score[par][slot];
             load_row<DT, VEC>(logits, ld, slot, lane, V, x[j]);
         }
     }
+    // 2. trie: child range (and the dense child mask at shallow depths) of every row
+    const bool dense = level < T.mask_depths;
+    const uint32_t lo_id = T.off[level], hi_id = T.off[level + 1];
+    bool ok[kRowsPerWave];
+    uint32_t cb[kRowsPerWave], ce[kRowsPerWave], m[kRowsPerWave][8];
+    bool bad_node = false;
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+        ok[j] = false;
+        cb[j] = ce[j] = 0u;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) m[j][w] = 0u;
+        if (!live[j]) continue;                                   // wave-uniform
+        const uint32_t n = (uint32_t)__builtin_amdgcn_readfirstlane(nd[j]);
+        if (n < lo_id || n >= hi_id) {
+            bad_node = true;
+            continue;
+        }
+        ok[j] = true;
+        cb[j] = T.child_begin[n];
+        if (dense) {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) m[j][w] = T.mask[(size_t)n * 8 + w];
+        } else {
+            ce[j] = T.child_begin[n + 1];
+        }
+    }
+    if (bad_node && lane == 0) atomicOr(W.err, kErrBadNode);
+    // 3. deeper down: each row's CSR child list becomes a mask in wave-private LDS
+    if (!dense) {
+        uint32_t cc[kRowsPerWave][4];
+#pragma unroll
+        for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t p = cb[j] + (uint32_t)(lane + 64 * q);
+                cc[j][q] = (ok[j] && p < ce[j]) ? (uint32_t)T.child_code[p] : 0xffffffffu;
+            }
+        if (lane < 8) {
+#pragma unroll
+            for (int j = 0; j < kRowsPerWave; ++j) s_wmask[wave][j][lane] = 0u;
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (cc[j][q] != 0xffffffffu) atomicOr(&s_wmask[wave][j][cc[j][q] >> 5], 1u << (cc[j][q] & 31));
+        wave_lds_sync();
+#pragma unroll
+        for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) m[j][w] = __builtin_amdgcn_readfirstlane(s_wmask[wave][j][w]);
+    }
 
-    uint32_t co[kE];     // order keys of this lane's candidates
+    // 4. masked log-softmax and the candidates of this lane's 4 codes of each row
+    uint32_t co[kE];     // order keys
     int32_t cn[kE];      // child node ids
     uint32_t valid = 0u;
     bool bad_value = false;
+    const int wl = lane >> 3, sh = (lane & 7) * 4;   // this lane's codes: word wl, bits sh..sh+3
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j) {
-        if (rr[j] >= rec.rows) continue;                       // wave-uniform
-        const uint32_t n = (uint32_t)__builtin_amdgcn_readfirstlane(nd[j]);
-        uint32_t m[8], cb = 0;
-        if (!row_children(T, n, level, lane, s_wmask[wave], m, cb)) {
-            if (lane == 0) atomicOr(W.err, kErrBadNode);
-            continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            co[j * 4 + q] = 0u;
+            cn[j * 4 + q] = 0;
         }
-        // this lane's 4 codes: word lane>>3, bits (lane&7)*4 .. +3
-        const int wl = lane >> 3, sh = (lane & 7) * 4;
+        if (!ok[j]) continue;                                     // wave-uniform
         uint32_t below = 0u, word = 0u;
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
-            below += (w < wl) ? (uint32_t)__popc(m[w]) : 0u;
-            word = (w == wl) ? m[w] : word;
+            below += (w < wl) ? (uint32_t)__popc(m[j][w]) : 0u;
+            word = (w == wl) ? m[j][w] : word;
         }
         const uint32_t bits4 = (word >> sh) & 0xFu;
         const uint32_t rank0 = below + (uint32_t)__popc(word & ((1u << sh) - 1u));
-
         if (W.validate) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 if (4 * lane + q < V && !isfinite(x[j][q])) bad_value = true;
         }
-        // masked log-softmax: max and sum over the support, fixed reduction order
         float mx = -INFINITY;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -431,9 +473,8 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand(TrieDev T, WaveDev W,
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int e = j * 4 + q;
-            const float cand = sr[j] + (x[j][q] - lse);
-            co[e] = f2ord(cand);
-            cn[e] = (int32_t)(cb + rank0 + (uint32_t)__popc(bits4 & ((1u << q) - 1u)));
+            co[e] = f2ord(sr[j] + (x[j][q] - lse));
+            cn[e] = (int32_t)(cb[j] + rank0 + (uint32_t)__popc(bits4 & ((1u << q) - 1u)));
             valid |= ((bits4 >> q) & 1u) << e;
         }
     }
@@ -442,31 +483,66 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand(TrieDev T, WaveDev W,
     auto flat_of = [&](int e) -> uint32_t {
         return (uint32_t)rr[e >> 2] * 256u + (uint32_t)(4 * lane + (e & 3));
     };
-    auto each = [&](auto fn) {
-#pragma unroll
-        for (int e = 0; e < kE; ++e)
-            if ((valid >> e) & 1u) fn(co[e], flat_of(e));
-    };
 
-    int total;
-    block_excl_scan<kExpandThreads>(__popc(valid), S.part, &total);
+    // 5. histogram of the tile's candidates over the request-wide score bins
+    __syncthreads();
+    {
+        uint32_t over = 0u;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            if ((valid >> e) & 1u) {
+                const uint32_t b = score_bin(sref, ord2f(co[e]));
+                if (b < (uint32_t)(kHistBins - 1)) atomicAdd(&s_hist[b], 1u);
+                else ++over;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) over += (uint32_t)__shfl_xor((int)over, o, 64);
+        if (lane == 0 && over) atomicAdd(&s_hist[kHistBins - 1], over);
+    }
+    __syncthreads();
+    // 6. boundary bin of the tile: where the count from the best bin reaches n_i
     const uint32_t width = (uint32_t)rec.width;
-    uint32_t thr = 0u;
-    if ((uint32_t)total > width) {
+    const uint32_t h = s_hist[tid];
+    int total;
+    const int before = block_excl_scan<kExpandThreads>((int)h, S.part, &total);
+    if ((uint32_t)total > width && (uint32_t)before < width && width <= (uint32_t)before + h) s_bstar = (uint32_t)tid;
+    __syncthreads();
+    const uint32_t bstar = s_bstar;
+    uint32_t keep = 0u;
+#pragma unroll
+    for (int e = 0; e < kE; ++e)
+        if (((valid >> e) & 1u) && score_bin(sref, ord2f(co[e])) <= bstar) keep |= 1u << e;
+    int kept;
+    int off = block_excl_scan<kExpandThreads>(__popc(keep), S.part, &kept);
+    const bool exact = kept > W.CAPT;
+    if (exact) {
+        // the boundary bin is too full (e.g. many exact ties): keep exactly the tile's top n_i
+        auto each = [&](auto fn) {
+#pragma unroll
+            for (int e = 0; e < kE; ++e)
+                if ((valid >> e) & 1u) fn(co[e], flat_of(e));
+        };
         uint32_t o_star, f_star;
         block_select<kExpandThreads>(each, width, S, o_star, f_star, W.err);
+        keep = 0u;
 #pragma unroll
         for (int e = 0; e < kE; ++e)
-            if (!key_le(co[e], flat_of(e), o_star, f_star)) valid &= ~(1u << e);
-        thr = o_star;
+            if (((valid >> e) & 1u) && key_le(co[e], flat_of(e), o_star, f_star)) keep |= 1u << e;
+        off = block_excl_scan<kExpandThreads>(__popc(keep), S.part, &kept);
+        s_hist[tid] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+            if ((keep >> e) & 1u) atomicAdd(&s_hist[score_bin(sref, ord2f(co[e]))], 1u);
+        __syncthreads();
     }
-    const int mine = __popc(valid);
-    const int off = block_excl_scan<kExpandThreads>(mine, S.part, &total);
+    // 7. emit the kept candidates and their bin counts
     Cand *out = reinterpret_cast<Cand *>(W.cand) + ((size_t)req * W.MT + lt) * W.CAPT;
     int i = off;
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
-        if ((valid >> e) & 1u) {
+        if ((keep >> e) & 1u) {
             Cand c;
             c.score = ord2f(co[e]);
             c.flat = flat_of(e);
@@ -475,25 +551,28 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand(TrieDev T, WaveDev W,
             out[i++] = c;
         }
     }
-    if (threadIdx.x == 0) {
-        W.tile_count[req * W.MT + lt] = total;
-        W.tile_thr[req * W.MT + lt] = thr;
-    }
+    const uint32_t hk = exact ? s_hist[tid] : ((uint32_t)tid <= bstar ? h : 0u);
+    W.tile_hist[((size_t)req * W.MT + lt) * kHistBins + tid] = (uint16_t)hk;
+    if (tid == 0) W.tile_count[req * W.MT + lt] = kept;
 }
 
 // ---------------------------------------------------------------------- merge
+// One workgroup per request. The tiles' bin counts give the request's boundary bin
+// b* before any candidate is read; only candidates in bins <= b* are staged, already
+// grouped by bin, and each finds its rank by counting the better members of its bin.
 struct MergeSmem {
     float s[kMergeCap];
     uint32_t f[kMergeCap];
     int32_t node[kMergeCap];
-    uint32_t order[TCB_MAX_WIDTH];
-    uint32_t bin_cnt[kSortBins];
-    uint32_t bin_start[kSortBins];
-    uint32_t bin_cur[kSortBins];
+    uint32_t ghist[kHistBins];
+    uint32_t gstart[kHistBins];
+    uint32_t cursor[kHistBins];
     int32_t tcnt[kMaxTilesPerReq];
     SelSmem sel;
-    uint32_t thr, n, n_all, omax;
+    uint32_t bstar, n, o_star, f_star;
 };
+
+constexpr int kBigBin = 1024;   // boundary bins larger than this use the exact selection
 
 __global__ __launch_bounds__(kMergeThreads) void k_merge(TrieDev T, WaveDev W, int par) {
     __shared__ MergeSmem M;
@@ -511,191 +590,145 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(TrieDev T, WaveDev W, i
         return;
     }
     const int ntile = (rec.rows + kTileRows - 1) / kTileRows;
-    if (t == 0) {
-        M.thr = 0u;
-        M.n = 0u;
-        M.n_all = 0u;
-        M.omax = 0u;
-    }
-    for (int i = t; i < kSortBins; i += NT) {
-        M.bin_cnt[i] = 0u;
-        M.bin_cur[i] = 0u;
-    }
-    __syncthreads();
-    for (int i = t; i < ntile; i += NT) {
-        const int c = W.tile_count[req * W.MT + i];
-        M.tcnt[i] = c;
-        atomicAdd(&M.n_all, (uint32_t)c);
-        atomicMax(&M.thr, W.tile_thr[req * W.MT + i]);
-    }
-    __syncthreads();
-    const uint32_t thr = M.thr;
-    const uint32_t n_all = M.n_all;
-    const uint32_t k = min((uint32_t)rec.width, n_all);
-    const Cand *cand = reinterpret_cast<const Cand *>(W.cand) + (size_t)req * W.MT * W.CAPT;
+    const float sref = W.score[par][rec.base];
     const int CAPT = W.CAPT;
+    const Cand *cand = reinterpret_cast<const Cand *>(W.cand) + (size_t)req * W.MT * CAPT;
+    const uint16_t *th = W.tile_hist + (size_t)req * W.MT * kHistBins;
 
-    // stage candidates at or above the largest tile threshold (wave-aggregated append)
-    constexpr int U = 8;
-    for (int tb = 0; tb < ntile; tb += U) {
-        for (int i0 = 0; i0 < CAPT; i0 += NT) {
-            Cand c[U];
-            bool ok[U];
+    // request-wide bin counts = sum of the tiles' counts
+    uint32_t h = 0u;
+    if (t < kHistBins) {
+        M.cursor[t] = 0u;
+        int tile = 0;
+        for (; tile + 4 <= ntile; tile += 4) {
+            const uint32_t a = th[(size_t)(tile + 0) * kHistBins + t];
+            const uint32_t b = th[(size_t)(tile + 1) * kHistBins + t];
+            const uint32_t c = th[(size_t)(tile + 2) * kHistBins + t];
+            const uint32_t d = th[(size_t)(tile + 3) * kHistBins + t];
+            h += a + b + c + d;
+        }
+        for (; tile < ntile; ++tile) h += th[(size_t)tile * kHistBins + t];
+        M.ghist[t] = h;
+    }
+    if (t < ntile) M.tcnt[t] = W.tile_count[req * W.MT + t];
+    if (t == 0) {
+        M.bstar = kHistBins - 1;
+        M.n = 0u;
+    }
+    int total;
+    const int before = block_excl_scan<NT>((int)h, M.sel.part, &total);
+    const uint32_t k = min((uint32_t)rec.width, (uint32_t)total);
+    if (t < kHistBins) {
+        M.gstart[t] = (uint32_t)before;
+        if ((uint32_t)before < k && k <= (uint32_t)before + h) M.bstar = (uint32_t)t;
+    }
+    __syncthreads();
+    const uint32_t bstar = M.bstar;
+    const uint32_t cbefore = M.gstart[bstar], cnt_b = M.ghist[bstar];
+    const uint32_t staged = cbefore + cnt_b;
+    const uint32_t need = k - cbefore;          // members of b* that survive
+    const int S = W.S;
+    const int level = rec.level;
+
+    auto write_row = [&](uint32_t rank, float score, uint32_t flat, int32_t node) {
+        const int slot = rec.base + (int)rank;
+        W.node[nxt][slot] = node;
+        W.score[nxt][slot] = score;
+        W.parent_slot[slot] = rec.base + (int)(flat >> 8);
+        W.hist[(size_t)level * S + slot] = flat;               // (r << 8) | c
+    };
+
+    if (staged <= (uint32_t)kMergeCap) {
+        // stage bins <= b*, grouped by bin
+        constexpr int U = 8;
+        for (int tb = 0; tb < ntile; tb += U) {
+            for (int i0 = 0; i0 < CAPT; i0 += NT) {
+                Cand c[U];
+                bool okc[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int tile = tb + u;
-                const int i = i0 + t;
-                ok[u] = tile < ntile && i < M.tcnt[tile < ntile ? tile : 0];
-                if (ok[u]) c[u] = cand[(size_t)tile * CAPT + i];
-            }
+                for (int u = 0; u < U; ++u) {
+                    const int tile = tb + u, i = i0 + t;
+                    okc[u] = tile < ntile && i < M.tcnt[tile < ntile ? tile : 0];
+                    if (okc[u]) c[u] = cand[(size_t)tile * CAPT + i];
+                }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const bool pass = ok[u] && f2ord(c[u].score) >= thr;
-                const uint64_t bal = __ballot(pass);
-                uint32_t wbase = 0;
-                if ((t & 63) == 0 && bal) wbase = atomicAdd(&M.n, (uint32_t)__popcll(bal));
-                wbase = __shfl(wbase, 0, 64);
-                if (pass) {
-                    const uint32_t p = wbase + (uint32_t)__popcll(bal & ((1ull << (t & 63)) - 1ull));
-                    if (p < (uint32_t)kMergeCap) {
-                        M.s[p] = c[u].score;
-                        M.f[p] = c[u].flat;
-                        M.node[p] = c[u].node;
+                for (int u = 0; u < U; ++u) {
+                    if (!okc[u]) continue;
+                    const uint32_t b = score_bin(sref, c[u].score);
+                    if (b <= bstar) {
+                        const uint32_t p = M.gstart[b] + atomicAdd(&M.cursor[b], 1u);
+                        if (p < staged) {          // holds by construction; never write past it
+                            M.s[p] = c[u].score;
+                            M.f[p] = c[u].flat;
+                            M.node[p] = c[u].node;
+                        }
                     }
                 }
             }
         }
-    }
-    __syncthreads();
-    uint32_t n = M.n;
-    uint32_t o_star = 0u, f_star = 0xffffffffu;       // default: keep everything staged
-    const bool did_select = n > k;
-    if (n > (uint32_t)kMergeCap) {
-        // too many survivors of the pruning for LDS: select straight from global memory,
-        // then stage exactly the k selected candidates
+        __syncthreads();
+        // a very full boundary bin: find its need-th member exactly first
+        const bool big = cnt_b > (uint32_t)kBigBin && need < cnt_b;
+        uint32_t o_star = 0u, f_star = 0xffffffffu;
+        if (big) {
+            auto each_b = [&](auto fn) {
+                for (uint32_t p = cbefore + t; p < staged; p += NT) fn(f2ord(M.s[p]), M.f[p]);
+            };
+            block_select<NT>(each_b, need, M.sel, o_star, f_star, W.err);
+        }
+        for (uint32_t p = t; p < staged; p += NT) {
+            const float sc = M.s[p];
+            const uint32_t o = f2ord(sc), fl = M.f[p];
+            const uint32_t b = score_bin(sref, sc);
+            if (b == bstar && big && !key_le(o, fl, o_star, f_star)) continue;
+            const uint32_t st = M.gstart[b], en = st + M.ghist[b];
+            uint32_t r = 0u;
+            for (uint32_t q = st; q < en; ++q) {
+                const uint32_t o2 = f2ord(M.s[q]), f2 = M.f[q];
+                r += (o2 > o || (o2 == o && f2 < fl)) ? 1u : 0u;
+            }
+            if (b < bstar || r < need) write_row(st + r, sc, fl, M.node[p]);
+        }
+    } else {
+        // spill: select straight from the tiles' buffers, then rank the k survivors
         if (t == 0) atomicOr(W.err, kInfoMergeSpill);
         auto each_g = [&](auto fn) {
             for (int tile = 0; tile < ntile; ++tile)
                 for (int i = t; i < M.tcnt[tile]; i += NT) {
                     const Cand c = cand[(size_t)tile * CAPT + i];
-                    const uint32_t o = f2ord(c.score);
-                    if (o >= thr) fn(o, c.flat);
+                    if (score_bin(sref, c.score) <= bstar) fn(f2ord(c.score), c.flat);
                 }
         };
+        uint32_t o_star, f_star;
         block_select<NT>(each_g, k, M.sel, o_star, f_star, W.err);
-        if (t == 0) M.n = 0u;
-        __syncthreads();
         for (int tile = 0; tile < ntile; ++tile)
-            for (int i0 = 0; i0 < M.tcnt[tile]; i0 += NT) {
-                const int i = i0 + t;
-                bool pass = false;
-                Cand c{};
-                if (i < M.tcnt[tile]) {
-                    c = cand[(size_t)tile * CAPT + i];
-                    const uint32_t o = f2ord(c.score);
-                    pass = o >= thr && key_le(o, c.flat, o_star, f_star);
-                }
-                const uint64_t bal = __ballot(pass);
-                uint32_t wbase = 0;
-                if ((t & 63) == 0 && bal) wbase = atomicAdd(&M.n, (uint32_t)__popcll(bal));
-                wbase = __shfl(wbase, 0, 64);
-                if (pass) {
-                    const uint32_t p = wbase + (uint32_t)__popcll(bal & ((1ull << (t & 63)) - 1ull));
-                    M.s[p] = c.score;
-                    M.f[p] = c.flat;
-                    M.node[p] = c.node;
+            for (int i = t; i < M.tcnt[tile]; i += NT) {
+                const Cand c = cand[(size_t)tile * CAPT + i];
+                const uint32_t o = f2ord(c.score);
+                if (score_bin(sref, c.score) <= bstar && key_le(o, c.flat, o_star, f_star)) {
+                    const uint32_t p = atomicAdd(&M.n, 1u);
+                    if (p < (uint32_t)kMergeCap) {
+                        M.s[p] = c.score;
+                        M.f[p] = c.flat;
+                        M.node[p] = c.node;
+                    }
                 }
             }
         __syncthreads();
-        n = M.n;
-    } else if (n > k) {
-        auto each_l = [&](auto fn) {
-            for (uint32_t e = t; e < n; e += NT) fn(f2ord(M.s[e]), M.f[e]);
-        };
-        block_select<NT>(each_l, k, M.sel, o_star, f_star, W.err);
-    }
-    if (t == 0 && n < k) atomicOr(W.err, kErrInternal);
-
-    // order the k selected: buckets by key distance to the best, then exact in-bucket rank
-    {
-        uint32_t b = 0u;
-        for (uint32_t e = t; e < n; e += NT) {
-            const uint32_t o = f2ord(M.s[e]);
-            if (key_le(o, M.f[e], o_star, f_star)) b = max(b, o);
+        const uint32_t n = min(M.n, (uint32_t)kMergeCap);
+        if (t == 0 && M.n != k) atomicOr(W.err, kErrInternal);
+        for (uint32_t p = t; p < n; p += NT) {
+            const uint32_t o = f2ord(M.s[p]), fl = M.f[p];
+            uint32_t r = 0u;
+            for (uint32_t q = 0; q < n; ++q) {
+                const uint32_t o2 = f2ord(M.s[q]), f2 = M.f[q];
+                r += (o2 > o || (o2 == o && f2 < fl)) ? 1u : 0u;
+            }
+            write_row(r, M.s[p], fl, M.node[p]);
         }
-        b = wave_max_u(b);
-        if ((t & 63) == 0) atomicMax(&M.omax, b);
-    }
-    __syncthreads();
-    const uint32_t omax = M.omax;
-    // smallest selected key: the k-th key after a selection, else the minimum staged key
-    uint32_t olo = o_star;
-    if (!did_select) {
-        if (t == 0) M.sel.lo = 0xffffffffu;
-        __syncthreads();
-        uint32_t a = 0xffffffffu;
-        for (uint32_t e = t; e < n; e += NT) a = min(a, f2ord(M.s[e]));
-        a = wave_min_u(a);
-        if ((t & 63) == 0) atomicMin(&M.sel.lo, a);
-        __syncthreads();
-        olo = M.sel.lo;
-    }
-    const int bsh = (omax > olo) ? range_shift(omax - olo) : 0;
-    for (uint32_t e = t; e < n; e += NT) {
-        const uint32_t o = f2ord(M.s[e]);
-        if (key_le(o, M.f[e], o_star, f_star)) atomicAdd(&M.bin_cnt[(omax - o) >> bsh], 1u);
-    }
-    __syncthreads();
-    {
-        constexpr int BPT = kSortBins / NT;
-        uint32_t loc[BPT];
-        int sum = 0;
-#pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            loc[i] = M.bin_cnt[t * BPT + i];
-            sum += (int)loc[i];
-        }
-        int total;
-        int before = block_excl_scan<NT>(sum, M.sel.part, &total);
-#pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            M.bin_start[t * BPT + i] = (uint32_t)before;
-            before += (int)loc[i];
-        }
-    }
-    __syncthreads();
-    for (uint32_t e = t; e < n; e += NT) {
-        const uint32_t o = f2ord(M.s[e]);
-        if (key_le(o, M.f[e], o_star, f_star)) {
-            const uint32_t bin = (omax - o) >> bsh;
-            const uint32_t p = M.bin_start[bin] + atomicAdd(&M.bin_cur[bin], 1u);
-            M.order[p] = e;
-        }
-    }
-    __syncthreads();
-    const int S = W.S;
-    const int level = rec.level;
-    const uint32_t kk = min(k, n);        // equal unless the invariant above failed
-    for (uint32_t p = t; p < kk; p += NT) {
-        const uint32_t e = M.order[p];
-        if (e >= n) continue;
-        const uint32_t o = f2ord(M.s[e]), f = M.f[e];
-        const uint32_t bin = (omax - o) >> bsh;
-        const uint32_t st = M.bin_start[bin], en = st + M.bin_cnt[bin];
-        uint32_t rank = st;
-        for (uint32_t q = st; q < en; ++q) {
-            const uint32_t e2 = M.order[q];
-            const uint32_t o2 = f2ord(M.s[e2]), f2 = M.f[e2];
-            rank += (o2 > o || (o2 == o && f2 < f)) ? 1u : 0u;
-        }
-        const int slot = rec.base + (int)rank;
-        W.node[nxt][slot] = M.node[e];
-        W.score[nxt][slot] = M.s[e];
-        W.parent_slot[slot] = rec.base + (int)(f >> 8);
-        W.hist[(size_t)level * S + slot] = f;             // (r << 8) | c
     }
     if (t == 0) {
-        W.rec[req].rows = (int32_t)kk;
+        W.rec[req].rows = (int32_t)k;
         W.rec[req].level = level + 1;
     }
 }
@@ -707,10 +740,7 @@ __global__ void k_clear_wave(WaveDev W) {
         ReqRec r{};
         W.rec[i] = r;
     }
-    if (i < W.R * W.MT) {
-        W.tile_count[i] = 0;
-        W.tile_thr[i] = 0u;
-    }
+    if (i < W.R * W.MT) W.tile_count[i] = 0;
     if (i == 0) *W.err = 0u;
 }
 

@@ -35,14 +35,14 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
     int32_t MT = 0, CAPT = 0;
     size_t node[2]{}, score[2]{}, parent_slot = 0, hist = 0, rec = 0;
-    size_t cand = 0, tile_count = 0, tile_thr = 0, err = 0;
+    size_t cand = 0, tile_count = 0, tile_hist = 0, err = 0;
     size_t fin_sids = 0, fin_scores = 0, fin_items = 0, fin_counts = 0, total = 0;
 };
 
 Layout make_layout(int L, int S, int R, int Bmax) {
     Layout l;
     l.MT = (Bmax + tcb::kTileRows - 1) / tcb::kTileRows;
-    l.CAPT = std::min(Bmax, tcb::kTileRows * TCB_MAX_V);
+    l.CAPT = std::min(Bmax + tcb::kTileSlack, tcb::kTileRows * TCB_MAX_V);
     size_t o = 0;
     auto take = [&](size_t bytes) {
         size_t at = o;
@@ -60,7 +60,7 @@ Layout make_layout(int L, int S, int R, int Bmax) {
     const size_t ncand = r * (size_t)l.MT * (size_t)l.CAPT;
     l.cand = take(ncand * 16);
     l.tile_count = take(r * (size_t)l.MT * 4);
-    l.tile_thr = take(r * (size_t)l.MT * 4);
+    l.tile_hist = take(r * (size_t)l.MT * tcb::kHistBins * 2);
     l.err = take(256);
     l.fin_sids = take(r * (size_t)Bmax * (size_t)L);
     l.fin_scores = take(r * (size_t)Bmax * 4);
@@ -260,7 +260,7 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
     w.rec = (tcb::ReqRec *)(ws + l.rec);
     w.cand = (void *)(ws + l.cand);
     w.tile_count = (int32_t *)(ws + l.tile_count);
-    w.tile_thr = (uint32_t *)(ws + l.tile_thr);
+    w.tile_hist = (uint16_t *)(ws + l.tile_hist);
     w.err = (uint32_t *)(ws + l.err);
     w.S = max_slots;
     w.R = max_requests;
@@ -350,10 +350,20 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
     tcb_status st = step_common(b);
     if (st) return st;
     const int nr = n_req_hw(b);
-    hipError_t e = tcb::launch_expand(b->tdev, b->w, b->par, nr, d_logits, ld, dtype, (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    const bool timed = b->timing_used < b->timing_cap;
+    hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 3] : nullptr;
+    hipError_t e = timed ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (e == hipSuccess) e = tcb::launch_expand(b->tdev, b->w, b->par, nr, d_logits, ld, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "expand launch");
-    e = tcb::launch_merge(b->tdev, b->w, b->par, nr, (hipStream_t)stream);
+    if (timed) e = hipEventRecord(ev[1], s);
+    if (e == hipSuccess) e = tcb::launch_merge(b->tdev, b->w, b->par, nr, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
+    if (timed) {
+        e = hipEventRecord(ev[2], s);
+        if (e != hipSuccess) return hip_fail(e, "event record");
+        b->timing_used++;
+    }
     step_done(b);
     return TCB_OK;
 }
@@ -368,11 +378,21 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
     tcb_status st = step_common(b);
     if (st) return st;
     const int nr = n_req_hw(b);
-    hipError_t e = tcb::launch_expand_lmhead(b->tdev, b->w, b->par, nr, d_hidden, ld_hidden, H,
-                                             d_weight, (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    const bool timed = b->timing_used < b->timing_cap;
+    hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 3] : nullptr;
+    hipError_t e = timed ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (e == hipSuccess)
+        e = tcb::launch_expand_lmhead(b->tdev, b->w, b->par, nr, d_hidden, ld_hidden, H, d_weight, s);
     if (e != hipSuccess) return hip_fail(e, "expand_lmhead launch");
-    e = tcb::launch_merge(b->tdev, b->w, b->par, nr, (hipStream_t)stream);
+    if (timed) e = hipEventRecord(ev[1], s);
+    if (e == hipSuccess) e = tcb::launch_merge(b->tdev, b->w, b->par, nr, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
+    if (timed) {
+        e = hipEventRecord(ev[2], s);
+        if (e != hipSuccess) return hip_fail(e, "event record");
+        b->timing_used++;
+    }
     step_done(b);
     return TCB_OK;
 }
@@ -465,6 +485,46 @@ tcb_status tcb_beam_finalize_device(tcb_beams *b, int32_t n, const int32_t *req_
     st = run_finalize(b, n, req_ids, d_sids, d_scores, d_items, d_counts, (hipStream_t)stream);
     if (st) return st;
     release(b, n, req_ids);
+    return TCB_OK;
+}
+
+tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity) {
+    if (!b || capacity < 0) return set_error(TCB_E_ARG, "enable_timing: bad arguments");
+    for (auto e : b->events) (void)hipEventDestroy(e);
+    b->events.clear();
+    b->timing_cap = 0;
+    b->timing_used = 0;
+    for (int32_t i = 0; i < capacity * 3; ++i) {
+        hipEvent_t e;
+        hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) {
+            for (auto x : b->events) (void)hipEventDestroy(x);
+            b->events.clear();
+            return hip_fail(r, "enable_timing: hipEventCreate");
+        }
+        b->events.push_back(e);
+    }
+    b->timing_cap = capacity;
+    return TCB_OK;
+}
+
+tcb_status tcb_beams_timing(tcb_beams *b, double *expand_ms, double *merge_ms, int32_t *steps) {
+    if (!b || !expand_ms || !merge_ms || !steps) return set_error(TCB_E_ARG, "timing: null pointer");
+    if (b->timing_cap == 0) return set_error(TCB_E_STATE, "timing: not enabled");
+    double ex = 0.0, mg = 0.0;
+    for (int32_t i = 0; i < b->timing_used; ++i) {
+        hipEvent_t *ev = &b->events[(size_t)i * 3];
+        hipError_t r = hipEventSynchronize(ev[2]);
+        float a = 0.f, c = 0.f;
+        if (r == hipSuccess) r = hipEventElapsedTime(&a, ev[0], ev[1]);
+        if (r == hipSuccess) r = hipEventElapsedTime(&c, ev[1], ev[2]);
+        if (r != hipSuccess) return hip_fail(r, "timing: elapsed time");
+        ex += a;
+        mg += c;
+    }
+    *expand_ms = ex;
+    *merge_ms = mg;
+    *steps = b->timing_used;
     return TCB_OK;
 }
 

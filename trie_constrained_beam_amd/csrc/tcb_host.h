@@ -38,6 +38,12 @@ struct tcb_beams {
     float *d_fin_scores = nullptr;
     int64_t *d_fin_items = nullptr;
     int32_t *d_fin_counts = nullptr;
+    // optional kernel timing: 3 events per step (before expand, after expand, after merge)
+    std::vector<hipEvent_t> events;
+    int32_t timing_cap = 0, timing_used = 0;
+    ~tcb_beams() {
+        for (auto e : events) (void)hipEventDestroy(e);
+    }
 };
 
 namespace tcb_host {

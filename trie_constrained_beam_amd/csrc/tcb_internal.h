@@ -16,12 +16,18 @@ constexpr int kTileWaves = 8;
 constexpr int kRowsPerWave = 4;
 constexpr int kTileRows = kTileWaves * kRowsPerWave;   // 32
 constexpr int kExpandThreads = kTileWaves * 64;        // 512
-// merge: one workgroup per request; candidates that survive pruning are staged in LDS
-constexpr int kMergeThreads = 512;
-constexpr int kMergeCap = 8192;
-constexpr int kSelBins = 1024;      // histogram bins of the selection passes
-constexpr int kSortBins = 1024;     // buckets of the survivors' ordering pass
+// merge: one workgroup per request
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeCap = 4096;     // candidates staged in LDS by the merge
+constexpr int kSelBins = 1024;      // histogram bins of the exact selection fallback
 constexpr int kMaxTilesPerReq = TCB_MAX_WIDTH / kTileRows;
+// Request-wide score bins: a candidate of score s falls in bin
+// min(kHistBins - 1, floor((s_ref - s) * kHistRes)), s_ref = the request's best row
+// score before the step. No candidate beats s_ref (log-probabilities are <= 0), so the
+// bins are known to every tile without communication.
+constexpr int kHistBins = 512;
+constexpr float kHistRes = 32.0f;   // bins per nat: 16 nats of resolution
+constexpr int kTileSlack = 512;     // extra tile capacity for the boundary bin
 
 // request status
 constexpr int kReqFree = 0;
@@ -59,8 +65,8 @@ struct WaveDev {
     uint32_t *hist;                // [L][S] back-pointer (r << 8) | c per level
     ReqRec *rec;                   // [R]
     void *cand;                    // [R][MT][CAPT] 16-byte candidate records kept by each tile
-    int32_t *tile_count;           // [R][MT]
-    uint32_t *tile_thr;            // [R][MT] order key of the tile's n_i-th score, 0 = none
+    int32_t *tile_count;           // [R][MT] candidates kept by each tile
+    uint16_t *tile_hist;           // [R][MT][kHistBins] score-bin counts of the kept candidates
     uint32_t *err;                 // sticky error / info bits
     int32_t S, R, MT, CAPT, Bmax, norm, validate, pad;
 };
