@@ -221,15 +221,15 @@ tcb_status tcb_beam_finalize_device(tcb_beams *b, int32_t n, const int32_t *req_
                                     uint8_t *d_sids, float *d_scores, int64_t *d_items,
                                     int32_t *d_counts, void *stream);
 
-/* Diagnostics: record HIP events on `stream` around the expand and merge kernels of
- * the next `capacity` steps (0 stops recording and releases the events). The events
- * are created here (no device memory). */
+/* Diagnostics: record HIP events on `stream` around the step kernel of the next
+ * `capacity` steps (0 stops recording and releases the events). The events are
+ * created here (no device memory). */
 tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity);
 
 /* Synchronise the recorded events and report, over the steps recorded since
- * tcb_beams_enable_timing, the summed expand and merge kernel durations (ms) and
- * the number of steps. Errors: TCB_E_STATE (timing not enabled), TCB_E_HIP. */
-tcb_status tcb_beams_timing(tcb_beams *b, double *expand_ms, double *merge_ms, int32_t *steps);
+ * tcb_beams_enable_timing, the summed step-kernel durations (ms) and the number of
+ * steps. Errors: TCB_E_STATE (timing not enabled), TCB_E_HIP. */
+tcb_status tcb_beams_timing(tcb_beams *b, double *step_ms, int32_t *steps);
 
 void tcb_beams_destroy(tcb_beams *b);
 

@@ -171,14 +171,14 @@ class Beams:
         return int(v.value)
 
     def enable_timing(self, capacity: int):
-        """Record HIP events around the expand and merge kernels of the next steps."""
+        """Record HIP events around the step kernel of the next ``capacity`` steps."""
         check(lib().tcb_beams_enable_timing(self._h, int(capacity)))
 
     def timing(self):
-        """(expand_ms, merge_ms, steps) summed over the recorded steps; synchronises."""
-        a, b, n = C.c_double(), C.c_double(), C.c_int32()
-        check(lib().tcb_beams_timing(self._h, C.byref(a), C.byref(b), C.byref(n)))
-        return float(a.value), float(b.value), int(n.value)
+        """(step_ms, steps): summed step-kernel durations over the recorded steps; synchronises."""
+        a, n = C.c_double(), C.c_int32()
+        check(lib().tcb_beams_timing(self._h, C.byref(a), C.byref(n)))
+        return float(a.value), int(n.value)
 
     def finalize(self, req_ids):
         """Ranked beams of finished requests (host arrays); releases their slots."""

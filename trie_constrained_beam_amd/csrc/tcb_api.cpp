@@ -34,8 +34,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
     int32_t MT = 0, CAPT = 0;
-    size_t node[2]{}, score[2]{}, parent_slot = 0, hist = 0, rec = 0;
-    size_t cand = 0, tile_count = 0, tile_hist = 0, err = 0;
+    size_t node[2]{}, score[2]{}, parent_slot = 0, hist = 0, rec[2]{}, done = 0;
+    size_t cs = 0, cf = 0, cn = 0, tcum = 0, err = 0;
     size_t fin_sids = 0, fin_scores = 0, fin_items = 0, fin_counts = 0, total = 0;
 };
 
@@ -56,11 +56,14 @@ Layout make_layout(int L, int S, int R, int Bmax) {
     l.score[1] = take(s * 4);
     l.parent_slot = take(s * 4);
     l.hist = take((size_t)L * s * 4);
-    l.rec = take(r * sizeof(tcb::ReqRec));
+    l.rec[0] = take(r * sizeof(tcb::ReqRec));
+    l.rec[1] = take(r * sizeof(tcb::ReqRec));
+    l.done = take(r * 4);
     const size_t ncand = r * (size_t)l.MT * (size_t)l.CAPT;
-    l.cand = take(ncand * 16);
-    l.tile_count = take(r * (size_t)l.MT * 4);
-    l.tile_hist = take(r * (size_t)l.MT * tcb::kHistBins * 2);
+    l.cs = take(ncand * 4);
+    l.cf = take(ncand * 4);
+    l.cn = take(ncand * 4);
+    l.tcum = take(r * (size_t)l.MT * tcb::kBins * 2);
     l.err = take(256);
     l.fin_sids = take(r * (size_t)Bmax * (size_t)L);
     l.fin_scores = take(r * (size_t)Bmax * 4);
@@ -145,7 +148,7 @@ tcb_status run_finalize(tcb_beams *b, int32_t n, const int32_t *req_ids, uint8_t
             fb.req[j] = req_ids[i0 + j];
             fb.out_row[j] = i0 + j;
         }
-        hipError_t e = tcb::launch_finalize(b->tdev, b->w, b->par, fb, sids, scores, items, counts, s);
+        hipError_t e = tcb::launch_finalize(b->tdev, b->w, b->rp, fb, sids, scores, items, counts, s);
         if (e != hipSuccess) return hip_fail(e, "finalize launch");
     }
     return TCB_OK;
@@ -257,10 +260,13 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
     }
     w.parent_slot = (int32_t *)(ws + l.parent_slot);
     w.hist = (uint32_t *)(ws + l.hist);
-    w.rec = (tcb::ReqRec *)(ws + l.rec);
-    w.cand = (void *)(ws + l.cand);
-    w.tile_count = (int32_t *)(ws + l.tile_count);
-    w.tile_hist = (uint16_t *)(ws + l.tile_hist);
+    w.rec[0] = (tcb::ReqRec *)(ws + l.rec[0]);
+    w.rec[1] = (tcb::ReqRec *)(ws + l.rec[1]);
+    w.done = (int32_t *)(ws + l.done);
+    w.cs = (float *)(ws + l.cs);
+    w.cf = (uint32_t *)(ws + l.cf);
+    w.cn = (int32_t *)(ws + l.cn);
+    w.tcum = (uint16_t *)(ws + l.tcum);
     w.err = (uint32_t *)(ws + l.err);
     w.S = max_slots;
     w.R = max_requests;
@@ -314,7 +320,7 @@ tcb_status tcb_beam_init(tcb_beams *b, int32_t n, const int32_t *widths, int32_t
             ib.base[j] = bases[(size_t)(i0 + j)];
             ib.width[j] = widths[i0 + j];
         }
-        hipError_t e = tcb::launch_init(b->w, b->par, ib, (hipStream_t)stream);
+        hipError_t e = tcb::launch_init(b->w, ib, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "beam_init launch");
     }
     b->free_ranges = fr;
@@ -337,7 +343,7 @@ static tcb_status step_common(tcb_beams *b) {
 }
 
 static void step_done(tcb_beams *b) {
-    b->par ^= 1;
+    b->rp ^= 1;
     b->steps++;
     for (auto &q : b->reqs)
         if (q.used && q.level < b->L) q.level++;
@@ -352,15 +358,12 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
     const int nr = n_req_hw(b);
     hipStream_t s = (hipStream_t)stream;
     const bool timed = b->timing_used < b->timing_cap;
-    hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 3] : nullptr;
+    hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 2] : nullptr;
     hipError_t e = timed ? hipEventRecord(ev[0], s) : hipSuccess;
-    if (e == hipSuccess) e = tcb::launch_expand(b->tdev, b->w, b->par, nr, d_logits, ld, dtype, s);
-    if (e != hipSuccess) return hip_fail(e, "expand launch");
-    if (timed) e = hipEventRecord(ev[1], s);
-    if (e == hipSuccess) e = tcb::launch_merge(b->tdev, b->w, b->par, nr, s);
-    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    if (e == hipSuccess) e = tcb::launch_step(b->tdev, b->w, b->rp, nr, d_logits, ld, dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "step launch");
     if (timed) {
-        e = hipEventRecord(ev[2], s);
+        e = hipEventRecord(ev[1], s);
         if (e != hipSuccess) return hip_fail(e, "event record");
         b->timing_used++;
     }
@@ -380,16 +383,13 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
     const int nr = n_req_hw(b);
     hipStream_t s = (hipStream_t)stream;
     const bool timed = b->timing_used < b->timing_cap;
-    hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 3] : nullptr;
+    hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 2] : nullptr;
     hipError_t e = timed ? hipEventRecord(ev[0], s) : hipSuccess;
     if (e == hipSuccess)
-        e = tcb::launch_expand_lmhead(b->tdev, b->w, b->par, nr, d_hidden, ld_hidden, H, d_weight, s);
-    if (e != hipSuccess) return hip_fail(e, "expand_lmhead launch");
-    if (timed) e = hipEventRecord(ev[1], s);
-    if (e == hipSuccess) e = tcb::launch_merge(b->tdev, b->w, b->par, nr, s);
-    if (e != hipSuccess) return hip_fail(e, "merge launch");
+        e = tcb::launch_step_lmhead(b->tdev, b->w, b->rp, nr, d_hidden, ld_hidden, H, d_weight, s);
+    if (e != hipSuccess) return hip_fail(e, "step_lmhead launch");
     if (timed) {
-        e = hipEventRecord(ev[2], s);
+        e = hipEventRecord(ev[1], s);
         if (e != hipSuccess) return hip_fail(e, "event record");
         b->timing_used++;
     }
@@ -403,15 +403,12 @@ tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, int32_
     hipStream_t s = (hipStream_t)stream;
     const size_t S = (size_t)b->w.S;
     hipError_t e = hipSuccess;
-    if (d_node && e == hipSuccess)
-        e = hipMemcpyAsync(d_node, b->w.node[b->par], S * 4, hipMemcpyDeviceToDevice, s);
-    if (d_score && e == hipSuccess)
-        e = hipMemcpyAsync(d_score, b->w.score[b->par], S * 4, hipMemcpyDeviceToDevice, s);
     if (d_parent_slot && e == hipSuccess)
         e = hipMemcpyAsync(d_parent_slot, b->w.parent_slot, S * 4, hipMemcpyDeviceToDevice, s);
     if (d_hist && e == hipSuccess)
         e = hipMemcpyAsync(d_hist, b->w.hist, (size_t)b->L * S * 4, hipMemcpyDeviceToDevice, s);
-    if ((d_rows || d_level) && e == hipSuccess) e = tcb::launch_export_req(b->w, d_rows, d_level, s);
+    if ((d_node || d_score || d_rows || d_level) && e == hipSuccess)
+        e = tcb::launch_export(b->w, b->rp, d_node, d_score, d_rows, d_level, s);
     if (e != hipSuccess) return hip_fail(e, "beam_export");
     return TCB_OK;
 }
@@ -494,7 +491,7 @@ tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity) {
     b->events.clear();
     b->timing_cap = 0;
     b->timing_used = 0;
-    for (int32_t i = 0; i < capacity * 3; ++i) {
+    for (int32_t i = 0; i < capacity * 2; ++i) {
         hipEvent_t e;
         hipError_t r = hipEventCreate(&e);
         if (r != hipSuccess) {
@@ -508,22 +505,19 @@ tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity) {
     return TCB_OK;
 }
 
-tcb_status tcb_beams_timing(tcb_beams *b, double *expand_ms, double *merge_ms, int32_t *steps) {
-    if (!b || !expand_ms || !merge_ms || !steps) return set_error(TCB_E_ARG, "timing: null pointer");
+tcb_status tcb_beams_timing(tcb_beams *b, double *step_ms, int32_t *steps) {
+    if (!b || !step_ms || !steps) return set_error(TCB_E_ARG, "timing: null pointer");
     if (b->timing_cap == 0) return set_error(TCB_E_STATE, "timing: not enabled");
-    double ex = 0.0, mg = 0.0;
+    double ms = 0.0;
     for (int32_t i = 0; i < b->timing_used; ++i) {
-        hipEvent_t *ev = &b->events[(size_t)i * 3];
-        hipError_t r = hipEventSynchronize(ev[2]);
-        float a = 0.f, c = 0.f;
+        hipEvent_t *ev = &b->events[(size_t)i * 2];
+        hipError_t r = hipEventSynchronize(ev[1]);
+        float a = 0.f;
         if (r == hipSuccess) r = hipEventElapsedTime(&a, ev[0], ev[1]);
-        if (r == hipSuccess) r = hipEventElapsedTime(&c, ev[1], ev[2]);
         if (r != hipSuccess) return hip_fail(r, "timing: elapsed time");
-        ex += a;
-        mg += c;
+        ms += a;
     }
-    *expand_ms = ex;
-    *merge_ms = mg;
+    *step_ms = ms;
     *steps = b->timing_used;
     return TCB_OK;
 }

@@ -29,7 +29,7 @@ struct tcb_beams {
     tcb::TrieDev tdev{};
     tcb::WaveDev w{};
     int32_t L = 0, V = 0;
-    int par = 0;
+    int rp = 0;                            // which request-record buffer is current
     int64_t steps = 0;
     std::vector<Req> reqs;
     std::vector<std::pair<int32_t, int32_t>> free_ranges;  // (start, length), sorted
@@ -38,7 +38,7 @@ struct tcb_beams {
     float *d_fin_scores = nullptr;
     int64_t *d_fin_items = nullptr;
     int32_t *d_fin_counts = nullptr;
-    // optional kernel timing: 3 events per step (before expand, after expand, after merge)
+    // optional kernel timing: 2 events per step (around the step kernel)
     std::vector<hipEvent_t> events;
     int32_t timing_cap = 0, timing_used = 0;
     ~tcb_beams() {

@@ -10,24 +10,26 @@
 namespace tcb {
 
 // --------------------------------------------------------------------- tile shapes
-// expand: one workgroup of kTileWaves wave64s handles kTileRows consecutive rows of
-// one request; wave w takes rows w, w + kTileWaves, ... of the tile.
-constexpr int kTileWaves = 8;
+// One beam row is held by 16 lanes (one DPP row of a wave64): lane j of the group
+// holds 16 of the row's 256 codes, so a wave holds 4 rows and a workgroup of
+// kWaves waves holds a tile of kTileRows consecutive rows of one request.
+constexpr int kWaves = 16;
+constexpr int kThreads = kWaves * 64;                 // 1024
 constexpr int kRowsPerWave = 4;
-constexpr int kTileRows = kTileWaves * kRowsPerWave;   // 32
-constexpr int kExpandThreads = kTileWaves * 64;        // 512
-// merge: one workgroup per request
-constexpr int kMergeThreads = 1024;
-constexpr int kMergeCap = 4096;     // candidates staged in LDS by the merge
-constexpr int kSelBins = 1024;      // histogram bins of the exact selection fallback
+constexpr int kTileRows = kWaves * kRowsPerWave;      // 64
 constexpr int kMaxTilesPerReq = TCB_MAX_WIDTH / kTileRows;
 // Request-wide score bins: a candidate of score s falls in bin
-// min(kHistBins - 1, floor((s_ref - s) * kHistRes)), s_ref = the request's best row
-// score before the step. No candidate beats s_ref (log-probabilities are <= 0), so the
-// bins are known to every tile without communication.
-constexpr int kHistBins = 512;
-constexpr float kHistRes = 32.0f;   // bins per nat: 16 nats of resolution
-constexpr int kTileSlack = 512;     // extra tile capacity for the boundary bin
+// min(kBins - 1, floor((s_ref - s) * kBinRes)), s_ref = the request's best row score
+// before the step. No candidate beats s_ref (log-probabilities are <= 0), so every
+// tile of the request bins identically without communicating; a lower bin always
+// holds strictly higher scores.
+constexpr int kBins = 1024;
+constexpr float kBinRes = 32.0f;                      // bins per nat: 32 nats of range
+static_assert(kBins == kThreads, "one bin per thread in the scans");
+constexpr int kTileSlack = 1024;                      // tile capacity beyond the beam width
+constexpr int kMergeCap = 4096;                       // candidates the merge stages in LDS
+static_assert(kMergeCap >= TCB_MAX_WIDTH, "the exact merge path stages up to n_i survivors");
+constexpr int kSelBins = 1024;                        // bins of the exact selection
 
 // request status
 constexpr int kReqFree = 0;
@@ -37,7 +39,8 @@ constexpr int kReqActive = 1;
 constexpr uint32_t kErrNonFinite = 1u;
 constexpr uint32_t kErrBadNode = 2u;
 constexpr uint32_t kErrInternal = 4u;
-constexpr uint32_t kInfoMergeSpill = 0x100u;   // merge used its global-memory path
+constexpr uint32_t kInfoMergeSpill = 0x100u;   // a merge used its exact (slow) path
+constexpr uint32_t kInfoTileExact = 0x200u;    // a tile used its exact (slow) path
 
 // --------------------------------------------------------------------- device views
 struct TrieDev {
@@ -52,21 +55,24 @@ struct TrieDev {
 struct ReqRec {                    // one per request id, 32 bytes
     int32_t base;                  // first slot
     int32_t width;                 // beam width n_i
-    int32_t rows;                  // live rows (written by the merge)
-    int32_t level;                 // steps taken
+    int32_t rows;                  // live rows
+    int32_t level;                 // steps taken (== L: finished)
     int32_t status;                // kReqFree / kReqActive
-    int32_t pad[3];
+    int32_t par;                   // which node/score buffer holds the live rows
+    int32_t pad[2];
 };
 
 struct WaveDev {
-    int32_t *node[2];              // [S] trie node of each slot's row, ping-pong
-    float *score[2];               // [S] beam score, ping-pong
-    int32_t *parent_slot;          // [S] parent slot at the last step
+    int32_t *node[2];              // [S] trie node of each slot's row (ping-pong per request)
+    float *score[2];               // [S] beam score (ping-pong per request)
+    int32_t *parent_slot;          // [S] parent slot at the request's last step
     uint32_t *hist;                // [L][S] back-pointer (r << 8) | c per level
-    ReqRec *rec;                   // [R]
-    void *cand;                    // [R][MT][CAPT] 16-byte candidate records kept by each tile
-    int32_t *tile_count;           // [R][MT] candidates kept by each tile
-    uint16_t *tile_hist;           // [R][MT][kHistBins] score-bin counts of the kept candidates
+    ReqRec *rec[2];                // [R] request records; a step reads one, writes the other
+    int32_t *done;                 // [R] tiles of the request that finished this step
+    float *cs;                     // [R][MT][CAPT] kept candidates of every tile: score
+    uint32_t *cf;                  //                                              flat r*256+c
+    int32_t *cn;                   //                                              child node
+    uint16_t *tcum;                // [R][MT][kBins] cumulative kept count of each tile by bin
     uint32_t *err;                 // sticky error / info bits
     int32_t S, R, MT, CAPT, Bmax, norm, validate, pad;
 };
@@ -86,16 +92,16 @@ struct FinBatch {
 };
 
 hipError_t launch_clear_wave(const WaveDev &w, hipStream_t s);
-hipError_t launch_init(const WaveDev &w, int par, const InitBatch &b, hipStream_t s);
-hipError_t launch_expand(const TrieDev &t, const WaveDev &w, int par, int n_req,
-                         const void *logits, int64_t ld, int dtype, hipStream_t s);
-hipError_t launch_expand_lmhead(const TrieDev &t, const WaveDev &w, int par, int n_req,
-                                const void *hidden, int64_t ld, int H, const void *weight,
-                                hipStream_t s);
-hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int par, int n_req, hipStream_t s);
-hipError_t launch_finalize(const TrieDev &t, const WaveDev &w, int par, const FinBatch &b,
+hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s);
+hipError_t launch_step(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *logits,
+                       int64_t ld, int dtype, hipStream_t s);
+hipError_t launch_step_lmhead(const TrieDev &t, const WaveDev &w, int rp, int n_req,
+                              const void *hidden, int64_t ld, int H, const void *weight,
+                              hipStream_t s);
+hipError_t launch_finalize(const TrieDev &t, const WaveDev &w, int rp, const FinBatch &b,
                            uint8_t *sids, float *scores, int64_t *items, int32_t *counts,
                            hipStream_t s);
-hipError_t launch_export_req(const WaveDev &w, int32_t *rows, int32_t *level, hipStream_t s);
+hipError_t launch_export(const WaveDev &w, int rp, int32_t *node, float *score, int32_t *rows,
+                         int32_t *level, hipStream_t s);
 
 }  // namespace tcb
