@@ -144,25 +144,25 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     if graphs is None:
-        step_ms, n_timed = beams.timing()
+        tile_ms, merge_ms, n_timed = beams.timing()
     else:
         # the same decodes again, eagerly, with per-kernel events (graph replays hide them)
         beams.enable_timing(args.steps * L)
         for d in range(args.steps):
             decode(d % n_copies)
-        step_ms, n_timed = beams.timing()
+        tile_ms, merge_ms, n_timed = beams.timing()
     beams.enable_timing(0)
 
     value = rows_x_steps * args.steps / elapsed
     dsize = 2 if wl.bf16 else 4
     expand_unit = V * dsize + EXPAND_STATE_BYTES + EXPAND_TRIE_BYTES
     expand_bytes_per_launch = rows_x_steps * expand_unit / L
-    expand_avg_s = step_ms / 1e3 / n_timed
+    expand_avg_s = tile_ms / 1e3 / n_timed
     achieved = expand_bytes_per_launch / expand_avg_s / 1e9
     path_unit = expand_unit + MERGE_WRITE_BYTES
     wall_gbps = rows_x_steps * path_unit * args.steps / elapsed / 1e9
-    log(f"[bench] {args.steps} decodes in {elapsed * 1e3:.1f} ms; step kernel avg "
-        f"{expand_avg_s * 1e6:.2f} us")
+    log(f"[bench] {args.steps} decodes in {elapsed * 1e3:.1f} ms; tile kernel avg "
+        f"{expand_avg_s * 1e6:.2f} us, merge kernel avg {merge_ms / n_timed * 1e3:.2f} us")
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -208,10 +208,11 @@ def main():
                    "logits": ("bf16" if wl.bf16 else "f32") + f" N(0,{wl.sigma:g}^2)",
                    "rows_x_steps_per_decode": rows_x_steps, "rows_per_step": rows_per_step,
                    "graph": bool(args.graph), "logits_pool_copies": n_copies},
-        "roofline": {"bound": "hbm", "kernel": "k_step", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": "k_tile", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                      "bytes_per_row_step": expand_unit, "avg_launch_us": expand_avg_s * 1e6},
         "hbm_GBps_wall": wall_gbps,
+        "merge_avg_us": merge_ms / n_timed * 1e3,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

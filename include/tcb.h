@@ -65,6 +65,8 @@ enum { TCB_NORM_CHILDREN = 0, TCB_NORM_LEVEL = 1 }; /* log-softmax normaliser   
 #define TCB_MAX_L 8
 #define TCB_MAX_V 256
 #define TCB_MAX_WIDTH 4096
+#define TCB_MASK_AUTO (-1)          /* mask_depths: choose from the trie's fanouts     */
+#define TCB_MASK_AUTO_FANOUT 32     /* ... depths whose mean fanout is at least this    */
 
 typedef struct tcb_trie tcb_trie;
 typedef struct tcb_beams tcb_beams;
@@ -81,7 +83,10 @@ const char *tcb_version(void);
  *   L           SID depth, 1..TCB_MAX_L
  *   V           codes per level, 2..256; every code must be < V
  *   mask_depths depths 0..mask_depths-1 also get a 256-bit child mask per node
- *               ("dense" trie); deeper nodes use only the CSR child list. 0..L.
+ *               ("dense" trie); deeper nodes use only the CSR child list. 0..L, or
+ *               TCB_MASK_AUTO: the leading depths whose nodes have on average at
+ *               least TCB_MASK_AUTO_FANOUT children (tcb_trie_info reports the choice).
+ *               Results do not depend on this choice; only speed does.
  * Duplicated SIDs collapse onto one leaf whose item is the lowest catalog row.
  * Nodes are numbered depth-major and lexicographically: the root is 0, depth d
  * holds ids [off_d, off_{d+1}) in ascending prefix order, so the children of a node
@@ -221,15 +226,15 @@ tcb_status tcb_beam_finalize_device(tcb_beams *b, int32_t n, const int32_t *req_
                                     uint8_t *d_sids, float *d_scores, int64_t *d_items,
                                     int32_t *d_counts, void *stream);
 
-/* Diagnostics: record HIP events on `stream` around the step kernel of the next
- * `capacity` steps (0 stops recording and releases the events). The events are
- * created here (no device memory). */
+/* Diagnostics: record HIP events on `stream` around the two kernels of each of the
+ * next `capacity` steps (the tile kernel, then the per-request merge kernel); 0 stops
+ * recording and releases the events. The events are created here (no device memory). */
 tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity);
 
 /* Synchronise the recorded events and report, over the steps recorded since
- * tcb_beams_enable_timing, the summed step-kernel durations (ms) and the number of
- * steps. Errors: TCB_E_STATE (timing not enabled), TCB_E_HIP. */
-tcb_status tcb_beams_timing(tcb_beams *b, double *step_ms, int32_t *steps);
+ * tcb_beams_enable_timing, the summed tile-kernel and merge-kernel durations (ms) and
+ * the number of steps. Errors: TCB_E_STATE (timing not enabled), TCB_E_HIP. */
+tcb_status tcb_beams_timing(tcb_beams *b, double *tile_ms, double *merge_ms, int32_t *steps);
 
 void tcb_beams_destroy(tcb_beams *b);
 

@@ -18,6 +18,7 @@ TCB_F32, TCB_BF16 = 0, 1
 TCB_NORM_CHILDREN, TCB_NORM_LEVEL = 0, 1
 TCB_MAX_L = 8
 TCB_MAX_WIDTH = 4096
+TCB_MASK_AUTO = -1
 
 
 class TrieInfo(C.Structure):
@@ -63,7 +64,7 @@ SIGNATURES = {
     "tcb_beam_finalize": (I32, [P, I32, P, P, P, P, P, P]),
     "tcb_beam_finalize_device": (I32, [P, I32, P, P, P, P, P, P]),
     "tcb_beams_enable_timing": (I32, [P, I32]),
-    "tcb_beams_timing": (I32, [P, C.POINTER(C.c_double), C.POINTER(I32)]),
+    "tcb_beams_timing": (I32, [P, C.POINTER(C.c_double), C.POINTER(C.c_double), C.POINTER(I32)]),
     "tcb_beams_destroy": (None, [P]),
 }
 

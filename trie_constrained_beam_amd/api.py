@@ -29,13 +29,14 @@ class Trie:
         if sids.ndim != 2:
             raise ValueError("sids must be [n_items, L]")
         n, depth = sids.shape
-        mask_depths = min(3, depth) if mask_depths is None else int(mask_depths)
+        mask_depths = L.TCB_MASK_AUTO if mask_depths is None else int(mask_depths)
         h = C.c_void_p()
         check(lib().tcb_build_trie(sids.ctypes.data, n, depth, V, mask_depths, C.byref(h)))
         self._h = h
         self.info = L.TrieInfo()
         check(lib().tcb_trie_info(h, C.byref(self.info)))
         self.L, self.V = int(self.info.L), int(self.info.V)
+        self.mask_depths = int(self.info.mask_depths)
         self.d_image = None
         if device is not None:
             self.upload(device)
@@ -171,14 +172,14 @@ class Beams:
         return int(v.value)
 
     def enable_timing(self, capacity: int):
-        """Record HIP events around the step kernel of the next ``capacity`` steps."""
+        """Record HIP events around the tile and merge kernels of the next ``capacity`` steps."""
         check(lib().tcb_beams_enable_timing(self._h, int(capacity)))
 
     def timing(self):
-        """(step_ms, steps): summed step-kernel durations over the recorded steps; synchronises."""
-        a, n = C.c_double(), C.c_int32()
-        check(lib().tcb_beams_timing(self._h, C.byref(a), C.byref(n)))
-        return float(a.value), int(n.value)
+        """(tile_ms, merge_ms, steps) summed over the recorded steps; synchronises."""
+        a, b, n = C.c_double(), C.c_double(), C.c_int32()
+        check(lib().tcb_beams_timing(self._h, C.byref(a), C.byref(b), C.byref(n)))
+        return float(a.value), float(b.value), int(n.value)
 
     def finalize(self, req_ids):
         """Ranked beams of finished requests (host arrays); releases their slots."""

@@ -8,21 +8,23 @@
 //   the request keeps its best n (beam width) candidates by (score desc, r*256+c asc),
 //   in rank order; survivor j records parent r, code c and the child node.
 //
-// One kernel per step (k_step). Workgroup = a tile of 64 consecutive rows of one
-// request; the tiles of one request are placed on one XCD (workgroups are dealt to
-// the 8 XCDs round-robin), so everything they exchange stays in that XCD's L2.
-//   tile   16 lanes per row (one DPP row), 16 codes per lane: a row is one coalesced
-//          1 KiB (fp32) or 512 B (bf16) load. The child set is a 256-bit mask, read
-//          from the dense per-node mask at shallow depths or built in LDS from the CSR
-//          child list deeper down (bit-identical results). Masked log-softmax with DPP
-//          reductions inside the 16-lane row. Candidates are counted in request-wide
-//          score bins; the tile keeps every bin down to the one where its own count
-//          reaches n (a superset of its top-n), writes them grouped by bin plus its
-//          cumulative bin counts, and bumps the request's arrival counter.
-//   merge  the last tile of the request to arrive sums the tiles' cumulative counts to
-//          find the bin b* of the request's n-th candidate, stages only bins <= b* in
-//          LDS, ranks each candidate by counting the better members of its own bin, and
-//          writes the new rows (parent-gather / trie-advance) and the back-pointers.
+// Two kernels per step:
+//   k_tile   workgroup = a tile of 64 consecutive rows of one request. 16 lanes per
+//            row (one DPP row), 16 codes per lane: a row is one coalesced 1 KiB (fp32)
+//            or 512 B (bf16) load. The child set is a 256-bit mask, read from the dense
+//            per-node mask at shallow depths or built in LDS from the CSR child list
+//            deeper down (bit-identical results). Masked log-softmax with DPP reductions
+//            inside the 16-lane row. Candidates are binned request-wide; a per-lane
+//            sample bounds the tile's n-th best so that only a few candidates need exact
+//            treatment; the tile keeps every bin down to the one where its own count
+//            reaches n (a superset of its top-n) and writes them grouped by bin, plus its
+//            cumulative bin counts.
+//   k_merge  one workgroup per request: sums the tiles' cumulative counts to find the
+//            bin b* of the request's n-th candidate, stages only bins <= b* in LDS, ranks
+//            each candidate by counting the better members of its own bin, and writes the
+//            new rows (parent-gather / trie-advance) and the back-pointers.
+// The tiles of a request and its merge run on one XCD (workgroups are dealt to the 8
+// XCDs round-robin), so the candidates pass through that XCD's L2.
 // Selection keys are unique (the flat index breaks score ties) and every float
 // reduction has a fixed order, so results are deterministic run to run.
 #include "tcb_internal.h"
@@ -42,6 +44,9 @@ __device__ __forceinline__ bool key_better(uint32_t o, uint32_t f, uint32_t o2, 
 __device__ __forceinline__ bool key_le(uint32_t o, uint32_t f, uint32_t o_star, uint32_t f_star) {
     return o > o_star || (o == o_star && f <= f_star);
 }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ uint32_t score_bin(float sref, float s) {
     const float d = (sref - s) * kBinRes;
@@ -85,18 +90,19 @@ __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
     for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
     return v;
 }
-__device__ __forceinline__ uint32_t wave_sum_u(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
-    return v;
+// Inclusive scan over the 64 lanes of a wave with DPP: shifts inside each row of 16
+// lanes, then the last lane of a row is broadcast into the following rows.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
 }
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
-        if (lane >= o) x += y;
-    }
+    x += dpp_u<0x111, 0xF>(x);   // row_shr:1
+    x += dpp_u<0x112, 0xF>(x);   // row_shr:2
+    x += dpp_u<0x114, 0xF>(x);   // row_shr:4
+    x += dpp_u<0x118, 0xF>(x);   // row_shr:8
+    x += dpp_u<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_u<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
     return x;
 }
 
@@ -333,12 +339,6 @@ __device__ __forceinline__ void load_row(const void *logits, int64_t ld, int slo
 }
 
 // ---------------------------------------------------------------------- shared memory
-struct TileSmem {
-    uint32_t hist[kBins];                          // bin counts, then inclusive cumulative
-    uint32_t cmask[kWaves][kRowsPerWave][8];       // child masks built from CSR lists
-    uint32_t part[kWaves];
-    uint32_t bt, ovf, pad[2];
-};
 struct MergeSmem {
     float s[kMergeCap];
     uint32_t f[kMergeCap];
@@ -348,14 +348,10 @@ struct MergeSmem {
     uint32_t toff[kMaxTilesPerReq + 1];            // staged entries before each tile
     uint32_t bstar, cnt, pad[2];
 };
-union StepSmem {
-    TileSmem a;
-    MergeSmem b;
-};
 
 // ---------------------------------------------------------------------- merge
-// Run by the last tile of request q to arrive. Every tile's kept candidates are in its
-// region of cs/cf/cn grouped by bin, with its cumulative kept counts in tcum.
+// One workgroup per request (k_merge). Every tile's kept candidates are in its region
+// of cs/cf/cn grouped by bin, with its cumulative kept counts in tcum.
 __device__ void merge_request(const WaveDev &W, int q, const ReqRec &rec, int rp, int ntile, float sref,
                               MergeSmem &M, SelSmem &sel) {
     const int tid = threadIdx.x;
@@ -509,18 +505,59 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqRec &rec, int rp
         nr.level = level + 1;
         nr.par = np;
         W.rec[rp ^ 1][q] = nr;
-        W.done[q] = 0;
     }
 }
 
-// ---------------------------------------------------------------------- step kernel
+__global__ __launch_bounds__(kThreads) void k_merge(TrieDev T, WaveDev W, int rp, int n_req) {
+    __shared__ MergeSmem M;
+    __shared__ SelSmem sel;
+    const int q = blockIdx.x;
+    if (q >= n_req) return;
+    const ReqRec rec = W.rec[rp][q];
+    if (rec.status != kReqActive || rec.level >= T.L || rec.rows <= 0) return;   // carried over by k_tile
+    const int ntile = (rec.rows + kTileRows - 1) / kTileRows;
+    merge_request(W, q, rec, rp, ntile, W.score[rec.par][rec.base], M, sel);
+}
+
+// ---------------------------------------------------------------------- tile kernel
+// Per tile of 64 rows: masked log-softmax, then a superset of the tile's top-n.
+//   rows  a wave takes its 4 rows either densely (each lane scores its 16 codes against
+//         the 256-bit child mask; used where rows have many children) or sparsely (at
+//         CSR depths when every row of the wave has at most 64 children: the row is
+//         staged in LDS and each lane scores children j, j+16, j+32, j+48 of the CSR
+//         list). Both give the same value for every candidate.
+//   pick  1. prefilter: the best candidate of each lane is one sample; the bin b_L where
+//            the samples' count reaches n bounds the tile's n-th best from below, so a
+//            candidate in a bin > b_L cannot make the request's top-n either;
+//         2. the survivors are compacted into LDS and binned exactly; the tile keeps every
+//            bin down to the one where its survivor count reaches n and writes them
+//            grouped by bin, with its cumulative bin counts.
+//   If the prefilter leaves more than kTileCap survivors (ties, or n above the number of
+//   lanes), an exact selection over all candidates keeps exactly the tile's top-n.
+union alignas(16) TileBuf {
+    float xs[kTileRows][256];                      // rows staged for the sparse path
+    struct {
+        float s[kTileCap];                         // survivors: score
+        uint32_t f[kTileCap];                      //   flat r * 256 + c
+        int32_t n[kTileCap];                       //   child node
+    } c;
+};
+struct TileSmem {
+    TileBuf buf;
+    uint32_t cmask[kWaves][kRowsPerWave][8];       // child masks built from CSR lists
+    uint32_t hist[kBins];                          // bin counts, then inclusive cumulative
+    uint32_t part[kWaves];
+    uint32_t nsurv, bL, bt, tot;
+};
+
+constexpr int kSparseMax = 64;                     // children per row on the sparse path
+
 template <int DT, int NORM, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_step(TrieDev T, WaveDev W, int rp, int n_req,
+__global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp, int n_req,
                                                    const void *__restrict__ logits, int64_t ld) {
     constexpr int CH = Lay<DT>::CH, CW = Lay<DT>::CW, SPAN = 256 / CH, WPC = SPAN / 32;
-    __shared__ StepSmem sm;
+    __shared__ TileSmem A;
     __shared__ SelSmem sel;
-    __shared__ uint32_t s_last;
 
     const int tid = threadIdx.x;
     const int MT = W.MT;
@@ -536,16 +573,20 @@ __global__ __launch_bounds__(kThreads) void k_step(TrieDev T, WaveDev W, int rp,
     const int ntile = (rec.rows + kTileRows - 1) / kTileRows;
     if (tile >= ntile) return;
 
-    TileSmem &A = sm.a;
     const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, j = lane & 15;
     const int level = rec.level, cp = rec.par;
-    const int r = tile * kTileRows + wave * kRowsPerWave + g;   // local rank of this lane's row
+    const int rt = wave * kRowsPerWave + g;                   // row within the tile
+    const int r = tile * kTileRows + rt;                       // local rank in the request
     const bool live = r < rec.rows;
+    const bool wave_live = tile * kTileRows + wave * kRowsPerWave < rec.rows;
     const int V = T.V;
+    const uint32_t width = (uint32_t)rec.width;
     A.hist[tid] = 0u;
     if (tid == 0) {
+        A.nsurv = 0u;
+        A.bL = kBins - 1;
         A.bt = kBins - 1;
-        A.ovf = 0u;
+        A.tot = 0u;
     }
 
     // 1. row state and logits (all issued before any use)
@@ -562,8 +603,8 @@ __global__ __launch_bounds__(kThreads) void k_step(TrieDev T, WaveDev W, int rp,
         load_row<DT, VEC>(logits, ld, slot, j, V, x);
     }
 
-    // 2. the row's child set as a 256-bit mask
-    const bool dense = level < T.mask_depths;
+    // 2. the row's node: child id range, and the dense mask at shallow depths
+    const bool dense_depth = level < T.mask_depths;
     const uint32_t lo_id = T.off[level], hi_id = T.off[level + 1];
     bool ok = false;
     uint32_t cb = 0u, ce = 0u;
@@ -575,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void k_step(TrieDev T, WaveDev W, int rp,
         if (n >= lo_id && n < hi_id) {
             ok = true;
             cb = T.child_begin[n];
-            if (dense) {
+            if (dense_depth) {
                 const u32x4 *mp = reinterpret_cast<const u32x4 *>(T.mask + (size_t)n * 8);
                 const u32x4 a = mp[0], b = mp[1];
 #pragma unroll
@@ -590,31 +631,115 @@ __global__ __launch_bounds__(kThreads) void k_step(TrieDev T, WaveDev W, int rp,
             atomicOr(W.err, kErrBadNode);
         }
     }
-    if (!dense) {
-        uint32_t *cm = A.cmask[wave][g];
-        if (j < 8) cm[j] = 0u;
-        wave_lds_sync();
-        if (ok) {
-            for (uint32_t a = (cb & ~3u) + 4u * (uint32_t)j; a < ce; a += 64u) {
-                const uint32_t wv = *reinterpret_cast<const uint32_t *>(T.child_code + a);
+    if (W.validate && live) {
+        bool bad = false;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t idx = a + (uint32_t)k;
-                    if (idx >= cb && idx < ce) {
-                        const uint32_t c = (wv >> (8 * k)) & 255u;
-                        atomicOr(&cm[c >> 5], 1u << (c & 31));
-                    }
-                }
+        for (int e = 0; e < kElems; ++e)
+            if (code_of<DT>(e, j) < V && !isfinite(x[e])) bad = true;
+        if (bad) atomicOr(W.err, kErrNonFinite);
+    }
+    // sparse rows: every row of the wave at a CSR depth with at most kSparseMax children
+    const bool sparse = NORM == TCB_NORM_CHILDREN && !dense_depth && wave_live &&
+                        __ballot(ok && ce - cb > (uint32_t)kSparseMax) == 0ull;
+
+    // 3. candidates of this lane: up to 16 slots (dense) or 4 slots (sparse), as score,
+    //    validity bit, code and child node
+    float cand[kElems];
+    uint32_t valid = 0u;
+    uint32_t ccode[4] = {0u, 0u, 0u, 0u};              // sparse: codes of slots 0..3
+    uint32_t rk0[CH], sub[CH];                        // dense: child bits and ranks per chunk
+#pragma unroll
+    for (int i = 0; i < CH; ++i) rk0[i] = sub[i] = 0u;
+    float lmax = -INFINITY;                           // this lane's best candidate
+    if (sparse) {
+        // stage the row in LDS; lane j scores children j + 16 i of the CSR list
+        float *row = A.buf.xs[rt];
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+#pragma unroll
+            for (int q4 = 0; q4 < CW; q4 += 4) {
+                f32x4 v;
+                v[0] = x[i * CW + q4 + 0];
+                v[1] = x[i * CW + q4 + 1];
+                v[2] = x[i * CW + q4 + 2];
+                v[3] = x[i * CW + q4 + 3];
+                *reinterpret_cast<f32x4 *>(row + i * SPAN + j * CW + q4) = v;
+            }
+        const uint32_t f = ok ? ce - cb : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t k = (uint32_t)j + 16u * (uint32_t)i;
+            if (k < f) {
+                ccode[i] = T.child_code[cb + k];
+                valid |= 1u << i;
             }
         }
         wave_lds_sync();
+        float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 8; ++w) m[w] = cm[w];
-    }
-
-    // 3. this lane's child bits and the rank of its first code among the children
-    uint32_t sub[CH], rk0[CH];
-    {
+        for (int i = 0; i < 4; ++i) {
+            cand[i] = ((valid >> i) & 1u) ? row[ccode[i]] : -INFINITY;
+            mx = fmaxf(mx, cand[i]);
+        }
+        lmax = mx;
+        mx = row16_max(mx);
+        const float mxl = mx * kLog2e;
+        // The sum of exponentials follows the dense layout's order exactly (each lane adds
+        // its 16 codes in element order, then the 16-lane tree; absent children add exact
+        // zeros), so both paths give bit-identical results: the children's terms are put
+        // back at their code positions and summed the dense way.
+        wave_lds_sync();
+        const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+#pragma unroll
+            for (int q4 = 0; q4 < CW; q4 += 4) *reinterpret_cast<f32x4 *>(row + i * SPAN + j * CW + q4) = zero4;
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if ((valid >> i) & 1u) row[ccode[i]] = __builtin_amdgcn_exp2f(fmaf(cand[i], kLog2e, -mxl));
+        wave_lds_sync();
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+#pragma unroll
+            for (int q4 = 0; q4 < CW; q4 += 4) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(row + i * SPAN + j * CW + q4);
+                sum += v[0];
+                sum += v[1];
+                sum += v[2];
+                sum += v[3];
+            }
+        sum = row16_sum(sum);
+        const float lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cand[i] = sr + (cand[i] - lse);
+        lmax = sr + (lmax - lse);
+#pragma unroll
+        for (int i = 4; i < kElems; ++i) cand[i] = -INFINITY;
+    } else if (wave_live) {
+        if (!dense_depth) {
+            // a CSR list with many children: build the 256-bit mask in LDS
+            uint32_t *cm = A.cmask[wave][g];
+            if (j < 8) cm[j] = 0u;
+            wave_lds_sync();
+            if (ok) {
+                for (uint32_t a = (cb & ~3u) + 4u * (uint32_t)j; a < ce; a += 64u) {
+                    const uint32_t wv = *reinterpret_cast<const uint32_t *>(T.child_code + a);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t idx = a + (uint32_t)k;
+                        if (idx >= cb && idx < ce) {
+                            const uint32_t c = (wv >> (8 * k)) & 255u;
+                            atomicOr(&cm[c >> 5], 1u << (c & 31));
+                        }
+                    }
+                }
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int w = 0; w < 8; ++w) m[w] = cm[w];
+        }
         uint32_t P[8];
         P[0] = 0u;
 #pragma unroll
@@ -630,149 +755,177 @@ __global__ __launch_bounds__(kThreads) void k_step(TrieDev T, WaveDev W, int rp,
             }
             sub[i] = ok ? (mw >> off) & ((1u << CW) - 1u) : 0u;
             rk0[i] = pw + (uint32_t)__popc(mw & ((1u << off) - 1u));
+            valid |= sub[i] << (i * CW);
         }
-    }
-
-    // 4. masked log-softmax; candidate scores overwrite the logits
-    if (W.validate && live) {
-        bool bad = false;
+        uint32_t sup = valid;
+        if constexpr (NORM == TCB_NORM_LEVEL) {
+            sup = 0u;
 #pragma unroll
-        for (int e = 0; e < kElems; ++e)
-            if (code_of<DT>(e, j) < V && !isfinite(x[e])) bad = true;
-        if (bad) atomicOr(W.err, kErrNonFinite);
+            for (int e = 0; e < kElems; ++e) sup |= (ok && code_of<DT>(e, j) < V) ? (1u << e) : 0u;
+        }
+        // masked log-softmax: codes outside the support become -inf
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) x[e] = ((sup >> e) & 1u) ? x[e] : -INFINITY;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) mx = fmaxf(mx, x[e]);
+        if constexpr (NORM == TCB_NORM_CHILDREN) {
+            lmax = mx;
+        } else {
+#pragma unroll
+            for (int e = 0; e < kElems; ++e) lmax = fmaxf(lmax, ((valid >> e) & 1u) ? x[e] : -INFINITY);
+        }
+        mx = row16_max(mx);
+        const float mxl = mx * kLog2e;
+        float sum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) sum += __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -mxl));
+        sum = row16_sum(sum);
+        const float lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) cand[e] = sr + (x[e] - lse);
+        lmax = sr + (lmax - lse);
     }
-    auto in_support = [&](int e) -> bool {
-        if constexpr (NORM == TCB_NORM_CHILDREN) return (sub[e / CW] >> (e % CW)) & 1u;
-        else return ok && code_of<DT>(e, j) < V;
+    const int ns_lane = sparse ? 4 : kElems;           // slots in use (wave-uniform)
+    auto flat_of = [&](int e) -> uint32_t {
+        const uint32_t c = sparse ? ccode[e & 3] : (uint32_t)code_of<DT>(e, j);
+        return (uint32_t)r * 256u + c;
     };
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < kElems; ++e)
-        if (in_support(e)) mx = fmaxf(mx, x[e]);
-    mx = row16_max(mx);
-    float sum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < kElems; ++e)
-        if (in_support(e)) sum += __expf(x[e] - mx);
-    sum = row16_sum(sum);
-    const float lse = mx + __logf(sum);
-    uint32_t valid = 0u;
-#pragma unroll
-    for (int i = 0; i < CH; ++i)
-#pragma unroll
-        for (int q2 = 0; q2 < CW; ++q2) {
-            const int e = i * CW + q2;
-            x[e] = sr + (x[e] - lse);
-            valid |= ((sub[i] >> q2) & 1u) << e;
-        }
-    auto flat_of = [&](int e) -> uint32_t { return (uint32_t)r * 256u + (uint32_t)code_of<DT>(e, j); };
     auto node_of = [&](int e) -> int32_t {
+        if (sparse) return (int32_t)(cb + (uint32_t)j + 16u * (uint32_t)(e & 3));
         const int i = e / CW, q2 = e % CW;
         return (int32_t)(cb + rk0[i] + (uint32_t)__popc(sub[i] & ((1u << q2) - 1u)));
     };
 
-    // 5. histogram over the request-wide bins; the atomic's return value is the
-    //    candidate's index inside its bin. The overflow bin is counted per wave.
+    // 4. prefilter: histogram of the lanes' best candidates, bin b_L where it reaches n
+    __syncthreads();   // the zeroed histogram and counters are visible; the staged rows are read
+    if (valid) atomicAdd(&A.hist[score_bin(sref, lmax)], 1u);
     __syncthreads();
-    uint32_t wb[kElems];
     {
-        uint32_t novf = 0u;
-#pragma unroll
-        for (int e = 0; e < kElems; ++e) {
-            wb[e] = 0u;
-            if ((valid >> e) & 1u) {
-                const uint32_t b = score_bin(sref, x[e]);
-                if (b < (uint32_t)(kBins - 1)) wb[e] = atomicAdd(&A.hist[b], 1u);
-                else ++novf;
-            }
-        }
-        novf = wave_sum_u(novf);
-        if (lane == 0 && novf) atomicAdd(&A.hist[kBins - 1], novf);
+        const uint32_t h = A.hist[tid];
+        const uint32_t C = block_incl_scan<kThreads>(h, A.part);
+        if (C >= width && C - h < width) A.bL = (uint32_t)tid;
+        A.hist[tid] = 0u;
     }
     __syncthreads();
-    const uint32_t width = (uint32_t)rec.width;
-    uint32_t h = A.hist[tid];
-    uint32_t C = block_incl_scan<kThreads>(h, A.part);
-    if (C >= width && C - h < width) A.bt = (uint32_t)tid;   // first bin reaching n
-    A.hist[tid] = C;
-    __syncthreads();
-    uint32_t bt = A.bt;
-    uint32_t kept = A.hist[bt];
-    uint32_t keep = 0u;
-    const int CAPT = W.CAPT;
+    const uint32_t bL = A.bL;
 
-    if (kept <= (uint32_t)CAPT) {
+    // 5. survivors (bin <= b_L) compacted into LDS
+    uint32_t surv = 0u;
 #pragma unroll
-        for (int e = 0; e < kElems; ++e)
-            if (((valid >> e) & 1u) && score_bin(sref, x[e]) <= bt) keep |= 1u << e;
-        if (bt == (uint32_t)(kBins - 1)) {
-            // the overflow bin is kept: give its members positions, a wave at a time
+    for (int e = 0; e < kElems; ++e)
+        if (e < ns_lane && ((valid >> e) & 1u) && score_bin(sref, cand[e]) <= bL) surv |= 1u << e;
+    {
+        const uint32_t cnt = (uint32_t)__popc(surv);
+        const uint32_t incl = wave_incl_scan(cnt);
+        uint32_t wbase = 0u;
+        if (lane == 63 && incl) wbase = atomicAdd(&A.nsurv, incl);
+        wbase = (uint32_t)__shfl((int)wbase, 63, 64);
+        uint32_t pos = wbase + incl - cnt;
+        if (surv) {
 #pragma unroll
             for (int e = 0; e < kElems; ++e) {
-                const bool pe = ((keep >> e) & 1u) && score_bin(sref, x[e]) == (uint32_t)(kBins - 1);
-                const uint64_t bal = __ballot(pe);
-                if (bal) {
-                    uint32_t b0 = 0u;
-                    if (lane == 0) b0 = atomicAdd(&A.ovf, (uint32_t)__popcll(bal));
-                    b0 = (uint32_t)__shfl((int)b0, 0, 64);
-                    if (pe) wb[e] = b0 + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+                if (e < ns_lane && ((surv >> e) & 1u)) {
+                    if (pos < (uint32_t)kTileCap) {
+                        A.buf.c.s[pos] = cand[e];
+                        A.buf.c.f[pos] = flat_of(e);
+                        A.buf.c.n[pos] = node_of(e);
+                    }
+                    ++pos;
                 }
             }
         }
+    }
+    __syncthreads();
+    const uint32_t ns = A.nsurv;
+    const int CAPT = W.CAPT;
+    const size_t reg = ((size_t)q * MT + tile) * (size_t)CAPT;
+
+    if (ns <= (uint32_t)kTileCap) {
+        // 6. exact bins of the survivors; keep bins down to where their count reaches n
+        constexpr int U = kTileCap / kThreads;
+        uint32_t wb[U], bn[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t p = (uint32_t)(tid + u * kThreads);
+            bn[u] = kBins;
+            wb[u] = 0u;
+            if (p < ns) {
+                bn[u] = score_bin(sref, A.buf.c.s[p]);
+                wb[u] = atomicAdd(&A.hist[bn[u]], 1u);
+            }
+        }
+        __syncthreads();
+        const uint32_t h = A.hist[tid];
+        const uint32_t C = block_incl_scan<kThreads>(h, A.part);
+        if (C >= width && C - h < width) A.bt = (uint32_t)tid;
+        A.hist[tid] = C;
+        __syncthreads();
+        const uint32_t bt = A.bt;
+        const uint32_t kept = A.hist[bt];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t p = (uint32_t)(tid + u * kThreads);
+            if (p < ns && bn[u] <= bt) {
+                const uint32_t dst = (bn[u] ? A.hist[bn[u] - 1] : 0u) + wb[u];
+                if (dst < kept) {
+                    W.cs[reg + dst] = A.buf.c.s[p];
+                    W.cf[reg + dst] = A.buf.c.f[p];
+                    W.cn[reg + dst] = A.buf.c.n[p];
+                } else {
+                    atomicOr(W.err, kErrInternal);
+                }
+            }
+        }
+        W.tcum[((size_t)q * MT + tile) * kBins + tid] = (uint16_t)min(C, kept);
     } else {
-        // exact path (a huge boundary bin, e.g. exact ties): keep exactly the tile's top n
+        // exact path: keep exactly the tile's top min(n, #candidates)
         if (tid == 0) atomicOr(W.err, kInfoTileExact);
-        const uint32_t kt = min(width, A.hist[kBins - 1]);
+        const uint32_t nv = (uint32_t)__popc(valid);
+        const uint32_t total = block_incl_scan<kThreads>(nv, A.part);
+        if (tid == kThreads - 1) A.tot = total;
+        __syncthreads();
+        const uint32_t kt = min(width, A.tot);
         auto each = [&](auto fn) {
 #pragma unroll
             for (int e = 0; e < kElems; ++e)
-                if ((valid >> e) & 1u) fn(f2ord(x[e]), flat_of(e));
+                if (e < ns_lane && ((valid >> e) & 1u)) fn(f2ord(cand[e]), flat_of(e));
         };
         uint32_t o_star, f_star;
         block_select<kThreads>(each, kt, sel, o_star, f_star, W.err);
+        uint32_t keep = 0u;
 #pragma unroll
         for (int e = 0; e < kElems; ++e)
-            if (((valid >> e) & 1u) && key_le(f2ord(x[e]), flat_of(e), o_star, f_star)) keep |= 1u << e;
-        A.hist[tid] = 0u;
-        __syncthreads();
+            if (e < ns_lane && ((valid >> e) & 1u) && key_le(f2ord(cand[e]), flat_of(e), o_star, f_star))
+                keep |= 1u << e;
+        uint32_t wbe[kElems];
 #pragma unroll
-        for (int e = 0; e < kElems; ++e)
-            if ((keep >> e) & 1u) wb[e] = atomicAdd(&A.hist[score_bin(sref, x[e])], 1u);
+        for (int e = 0; e < kElems; ++e) {
+            wbe[e] = 0u;
+            if ((keep >> e) & 1u) wbe[e] = atomicAdd(&A.hist[score_bin(sref, cand[e])], 1u);
+        }
         __syncthreads();
-        h = A.hist[tid];
-        C = block_incl_scan<kThreads>(h, A.part);
+        const uint32_t h = A.hist[tid];
+        const uint32_t C = block_incl_scan<kThreads>(h, A.part);
         A.hist[tid] = C;
         __syncthreads();
-        kept = A.hist[kBins - 1];
-    }
-
-    // 6. kept candidates, grouped by bin, and the tile's cumulative counts
-    const size_t reg = ((size_t)q * MT + tile) * (size_t)CAPT;
+        const uint32_t kept = A.hist[kBins - 1];
 #pragma unroll
-    for (int e = 0; e < kElems; ++e) {
-        if ((keep >> e) & 1u) {
-            const uint32_t b = score_bin(sref, x[e]);
-            const uint32_t p = (b ? A.hist[b - 1] : 0u) + wb[e];
-            if (p < kept) {
-                W.cs[reg + p] = x[e];
-                W.cf[reg + p] = flat_of(e);
-                W.cn[reg + p] = node_of(e);
-            } else {
-                atomicOr(W.err, kErrInternal);
+        for (int e = 0; e < kElems; ++e) {
+            if ((keep >> e) & 1u) {
+                const uint32_t b = score_bin(sref, cand[e]);
+                const uint32_t dst = (b ? A.hist[b - 1] : 0u) + wbe[e];
+                if (dst < kept && dst < (uint32_t)CAPT) {
+                    W.cs[reg + dst] = cand[e];
+                    W.cf[reg + dst] = flat_of(e);
+                    W.cn[reg + dst] = node_of(e);
+                } else {
+                    atomicOr(W.err, kErrInternal);
+                }
             }
         }
+        W.tcum[((size_t)q * MT + tile) * kBins + tid] = (uint16_t)C;
     }
-    W.tcum[((size_t)q * MT + tile) * kBins + tid] = (uint16_t)min(C, kept);
-
-    // 7. arrival; the last tile of the request merges
-    __syncthreads();
-    if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(&W.done[q], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == ntile - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    merge_request(W, q, rec, rp, ntile, sref, sm.b, sel);
 }
 
 // ---------------------------------------------------------------------- small kernels
@@ -782,7 +935,6 @@ __global__ void k_clear_wave(WaveDev W) {
         const ReqRec r{};
         W.rec[0][i] = r;
         W.rec[1][i] = r;
-        W.done[i] = 0;
     }
     if (i == 0) *W.err = 0u;
 }
@@ -879,30 +1031,36 @@ hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s) {
 }
 
 template <int DT, int NORM, bool VEC>
-static void launch_step_t(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *logits, int64_t ld,
+static void launch_tile_t(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *logits, int64_t ld,
                           hipStream_t s) {
     const int groups = (n_req + 7) / 8;
-    hipLaunchKernelGGL((k_step<DT, NORM, VEC>), dim3(8 * groups * w.MT), dim3(kThreads), 0, s, t, w, rp, n_req,
+    hipLaunchKernelGGL((k_tile<DT, NORM, VEC>), dim3(8 * groups * w.MT), dim3(kThreads), 0, s, t, w, rp, n_req,
                        logits, ld);
 }
 
-hipError_t launch_step(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *logits, int64_t ld,
+hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *logits, int64_t ld,
                        int dtype, hipStream_t s) {
     if (n_req <= 0) return hipSuccess;
     // 16-byte row pieces: ld a multiple of 4 (fp32) or 8 (bf16) elements, 16-byte base
     const bool vec = t.V == 256 && (ld % (dtype == TCB_F32 ? 4 : 8)) == 0 && ((uintptr_t)logits % 16) == 0;
     const bool lvl = w.norm == TCB_NORM_LEVEL;
     if (dtype == TCB_F32) {
-        if (vec) lvl ? launch_step_t<TCB_F32, TCB_NORM_LEVEL, true>(t, w, rp, n_req, logits, ld, s)
-                     : launch_step_t<TCB_F32, TCB_NORM_CHILDREN, true>(t, w, rp, n_req, logits, ld, s);
-        else lvl ? launch_step_t<TCB_F32, TCB_NORM_LEVEL, false>(t, w, rp, n_req, logits, ld, s)
-                 : launch_step_t<TCB_F32, TCB_NORM_CHILDREN, false>(t, w, rp, n_req, logits, ld, s);
+        if (vec) lvl ? launch_tile_t<TCB_F32, TCB_NORM_LEVEL, true>(t, w, rp, n_req, logits, ld, s)
+                     : launch_tile_t<TCB_F32, TCB_NORM_CHILDREN, true>(t, w, rp, n_req, logits, ld, s);
+        else lvl ? launch_tile_t<TCB_F32, TCB_NORM_LEVEL, false>(t, w, rp, n_req, logits, ld, s)
+                 : launch_tile_t<TCB_F32, TCB_NORM_CHILDREN, false>(t, w, rp, n_req, logits, ld, s);
     } else {
-        if (vec) lvl ? launch_step_t<TCB_BF16, TCB_NORM_LEVEL, true>(t, w, rp, n_req, logits, ld, s)
-                     : launch_step_t<TCB_BF16, TCB_NORM_CHILDREN, true>(t, w, rp, n_req, logits, ld, s);
-        else lvl ? launch_step_t<TCB_BF16, TCB_NORM_LEVEL, false>(t, w, rp, n_req, logits, ld, s)
-                 : launch_step_t<TCB_BF16, TCB_NORM_CHILDREN, false>(t, w, rp, n_req, logits, ld, s);
+        if (vec) lvl ? launch_tile_t<TCB_BF16, TCB_NORM_LEVEL, true>(t, w, rp, n_req, logits, ld, s)
+                     : launch_tile_t<TCB_BF16, TCB_NORM_CHILDREN, true>(t, w, rp, n_req, logits, ld, s);
+        else lvl ? launch_tile_t<TCB_BF16, TCB_NORM_LEVEL, false>(t, w, rp, n_req, logits, ld, s)
+                 : launch_tile_t<TCB_BF16, TCB_NORM_CHILDREN, false>(t, w, rp, n_req, logits, ld, s);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, int n_req, hipStream_t s) {
+    if (n_req <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_merge, dim3(n_req), dim3(kThreads), 0, s, t, w, rp, n_req);
     return hipGetLastError();
 }
 
@@ -918,7 +1076,7 @@ hipError_t launch_export(const WaveDev &w, int rp, int32_t *node, float *score, 
     return hipGetLastError();
 }
 
-hipError_t launch_step_lmhead(const TrieDev &, const WaveDev &, int, int, const void *, int64_t, int, const void *,
+hipError_t launch_tile_lmhead(const TrieDev &, const WaveDev &, int, int, const void *, int64_t, int, const void *,
                               hipStream_t) {
     return hipErrorNotSupported;
 }

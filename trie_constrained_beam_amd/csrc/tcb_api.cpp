@@ -34,7 +34,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
     int32_t MT = 0, CAPT = 0;
-    size_t node[2]{}, score[2]{}, parent_slot = 0, hist = 0, rec[2]{}, done = 0;
+    size_t node[2]{}, score[2]{}, parent_slot = 0, hist = 0, rec[2]{};
     size_t cs = 0, cf = 0, cn = 0, tcum = 0, err = 0;
     size_t fin_sids = 0, fin_scores = 0, fin_items = 0, fin_counts = 0, total = 0;
 };
@@ -42,7 +42,7 @@ struct Layout {
 Layout make_layout(int L, int S, int R, int Bmax) {
     Layout l;
     l.MT = (Bmax + tcb::kTileRows - 1) / tcb::kTileRows;
-    l.CAPT = std::min(Bmax + tcb::kTileSlack, tcb::kTileRows * TCB_MAX_V);
+    l.CAPT = tcb::kTileCap;
     size_t o = 0;
     auto take = [&](size_t bytes) {
         size_t at = o;
@@ -58,7 +58,6 @@ Layout make_layout(int L, int S, int R, int Bmax) {
     l.hist = take((size_t)L * s * 4);
     l.rec[0] = take(r * sizeof(tcb::ReqRec));
     l.rec[1] = take(r * sizeof(tcb::ReqRec));
-    l.done = take(r * 4);
     const size_t ncand = r * (size_t)l.MT * (size_t)l.CAPT;
     l.cs = take(ncand * 4);
     l.cf = take(ncand * 4);
@@ -262,7 +261,6 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
     w.hist = (uint32_t *)(ws + l.hist);
     w.rec[0] = (tcb::ReqRec *)(ws + l.rec[0]);
     w.rec[1] = (tcb::ReqRec *)(ws + l.rec[1]);
-    w.done = (int32_t *)(ws + l.done);
     w.cs = (float *)(ws + l.cs);
     w.cf = (uint32_t *)(ws + l.cf);
     w.cn = (int32_t *)(ws + l.cn);
@@ -349,26 +347,42 @@ static void step_done(tcb_beams *b) {
         if (q.used && q.level < b->L) q.level++;
 }
 
+// Launch the tile kernel through `tile`, then the merge kernel; with timing on, HIP
+// events bracket the two kernels separately.
+}  // extern "C"
+
+template <class TileLaunch>
+static tcb_status run_step(tcb_beams *b, hipStream_t s, TileLaunch tile) {
+    const int nr = n_req_hw(b);
+    const bool timed = b->timing_used < b->timing_cap;
+    hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 3] : nullptr;
+    hipError_t e = timed ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (e == hipSuccess) e = tile(nr);
+    if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
+    if (timed) e = hipEventRecord(ev[1], s);
+    if (e == hipSuccess) e = tcb::launch_merge(b->tdev, b->w, b->rp, nr, s);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    if (timed) {
+        e = hipEventRecord(ev[2], s);
+        if (e != hipSuccess) return hip_fail(e, "event record");
+        b->timing_used++;
+    }
+    step_done(b);
+    return TCB_OK;
+}
+
+extern "C" {
+
 tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t dtype, void *stream) {
     if (!b || !d_logits) return set_error(TCB_E_ARG, "beam_step: null pointer");
     if (dtype != TCB_F32 && dtype != TCB_BF16) return set_error(TCB_E_ARG, "beam_step: bad dtype");
     if (ld < b->V) return set_error(TCB_E_ARG, "beam_step: ld < V");
     tcb_status st = step_common(b);
     if (st) return st;
-    const int nr = n_req_hw(b);
     hipStream_t s = (hipStream_t)stream;
-    const bool timed = b->timing_used < b->timing_cap;
-    hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 2] : nullptr;
-    hipError_t e = timed ? hipEventRecord(ev[0], s) : hipSuccess;
-    if (e == hipSuccess) e = tcb::launch_step(b->tdev, b->w, b->rp, nr, d_logits, ld, dtype, s);
-    if (e != hipSuccess) return hip_fail(e, "step launch");
-    if (timed) {
-        e = hipEventRecord(ev[1], s);
-        if (e != hipSuccess) return hip_fail(e, "event record");
-        b->timing_used++;
-    }
-    step_done(b);
-    return TCB_OK;
+    return run_step(b, s, [&](int nr) {
+        return tcb::launch_tile(b->tdev, b->w, b->rp, nr, d_logits, ld, dtype, s);
+    });
 }
 
 tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_hidden, int32_t H,
@@ -380,21 +394,10 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
         return set_error(TCB_E_ARG, "beam_step_lmhead: hidden/weight must be 16-byte aligned, ld % 8 == 0");
     tcb_status st = step_common(b);
     if (st) return st;
-    const int nr = n_req_hw(b);
     hipStream_t s = (hipStream_t)stream;
-    const bool timed = b->timing_used < b->timing_cap;
-    hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 2] : nullptr;
-    hipError_t e = timed ? hipEventRecord(ev[0], s) : hipSuccess;
-    if (e == hipSuccess)
-        e = tcb::launch_step_lmhead(b->tdev, b->w, b->rp, nr, d_hidden, ld_hidden, H, d_weight, s);
-    if (e != hipSuccess) return hip_fail(e, "step_lmhead launch");
-    if (timed) {
-        e = hipEventRecord(ev[1], s);
-        if (e != hipSuccess) return hip_fail(e, "event record");
-        b->timing_used++;
-    }
-    step_done(b);
-    return TCB_OK;
+    return run_step(b, s, [&](int nr) {
+        return tcb::launch_tile_lmhead(b->tdev, b->w, b->rp, nr, d_hidden, ld_hidden, H, d_weight, s);
+    });
 }
 
 tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, int32_t *d_parent_slot,
@@ -491,7 +494,7 @@ tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity) {
     b->events.clear();
     b->timing_cap = 0;
     b->timing_used = 0;
-    for (int32_t i = 0; i < capacity * 2; ++i) {
+    for (int32_t i = 0; i < capacity * 3; ++i) {
         hipEvent_t e;
         hipError_t r = hipEventCreate(&e);
         if (r != hipSuccess) {
@@ -505,19 +508,22 @@ tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity) {
     return TCB_OK;
 }
 
-tcb_status tcb_beams_timing(tcb_beams *b, double *step_ms, int32_t *steps) {
-    if (!b || !step_ms || !steps) return set_error(TCB_E_ARG, "timing: null pointer");
+tcb_status tcb_beams_timing(tcb_beams *b, double *tile_ms, double *merge_ms, int32_t *steps) {
+    if (!b || !tile_ms || !merge_ms || !steps) return set_error(TCB_E_ARG, "timing: null pointer");
     if (b->timing_cap == 0) return set_error(TCB_E_STATE, "timing: not enabled");
-    double ms = 0.0;
+    double ta = 0.0, tb = 0.0;
     for (int32_t i = 0; i < b->timing_used; ++i) {
-        hipEvent_t *ev = &b->events[(size_t)i * 2];
-        hipError_t r = hipEventSynchronize(ev[1]);
-        float a = 0.f;
+        hipEvent_t *ev = &b->events[(size_t)i * 3];
+        hipError_t r = hipEventSynchronize(ev[2]);
+        float a = 0.f, c = 0.f;
         if (r == hipSuccess) r = hipEventElapsedTime(&a, ev[0], ev[1]);
+        if (r == hipSuccess) r = hipEventElapsedTime(&c, ev[1], ev[2]);
         if (r != hipSuccess) return hip_fail(r, "timing: elapsed time");
-        ms += a;
+        ta += a;
+        tb += c;
     }
-    *step_ms = ms;
+    *tile_ms = ta;
+    *merge_ms = tb;
     *steps = b->timing_used;
     return TCB_OK;
 }

@@ -26,8 +26,10 @@ constexpr int kMaxTilesPerReq = TCB_MAX_WIDTH / kTileRows;
 constexpr int kBins = 1024;
 constexpr float kBinRes = 32.0f;                      // bins per nat: 32 nats of range
 static_assert(kBins == kThreads, "one bin per thread in the scans");
-constexpr int kTileSlack = 1024;                      // tile capacity beyond the beam width
+constexpr int kTileCap = 4096;                        // survivors a tile treats exactly (and keeps)
 constexpr int kMergeCap = 4096;                       // candidates the merge stages in LDS
+static_assert(kTileCap >= TCB_MAX_WIDTH, "a tile's exact path keeps up to n_i candidates");
+static_assert(kTileCap % kThreads == 0 && kMergeCap % kThreads == 0, "whole rounds of the workgroup");
 static_assert(kMergeCap >= TCB_MAX_WIDTH, "the exact merge path stages up to n_i survivors");
 constexpr int kSelBins = 1024;                        // bins of the exact selection
 
@@ -68,7 +70,6 @@ struct WaveDev {
     int32_t *parent_slot;          // [S] parent slot at the request's last step
     uint32_t *hist;                // [L][S] back-pointer (r << 8) | c per level
     ReqRec *rec[2];                // [R] request records; a step reads one, writes the other
-    int32_t *done;                 // [R] tiles of the request that finished this step
     float *cs;                     // [R][MT][CAPT] kept candidates of every tile: score
     uint32_t *cf;                  //                                              flat r*256+c
     int32_t *cn;                   //                                              child node
@@ -93,11 +94,14 @@ struct FinBatch {
 
 hipError_t launch_clear_wave(const WaveDev &w, hipStream_t s);
 hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s);
-hipError_t launch_step(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *logits,
+// A step is the tile kernel (logits from memory, or computed by the SID-range lm_head)
+// followed by the per-request merge kernel.
+hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *logits,
                        int64_t ld, int dtype, hipStream_t s);
-hipError_t launch_step_lmhead(const TrieDev &t, const WaveDev &w, int rp, int n_req,
+hipError_t launch_tile_lmhead(const TrieDev &t, const WaveDev &w, int rp, int n_req,
                               const void *hidden, int64_t ld, int H, const void *weight,
                               hipStream_t s);
+hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, int n_req, hipStream_t s);
 hipError_t launch_finalize(const TrieDev &t, const WaveDev &w, int rp, const FinBatch &b,
                            uint8_t *sids, float *scores, int64_t *items, int32_t *counts,
                            hipStream_t s);

@@ -49,8 +49,8 @@ tcb_status tcb_trie_build_impl(const uint8_t *sids, int64_t n_items, int32_t L, 
     if (n_items <= 0) return set_error(TCB_E_ARG, "build_trie: n_items must be > 0");
     if (L < 1 || L > TCB_MAX_L) return set_error(TCB_E_RANGE, "build_trie: L must be in 1..8");
     if (V < 2 || V > TCB_MAX_V) return set_error(TCB_E_RANGE, "build_trie: V must be in 2..256");
-    if (mask_depths < 0 || mask_depths > L)
-        return set_error(TCB_E_ARG, "build_trie: mask_depths must be in 0..L");
+    if (mask_depths < TCB_MASK_AUTO || mask_depths > L)
+        return set_error(TCB_E_ARG, "build_trie: mask_depths must be TCB_MASK_AUTO or in 0..L");
     *out = nullptr;
 
     std::vector<KeyItem> ki;
@@ -77,7 +77,6 @@ tcb_status tcb_trie_build_impl(const uint8_t *sids, int64_t n_items, int32_t L, 
     if (!t) return set_error(TCB_E_ARG, "build_trie: out of host memory");
     t->L = L;
     t->V = V;
-    t->mask_depths = mask_depths;
     t->n_items = n_items;
 
     // distinct SIDs (leaves) and their lowest catalog row
@@ -113,6 +112,14 @@ tcb_status tcb_trie_build_impl(const uint8_t *sids, int64_t n_items, int32_t L, 
         t->nodes_per_depth.push_back((int64_t)P[d].size());
         t->off[d + 1] = t->off[d] + (int64_t)P[d].size();
     }
+    if (mask_depths == TCB_MASK_AUTO) {
+        // dense masks on the leading depths whose nodes have many children on average
+        mask_depths = 0;
+        while (mask_depths < L &&
+               P[mask_depths + 1].size() >= (size_t)TCB_MASK_AUTO_FANOUT * P[mask_depths].size())
+            ++mask_depths;
+    }
+    t->mask_depths = mask_depths;
     const int64_t n_nodes = t->off[L + 1];
     const int64_t n_internal = t->off[L];
     if (n_nodes >= (int64_t)0xFFFFFFF0) {
