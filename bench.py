@@ -144,13 +144,13 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     if graphs is None:
-        tile_ms, merge_ms, n_timed = beams.timing()
+        _, tile_ms, merge_ms, n_timed = beams.timing()
     else:
         # the same decodes again, eagerly, with per-kernel events (graph replays hide them)
         beams.enable_timing(args.steps * L)
         for d in range(args.steps):
             decode(d % n_copies)
-        tile_ms, merge_ms, n_timed = beams.timing()
+        _, tile_ms, merge_ms, n_timed = beams.timing()
     beams.enable_timing(0)
 
     value = rows_x_steps * args.steps / elapsed

@@ -168,9 +168,13 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
 /* Same step with the logits computed on chip by the SID-range lm_head ([FR]
  * Decoding: lm_head only over the SID token range):
  *   x[slot][c] = sum_h hidden[slot][h] * W[level][c][h], fp32 accumulate, no bias.
- *   d_hidden  device bf16 [max_slots][ld_hidden], ld_hidden >= H, H % 64 == 0
- *   d_weight  device bf16 [L][V][H] contiguous (one [V][H] matrix per level)
- * Errors as tcb_beam_step. */
+ *   d_hidden  device bf16 [max_slots][ld_hidden], ld_hidden >= H, ld_hidden % 8 == 0,
+ *             H % 64 == 0, 16-byte aligned; row `slot` is that slot's hidden state
+ *   d_weight  device bf16 [L][256][H] contiguous (one [256][H] matrix per level),
+ *             16-byte aligned; the trie must have V = 256
+ * The logits pass through an fp32 [max_slots][256] part of the workspace; the masked
+ * log-softmax and selection are those of tcb_beam_step.
+ * Errors as tcb_beam_step; TCB_E_ARG for the shape and alignment conditions above. */
 tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_hidden,
                                 int32_t H, const void *d_weight, void *stream);
 
@@ -226,15 +230,18 @@ tcb_status tcb_beam_finalize_device(tcb_beams *b, int32_t n, const int32_t *req_
                                     uint8_t *d_sids, float *d_scores, int64_t *d_items,
                                     int32_t *d_counts, void *stream);
 
-/* Diagnostics: record HIP events on `stream` around the two kernels of each of the
- * next `capacity` steps (the tile kernel, then the per-request merge kernel); 0 stops
- * recording and releases the events. The events are created here (no device memory). */
+/* Diagnostics: record HIP events on `stream` around the kernels of each of the next
+ * `capacity` steps (the lm_head kernel of tcb_beam_step_lmhead, the tile kernel, then the
+ * per-request merge kernel); 0 stops recording and releases the events. The events are
+ * created here (no device memory). */
 tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity);
 
 /* Synchronise the recorded events and report, over the steps recorded since
- * tcb_beams_enable_timing, the summed tile-kernel and merge-kernel durations (ms) and
- * the number of steps. Errors: TCB_E_STATE (timing not enabled), TCB_E_HIP. */
-tcb_status tcb_beams_timing(tcb_beams *b, double *tile_ms, double *merge_ms, int32_t *steps);
+ * tcb_beams_enable_timing, the summed lm_head (0 for tcb_beam_step), tile-kernel and
+ * merge-kernel durations (ms) and the number of steps.
+ * Errors: TCB_E_STATE (timing not enabled), TCB_E_HIP. */
+tcb_status tcb_beams_timing(tcb_beams *b, double *head_ms, double *tile_ms, double *merge_ms,
+                            int32_t *steps);
 
 void tcb_beams_destroy(tcb_beams *b);
 

@@ -135,8 +135,8 @@ class Beams:
             raise TypeError("hidden and weight must be bfloat16")
         if hidden.dim() != 2 or hidden.stride(1) != 1 or hidden.shape[0] < self.max_slots:
             raise ValueError("hidden must be a row-major [max_slots, ld] CUDA tensor")
-        if not weight.is_contiguous() or weight.shape[0] != self.trie.L or weight.shape[1] != self.trie.V:
-            raise ValueError("weight must be a contiguous [L, V, H] tensor")
+        if not weight.is_contiguous() or weight.shape[0] != self.trie.L or weight.shape[1] != 256:
+            raise ValueError("weight must be a contiguous [L, 256, H] tensor")
         H = int(weight.shape[2])
         check(lib().tcb_beam_step_lmhead(self._h, _ptr(hidden), hidden.stride(0), H,
                                          _ptr(weight), _stream()))
@@ -176,10 +176,10 @@ class Beams:
         check(lib().tcb_beams_enable_timing(self._h, int(capacity)))
 
     def timing(self):
-        """(tile_ms, merge_ms, steps) summed over the recorded steps; synchronises."""
-        a, b, n = C.c_double(), C.c_double(), C.c_int32()
-        check(lib().tcb_beams_timing(self._h, C.byref(a), C.byref(b), C.byref(n)))
-        return float(a.value), float(b.value), int(n.value)
+        """(head_ms, tile_ms, merge_ms, steps) summed over the recorded steps; synchronises."""
+        h, a, b, n = C.c_double(), C.c_double(), C.c_double(), C.c_int32()
+        check(lib().tcb_beams_timing(self._h, C.byref(h), C.byref(a), C.byref(b), C.byref(n)))
+        return float(h.value), float(a.value), float(b.value), int(n.value)
 
     def finalize(self, req_ids):
         """Ranked beams of finished requests (host arrays); releases their slots."""

@@ -1076,9 +1076,6 @@ hipError_t launch_export(const WaveDev &w, int rp, int32_t *node, float *score, 
     return hipGetLastError();
 }
 
-hipError_t launch_tile_lmhead(const TrieDev &, const WaveDev &, int, int, const void *, int64_t, int, const void *,
-                              hipStream_t) {
-    return hipErrorNotSupported;
-}
+
 
 }  // namespace tcb

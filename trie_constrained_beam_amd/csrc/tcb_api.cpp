@@ -35,7 +35,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
     int32_t MT = 0, CAPT = 0;
     size_t node[2]{}, score[2]{}, parent_slot = 0, hist = 0, rec[2]{};
-    size_t cs = 0, cf = 0, cn = 0, tcum = 0, err = 0;
+    size_t cs = 0, cf = 0, cn = 0, tcum = 0, lmx = 0, err = 0;
     size_t fin_sids = 0, fin_scores = 0, fin_items = 0, fin_counts = 0, total = 0;
 };
 
@@ -63,6 +63,7 @@ Layout make_layout(int L, int S, int R, int Bmax) {
     l.cf = take(ncand * 4);
     l.cn = take(ncand * 4);
     l.tcum = take(r * (size_t)l.MT * tcb::kBins * 2);
+    l.lmx = take(s * 256 * 4);
     l.err = take(256);
     l.fin_sids = take(r * (size_t)Bmax * (size_t)L);
     l.fin_scores = take(r * (size_t)Bmax * 4);
@@ -265,6 +266,7 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
     w.cf = (uint32_t *)(ws + l.cf);
     w.cn = (int32_t *)(ws + l.cn);
     w.tcum = (uint16_t *)(ws + l.tcum);
+    w.lmx = (float *)(ws + l.lmx);
     w.err = (uint32_t *)(ws + l.err);
     w.S = max_slots;
     w.R = max_requests;
@@ -347,23 +349,27 @@ static void step_done(tcb_beams *b) {
         if (q.used && q.level < b->L) q.level++;
 }
 
-// Launch the tile kernel through `tile`, then the merge kernel; with timing on, HIP
-// events bracket the two kernels separately.
 }  // extern "C"
 
-template <class TileLaunch>
-static tcb_status run_step(tcb_beams *b, hipStream_t s, TileLaunch tile) {
+// Launch the optional lm_head kernel through `head` (which may launch nothing), the tile
+// kernel through `tile`, then the merge kernel. With timing on, HIP events bracket the
+// three launches separately.
+template <class HeadLaunch, class TileLaunch>
+static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLaunch tile) {
     const int nr = n_req_hw(b);
     const bool timed = b->timing_used < b->timing_cap;
-    hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 3] : nullptr;
+    hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 4] : nullptr;
     hipError_t e = timed ? hipEventRecord(ev[0], s) : hipSuccess;
+    if (e == hipSuccess) e = head(nr);
+    if (e != hipSuccess) return hip_fail(e, "lm_head kernel launch");
+    if (timed) e = hipEventRecord(ev[1], s);
     if (e == hipSuccess) e = tile(nr);
     if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
-    if (timed) e = hipEventRecord(ev[1], s);
+    if (timed) e = hipEventRecord(ev[2], s);
     if (e == hipSuccess) e = tcb::launch_merge(b->tdev, b->w, b->rp, nr, s);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     if (timed) {
-        e = hipEventRecord(ev[2], s);
+        e = hipEventRecord(ev[3], s);
         if (e != hipSuccess) return hip_fail(e, "event record");
         b->timing_used++;
     }
@@ -380,7 +386,7 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
     tcb_status st = step_common(b);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    return run_step(b, s, [&](int nr) {
+    return run_step(b, s, [](int) { return hipSuccess; }, [&](int nr) {
         return tcb::launch_tile(b->tdev, b->w, b->rp, nr, d_logits, ld, dtype, s);
     });
 }
@@ -392,12 +398,16 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
     if (ld_hidden < H) return set_error(TCB_E_ARG, "beam_step_lmhead: ld_hidden < H");
     if (((uintptr_t)d_hidden & 15) || ((uintptr_t)d_weight & 15) || (ld_hidden % 8))
         return set_error(TCB_E_ARG, "beam_step_lmhead: hidden/weight must be 16-byte aligned, ld % 8 == 0");
+    if (b->V != 256) return set_error(TCB_E_ARG, "beam_step_lmhead: needs a trie with V = 256");
     tcb_status st = step_common(b);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    return run_step(b, s, [&](int nr) {
-        return tcb::launch_tile_lmhead(b->tdev, b->w, b->rp, nr, d_hidden, ld_hidden, H, d_weight, s);
-    });
+    return run_step(
+        b, s,
+        [&](int nr) {
+            return tcb::launch_lmhead(b->tdev, b->w, b->rp, nr, d_hidden, ld_hidden, H, d_weight, b->w.lmx, s);
+        },
+        [&](int nr) { return tcb::launch_tile(b->tdev, b->w, b->rp, nr, b->w.lmx, 256, TCB_F32, s); });
 }
 
 tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, int32_t *d_parent_slot,
@@ -494,7 +504,7 @@ tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity) {
     b->events.clear();
     b->timing_cap = 0;
     b->timing_used = 0;
-    for (int32_t i = 0; i < capacity * 3; ++i) {
+    for (int32_t i = 0; i < capacity * 4; ++i) {
         hipEvent_t e;
         hipError_t r = hipEventCreate(&e);
         if (r != hipSuccess) {
@@ -508,20 +518,23 @@ tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity) {
     return TCB_OK;
 }
 
-tcb_status tcb_beams_timing(tcb_beams *b, double *tile_ms, double *merge_ms, int32_t *steps) {
-    if (!b || !tile_ms || !merge_ms || !steps) return set_error(TCB_E_ARG, "timing: null pointer");
+tcb_status tcb_beams_timing(tcb_beams *b, double *head_ms, double *tile_ms, double *merge_ms, int32_t *steps) {
+    if (!b || !head_ms || !tile_ms || !merge_ms || !steps) return set_error(TCB_E_ARG, "timing: null pointer");
     if (b->timing_cap == 0) return set_error(TCB_E_STATE, "timing: not enabled");
-    double ta = 0.0, tb = 0.0;
+    double th = 0.0, ta = 0.0, tb = 0.0;
     for (int32_t i = 0; i < b->timing_used; ++i) {
-        hipEvent_t *ev = &b->events[(size_t)i * 3];
-        hipError_t r = hipEventSynchronize(ev[2]);
-        float a = 0.f, c = 0.f;
-        if (r == hipSuccess) r = hipEventElapsedTime(&a, ev[0], ev[1]);
-        if (r == hipSuccess) r = hipEventElapsedTime(&c, ev[1], ev[2]);
+        hipEvent_t *ev = &b->events[(size_t)i * 4];
+        hipError_t r = hipEventSynchronize(ev[3]);
+        float h = 0.f, a = 0.f, c = 0.f;
+        if (r == hipSuccess) r = hipEventElapsedTime(&h, ev[0], ev[1]);
+        if (r == hipSuccess) r = hipEventElapsedTime(&a, ev[1], ev[2]);
+        if (r == hipSuccess) r = hipEventElapsedTime(&c, ev[2], ev[3]);
         if (r != hipSuccess) return hip_fail(r, "timing: elapsed time");
+        th += h;
         ta += a;
         tb += c;
     }
+    *head_ms = th;
     *tile_ms = ta;
     *merge_ms = tb;
     *steps = b->timing_used;

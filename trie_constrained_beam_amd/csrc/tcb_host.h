@@ -38,7 +38,8 @@ struct tcb_beams {
     float *d_fin_scores = nullptr;
     int64_t *d_fin_items = nullptr;
     int32_t *d_fin_counts = nullptr;
-    // optional kernel timing: 3 events per step (before the tile kernel, between, after the merge)
+    // optional kernel timing: 4 events per step (before the lm_head, before the tile kernel,
+    // before the merge, after the merge)
     std::vector<hipEvent_t> events;
     int32_t timing_cap = 0, timing_used = 0;
     ~tcb_beams() {

@@ -74,6 +74,7 @@ struct WaveDev {
     uint32_t *cf;                  //                                              flat r*256+c
     int32_t *cn;                   //                                              child node
     uint16_t *tcum;                // [R][MT][kBins] cumulative kept count of each tile by bin
+    float *lmx;                    // [S][256] logits computed by the SID-range lm_head
     uint32_t *err;                 // sticky error / info bits
     int32_t S, R, MT, CAPT, Bmax, norm, validate, pad;
 };
@@ -94,13 +95,12 @@ struct FinBatch {
 
 hipError_t launch_clear_wave(const WaveDev &w, hipStream_t s);
 hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s);
-// A step is the tile kernel (logits from memory, or computed by the SID-range lm_head)
-// followed by the per-request merge kernel.
+// A step is the tile kernel followed by the per-request merge kernel; with the SID-range
+// lm_head, the lm_head kernel first writes the logits to WaveDev::lmx.
 hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *logits,
                        int64_t ld, int dtype, hipStream_t s);
-hipError_t launch_tile_lmhead(const TrieDev &t, const WaveDev &w, int rp, int n_req,
-                              const void *hidden, int64_t ld, int H, const void *weight,
-                              hipStream_t s);
+hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *hidden,
+                         int64_t ld, int H, const void *weight, float *out, hipStream_t s);
 hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, int n_req, hipStream_t s);
 hipError_t launch_finalize(const TrieDev &t, const WaveDev &w, int rp, const FinBatch &b,
                            uint8_t *sids, float *scores, int64_t *items, int32_t *counts,
