@@ -1,0 +1,174 @@
+"""The benchmark workloads at full size, in the launch configuration bench.py times.
+
+Every workload runs on the GPU exactly as benchmarked (one wave holding all requests,
+or FIFO admission under the 32,768-slot budget for the mixed wave). Sampled requests
+are checked at every step against the oracle, teacher-forced from the GPU's pre-step
+state; every finalized beam of every request is checked for legality (a catalog SID,
+no duplicates, ranked best-first, the lowest catalog row as its item).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as gh
+import oracle
+from trie_constrained_beam_amd import Beams, Trie, run_wave, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    print(f"\n[gpu] {request.node.name}", flush=True)
+
+
+_CACHE = {}
+
+
+def _workload(name):
+    if name not in _CACHE:
+        wl = synth.WORKLOADS[name]
+        cat = wl.catalog()
+        keys = synth.pack_sids(cat)
+        first = {}
+        order = np.argsort(keys, kind="stable")
+        sk = keys[order]
+        newk = np.ones(sk.size, dtype=bool)
+        newk[1:] = sk[1:] != sk[:-1]
+        lowest = dict(zip(sk[newk].tolist(), order[newk].tolist()))
+        _CACHE[name] = (wl, cat, oracle.OracleTrie(cat), lowest)
+    return _CACHE[name]
+
+
+def _check_legal(lowest, sids, scores, items, width, ctx):
+    cnt = sids.shape[0]
+    assert cnt <= width, ctx
+    keys = synth.pack_sids(sids)
+    assert np.unique(keys).size == cnt, f"{ctx}: duplicate SIDs"
+    for key, item in zip(keys.tolist(), items.tolist()):
+        assert lowest.get(key) == item, f"{ctx}: illegal SID or wrong item"
+    assert (np.diff(scores) <= 0).all(), f"{ctx}: not ranked best-first"
+
+
+def _check_request(run_state_pre, run_state_post, otrie, rid, base, level, x_rows, dtype, width, ctx, x64=None):
+    rows = int(run_state_pre["rows"][rid])
+    pref = gh.walk_prefixes(run_state_pre["hist"], base, rows, level)
+    if x64 is None:
+        x64 = oracle.widen_logits(x_rows[:rows], dtype)
+    ref = oracle.expand_request(otrie, level, pref, run_state_pre["score"][base:base + rows].astype(np.float64),
+                                x64, width)
+    k = int(run_state_post["rows"][rid])
+    h = run_state_post["hist"][level, base:base + k].astype(np.int64)
+    gh.compare_step(ref, h >> 8, h & 255, run_state_post["node"][base:base + k],
+                    run_state_post["score"][base:base + k], ctx=ctx)
+
+
+def _state(beams):
+    ex = beams.export()
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in ex.items()}
+
+
+@pytest.mark.parametrize("name,sample", [
+    ("b50x1_l3_20k_f32", [0]),
+    ("b128x64_l4_1m_zipf_f32", [0, 17, 42, 63]),
+    ("b512x32_l4_4m_zipf_bf16", [0, 13, 31]),
+])
+def test_fullsize_one_wave(name, sample):
+    wl, cat, otrie, lowest = _workload(name)
+    widths = list(wl.widths)
+    S, R, B = sum(widths), len(widths), max(widths)
+    trie = Trie(cat, device="cuda")
+    beams = Beams(trie, S, R, B)
+    ids, bases = beams.init(widths)
+    dt = "bf16" if wl.bf16 else "f32"
+    for t in range(wl.L):
+        xs = [synth.logits_rowkeyed(wl.seed, t, i, w, wl.sigma, bf16=wl.bf16) for i, w in enumerate(widths)]
+        host = np.zeros((S, 256), dtype=np.uint16 if wl.bf16 else np.float32)
+        for x, b in zip(xs, bases):
+            host[b:b + x.shape[0]] = x
+        dev = torch.from_numpy(host.view(np.int16) if wl.bf16 else host).cuda()
+        pre = _state(beams)
+        beams.step(dev.view(torch.bfloat16) if wl.bf16 else dev)
+        post = _state(beams)
+        for i in sample:
+            _check_request(pre, post, otrie, int(ids[i]), int(bases[i]), t, xs[i], dt, widths[i],
+                           f"{name} req {i} step {t}")
+    beams.check()
+    out = beams.finalize(ids)
+    for i, w in enumerate(widths):
+        c = int(out["counts"][i])
+        assert c == w
+        _check_legal(lowest, out["sids"][i, :c], out["scores"][i, :c], out["items"][i, :c], w, f"{name} req {i}")
+
+
+def test_fullsize_mixed_wave_fifo():
+    """256 requests, widths from {50, 128, 256, 512}, FIFO admission under 32,768 slots, L=5."""
+    wl, cat, otrie, lowest = _workload("mixed256_l5_8m_f32")
+    widths = list(wl.widths)
+    trie = Trie(cat, device="cuda")
+    beams = Beams(trie, wl.slot_budget, len(widths), max(widths))
+    sample = set(range(0, len(widths), 16))
+    checked = []
+    live_widths = []
+
+    def step_fn(step, live):
+        live_widths.append(sum(q.width for q in live))
+        host = np.zeros((wl.slot_budget, 256), dtype=np.float32)
+        xs = {}
+        for q in live:
+            x = synth.logits_rowkeyed(wl.seed, q.level, q.index, q.width, wl.sigma)
+            host[q.base:q.base + q.width] = x
+            xs[q.index] = x
+        pre = _state(beams)
+        beams.step(torch.from_numpy(host).cuda())
+        post = _state(beams)
+        for q in live:
+            if q.index in sample:
+                _check_request(pre, post, otrie, q.rid, q.base, q.level, xs[q.index], "f32", q.width,
+                               f"mixed req {q.index} level {q.level}")
+                checked.append((q.index, q.level))
+
+    results = run_wave(beams, widths, step_fn)
+    assert sorted(results) == list(range(len(widths)))
+    assert max(live_widths) <= wl.slot_budget
+    assert len(checked) == len(sample) * wl.L
+    for i, r in results.items():
+        _check_legal(lowest, r["sids"], r["scores"], r["items"], widths[i], f"mixed req {i}")
+    beams.check()
+
+
+def test_fullsize_lmhead():
+    """8 requests x 512 beams, hidden 2048, SID-range lm_head on MFMA, then the step."""
+    wl, cat, otrie, lowest = _workload("lmhead_b512x8_l4_1m_h2048")
+    widths = list(wl.widths)
+    S, R, B, H = sum(widths), len(widths), max(widths), wl.hidden
+    trie = Trie(cat, device="cuda")
+    beams = Beams(trie, S, R, B)
+    ids, bases = beams.init(widths)
+    weights = np.stack([synth.lmhead_weight(wl.seed, lv, 256, H) for lv in range(wl.L)])
+    w_dev = torch.from_numpy(weights.view(np.int16)).cuda().view(torch.bfloat16)
+    for t in range(wl.L):
+        hid = synth.hidden_states(wl.seed, t, S, H)
+        pre = _state(beams)
+        beams.step_lmhead(torch.from_numpy(hid.view(np.int16)).cuda().view(torch.bfloat16), w_dev)
+        post = _state(beams)
+        for i in (0, 5):
+            base, rows = int(bases[i]), int(pre["rows"][ids[i]])
+            x64 = oracle.lmhead_logits(hid[base:base + rows], weights[t])
+            _check_request(pre, post, otrie, int(ids[i]), base, t, None, None, widths[i],
+                           f"lmhead req {i} step {t}", x64=x64)
+    beams.check()
+    out = beams.finalize(ids)
+    for i, w in enumerate(widths):
+        c = int(out["counts"][i])
+        _check_legal(lowest, out["sids"][i, :c], out["scores"][i, :c], out["items"][i, :c], w, f"lmhead req {i}")
+
+
+def test_maximum_width():
+    """Beam width 4096 (the largest accepted): the tiles' sample bound cannot prune and
+    both kernels take their exact selection paths."""
+    cat = synth.catalog(100_000, 3, ("uniform",) * 3, [61, 1])
+    run, stats = gh.run_rowkeyed(cat, [4096, 1000], 61, 2.0)
+    assert stats["checked"] == 6

@@ -7,5 +7,6 @@ seeded workload generators in ``synth``.
 from . import _lib
 from .api import Beams, Trie
 from ._lib import TcbError
+from .wave import run_wave
 
-__all__ = ["Beams", "Trie", "TcbError"]
+__all__ = ["Beams", "Trie", "TcbError", "run_wave"]
