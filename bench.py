@@ -3,18 +3,28 @@
 
 One bench step = one full decode of the workload's batch on the GPU: admit every
 request at the root, run L constrained beam steps (masked log-softmax, per-request
-top-n, parent-gather / trie-advance) and gather the ranked beams into device
-buffers. Inputs (trie image, per-step logits) are resident in HBM before the timed
-region; the logits of consecutive decodes come from a pool of identical copies
-larger than the 256 MB Infinity Cache, so every decode streams them from HBM.
+top-n, parent-gather / trie-advance) and gather the ranked beams into device buffers.
+The default workload is 32 requests x beam 512, L = 4, a catalog of 4M Zipf(1.1) SIDs
+and bf16 logits N(0, 3^2). Inputs (trie image, per-step logits) are resident in HBM
+before the timed region; consecutive decodes rotate through a pool of input copies
+larger than the 256 MB Infinity Cache, so every decode streams its logits from HBM.
+Each decode is replayed as a captured HIP graph (``--graph 0``: eager launches).
 
-Prints one JSON line. Progress goes to stderr.
+Also measured in the same run:
+  * per-kernel durations with HIP events on the launch stream (an eager pass);
+  * the SID-range lm_head leg: 8 requests x beam 512, hidden 2048, its MFMA kernel
+    against the bf16 dense peak;
+  * the CPU oracle on a bounded sample of the same workload (a baseline, not a target).
+
+Prints one JSON line on stdout. Progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
+import multiprocessing as mp
 import os
 import platform
 import sys
@@ -23,81 +33,150 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "constrained beam-rows×steps/sec and achieved HBM GB/s at B=512, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-EXPAND_STATE_BYTES = 8           # node id + score per live row
-EXPAND_TRIE_BYTES = 8            # first/last child id (or first child id + mask word) per row
-MERGE_WRITE_BYTES = 18           # node, score, parent slot, back-pointer (+ code) per survivor
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak, published
+STATE_BYTES = 8                 # node id + score read per live row
+TRIE_BYTES = 8                  # child range (or first child + mask word) per live row
+MERGE_WRITE_BYTES = 18          # node, score, parent slot, back-pointer (+ code) per survivor
+KERNEL_SOURCES = ["trie_constrained_beam_amd/csrc/kernels.hip", "trie_constrained_beam_amd/csrc/tcb_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_tile_b512x32_l4_4m_zipf_bf16_traffic.txt")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000, help="timed decodes")
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="b512x32_l4_4m_zipf_bf16")
-    ap.add_argument("--pool-gib", type=float, default=1.0, help="size of the rotated logits pool")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle baseline budget (0: skip)")
-    ap.add_argument("--graph", type=int, default=0, help="replay each decode as a captured HIP graph")
-    args = ap.parse_args()
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "requests are independent, so the path shards by request with no per-step "
-              "communication; run one process per GPU instead.", file=sys.stderr)
-        sys.exit(2)
 
+def recorded_traffic():
+    """HBM bytes per tile-kernel launch from the committed counter profile, if it was
+    taken on the current kernel source (else None)."""
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+    except OSError:
+        return None
+    if fields.get("kernel_source_sha", "").strip() != kernel_source_sha():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------- CPU oracle
+_CPU = {}
+
+
+def _oracle_request(i):
+    import oracle
+    wl, widths, xs = _CPU["wl"], _CPU["widths"], _CPU["xs"][i]
+    res = oracle.decode(_CPU["otrie"], widths[i],
+                        lambda t, pref: oracle.widen_logits(xs[t][:len(pref)], "bf16" if wl.bf16 else "f32"))
+    return sum(int(h["cand_parent"].max()) + 1 for h in res["history"])
+
+
+def cpu_baseline(wl, cat, seconds):
+    """The oracle decoding requests of this workload in a process pool (one request per
+    task) until ``seconds`` have passed; rows x steps per second of wall time."""
+    import oracle
+    from trie_constrained_beam_amd import synth
+    widths = list(wl.widths)
+    _CPU.update(wl=wl, widths=widths, otrie=oracle.OracleTrie(cat),
+                xs=[[synth.logits_rowkeyed(wl.seed, t, i, w, wl.sigma, bf16=wl.bf16) for t in range(wl.L)]
+                    for i, w in enumerate(widths)])
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    workers = max(1, min(16, cores, len(widths)))
+    ctx = mp.get_context("fork")                 # before any GPU use in this process
+    done_rows, n_req = 0, 0
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        while time.perf_counter() - t0 < seconds:
+            batch = [(n_req + k) % len(widths) for k in range(workers)]
+            done_rows += sum(pool.map(_oracle_request, batch))
+            n_req += len(batch)
+    el = time.perf_counter() - t0
+    return {"value": done_rows / el, "unit": "beam-rows x steps/s", "cores": workers, "kind": "oracle",
+            "sample": f"{n_req} request decodes of this workload ({done_rows} beam-rows x steps) in "
+                      f"{el:.1f} s, {workers} worker processes (one request each, numpy float64) on "
+                      f"{platform.machine()} with {cores} cores available"}
+
+
+# ----------------------------------------------------------------------------- GPU legs
+def make_pool(tensors_fn, per_decode_bytes, pool_gib):
+    n = max(1, math.ceil(pool_gib * 2 ** 30 / per_decode_bytes))
+    first = tensors_fn()
+    return [first] + [[x.clone() for x in first] for _ in range(n - 1)]
+
+
+def capture(decode, n):
+    import torch
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in range(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                decode(c)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def timed(run, steps, warmup):
+    import torch
+    for d in range(warmup):
+        run(d)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for d in range(steps):
+        run(d)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def main_leg(args, wl, cat, dev):
     import numpy as np
     import torch
-
     from trie_constrained_beam_amd import Beams, Trie, synth
-
-    wl = synth.WORKLOADS[args.workload]
-    if wl.slot_budget or wl.hidden:
-        raise SystemExit(f"workload {wl.name} is a parity case, not a bench line")
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    t0 = time.perf_counter()
-    cat = wl.catalog()
-    log(f"[bench] catalog {cat.shape} in {time.perf_counter() - t0:.1f}s")
     trie = Trie(cat, device=dev)
     widths = list(wl.widths)
-    S, R, B = sum(widths), len(widths), max(widths)
-    V, L = trie.V, trie.L
+    S, R, B, V, L = sum(widths), len(widths), max(widths), trie.V, trie.L
     beams = Beams(trie, S, R, B, device=dev)
-
-    # ---------------------------------------------------------------- inputs in HBM
     ids, bases = beams.init(widths)
-    host_steps = []
+    host = []
     for t in range(L):
-        host = np.zeros((S, V), dtype=np.uint16 if wl.bf16 else np.float32)
+        h = np.zeros((S, V), dtype=np.uint16 if wl.bf16 else np.float32)
         for i, (w, b) in enumerate(zip(widths, bases)):
-            host[b:b + w] = synth.logits_rowkeyed(wl.seed, t, i, w, wl.sigma, bf16=wl.bf16)
-        host_steps.append(host)
+            h[b:b + w] = synth.logits_rowkeyed(wl.seed, t, i, w, wl.sigma, bf16=wl.bf16)
+        host.append(h)
 
-    def to_dev(h):
+    def upload():
         if wl.bf16:
-            return torch.from_numpy(h.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(h).to(dev)
-    base_set = [to_dev(h) for h in host_steps]
-    per_decode_bytes = sum(x.numel() * x.element_size() for x in base_set)
-    n_copies = max(1, math.ceil(args.pool_gib * 2 ** 30 / per_decode_bytes))
-    pool = [base_set] + [[x.clone() for x in base_set] for _ in range(n_copies - 1)]
+            return [torch.from_numpy(h.view(np.int16)).to(dev).view(torch.bfloat16) for h in host]
+        return [torch.from_numpy(h).to(dev) for h in host]
+    per_decode = sum(h.nbytes for h in host)
+    pool = make_pool(upload, per_decode, args.pool_gib)
     out = {"sids": torch.empty((R, B, L), dtype=torch.uint8, device=dev),
            "scores": torch.empty((R, B), dtype=torch.float32, device=dev),
            "items": torch.empty((R, B), dtype=torch.int64, device=dev),
            "counts": torch.empty(R, dtype=torch.int32, device=dev)}
-    log(f"[bench] pool {n_copies} x {per_decode_bytes / 2**20:.1f} MiB of logits")
-
-    # live rows per step (untimed decode, read back once)
+    log(f"[bench] pool {len(pool)} x {per_decode / 2**20:.1f} MiB of logits")
     rows_per_step = []
+    idx = torch.as_tensor(ids, device=dev).long()
     for t in range(L):
-        ex = beams.export()
-        rows_per_step.append(int(ex["rows"][torch.as_tensor(ids, device=dev).long()].sum().item()))
+        rows_per_step.append(int(beams.export()["rows"][idx].sum().item()))
         beams.step(pool[0][t])
     beams.finalize_device(ids, out)
     torch.cuda.synchronize()
@@ -109,111 +188,162 @@ def main():
         for t in range(L):
             beams.step(pool[c][t])
         beams.finalize_device(rid, out)
-
-    graphs = None
-    if args.graph:
-        graphs = []
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for c in range(n_copies):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=s):
-                    decode(c)
-                graphs.append(g)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
+    graphs = capture(decode, len(pool)) if args.graph else None
 
     def run(d):
         if graphs is not None:
-            graphs[d % n_copies].replay()
+            graphs[d % len(pool)].replay()
         else:
-            decode(d % n_copies)
-
-    for d in range(args.warmup):
-        run(d)
-    torch.cuda.synchronize()
-
-    # ---------------------------------------------------------------- timed region
-    if graphs is None:
-        beams.enable_timing(args.steps * L)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for d in range(args.steps):
-        run(d)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    if graphs is None:
-        _, tile_ms, merge_ms, n_timed = beams.timing()
-    else:
-        # the same decodes again, eagerly, with per-kernel events (graph replays hide them)
-        beams.enable_timing(args.steps * L)
-        for d in range(args.steps):
-            decode(d % n_copies)
-        _, tile_ms, merge_ms, n_timed = beams.timing()
+            decode(d % len(pool))
+    elapsed = timed(run, args.steps, args.warmup)
+    # per-kernel durations: the same decodes again, eagerly, with events on the launch stream
+    n_ev = min(args.steps, 200)
+    beams.enable_timing(n_ev * L)
+    for d in range(n_ev):
+        decode(d % len(pool))
+    _, tile_ms, merge_ms, n_timed = beams.timing()
     beams.enable_timing(0)
+    return {"elapsed": elapsed, "rows_x_steps": rows_x_steps, "rows_per_step": rows_per_step,
+            "tile_us": tile_ms * 1e3 / n_timed, "merge_us": merge_ms * 1e3 / n_timed, "pool": len(pool),
+            "dsize": 2 if wl.bf16 else 4, "V": V, "L": L, "R": R, "B": B}
 
-    value = rows_x_steps * args.steps / elapsed
-    dsize = 2 if wl.bf16 else 4
-    expand_unit = V * dsize + EXPAND_STATE_BYTES + EXPAND_TRIE_BYTES
-    expand_bytes_per_launch = rows_x_steps * expand_unit / L
-    expand_avg_s = tile_ms / 1e3 / n_timed
-    achieved = expand_bytes_per_launch / expand_avg_s / 1e9
-    path_unit = expand_unit + MERGE_WRITE_BYTES
-    wall_gbps = rows_x_steps * path_unit * args.steps / elapsed / 1e9
-    log(f"[bench] {args.steps} decodes in {elapsed * 1e3:.1f} ms; tile kernel avg "
-        f"{expand_avg_s * 1e6:.2f} us, merge kernel avg {merge_ms / n_timed * 1e3:.2f} us")
 
-    # ---------------------------------------------------------------- CPU oracle baseline
+def lmhead_leg(args, dev):
+    import numpy as np
+    import torch
+    from trie_constrained_beam_amd import Beams, Trie, synth
+    wl = synth.WORKLOADS["lmhead_b512x8_l4_1m_h2048"]
+    cat = wl.catalog()
+    trie = Trie(cat, device=dev)
+    widths = list(wl.widths)
+    S, R, B, L, H = sum(widths), len(widths), max(widths), wl.L, wl.hidden
+    beams = Beams(trie, S, R, B, device=dev)
+    weights = np.stack([synth.lmhead_weight(wl.seed, lv, 256, H) for lv in range(L)])
+    w_dev = torch.from_numpy(weights.view(np.int16)).to(dev).view(torch.bfloat16)
+    host = [synth.hidden_states(wl.seed, t, S, H) for t in range(L)]
+    per_decode = sum(h.nbytes for h in host)
+    pool = make_pool(lambda: [torch.from_numpy(h.view(np.int16)).to(dev).view(torch.bfloat16) for h in host],
+                     per_decode, args.pool_gib)
+    out = {"sids": torch.empty((R, B, L), dtype=torch.uint8, device=dev),
+           "scores": torch.empty((R, B), dtype=torch.float32, device=dev),
+           "items": torch.empty((R, B), dtype=torch.int64, device=dev),
+           "counts": torch.empty(R, dtype=torch.int32, device=dev)}
+    ids, _ = beams.init(widths)
+    rows_per_step = []
+    idx = torch.as_tensor(ids, device=dev).long()
+    for t in range(L):
+        rows_per_step.append(int(beams.export()["rows"][idx].sum().item()))
+        beams.step_lmhead(pool[0][t], w_dev)
+    beams.finalize_device(ids, out)
+    torch.cuda.synchronize()
+
+    def decode(c):
+        rid, _ = beams.init(widths)
+        for t in range(L):
+            beams.step_lmhead(pool[c][t], w_dev)
+        beams.finalize_device(rid, out)
+    graphs = capture(decode, len(pool)) if args.graph else None
+
+    def run(d):
+        if graphs is not None:
+            graphs[d % len(pool)].replay()
+        else:
+            decode(d % len(pool))
+    steps = max(10, args.steps // 5)
+    elapsed = timed(run, steps, max(2, args.warmup // 5))
+    n_ev = min(steps, 100)
+    beams.enable_timing(n_ev * L)
+    for d in range(n_ev):
+        decode(d % len(pool))
+    head_ms, tile_ms, merge_ms, n_timed = beams.timing()
+    beams.enable_timing(0)
+    rows_x_steps = sum(rows_per_step)
+    flop_per_decode = 2.0 * rows_x_steps * 256 * H
+    head_s = head_ms / 1e3 / n_timed                       # average lm_head launch
+    achieved = flop_per_decode / L / head_s / 1e12
+    log(f"[bench] lm_head leg: rows per step {rows_per_step}; lm_head avg {head_s * 1e6:.2f} us "
+        f"({achieved:.0f} TFLOP/s), tile {tile_ms * 1e3 / n_timed:.2f} us, merge {merge_ms * 1e3 / n_timed:.2f} us")
+    return {"workload": wl.name, "rows_per_step": rows_per_step,
+            "value": rows_x_steps * steps / elapsed, "unit": "beam-rows x steps/s",
+            "ms_per_step": elapsed * 1e3 / steps, "steps": steps,
+            "roofline": {"bound": "mfma", "kernel": "k_lmhead", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                         "flop_per_launch": flop_per_decode / L, "avg_launch_us": head_s * 1e6},
+            "tile_avg_us": tile_ms * 1e3 / n_timed, "merge_avg_us": merge_ms * 1e3 / n_timed}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000, help="timed decodes")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="b512x32_l4_4m_zipf_bf16")
+    ap.add_argument("--pool-gib", type=float, default=1.0, help="size of each rotated input pool")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle baseline budget (0: skip)")
+    ap.add_argument("--graph", type=int, default=1, help="replay each decode as a captured HIP graph")
+    ap.add_argument("--lmhead", type=int, default=1, help="also run the SID-range lm_head leg")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): requests "
+              "are independent, so the path shards by request with no per-step communication; "
+              "run one process per GPU instead.", file=sys.stderr)
+        sys.exit(2)
+
+    from trie_constrained_beam_amd import synth
+    wl = synth.WORKLOADS[args.workload]
+    if wl.slot_budget or wl.hidden:
+        raise SystemExit(f"workload {wl.name} is a parity case, not a bench line")
+    t0 = time.perf_counter()
+    cat = wl.catalog()
+    log(f"[bench] catalog {cat.shape} in {time.perf_counter() - t0:.1f}s")
     cpu = None
     if args.cpu_seconds > 0:
-        import oracle
-        otrie = oracle.OracleTrie(cat)
-        per_req = []
-        for i, w in enumerate(widths):
-            per_req.append([synth.logits_rowkeyed(wl.seed, t, i, w, wl.sigma, bf16=wl.bf16)
-                            for t in range(L)])
-        done_rows, n_req_done = 0, 0
-        c0 = time.perf_counter()
-        while time.perf_counter() - c0 < args.cpu_seconds and n_req_done < 10 * R:
-            i = n_req_done % R
-            xs = per_req[i]
-            res = oracle.decode(otrie, widths[i],
-                                lambda t, pref: oracle.widen_logits(xs[t][:len(pref)],
-                                                                    "bf16" if wl.bf16 else "f32"))
-            done_rows += sum(h["cand_parent"].max() + 1 for h in res["history"])
-            n_req_done += 1
-        cpu_s = time.perf_counter() - c0
-        cpu = {"value": done_rows / cpu_s, "unit": "beam-rows x steps/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n_req_done} request decodes of this workload ({done_rows} beam-rows x steps, "
-                         f"{cpu_s:.1f} s) on {platform.processor() or platform.machine()}, "
-                         f"numpy float64, single thread"}
-        log(f"[bench] oracle {cpu['value']:.0f} rows x steps/s over {cpu_s:.1f}s")
+        cpu = cpu_baseline(wl, cat, args.cpu_seconds)
+        log(f"[bench] oracle {cpu['value']:.0f} rows x steps/s ({cpu['cores']} processes)")
+
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m = main_leg(args, wl, cat, dev)
+    value = m["rows_x_steps"] * args.steps / m["elapsed"]
+    unit_bytes = m["V"] * m["dsize"] + STATE_BYTES + TRIE_BYTES          # per row-step, tile kernel
+    bytes_per_launch = m["rows_x_steps"] * unit_bytes / m["L"]
+    achieved = bytes_per_launch / (m["tile_us"] * 1e-6) / 1e9
+    traffic = recorded_traffic()
+    log(f"[bench] {args.steps} decodes in {m['elapsed'] * 1e3:.1f} ms; tile kernel avg {m['tile_us']:.2f} us "
+        f"({achieved:.0f} GB/s), merge kernel avg {m['merge_us']:.2f} us")
+    lm = lmhead_leg(args, dev) if args.lmhead else None
 
     line = {
-        "metric": "constrained beam-rows x steps/sec (and achieved HBM GB/s) at B=512, 1 MI355X",
+        "metric": METRIC,
         "value": value,
         "unit": "beam-rows x steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": elapsed * 1e3 / args.steps,
+        "ms_per_step": m["elapsed"] * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "requests": R, "beam_width": B, "L": L, "catalog": int(cat.shape[0]),
-                   "catalog_levels": "zipf(1.1)" if wl.level_dists[0] == "zipf" else "/".join(wl.level_dists),
-                   "logits": ("bf16" if wl.bf16 else "f32") + f" N(0,{wl.sigma:g}^2)",
-                   "rows_x_steps_per_decode": rows_x_steps, "rows_per_step": rows_per_step,
-                   "graph": bool(args.graph), "logits_pool_copies": n_copies},
+        "config": {"workload": wl.name, "requests": m["R"], "beam_width": m["B"], "L": m["L"],
+                   "catalog": int(cat.shape[0]), "catalog_levels": "zipf(1.1) at every level",
+                   "logits": ("bf16" if wl.bf16 else "f32") + f" N(0,{wl.sigma:g}^2), upcast to f32",
+                   "rows_x_steps_per_decode": m["rows_x_steps"], "rows_per_step": m["rows_per_step"],
+                   "graph": bool(args.graph), "input_pool_copies": m["pool"]},
         "roofline": {"bound": "hbm", "kernel": "k_tile", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "bytes_per_row_step": expand_unit, "avg_launch_us": expand_avg_s * 1e6},
-        "hbm_GBps_wall": wall_gbps,
-        "merge_avg_us": merge_ms / n_timed * 1e3,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None if traffic is None else traffic / (m["tile_us"] * 1e-6) / 1e9,
+                     "bytes_per_row_step": unit_bytes, "bytes_per_launch": bytes_per_launch,
+                     "avg_launch_us": m["tile_us"]},
+        "hbm_GBps_wall": m["rows_x_steps"] * (unit_bytes + MERGE_WRITE_BYTES) * args.steps / m["elapsed"] / 1e9,
+        "merge_avg_us": m["merge_us"],
+        "lmhead": lm,
         "cpu_baseline": cpu,
+        "kernel_source_sha": kernel_source_sha(),
     }
     print(json.dumps(line), flush=True)
 

@@ -169,7 +169,7 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
  * Decoding: lm_head only over the SID token range):
  *   x[slot][c] = sum_h hidden[slot][h] * W[level][c][h], fp32 accumulate, no bias.
  *   d_hidden  device bf16 [max_slots][ld_hidden], ld_hidden >= H, ld_hidden % 8 == 0,
- *             H % 64 == 0, 16-byte aligned; row `slot` is that slot's hidden state
+ *             H % 128 == 0, 16-byte aligned; row `slot` is that slot's hidden state
  *   d_weight  device bf16 [L][256][H] contiguous (one [256][H] matrix per level),
  *             16-byte aligned; the trie must have V = 256
  * The logits pass through an fp32 [max_slots][256] part of the workspace; the masked

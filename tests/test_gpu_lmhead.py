@@ -55,7 +55,7 @@ def _run_lmhead(cat, widths, H, seed, check_reqs=None):
 
 def test_lmhead_step_parity_small():
     cat = synth.catalog(30_000, 4, ("uniform",) * 4, [51, 1])
-    _run_lmhead(cat, [64, 130, 7], 256, 51)
+    _run_lmhead(cat, [64, 130, 7], 384, 51)
 
 
 def test_lmhead_step_parity_wide_k():
@@ -95,4 +95,4 @@ def test_lmhead_argument_errors():
     with pytest.raises(ValueError):
         beams.step_lmhead(torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda"), w[:1])
     with pytest.raises(TcbError, match="ARG"):
-        beams.step_lmhead(torch.zeros((64, 96), dtype=torch.bfloat16, device="cuda"), w[:, :, :96].contiguous())
+        beams.step_lmhead(torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda"), w[:, :, :64].contiguous())

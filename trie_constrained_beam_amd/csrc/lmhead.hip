@@ -8,20 +8,15 @@
 // so the masked log-softmax and selection are the same code as for logits from memory.
 //
 // Tiling. A workgroup of 4 waves computes a 64-row x 64-code block with
-// v_mfma_f32_16x16x32_bf16: wave w owns rows 16w..16w+15 and keeps four 16x16 fp32
-// accumulators (codes 0..63 of the block). K is walked in chunks of 64: the block's
-// 64 x 64 slice of W is shared through LDS (double-buffered, one barrier per chunk),
-// each wave reads its own 16 rows of hidden straight into MFMA operand registers. The
-// four code blocks of one row tile are dealt to the same XCD, so the hidden rows they
-// share are read from HBM once and then hit that XCD's L2. Each output element is
-// accumulated by one wave in a fixed K order: results are deterministic.
+// v_mfma_f32_16x16x32_bf16. The block's K range is split across the waves: wave w
+// accumulates the whole 64 x 64 block (4 x 4 tiles of 16 x 16, 64 fp32 per lane) over
+// its quarter of K, reading its A and B operands straight from memory into registers
+// with many K-steps of loads in flight (one workgroup per CU leaves each wave a whole
+// SIMD and its register file). The four partial blocks are then added through LDS in a
+// fixed order (wave 0 + 1 + 2 + 3), so results are deterministic. The four code blocks
+// of one row tile are dealt to the same XCD, so the hidden rows they share are read
+// from HBM once and then hit that XCD's L2.
 //
-// Operand layouts of v_mfma_f32_16x16x32_bf16 (64 lanes, l = lane):
-//   A (16 x 32):  lane l holds A[l % 16][8 (l / 16) .. 8 (l / 16) + 7]
-//   B (32 x 16):  lane l holds B[8 (l / 16) .. 8 (l / 16) + 7][l % 16]
-//   D (16 x 16):  lane l holds D[4 (l / 16) + i][l % 16], i = 0..3
-// With A = hidden rows and B[k][c] = W[c][k], both operands are 16 contiguous bytes of
-// a row-major array.
 #include "tcb_internal.h"
 
 namespace tcb {
@@ -33,15 +28,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGRows = 64;                 // rows of a block
 constexpr int kGCodes = 64;                // codes of a block (4 blocks cover V = 256)
-constexpr int kGK = 64;                    // K chunk
-constexpr int kGThreads = 256;
-constexpr int kBStride = kGK + 8;          // bf16 per code row in LDS (16-byte pad)
+constexpr int kGThreads = 256;             // 4 waves, each over a quarter of K
+constexpr int kKStep = 32;                 // K of one MFMA
 
-__global__ __launch_bounds__(kGThreads) void k_lmhead(TrieDev T, WaveDev W, int rp, int n_req,
+// NS = K-steps of 32 per wave (H = 4 * 32 * NS); NS = 0: any H % 128 == 0, one step
+// of loads in flight.
+template <int NS>
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_lmhead(TrieDev T, WaveDev W, int rp, int n_req,
                                                       const uint16_t *__restrict__ hidden, int64_t ld, int H,
                                                       const uint16_t *__restrict__ weight,
                                                       float *__restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][kGCodes * kBStride];
+    __shared__ f32x4 red[4][4][4][64];                        // [wave][row blk][code blk][lane]
     const int MT = W.MT;
     const int xcd = (int)(blockIdx.x & 7u), i8 = (int)(blockIdx.x >> 3);
     const int cblk = i8 & 3;                                  // code block 0..3
@@ -55,52 +52,81 @@ __global__ __launch_bounds__(kGThreads) void k_lmhead(TrieDev T, WaveDev W, int 
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kq = lane >> 4;
-    // A: this lane's hidden row (dead rows read row r0 and are never stored)
-    const int ar = r0 + wave * 16 + l16;
-    const uint16_t *arow = hidden + (size_t)(rec.base + (ar < rec.rows ? ar : r0)) * (size_t)ld + 8 * kq;
-    // B loader: thread t copies 16 k-values of code t / 4 per chunk
-    const int bc = tid >> 2, bk = (tid & 3) * 16;
-    const uint16_t *brow = weight + ((size_t)rec.level * 256 + (size_t)cblk * kGCodes + bc) * (size_t)H + bk;
-
-    f32x4 acc[4];
+    const int nsteps = NS > 0 ? NS : H / (4 * kKStep);
+    const int k0 = wave * nsteps * kKStep + 8 * kq;           // this lane's first k
+    const uint16_t *ap[4], *bp[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const int nk = H / kGK;
-    u32x4 nb0 = *reinterpret_cast<const u32x4 *>(brow);
-    u32x4 nb1 = *reinterpret_cast<const u32x4 *>(brow + 8);
-    u32x4 na0 = *reinterpret_cast<const u32x4 *>(arow);
-    u32x4 na1 = *reinterpret_cast<const u32x4 *>(arow + 32);
-    for (int kc = 0; kc < nk; ++kc) {
-        uint16_t *sb = sB[kc & 1];
-        *reinterpret_cast<u32x4 *>(sb + bc * kBStride + bk) = nb0;
-        *reinterpret_cast<u32x4 *>(sb + bc * kBStride + bk + 8) = nb1;
-        const u32x4 a0 = na0, a1 = na1;
-        __syncthreads();
-        if (kc + 1 < nk) {                                    // prefetch the next chunk
-            const size_t ko = (size_t)(kc + 1) * kGK;
-            nb0 = *reinterpret_cast<const u32x4 *>(brow + ko);
-            nb1 = *reinterpret_cast<const u32x4 *>(brow + ko + 8);
-            na0 = *reinterpret_cast<const u32x4 *>(arow + ko);
-            na1 = *reinterpret_cast<const u32x4 *>(arow + ko + 32);
-        }
+    for (int b = 0; b < 4; ++b) {
+        const int ar = r0 + 16 * b + l16;                     // dead rows read row r0, never stored
+        ap[b] = hidden + (size_t)(rec.base + (ar < rec.rows ? ar : r0)) * (size_t)ld + k0;
+        bp[b] = weight + ((size_t)rec.level * 256 + (size_t)cblk * kGCodes + 16 * b + l16) * (size_t)H + k0;
+    }
+    f32x4 acc[4][4];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, ks ? a1 : a0);
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x4 bv = *reinterpret_cast<const u32x4 *>(sb + (16 * c + l16) * kBStride + 32 * ks + 8 * kq);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv), acc[c], 0, 0, 0);
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto mfma_step = [&](const u32x4 (&av)[4], const u32x4 (&bv)[4]) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[a]),
+                                                                    __builtin_bit_cast(bf16x8, bv[b]), acc[a][b],
+                                                                    0, 0, 0);
+    };
+    if constexpr (NS > 0) {
+        // a ring of PD K-steps of operands in registers, refilled as each step is used
+        constexpr int PD = NS < 8 ? NS : 8;
+        u32x4 ra[PD][4], rb[PD][4];
+#pragma unroll
+        for (int s = 0; s < PD; ++s)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                ra[s][b] = *reinterpret_cast<const u32x4 *>(ap[b] + s * kKStep);
+                rb[s][b] = *reinterpret_cast<const u32x4 *>(bp[b] + s * kKStep);
             }
+        __builtin_amdgcn_sched_barrier(0);                    // keep the ring's loads issued up front
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            mfma_step(ra[s % PD], rb[s % PD]);
+            if (s + PD < NS) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    ra[s % PD][b] = *reinterpret_cast<const u32x4 *>(ap[b] + (s + PD) * kKStep);
+                    rb[s % PD][b] = *reinterpret_cast<const u32x4 *>(bp[b] + (s + PD) * kKStep);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);                // the refill stays behind its step
+        }
+    } else {
+        for (int s = 0; s < nsteps; ++s) {
+            u32x4 av[4], bv[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                av[b] = *reinterpret_cast<const u32x4 *>(ap[b] + s * kKStep);
+                bv[b] = *reinterpret_cast<const u32x4 *>(bp[b] + s * kKStep);
+            }
+            mfma_step(av, bv);
         }
     }
-    // D: rows 4 kq + i of the wave's 16, code 16 c + l16 of the block
+    // partial blocks of the four waves, added in a fixed order; wave w finishes row block w
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = r0 + wave * 16 + 4 * kq + i;
-        if (row < rec.rows) {
-            float *o = out + (size_t)(rec.base + row) * 256 + cblk * kGCodes + l16;
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) o[16 * c] = acc[c][i];
+        for (int b = 0; b < 4; ++b) red[wave][a][b][lane] = acc[a][b];
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        f32x4 v = red[0][wave][b][lane];
+        v += red[1][wave][b][lane];
+        v += red[2][wave][b][lane];
+        v += red[3][wave][b][lane];
+        // D layout: rows 4 kq + i of row block `wave`, code 16 b + l16 of the block
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = r0 + 16 * wave + 4 * kq + i;
+            if (row < rec.rows) out[(size_t)(rec.base + row) * 256 + cblk * kGCodes + 16 * b + l16] = v[i];
         }
     }
 }
@@ -112,8 +138,15 @@ hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, int n_req, 
     if (n_req <= 0) return hipSuccess;
     const int tiles = n_req * w.MT;                           // row tiles over all requests
     const int groups = (tiles + 7) / 8;
-    hipLaunchKernelGGL(k_lmhead, dim3(8 * groups * 4), dim3(kGThreads), 0, s, t, w, rp, n_req,
-                       static_cast<const uint16_t *>(hidden), ld, H, static_cast<const uint16_t *>(weight), out);
+    const dim3 grid(8 * groups * 4), block(kGThreads);
+    const uint16_t *h = static_cast<const uint16_t *>(hidden), *wt = static_cast<const uint16_t *>(weight);
+    switch (H) {
+    case 512: hipLaunchKernelGGL(k_lmhead<4>, grid, block, 0, s, t, w, rp, n_req, h, ld, H, wt, out); break;
+    case 1024: hipLaunchKernelGGL(k_lmhead<8>, grid, block, 0, s, t, w, rp, n_req, h, ld, H, wt, out); break;
+    case 2048: hipLaunchKernelGGL(k_lmhead<16>, grid, block, 0, s, t, w, rp, n_req, h, ld, H, wt, out); break;
+    case 4096: hipLaunchKernelGGL(k_lmhead<32>, grid, block, 0, s, t, w, rp, n_req, h, ld, H, wt, out); break;
+    default: hipLaunchKernelGGL(k_lmhead<0>, grid, block, 0, s, t, w, rp, n_req, h, ld, H, wt, out); break;
+    }
     return hipGetLastError();
 }
 

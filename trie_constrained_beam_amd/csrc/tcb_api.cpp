@@ -394,7 +394,7 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
 tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_hidden, int32_t H,
                                 const void *d_weight, void *stream) {
     if (!b || !d_hidden || !d_weight) return set_error(TCB_E_ARG, "beam_step_lmhead: null pointer");
-    if (H <= 0 || H % 64 != 0) return set_error(TCB_E_ARG, "beam_step_lmhead: H must be a positive multiple of 64");
+    if (H <= 0 || H % 128 != 0) return set_error(TCB_E_ARG, "beam_step_lmhead: H must be a positive multiple of 128");
     if (ld_hidden < H) return set_error(TCB_E_ARG, "beam_step_lmhead: ld_hidden < H");
     if (((uintptr_t)d_hidden & 15) || ((uintptr_t)d_weight & 15) || (ld_hidden % 8))
         return set_error(TCB_E_ARG, "beam_step_lmhead: hidden/weight must be 16-byte aligned, ld % 8 == 0");
