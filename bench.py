@@ -197,8 +197,9 @@ def main_leg(args, wl, cat, dev):
             decode(d % len(pool))
     elapsed = timed(run, args.steps, args.warmup)
     # per-kernel durations: the same decodes again, eagerly, with events on the launch stream
-    n_ev = min(args.steps, 200)
-    beams.enable_timing(n_ev * L)
+    # around 10 back-to-back launches of each kernel (dispatch latency amortised)
+    n_ev = min(args.steps, 100)
+    beams.enable_timing(n_ev * L, 10)
     for d in range(n_ev):
         decode(d % len(pool))
     _, tile_ms, merge_ms, n_timed = beams.timing()
@@ -251,8 +252,8 @@ def lmhead_leg(args, dev):
             decode(d % len(pool))
     steps = max(10, args.steps // 5)
     elapsed = timed(run, steps, max(2, args.warmup // 5))
-    n_ev = min(steps, 100)
-    beams.enable_timing(n_ev * L)
+    n_ev = min(steps, 50)
+    beams.enable_timing(n_ev * L, 10)
     for d in range(n_ev):
         decode(d % len(pool))
     head_ms, tile_ms, merge_ms, n_timed = beams.timing()

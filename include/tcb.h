@@ -232,13 +232,16 @@ tcb_status tcb_beam_finalize_device(tcb_beams *b, int32_t n, const int32_t *req_
 
 /* Diagnostics: record HIP events on `stream` around the kernels of each of the next
  * `capacity` steps (the lm_head kernel of tcb_beam_step_lmhead, the tile kernel, then the
- * per-request merge kernel); 0 stops recording and releases the events. The events are
- * created here (no device memory). */
-tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity);
+ * per-request merge kernel); 0 stops recording and releases the events. While recording,
+ * each kernel is launched `repeat` times (1..1000) back to back between its events; within
+ * a step every kernel rewrites the same outputs from unchanged inputs, so results do not
+ * change, and the reported durations are per launch. The events are created here (no
+ * device memory). */
+tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity, int32_t repeat);
 
 /* Synchronise the recorded events and report, over the steps recorded since
- * tcb_beams_enable_timing, the summed lm_head (0 for tcb_beam_step), tile-kernel and
- * merge-kernel durations (ms) and the number of steps.
+ * tcb_beams_enable_timing, the summed per-launch lm_head (0 for tcb_beam_step), tile-kernel
+ * and merge-kernel durations (ms) and the number of steps.
  * Errors: TCB_E_STATE (timing not enabled), TCB_E_HIP. */
 tcb_status tcb_beams_timing(tcb_beams *b, double *head_ms, double *tile_ms, double *merge_ms,
                             int32_t *steps);

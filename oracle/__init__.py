@@ -10,7 +10,7 @@ What it computes, and where the pages say so:
   * the trie restricts every continuation to valid catalog SIDs, so an illegal SID
     is never a candidate (flashrec 0.1.0, Features > Decoding, "SID constraint");
   * each beam's score is the sum of token log-probabilities (SPRINT summary,
-    inference paragraph: "token log-probability sum"; flashrec 0.1.0, Quickstart:
+    inference paragraph: a SID is scored by the sum of its tokens' log-probabilities; flashrec 0.1.0, Quickstart:
     beams are returned ranked best-first with a sequence score);
   * selection is deterministic top-k at temperature 0 (flashrec 0.1.0,
     Features > Serving, "API");

@@ -171,9 +171,10 @@ class Beams:
         check(lib().tcb_request_level(self._h, int(req_id), C.byref(v)))
         return int(v.value)
 
-    def enable_timing(self, capacity: int):
-        """Record HIP events around the tile and merge kernels of the next ``capacity`` steps."""
-        check(lib().tcb_beams_enable_timing(self._h, int(capacity)))
+    def enable_timing(self, capacity: int, repeat: int = 1):
+        """Record HIP events around the kernels of the next ``capacity`` steps, each kernel
+        launched ``repeat`` times back to back (durations are reported per launch)."""
+        check(lib().tcb_beams_enable_timing(self._h, int(capacity), int(repeat)))
 
     def timing(self):
         """(head_ms, tile_ms, merge_ms, steps) summed over the recorded steps; synchronises."""

@@ -359,14 +359,17 @@ static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLau
     const int nr = n_req_hw(b);
     const bool timed = b->timing_used < b->timing_cap;
     hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 4] : nullptr;
+    // with timing on, each kernel runs timing_repeat times back to back between its events:
+    // within a step every kernel rewrites the same outputs from unchanged inputs
+    const int rep = timed ? b->timing_repeat : 1;
     hipError_t e = timed ? hipEventRecord(ev[0], s) : hipSuccess;
-    if (e == hipSuccess) e = head(nr);
+    for (int i = 0; i < rep && e == hipSuccess; ++i) e = head(nr);
     if (e != hipSuccess) return hip_fail(e, "lm_head kernel launch");
     if (timed) e = hipEventRecord(ev[1], s);
-    if (e == hipSuccess) e = tile(nr);
+    for (int i = 0; i < rep && e == hipSuccess; ++i) e = tile(nr);
     if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
     if (timed) e = hipEventRecord(ev[2], s);
-    if (e == hipSuccess) e = tcb::launch_merge(b->tdev, b->w, b->rp, nr, s);
+    for (int i = 0; i < rep && e == hipSuccess; ++i) e = tcb::launch_merge(b->tdev, b->w, b->rp, nr, s);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     if (timed) {
         e = hipEventRecord(ev[3], s);
@@ -498,12 +501,13 @@ tcb_status tcb_beam_finalize_device(tcb_beams *b, int32_t n, const int32_t *req_
     return TCB_OK;
 }
 
-tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity) {
-    if (!b || capacity < 0) return set_error(TCB_E_ARG, "enable_timing: bad arguments");
+tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity, int32_t repeat) {
+    if (!b || capacity < 0 || repeat < 1 || repeat > 1000) return set_error(TCB_E_ARG, "enable_timing: bad arguments");
     for (auto e : b->events) (void)hipEventDestroy(e);
     b->events.clear();
     b->timing_cap = 0;
     b->timing_used = 0;
+    b->timing_repeat = repeat;
     for (int32_t i = 0; i < capacity * 4; ++i) {
         hipEvent_t e;
         hipError_t r = hipEventCreate(&e);
@@ -530,9 +534,9 @@ tcb_status tcb_beams_timing(tcb_beams *b, double *head_ms, double *tile_ms, doub
         if (r == hipSuccess) r = hipEventElapsedTime(&a, ev[1], ev[2]);
         if (r == hipSuccess) r = hipEventElapsedTime(&c, ev[2], ev[3]);
         if (r != hipSuccess) return hip_fail(r, "timing: elapsed time");
-        th += h;
-        ta += a;
-        tb += c;
+        th += h / b->timing_repeat;
+        ta += a / b->timing_repeat;
+        tb += c / b->timing_repeat;
     }
     *head_ms = th;
     *tile_ms = ta;

@@ -41,7 +41,7 @@ struct tcb_beams {
     // optional kernel timing: 4 events per step (before the lm_head, before the tile kernel,
     // before the merge, after the merge)
     std::vector<hipEvent_t> events;
-    int32_t timing_cap = 0, timing_used = 0;
+    int32_t timing_cap = 0, timing_used = 0, timing_repeat = 1;
     ~tcb_beams() {
         for (auto e : events) (void)hipEventDestroy(e);
     }
