@@ -65,8 +65,8 @@ enum { TCB_NORM_CHILDREN = 0, TCB_NORM_LEVEL = 1 }; /* log-softmax normaliser   
 #define TCB_MAX_L 8
 #define TCB_MAX_V 256
 #define TCB_MAX_WIDTH 4096
-#define TCB_MASK_AUTO (-1)          /* mask_depths: choose from the trie's fanouts     */
-#define TCB_MASK_AUTO_FANOUT 32     /* ... depths whose mean fanout is at least this    */
+#define TCB_MASK_AUTO (-1)          /* mask_depths: choose from the trie's size        */
+#define TCB_MASK_AUTO_BYTES (1ll << 30) /* ... masks on the leading depths up to this  */
 
 typedef struct tcb_trie tcb_trie;
 typedef struct tcb_beams tcb_beams;
@@ -84,8 +84,9 @@ const char *tcb_version(void);
  *   V           codes per level, 2..256; every code must be < V
  *   mask_depths depths 0..mask_depths-1 also get a 256-bit child mask per node
  *               ("dense" trie); deeper nodes use only the CSR child list. 0..L, or
- *               TCB_MASK_AUTO: the leading depths whose nodes have on average at
- *               least TCB_MASK_AUTO_FANOUT children (tcb_trie_info reports the choice).
+ *               TCB_MASK_AUTO: every leading depth whose masks, counted together with
+ *               the shallower depths' (32 bytes per node), fit in TCB_MASK_AUTO_BYTES;
+ *               normally all of them (tcb_trie_info reports the choice).
  *               Results do not depend on this choice; only speed does.
  * Duplicated SIDs collapse onto one leaf whose item is the lowest catalog row.
  * Nodes are numbered depth-major and lexicographically: the root is 0, depth d

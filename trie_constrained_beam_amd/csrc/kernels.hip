@@ -11,14 +11,14 @@
 // Two kernels per step:
 //   k_tile   workgroup = a tile of 64 consecutive rows of one request. 16 lanes per
 //            row (one DPP row), 16 codes per lane: a row is one coalesced 1 KiB (fp32)
-//            or 512 B (bf16) load. The child set is a 256-bit mask, read from the dense
-//            per-node mask at shallow depths or built in LDS from the CSR child list
-//            deeper down (bit-identical results). Masked log-softmax with DPP reductions
-//            inside the 16-lane row. Candidates are binned request-wide; a per-lane
-//            sample bounds the tile's n-th best so that only a few candidates need exact
-//            treatment; the tile keeps every bin down to the one where its own count
-//            reaches n (a superset of its top-n) and writes them grouped by bin, plus its
-//            cumulative bin counts.
+//            or 512 B (bf16) load. The child set is a 256-bit mask, read from the
+//            trie's per-node masks or, at depths stored without them, built in LDS from
+//            the CSR child list (bit-identical results). Masked log-softmax with DPP
+//            reductions inside the 16-lane row. Candidates are binned request-wide; a
+//            per-lane sample bounds the tile's n-th best so that only a few candidates
+//            need exact treatment; the tile keeps every bin down to the one where its own
+//            count reaches n (a superset of its top-n) and writes them as 16-byte
+//            records grouped by bin, plus its cumulative bin counts.
 //   k_merge  one workgroup per request: sums the tiles' cumulative counts to find the
 //            bin b* of the request's n-th candidate, stages only bins <= b* in LDS, ranks
 //            each candidate by counting the better members of its own bin, and writes the
@@ -48,9 +48,12 @@ __device__ __forceinline__ bool key_le(uint32_t o, uint32_t f, uint32_t o_star, 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// bin = min(kBins - 1, floor(max(0, (sref - s) * kBinRes))). The fma rounds
+// kBinRes * sref - kBinRes * s once, which equals kBinRes * fl(sref - s) exactly
+// (kBinRes is a power of two), so every caller bins identically.
 __device__ __forceinline__ uint32_t score_bin(float sref, float s) {
-    const float d = (sref - s) * kBinRes;
-    return d < (float)(kBins - 1) ? (uint32_t)fmaxf(d, 0.0f) : (uint32_t)(kBins - 1);
+    const float d = fmaf(s, -kBinRes, sref * kBinRes);
+    return (uint32_t)__builtin_amdgcn_fmed3f(d, 0.0f, (float)(kBins - 1));
 }
 
 // DPP moves within a row of 16 lanes; every reduction below leaves the result in all
@@ -351,7 +354,7 @@ struct MergeSmem {
 
 // ---------------------------------------------------------------------- merge
 // One workgroup per request (k_merge). Every tile's kept candidates are in its region
-// of cs/cf/cn grouped by bin, with its cumulative kept counts in tcum.
+// of the candidate records grouped by bin, with its cumulative kept counts in tcum.
 __device__ void merge_request(const WaveDev &W, int q, const ReqRec &rec, int rp, int ntile, float sref,
                               MergeSmem &M, SelSmem &sel) {
     const int tid = threadIdx.x;
@@ -427,10 +430,10 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqRec &rec, int rp
         for (int u = 0; u < U; ++u) {
             const uint32_t p = (uint32_t)(tid + u * kThreads);
             if (p < staged) {
-                const size_t idx = cand_index(p);
-                sc[u] = W.cs[idx];
-                fl[u] = W.cf[idx];
-                nd[u] = W.cn[idx];
+                const Cand c = W.cand[cand_index(p)];
+                sc[u] = c.s;
+                fl[u] = c.f;
+                nd[u] = c.n;
             }
         }
 #pragma unroll
@@ -470,22 +473,20 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqRec &rec, int rp
         if (tid == 0) atomicOr(W.err, kInfoMergeSpill);
         auto each = [&](auto fn) {
             for (uint32_t p = tid; p < staged; p += kThreads) {
-                const size_t idx = cand_index(p);
-                fn(f2ord(W.cs[idx]), W.cf[idx]);
+                const Cand c = W.cand[cand_index(p)];
+                fn(f2ord(c.s), c.f);
             }
         };
         uint32_t o_star, f_star;
         block_select<kThreads>(each, k, sel, o_star, f_star, W.err);
         for (uint32_t p = tid; p < staged; p += kThreads) {
-            const size_t idx = cand_index(p);
-            const float s = W.cs[idx];
-            const uint32_t f = W.cf[idx];
-            if (key_le(f2ord(s), f, o_star, f_star)) {
+            const Cand c = W.cand[cand_index(p)];
+            if (key_le(f2ord(c.s), c.f, o_star, f_star)) {
                 const uint32_t pos = atomicAdd(&M.cnt, 1u);
                 if (pos < (uint32_t)kMergeCap) {
-                    M.s[pos] = s;
-                    M.f[pos] = f;
-                    M.n[pos] = W.cn[idx];
+                    M.s[pos] = c.s;
+                    M.f[pos] = c.f;
+                    M.n[pos] = c.n;
                 }
             }
         }
@@ -521,41 +522,57 @@ __global__ __launch_bounds__(kThreads) void k_merge(TrieDev T, WaveDev W, int rp
 
 // ---------------------------------------------------------------------- tile kernel
 // Per tile of 64 rows: masked log-softmax, then a superset of the tile's top-n.
-//   rows  a wave takes its 4 rows either densely (each lane scores its 16 codes against
-//         the 256-bit child mask; used where rows have many children) or sparsely (at
-//         CSR depths when every row of the wave has at most 64 children: the row is
-//         staged in LDS and each lane scores children j, j+16, j+32, j+48 of the CSR
-//         list). Both give the same value for every candidate.
+//   rows  lane j of a row's 16-lane group takes 16 of its codes and their bits of the
+//         row's 256-bit child mask (read from the trie's per-node masks, or built in LDS
+//         from the CSR child list at depths that have none: both give the same bits).
 //   pick  1. prefilter: the best candidate of each lane is one sample; the bin b_L where
 //            the samples' count reaches n bounds the tile's n-th best from below, so a
-//            candidate in a bin > b_L cannot make the request's top-n either;
-//         2. the survivors are compacted into LDS and binned exactly; the tile keeps every
-//            bin down to the one where its survivor count reaches n and writes them
-//            grouped by bin, with its cumulative bin counts.
-//   If the prefilter leaves more than kTileCap survivors (ties, or n above the number of
-//   lanes), an exact selection over all candidates keeps exactly the tile's top-n.
-union alignas(16) TileBuf {
-    float xs[kTileRows][256];                      // rows staged for the sparse path
-    struct {
-        float s[kTileCap];                         // survivors: score
-        uint32_t f[kTileCap];                      //   flat r * 256 + c
-        int32_t n[kTileCap];                       //   child node
-    } c;
-};
+//            candidate in a bin > b_L cannot make the request's top-n either. Each lane
+//            turns b_L into a threshold on its raw logits (with a margin far above the
+//            rounding error), so the test costs one compare per candidate;
+//         2. the survivors are binned exactly from registers (a wave skips an element
+//            slot none of its lanes needs): the histogram atomics give every survivor its
+//            place within its bin, the scan gives the bins' offsets, and the tile writes
+//            every bin down to the one where its count reaches n (a superset of its
+//            top-n) grouped by bin, with its cumulative bin counts.
+//   If that keeps more than the tile's region holds (massive ties), an exact selection
+//   over all candidates keeps exactly the tile's top-n instead.
 struct TileSmem {
-    TileBuf buf;
     uint32_t cmask[kWaves][kRowsPerWave][8];       // child masks built from CSR lists
-    uint32_t hist[kBins];                          // bin counts, then inclusive cumulative
-    uint32_t part[kWaves];
-    uint32_t nsurv, bL, bt, tot;
+    uint32_t h1[kBins];                            // bins of the lanes' best candidates
+    uint32_t h2[kBins];                            // survivors' bins, then inclusive cumulative
+    uint32_t p1[kWaves], p2[kWaves];               // wave totals of the two scans
+    uint32_t bL, bt, tot, pad;
 };
 
-constexpr int kSparseMax = 64;                     // children per row on the sparse path
+// inclusive scan over the 16 lanes of each DPP row
+__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t x) {
+    x += dpp_u<0x111, 0xF>(x);   // row_shr:1
+    x += dpp_u<0x112, 0xF>(x);   // row_shr:2
+    x += dpp_u<0x114, 0xF>(x);   // row_shr:4
+    x += dpp_u<0x118, 0xF>(x);   // row_shr:8
+    return x;
+}
+__device__ __forceinline__ uint32_t row16_sum_u(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadXor1, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadXor2, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kHalfMirror, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kMirror, 0xF, 0xF, false);
+    return v;
+}
+// Sum of the totals of waves 0..w-1 (part[] holds each wave's total; w is uniform).
+__device__ __forceinline__ uint32_t waves_before(const uint32_t *part, int w) {
+    const int lane = threadIdx.x & 63;
+    uint32_t v = lane < kWaves ? part[lane] : 0u;
+    v = row16_incl_scan(v);
+    return w ? (uint32_t)__builtin_amdgcn_readlane((int)v, w - 1) : 0u;
+}
 
 template <int DT, int NORM, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp, int n_req,
                                                    const void *__restrict__ logits, int64_t ld) {
-    constexpr int CH = Lay<DT>::CH, CW = Lay<DT>::CW, SPAN = 256 / CH, WPC = SPAN / 32;
+    constexpr int CH = Lay<DT>::CH, CW = Lay<DT>::CW, SPAN = 256 / CH;
+    static_assert(CH * CW == kElems && (SPAN / CW) * 8 <= 256, "row layout");
     __shared__ TileSmem A;
     __shared__ SelSmem sel;
 
@@ -573,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
     const int ntile = (rec.rows + kTileRows - 1) / kTileRows;
     if (tile >= ntile) return;
 
-    const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, j = lane & 15;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, j = lane & 15;
     const int level = rec.level, cp = rec.par;
     const int rt = wave * kRowsPerWave + g;                   // row within the tile
     const int r = tile * kTileRows + rt;                       // local rank in the request
@@ -581,9 +598,9 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
     const bool wave_live = tile * kTileRows + wave * kRowsPerWave < rec.rows;
     const int V = T.V;
     const uint32_t width = (uint32_t)rec.width;
-    A.hist[tid] = 0u;
+    A.h1[tid] = 0u;
+    A.h2[tid] = 0u;
     if (tid == 0) {
-        A.nsurv = 0u;
         A.bL = kBins - 1;
         A.bt = kBins - 1;
         A.tot = 0u;
@@ -603,32 +620,56 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
         load_row<DT, VEC>(logits, ld, slot, j, V, x);
     }
 
-    // 2. the row's node: child id range, and the dense mask at shallow depths
+    // 2. the row's node: first child id and this lane's child bits (chunk i holds the
+    //    CW codes i * SPAN + j * CW ...)
     const bool dense_depth = level < T.mask_depths;
     const uint32_t lo_id = T.off[level], hi_id = T.off[level + 1];
     bool ok = false;
     uint32_t cb = 0u, ce = 0u;
-    uint32_t m[8];
+    uint32_t bits[CH];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) m[w] = 0u;
+    for (int i = 0; i < CH; ++i) bits[i] = 0u;
     if (live) {
         const uint32_t n = (uint32_t)nd;
         if (n >= lo_id && n < hi_id) {
             ok = true;
             cb = T.child_begin[n];
             if (dense_depth) {
-                const u32x4 *mp = reinterpret_cast<const u32x4 *>(T.mask + (size_t)n * 8);
-                const u32x4 a = mp[0], b = mp[1];
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    m[w] = a[w];
-                    m[4 + w] = b[w];
+                for (int i = 0; i < CH; ++i) {
+                    const int c0 = i * SPAN + j * CW;
+                    bits[i] = (T.mask[(size_t)n * 8 + (c0 >> 5)] >> (c0 & 31)) & ((1u << CW) - 1u);
                 }
             } else {
                 ce = T.child_begin[n + 1];
             }
         } else if (j == 0) {
             atomicOr(W.err, kErrBadNode);
+        }
+    }
+    if (!dense_depth && wave_live) {
+        // no stored mask at this depth: build the row's 256-bit mask in LDS
+        uint32_t *cm = A.cmask[wave][g];
+        if (j < 8) cm[j] = 0u;
+        wave_lds_sync();
+        if (ok) {
+            for (uint32_t a = (cb & ~3u) + 4u * (uint32_t)j; a < ce; a += 64u) {
+                const uint32_t wv = *reinterpret_cast<const uint32_t *>(T.child_code + a);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t idx = a + (uint32_t)k;
+                    if (idx >= cb && idx < ce) {
+                        const uint32_t c = (wv >> (8 * k)) & 255u;
+                        atomicOr(&cm[c >> 5], 1u << (c & 31));
+                    }
+                }
+            }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c0 = i * SPAN + j * CW;
+            bits[i] = ok ? (cm[c0 >> 5] >> (c0 & 31)) & ((1u << CW) - 1u) : 0u;
         }
     }
     if (W.validate && live) {
@@ -638,142 +679,29 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
             if (code_of<DT>(e, j) < V && !isfinite(x[e])) bad = true;
         if (bad) atomicOr(W.err, kErrNonFinite);
     }
-    // sparse rows: every row of the wave at a CSR depth with at most kSparseMax children
-    const bool sparse = NORM == TCB_NORM_CHILDREN && !dense_depth && wave_live &&
-                        __ballot(ok && ce - cb > (uint32_t)kSparseMax) == 0ull;
-
-    // 3. candidates of this lane: up to 16 slots (dense) or 4 slots (sparse), as score,
-    //    validity bit, code and child node
-    float cand[kElems];
     uint32_t valid = 0u;
-    uint32_t ccode[4] = {0u, 0u, 0u, 0u};              // sparse: codes of slots 0..3
-    uint32_t rk0[CH], sub[CH];                        // dense: child bits and ranks per chunk
 #pragma unroll
-    for (int i = 0; i < CH; ++i) rk0[i] = sub[i] = 0u;
-    float lmax = -INFINITY;                           // this lane's best candidate
-    if (sparse) {
-        // stage the row in LDS; lane j scores children j + 16 i of the CSR list
-        float *row = A.buf.xs[rt];
-#pragma unroll
-        for (int i = 0; i < CH; ++i)
-#pragma unroll
-            for (int q4 = 0; q4 < CW; q4 += 4) {
-                f32x4 v;
-                v[0] = x[i * CW + q4 + 0];
-                v[1] = x[i * CW + q4 + 1];
-                v[2] = x[i * CW + q4 + 2];
-                v[3] = x[i * CW + q4 + 3];
-                *reinterpret_cast<f32x4 *>(row + i * SPAN + j * CW + q4) = v;
-            }
-        const uint32_t f = ok ? ce - cb : 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t k = (uint32_t)j + 16u * (uint32_t)i;
-            if (k < f) {
-                ccode[i] = T.child_code[cb + k];
-                valid |= 1u << i;
-            }
-        }
-        wave_lds_sync();
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            cand[i] = ((valid >> i) & 1u) ? row[ccode[i]] : -INFINITY;
-            mx = fmaxf(mx, cand[i]);
-        }
-        lmax = mx;
-        mx = row16_max(mx);
-        const float mxl = mx * kLog2e;
-        // The sum of exponentials follows the dense layout's order exactly (each lane adds
-        // its 16 codes in element order, then the 16-lane tree; absent children add exact
-        // zeros), so both paths give bit-identical results: the children's terms are put
-        // back at their code positions and summed the dense way.
-        wave_lds_sync();
-        const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < CH; ++i)
-#pragma unroll
-            for (int q4 = 0; q4 < CW; q4 += 4) *reinterpret_cast<f32x4 *>(row + i * SPAN + j * CW + q4) = zero4;
-        wave_lds_sync();
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if ((valid >> i) & 1u) row[ccode[i]] = __builtin_amdgcn_exp2f(fmaf(cand[i], kLog2e, -mxl));
-        wave_lds_sync();
-        float sum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < CH; ++i)
-#pragma unroll
-            for (int q4 = 0; q4 < CW; q4 += 4) {
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(row + i * SPAN + j * CW + q4);
-                sum += v[0];
-                sum += v[1];
-                sum += v[2];
-                sum += v[3];
-            }
-        sum = row16_sum(sum);
-        const float lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cand[i] = sr + (cand[i] - lse);
-        lmax = sr + (lmax - lse);
-#pragma unroll
-        for (int i = 4; i < kElems; ++i) cand[i] = -INFINITY;
-    } else if (wave_live) {
-        if (!dense_depth) {
-            // a CSR list with many children: build the 256-bit mask in LDS
-            uint32_t *cm = A.cmask[wave][g];
-            if (j < 8) cm[j] = 0u;
-            wave_lds_sync();
-            if (ok) {
-                for (uint32_t a = (cb & ~3u) + 4u * (uint32_t)j; a < ce; a += 64u) {
-                    const uint32_t wv = *reinterpret_cast<const uint32_t *>(T.child_code + a);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t idx = a + (uint32_t)k;
-                        if (idx >= cb && idx < ce) {
-                            const uint32_t c = (wv >> (8 * k)) & 255u;
-                            atomicOr(&cm[c >> 5], 1u << (c & 31));
-                        }
-                    }
-                }
-            }
-            wave_lds_sync();
-#pragma unroll
-            for (int w = 0; w < 8; ++w) m[w] = cm[w];
-        }
-        uint32_t P[8];
-        P[0] = 0u;
-#pragma unroll
-        for (int w = 1; w < 8; ++w) P[w] = P[w - 1] + (uint32_t)__popc(m[w - 1]);
-        const int wi = (j * CW) >> 5, off = (j * CW) & 31;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            uint32_t mw = 0u, pw = 0u;
-#pragma unroll
-            for (int k = 0; k < WPC; ++k) {
-                mw = (k == wi) ? m[i * WPC + k] : mw;
-                pw = (k == wi) ? P[i * WPC + k] : pw;
-            }
-            sub[i] = ok ? (mw >> off) & ((1u << CW) - 1u) : 0u;
-            rk0[i] = pw + (uint32_t)__popc(mw & ((1u << off) - 1u));
-            valid |= sub[i] << (i * CW);
-        }
+    for (int i = 0; i < CH; ++i) valid |= bits[i] << (i * CW);
+
+    // 3. masked log-softmax; codes outside the support become -inf
+    float lse = 0.0f, lbest = -INFINITY;
+    if (wave_live) {
         uint32_t sup = valid;
         if constexpr (NORM == TCB_NORM_LEVEL) {
             sup = 0u;
 #pragma unroll
             for (int e = 0; e < kElems; ++e) sup |= (ok && code_of<DT>(e, j) < V) ? (1u << e) : 0u;
         }
-        // masked log-softmax: codes outside the support become -inf
 #pragma unroll
         for (int e = 0; e < kElems; ++e) x[e] = ((sup >> e) & 1u) ? x[e] : -INFINITY;
         float mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < kElems; ++e) mx = fmaxf(mx, x[e]);
-        if constexpr (NORM == TCB_NORM_CHILDREN) {
-            lmax = mx;
-        } else {
+        float lm = mx;                                // this lane's best candidate logit
+        if constexpr (NORM == TCB_NORM_LEVEL) {
+            lm = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < kElems; ++e) lmax = fmaxf(lmax, ((valid >> e) & 1u) ? x[e] : -INFINITY);
+            for (int e = 0; e < kElems; ++e) lm = fmaxf(lm, ((valid >> e) & 1u) ? x[e] : -INFINITY);
         }
         mx = row16_max(mx);
         const float mxl = mx * kLog2e;
@@ -781,97 +709,124 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
 #pragma unroll
         for (int e = 0; e < kElems; ++e) sum += __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -mxl));
         sum = row16_sum(sum);
-        const float lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+        lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+        lbest = sr + (lm - lse);
+        // from here on x[e] is the candidate's score (-inf off the child set)
 #pragma unroll
-        for (int e = 0; e < kElems; ++e) cand[e] = sr + (x[e] - lse);
-        lmax = sr + (lmax - lse);
+        for (int e = 0; e < kElems; ++e) {
+            float sc = sr + (x[e] - lse);
+            if constexpr (NORM == TCB_NORM_LEVEL) sc = ((valid >> e) & 1u) ? sc : -INFINITY;
+            x[e] = sc;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) x[e] = -INFINITY;
     }
-    const int ns_lane = sparse ? 4 : kElems;           // slots in use (wave-uniform)
-    auto flat_of = [&](int e) -> uint32_t {
-        const uint32_t c = sparse ? ccode[e & 3] : (uint32_t)code_of<DT>(e, j);
-        return (uint32_t)r * 256u + c;
-    };
-    auto node_of = [&](int e) -> int32_t {
-        if (sparse) return (int32_t)(cb + (uint32_t)j + 16u * (uint32_t)(e & 3));
-        const int i = e / CW, q2 = e % CW;
-        return (int32_t)(cb + rk0[i] + (uint32_t)__popc(sub[i] & ((1u << q2) - 1u)));
-    };
 
     // 4. prefilter: histogram of the lanes' best candidates, bin b_L where it reaches n
-    __syncthreads();   // the zeroed histogram and counters are visible; the staged rows are read
-    if (valid) atomicAdd(&A.hist[score_bin(sref, lmax)], 1u);
+    __syncthreads();                                  // the zeroed histograms are visible
+    if (valid) atomicAdd(&A.h1[score_bin(sref, lbest)], 1u);
     __syncthreads();
     {
-        const uint32_t h = A.hist[tid];
-        const uint32_t C = block_incl_scan<kThreads>(h, A.part);
+        const uint32_t h = A.h1[tid];
+        const uint32_t incl = wave_incl_scan(h);
+        if (lane == 63) A.p1[wave] = incl;
+        __syncthreads();
+        const uint32_t C = waves_before(A.p1, wave) + incl;
         if (C >= width && C - h < width) A.bL = (uint32_t)tid;
-        A.hist[tid] = 0u;
     }
     __syncthreads();
     const uint32_t bL = A.bL;
 
-    // 5. survivors (bin <= b_L) compacted into LDS
-    uint32_t surv = 0u;
+    // 5.-6. survivors and their exact bins. A candidate in a bin <= b_L scores above
+    //    ts = sref - (b_L + 1) / kBinRes less the bin arithmetic's rounding; the margin
+    //    covers that many times over (extra survivors are binned exactly and cut at b_t).
+    //    Each element slot is one branch the wave skips when none of its lanes needs it;
+    //    all of a lane's atomics are issued before any result is used.
+    uint32_t bn[kElems], wb[kElems];
 #pragma unroll
-    for (int e = 0; e < kElems; ++e)
-        if (e < ns_lane && ((valid >> e) & 1u) && score_bin(sref, cand[e]) <= bL) surv |= 1u << e;
-    {
-        const uint32_t cnt = (uint32_t)__popc(surv);
-        const uint32_t incl = wave_incl_scan(cnt);
-        uint32_t wbase = 0u;
-        if (lane == 63 && incl) wbase = atomicAdd(&A.nsurv, incl);
-        wbase = (uint32_t)__shfl((int)wbase, 63, 64);
-        uint32_t pos = wbase + incl - cnt;
-        if (surv) {
+    for (int e = 0; e < kElems; ++e) {
+        bn[e] = kBins;                                // not a survivor
+        wb[e] = 0u;
+    }
+    if (bL < (uint32_t)(kBins - 1)) {
+        const float ts = sref - (float)(bL + 1u) * (1.0f / kBinRes);
+        const float thr = ts - (1.0f / 65536.0f) * (1.0f + 2.0f * fabsf(sref) + fabsf(ts));
 #pragma unroll
-            for (int e = 0; e < kElems; ++e) {
-                if (e < ns_lane && ((surv >> e) & 1u)) {
-                    if (pos < (uint32_t)kTileCap) {
-                        A.buf.c.s[pos] = cand[e];
-                        A.buf.c.f[pos] = flat_of(e);
-                        A.buf.c.n[pos] = node_of(e);
-                    }
-                    ++pos;
-                }
+        for (int e = 0; e < kElems; ++e) {
+            if (x[e] >= thr) {                        // -inf off the child set never passes
+                const uint32_t b = score_bin(sref, x[e]);
+                bn[e] = b;
+                wb[e] = atomicAdd(&A.h2[b], 1u);
+            }
+        }
+    } else {                                          // fewer samples than n: every candidate
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) {
+            if ((valid >> e) & 1u) {
+                const uint32_t b = score_bin(sref, x[e]);
+                bn[e] = b;
+                wb[e] = atomicAdd(&A.h2[b], 1u);
             }
         }
     }
     __syncthreads();
-    const uint32_t ns = A.nsurv;
+    uint32_t C;
+    {
+        const uint32_t h = A.h2[tid];
+        const uint32_t incl = wave_incl_scan(h);
+        if (lane == 63) A.p2[wave] = incl;
+        __syncthreads();
+        C = waves_before(A.p2, wave) + incl;
+        if (C >= width && C - h < width) A.bt = (uint32_t)tid;
+        A.h2[tid] = C;                                // this thread's bin only
+    }
+    __syncthreads();
+    const uint32_t bt = A.bt;
+    const uint32_t kept = A.h2[bt];
     const int CAPT = W.CAPT;
     const size_t reg = ((size_t)q * MT + tile) * (size_t)CAPT;
 
-    if (ns <= (uint32_t)kTileCap) {
-        // 6. exact bins of the survivors; keep bins down to where their count reaches n
-        constexpr int U = kTileCap / kThreads;
-        uint32_t wb[U], bn[U];
+    // child node ids: byte i of rk holds the rank, among the row's children, of the
+    // lane's first code in chunk i (a 16-lane scan of per-chunk child counts; every
+    // partial sum stays below 256, so the bytes never carry); node(e) = first child id
+    // + that rank + the lane's children in the chunk below element e
+    uint32_t rk;
+    {
+        uint32_t pc = 0u;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t p = (uint32_t)(tid + u * kThreads);
-            bn[u] = kBins;
-            wb[u] = 0u;
-            if (p < ns) {
-                bn[u] = score_bin(sref, A.buf.c.s[p]);
-                wb[u] = atomicAdd(&A.hist[bn[u]], 1u);
-            }
+        for (int i = 0; i < CH; ++i) pc |= (uint32_t)__popc(bits[i]) << (8 * i);
+        const uint32_t excl = row16_incl_scan(pc) - pc;
+        const uint32_t tot = row16_sum_u(pc);
+        rk = excl + tot * 0x01010100u;               // byte i: children before chunk i
+    }
+    const uint32_t flat0 = (uint32_t)r * 256u + (uint32_t)j * CW;
+    auto flat_of = [&](int e) -> uint32_t { return flat0 + (uint32_t)((e / CW) * SPAN + e % CW); };
+    auto node_of = [&](int e) -> int32_t {
+        const uint32_t below = valid & ((1u << e) - (1u << (e & ~(CW - 1))));
+        return (int32_t)(cb + ((rk >> (8 * (e / CW))) & 255u) + (uint32_t)__popc(below));
+    };
+
+    if (kept <= (uint32_t)CAPT) {
+        // 7. write bins <= b_t grouped by bin (the bins' offsets are all read first)
+        uint32_t at[kElems];
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) {
+            at[e] = 0u;
+            if (bn[e] != 0u && bn[e] <= bt) at[e] = A.h2[bn[e] - 1];
         }
-        __syncthreads();
-        const uint32_t h = A.hist[tid];
-        const uint32_t C = block_incl_scan<kThreads>(h, A.part);
-        if (C >= width && C - h < width) A.bt = (uint32_t)tid;
-        A.hist[tid] = C;
-        __syncthreads();
-        const uint32_t bt = A.bt;
-        const uint32_t kept = A.hist[bt];
+        Cand *out = W.cand + reg;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t p = (uint32_t)(tid + u * kThreads);
-            if (p < ns && bn[u] <= bt) {
-                const uint32_t dst = (bn[u] ? A.hist[bn[u] - 1] : 0u) + wb[u];
+        for (int e = 0; e < kElems; ++e) {
+            if (bn[e] <= bt) {
+                const uint32_t dst = at[e] + wb[e];
                 if (dst < kept) {
-                    W.cs[reg + dst] = A.buf.c.s[p];
-                    W.cf[reg + dst] = A.buf.c.f[p];
-                    W.cn[reg + dst] = A.buf.c.n[p];
+                    Cand c;
+                    c.s = x[e];
+                    c.f = flat_of(e);
+                    c.n = node_of(e);
+                    c.pad = 0u;
+                    out[dst] = c;
                 } else {
                     atomicOr(W.err, kErrInternal);
                 }
@@ -881,50 +836,54 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
     } else {
         // exact path: keep exactly the tile's top min(n, #candidates)
         if (tid == 0) atomicOr(W.err, kInfoTileExact);
-        const uint32_t nv = (uint32_t)__popc(valid);
-        const uint32_t total = block_incl_scan<kThreads>(nv, A.part);
+        const uint32_t total = block_incl_scan<kThreads>((uint32_t)__popc(valid), A.p1);
         if (tid == kThreads - 1) A.tot = total;
+        A.h2[tid] = 0u;                               // every thread has read kept
         __syncthreads();
         const uint32_t kt = min(width, A.tot);
         auto each = [&](auto fn) {
 #pragma unroll
             for (int e = 0; e < kElems; ++e)
-                if (e < ns_lane && ((valid >> e) & 1u)) fn(f2ord(cand[e]), flat_of(e));
+                if ((valid >> e) & 1u) fn(f2ord(x[e]), flat_of(e));
         };
         uint32_t o_star, f_star;
         block_select<kThreads>(each, kt, sel, o_star, f_star, W.err);
         uint32_t keep = 0u;
 #pragma unroll
         for (int e = 0; e < kElems; ++e)
-            if (e < ns_lane && ((valid >> e) & 1u) && key_le(f2ord(cand[e]), flat_of(e), o_star, f_star))
+            if (((valid >> e) & 1u) && key_le(f2ord(x[e]), flat_of(e), o_star, f_star))
                 keep |= 1u << e;
         uint32_t wbe[kElems];
 #pragma unroll
         for (int e = 0; e < kElems; ++e) {
             wbe[e] = 0u;
-            if ((keep >> e) & 1u) wbe[e] = atomicAdd(&A.hist[score_bin(sref, cand[e])], 1u);
+            if ((keep >> e) & 1u) wbe[e] = atomicAdd(&A.h2[score_bin(sref, x[e])], 1u);
         }
         __syncthreads();
-        const uint32_t h = A.hist[tid];
-        const uint32_t C = block_incl_scan<kThreads>(h, A.part);
-        A.hist[tid] = C;
+        const uint32_t h = A.h2[tid];
+        const uint32_t Cx = block_incl_scan<kThreads>(h, A.p1);
+        A.h2[tid] = Cx;
         __syncthreads();
-        const uint32_t kept = A.hist[kBins - 1];
+        const uint32_t kx = A.h2[kBins - 1];
 #pragma unroll
         for (int e = 0; e < kElems; ++e) {
             if ((keep >> e) & 1u) {
-                const uint32_t b = score_bin(sref, cand[e]);
-                const uint32_t dst = (b ? A.hist[b - 1] : 0u) + wbe[e];
-                if (dst < kept && dst < (uint32_t)CAPT) {
-                    W.cs[reg + dst] = cand[e];
-                    W.cf[reg + dst] = flat_of(e);
-                    W.cn[reg + dst] = node_of(e);
+                const float s = x[e];
+                const uint32_t b = score_bin(sref, s);
+                const uint32_t dst = (b ? A.h2[b - 1] : 0u) + wbe[e];
+                if (dst < kx && dst < (uint32_t)CAPT) {
+                    Cand c;
+                    c.s = s;
+                    c.f = flat_of(e);
+                    c.n = node_of(e);
+                    c.pad = 0u;
+                    W.cand[reg + dst] = c;
                 } else {
                     atomicOr(W.err, kErrInternal);
                 }
             }
         }
-        W.tcum[((size_t)q * MT + tile) * kBins + tid] = (uint16_t)C;
+        W.tcum[((size_t)q * MT + tile) * kBins + tid] = (uint16_t)Cx;
     }
 }
 

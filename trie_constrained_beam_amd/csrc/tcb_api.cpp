@@ -35,7 +35,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
     int32_t MT = 0, CAPT = 0;
     size_t node[2]{}, score[2]{}, parent_slot = 0, hist = 0, rec[2]{};
-    size_t cs = 0, cf = 0, cn = 0, tcum = 0, lmx = 0, err = 0;
+    size_t cand = 0, tcum = 0, lmx = 0, err = 0;
     size_t fin_sids = 0, fin_scores = 0, fin_items = 0, fin_counts = 0, total = 0;
 };
 
@@ -59,9 +59,7 @@ Layout make_layout(int L, int S, int R, int Bmax) {
     l.rec[0] = take(r * sizeof(tcb::ReqRec));
     l.rec[1] = take(r * sizeof(tcb::ReqRec));
     const size_t ncand = r * (size_t)l.MT * (size_t)l.CAPT;
-    l.cs = take(ncand * 4);
-    l.cf = take(ncand * 4);
-    l.cn = take(ncand * 4);
+    l.cand = take(ncand * sizeof(tcb::Cand));
     l.tcum = take(r * (size_t)l.MT * tcb::kBins * 2);
     l.lmx = take(s * 256 * 4);
     l.err = take(256);
@@ -262,9 +260,7 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
     w.hist = (uint32_t *)(ws + l.hist);
     w.rec[0] = (tcb::ReqRec *)(ws + l.rec[0]);
     w.rec[1] = (tcb::ReqRec *)(ws + l.rec[1]);
-    w.cs = (float *)(ws + l.cs);
-    w.cf = (uint32_t *)(ws + l.cf);
-    w.cn = (int32_t *)(ws + l.cn);
+    w.cand = (tcb::Cand *)(ws + l.cand);
     w.tcum = (uint16_t *)(ws + l.tcum);
     w.lmx = (float *)(ws + l.lmx);
     w.err = (uint32_t *)(ws + l.err);

@@ -26,10 +26,10 @@ constexpr int kMaxTilesPerReq = TCB_MAX_WIDTH / kTileRows;
 constexpr int kBins = 1024;
 constexpr float kBinRes = 32.0f;                      // bins per nat: 32 nats of range
 static_assert(kBins == kThreads, "one bin per thread in the scans");
-constexpr int kTileCap = 4096;                        // survivors a tile treats exactly (and keeps)
+constexpr int kTileCap = 4096;                        // candidates a tile keeps (its region)
 constexpr int kMergeCap = 4096;                       // candidates the merge stages in LDS
 static_assert(kTileCap >= TCB_MAX_WIDTH, "a tile's exact path keeps up to n_i candidates");
-static_assert(kTileCap % kThreads == 0 && kMergeCap % kThreads == 0, "whole rounds of the workgroup");
+static_assert(kMergeCap % kThreads == 0, "whole rounds of the workgroup");
 static_assert(kMergeCap >= TCB_MAX_WIDTH, "the exact merge path stages up to n_i survivors");
 constexpr int kSelBins = 1024;                        // bins of the exact selection
 
@@ -64,15 +64,20 @@ struct ReqRec {                    // one per request id, 32 bytes
     int32_t pad[2];
 };
 
+struct alignas(16) Cand {          // a tile's kept candidate, one 16-byte store / load
+    float s;                       // beam score after the step
+    uint32_t f;                    // flat index r * 256 + c within the request
+    int32_t n;                     // child node id
+    uint32_t pad;
+};
+
 struct WaveDev {
     int32_t *node[2];              // [S] trie node of each slot's row (ping-pong per request)
     float *score[2];               // [S] beam score (ping-pong per request)
     int32_t *parent_slot;          // [S] parent slot at the request's last step
     uint32_t *hist;                // [L][S] back-pointer (r << 8) | c per level
     ReqRec *rec[2];                // [R] request records; a step reads one, writes the other
-    float *cs;                     // [R][MT][CAPT] kept candidates of every tile: score
-    uint32_t *cf;                  //                                              flat r*256+c
-    int32_t *cn;                   //                                              child node
+    Cand *cand;                    // [R][MT][CAPT] kept candidates of every tile
     uint16_t *tcum;                // [R][MT][kBins] cumulative kept count of each tile by bin
     float *lmx;                    // [S][256] logits computed by the SID-range lm_head
     uint32_t *err;                 // sticky error / info bits

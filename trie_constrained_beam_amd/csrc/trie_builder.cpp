@@ -113,10 +113,9 @@ tcb_status tcb_trie_build_impl(const uint8_t *sids, int64_t n_items, int32_t L, 
         t->off[d + 1] = t->off[d] + (int64_t)P[d].size();
     }
     if (mask_depths == TCB_MASK_AUTO) {
-        // dense masks on the leading depths whose nodes have many children on average
+        // masks on every depth whose table (32 bytes per node, cumulative) fits the budget
         mask_depths = 0;
-        while (mask_depths < L &&
-               P[mask_depths + 1].size() >= (size_t)TCB_MASK_AUTO_FANOUT * P[mask_depths].size())
+        while (mask_depths < L && (uint64_t)t->off[mask_depths + 1] * 32u <= (uint64_t)TCB_MASK_AUTO_BYTES)
             ++mask_depths;
     }
     t->mask_depths = mask_depths;
