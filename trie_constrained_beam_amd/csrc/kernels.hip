@@ -355,25 +355,27 @@ struct MergeSmem {
 // ---------------------------------------------------------------------- merge
 // One workgroup per request (k_merge). Every tile's kept candidates are in its region
 // of the candidate records grouped by bin, with its cumulative kept counts in tcum.
-__device__ void merge_request(const WaveDev &W, int q, const ReqRec &rec, int rp, int ntile, float sref,
-                              MergeSmem &M, SelSmem &sel) {
+__device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, MergeSmem &M, SelSmem &sel) {
     const int tid = threadIdx.x;
     const int MT = W.MT, CAPT = W.CAPT;
     const uint16_t *tc = W.tcum + (size_t)q * MT * kBins;
     const size_t reg0 = (size_t)q * MT * CAPT;
+    // the live-row count (how many tiles wrote counts), the best row's score and the
+    // tiles' counts are all loaded at once: the counts of every tile the request could
+    // have are read and those past the live tiles are dropped
+    const int rows = W.rec[rp][q].rows;
+    const float sref = W.score[ra.par()][ra.base];
+    const int tmax = (ra.rmax() + kTileRows - 1) / kTileRows;
 
     // 1. request-wide cumulative kept counts and the boundary bin b*
+    const int ntile = (rows + kTileRows - 1) / kTileRows;
     uint32_t g = 0u;
-    {
-        int jt = 0;
-        for (; jt + 8 <= ntile; jt += 8) {
-            uint32_t a[8];
+    for (int jt = 0; jt < tmax; jt += 8) {
+        uint32_t a[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) a[u] = tc[(size_t)(jt + u) * kBins + tid];
+        for (int u = 0; u < 8; ++u) a[u] = (jt + u < tmax) ? tc[(size_t)(jt + u) * kBins + tid] : 0u;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) g += a[u];
-        }
-        for (; jt < ntile; ++jt) g += tc[(size_t)jt * kBins + tid];
+        for (int u = 0; u < 8; ++u) g += (jt + u < ntile) ? a[u] : 0u;
     }
     M.G[tid] = g;
     M.cur[tid] = 0u;
@@ -383,7 +385,7 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqRec &rec, int rp
     }
     __syncthreads();
     const uint32_t Ktot = M.G[kBins - 1];
-    const uint32_t k = min((uint32_t)rec.width, Ktot);
+    const uint32_t k = min((uint32_t)ra.width(), Ktot);
     if (g >= k && (tid == 0 || M.G[tid - 1] < k)) M.bstar = (uint32_t)tid;
     __syncthreads();
     const uint32_t bs = M.bstar;
@@ -410,9 +412,9 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqRec &rec, int rp
         return reg0 + (size_t)jt * CAPT + (p - M.toff[jt]);
     };
 
-    const int level = rec.level, np = rec.par ^ 1, S = W.S, base = rec.base;
+    const int level = ra.level(), np = ra.par() ^ 1, S = W.S, base = ra.base;
     auto write_row = [&](uint32_t rank, float score, uint32_t flat, int32_t node) {
-        if (rank >= (uint32_t)rec.width) return;      // cannot happen; never write past the request
+        if (rank >= (uint32_t)ra.width()) return;     // cannot happen; never write past the request
         const int slot = base + (int)rank;
         W.node[np][slot] = node;
         W.score[np][slot] = score;
@@ -501,23 +503,25 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqRec &rec, int rp
         }
     }
     if (tid == 0) {
-        ReqRec nr = rec;
+        ReqRec nr{};
+        nr.base = base;
+        nr.width = ra.width();
         nr.rows = (int32_t)k;
         nr.level = level + 1;
+        nr.status = kReqActive;
         nr.par = np;
         W.rec[rp ^ 1][q] = nr;
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_merge(TrieDev T, WaveDev W, int rp, int n_req) {
+__global__ __launch_bounds__(kThreads) void k_merge(TrieDev T, WaveDev W, int rp, StepReqs R) {
     __shared__ MergeSmem M;
     __shared__ SelSmem sel;
-    const int q = blockIdx.x;
-    if (q >= n_req) return;
-    const ReqRec rec = W.rec[rp][q];
-    if (rec.status != kReqActive || rec.level >= T.L || rec.rows <= 0) return;   // carried over by k_tile
-    const int ntile = (rec.rows + kTileRows - 1) / kTileRows;
-    merge_request(W, q, rec, rp, ntile, W.score[rec.par][rec.base], M, sel);
+    const int ql = blockIdx.x;
+    if (ql >= R.n) return;
+    const ReqArg ra = R.r[ql];
+    if (!ra.step()) return;                            // carried over by k_tile
+    merge_request(W, R.q0 + ql, ra, rp, M, sel);
 }
 
 // ---------------------------------------------------------------------- tile kernel
@@ -569,7 +573,7 @@ __device__ __forceinline__ uint32_t waves_before(const uint32_t *part, int w) {
 }
 
 template <int DT, int NORM, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp, int n_req,
+__global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp, StepReqs R,
                                                    const void *__restrict__ logits, int64_t ld) {
     constexpr int CH = Lay<DT>::CH, CW = Lay<DT>::CW, SPAN = 256 / CH;
     static_assert(CH * CW == kElems && (SPAN / CW) * 8 <= 256, "row layout");
@@ -579,25 +583,23 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
     const int tid = threadIdx.x;
     const int MT = W.MT;
     const int i8 = (int)(blockIdx.x >> 3);
-    const int q = (int)(blockIdx.x & 7u) + 8 * (i8 / MT);   // all tiles of q on one XCD
+    const int ql = (int)(blockIdx.x & 7u) + 8 * (i8 / MT);  // all tiles of a request on one XCD
     const int tile = i8 % MT;
-    if (q >= n_req) return;
-    const ReqRec rec = W.rec[rp][q];
-    if (rec.status != kReqActive || rec.level >= T.L || rec.rows <= 0) {
-        if (tile == 0 && tid == 0) W.rec[rp ^ 1][q] = rec;  // not stepped: carried over
+    if (ql >= R.n) return;
+    const int q = R.q0 + ql;
+    const ReqArg ra = R.r[ql];
+    if (!ra.step()) {
+        if (tile == 0 && tid == 0) W.rec[rp ^ 1][q] = W.rec[rp][q];   // not stepped: carried over
         return;
     }
-    const int ntile = (rec.rows + kTileRows - 1) / kTileRows;
-    if (tile >= ntile) return;
+    if (tile * kTileRows >= ra.rmax()) return;          // past any row the request can have
 
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, j = lane & 15;
-    const int level = rec.level, cp = rec.par;
+    const int level = ra.level(), cp = ra.par(), base = ra.base;
     const int rt = wave * kRowsPerWave + g;                   // row within the tile
     const int r = tile * kTileRows + rt;                       // local rank in the request
-    const bool live = r < rec.rows;
-    const bool wave_live = tile * kTileRows + wave * kRowsPerWave < rec.rows;
     const int V = T.V;
-    const uint32_t width = (uint32_t)rec.width;
+    const uint32_t width = (uint32_t)ra.width();
     A.h1[tid] = 0u;
     A.h2[tid] = 0u;
     if (tid == 0) {
@@ -606,19 +608,25 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
         A.tot = 0u;
     }
 
-    // 1. row state and logits (all issued before any use)
-    const float sref = W.score[cp][rec.base];          // best row of the request
+    // 1. row state and logits, all issued at once: the live-row count arrives with the
+    //    rows, which are read for every row the request can have and dropped if dead
+    const int rows = W.rec[rp][q].rows;
+    const float sref = W.score[cp][base];              // best row of the request
+    const bool in_range = r < ra.rmax();
     int32_t nd = -1;
     float sr = 0.0f;
     float x[kElems];
 #pragma unroll
     for (int e = 0; e < kElems; ++e) x[e] = 0.0f;
-    if (live) {
-        const int slot = rec.base + r;
+    if (in_range) {
+        const int slot = base + r;
         nd = W.node[cp][slot];
         sr = W.score[cp][slot];
         load_row<DT, VEC>(logits, ld, slot, j, V, x);
     }
+    if (tile * kTileRows >= rows) return;              // a tile with no live row
+    const bool live = r < rows;
+    const bool wave_live = tile * kTileRows + wave * kRowsPerWave < rows;
 
     // 2. the row's node: first child id and this lane's child bits (chunk i holds the
     //    CW codes i * SPAN + j * CW ...)
@@ -990,36 +998,36 @@ hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s) {
 }
 
 template <int DT, int NORM, bool VEC>
-static void launch_tile_t(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *logits, int64_t ld,
-                          hipStream_t s) {
-    const int groups = (n_req + 7) / 8;
-    hipLaunchKernelGGL((k_tile<DT, NORM, VEC>), dim3(8 * groups * w.MT), dim3(kThreads), 0, s, t, w, rp, n_req,
+static void launch_tile_t(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
+                          int64_t ld, hipStream_t s) {
+    const int groups = (R.n + 7) / 8;
+    hipLaunchKernelGGL((k_tile<DT, NORM, VEC>), dim3(8 * groups * w.MT), dim3(kThreads), 0, s, t, w, rp, R,
                        logits, ld);
 }
 
-hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *logits, int64_t ld,
-                       int dtype, hipStream_t s) {
-    if (n_req <= 0) return hipSuccess;
+hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
+                       int64_t ld, int dtype, hipStream_t s) {
+    if (R.n <= 0) return hipSuccess;
     // 16-byte row pieces: ld a multiple of 4 (fp32) or 8 (bf16) elements, 16-byte base
     const bool vec = t.V == 256 && (ld % (dtype == TCB_F32 ? 4 : 8)) == 0 && ((uintptr_t)logits % 16) == 0;
     const bool lvl = w.norm == TCB_NORM_LEVEL;
     if (dtype == TCB_F32) {
-        if (vec) lvl ? launch_tile_t<TCB_F32, TCB_NORM_LEVEL, true>(t, w, rp, n_req, logits, ld, s)
-                     : launch_tile_t<TCB_F32, TCB_NORM_CHILDREN, true>(t, w, rp, n_req, logits, ld, s);
-        else lvl ? launch_tile_t<TCB_F32, TCB_NORM_LEVEL, false>(t, w, rp, n_req, logits, ld, s)
-                 : launch_tile_t<TCB_F32, TCB_NORM_CHILDREN, false>(t, w, rp, n_req, logits, ld, s);
+        if (vec) lvl ? launch_tile_t<TCB_F32, TCB_NORM_LEVEL, true>(t, w, rp, R, logits, ld, s)
+                     : launch_tile_t<TCB_F32, TCB_NORM_CHILDREN, true>(t, w, rp, R, logits, ld, s);
+        else lvl ? launch_tile_t<TCB_F32, TCB_NORM_LEVEL, false>(t, w, rp, R, logits, ld, s)
+                 : launch_tile_t<TCB_F32, TCB_NORM_CHILDREN, false>(t, w, rp, R, logits, ld, s);
     } else {
-        if (vec) lvl ? launch_tile_t<TCB_BF16, TCB_NORM_LEVEL, true>(t, w, rp, n_req, logits, ld, s)
-                     : launch_tile_t<TCB_BF16, TCB_NORM_CHILDREN, true>(t, w, rp, n_req, logits, ld, s);
-        else lvl ? launch_tile_t<TCB_BF16, TCB_NORM_LEVEL, false>(t, w, rp, n_req, logits, ld, s)
-                 : launch_tile_t<TCB_BF16, TCB_NORM_CHILDREN, false>(t, w, rp, n_req, logits, ld, s);
+        if (vec) lvl ? launch_tile_t<TCB_BF16, TCB_NORM_LEVEL, true>(t, w, rp, R, logits, ld, s)
+                     : launch_tile_t<TCB_BF16, TCB_NORM_CHILDREN, true>(t, w, rp, R, logits, ld, s);
+        else lvl ? launch_tile_t<TCB_BF16, TCB_NORM_LEVEL, false>(t, w, rp, R, logits, ld, s)
+                 : launch_tile_t<TCB_BF16, TCB_NORM_CHILDREN, false>(t, w, rp, R, logits, ld, s);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, int n_req, hipStream_t s) {
-    if (n_req <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_merge, dim3(n_req), dim3(kThreads), 0, s, t, w, rp, n_req);
+hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, hipStream_t s) {
+    if (R.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_merge, dim3(R.n), dim3(kThreads), 0, s, t, w, rp, R);
     return hipGetLastError();
 }
 

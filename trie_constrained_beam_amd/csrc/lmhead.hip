@@ -34,7 +34,7 @@ constexpr int kKStep = 32;                 // K of one MFMA
 // NS = K-steps of 32 per wave (H = 4 * 32 * NS); NS = 0: any H % 128 == 0, one step
 // of loads in flight.
 template <int NS>
-__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_lmhead(TrieDev T, WaveDev W, int rp, int n_req,
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_lmhead(TrieDev T, WaveDev W, int rp, StepReqs R,
                                                       const uint16_t *__restrict__ hidden, int64_t ld, int H,
                                                       const uint16_t *__restrict__ weight,
                                                       float *__restrict__ out) {
@@ -43,12 +43,15 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     const int xcd = (int)(blockIdx.x & 7u), i8 = (int)(blockIdx.x >> 3);
     const int cblk = i8 & 3;                                  // code block 0..3
     const int gt = (i8 >> 2) * 8 + xcd;                       // row tile over (request, tile)
-    const int q = gt / MT, rt = gt - q * MT;
-    if (q >= n_req) return;
-    const ReqRec rec = W.rec[rp][q];
-    if (rec.status != kReqActive || rec.level >= T.L || rec.rows <= 0) return;
+    const int ql = gt / MT, rt = gt - ql * MT;
+    if (ql >= R.n) return;
+    const ReqArg ra = R.r[ql];
+    if (!ra.step()) return;
     const int r0 = rt * kGRows;
-    if (r0 >= rec.rows) return;
+    if (r0 >= ra.rmax()) return;
+    // operand loads are issued for every row the request can have; the live-row count
+    // arrives with them and decides which results are stored
+    const int rows_bound = ra.rmax(), base = ra.base, level = ra.level();
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kq = lane >> 4;
@@ -57,9 +60,9 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     const uint16_t *ap[4], *bp[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        const int ar = r0 + 16 * b + l16;                     // dead rows read row r0, never stored
-        ap[b] = hidden + (size_t)(rec.base + (ar < rec.rows ? ar : r0)) * (size_t)ld + k0;
-        bp[b] = weight + ((size_t)rec.level * 256 + (size_t)cblk * kGCodes + 16 * b + l16) * (size_t)H + k0;
+        const int ar = r0 + 16 * b + l16;                     // rows past the bound read row r0, never stored
+        ap[b] = hidden + (size_t)(base + (ar < rows_bound ? ar : r0)) * (size_t)ld + k0;
+        bp[b] = weight + ((size_t)level * 256 + (size_t)cblk * kGCodes + 16 * b + l16) * (size_t)H + k0;
     }
     f32x4 acc[4][4];
 #pragma unroll
@@ -110,6 +113,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
             mfma_step(av, bv);
         }
     }
+    const int rows = W.rec[rp][R.q0 + ql].rows;
     // partial blocks of the four waves, added in a fixed order; wave w finishes row block w
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -126,26 +130,26 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = r0 + 16 * wave + 4 * kq + i;
-            if (row < rec.rows) out[(size_t)(rec.base + row) * 256 + cblk * kGCodes + 16 * b + l16] = v[i];
+            if (row < rows) out[(size_t)(base + row) * 256 + cblk * kGCodes + 16 * b + l16] = v[i];
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *hidden, int64_t ld,
-                         int H, const void *weight, float *out, hipStream_t s) {
-    if (n_req <= 0) return hipSuccess;
-    const int tiles = n_req * w.MT;                           // row tiles over all requests
+hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
+                         int64_t ld, int H, const void *weight, float *out, hipStream_t s) {
+    if (R.n <= 0) return hipSuccess;
+    const int tiles = R.n * w.MT;                             // row tiles over all requests
     const int groups = (tiles + 7) / 8;
     const dim3 grid(8 * groups * 4), block(kGThreads);
     const uint16_t *h = static_cast<const uint16_t *>(hidden), *wt = static_cast<const uint16_t *>(weight);
     switch (H) {
-    case 512: hipLaunchKernelGGL(k_lmhead<4>, grid, block, 0, s, t, w, rp, n_req, h, ld, H, wt, out); break;
-    case 1024: hipLaunchKernelGGL(k_lmhead<8>, grid, block, 0, s, t, w, rp, n_req, h, ld, H, wt, out); break;
-    case 2048: hipLaunchKernelGGL(k_lmhead<16>, grid, block, 0, s, t, w, rp, n_req, h, ld, H, wt, out); break;
-    case 4096: hipLaunchKernelGGL(k_lmhead<32>, grid, block, 0, s, t, w, rp, n_req, h, ld, H, wt, out); break;
-    default: hipLaunchKernelGGL(k_lmhead<0>, grid, block, 0, s, t, w, rp, n_req, h, ld, H, wt, out); break;
+    case 512: hipLaunchKernelGGL(k_lmhead<4>, grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
+    case 1024: hipLaunchKernelGGL(k_lmhead<8>, grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
+    case 2048: hipLaunchKernelGGL(k_lmhead<16>, grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
+    case 4096: hipLaunchKernelGGL(k_lmhead<32>, grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
+    default: hipLaunchKernelGGL(k_lmhead<0>, grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
     }
     return hipGetLastError();
 }

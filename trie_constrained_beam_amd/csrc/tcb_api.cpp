@@ -350,22 +350,48 @@ static void step_done(tcb_beams *b) {
 // Launch the optional lm_head kernel through `head` (which may launch nothing), the tile
 // kernel through `tile`, then the merge kernel. With timing on, HIP events bracket the
 // three launches separately.
+// The per-request kernel arguments of one step, in launches of up to tcb::kArgReqs ids.
+static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out) {
+    const int nr = n_req_hw(b);
+    out.clear();
+    for (int q0 = 0; q0 < nr; q0 += tcb::kArgReqs) {
+        out.emplace_back();
+        tcb::StepReqs &R = out.back();
+        R.q0 = q0;
+        R.n = std::min(nr - q0, tcb::kArgReqs);
+        for (int i = 0; i < R.n; ++i) {
+            const auto &rq = b->reqs[(size_t)(q0 + i)];
+            const bool step = rq.used && rq.level < b->L;
+            const uint32_t width = step ? (uint32_t)rq.width : 0u;
+            const uint32_t rmax = rq.level == 0 ? 1u : width;        // a request starts at its root
+            const uint32_t level = step ? (uint32_t)rq.level : 0u;
+            R.r[i].base = rq.base;
+            R.r[i].bits = width | rmax << 13 | level << 26 | (step ? 1u : 0u) << 30 | (level & 1u) << 31;
+        }
+    }
+}
+
 template <class HeadLaunch, class TileLaunch>
 static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLaunch tile) {
-    const int nr = n_req_hw(b);
+    static thread_local std::vector<tcb::StepReqs> args;
+    step_args(b, args);
     const bool timed = b->timing_used < b->timing_cap;
     hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 4] : nullptr;
     // with timing on, each kernel runs timing_repeat times back to back between its events:
     // within a step every kernel rewrites the same outputs from unchanged inputs
     const int rep = timed ? b->timing_repeat : 1;
     hipError_t e = timed ? hipEventRecord(ev[0], s) : hipSuccess;
-    for (int i = 0; i < rep && e == hipSuccess; ++i) e = head(nr);
+    for (int i = 0; i < rep && e == hipSuccess; ++i)
+        for (size_t c = 0; c < args.size() && e == hipSuccess; ++c) e = head(args[c]);
     if (e != hipSuccess) return hip_fail(e, "lm_head kernel launch");
     if (timed) e = hipEventRecord(ev[1], s);
-    for (int i = 0; i < rep && e == hipSuccess; ++i) e = tile(nr);
+    for (int i = 0; i < rep && e == hipSuccess; ++i)
+        for (size_t c = 0; c < args.size() && e == hipSuccess; ++c) e = tile(args[c]);
     if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
     if (timed) e = hipEventRecord(ev[2], s);
-    for (int i = 0; i < rep && e == hipSuccess; ++i) e = tcb::launch_merge(b->tdev, b->w, b->rp, nr, s);
+    for (int i = 0; i < rep && e == hipSuccess; ++i)
+        for (size_t c = 0; c < args.size() && e == hipSuccess; ++c)
+            e = tcb::launch_merge(b->tdev, b->w, b->rp, args[c], s);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     if (timed) {
         e = hipEventRecord(ev[3], s);
@@ -385,8 +411,8 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
     tcb_status st = step_common(b);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    return run_step(b, s, [](int) { return hipSuccess; }, [&](int nr) {
-        return tcb::launch_tile(b->tdev, b->w, b->rp, nr, d_logits, ld, dtype, s);
+    return run_step(b, s, [](const tcb::StepReqs &) { return hipSuccess; }, [&](const tcb::StepReqs &R) {
+        return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, s);
     });
 }
 
@@ -403,10 +429,10 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
     hipStream_t s = (hipStream_t)stream;
     return run_step(
         b, s,
-        [&](int nr) {
-            return tcb::launch_lmhead(b->tdev, b->w, b->rp, nr, d_hidden, ld_hidden, H, d_weight, b->w.lmx, s);
+        [&](const tcb::StepReqs &R) {
+            return tcb::launch_lmhead(b->tdev, b->w, b->rp, R, d_hidden, ld_hidden, H, d_weight, b->w.lmx, s);
         },
-        [&](int nr) { return tcb::launch_tile(b->tdev, b->w, b->rp, nr, b->w.lmx, 256, TCB_F32, s); });
+        [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, b->w.lmx, 256, TCB_F32, s); });
 }
 
 tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, int32_t *d_parent_slot,

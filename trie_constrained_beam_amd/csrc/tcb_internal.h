@@ -84,6 +84,26 @@ struct WaveDev {
     int32_t S, R, MT, CAPT, Bmax, norm, validate, pad;
 };
 
+// --------------------------------------------------------------------- step arguments
+// What the host knows of every request it steps, passed by value so a kernel's first
+// loads need no device-side lookup. Only the live-row count stays on the device.
+struct ReqArg {
+    int32_t base;                  // first slot
+    uint32_t bits;                 // width | rmax << 13 | level << 26 | step << 30 | par << 31
+    __host__ __device__ int width() const { return (int)(bits & 0x1FFFu); }
+    __host__ __device__ int rmax() const { return (int)((bits >> 13) & 0x1FFFu); }   // bound on live rows
+    __host__ __device__ int level() const { return (int)((bits >> 26) & 0xFu); }
+    __host__ __device__ bool step() const { return (bits >> 30) & 1u; }
+    __host__ __device__ int par() const { return (int)(bits >> 31); }                // node/score buffer
+};
+static_assert(TCB_MAX_WIDTH < (1 << 13) && TCB_MAX_L <= 15, "ReqArg field widths");
+constexpr int kArgReqs = 400;      // requests per launch (the arguments stay under 4 KiB)
+struct StepReqs {
+    int32_t n;                     // request ids q0 .. q0 + n - 1
+    int32_t q0;
+    ReqArg r[kArgReqs];
+};
+
 // --------------------------------------------------------------------- launchers
 struct InitBatch {                 // admitted requests, passed by value
     static constexpr int kMax = 32;
@@ -102,11 +122,11 @@ hipError_t launch_clear_wave(const WaveDev &w, hipStream_t s);
 hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s);
 // A step is the tile kernel followed by the per-request merge kernel; with the SID-range
 // lm_head, the lm_head kernel first writes the logits to WaveDev::lmx.
-hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *logits,
+hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
                        int64_t ld, int dtype, hipStream_t s);
-hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, int n_req, const void *hidden,
+hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
                          int64_t ld, int H, const void *weight, float *out, hipStream_t s);
-hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, int n_req, hipStream_t s);
+hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, hipStream_t s);
 hipError_t launch_finalize(const TrieDev &t, const WaveDev &w, int rp, const FinBatch &b,
                            uint8_t *sids, float *scores, int64_t *items, int32_t *counts,
                            hipStream_t s);
