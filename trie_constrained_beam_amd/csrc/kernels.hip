@@ -370,33 +370,52 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
     // 1. request-wide cumulative kept counts and the boundary bin b*
     const int ntile = (rows + kTileRows - 1) / kTileRows;
     uint32_t g = 0u;
+    uint32_t a8[8];                                   // this bin's counts of tiles 0..7
     for (int jt = 0; jt < tmax; jt += 8) {
         uint32_t a[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) a[u] = (jt + u < tmax) ? tc[(size_t)(jt + u) * kBins + tid] : 0u;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) g += (jt + u < ntile) ? a[u] : 0u;
+        for (int u = 0; u < 8; ++u) {
+            a[u] = (jt + u < ntile) ? a[u] : 0u;
+            g += a[u];
+            if (jt == 0) a8[u] = a[u];
+        }
     }
     M.G[tid] = g;
     M.cur[tid] = 0u;
     if (tid == 0) {
         M.bstar = kBins - 1;
         M.cnt = 0u;
+        M.toff[0] = 0u;
     }
     __syncthreads();
     const uint32_t Ktot = M.G[kBins - 1];
     const uint32_t k = min((uint32_t)ra.width(), Ktot);
-    if (g >= k && (tid == 0 || M.G[tid - 1] < k)) M.bstar = (uint32_t)tid;
+    // the bin of the request's k-th candidate; the thread holding it also knows how many
+    // entries of each tile are staged (tcum_j[b*]) when the request has at most 8 tiles
+    if (g >= k && (tid == 0 || M.G[tid - 1] < k)) {
+        M.bstar = (uint32_t)tid;
+        if (ntile <= 8) {
+            uint32_t acc = 0u;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                acc += a8[u];
+                if (u < ntile) M.toff[u + 1] = acc;
+            }
+        }
+    }
     __syncthreads();
     const uint32_t bs = M.bstar;
     const uint32_t staged = M.G[bs];
-    if (tid < 64) {                                   // tiles' staged counts: tcum_j[b*]
-        const uint32_t c = tid < ntile ? (uint32_t)tc[(size_t)tid * kBins + bs] : 0u;
-        const uint32_t incl = wave_incl_scan(c);
-        if (tid < ntile) M.toff[tid + 1] = incl;
-        if (tid == 0) M.toff[0] = 0u;
+    if (ntile > 8) {                                  // more tiles: read tcum_j[b*] again
+        if (tid < 64) {
+            const uint32_t c = tid < ntile ? (uint32_t)tc[(size_t)tid * kBins + bs] : 0u;
+            const uint32_t incl = wave_incl_scan(c);
+            if (tid < ntile) M.toff[tid + 1] = incl;
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     auto tile_of = [&](uint32_t p) {                  // largest tile j with toff[j] <= p
         int lo = 0, hi = ntile - 1;
@@ -529,11 +548,12 @@ __global__ __launch_bounds__(kThreads) void k_merge(TrieDev T, WaveDev W, int rp
 //   rows  lane j of a row's 16-lane group takes 16 of its codes and their bits of the
 //         row's 256-bit child mask (read from the trie's per-node masks, or built in LDS
 //         from the CSR child list at depths that have none: both give the same bits).
-//   pick  1. prefilter: the best candidate of each lane is one sample; the bin b_L where
-//            the samples' count reaches n bounds the tile's n-th best from below, so a
-//            candidate in a bin > b_L cannot make the request's top-n either. Each lane
-//            turns b_L into a threshold on its raw logits (with a margin far above the
-//            rounding error), so the test costs one compare per candidate;
+//   pick  1. prefilter (at depths whose nodes have many children on average; elsewhere
+//            every candidate goes to step 2): the best candidate of each lane is one
+//            sample; the bin b_L where the samples' count reaches n bounds the tile's
+//            n-th best from below, so a candidate in a bin > b_L cannot make the
+//            request's top-n either. b_L becomes a score threshold (with a margin far
+//            above the rounding error), so the test costs one compare per candidate;
 //         2. the survivors are binned exactly from registers (a wave skips an element
 //            slot none of its lanes needs): the histogram atomics give every survivor its
 //            place within its bin, the scan gives the bins' offsets, and the tile writes
@@ -731,20 +751,22 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
         for (int e = 0; e < kElems; ++e) x[e] = -INFINITY;
     }
 
-    // 4. prefilter: histogram of the lanes' best candidates, bin b_L where it reaches n
+    // 4. prefilter (at depths with many children per row): histogram of the lanes' best
+    //    candidates, bin b_L where it reaches n. Elsewhere every candidate is binned exactly.
     __syncthreads();                                  // the zeroed histograms are visible
-    if (valid) atomicAdd(&A.h1[score_bin(sref, lbest)], 1u);
-    __syncthreads();
-    {
+    uint32_t bL = kBins - 1;
+    if (ra.prefilter()) {
+        if (valid) atomicAdd(&A.h1[score_bin(sref, lbest)], 1u);
+        __syncthreads();
         const uint32_t h = A.h1[tid];
         const uint32_t incl = wave_incl_scan(h);
         if (lane == 63) A.p1[wave] = incl;
         __syncthreads();
         const uint32_t C = waves_before(A.p1, wave) + incl;
         if (C >= width && C - h < width) A.bL = (uint32_t)tid;
+        __syncthreads();
+        bL = A.bL;
     }
-    __syncthreads();
-    const uint32_t bL = A.bL;
 
     // 5.-6. survivors and their exact bins. A candidate in a bin <= b_L scores above
     //    ts = sref - (b_L + 1) / kBinRes less the bin arithmetic's rounding; the margin

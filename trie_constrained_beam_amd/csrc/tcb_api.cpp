@@ -239,6 +239,9 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
     if (!b) return set_error(TCB_E_ARG, "beams_create: out of host memory");
     b->L = t->L;
     b->V = t->V;
+    for (int d = 0; d < t->L; ++d)
+        if (t->nodes_per_depth[(size_t)d + 1] >= (int64_t)tcb::kPrefilterFanout * t->nodes_per_depth[(size_t)d])
+            b->prefilter_levels |= 1u << d;
     const uint8_t *img = (const uint8_t *)t->d_image;
     b->tdev.child_begin = (const uint32_t *)(img + t->o_child_begin);
     b->tdev.child_code = img + t->o_child_code;
@@ -365,8 +368,9 @@ static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out) {
             const uint32_t width = step ? (uint32_t)rq.width : 0u;
             const uint32_t rmax = rq.level == 0 ? 1u : width;        // a request starts at its root
             const uint32_t level = step ? (uint32_t)rq.level : 0u;
+            const uint32_t pre = (b->prefilter_levels >> level) & 1u;
             R.r[i].base = rq.base;
-            R.r[i].bits = width | rmax << 13 | level << 26 | (step ? 1u : 0u) << 30 | (level & 1u) << 31;
+            R.r[i].bits = width | rmax << 13 | level << 26 | pre << 29 | (step ? 1u : 0u) << 30 | (level & 1u) << 31;
         }
     }
 }

@@ -29,6 +29,7 @@ struct tcb_beams {
     tcb::TrieDev tdev{};
     tcb::WaveDev w{};
     int32_t L = 0, V = 0;
+    uint32_t prefilter_levels = 0;         // bit d: the tile kernel prefilters rows at depth d
     int rp = 0;                            // which request-record buffer is current
     int64_t steps = 0;
     std::vector<Req> reqs;

@@ -89,14 +89,19 @@ struct WaveDev {
 // loads need no device-side lookup. Only the live-row count stays on the device.
 struct ReqArg {
     int32_t base;                  // first slot
-    uint32_t bits;                 // width | rmax << 13 | level << 26 | step << 30 | par << 31
+    uint32_t bits;                 // width | rmax << 13 | level << 26 | pre << 29 | step << 30 | par << 31
     __host__ __device__ int width() const { return (int)(bits & 0x1FFFu); }
     __host__ __device__ int rmax() const { return (int)((bits >> 13) & 0x1FFFu); }   // bound on live rows
-    __host__ __device__ int level() const { return (int)((bits >> 26) & 0xFu); }
+    __host__ __device__ int level() const { return (int)((bits >> 26) & 0x7u); }
+    __host__ __device__ bool prefilter() const { return (bits >> 29) & 1u; }        // sample-bound pruning
     __host__ __device__ bool step() const { return (bits >> 30) & 1u; }
     __host__ __device__ int par() const { return (int)(bits >> 31); }                // node/score buffer
 };
-static_assert(TCB_MAX_WIDTH < (1 << 13) && TCB_MAX_L <= 15, "ReqArg field widths");
+static_assert(TCB_MAX_WIDTH < (1 << 13) && TCB_MAX_L <= 8, "ReqArg field widths");
+// The tile kernel's prefilter pays off only where rows have many children: it is used
+// at depths whose nodes have at least this many children on average (results do not
+// depend on it).
+constexpr int kPrefilterFanout = 64;
 constexpr int kArgReqs = 400;      // requests per launch (the arguments stay under 4 KiB)
 struct StepReqs {
     int32_t n;                     // request ids q0 .. q0 + n - 1
