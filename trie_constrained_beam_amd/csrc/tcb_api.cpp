@@ -242,6 +242,7 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
     for (int d = 0; d < t->L; ++d)
         if (t->nodes_per_depth[(size_t)d + 1] >= (int64_t)tcb::kPrefilterFanout * t->nodes_per_depth[(size_t)d])
             b->prefilter_levels |= 1u << d;
+    for (int d = 0; d <= t->L; ++d) b->depth_nodes[d] = t->nodes_per_depth[(size_t)d];
     const uint8_t *img = (const uint8_t *)t->d_image;
     b->tdev.child_begin = (const uint32_t *)(img + t->o_child_begin);
     b->tdev.child_code = img + t->o_child_code;
@@ -366,7 +367,8 @@ static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out) {
             const auto &rq = b->reqs[(size_t)(q0 + i)];
             const bool step = rq.used && rq.level < b->L;
             const uint32_t width = step ? (uint32_t)rq.width : 0u;
-            const uint32_t rmax = rq.level == 0 ? 1u : width;        // a request starts at its root
+            // rows at level t are distinct depth-t prefixes, at most the beam width
+            const uint32_t rmax = (uint32_t)std::min<int64_t>(width, b->depth_nodes[rq.level < b->L ? rq.level : 0]);
             const uint32_t level = step ? (uint32_t)rq.level : 0u;
             const uint32_t pre = (b->prefilter_levels >> level) & 1u;
             R.r[i].base = rq.base;

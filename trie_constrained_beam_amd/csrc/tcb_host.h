@@ -30,6 +30,7 @@ struct tcb_beams {
     tcb::WaveDev w{};
     int32_t L = 0, V = 0;
     uint32_t prefilter_levels = 0;         // bit d: the tile kernel prefilters rows at depth d
+    int64_t depth_nodes[TCB_MAX_L + 1] = {};   // trie nodes per depth: a bound on any request's rows
     int rp = 0;                            // which request-record buffer is current
     int64_t steps = 0;
     std::vector<Req> reqs;
