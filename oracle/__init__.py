@@ -12,8 +12,8 @@ What it computes, and where the pages say so:
   * each beam's score is the sum of token log-probabilities (SPRINT summary,
     inference paragraph: a SID is scored by the sum of its tokens' log-probabilities; flashrec 0.1.0, Quickstart:
     beams are returned ranked best-first with a sequence score);
-  * selection is deterministic top-k at temperature 0 (flashrec 0.1.0,
-    Features > Serving, "API");
+  * selection is deterministic top-k at temperature 0, and a Gumbel top-k without
+    replacement above it (flashrec 0.1.0, Features > Serving, "API"; ``oracle.sample``);
   * candidates are selected globally over all (beam, child) pairs of a request
     (OneLA summary, section 2.1), and survivors keep only an index to their parent
     (OneLA summary, sections 2.4 and 3.3);
@@ -26,6 +26,10 @@ Readings of points the pages leave open are listed in the module docstrings of
 from .trie import OracleTrie
 from .beam import (widen_logits, masked_log_softmax, expand_request, decode,
                    lmhead_logits, NORM_CHILDREN, NORM_LEVEL)
+from .sample import (splitmix64, noise_uniform, gumbel, condition_on_max,
+                     expand_request_sampled, decode_sampled)
 
 __all__ = ["OracleTrie", "widen_logits", "masked_log_softmax", "expand_request",
-           "decode", "lmhead_logits", "NORM_CHILDREN", "NORM_LEVEL"]
+           "decode", "lmhead_logits", "NORM_CHILDREN", "NORM_LEVEL", "splitmix64",
+           "noise_uniform", "gumbel", "condition_on_max", "expand_request_sampled",
+           "decode_sampled"]

@@ -64,3 +64,36 @@ def beam_replay(catalog, V, width, logit_fn, norm=CHILDREN, steps=None):
         cands.sort(key=lambda t: (-t[0], t[1]))
         beams = [(s, p) for s, _, p in cands[:width]]
     return beams
+
+
+def leaf_probs(catalog, V, logit_fn, temperature):
+    """{sid: probability} of every distinct SID when each level picks a child of the
+    prefix with probability softmax(x / T) over the prefix's children (math module)."""
+    kids = _children_map(catalog)
+    out = {}
+    for sid in sorted(set(tuple(s) for s in catalog)):
+        lp = 0.0
+        for d in range(len(sid)):
+            row = [v / temperature for v in logit_fn(d, tuple(sid[:d]))]
+            lp += _logp(row, kids[tuple(sid[:d])], sid[d])
+        out[sid] = math.exp(lp)
+    return out
+
+
+def pl_inclusion(probs, k):
+    """Probability that each item is among k draws without replacement, each draw
+    picking a remaining item with probability proportional to its weight (explicit
+    enumeration of the ordered draws)."""
+    items = list(probs)
+    incl = {s: 0.0 for s in items}
+
+    def rec(chosen, p_seq, rest_mass):
+        if len(chosen) == k or len(chosen) == len(items):
+            for s in chosen:
+                incl[s] += p_seq
+            return
+        for s in items:
+            if s not in chosen:
+                rec(chosen + [s], p_seq * probs[s] / rest_mass, rest_mass - probs[s])
+    rec([], 1.0, math.fsum(probs.values()))
+    return incl

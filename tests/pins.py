@@ -353,8 +353,94 @@ def pin_decode_api(orc, seed=8):
         assert all(tuple(cat[j]) != unpack(p, 3) for j in range(item))
 
 
+# --------------------------------------------------------------------------- sampled (T > 0)
+def _sampled_inclusion(orc, cat, V, logits, T, k, N):
+    """Largest z-score, over distinct SIDs, of the sampled decode's inclusion frequency
+    (seeds 0..N-1) against the exact Plackett-Luce inclusion probability."""
+    fn = lambda d, p: logits.get(p, [0.0] * V)
+    trie = orc.OracleTrie(np.asarray(cat), V=V)
+    L = len(cat[0])
+
+    def logits_for(t, prefixes):
+        return np.stack([np.asarray(fn(t, unpack(p, t)), dtype=np.float64) for p in prefixes])
+    incl = bf.pl_inclusion(bf.leaf_probs(cat, V, fn, T), k)
+    cnt = dict.fromkeys(incl, 0)
+    for seed in range(N):
+        out = orc.decode_sampled(trie, k, logits_for, T, seed, 1)
+        sids = [unpack(p, L) for p in out["sids"]]
+        assert len(sids) == min(k, len(incl)) and len(set(sids)) == len(sids)
+        for s in sids:
+            cnt[s] += 1
+    return max(abs(cnt[s] / N - q) / math.sqrt(q * (1 - q) / N + 1e-12) for s, q in incl.items())
+
+
+def pin_sampled_plackett_luce(orc):
+    """Above temperature 0 the beams are a Gumbel top-k without replacement (flashrec
+    0.1.0, Features > Serving, "API"): over many seeds, how often each SID is returned
+    matches the exact probability that it is among k draws without replacement from the
+    tempered SID distribution (Plackett-Luce, enumerated in tests/bruteforce.py)."""
+    # an unbalanced three-level trie: one single-child chain, one 3 x 3 subtree
+    cat = [(0, 0, 0)] + [(1, a, b) for a in range(3) for b in range(3)] + [(2, 0, 0), (2, 0, 1)]
+    logits = {(): [1.5, 0.0, 0.3], (1,): [0.0, 0.2, -0.3], (1, 0): [0.1, 0.0, -0.2],
+              (1, 1): [0.0, 0.4, 0.0], (1, 2): [0.3, 0.0, 0.0], (2, 0): [0.6, 0.0, 0.0]}
+    assert _sampled_inclusion(orc, cat, 3, logits, 1.0, 3, 5000) < 4.5
+    # two levels, temperature 0.5
+    cat2 = [(0, 0), (0, 1), (0, 2), (1, 0), (2, 0), (2, 1)]
+    logits2 = {(): [0.3, 1.1, -0.4, 0.0], (0,): [0.5, -0.2, 0.9, 0.0], (1,): [0.2, 0.0, 0.0, 0.0],
+               (2,): [-1.0, 0.7, 0.0, 0.0]}
+    assert _sampled_inclusion(orc, cat2, 4, logits2, 0.5, 2, 4000) < 4.5
+
+
+def pin_sampled_key_invariants(orc, seed=9):
+    """Stochastic beam search invariants: among a beam's children the largest key equals
+    the beam's own key exactly and no child's key exceeds it; a beam's log-probability is
+    its parent's plus the child's tempered log-softmax; survivors are in key order."""
+    rng = np.random.default_rng(seed)
+    V, L = 256, 3
+    cat = [tuple(int(c) for c in rng.integers(0, 6, L)) for _ in range(150)]
+    trie = orc.OracleTrie(np.asarray(cat), V=V)
+    fn = gaussian_logit_fn(seed, V)
+
+    def logits_for(t, prefixes):
+        return np.stack([np.asarray(fn(t, unpack(p, t))) for p in prefixes])
+    T = 0.8
+    out = orc.decode_sampled(trie, 12, logits_for, T, 1234, 5)
+    prev_keys, prev_phi, prev_pref = np.zeros(1), np.zeros(1), [()]
+    for d, h in enumerate(out["history"]):
+        for r in range(len(prev_keys)):
+            sel = h["cand_parent"] == r
+            assert sel.any()
+            assert h["cand_key"][sel].max() == prev_keys[r]
+            assert (h["cand_key"][sel] <= prev_keys[r]).all()
+            row = np.asarray(fn(d, prev_pref[r]))
+            codes = h["cand_code"][sel]
+            kids = sorted(set(c[d] for c in cat if c[:d] == prev_pref[r]))
+            m = max(row[c] / T for c in kids)
+            lse = m + math.log(math.fsum(math.exp(row[c] / T - m) for c in kids))
+            want = prev_phi[r] + np.asarray([row[c] / T - lse for c in codes])
+            assert np.max(np.abs(h["cand_phi"][sel] - want)) < 1e-12
+        assert all(h["key"][i] >= h["key"][i + 1] for i in range(len(h["key"]) - 1))
+        prev_keys, prev_phi = h["key"], h["phi"]
+        prev_pref = [prev_pref[p] + (int(c),) for p, c in zip(h["parent"], h["code"])]
+
+
+def pin_sampled_noise_moments(orc):
+    """The per-child noise is standard Gumbel: mean = Euler's constant, variance = pi^2/6
+    (closed forms), and the underlying uniforms are uniform on (0, 1)."""
+    u = np.asarray([orc.noise_uniform(77, q, lv, r, c) for q in range(2) for lv in range(2)
+                    for r in range(100) for c in range(256)])
+    assert 0.0 < u.min() and u.max() < 1.0
+    assert abs(u.mean() - 0.5) < 0.005
+    hist, _ = np.histogram(u, bins=16, range=(0.0, 1.0))
+    assert hist.min() > 0.9 * u.size / 16 and hist.max() < 1.1 * u.size / 16
+    g = np.asarray([orc.gumbel(x) for x in u])
+    assert abs(g.mean() - 0.5772156649015329) < 0.02
+    assert abs(g.var() - math.pi ** 2 / 6) < 0.05
+
+
 ALL_PINS = [pin_handworked, pin_trie_numbering, pin_dedupe_lowest_row,
             pin_masked_log_softmax_vs_torch, pin_single_child_and_constant, pin_ties_lower_flat,
             pin_full_catalog_unconstrained, pin_width_one_greedy, pin_wide_equals_bruteforce,
             pin_tiny_vs_replay, pin_legality, pin_lmhead_exact, pin_bf16_widening,
-            pin_decode_api]
+            pin_decode_api, pin_sampled_plackett_luce, pin_sampled_key_invariants,
+            pin_sampled_noise_moments]

@@ -5,6 +5,7 @@ transposed operand, a flipped tie-break...). A mutant that every pin accepts wou
 mean the pins cannot tell that mistake from the method. CPU only; nothing here
 touches the HIP path.
 """
+import math
 import types
 
 import numpy as np
@@ -126,10 +127,57 @@ def _lmhead_f32(h, w):
             ob.widen_logits(w, "bf16").astype(np.float32).T).astype(np.float64)
 
 
+def _decode_sampled_mut(*, cond=None, gum=None, temp_mul=False, shared_noise=False,
+                        parent_key=True, accumulate=True):
+    """A copy of the sampled decode with one planted mistake."""
+    from oracle import sample as osm
+    cond = cond or osm.condition_on_max
+    gum = gum or osm.gumbel
+
+    def decode(trie, beam_width, logits_for, temperature, seed, req=0, norm=0):
+        prefixes = np.zeros(1, dtype=np.uint64)
+        phis, keys = np.zeros(1), np.zeros(1)
+        hist = []
+        for t in range(trie.L):
+            x = logits_for(t, prefixes)
+            V = trie.V
+            ck, cphi, cflat, cpar, ccode, cnode = [], [], [], [], [], []
+            for r in range(len(prefixes)):
+                codes, nodes = trie.children(t, prefixes[r])
+                xs = x[r] * temperature if temp_mul else x[r] / temperature
+                logp = ob.masked_log_softmax(xs, codes, norm)
+                phi = (float(phis[r]) if accumulate else 0.0) + logp
+                g = np.asarray([phi[i] + gum(osm.noise_uniform(seed, req, t, r, 0 if shared_noise else int(c)))
+                                for i, c in enumerate(codes)])
+                pk = float(keys[r]) if parent_key else 0.0
+                ck.append(np.asarray([cond(pk, float(g.max()), float(gi)) for gi in g]))
+                cphi.append(phi)
+                cflat.append(r * V + codes)
+                cpar.append(np.full(codes.size, r))
+                ccode.append(codes)
+                cnode.append(nodes)
+            key, flat = np.concatenate(ck), np.concatenate(cflat)
+            order = np.lexsort((flat, -key))
+            h = {"cand_key": key[order], "cand_phi": np.concatenate(cphi)[order],
+                 "cand_parent": np.concatenate(cpar)[order], "cand_code": np.concatenate(ccode)[order],
+                 "cand_node": np.concatenate(cnode)[order]}
+            k = min(beam_width, key.size)
+            for name in ("parent", "code", "node", "key", "phi"):
+                h[name] = h["cand_" + name][:k]
+            pref = np.asarray([int(p) for p in prefixes], dtype=np.uint64)
+            prefixes = pref[h["parent"]] * np.uint64(256) + h["code"].astype(np.uint64)
+            phis, keys = h["phi"], h["key"]
+            hist.append(h)
+        return {"sids": prefixes, "phi": phis, "keys": keys, "history": hist}
+    return decode
+
+
 def _ns(**over):
     ns = dict(OracleTrie=oracle.OracleTrie, expand_request=oracle.expand_request,
               masked_log_softmax=oracle.masked_log_softmax, decode=oracle.decode,
-              lmhead_logits=oracle.lmhead_logits, widen_logits=oracle.widen_logits)
+              lmhead_logits=oracle.lmhead_logits, widen_logits=oracle.widen_logits,
+              decode_sampled=oracle.decode_sampled, noise_uniform=oracle.noise_uniform,
+              gumbel=oracle.gumbel)
     ns.update(over)
     return types.SimpleNamespace(**ns)
 
@@ -158,6 +206,13 @@ MUTANTS = {
     "bf16_widened_wrong_shift": dict(widen_logits=_widen_shift8),
     "lmhead_operand_transposed": dict(lmhead_logits=_lmhead_transposed),
     "lmhead_fp32_accumulate": dict(lmhead_logits=_lmhead_f32),
+    "sampled_keys_not_conditioned": dict(decode_sampled=_decode_sampled_mut(cond=lambda pk, z, g: g)),
+    "sampled_gumbel_sign_flipped": dict(decode_sampled=_decode_sampled_mut(gum=lambda u: math.log(-math.log(u))),
+                                        gumbel=lambda u: math.log(-math.log(u))),
+    "sampled_temperature_multiplies": dict(decode_sampled=_decode_sampled_mut(temp_mul=True)),
+    "sampled_noise_shared_by_siblings": dict(decode_sampled=_decode_sampled_mut(shared_noise=True)),
+    "sampled_parent_key_dropped": dict(decode_sampled=_decode_sampled_mut(parent_key=False)),
+    "sampled_phi_not_accumulated": dict(decode_sampled=_decode_sampled_mut(accumulate=False)),
 }
 
 

@@ -12,7 +12,9 @@ def oracle_ns():
     return types.SimpleNamespace(
         OracleTrie=oracle.OracleTrie, expand_request=oracle.expand_request,
         masked_log_softmax=oracle.masked_log_softmax, decode=oracle.decode,
-        lmhead_logits=oracle.lmhead_logits, widen_logits=oracle.widen_logits)
+        lmhead_logits=oracle.lmhead_logits, widen_logits=oracle.widen_logits,
+        decode_sampled=oracle.decode_sampled, noise_uniform=oracle.noise_uniform,
+        gumbel=oracle.gumbel)
 
 
 @pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
