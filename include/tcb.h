@@ -156,8 +156,9 @@ tcb_status tcb_beam_init(tcb_beams *b, int32_t n, const int32_t *widths,
 /* One constrained beam step for every admitted, unfinished request ([FR] Decoding;
  * [OLA] 2.1; [SP] inference).
  *   d_logits  device [max_slots][ld] of dtype TCB_F32 or TCB_BF16; row `slot` holds
- *             the V logits of that slot's row at its request's current level. Only
- *             live rows are read. ld >= V (elements).
+ *             the V logits of that slot's row at its request's current level. Rows
+ *             of a request's slot range beyond its live rows may be read and are
+ *             ignored. ld >= V (elements).
  * Per request: candidates (r, c) for every live row r and child code c of its node,
  * scored s_r + logp(c); the best min(n_i, #candidates) by (score desc, r*V+c asc)
  * become the new rows in rank order, with parent slot base_i + r and a
@@ -165,6 +166,23 @@ tcb_status tcb_beam_init(tcb_beams *b, int32_t n, const int32_t *widths,
  * Errors: TCB_E_ARG, TCB_E_STATE (no unfinished request), TCB_E_HIP. */
 tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t dtype,
                          void *stream);
+
+/* The step above temperature 0: a Gumbel top-k without replacement over SIDs ([FR]
+ * Serving, "API": deterministic top-k at temperature 0, Gumbel top-k without
+ * replacement above it). Same arguments as tcb_beam_step plus
+ *   temperature  finite and > 0: each row's children are scored by the masked
+ *                log-softmax of x / temperature; a beam's log-probability phi is the
+ *                sum of those terms (reported as its score by tcb_beam_finalize)
+ *   seed         the noise seed of this step
+ * Every beam carries phi and a perturbed key G (root: 0, 0). Child c of row r draws
+ * g = phi_r + logp(c) + Gumbel(0, 1), the uniform coming from SplitMix64 keyed by
+ * (seed, request id, level, r, c); its key is g conditioned on the maximum over r's
+ * children being G_r (stochastic beam search), and the request keeps its best
+ * min(n_i, #candidates) children by (key desc, r*V+c asc). Over a whole decode the
+ * beams are then a sample of distinct SIDs without replacement from the tempered SID
+ * distribution. Errors as tcb_beam_step; TCB_E_ARG for a bad temperature. */
+tcb_status tcb_beam_step_sampled(tcb_beams *b, const void *d_logits, int64_t ld, int32_t dtype,
+                                 float temperature, uint64_t seed, void *stream);
 
 /* Same step with the logits computed on chip by the SID-range lm_head ([FR]
  * Decoding: lm_head only over the SID token range):
@@ -180,12 +198,14 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
                                 int32_t H, const void *d_weight, void *stream);
 
 /* Copy the current wave state into caller device buffers (any may be NULL):
- *   d_node, d_score       [max_slots]  node id and score of each slot's row
+ *   d_node, d_score       [max_slots]  node id and selection key of each slot's row
+ *   d_phi                 [max_slots]  summed log-probability of each slot's row (equal
+ *                                      to the key unless a step was sampled)
  *   d_parent_slot         [max_slots]  slot of each row's parent at the last step
  *   d_hist                [L][max_slots] back-pointer of level t: (r << 8) | c
  *   d_rows, d_level       [max_requests] live rows and levels per request id
  * Rows beyond a request's live count hold stale values. Asynchronous. */
-tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score,
+tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, float *d_phi,
                            int32_t *d_parent_slot, uint32_t *d_hist, int32_t *d_rows,
                            int32_t *d_level, void *stream);
 

@@ -40,8 +40,9 @@ def walk_prefixes(hist, base, rows, level):
     return key
 
 
-def compare_step(ref, g_parent, g_code, g_node, g_score, ctx=""):
+def compare_step(ref, g_parent, g_code, g_node, g_score, ctx="", win=WIN, tol=TOL):
     """Apply the parity rule; returns a dict of diagnostics (near-ties seen)."""
+    WIN, TOL = win, tol
     k = ref["parent"].size
     assert g_parent.size == k, f"{ctx}: kept {g_parent.size} != {k}"
     V = 256
@@ -155,3 +156,24 @@ def run_rowkeyed(catalog, widths, seed, sigma, bf16=False, mask_depths=None, nor
         run.step_and_check(t, rowkeyed_logits(seed, t, widths, sigma, bf16),
                            "bf16" if bf16 else "f32", stats, check_reqs)
     return run, stats
+
+
+# Sampled steps: keys pass through Gumbel noise and the conditioning logarithms in fp32,
+# so the window and tolerance are wider than at temperature 0.
+WIN_SAMPLED = 1e-4
+TOL_SAMPLED = 3e-4
+
+
+def compare_sampled_step(ref, post, base, k, level, ctx=""):
+    """Parity of one sampled step: the kept set and order follow the oracle's keys (up to
+    near-ties), and each survivor's key and log-probability match the oracle's."""
+    h = post["hist"][level, base:base + k].astype(np.int64)
+    r = dict(ref)
+    r["cand_score"] = ref["cand_key"]
+    d = compare_step(r, h >> 8, h & 255, post["node"][base:base + k], post["score"][base:base + k],
+                     ctx=ctx, win=WIN_SAMPLED, tol=TOL_SAMPLED)
+    pos = {int(p) * 256 + int(c): i for i, (p, c) in enumerate(zip(ref["cand_parent"], ref["cand_code"]))}
+    idx = np.asarray([pos[int(x)] for x in (h >> 8) * 256 + (h & 255)])
+    err = np.abs(ref["cand_phi"][idx] - post["phi"][base:base + k].astype(np.float64))
+    assert err.max(initial=0.0) <= TOL_SAMPLED, f"{ctx}: log-probability error {err.max()}"
+    return d

@@ -55,8 +55,9 @@ SIGNATURES = {
     "tcb_beams_create": (I32, [P, I32, I32, I32, I32, P, C.c_size_t, P, C.POINTER(P)]),
     "tcb_beam_init": (I32, [P, I32, P, P, P, P]),
     "tcb_beam_step": (I32, [P, P, I64, I32, P]),
+    "tcb_beam_step_sampled": (I32, [P, P, I64, I32, C.c_float, C.c_uint64, P]),
     "tcb_beam_step_lmhead": (I32, [P, P, I64, I32, P, P]),
-    "tcb_beam_export": (I32, [P, P, P, P, P, P, P, P]),
+    "tcb_beam_export": (I32, [P, P, P, P, P, P, P, P, P]),
     "tcb_beams_status": (I32, [P, C.POINTER(BeamsStatus)]),
     "tcb_request_level": (I32, [P, I32, C.POINTER(I32)]),
     "tcb_beams_set_validate": (I32, [P, I32]),

@@ -117,7 +117,9 @@ class Beams:
                                   bases.ctypes.data, _stream()))
         return ids, bases
 
-    def step(self, logits: torch.Tensor):
+    def step(self, logits: torch.Tensor, temperature: float = 0.0, seed: int = 0):
+        """One step. temperature 0: deterministic top-k; above 0: the Gumbel top-k
+        without replacement of tcb_beam_step_sampled with this step's noise seed."""
         if logits.dtype == torch.float32:
             dt = L.TCB_F32
         elif logits.dtype == torch.bfloat16:
@@ -128,7 +130,11 @@ class Beams:
             raise ValueError("logits must be a row-major [max_slots, ld] CUDA tensor")
         if logits.shape[0] < self.max_slots:
             raise ValueError("logits must have max_slots rows")
-        check(lib().tcb_beam_step(self._h, _ptr(logits), logits.stride(0), dt, _stream()))
+        if temperature == 0.0:
+            check(lib().tcb_beam_step(self._h, _ptr(logits), logits.stride(0), dt, _stream()))
+        else:
+            check(lib().tcb_beam_step_sampled(self._h, _ptr(logits), logits.stride(0), dt,
+                                              float(temperature), int(seed) & (2 ** 64 - 1), _stream()))
 
     def step_lmhead(self, hidden: torch.Tensor, weight: torch.Tensor):
         if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
@@ -146,11 +152,12 @@ class Beams:
         dev = self.device
         out = {"node": torch.empty(S, dtype=torch.int32, device=dev),
                "score": torch.empty(S, dtype=torch.float32, device=dev),
+               "phi": torch.empty(S, dtype=torch.float32, device=dev),
                "parent_slot": torch.empty(S, dtype=torch.int32, device=dev),
                "hist": torch.empty((Lv, S), dtype=torch.int32, device=dev),
                "rows": torch.empty(R, dtype=torch.int32, device=dev),
                "level": torch.empty(R, dtype=torch.int32, device=dev)}
-        check(lib().tcb_beam_export(self._h, _ptr(out["node"]), _ptr(out["score"]),
+        check(lib().tcb_beam_export(self._h, _ptr(out["node"]), _ptr(out["score"]), _ptr(out["phi"]),
                                     _ptr(out["parent_slot"]), _ptr(out["hist"]),
                                     _ptr(out["rows"]), _ptr(out["level"]), _stream()))
         return out

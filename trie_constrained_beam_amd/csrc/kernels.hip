@@ -346,6 +346,7 @@ struct MergeSmem {
     float s[kMergeCap];
     uint32_t f[kMergeCap];
     int32_t n[kMergeCap];
+    float phi[kMergeCap];
     uint32_t G[kBins];                             // request-wide cumulative kept count
     uint32_t cur[kBins];                           // staging cursors
     uint32_t toff[kMaxTilesPerReq + 1];            // staged entries before each tile
@@ -432,11 +433,12 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
     };
 
     const int level = ra.level(), np = ra.par() ^ 1, S = W.S, base = ra.base;
-    auto write_row = [&](uint32_t rank, float score, uint32_t flat, int32_t node) {
+    auto write_row = [&](uint32_t rank, float score, uint32_t flat, int32_t node, float phi) {
         if (rank >= (uint32_t)ra.width()) return;     // cannot happen; never write past the request
         const int slot = base + (int)rank;
         W.node[np][slot] = node;
         W.score[np][slot] = score;
+        W.phi[np][slot] = phi;
         W.parent_slot[slot] = base + (int)(flat >> 8);
         W.hist[(size_t)level * S + slot] = flat;      // (r << 8) | c
     };
@@ -444,7 +446,7 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
     if (staged <= (uint32_t)kMergeCap) {
         // 2. stage bins <= b* grouped by bin (each tile's first tcum_j[b*] entries)
         constexpr int U = kMergeCap / kThreads;
-        float sc[U];
+        float sc[U], ph[U];
         uint32_t fl[U];
         int32_t nd[U];
 #pragma unroll
@@ -455,6 +457,7 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
                 sc[u] = c.s;
                 fl[u] = c.f;
                 nd[u] = c.n;
+                ph[u] = c.phi;
             }
         }
 #pragma unroll
@@ -467,6 +470,7 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
                     M.s[pos] = sc[u];
                     M.f[pos] = fl[u];
                     M.n[pos] = nd[u];
+                    M.phi[pos] = ph[u];
                 } else {
                     atomicOr(W.err, kErrInternal);
                 }
@@ -485,7 +489,7 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
                 uint32_t r = 0u;
                 for (uint32_t qq = st; qq < en; ++qq) r += key_better(f2ord(M.s[qq]), M.f[qq], o, f) ? 1u : 0u;
                 const uint32_t rank = st + r;
-                if (rank < k) write_row(rank, s, f, M.n[p]);
+                if (rank < k) write_row(rank, s, f, M.n[p], M.phi[p]);
             }
         }
     } else {
@@ -508,6 +512,7 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
                     M.s[pos] = c.s;
                     M.f[pos] = c.f;
                     M.n[pos] = c.n;
+                    M.phi[pos] = c.phi;
                 }
             }
         }
@@ -518,7 +523,7 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
             const uint32_t o = f2ord(M.s[p]), f = M.f[p];
             uint32_t r = 0u;
             for (uint32_t qq = 0; qq < n; ++qq) r += key_better(f2ord(M.s[qq]), M.f[qq], o, f) ? 1u : 0u;
-            write_row(r, M.s[p], f, M.n[p]);
+            write_row(r, M.s[p], f, M.n[p], M.phi[p]);
         }
     }
     if (tid == 0) {
@@ -592,7 +597,49 @@ __device__ __forceinline__ uint32_t waves_before(const uint32_t *part, int w) {
     return w ? (uint32_t)__builtin_amdgcn_readlane((int)v, w - 1) : 0u;
 }
 
-template <int DT, int NORM, bool VEC>
+// SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): one output for state x.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+    uint64_t z = x + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+// The uniform draw of child `code` of the beam at local rank `rank`:
+// u = (hash >> 40 + 1/2) / 2^24 from a counter-based hash keyed by (seed, request,
+// level, rank, code). u needs 25 significant bits, so it is formed in double (near
+// u = 1 a float's rounding alone would move -log u by a relative 2^-24 / (1 - u)).
+// The child's Gumbel noise is -log(-log u).
+__device__ __forceinline__ double noise_uniform(uint64_t seed_hash, uint32_t q, uint32_t level, uint32_t rank,
+                                                uint32_t code) {
+    const uint64_t key = seed_hash ^ ((uint64_t)q << 40) ^ ((uint64_t)level << 32) ^ ((uint64_t)rank << 8) ^ code;
+    return ((double)(splitmix64(key) >> 40) + 0.5) * (1.0 / 16777216.0);
+}
+// Key of a child whose perturbed score lies delta below its siblings' maximum z, the
+// maximum being conditioned to equal the parent's key pk (stochastic beam search, Kool,
+// van Hoof and Welling, ICML 2019):
+//   key = -log(exp(-pk) - exp(-z) + exp(-(z - delta))) = pk - log1p(exp(pk - z) expm1(delta)),
+// evaluated as pk - softplus(pk - z + log expm1(delta)). Near the maximum the key moves
+// by about exp(pk - z) times delta, so delta is formed in float64 by the caller.
+__device__ __forceinline__ float conditioned_key(float pk, float pk_minus_z, float delta) {
+    if (!(delta > 0.0f)) return pk;                    // the maximum itself (and exact ties)
+    const float lem = delta < 1.0f ? logf(expm1f(delta)) : delta + log1pf(-expf(-delta));
+    const float w = pk_minus_z + lem;
+    return pk - (fmaxf(w, 0.0f) + log1pf(expf(-fabsf(w))));
+}
+__device__ __forceinline__ double row16_max_d(double v) {
+    auto step = [](double a, auto dpp) {
+        const uint64_t u = __builtin_bit_cast(uint64_t, a);
+        const uint32_t lo = (uint32_t)dpp((int)(uint32_t)u), hi = (uint32_t)dpp((int)(uint32_t)(u >> 32));
+        return fmax(a, __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo));
+    };
+    v = step(v, [](int x) { return __builtin_amdgcn_update_dpp(0, x, kQuadXor1, 0xF, 0xF, false); });
+    v = step(v, [](int x) { return __builtin_amdgcn_update_dpp(0, x, kQuadXor2, 0xF, 0xF, false); });
+    v = step(v, [](int x) { return __builtin_amdgcn_update_dpp(0, x, kHalfMirror, 0xF, 0xF, false); });
+    v = step(v, [](int x) { return __builtin_amdgcn_update_dpp(0, x, kMirror, 0xF, 0xF, false); });
+    return v;
+}
+
+template <int DT, int NORM, bool VEC, bool SAMPLE>
 __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp, StepReqs R,
                                                    const void *__restrict__ logits, int64_t ld) {
     constexpr int CH = Lay<DT>::CH, CW = Lay<DT>::CW, SPAN = 256 / CH;
@@ -634,7 +681,7 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
     const float sref = W.score[cp][base];              // best row of the request
     const bool in_range = r < ra.rmax();
     int32_t nd = -1;
-    float sr = 0.0f;
+    float sr = 0.0f, pr = 0.0f;                        // the row's key and (sampled) log-probability
     float x[kElems];
 #pragma unroll
     for (int e = 0; e < kElems; ++e) x[e] = 0.0f;
@@ -642,6 +689,7 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
         const int slot = base + r;
         nd = W.node[cp][slot];
         sr = W.score[cp][slot];
+        if constexpr (SAMPLE) pr = W.phi[cp][slot];
         load_row<DT, VEC>(logits, ld, slot, j, V, x);
     }
     if (tile * kTileRows >= rows) return;              // a tile with no live row
@@ -711,8 +759,9 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
 #pragma unroll
     for (int i = 0; i < CH; ++i) valid |= bits[i] << (i * CW);
 
-    // 3. masked log-softmax; codes outside the support become -inf
+    // 3. masked log-softmax (sampled steps: of x / T); codes outside the support become -inf
     float lse = 0.0f, lbest = -INFINITY;
+    float ph[SAMPLE ? kElems : 1];                    // sampled steps: the candidates' log-probabilities
     if (wave_live) {
         uint32_t sup = valid;
         if constexpr (NORM == TCB_NORM_LEVEL) {
@@ -720,31 +769,73 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
 #pragma unroll
             for (int e = 0; e < kElems; ++e) sup |= (ok && code_of<DT>(e, j) < V) ? (1u << e) : 0u;
         }
+        if constexpr (!SAMPLE) {
 #pragma unroll
-        for (int e = 0; e < kElems; ++e) x[e] = ((sup >> e) & 1u) ? x[e] : -INFINITY;
-        float mx = -INFINITY;
+            for (int e = 0; e < kElems; ++e) x[e] = ((sup >> e) & 1u) ? x[e] : -INFINITY;
+            float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < kElems; ++e) mx = fmaxf(mx, x[e]);
-        float lm = mx;                                // this lane's best candidate logit
-        if constexpr (NORM == TCB_NORM_LEVEL) {
-            lm = -INFINITY;
+            for (int e = 0; e < kElems; ++e) mx = fmaxf(mx, x[e]);
+            float lm = mx;                            // this lane's best candidate logit
+            if constexpr (NORM == TCB_NORM_LEVEL) {
+                lm = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < kElems; ++e) lm = fmaxf(lm, ((valid >> e) & 1u) ? x[e] : -INFINITY);
-        }
-        mx = row16_max(mx);
-        const float mxl = mx * kLog2e;
-        float sum = 0.0f;
+                for (int e = 0; e < kElems; ++e) lm = fmaxf(lm, ((valid >> e) & 1u) ? x[e] : -INFINITY);
+            }
+            mx = row16_max(mx);
+            const float mxl = mx * kLog2e;
+            float sum = 0.0f;
 #pragma unroll
-        for (int e = 0; e < kElems; ++e) sum += __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -mxl));
-        sum = row16_sum(sum);
-        lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
-        lbest = sr + (lm - lse);
-        // from here on x[e] is the candidate's score (-inf off the child set)
+            for (int e = 0; e < kElems; ++e) sum += __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -mxl));
+            sum = row16_sum(sum);
+            lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+            lbest = sr + (lm - lse);
+            // from here on x[e] is the candidate's score (-inf off the child set)
 #pragma unroll
-        for (int e = 0; e < kElems; ++e) {
-            float sc = sr + (x[e] - lse);
-            if constexpr (NORM == TCB_NORM_LEVEL) sc = ((valid >> e) & 1u) ? sc : -INFINITY;
-            x[e] = sc;
+            for (int e = 0; e < kElems; ++e) {
+                float sc = sr + (x[e] - lse);
+                if constexpr (NORM == TCB_NORM_LEVEL) sc = ((valid >> e) & 1u) ? sc : -INFINITY;
+                x[e] = sc;
+            }
+        } else {
+            // the same log-softmax of x / T, leaving x unscaled
+            const float it = R.inv_temp;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < kElems; ++e) mx = fmaxf(mx, ((sup >> e) & 1u) ? x[e] * it : -INFINITY);
+            mx = row16_max(mx);
+            const float mxl = mx * kLog2e;
+            float sum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < kElems; ++e)
+                sum += __builtin_amdgcn_exp2f(fmaf(((sup >> e) & 1u) ? x[e] * it : -INFINITY, kLog2e, -mxl));
+            sum = row16_sum(sum);
+            lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+            // Gumbel top-k without replacement over SIDs (stochastic beam search): child c
+            // draws g_c = phi_c + Gumbel noise = (pr - lse) + t_c, t_c = x_c / T + Gumbel;
+            // its key is g_c conditioned on the siblings' maximum z equalling the row's key.
+            // t_c and the gap t* - t_c are formed in float64 from the unscaled logit.
+            // From here on x[e] is the child's key.
+            const uint64_t sh = splitmix64(R.seed);
+            auto t_of = [&](int e) -> double {
+                const double u = noise_uniform(sh, (uint32_t)q, (uint32_t)level, (uint32_t)r,
+                                               (uint32_t)code_of<DT>(e, j));
+                return (double)x[e] * R.inv_temp_d - log(-log(u));
+            };
+            double tmax = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < kElems; ++e) {
+                ph[e] = pr + (x[e] * it - lse);
+                if ((valid >> e) & 1u) tmax = fmax(tmax, t_of(e));
+            }
+            tmax = row16_max_d(tmax);
+            const float pz = (float)((double)sr - (double)pr + (double)lse - tmax);   // pk - z
+#pragma unroll
+            for (int e = 0; e < kElems; ++e) {
+                float key = -INFINITY;
+                if ((valid >> e) & 1u) key = conditioned_key(sr, pz, (float)(tmax - t_of(e)));
+                x[e] = key;
+                lbest = fmaxf(lbest, key);
+            }
         }
     } else {
 #pragma unroll
@@ -855,7 +946,8 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
                     c.s = x[e];
                     c.f = flat_of(e);
                     c.n = node_of(e);
-                    c.pad = 0u;
+                    if constexpr (SAMPLE) c.phi = ph[e];
+                    else c.phi = x[e];
                     out[dst] = c;
                 } else {
                     atomicOr(W.err, kErrInternal);
@@ -906,7 +998,8 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
                     c.s = s;
                     c.f = flat_of(e);
                     c.n = node_of(e);
-                    c.pad = 0u;
+                    if constexpr (SAMPLE) c.phi = ph[e];
+                    else c.phi = s;
                     W.cand[reg + dst] = c;
                 } else {
                     atomicOr(W.err, kErrInternal);
@@ -942,6 +1035,7 @@ __global__ void k_init(WaveDev W, InitBatch b) {
     W.rec[1][b.req[i]] = r;
     W.node[0][b.base[i]] = 0;          // the root
     W.score[0][b.base[i]] = 0.0f;
+    W.phi[0][b.base[i]] = 0.0f;
 }
 
 __global__ void k_finalize(TrieDev T, WaveDev W, int rp, FinBatch fb, uint8_t *sids, float *scores,
@@ -971,7 +1065,7 @@ __global__ void k_finalize(TrieDev T, WaveDev W, int rp, FinBatch fb, uint8_t *s
                 sids[out * L + lv] = (uint8_t)(h & 255u);
                 r = h >> 8;
             }
-            scores[out] = W.score[par][slot];
+            scores[out] = W.phi[par][slot];          // summed log-probability
             items[out] = item;
         } else {
             for (int lv = 0; lv < L; ++lv) sids[out * L + lv] = 0;
@@ -990,7 +1084,8 @@ __global__ void k_finalize(TrieDev T, WaveDev W, int rp, FinBatch fb, uint8_t *s
 }
 
 // One workgroup per request id: each request's live rows from its own buffer.
-__global__ void k_export(WaveDev W, int rp, int32_t *node, float *score, int32_t *rows, int32_t *level) {
+__global__ void k_export(WaveDev W, int rp, int32_t *node, float *score, float *phi, int32_t *rows,
+                         int32_t *level) {
     const int q = blockIdx.x;
     const ReqRec r = W.rec[rp][q];
     const bool act = r.status == kReqActive;
@@ -1003,6 +1098,7 @@ __global__ void k_export(WaveDev W, int rp, int32_t *node, float *score, int32_t
         const int slot = r.base + j;
         if (node) node[slot] = W.node[r.par][slot];
         if (score) score[slot] = W.score[r.par][slot];
+        if (phi) phi[slot] = W.phi[r.par][slot];
     }
 }
 
@@ -1019,30 +1115,35 @@ hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int DT, int NORM, bool VEC>
+template <int DT, int NORM, bool VEC, bool SAMPLE>
 static void launch_tile_t(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
                           int64_t ld, hipStream_t s) {
     const int groups = (R.n + 7) / 8;
-    hipLaunchKernelGGL((k_tile<DT, NORM, VEC>), dim3(8 * groups * w.MT), dim3(kThreads), 0, s, t, w, rp, R,
-                       logits, ld);
+    hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE>), dim3(8 * groups * w.MT), dim3(kThreads), 0, s, t, w, rp,
+                       R, logits, ld);
+}
+
+template <int DT, bool SAMPLE>
+static void launch_tile_dt(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
+                           int64_t ld, bool vec, hipStream_t s) {
+    const bool lvl = w.norm == TCB_NORM_LEVEL;
+    if (vec) lvl ? launch_tile_t<DT, TCB_NORM_LEVEL, true, SAMPLE>(t, w, rp, R, logits, ld, s)
+                 : launch_tile_t<DT, TCB_NORM_CHILDREN, true, SAMPLE>(t, w, rp, R, logits, ld, s);
+    else lvl ? launch_tile_t<DT, TCB_NORM_LEVEL, false, SAMPLE>(t, w, rp, R, logits, ld, s)
+             : launch_tile_t<DT, TCB_NORM_CHILDREN, false, SAMPLE>(t, w, rp, R, logits, ld, s);
 }
 
 hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                       int64_t ld, int dtype, hipStream_t s) {
+                       int64_t ld, int dtype, bool sampled, hipStream_t s) {
     if (R.n <= 0) return hipSuccess;
     // 16-byte row pieces: ld a multiple of 4 (fp32) or 8 (bf16) elements, 16-byte base
     const bool vec = t.V == 256 && (ld % (dtype == TCB_F32 ? 4 : 8)) == 0 && ((uintptr_t)logits % 16) == 0;
-    const bool lvl = w.norm == TCB_NORM_LEVEL;
     if (dtype == TCB_F32) {
-        if (vec) lvl ? launch_tile_t<TCB_F32, TCB_NORM_LEVEL, true>(t, w, rp, R, logits, ld, s)
-                     : launch_tile_t<TCB_F32, TCB_NORM_CHILDREN, true>(t, w, rp, R, logits, ld, s);
-        else lvl ? launch_tile_t<TCB_F32, TCB_NORM_LEVEL, false>(t, w, rp, R, logits, ld, s)
-                 : launch_tile_t<TCB_F32, TCB_NORM_CHILDREN, false>(t, w, rp, R, logits, ld, s);
+        if (sampled) launch_tile_dt<TCB_F32, true>(t, w, rp, R, logits, ld, vec, s);
+        else launch_tile_dt<TCB_F32, false>(t, w, rp, R, logits, ld, vec, s);
     } else {
-        if (vec) lvl ? launch_tile_t<TCB_BF16, TCB_NORM_LEVEL, true>(t, w, rp, R, logits, ld, s)
-                     : launch_tile_t<TCB_BF16, TCB_NORM_CHILDREN, true>(t, w, rp, R, logits, ld, s);
-        else lvl ? launch_tile_t<TCB_BF16, TCB_NORM_LEVEL, false>(t, w, rp, R, logits, ld, s)
-                 : launch_tile_t<TCB_BF16, TCB_NORM_CHILDREN, false>(t, w, rp, R, logits, ld, s);
+        if (sampled) launch_tile_dt<TCB_BF16, true>(t, w, rp, R, logits, ld, vec, s);
+        else launch_tile_dt<TCB_BF16, false>(t, w, rp, R, logits, ld, vec, s);
     }
     return hipGetLastError();
 }
@@ -1059,9 +1160,9 @@ hipError_t launch_finalize(const TrieDev &t, const WaveDev &w, int rp, const Fin
     return hipGetLastError();
 }
 
-hipError_t launch_export(const WaveDev &w, int rp, int32_t *node, float *score, int32_t *rows, int32_t *level,
-                         hipStream_t s) {
-    hipLaunchKernelGGL(k_export, dim3(w.R), dim3(256), 0, s, w, rp, node, score, rows, level);
+hipError_t launch_export(const WaveDev &w, int rp, int32_t *node, float *score, float *phi, int32_t *rows,
+                         int32_t *level, hipStream_t s) {
+    hipLaunchKernelGGL(k_export, dim3(w.R), dim3(256), 0, s, w, rp, node, score, phi, rows, level);
     return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@
 // admitted between steps under a beam-row slot budget, and the rows of every admitted
 // request share each step. Requests never compete for survivors.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -34,7 +35,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
     int32_t MT = 0, CAPT = 0;
-    size_t node[2]{}, score[2]{}, parent_slot = 0, hist = 0, rec[2]{};
+    size_t node[2]{}, score[2]{}, phi[2]{}, parent_slot = 0, hist = 0, rec[2]{};
     size_t cand = 0, tcum = 0, lmx = 0, err = 0;
     size_t fin_sids = 0, fin_scores = 0, fin_items = 0, fin_counts = 0, total = 0;
 };
@@ -54,6 +55,8 @@ Layout make_layout(int L, int S, int R, int Bmax) {
     l.node[1] = take(s * 4);
     l.score[0] = take(s * 4);
     l.score[1] = take(s * 4);
+    l.phi[0] = take(s * 4);
+    l.phi[1] = take(s * 4);
     l.parent_slot = take(s * 4);
     l.hist = take((size_t)L * s * 4);
     l.rec[0] = take(r * sizeof(tcb::ReqRec));
@@ -259,6 +262,7 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
     for (int p = 0; p < 2; ++p) {
         w.node[p] = (int32_t *)(ws + l.node[p]);
         w.score[p] = (float *)(ws + l.score[p]);
+        w.phi[p] = (float *)(ws + l.phi[p]);
     }
     w.parent_slot = (int32_t *)(ws + l.parent_slot);
     w.hist = (uint32_t *)(ws + l.hist);
@@ -378,9 +382,15 @@ static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out) {
 }
 
 template <class HeadLaunch, class TileLaunch>
-static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLaunch tile) {
+static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLaunch tile, double temperature = 0.0,
+                           uint64_t seed = 0) {
     static thread_local std::vector<tcb::StepReqs> args;
     step_args(b, args);
+    for (auto &R : args) {
+        R.inv_temp_d = temperature > 0.0 ? 1.0 / temperature : 0.0;
+        R.inv_temp = (float)R.inv_temp_d;
+        R.seed = seed;
+    }
     const bool timed = b->timing_used < b->timing_cap;
     hipEvent_t *ev = timed ? &b->events[(size_t)b->timing_used * 4] : nullptr;
     // with timing on, each kernel runs timing_repeat times back to back between its events:
@@ -418,8 +428,24 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     return run_step(b, s, [](const tcb::StepReqs &) { return hipSuccess; }, [&](const tcb::StepReqs &R) {
-        return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, s);
+        return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, false, s);
     });
+}
+
+tcb_status tcb_beam_step_sampled(tcb_beams *b, const void *d_logits, int64_t ld, int32_t dtype, float temperature,
+                                 uint64_t seed, void *stream) {
+    if (!b || !d_logits) return set_error(TCB_E_ARG, "beam_step_sampled: null pointer");
+    if (dtype != TCB_F32 && dtype != TCB_BF16) return set_error(TCB_E_ARG, "beam_step_sampled: bad dtype");
+    if (ld < b->V) return set_error(TCB_E_ARG, "beam_step_sampled: ld < V");
+    if (!(temperature > 0.0f) || !std::isfinite(temperature) || !std::isfinite(1.0f / temperature))
+        return set_error(TCB_E_ARG, "beam_step_sampled: temperature must be finite and > 0");
+    tcb_status st = step_common(b);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    return run_step(
+        b, s, [](const tcb::StepReqs &) { return hipSuccess; },
+        [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, true, s); },
+        (double)temperature, seed);
 }
 
 tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_hidden, int32_t H,
@@ -438,10 +464,10 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
         [&](const tcb::StepReqs &R) {
             return tcb::launch_lmhead(b->tdev, b->w, b->rp, R, d_hidden, ld_hidden, H, d_weight, b->w.lmx, s);
         },
-        [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, b->w.lmx, 256, TCB_F32, s); });
+        [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, b->w.lmx, 256, TCB_F32, false, s); });
 }
 
-tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, int32_t *d_parent_slot,
+tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, float *d_phi, int32_t *d_parent_slot,
                            uint32_t *d_hist, int32_t *d_rows, int32_t *d_level, void *stream) {
     if (!b) return set_error(TCB_E_ARG, "beam_export: null wave");
     hipStream_t s = (hipStream_t)stream;
@@ -451,8 +477,8 @@ tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, int32_
         e = hipMemcpyAsync(d_parent_slot, b->w.parent_slot, S * 4, hipMemcpyDeviceToDevice, s);
     if (d_hist && e == hipSuccess)
         e = hipMemcpyAsync(d_hist, b->w.hist, (size_t)b->L * S * 4, hipMemcpyDeviceToDevice, s);
-    if ((d_node || d_score || d_rows || d_level) && e == hipSuccess)
-        e = tcb::launch_export(b->w, b->rp, d_node, d_score, d_rows, d_level, s);
+    if ((d_node || d_score || d_phi || d_rows || d_level) && e == hipSuccess)
+        e = tcb::launch_export(b->w, b->rp, d_node, d_score, d_phi, d_rows, d_level, s);
     if (e != hipSuccess) return hip_fail(e, "beam_export");
     return TCB_OK;
 }

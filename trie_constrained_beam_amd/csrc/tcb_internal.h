@@ -65,15 +65,16 @@ struct ReqRec {                    // one per request id, 32 bytes
 };
 
 struct alignas(16) Cand {          // a tile's kept candidate, one 16-byte store / load
-    float s;                       // beam score after the step
+    float s;                       // selection key: the beam score (sampled steps: the perturbed key)
     uint32_t f;                    // flat index r * 256 + c within the request
     int32_t n;                     // child node id
-    uint32_t pad;
+    float phi;                     // summed log-probability (equal to s at temperature 0)
 };
 
 struct WaveDev {
     int32_t *node[2];              // [S] trie node of each slot's row (ping-pong per request)
-    float *score[2];               // [S] beam score (ping-pong per request)
+    float *score[2];               // [S] selection key of the row (ping-pong per request)
+    float *phi[2];                 // [S] summed log-probability of the row (= score at T = 0)
     int32_t *parent_slot;          // [S] parent slot at the request's last step
     uint32_t *hist;                // [L][S] back-pointer (r << 8) | c per level
     ReqRec *rec[2];                // [R] request records; a step reads one, writes the other
@@ -106,6 +107,10 @@ constexpr int kArgReqs = 400;      // requests per launch (the arguments stay un
 struct StepReqs {
     int32_t n;                     // request ids q0 .. q0 + n - 1
     int32_t q0;
+    float inv_temp;                // sampled steps: 1 / temperature
+    int32_t pad;
+    double inv_temp_d;             //                the same in float64
+    uint64_t seed;                 //                noise seed
     ReqArg r[kArgReqs];
 };
 
@@ -128,14 +133,14 @@ hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s);
 // A step is the tile kernel followed by the per-request merge kernel; with the SID-range
 // lm_head, the lm_head kernel first writes the logits to WaveDev::lmx.
 hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                       int64_t ld, int dtype, hipStream_t s);
+                       int64_t ld, int dtype, bool sampled, hipStream_t s);
 hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
                          int64_t ld, int H, const void *weight, float *out, hipStream_t s);
 hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, hipStream_t s);
 hipError_t launch_finalize(const TrieDev &t, const WaveDev &w, int rp, const FinBatch &b,
                            uint8_t *sids, float *scores, int64_t *items, int32_t *counts,
                            hipStream_t s);
-hipError_t launch_export(const WaveDev &w, int rp, int32_t *node, float *score, int32_t *rows,
+hipError_t launch_export(const WaveDev &w, int rp, int32_t *node, float *score, float *phi, int32_t *rows,
                          int32_t *level, hipStream_t s);
 
 }  // namespace tcb
