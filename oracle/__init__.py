@@ -25,11 +25,11 @@ Readings of points the pages leave open are listed in the module docstrings of
 """
 from .trie import OracleTrie
 from .beam import (widen_logits, masked_log_softmax, expand_request, decode,
-                   lmhead_logits, NORM_CHILDREN, NORM_LEVEL)
+                   lmhead_logits, NORM_CHILDREN, NORM_LEVEL, NORM_OPEN)
 from .sample import (splitmix64, noise_uniform, gumbel, condition_on_max,
                      expand_request_sampled, decode_sampled)
 
 __all__ = ["OracleTrie", "widen_logits", "masked_log_softmax", "expand_request",
-           "decode", "lmhead_logits", "NORM_CHILDREN", "NORM_LEVEL", "splitmix64",
+           "decode", "lmhead_logits", "NORM_CHILDREN", "NORM_LEVEL", "NORM_OPEN", "splitmix64",
            "noise_uniform", "gumbel", "condition_on_max", "expand_request_sampled",
            "decode_sampled"]

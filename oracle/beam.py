@@ -29,6 +29,11 @@ import numpy as np
 
 NORM_CHILDREN = 0
 NORM_LEVEL = 1
+# No SID constraint (the open-vocabulary comparison of flashrec 0.1.0, Evaluation, where
+# engines without the constraint leave a share of beams outside the catalog): every code
+# of the level is a candidate, normalised over all V codes; the trie only tags a beam's
+# node, -1 once its prefix has left the catalog.
+NORM_OPEN = 2
 
 
 # --------------------------------------------------------------------------- inputs
@@ -66,6 +71,7 @@ def expand_request(trie, depth: int, prefixes, scores, logits64: np.ndarray,
 
     ``prefixes[r]`` (packed) and ``scores[r]`` describe live row r, in rank order;
     ``logits64[r]`` is row r's logits over the level's V codes, widened to float64.
+    With ``norm == NORM_OPEN`` every code is a candidate and a node is -1 off the catalog.
     Returns a dict of numpy arrays:
       cand_*   every candidate, sorted best-first (score, flat, parent, code, node)
       parent, code, node, score, prefix   the kept survivors, in rank order
@@ -75,9 +81,15 @@ def expand_request(trie, depth: int, prefixes, scores, logits64: np.ndarray,
     c_score, c_flat, c_par, c_code, c_node = [], [], [], [], []
     for r in range(R):
         codes, nodes = trie.children(depth, prefixes[r])
-        if codes.size == 0:
+        if norm == NORM_OPEN:
+            tagged = np.full(V, -1, dtype=np.int64)
+            tagged[codes] = nodes
+            codes, nodes = np.arange(V, dtype=np.int64), tagged
+            logp = masked_log_softmax(logits64[r], codes, NORM_LEVEL)
+        elif codes.size == 0:
             raise ValueError("a live row sits on a node without children")
-        logp = masked_log_softmax(logits64[r], codes, norm)
+        else:
+            logp = masked_log_softmax(logits64[r], codes, norm)
         c_score.append(float(scores[r]) + logp)
         c_flat.append(r * V + codes)
         c_par.append(np.full(codes.size, r, dtype=np.int64))
@@ -116,6 +128,6 @@ def decode(trie, beam_width: int, logits_for, norm: int = NORM_CHILDREN, n_steps
         res = expand_request(trie, t, prefixes, scores, x, beam_width, norm)
         history.append(res)
         prefixes, scores = res["prefix"], res["score"]
-    items = (np.asarray([trie.item_of(p) for p in prefixes], dtype=np.int64)
+    items = (np.asarray([trie.item_of(p) if trie.contains(p) else -1 for p in prefixes], dtype=np.int64)
              if n_steps == trie.L else None)
     return {"sids": prefixes, "scores": scores, "items": items, "history": history}

@@ -353,6 +353,49 @@ def pin_decode_api(orc, seed=8):
         assert all(tuple(cat[j]) != unpack(p, 3) for j in range(item))
 
 
+def pin_open_vocabulary(orc, seed=10):
+    """Without the SID constraint the step is the plain beam search of torch.log_softmax
+    over all V codes plus a stable descending torch.sort (library routines), whatever the
+    catalog; a beam's node is the catalog node of its prefix, -1 once the prefix has left
+    the catalog (checked against the catalog as a set); finished beams outside the
+    catalog carry item -1 (flashrec 0.1.0, Evaluation: open-vocabulary engines leave a
+    share of beams illegal, the constrained engine none)."""
+    rng = np.random.default_rng(seed)
+    for V, L, n, width in [(6, 3, 40, 9), (16, 2, 30, 12), (256, 3, 200, 20)]:
+        cat = [tuple(int(c) for c in rng.integers(0, min(V, 8), L)) for _ in range(n)]
+        prefset = set(c[:d] for c in cat for d in range(L + 1))
+        trie = orc.OracleTrie(np.asarray(cat), V=V)
+        fn = gaussian_logit_fn(seed + V, V)
+        sids, scores, hist = run_decode(orc, trie, width, fn, 2)
+        beams, sc = [()], torch.zeros(1, dtype=torch.float64)
+        for d in range(L):
+            x = torch.tensor(np.stack([fn(d, p) for p in beams]), dtype=torch.float64)
+            cand = (sc[:, None] + torch.log_softmax(x, dim=1)).reshape(-1)
+            s_sorted, idx = torch.sort(cand, descending=True, stable=True)
+            k = min(width, cand.numel())
+            beams = [beams[i // V] + (i % V,) for i in idx[:k].tolist()]
+            sc = s_sorted[:k]
+        assert beams == sids
+        assert np.max(np.abs(sc.numpy() - np.asarray(scores))) < 1e-12
+        prev = [()]
+        for d, h in enumerate(hist):
+            cur = [prev[p] + (int(c),) for p, c in zip(h["parent"], h["code"])]
+            for p, node in zip(cur, h["node"]):
+                assert (int(node) >= 0) == (p in prefset)
+                if node >= 0:
+                    assert trie.node_id(d + 1, pack(p)) == node
+            prev = cur
+
+        def logits_for(t, prefixes):
+            return np.stack([np.asarray(fn(t, unpack(p, t))) for p in prefixes])
+        out = orc.decode(trie, width, logits_for, 2)
+        for p, item in zip(out["sids"], out["items"]):
+            sid = unpack(p, L)
+            assert (item >= 0) == (sid in set(cat))
+            if item >= 0:
+                assert tuple(cat[item]) == sid
+
+
 # --------------------------------------------------------------------------- sampled (T > 0)
 def _sampled_inclusion(orc, cat, V, logits, T, k, N):
     """Largest z-score, over distinct SIDs, of the sampled decode's inclusion frequency
@@ -442,5 +485,5 @@ ALL_PINS = [pin_handworked, pin_trie_numbering, pin_dedupe_lowest_row,
             pin_masked_log_softmax_vs_torch, pin_single_child_and_constant, pin_ties_lower_flat,
             pin_full_catalog_unconstrained, pin_width_one_greedy, pin_wide_equals_bruteforce,
             pin_tiny_vs_replay, pin_legality, pin_lmhead_exact, pin_bf16_widening,
-            pin_decode_api, pin_sampled_plackett_luce, pin_sampled_key_invariants,
+            pin_decode_api, pin_open_vocabulary, pin_sampled_plackett_luce, pin_sampled_key_invariants,
             pin_sampled_noise_moments]

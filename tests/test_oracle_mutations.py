@@ -172,6 +172,11 @@ def _decode_sampled_mut(*, cond=None, gum=None, temp_mul=False, shared_noise=Fal
     return decode
 
 
+def _exp_open_constrained(trie, depth, prefixes, scores, logits64, beam_width, norm=0):
+    # open-vocabulary mode that still restricts candidates to the trie's children
+    return ob.expand_request(trie, depth, prefixes, scores, logits64, beam_width, 1 if norm == 2 else norm)
+
+
 def _ns(**over):
     ns = dict(OracleTrie=oracle.OracleTrie, expand_request=oracle.expand_request,
               masked_log_softmax=oracle.masked_log_softmax, decode=oracle.decode,
@@ -206,6 +211,7 @@ MUTANTS = {
     "bf16_widened_wrong_shift": dict(widen_logits=_widen_shift8),
     "lmhead_operand_transposed": dict(lmhead_logits=_lmhead_transposed),
     "lmhead_fp32_accumulate": dict(lmhead_logits=_lmhead_f32),
+    "open_mode_keeps_constraint": dict(expand_request=_exp_open_constrained),
     "sampled_keys_not_conditioned": dict(decode_sampled=_decode_sampled_mut(cond=lambda pk, z, g: g)),
     "sampled_gumbel_sign_flipped": dict(decode_sampled=_decode_sampled_mut(gum=lambda u: math.log(-math.log(u))),
                                         gumbel=lambda u: math.log(-math.log(u))),
