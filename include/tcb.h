@@ -60,7 +60,7 @@ enum {
 };
 
 enum { TCB_F32 = 0, TCB_BF16 = 1 };                 /* logits element type           */
-enum { TCB_NORM_CHILDREN = 0, TCB_NORM_LEVEL = 1 }; /* log-softmax normaliser        */
+enum { TCB_NORM_CHILDREN = 0, TCB_NORM_LEVEL = 1, TCB_NORM_OPEN = 2 }; /* normaliser / constraint */
 
 #define TCB_MAX_L 8
 #define TCB_MAX_V 256
@@ -133,8 +133,13 @@ tcb_status tcb_beams_workspace_bytes(const tcb_trie *t, int32_t max_slots,
 
 /* Create a decode wave over an uploaded trie ([FR] Decoding, "Scheduling": rows of
  * different requests share a step under a beam-row slot budget).
- *   norm   TCB_NORM_CHILDREN (log-softmax over the node's children) or
- *          TCB_NORM_LEVEL (over all V codes of the level, then masked)
+ *   norm   TCB_NORM_CHILDREN (log-softmax over the node's children),
+ *          TCB_NORM_LEVEL (over all V codes of the level, then masked), or
+ *          TCB_NORM_OPEN: no SID constraint, as an open-vocabulary engine decodes
+ *          ([FR] Evaluation compares the share of illegal beams with and without
+ *          the constraint): every code is a candidate, normalised over all V
+ *          codes; a row whose prefix has left the catalog has node -1, and such
+ *          beams are finalised with item -1
  *   d_ws   caller-owned device workspace of ws_bytes >= tcb_beams_workspace_bytes,
  *          256-byte aligned; the wave initialises it on `stream`.
  * Errors: TCB_E_ARG, TCB_E_STATE (trie not uploaded), TCB_E_WORKSPACE, TCB_E_HIP. */

@@ -22,7 +22,9 @@ than that; the readings taken here (each also listed in the design doc):
     Flood, OOPSLA 2014), keyed by (seed, request id, level, parent rank, code):
         h = sm64(sm64(seed) ^ req << 40 ^ level << 32 ^ rank << 8 ^ code)
         u = ((h >> 40) + 1/2) / 2^24,   Gumbel = -log(-log u);
-  * the score returned with a beam is phi; beams are ranked by G.
+  * the score returned with a beam is phi; beams are ranked by G;
+  * without the SID constraint (NORM_OPEN) every code is a candidate, as in
+    ``oracle.beam``.
 """
 from __future__ import annotations
 
@@ -30,7 +32,7 @@ import math
 
 import numpy as np
 
-from .beam import masked_log_softmax, NORM_CHILDREN
+from .beam import masked_log_softmax, NORM_CHILDREN, NORM_LEVEL, NORM_OPEN
 
 _M64 = (1 << 64) - 1
 
@@ -81,9 +83,15 @@ def expand_request_sampled(trie, depth: int, prefixes, phis, keys, logits64: np.
     ck, cphi, cflat, cpar, ccode, cnode = [], [], [], [], [], []
     for r in range(len(prefixes)):
         codes, nodes = trie.children(depth, prefixes[r])
-        if codes.size == 0:
+        if norm == NORM_OPEN:                       # no constraint: every code, nodes tagged
+            tagged = np.full(V, -1, dtype=np.int64)
+            tagged[codes] = nodes
+            codes, nodes = np.arange(V, dtype=np.int64), tagged
+            logp = masked_log_softmax(logits64[r] / temperature, codes, NORM_LEVEL)
+        elif codes.size == 0:
             raise ValueError("a live row sits on a node without children")
-        logp = masked_log_softmax(logits64[r] / temperature, codes, norm)
+        else:
+            logp = masked_log_softmax(logits64[r] / temperature, codes, norm)
         phi = float(phis[r]) + logp
         g = np.asarray([phi[i] + gumbel(noise_uniform(seed, req, depth, r, int(c)))
                         for i, c in enumerate(codes)])

@@ -96,7 +96,7 @@ class Run:
         self.otrie = oracle.OracleTrie(self.catalog.astype(np.int64), V=V)
         self.V = V
         self.L = self.catalog.shape[1]
-        self.norm = 0 if norm == "children" else 1
+        self.norm = {"children": 0, "level": 1, "open": 2}[norm]
         self.max_slots = max_slots or int(sum(self.widths))
         self.max_width = max_width or max(self.widths)
         self.beams = Beams(self.trie, self.max_slots, len(self.widths), self.max_width, norm=norm)

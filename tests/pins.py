@@ -397,19 +397,21 @@ def pin_open_vocabulary(orc, seed=10):
 
 
 # --------------------------------------------------------------------------- sampled (T > 0)
-def _sampled_inclusion(orc, cat, V, logits, T, k, N):
+def _sampled_inclusion(orc, cat, V, logits, T, k, N, norm=0):
     """Largest z-score, over distinct SIDs, of the sampled decode's inclusion frequency
-    (seeds 0..N-1) against the exact Plackett-Luce inclusion probability."""
+    (seeds 0..N-1) against the exact Plackett-Luce inclusion probability. Without the
+    constraint (norm 2) the SIDs are every code tuple, not the catalog."""
     fn = lambda d, p: logits.get(p, [0.0] * V)
     trie = orc.OracleTrie(np.asarray(cat), V=V)
     L = len(cat[0])
 
     def logits_for(t, prefixes):
         return np.stack([np.asarray(fn(t, unpack(p, t)), dtype=np.float64) for p in prefixes])
-    incl = bf.pl_inclusion(bf.leaf_probs(cat, V, fn, T), k)
+    space = cat if norm != 2 else list(itertools.product(range(V), repeat=L))
+    incl = bf.pl_inclusion(bf.leaf_probs(space, V, fn, T), k)
     cnt = dict.fromkeys(incl, 0)
     for seed in range(N):
-        out = orc.decode_sampled(trie, k, logits_for, T, seed, 1)
+        out = orc.decode_sampled(trie, k, logits_for, T, seed, 1, norm)
         sids = [unpack(p, L) for p in out["sids"]]
         assert len(sids) == min(k, len(incl)) and len(set(sids)) == len(sids)
         for s in sids:
@@ -432,6 +434,9 @@ def pin_sampled_plackett_luce(orc):
     logits2 = {(): [0.3, 1.1, -0.4, 0.0], (0,): [0.5, -0.2, 0.9, 0.0], (1,): [0.2, 0.0, 0.0, 0.0],
                (2,): [-1.0, 0.7, 0.0, 0.0]}
     assert _sampled_inclusion(orc, cat2, 4, logits2, 0.5, 2, 4000) < 4.5
+    # no constraint: a partial catalog, SIDs drawn from all 3 x 3 code pairs
+    logits3 = {(): [0.4, -0.3, 0.0], (0,): [0.2, 0.9, -0.5], (1,): [0.0, 0.3, 0.1], (2,): [-0.6, 0.0, 0.5]}
+    assert _sampled_inclusion(orc, [(0, 1), (2, 2)], 3, logits3, 0.8, 3, 3000, norm=2) < 4.5
 
 
 def pin_sampled_key_invariants(orc, seed=9):

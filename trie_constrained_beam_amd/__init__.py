@@ -5,8 +5,8 @@ include/tcb.h); this package is its Python binding (``Trie``, ``Beams``) plus th
 seeded workload generators in ``synth``.
 """
 from . import _lib
-from .api import Beams, Trie
+from .api import Beams, Trie, invalid_rate
 from ._lib import TcbError
 from .wave import run_wave
 
-__all__ = ["Beams", "Trie", "TcbError", "run_wave"]
+__all__ = ["Beams", "Trie", "TcbError", "run_wave", "invalid_rate"]

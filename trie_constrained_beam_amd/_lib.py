@@ -15,7 +15,7 @@ TCB_OK = 0
 ERRORS = {-1: "TCB_E_ARG", -2: "TCB_E_RANGE", -3: "TCB_E_BUDGET", -4: "TCB_E_STATE",
           -5: "TCB_E_WORKSPACE", -6: "TCB_E_HIP", -7: "TCB_E_NONFINITE", -8: "TCB_E_DEVICE"}
 TCB_F32, TCB_BF16 = 0, 1
-TCB_NORM_CHILDREN, TCB_NORM_LEVEL = 0, 1
+TCB_NORM_CHILDREN, TCB_NORM_LEVEL, TCB_NORM_OPEN = 0, 1, 2
 TCB_MAX_L = 8
 TCB_MAX_WIDTH = 4096
 TCB_MASK_AUTO = -1

@@ -93,7 +93,7 @@ class Beams:
         check(lib().tcb_beams_workspace_bytes(trie.handle, max_slots, max_requests, max_width,
                                               C.byref(nb)))
         self.ws = torch.empty(int(nb.value), dtype=torch.uint8, device=device)
-        n = {"children": L.TCB_NORM_CHILDREN, "level": L.TCB_NORM_LEVEL}[norm]
+        n = {"children": L.TCB_NORM_CHILDREN, "level": L.TCB_NORM_LEVEL, "open": L.TCB_NORM_OPEN}[norm]
         h = C.c_void_p()
         check(lib().tcb_beams_create(trie.handle, max_slots, max_requests, max_width, n,
                                      _ptr(self.ws), int(nb.value), _stream(), C.byref(h)))
@@ -216,3 +216,17 @@ class Beams:
                                              _ptr(out["scores"]), _ptr(out["items"]),
                                              _ptr(out["counts"]), _stream()))
         return out
+
+
+def invalid_rate(out) -> float:
+    """Share of returned beams that are not catalog SIDs (item < 0) in a finalize result:
+    0 under the SID constraint; the open-vocabulary comparison of flashrec 0.1.0,
+    Evaluation reports how many beams an unconstrained decode leaves illegal."""
+    items, counts = out["items"], out["counts"]
+    if isinstance(items, torch.Tensor):
+        items, counts = items.cpu().numpy(), counts.cpu().numpy()
+    total = int(np.sum(counts))
+    if total == 0:
+        return 0.0
+    bad = sum(int(np.sum(items[i, :int(c)] < 0)) for i, c in enumerate(counts))
+    return bad / total

@@ -719,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
             } else {
                 ce = T.child_begin[n + 1];
             }
-        } else if (j == 0) {
+        } else if (j == 0 && !(NORM == TCB_NORM_OPEN && nd == -1)) {   // -1: off the catalog (open)
             atomicOr(W.err, kErrBadNode);
         }
     }
@@ -755,9 +755,15 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
             if (code_of<DT>(e, j) < V && !isfinite(x[e])) bad = true;
         if (bad) atomicOr(W.err, kErrNonFinite);
     }
-    uint32_t valid = 0u;
+    uint32_t tv = 0u;                                 // this lane's codes that are trie children
 #pragma unroll
-    for (int i = 0; i < CH; ++i) valid |= bits[i] << (i * CW);
+    for (int i = 0; i < CH; ++i) tv |= bits[i] << (i * CW);
+    uint32_t valid = tv;                              // this lane's candidates
+    if constexpr (NORM == TCB_NORM_OPEN) {            // no constraint: every code of a live row
+        valid = 0u;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) valid |= (live && code_of<DT>(e, j) < V) ? (1u << e) : 0u;
+    }
 
     // 3. masked log-softmax (sampled steps: of x / T); codes outside the support become -inf
     float lse = 0.0f, lbest = -INFINITY;
@@ -924,8 +930,10 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
     const uint32_t flat0 = (uint32_t)r * 256u + (uint32_t)j * CW;
     auto flat_of = [&](int e) -> uint32_t { return flat0 + (uint32_t)((e / CW) * SPAN + e % CW); };
     auto node_of = [&](int e) -> int32_t {
-        const uint32_t below = valid & ((1u << e) - (1u << (e & ~(CW - 1))));
-        return (int32_t)(cb + ((rk >> (8 * (e / CW))) & 255u) + (uint32_t)__popc(below));
+        const uint32_t below = tv & ((1u << e) - (1u << (e & ~(CW - 1))));
+        const int32_t n = (int32_t)(cb + ((rk >> (8 * (e / CW))) & 255u) + (uint32_t)__popc(below));
+        if constexpr (NORM == TCB_NORM_OPEN) return ((tv >> e) & 1u) ? n : -1;   // -1: off the catalog
+        return n;
     };
 
     if (kept <= (uint32_t)CAPT) {
@@ -1054,7 +1062,7 @@ __global__ void k_finalize(TrieDev T, WaveDev W, int rp, FinBatch fb, uint8_t *s
             const uint32_t node = (uint32_t)W.node[par][slot];
             int64_t item = -1;
             if (node >= leaf0 && node < leaf1) item = T.leaf_item[node - leaf0];
-            else atomicOr(W.err, kErrBadNode);
+            else if (!(W.norm == TCB_NORM_OPEN && (int32_t)node == -1)) atomicOr(W.err, kErrBadNode);
             uint32_t r = (uint32_t)j;
             for (int lv = L - 1; lv >= 0; --lv) {
                 if (r >= (uint32_t)rec.width) {      // corrupt back-pointer: never read past the request
@@ -1123,14 +1131,21 @@ static void launch_tile_t(const TrieDev &t, const WaveDev &w, int rp, const Step
                        R, logits, ld);
 }
 
+template <int DT, bool SAMPLE, bool VEC>
+static void launch_tile_v(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
+                          int64_t ld, hipStream_t s) {
+    switch (w.norm) {
+    case TCB_NORM_LEVEL: launch_tile_t<DT, TCB_NORM_LEVEL, VEC, SAMPLE>(t, w, rp, R, logits, ld, s); break;
+    case TCB_NORM_OPEN: launch_tile_t<DT, TCB_NORM_OPEN, VEC, SAMPLE>(t, w, rp, R, logits, ld, s); break;
+    default: launch_tile_t<DT, TCB_NORM_CHILDREN, VEC, SAMPLE>(t, w, rp, R, logits, ld, s); break;
+    }
+}
+
 template <int DT, bool SAMPLE>
 static void launch_tile_dt(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
                            int64_t ld, bool vec, hipStream_t s) {
-    const bool lvl = w.norm == TCB_NORM_LEVEL;
-    if (vec) lvl ? launch_tile_t<DT, TCB_NORM_LEVEL, true, SAMPLE>(t, w, rp, R, logits, ld, s)
-                 : launch_tile_t<DT, TCB_NORM_CHILDREN, true, SAMPLE>(t, w, rp, R, logits, ld, s);
-    else lvl ? launch_tile_t<DT, TCB_NORM_LEVEL, false, SAMPLE>(t, w, rp, R, logits, ld, s)
-             : launch_tile_t<DT, TCB_NORM_CHILDREN, false, SAMPLE>(t, w, rp, R, logits, ld, s);
+    if (vec) launch_tile_v<DT, SAMPLE, true>(t, w, rp, R, logits, ld, s);
+    else launch_tile_v<DT, SAMPLE, false>(t, w, rp, R, logits, ld, s);
 }
 
 hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,

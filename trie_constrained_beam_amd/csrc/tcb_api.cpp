@@ -230,7 +230,7 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
                             void *stream, tcb_beams **out) {
     if (!t || !d_ws || !out) return set_error(TCB_E_ARG, "beams_create: null pointer");
     if (!t->d_image) return set_error(TCB_E_STATE, "beams_create: trie not uploaded");
-    if (norm != TCB_NORM_CHILDREN && norm != TCB_NORM_LEVEL)
+    if (norm != TCB_NORM_CHILDREN && norm != TCB_NORM_LEVEL && norm != TCB_NORM_OPEN)
         return set_error(TCB_E_ARG, "beams_create: bad norm");
     size_t need = 0;
     tcb_status st = tcb_beams_workspace_bytes(t, max_slots, max_requests, max_width, &need);
@@ -371,10 +371,13 @@ static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out) {
             const auto &rq = b->reqs[(size_t)(q0 + i)];
             const bool step = rq.used && rq.level < b->L;
             const uint32_t width = step ? (uint32_t)rq.width : 0u;
-            // rows at level t are distinct depth-t prefixes, at most the beam width
-            const uint32_t rmax = (uint32_t)std::min<int64_t>(width, b->depth_nodes[rq.level < b->L ? rq.level : 0]);
+            // rows at level t are distinct depth-t prefixes (catalog prefixes unless the wave
+            // is unconstrained), at most the beam width
+            const bool open = b->w.norm == TCB_NORM_OPEN;
+            const int64_t prefixes = rq.level == 0 ? 1 : open ? (int64_t)width : b->depth_nodes[rq.level < b->L ? rq.level : 0];
+            const uint32_t rmax = (uint32_t)std::min<int64_t>(width, prefixes);
             const uint32_t level = step ? (uint32_t)rq.level : 0u;
-            const uint32_t pre = (b->prefilter_levels >> level) & 1u;
+            const uint32_t pre = open ? 1u : (b->prefilter_levels >> level) & 1u;
             R.r[i].base = rq.base;
             R.r[i].bits = width | rmax << 13 | level << 26 | pre << 29 | (step ? 1u : 0u) << 30 | (level & 1u) << 31;
         }
