@@ -56,7 +56,9 @@ def _decode(cat, widths, norm, seed=83):
 def test_invalid_rate_constrained_vs_open():
     """Same logits, same kernels: the constrained decode returns only catalog SIDs, the
     open one leaves a share outside (items -1), and every item it does return is right."""
-    cat = synth.catalog(50_000, 4, ("zipf",) * 4, [84, 1])
+    # dense enough (30k of the 65,536 code pairs) that random logits land in the catalog
+    # often; with sparse catalogs nearly every open beam is illegal
+    cat = synth.catalog(30_000, 2, ("uniform",) * 2, [84, 1])
     keys = synth.pack_sids(cat)
     first = {}
     for row, k in enumerate(keys.tolist()):
