@@ -228,8 +228,22 @@ tcb_status tcb_beams_status(const tcb_beams *b, tcb_beams_status_t *out);
 /* Level of a request (host-side; levels advance by one per step). */
 tcb_status tcb_request_level(const tcb_beams *b, int32_t req_id, int32_t *level);
 
-/* Turn on non-finite checks of every logit read (sticky TCB_E_NONFINITE). */
+/* Turn on non-finite checks of every logit read (sticky TCB_E_NONFINITE). With sector
+ * gathering (below) only the logits of a row's children are read and checked. */
 tcb_status tcb_beams_set_validate(tcb_beams *b, int32_t on);
+
+/* How tcb_beam_step / tcb_beam_step_sampled read a row's logits ([FR] Decoding: a
+ * dense or CSR-sparse trie; the sparse reading applied to the logits traffic):
+ *   TCB_READ_AUTO    whole rows at depths with many children per row; where a row's
+ *                    children touch under half of its 64-byte sectors on average, only
+ *                    the 16-byte pieces holding a child (default)
+ *   TCB_READ_DENSE   always whole rows
+ *   TCB_READ_GATHER  always only the pieces holding a child
+ * Results are bitwise the same in every mode; only traffic and latency differ. Sector
+ * gathering applies to the children normaliser with 16-byte aligned rows (otherwise
+ * rows are read whole). Errors: TCB_E_ARG. */
+enum { TCB_READ_AUTO = 0, TCB_READ_DENSE = 1, TCB_READ_GATHER = 2 };
+tcb_status tcb_beams_set_read_mode(tcb_beams *b, int32_t mode);
 
 /* Synchronise `stream` and report a sticky device error, if any. */
 tcb_status tcb_beam_check(tcb_beams *b, void *stream);

@@ -89,7 +89,7 @@ class Run:
     """One wave on the GPU plus the matching oracle trie."""
 
     def __init__(self, catalog, widths, V=256, mask_depths=None, norm="children", max_slots=None,
-                 max_width=None):
+                 max_width=None, read_mode="auto"):
         self.catalog = np.ascontiguousarray(catalog, dtype=np.uint8)
         self.widths = list(widths)
         self.trie = Trie(self.catalog, V=V, mask_depths=mask_depths, device="cuda")
@@ -100,6 +100,7 @@ class Run:
         self.max_slots = max_slots or int(sum(self.widths))
         self.max_width = max_width or max(self.widths)
         self.beams = Beams(self.trie, self.max_slots, len(self.widths), self.max_width, norm=norm)
+        self.beams.set_read_mode(read_mode)
         self.ids, self.bases = self.beams.init(np.asarray(self.widths, dtype=np.int32))
 
     def state(self):
@@ -149,8 +150,8 @@ def rowkeyed_logits(seed, t, widths, sigma, bf16):
 
 
 def run_rowkeyed(catalog, widths, seed, sigma, bf16=False, mask_depths=None, norm="children",
-                 check_reqs=None):
-    run = Run(catalog, widths, mask_depths=mask_depths, norm=norm)
+                 check_reqs=None, read_mode="auto"):
+    run = Run(catalog, widths, mask_depths=mask_depths, norm=norm, read_mode=read_mode)
     stats = {}
     for t in range(run.L):
         run.step_and_check(t, rowkeyed_logits(seed, t, widths, sigma, bf16),

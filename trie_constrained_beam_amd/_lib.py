@@ -16,6 +16,7 @@ ERRORS = {-1: "TCB_E_ARG", -2: "TCB_E_RANGE", -3: "TCB_E_BUDGET", -4: "TCB_E_STA
           -5: "TCB_E_WORKSPACE", -6: "TCB_E_HIP", -7: "TCB_E_NONFINITE", -8: "TCB_E_DEVICE"}
 TCB_F32, TCB_BF16 = 0, 1
 TCB_NORM_CHILDREN, TCB_NORM_LEVEL, TCB_NORM_OPEN = 0, 1, 2
+TCB_READ_AUTO, TCB_READ_DENSE, TCB_READ_GATHER = 0, 1, 2
 TCB_MAX_L = 8
 TCB_MAX_WIDTH = 4096
 TCB_MASK_AUTO = -1
@@ -61,6 +62,7 @@ SIGNATURES = {
     "tcb_beams_status": (I32, [P, C.POINTER(BeamsStatus)]),
     "tcb_request_level": (I32, [P, I32, C.POINTER(I32)]),
     "tcb_beams_set_validate": (I32, [P, I32]),
+    "tcb_beams_set_read_mode": (I32, [P, I32]),
     "tcb_beam_check": (I32, [P, P]),
     "tcb_beam_finalize": (I32, [P, I32, P, P, P, P, P, P]),
     "tcb_beam_finalize_device": (I32, [P, I32, P, P, P, P, P, P]),

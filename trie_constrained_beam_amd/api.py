@@ -33,6 +33,7 @@ class Trie:
         h = C.c_void_p()
         check(lib().tcb_build_trie(sids.ctypes.data, n, depth, V, mask_depths, C.byref(h)))
         self._h = h
+        self._destroy = lib().tcb_trie_destroy        # held so teardown at exit needs no globals
         self.info = L.TrieInfo()
         check(lib().tcb_trie_info(h, C.byref(self.info)))
         self.L, self.V = int(self.info.L), int(self.info.V)
@@ -42,8 +43,8 @@ class Trie:
             self.upload(device)
 
     def __del__(self):
-        if getattr(self, "_h", None) and lib is not None:
-            lib().tcb_trie_destroy(self._h)
+        if getattr(self, "_h", None):
+            self._destroy(self._h)
             self._h = None
 
     @property
@@ -98,11 +99,12 @@ class Beams:
         check(lib().tcb_beams_create(trie.handle, max_slots, max_requests, max_width, n,
                                      _ptr(self.ws), int(nb.value), _stream(), C.byref(h)))
         self._h = h
+        self._destroy = lib().tcb_beams_destroy
         self.device = device
 
     def __del__(self):
         if getattr(self, "_h", None):
-            lib().tcb_beams_destroy(self._h)
+            self._destroy(self._h)
             self._h = None
 
     @property
@@ -161,6 +163,11 @@ class Beams:
                                     _ptr(out["parent_slot"]), _ptr(out["hist"]),
                                     _ptr(out["rows"]), _ptr(out["level"]), _stream()))
         return out
+
+    def set_read_mode(self, mode: str = "auto"):
+        """'auto', 'dense' or 'gather': how rows' logits are read (results identical)."""
+        m = {"auto": L.TCB_READ_AUTO, "dense": L.TCB_READ_DENSE, "gather": L.TCB_READ_GATHER}[mode]
+        check(lib().tcb_beams_set_read_mode(self._h, m))
 
     def set_validate(self, on: bool = True):
         check(lib().tcb_beams_set_validate(self._h, 1 if on else 0))

@@ -341,6 +341,37 @@ __device__ __forceinline__ void load_row(const void *logits, int64_t ld, int slo
     }
 }
 
+// Only the chunks of a row whose bit in `chunks` is set (16-byte pieces, as load_row reads
+// them); the others stay 0. Used where a row's children touch few of its sectors.
+template <int DT>
+__device__ __forceinline__ void load_row_chunks(const void *logits, int64_t ld, int slot, int j, uint32_t chunks,
+                                                float (&x)[kElems]) {
+    if constexpr (DT == TCB_F32) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(static_cast<const float *>(logits) + (size_t)slot * (size_t)ld);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if ((chunks >> i) & 1u) {
+                const f32x4 v = __builtin_nontemporal_load(p + 16 * i + j);
+                x[4 * i + 0] = v[0];
+                x[4 * i + 1] = v[1];
+                x[4 * i + 2] = v[2];
+                x[4 * i + 3] = v[3];
+            }
+    } else {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(logits) + (size_t)slot * (size_t)ld);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            if ((chunks >> i) & 1u) {
+                const u32x4 v = __builtin_nontemporal_load(p + 16 * i + j);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    x[8 * i + 2 * w] = __uint_as_float(v[w] << 16);
+                    x[8 * i + 2 * w + 1] = __uint_as_float(v[w] & 0xffff0000u);
+                }
+            }
+    }
+}
+
 // ---------------------------------------------------------------------- shared memory
 struct MergeSmem {
     float s[kMergeCap];
@@ -365,7 +396,7 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
     // tiles' counts are all loaded at once: the counts of every tile the request could
     // have are read and those past the live tiles are dropped
     const int rows = W.rec[rp][q].rows;
-    const float sref = W.score[ra.par()][ra.base];
+    const float sref = W.score[ra.par()][ra.base()];
     const int tmax = (ra.rmax() + kTileRows - 1) / kTileRows;
 
     // 1. request-wide cumulative kept counts and the boundary bin b*
@@ -432,7 +463,7 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
         return reg0 + (size_t)jt * CAPT + (p - M.toff[jt]);
     };
 
-    const int level = ra.level(), np = ra.par() ^ 1, S = W.S, base = ra.base;
+    const int level = ra.level(), np = ra.par() ^ 1, S = W.S, base = ra.base();
     auto write_row = [&](uint32_t rank, float score, uint32_t flat, int32_t node, float phi) {
         if (rank >= (uint32_t)ra.width()) return;     // cannot happen; never write past the request
         const int slot = base + (int)rank;
@@ -662,7 +693,7 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
     if (tile * kTileRows >= ra.rmax()) return;          // past any row the request can have
 
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, j = lane & 15;
-    const int level = ra.level(), cp = ra.par(), base = ra.base;
+    const int level = ra.level(), cp = ra.par(), base = ra.base();
     const int rt = wave * kRowsPerWave + g;                   // row within the tile
     const int r = tile * kTileRows + rt;                       // local rank in the request
     const int V = T.V;
@@ -685,12 +716,15 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
     float x[kElems];
 #pragma unroll
     for (int e = 0; e < kElems; ++e) x[e] = 0.0f;
+    // at depths with few children per row the logits wait for the trie and only the
+    // 16-byte pieces holding a child are read (the rest is masked off either way)
+    const bool gather = VEC && ra.gather();
     if (in_range) {
         const int slot = base + r;
         nd = W.node[cp][slot];
         sr = W.score[cp][slot];
         if constexpr (SAMPLE) pr = W.phi[cp][slot];
-        load_row<DT, VEC>(logits, ld, slot, j, V, x);
+        if (!gather) load_row<DT, VEC>(logits, ld, slot, j, V, x);
     }
     if (tile * kTileRows >= rows) return;              // a tile with no live row
     const bool live = r < rows;
@@ -747,6 +781,12 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
             const int c0 = i * SPAN + j * CW;
             bits[i] = ok ? (cm[c0 >> 5] >> (c0 & 31)) & ((1u << CW) - 1u) : 0u;
         }
+    }
+    if (gather && live) {
+        uint32_t chunks = 0u;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) chunks |= (bits[i] != 0u ? 1u : 0u) << i;
+        load_row_chunks<DT>(logits, ld, base + r, j, chunks, x);
     }
     if (W.validate && live) {
         bool bad = false;

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     if (r0 >= ra.rmax()) return;
     // operand loads are issued for every row the request can have; the live-row count
     // arrives with them and decides which results are stored
-    const int rows_bound = ra.rmax(), base = ra.base, level = ra.level();
+    const int rows_bound = ra.rmax(), base = ra.base(), level = ra.level();
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kq = lane >> 4;

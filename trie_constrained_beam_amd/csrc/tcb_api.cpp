@@ -246,6 +246,15 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
         if (t->nodes_per_depth[(size_t)d + 1] >= (int64_t)tcb::kPrefilterFanout * t->nodes_per_depth[(size_t)d])
             b->prefilter_levels |= 1u << d;
     for (int d = 0; d <= t->L; ++d) b->depth_nodes[d] = t->nodes_per_depth[(size_t)d];
+    // gather at depths where a row's children touch under half of its 64-byte sectors
+    // (16 of them for fp32 rows, 8 for bf16), by the depth's mean fanout
+    for (int d = 0; d < t->L; ++d) {
+        const double fan = (double)t->nodes_per_depth[(size_t)d + 1] / (double)t->nodes_per_depth[(size_t)d];
+        for (int k = 0; k < 2; ++k) {
+            const double sectors = k == 0 ? 16.0 : 8.0;
+            if (1.0 - std::pow(1.0 - 1.0 / sectors, fan) < 0.5) b->gather_levels[k] |= 1u << d;
+        }
+    }
     const uint8_t *img = (const uint8_t *)t->d_image;
     b->tdev.child_begin = (const uint32_t *)(img + t->o_child_begin);
     b->tdev.child_code = img + t->o_child_code;
@@ -359,7 +368,7 @@ static void step_done(tcb_beams *b) {
 // kernel through `tile`, then the merge kernel. With timing on, HIP events bracket the
 // three launches separately.
 // The per-request kernel arguments of one step, in launches of up to tcb::kArgReqs ids.
-static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out) {
+static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out, int dt_index) {
     const int nr = n_req_hw(b);
     out.clear();
     for (int q0 = 0; q0 < nr; q0 += tcb::kArgReqs) {
@@ -378,17 +387,28 @@ static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out) {
             const uint32_t rmax = (uint32_t)std::min<int64_t>(width, prefixes);
             const uint32_t level = step ? (uint32_t)rq.level : 0u;
             const uint32_t pre = open ? 1u : (b->prefilter_levels >> level) & 1u;
-            R.r[i].base = rq.base;
+            // gather only the logit sectors that hold a child where rows have few children
+            const bool by_level = b->read_mode == TCB_READ_GATHER || (b->read_mode == TCB_READ_AUTO &&
+                                                                      (b->gather_levels[dt_index] >> level & 1u));
+            const bool gather = !open && b->w.norm == TCB_NORM_CHILDREN && step && dt_index < 2 && by_level;
+            R.r[i].base_flags = rq.base | (gather ? 1 << 24 : 0);
             R.r[i].bits = width | rmax << 13 | level << 26 | pre << 29 | (step ? 1u : 0u) << 30 | (level & 1u) << 31;
         }
     }
 }
 
+// Which per-level gather mask applies to a step: 0 (fp32 rows) or 1 (bf16 rows) when the
+// tile kernel reads the rows with 16-byte vector loads, else 2 (never gather).
+static int gather_index(const void *logits, int64_t ld, int32_t dtype, int V) {
+    const bool vec = V == 256 && (ld % (dtype == TCB_F32 ? 4 : 8)) == 0 && ((uintptr_t)logits % 16) == 0;
+    return vec ? (dtype == TCB_F32 ? 0 : 1) : 2;
+}
+
 template <class HeadLaunch, class TileLaunch>
-static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLaunch tile, double temperature = 0.0,
-                           uint64_t seed = 0) {
+static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLaunch tile, int dt_index,
+                           double temperature = 0.0, uint64_t seed = 0) {
     static thread_local std::vector<tcb::StepReqs> args;
-    step_args(b, args);
+    step_args(b, args, dt_index);
     for (auto &R : args) {
         R.inv_temp_d = temperature > 0.0 ? 1.0 / temperature : 0.0;
         R.inv_temp = (float)R.inv_temp_d;
@@ -430,9 +450,10 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
     tcb_status st = step_common(b);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    return run_step(b, s, [](const tcb::StepReqs &) { return hipSuccess; }, [&](const tcb::StepReqs &R) {
-        return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, false, s);
-    });
+    return run_step(
+        b, s, [](const tcb::StepReqs &) { return hipSuccess; },
+        [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, false, s); },
+        gather_index(d_logits, ld, dtype, b->V));
 }
 
 tcb_status tcb_beam_step_sampled(tcb_beams *b, const void *d_logits, int64_t ld, int32_t dtype, float temperature,
@@ -448,7 +469,7 @@ tcb_status tcb_beam_step_sampled(tcb_beams *b, const void *d_logits, int64_t ld,
     return run_step(
         b, s, [](const tcb::StepReqs &) { return hipSuccess; },
         [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, true, s); },
-        (double)temperature, seed);
+        gather_index(d_logits, ld, dtype, b->V), (double)temperature, seed);
 }
 
 tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_hidden, int32_t H,
@@ -467,7 +488,8 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
         [&](const tcb::StepReqs &R) {
             return tcb::launch_lmhead(b->tdev, b->w, b->rp, R, d_hidden, ld_hidden, H, d_weight, b->w.lmx, s);
         },
-        [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, b->w.lmx, 256, TCB_F32, false, s); });
+        [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, b->w.lmx, 256, TCB_F32, false, s); },
+        2);
 }
 
 tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, float *d_phi, int32_t *d_parent_slot,
@@ -507,6 +529,12 @@ tcb_status tcb_request_level(const tcb_beams *b, int32_t req_id, int32_t *level)
     if (req_id < 0 || req_id >= (int)b->reqs.size() || !b->reqs[(size_t)req_id].used)
         return set_error(TCB_E_ARG, "request_level: unknown request id");
     *level = b->reqs[(size_t)req_id].level;
+    return TCB_OK;
+}
+
+tcb_status tcb_beams_set_read_mode(tcb_beams *b, int32_t mode) {
+    if (!b || mode < TCB_READ_AUTO || mode > TCB_READ_GATHER) return set_error(TCB_E_ARG, "set_read_mode: bad arguments");
+    b->read_mode = mode;
     return TCB_OK;
 }
 

@@ -30,6 +30,8 @@ struct tcb_beams {
     tcb::WaveDev w{};
     int32_t L = 0, V = 0;
     uint32_t prefilter_levels = 0;         // bit d: the tile kernel prefilters rows at depth d
+    uint32_t gather_levels[3] = {0, 0, 0}; // bit d: fp32 / bf16 rows at depth d read children's sectors only
+    int32_t read_mode = TCB_READ_AUTO;
     int64_t depth_nodes[TCB_MAX_L + 1] = {};   // trie nodes per depth: a bound on any request's rows
     int rp = 0;                            // which request-record buffer is current
     int64_t steps = 0;

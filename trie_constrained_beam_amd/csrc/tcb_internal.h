@@ -89,8 +89,10 @@ struct WaveDev {
 // What the host knows of every request it steps, passed by value so a kernel's first
 // loads need no device-side lookup. Only the live-row count stays on the device.
 struct ReqArg {
-    int32_t base;                  // first slot
+    int32_t base_flags;            // first slot (< 2^24) | gather << 24
     uint32_t bits;                 // width | rmax << 13 | level << 26 | pre << 29 | step << 30 | par << 31
+    __host__ __device__ int base() const { return base_flags & 0xFFFFFF; }
+    __host__ __device__ bool gather() const { return (base_flags >> 24) & 1; }        // children's sectors only
     __host__ __device__ int width() const { return (int)(bits & 0x1FFFu); }
     __host__ __device__ int rmax() const { return (int)((bits >> 13) & 0x1FFFu); }   // bound on live rows
     __host__ __device__ int level() const { return (int)((bits >> 26) & 0x7u); }
