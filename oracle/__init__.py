@@ -18,7 +18,10 @@ What it computes, and where the pages say so:
     (OneLA summary, section 2.1), and survivors keep only an index to their parent
     (OneLA summary, sections 2.4 and 3.3);
   * rows of different requests share a step but never compete (flashrec 0.1.0,
-    Features > Decoding, "Scheduling").
+    Features > Decoding, "Scheduling");
+  * single-pass scoring: every valid SID is scored from a per-user table of token
+    log-probabilities plus a SID-level similarity, then the top K are kept (SPRINT
+    summary, method and inference paragraphs; ``oracle.score``).
 
 Readings of points the pages leave open are listed in the module docstrings of
 ``oracle.beam``. Pins: ``tests/test_oracle_pins.py`` and ``tests/golden/``.
@@ -28,8 +31,11 @@ from .beam import (widen_logits, masked_log_softmax, expand_request, decode,
                    lmhead_logits, NORM_CHILDREN, NORM_LEVEL, NORM_OPEN)
 from .sample import (splitmix64, noise_uniform, gumbel, condition_on_max,
                      expand_request_sampled, decode_sampled)
+from .score import (leaf_codes, token_log_probs, sid_scores, score_catalog, TABLE_LOGPROB,
+                    TABLE_LOGITS)
 
 __all__ = ["OracleTrie", "widen_logits", "masked_log_softmax", "expand_request",
            "decode", "lmhead_logits", "NORM_CHILDREN", "NORM_LEVEL", "NORM_OPEN", "splitmix64",
            "noise_uniform", "gumbel", "condition_on_max", "expand_request_sampled",
-           "decode_sampled"]
+           "decode_sampled", "leaf_codes", "token_log_probs", "sid_scores", "score_catalog",
+           "TABLE_LOGPROB", "TABLE_LOGITS"]

@@ -97,3 +97,41 @@ def pl_inclusion(probs, k):
                 rec(chosen + [s], p_seq * probs[s] / rest_mass, rest_mass - probs[s])
     rec([], 1.0, math.fsum(probs.values()))
     return incl
+
+
+def sprint_scores(catalog, V, table, table_logits, user_vec=None, emb=None, weight=1.0):
+    """{sid: score} for every valid SID of a tiny catalog, found by walking all V^L
+    tuples and keeping those in the catalog (math module only).
+
+    Score = sum over positions of the token log-probability (``table[j]`` itself, or
+    its log-softmax over the V codes when ``table_logits``) plus ``weight`` times the
+    dot product of ``user_vec`` with ``emb[sid]`` (a dict keyed by SID tuple)."""
+    import itertools
+    valid = set(tuple(int(c) for c in s) for s in catalog)
+    L = len(next(iter(valid)))
+    logp = []
+    for j in range(L):
+        row = [float(v) for v in table[j]]
+        if table_logits:
+            lse = _logp(row, range(V), 0) - row[0]          # -(log-sum-exp of the row)
+            row = [v + lse for v in row]
+        logp.append(row)
+    out = {}
+    for t in itertools.product(range(V), repeat=L):
+        if t not in valid:
+            continue
+        s = math.fsum(logp[j][t[j]] for j in range(L))
+        if user_vec is not None:
+            s += weight * math.fsum(float(a) * float(b) for a, b in zip(user_vec, emb[t]))
+        out[t] = s
+    return out
+
+
+def ranked(scores):
+    """[(sid, score)] best first; the smaller SID wins a tie."""
+    return sorted(scores.items(), key=lambda kv: (-kv[1], kv[0]))
+
+
+def log_sum_exp(values):
+    m = max(values)
+    return m + math.log(math.fsum(math.exp(v - m) for v in values))

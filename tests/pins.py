@@ -486,9 +486,126 @@ def pin_sampled_noise_moments(orc):
     assert abs(g.var() - math.pi ** 2 / 6) < 0.05
 
 
+# --------------------------------------------------------------------------- single-pass scoring
+def _random_sids(rng, V, L, n):
+    return [tuple(int(c) for c in rng.integers(0, V, L)) for _ in range(n)]
+
+
+def pin_score_bruteforce(orc, seed=11):
+    """Tiny catalogs (duplicates included), both table kinds, with and without the
+    SID-level term, any k: equal to the pure-Python walk over all V^L tuples
+    (tests/bruteforce.py), scores, ranking, log-normaliser and catalog items."""
+    rng = np.random.default_rng(seed)
+    for case in range(40):
+        V, L = int(rng.integers(2, 6)), int(rng.integers(1, 4))
+        cat = _random_sids(rng, V, L, int(rng.integers(1, V ** L + 3)))
+        trie = orc.OracleTrie(np.asarray(cat), V=V)
+        sids = sorted(set(cat))
+        table = rng.normal(0.0, 2.0, (L, V))
+        logits = bool(case % 2)
+        use = case % 3 != 0
+        D = int(rng.integers(1, 6))
+        emb = {t: rng.normal(0.0, 1.0, D) for t in sids}
+        u, w = rng.normal(0.0, 1.0, D), float(rng.normal())
+        ref = bf.sprint_scores(cat, V, table, logits, u if use else None, emb, w)
+        rk = bf.ranked(ref)
+        k = int(rng.integers(1, len(sids) + 3))
+        out = orc.score_catalog(trie, table, k, 1 if logits else 0, u if use else None,
+                                np.stack([emb[t] for t in sids]) if use else None, w)
+        kk = min(k, len(sids))
+        assert [sids[int(l)] for l in out["leaf"]] == [t for t, _ in rk[:kk]], case
+        assert np.max(np.abs(out["score"] - np.asarray([v for _, v in rk[:kk]]))) < 1e-12
+        assert abs(out["lse"] - bf.log_sum_exp(list(ref.values()))) < 1e-12
+        for l, it in zip(out["leaf"], out["item"]):
+            assert int(it) == cat.index(sids[int(l)])
+
+
+def pin_score_equals_wide_beam(orc, seed=12):
+    """With position-independent logits, the level-normalised beam search at a width
+    that prunes nothing ranks every valid SID by the same sum of per-position
+    log-softmax terms: single-pass scoring of raw logits must give that ranking."""
+    rng = np.random.default_rng(seed)
+    for V, L, n in [(256, 3, 300), (6, 3, 80), (256, 2, 500)]:
+        cat = _random_sids(rng, V, L, n)
+        trie = orc.OracleTrie(np.asarray(cat), V=V)
+        table = rng.normal(0.0, 2.0, (L, V))
+        width = max(trie.nodes_per_depth)
+        beams, scores, _ = run_decode(orc, trie, width, lambda d, p: table[d], norm=1)
+        out = orc.score_catalog(trie, table, trie.n_distinct, 1)
+        sids = sorted(set(cat))
+        assert [sids[int(l)] for l in out["leaf"]] == beams
+        assert np.max(np.abs(out["score"] - np.asarray(scores))) < 1e-12
+
+
+def pin_score_full_catalog(orc, seed=13):
+    """Every V^L tuple valid: the token distributions multiply to a distribution over
+    the product space, so the log-normaliser is 0; the best k equal a stable
+    descending torch.sort of the outer sum of torch.log_softmax rows."""
+    rng = np.random.default_rng(seed)
+    V, L, k = 16, 3, 50
+    cat = list(itertools.product(range(V), repeat=L))
+    perm = rng.permutation(len(cat))
+    cat = [cat[i] for i in perm]                       # catalog rows != leaf order
+    trie = orc.OracleTrie(np.asarray(cat), V=V)
+    table = rng.normal(0.0, 3.0, (L, V))
+    lp = torch.log_softmax(torch.tensor(table, dtype=torch.float64), dim=1)
+    total = (lp[0][:, None, None] + lp[1][None, :, None] + lp[2][None, None, :]).reshape(-1)
+    s_sorted, idx = torch.sort(total, descending=True, stable=True)
+    for kind, tab in ((1, table), (0, lp.numpy())):
+        out = orc.score_catalog(trie, tab, k, kind)
+        assert abs(out["lse"]) < 1e-12
+        assert out["leaf"].tolist() == idx[:k].tolist()
+        assert np.max(np.abs(out["score"] - s_sorted[:k].numpy())) < 1e-12
+        inv = np.argsort(perm)
+        assert out["item"].tolist() == [int(inv[l]) for l in out["leaf"]]
+
+
+def pin_score_sid_term_closed_form(orc, seed=14):
+    """Zero token table and one-hot SID embeddings (leaf l -> 2 e_(l mod 8)): the
+    matrix product reduces to a lookup, score(l) = 2 w u[l mod 8], and the
+    log-normaliser is log sum over residues r of count_r exp(2 w u[r])."""
+    rng = np.random.default_rng(seed)
+    V, L, D, w = 256, 2, 8, 0.75
+    trie = orc.OracleTrie(np.asarray(_random_sids(rng, V, L, 400)), V=V)
+    n = trie.n_distinct
+    emb = np.zeros((n, D))
+    emb[np.arange(n), np.arange(n) % D] = 2.0
+    u = rng.permutation(D).astype(np.float64) - 3.5
+    out = orc.score_catalog(trie, np.zeros((L, V)), 37, 0, u, emb, w)
+    expect = sorted(range(n), key=lambda l: (-2 * w * u[l % D], l))[:37]
+    assert out["leaf"].tolist() == expect
+    assert np.max(np.abs(out["score"] - 2 * w * u[np.asarray(expect) % D])) < 1e-12
+    cnt = np.bincount(np.arange(n) % D, minlength=D)
+    lse = math.log(math.fsum(float(cnt[r]) * math.exp(2 * w * u[r]) for r in range(D)))
+    assert abs(out["lse"] - lse) < 1e-12
+
+
+def pin_score_invariances(orc, seed=15):
+    """A per-position constant added to raw logits changes nothing; added to
+    log-probabilities it shifts every score and the log-normaliser by the constants'
+    sum. A constant table ties every SID: the k smallest SIDs win, and the
+    log-normaliser is log n + L c."""
+    rng = np.random.default_rng(seed)
+    V, L = 256, 3
+    trie = orc.OracleTrie(np.asarray(_random_sids(rng, V, L, 2000)), V=V)
+    table = rng.normal(0.0, 2.0, (L, V))
+    c = rng.normal(0.0, 5.0, L)
+    a, b = orc.score_catalog(trie, table, 100, 1), orc.score_catalog(trie, table + c[:, None], 100, 1)
+    assert a["leaf"].tolist() == b["leaf"].tolist()
+    assert np.max(np.abs(a["score"] - b["score"])) < 1e-11 and abs(a["lse"] - b["lse"]) < 1e-11
+    a, b = orc.score_catalog(trie, table, 100, 0), orc.score_catalog(trie, table + c[:, None], 100, 0)
+    assert a["leaf"].tolist() == b["leaf"].tolist()
+    assert np.max(np.abs(b["score"] - a["score"] - c.sum())) < 1e-11
+    assert abs(b["lse"] - a["lse"] - c.sum()) < 1e-11
+    out = orc.score_catalog(trie, np.full((L, V), -1.25), 64, 0)
+    assert out["leaf"].tolist() == list(range(64))
+    assert abs(out["lse"] - (math.log(trie.n_distinct) - 1.25 * L)) < 1e-11
+
+
 ALL_PINS = [pin_handworked, pin_trie_numbering, pin_dedupe_lowest_row,
             pin_masked_log_softmax_vs_torch, pin_single_child_and_constant, pin_ties_lower_flat,
             pin_full_catalog_unconstrained, pin_width_one_greedy, pin_wide_equals_bruteforce,
             pin_tiny_vs_replay, pin_legality, pin_lmhead_exact, pin_bf16_widening,
             pin_decode_api, pin_open_vocabulary, pin_sampled_plackett_luce, pin_sampled_key_invariants,
-            pin_sampled_noise_moments]
+            pin_sampled_noise_moments, pin_score_bruteforce, pin_score_equals_wide_beam,
+            pin_score_full_catalog, pin_score_sid_term_closed_form, pin_score_invariances]

@@ -177,12 +177,41 @@ def _exp_open_constrained(trie, depth, prefixes, scores, logits64, beam_width, n
     return ob.expand_request(trie, depth, prefixes, scores, logits64, beam_width, 1 if norm == 2 else norm)
 
 
+def _score_mut(*, drop_level=False, reverse_levels=False, normalise=True, sid_sign=1.0,
+               emb_by_item=False, tie_sign=1, lse_topk=False, extra=0, ignore_weight=False):
+    """A copy of the single-pass scoring with one planted mistake."""
+    from oracle import score as osc
+
+    def score_catalog(trie, table64, k, table_kind=0, user_vec=None, sid_emb=None, sid_weight=1.0):
+        codes = osc.leaf_codes(trie)
+        t = np.asarray(table64, dtype=np.float64)
+        logp = osc.token_log_probs(t, table_kind) if normalise else t
+        L = trie.L
+        score = np.zeros(trie.n_distinct)
+        for j in range(L - 1 if drop_level else L):
+            score += logp[j, codes[:, L - 1 - j] if reverse_levels else codes[:, j]]
+        if user_vec is not None:
+            emb = np.asarray(sid_emb, dtype=np.float64)
+            if emb_by_item:
+                emb = emb[trie.leaf_item]
+            w = 1.0 if ignore_weight else float(sid_weight)
+            score += sid_sign * w * (emb @ np.asarray(user_vec, dtype=np.float64))
+        leaf = np.arange(score.size)
+        order = np.lexsort((tie_sign * leaf, -score))
+        top = order[:min(int(k) + extra, score.size)]
+        pool = score[top] if lse_topk else score
+        m = pool.max()
+        lse = m + np.log(np.sum(np.exp(pool - m)))
+        return {"leaf": top, "item": trie.leaf_item[top], "score": score[top], "lse": float(lse)}
+    return score_catalog
+
+
 def _ns(**over):
     ns = dict(OracleTrie=oracle.OracleTrie, expand_request=oracle.expand_request,
               masked_log_softmax=oracle.masked_log_softmax, decode=oracle.decode,
               lmhead_logits=oracle.lmhead_logits, widen_logits=oracle.widen_logits,
               decode_sampled=oracle.decode_sampled, noise_uniform=oracle.noise_uniform,
-              gumbel=oracle.gumbel)
+              gumbel=oracle.gumbel, score_catalog=oracle.score_catalog)
     ns.update(over)
     return types.SimpleNamespace(**ns)
 
@@ -219,6 +248,15 @@ MUTANTS = {
     "sampled_noise_shared_by_siblings": dict(decode_sampled=_decode_sampled_mut(shared_noise=True)),
     "sampled_parent_key_dropped": dict(decode_sampled=_decode_sampled_mut(parent_key=False)),
     "sampled_phi_not_accumulated": dict(decode_sampled=_decode_sampled_mut(accumulate=False)),
+    "score_last_level_dropped": dict(score_catalog=_score_mut(drop_level=True)),
+    "score_levels_reversed": dict(score_catalog=_score_mut(reverse_levels=True)),
+    "score_logits_not_normalised": dict(score_catalog=_score_mut(normalise=False)),
+    "score_sid_term_sign_flipped": dict(score_catalog=_score_mut(sid_sign=-1.0)),
+    "score_embedding_by_catalog_row": dict(score_catalog=_score_mut(emb_by_item=True)),
+    "score_tie_larger_sid_first": dict(score_catalog=_score_mut(tie_sign=-1)),
+    "score_lse_over_top_k_only": dict(score_catalog=_score_mut(lse_topk=True)),
+    "score_keeps_one_extra": dict(score_catalog=_score_mut(extra=1)),
+    "score_sid_weight_ignored": dict(score_catalog=_score_mut(ignore_weight=True)),
 }
 
 

@@ -14,7 +14,7 @@ def oracle_ns():
         masked_log_softmax=oracle.masked_log_softmax, decode=oracle.decode,
         lmhead_logits=oracle.lmhead_logits, widen_logits=oracle.widen_logits,
         decode_sampled=oracle.decode_sampled, noise_uniform=oracle.noise_uniform,
-        gumbel=oracle.gumbel)
+        gumbel=oracle.gumbel, score_catalog=oracle.score_catalog)
 
 
 @pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
