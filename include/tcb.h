@@ -19,8 +19,11 @@
  *   [OLA] OneLA summary: section 2.1 (candidates globally selected across the
  *         beam), sections 2.4 / 3.3 (children keep an index to their parent;
  *         records are append-only and never moved).
- *   [SP]  SPRINT summary, inference paragraph (valid SIDs of a prefix trie scored
- *         by their token log-probability sum).
+ *   [SP]  SPRINT summary, method paragraph (one pass gives an L x M table of
+ *         per-position token distributions and a user vector; scoring a valid SID
+ *         is a table lookup plus one matrix product) and inference paragraph (valid
+ *         SIDs of a prefix trie scored by their token log-probability sum plus a
+ *         SID-level similarity, then top-K; the softmax runs over the valid SIDs).
  *
  * Conventions
  *   - Every call returns tcb_status: TCB_OK (0) or a negative error code. On error
@@ -287,6 +290,58 @@ tcb_status tcb_beams_timing(tcb_beams *b, double *head_ms, double *tile_ms, doub
                             int32_t *steps);
 
 void tcb_beams_destroy(tcb_beams *b);
+
+/* ------------------------------------------------------------------------------
+ * Single-pass scoring of every valid SID ([SP] method and inference paragraphs)
+ *
+ *   score(u, s) = sum_d T_u[d][c_d(s)] + w * <v_u, e_s>
+ *   lse(u)      = log sum over valid s of exp(score(u, s))      (P(s|u) = exp(score - lse))
+ *
+ * over the trie's leaves s (distinct SIDs, leaf j = the j-th smallest SID). T_u is user
+ * u's L x V table of per-position token log-probabilities (or raw per-position logits,
+ * normalised here by a log-softmax over the V codes of each position); v_u (the user
+ * vector) and e_s (one SID-level embedding row per leaf) are bf16, accumulated in
+ * fp32. Users never interact. The K best SIDs per user are returned ranked by
+ * (score desc, leaf asc).
+ * ------------------------------------------------------------------------------ */
+#define TCB_SCORE_MAX_K 512
+enum { TCB_TABLE_LOGPROB = 0, TCB_TABLE_LOGITS = 1 };
+
+/* Device copy of every leaf's codes, needed by tcb_score_catalog: 4 bytes per leaf for
+ * L <= 4, 8 bytes otherwise (byte d = the code at depth d). tcb_trie_upload_codes
+ * copies it asynchronously into caller memory (256-byte aligned) of at least
+ * *bytes; the host copy stays owned by the trie. Errors: TCB_E_ARG, TCB_E_WORKSPACE,
+ * TCB_E_HIP. */
+tcb_status tcb_trie_codes_bytes(const tcb_trie *t, size_t *bytes);
+tcb_status tcb_trie_upload_codes(tcb_trie *t, void *d_buf, size_t bytes, void *stream);
+
+/* Workspace for tcb_score_catalog calls of up to max_users users on this trie: the
+ * normalised tables, the best score of every 16-SID group and 256-SID block per user,
+ * and log-normaliser partials (about 4.3 bytes per user and leaf). */
+tcb_status tcb_score_workspace_bytes(const tcb_trie *t, int32_t max_users, size_t *bytes);
+
+/* Score every valid SID for n_users users and keep each user's best k.
+ *   d_table     float [n_users][L][V]: per-position log-probabilities
+ *               (TCB_TABLE_LOGPROB) or raw logits (TCB_TABLE_LOGITS)
+ *   d_user_vec  bf16 bits [n_users][dim] and d_sid_emb bf16 bits [n_distinct][dim] in
+ *               leaf order, both 16-byte aligned, or both NULL (no SID-level term);
+ *               dim in {32, 64, 128, 256}
+ *   sid_weight  w, a finite scalar
+ *   k           1..TCB_SCORE_MAX_K
+ *   outputs     d_leaf int32 [n_users][k] leaf ids (node id - node_offset[L]),
+ *               d_score float [n_users][k], d_item int32 [n_users][k] (catalog row,
+ *               may be NULL), d_lse float [n_users] (may be NULL: the log-normaliser
+ *               is then not computed); rows past n_distinct get leaf -1, item -1 and
+ *               score -inf
+ * Inputs must be finite. Needs tcb_trie_upload and tcb_trie_upload_codes first and a
+ * workspace of tcb_score_workspace_bytes(t, n_users) (256-byte aligned). Asynchronous
+ * on stream; no device memory is allocated. Errors: TCB_E_ARG, TCB_E_STATE (trie or
+ * codes not uploaded), TCB_E_WORKSPACE, TCB_E_HIP. */
+tcb_status tcb_score_catalog(const tcb_trie *t, int32_t n_users, const float *d_table,
+                             int32_t table_kind, const void *d_user_vec, const void *d_sid_emb,
+                             int32_t dim, float sid_weight, int32_t k, int32_t *d_leaf,
+                             int32_t *d_item, float *d_score, float *d_lse, void *d_ws,
+                             size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -1,6 +1,6 @@
 """Python face of libtcb: the same calls as include/tcb.h, with torch for device memory
-and streams. Every step of the beam path runs in the HIP library; this module only
-marshals arguments.
+and streams. Every step of the beam path and of single-pass scoring runs in the HIP
+library; this module only marshals arguments.
 """
 from __future__ import annotations
 
@@ -39,6 +39,7 @@ class Trie:
         self.L, self.V = int(self.info.L), int(self.info.V)
         self.mask_depths = int(self.info.mask_depths)
         self.d_image = None
+        self.d_codes = None
         if device is not None:
             self.upload(device)
 
@@ -78,6 +79,16 @@ class Trie:
         nbytes = int(self.info.device_bytes)
         self.d_image = torch.empty(nbytes, dtype=torch.uint8, device=device)
         check(lib().tcb_trie_upload(self._h, _ptr(self.d_image), nbytes, _stream()))
+        return self
+
+    def upload_codes(self, device="cuda"):
+        """Copy every leaf's codes to the device (needed by ``score_catalog``)."""
+        if self.d_image is None:
+            self.upload(device)
+        nb = C.c_size_t()
+        check(lib().tcb_trie_codes_bytes(self._h, C.byref(nb)))
+        self.d_codes = torch.empty(max(int(nb.value), 1), dtype=torch.uint8, device=device)
+        check(lib().tcb_trie_upload_codes(self._h, _ptr(self.d_codes), self.d_codes.numel(), _stream()))
         return self
 
 
@@ -237,3 +248,48 @@ def invalid_rate(out) -> float:
         return 0.0
     bad = sum(int(np.sum(items[i, :int(c)] < 0)) for i, c in enumerate(counts))
     return bad / total
+
+
+def score_workspace_bytes(trie: Trie, max_users: int) -> int:
+    nb = C.c_size_t()
+    check(lib().tcb_score_workspace_bytes(trie.handle, int(max_users), C.byref(nb)))
+    return int(nb.value)
+
+
+def score_catalog(trie: Trie, table, k: int, table_kind: str = "logprob", user_vec=None,
+                  sid_emb=None, sid_weight: float = 1.0, want_lse: bool = True, workspace=None):
+    """Single-pass scoring of every valid SID for a batch of users (tcb_score_catalog).
+
+    ``table``: float32 [U, L, V] on the device, per-position log-probabilities
+    ("logprob") or raw logits ("logits"); ``user_vec`` bfloat16 [U, D] and ``sid_emb``
+    bfloat16 [n_distinct, D] (leaf order) for the SID-level term, or both None.
+    Returns device tensors: leaf, item (int32 [U, k]), score (float32 [U, k]) and lse
+    (float32 [U], or None)."""
+    if trie.d_codes is None:
+        trie.upload_codes(table.device)
+    U = int(table.shape[0])
+    if table.dtype != torch.float32 or not table.is_contiguous() or tuple(table.shape[1:]) != (trie.L, trie.V):
+        raise ValueError("table must be a contiguous float32 [U, L, V] tensor")
+    D = 0
+    if user_vec is not None or sid_emb is not None:
+        if user_vec is None or sid_emb is None:
+            raise ValueError("user_vec and sid_emb go together")
+        for t in (user_vec, sid_emb):
+            if t.dtype != torch.bfloat16 or not t.is_contiguous():
+                raise ValueError("user_vec and sid_emb must be contiguous bfloat16")
+        D = int(user_vec.shape[1])
+        if tuple(user_vec.shape) != (U, D) or tuple(sid_emb.shape) != (trie.n_distinct, D):
+            raise ValueError("user_vec must be [U, D] and sid_emb [n_distinct, D]")
+    kind = {"logprob": L.TCB_TABLE_LOGPROB, "logits": L.TCB_TABLE_LOGITS}[table_kind]
+    dev = table.device
+    nb = score_workspace_bytes(trie, U)
+    if workspace is None or workspace.numel() < nb:
+        workspace = torch.empty(nb, dtype=torch.uint8, device=dev)
+    leaf = torch.empty((U, k), dtype=torch.int32, device=dev)
+    item = torch.empty((U, k), dtype=torch.int32, device=dev)
+    score = torch.empty((U, k), dtype=torch.float32, device=dev)
+    lse = torch.empty(U, dtype=torch.float32, device=dev) if want_lse else None
+    check(lib().tcb_score_catalog(trie.handle, U, _ptr(table), kind, _ptr(user_vec), _ptr(sid_emb), D,
+                                  float(sid_weight), int(k), _ptr(leaf), _ptr(item), _ptr(score), _ptr(lse),
+                                  _ptr(workspace), workspace.numel(), _stream()))
+    return {"leaf": leaf, "item": item, "score": score, "lse": lse}

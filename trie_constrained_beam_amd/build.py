@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtcb.so")
-SOURCES = ["kernels.hip", "lmhead.hip", "tcb_api.cpp", "trie_builder.cpp"]
+SOURCES = ["kernels.hip", "lmhead.hip", "score.hip", "tcb_api.cpp", "score_api.cpp", "trie_builder.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -19,6 +19,8 @@ struct tcb_trie {
     std::vector<uint8_t> image;            // device image, uploaded as one copy
     size_t o_child_begin = 0, o_child_code = 0, o_leaf = 0, o_mask = 0, image_bytes = 0;
     void *d_image = nullptr;               // caller-owned, set by tcb_trie_upload
+    std::vector<uint8_t> codes;            // leaf codes for single-pass scoring (built on demand)
+    void *d_codes = nullptr;               // caller-owned, set by tcb_trie_upload_codes
 };
 
 struct tcb_beams {

@@ -160,6 +160,41 @@ def lmhead_weight(workload_seed: int, level: int, V: int, H: int, std: float = 0
     return f32_to_bf16_bits((rng.standard_normal((V, H), dtype=np.float32) * np.float32(std)))
 
 
+# --------------------------------------------------------------------------- scoring inputs
+# Single-pass scoring (SPRINT summary, method paragraph): per user an L x V table of
+# per-position token distributions and a user vector; per valid SID an embedding row.
+def score_logits(seed, users: int, L: int, sigma: float = 2.0, V: int = V_DEFAULT) -> np.ndarray:
+    """float32 [users, L, V] raw per-position logits N(0, sigma^2), ``default_rng([seed, 6])``."""
+    rng = np.random.default_rng([seed, 6])
+    return (rng.standard_normal((users, L, V), dtype=np.float32) * np.float32(sigma))
+
+
+def score_logprobs(seed, users: int, L: int, alpha: float = 0.3, V: int = V_DEFAULT) -> np.ndarray:
+    """float32 [users, L, V] log-probabilities of random per-position distributions:
+    Dirichlet(alpha) draws (peaked for alpha < 1), floored at 1e-30 before the log."""
+    rng = np.random.default_rng([seed, 7])
+    p = rng.dirichlet(np.full(V, alpha), size=(users, L))
+    return np.log(np.maximum(p, 1e-30)).astype(np.float32)
+
+
+def user_vectors(seed, users: int, D: int) -> np.ndarray:
+    """bf16 bits [users, D] of user vectors N(0, 1), ``default_rng([seed, 8])``."""
+    rng = np.random.default_rng([seed, 8])
+    return f32_to_bf16_bits(rng.standard_normal((users, D), dtype=np.float32))
+
+
+def sid_embeddings(seed, n: int, D: int) -> np.ndarray:
+    """bf16 bits [n, D] of SID-level embeddings N(0, 1/D) in leaf order, drawn in chunks
+    of 2^20 rows from ``default_rng([seed, 9, chunk])``."""
+    out = np.empty((n, D), dtype=np.uint16)
+    scale = np.float32(1.0 / math.sqrt(D))
+    for c0 in range(0, n, CHUNK):
+        rows = min(CHUNK, n - c0)
+        rng = np.random.default_rng([seed, 9, c0 // CHUNK])
+        out[c0:c0 + rows] = f32_to_bf16_bits(rng.standard_normal((rows, D), dtype=np.float32) * scale)
+    return out
+
+
 # --------------------------------------------------------------------------- workloads
 @dataclasses.dataclass(frozen=True)
 class Workload:
@@ -204,4 +239,27 @@ WORKLOADS = {
     # fused SID-range lm_head: 8 requests x beam 512, hidden 2048, L=4, 1M uniform SIDs
     "lmhead_b512x8_l4_1m_h2048": Workload("lmhead_b512x8_l4_1m_h2048", 5, 4, 1_000_000,
                                           ("uniform",) * 4, (512,) * 8, hidden=2048),
+}
+
+
+@dataclasses.dataclass(frozen=True)
+class ScoreWorkload:
+    """A single-pass scoring workload: every valid SID of a catalog scored for a batch of
+    users from raw per-position logits plus a SID-level term, best k kept."""
+    name: str
+    seed: int
+    catalog_of: str            # the beam workload whose catalog is scored
+    users: int
+    dim: int
+    k: int
+    sigma: float = 2.0
+
+    def catalog(self) -> np.ndarray:
+        return WORKLOADS[self.catalog_of].catalog()
+
+
+SCORE_WORKLOADS = {
+    # the 4M-SID Zipf catalog of the beam line, 32 users, 64-dim SID embeddings, top 512
+    "score_u32_k512_l4_4m_zipf_d64": ScoreWorkload("score_u32_k512_l4_4m_zipf_d64", 6,
+                                                   "b512x32_l4_4m_zipf_bf16", 32, 64, 512),
 }
