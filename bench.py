@@ -14,6 +14,9 @@ Also measured in the same run:
   * per-kernel durations with HIP events on the launch stream (an eager pass);
   * the SID-range lm_head leg: 8 requests x beam 512, hidden 2048, its MFMA kernel
     against the bf16 dense peak;
+  * the single-pass scoring leg: every SID of the same 4M catalog scored for 32 users
+    (per-position logits plus a 64-dim SID-level term), top 512 kept per user; its scan
+    kernel against the HBM peak;
   * the CPU oracle on a bounded sample of the same workload (a baseline, not a target).
 
 Prints one JSON line on stdout. Progress goes to stderr.
@@ -41,28 +44,30 @@ TRIE_BYTES = 8                  # child range (or first child + mask word) per l
 MERGE_WRITE_BYTES = 18          # node, score, parent slot, back-pointer (+ code) per survivor
 KERNEL_SOURCES = ["trie_constrained_beam_amd/csrc/kernels.hip", "trie_constrained_beam_amd/csrc/tcb_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_tile_b512x32_l4_4m_zipf_bf16_traffic.txt")
+SCORE_SOURCES = ["trie_constrained_beam_amd/csrc/score.hip", "trie_constrained_beam_amd/csrc/score_internal.h"]
+SCORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_score_scan_score_u32_k512_l4_4m_zipf_d64_traffic.txt")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha():
+def kernel_source_sha(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per tile-kernel launch from the committed counter profile, if it was
+def recorded_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
+    """HBM bytes per launch of a kernel from its committed counter profile, if that was
     taken on the current kernel source (else None)."""
     try:
-        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+        fields = dict(line.split(":", 1) for line in open(path) if ":" in line)
     except OSError:
         return None
-    if fields.get("kernel_source_sha", "").strip() != kernel_source_sha():
+    if fields.get("kernel_source_sha", "").strip() != kernel_source_sha(sources):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -273,6 +278,87 @@ def lmhead_leg(args, dev):
             "tile_avg_us": tile_ms * 1e3 / n_timed, "merge_avg_us": merge_ms * 1e3 / n_timed}
 
 
+def _score_inputs(wl, trie, dev):
+    import numpy as np
+    import torch
+    from trie_constrained_beam_amd import synth
+    table = torch.from_numpy(synth.score_logits(wl.seed, wl.users, trie.L, wl.sigma)).to(dev)
+    uvec_h = synth.user_vectors(wl.seed, wl.users, wl.dim)
+    emb_h = synth.sid_embeddings(wl.seed, trie.n_distinct, wl.dim)
+    uvec = torch.from_numpy(uvec_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    emb = torch.from_numpy(emb_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    return table, uvec, emb, uvec_h, emb_h
+
+
+def score_cpu_baseline(wl, cat, seconds):
+    """The oracle scoring every SID for users of this workload, one after another, until
+    ``seconds`` have passed; user-SID scores per second."""
+    import numpy as np
+    import oracle
+    from trie_constrained_beam_amd import synth
+    otrie = oracle.OracleTrie(cat)
+    tab = synth.score_logits(wl.seed, wl.users, otrie.L, wl.sigma)
+    u64 = oracle.widen_logits(synth.user_vectors(wl.seed, wl.users, wl.dim), "bf16")
+    e64 = oracle.widen_logits(synth.sid_embeddings(wl.seed, otrie.n_distinct, wl.dim), "bf16")
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        u = done % wl.users
+        oracle.score_catalog(otrie, tab[u].astype(np.float64), wl.k, oracle.TABLE_LOGITS, u64[u], e64, 1.0)
+        done += 1
+    el = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    return {"value": done * otrie.n_distinct / el, "unit": "user-SID scores/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} users x {otrie.n_distinct} SIDs scored and ranked in {el:.1f} s (numpy float64, "
+                      f"one process; its BLAS product may use up to {threads} threads)"}
+
+
+def score_leg(args, cat, dev):
+    import ctypes as C
+    import torch
+    from trie_constrained_beam_amd import Trie, score_catalog, score_workspace_bytes, synth
+    from trie_constrained_beam_amd import _lib
+    wl = synth.SCORE_WORKLOADS["score_u32_k512_l4_4m_zipf_d64"]
+    trie = Trie(cat, device=dev).upload_codes(dev)
+    n = trie.n_distinct
+    table, uvec, emb, _, _ = _score_inputs(wl, trie, dev)
+    ws = torch.empty(score_workspace_bytes(trie, wl.users), dtype=torch.uint8, device=dev)
+
+    def run(_):
+        score_catalog(trie, table, wl.k, "logits", uvec, emb, 1.0, want_lse=True, workspace=ws)
+    steps = max(10, args.steps // 20)
+    elapsed = timed(run, steps, max(2, args.warmup // 5))
+    n_ev = min(steps, 50)
+    lib = _lib.lib()
+    _lib.check(lib.tcb_score_enable_timing(n_ev))
+    for d in range(n_ev):
+        run(d)
+    t_ms, s_ms, x_ms, calls = C.c_double(), C.c_double(), C.c_double(), C.c_int32()
+    _lib.check(lib.tcb_score_timing(C.byref(t_ms), C.byref(s_ms), C.byref(x_ms), C.byref(calls)))
+    _lib.check(lib.tcb_score_enable_timing(0))
+    k = max(1, calls.value)
+    scan_us, table_us, sel_us = s_ms.value * 1e3 / k, t_ms.value * 1e3 / k, x_ms.value * 1e3 / k
+    code_bytes = 4 if trie.L <= 4 else 8
+    unit_bytes = code_bytes + 2 * wl.dim                     # per SID and group of 32 users
+    groups = -(-wl.users // 32)
+    bytes_per_launch = float(n) * unit_bytes * groups
+    achieved = bytes_per_launch / (scan_us * 1e-6) / 1e9
+    traffic = recorded_traffic(SCORE_TRAFFIC_FILE, SCORE_SOURCES)
+    value = wl.users * n * steps / elapsed
+    log(f"[bench] scoring leg: {wl.users} users x {n} SIDs, top {wl.k}: {elapsed * 1e3 / steps:.3f} ms per call; "
+        f"scan {scan_us:.1f} us ({achieved:.0f} GB/s), table {table_us:.1f} us, select {sel_us:.1f} us")
+    return {"workload": wl.name, "value": value, "unit": "user-SID scores/s", "steps": steps,
+            "ms_per_step": elapsed * 1e3 / steps, "users": wl.users, "sids": n, "dim": wl.dim, "k": wl.k,
+            "roofline": {"bound": "hbm", "kernel": "k_score_scan", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                         "traffic": None if traffic is None else traffic / (scan_us * 1e-6) / 1e9,
+                         "traffic_bytes_per_launch": traffic,
+                         "bytes_per_sid": unit_bytes, "bytes_per_launch": bytes_per_launch,
+                         "avg_launch_us": scan_us},
+            "table_avg_us": table_us, "select_avg_us": sel_us,
+            "kernel_source_sha": kernel_source_sha(SCORE_SOURCES)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +369,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle baseline budget (0: skip)")
     ap.add_argument("--graph", type=int, default=1, help="replay each decode as a captured HIP graph")
     ap.add_argument("--lmhead", type=int, default=1, help="also run the SID-range lm_head leg")
+    ap.add_argument("--score", type=int, default=1, help="also run the single-pass scoring leg")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -299,10 +386,15 @@ def main():
     t0 = time.perf_counter()
     cat = wl.catalog()
     log(f"[bench] catalog {cat.shape} in {time.perf_counter() - t0:.1f}s")
-    cpu = None
+    cpu = score_cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(wl, cat, args.cpu_seconds)
         log(f"[bench] oracle {cpu['value']:.0f} rows x steps/s ({cpu['cores']} processes)")
+        if args.score:
+            swl = synth.SCORE_WORKLOADS["score_u32_k512_l4_4m_zipf_d64"]
+            score_cpu = score_cpu_baseline(swl, cat if swl.catalog_of == wl.name else swl.catalog(),
+                                           max(3.0, args.cpu_seconds / 3))
+            log(f"[bench] oracle scoring {score_cpu['value']:.3g} user-SID scores/s")
 
     import torch
     dev = torch.device("cuda:0")
@@ -316,6 +408,11 @@ def main():
     log(f"[bench] {args.steps} decodes in {m['elapsed'] * 1e3:.1f} ms; tile kernel avg {m['tile_us']:.2f} us "
         f"({achieved:.0f} GB/s), merge kernel avg {m['merge_us']:.2f} us")
     lm = lmhead_leg(args, dev) if args.lmhead else None
+    sc = None
+    if args.score:
+        swl = synth.SCORE_WORKLOADS["score_u32_k512_l4_4m_zipf_d64"]
+        sc = score_leg(args, cat if swl.catalog_of == wl.name else swl.catalog(), dev)
+        sc["cpu_baseline"] = score_cpu
 
     line = {
         "metric": METRIC,
@@ -338,11 +435,12 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "k_tile", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": None if traffic is None else traffic / (m["tile_us"] * 1e-6) / 1e9,
-                     "bytes_per_row_step": unit_bytes, "bytes_per_launch": bytes_per_launch,
+                     "traffic_bytes_per_launch": traffic, "bytes_per_row_step": unit_bytes, "bytes_per_launch": bytes_per_launch,
                      "avg_launch_us": m["tile_us"]},
         "hbm_GBps_wall": m["rows_x_steps"] * (unit_bytes + MERGE_WRITE_BYTES) * args.steps / m["elapsed"] / 1e9,
         "merge_avg_us": m["merge_us"],
         "lmhead": lm,
+        "score": sc,
         "cpu_baseline": cpu,
         "kernel_source_sha": kernel_source_sha(),
     }

@@ -343,6 +343,16 @@ tcb_status tcb_score_catalog(const tcb_trie *t, int32_t n_users, const float *d_
                              int32_t *d_item, float *d_score, float *d_lse, void *d_ws,
                              size_t ws_bytes, void *stream);
 
+/* Diagnostics: record HIP events around the three kernels (table normalisation, scan,
+ * selection) of each of the next `capacity` tcb_score_catalog calls in this process
+ * (0..100000; 0 stops recording and releases the events). */
+tcb_status tcb_score_enable_timing(int32_t capacity);
+
+/* Synchronise the recorded events and report the summed durations (ms) of the table,
+ * scan and selection kernels over the calls recorded since tcb_score_enable_timing, and
+ * their number. Errors: TCB_E_STATE (timing not enabled), TCB_E_HIP. */
+tcb_status tcb_score_timing(double *table_ms, double *scan_ms, double *select_ms, int32_t *calls);
+
 #ifdef __cplusplus
 }
 #endif

@@ -525,24 +525,27 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_select(ScoreDev a) {
 }
 
 template <bool WIDE, int KS>
-hipError_t launch_ks(const ScoreDev &a, hipStream_t s) {
+hipError_t launch_ks(const ScoreDev &a, hipStream_t s, const hipEvent_t *ev) {
     const dim3 scan_grid(kScanWGs, a.groups);
+    if (ev) (void)hipEventRecord(ev[1], s);
     if (a.out_lse)
         hipLaunchKernelGGL((k_score_scan<WIDE, KS, true>), scan_grid, dim3(kScanThreads), 0, s, a);
     else
         hipLaunchKernelGGL((k_score_scan<WIDE, KS, false>), scan_grid, dim3(kScanThreads), 0, s, a);
+    if (ev) (void)hipEventRecord(ev[2], s);
     hipLaunchKernelGGL((k_score_select<WIDE, KS>), dim3(a.U), dim3(kSelectThreads), 0, s, a);
+    if (ev) (void)hipEventRecord(ev[3], s);
     return hipGetLastError();
 }
 
 template <bool WIDE>
-hipError_t launch_w(const ScoreDev &a, hipStream_t s) {
+hipError_t launch_w(const ScoreDev &a, hipStream_t s, const hipEvent_t *ev) {
     switch (a.user_vec ? a.D / 32 : 0) {
-    case 0: return launch_ks<WIDE, 0>(a, s);
-    case 1: return launch_ks<WIDE, 1>(a, s);
-    case 2: return launch_ks<WIDE, 2>(a, s);
-    case 4: return launch_ks<WIDE, 4>(a, s);
-    case 8: return launch_ks<WIDE, 8>(a, s);
+    case 0: return launch_ks<WIDE, 0>(a, s, ev);
+    case 1: return launch_ks<WIDE, 1>(a, s, ev);
+    case 2: return launch_ks<WIDE, 2>(a, s, ev);
+    case 4: return launch_ks<WIDE, 4>(a, s, ev);
+    case 8: return launch_ks<WIDE, 8>(a, s, ev);
     default: return hipErrorInvalidValue;
     }
 }
@@ -563,12 +566,13 @@ ScoreLayout score_layout(int L, int64_t n, int max_users) {
     return o;
 }
 
-hipError_t launch_score(const ScoreDev &a, hipStream_t s) {
+hipError_t launch_score(const ScoreDev &a, hipStream_t s, const hipEvent_t *ev) {
     const int waves = a.groups * a.ug * a.L;
+    if (ev) (void)hipEventRecord(ev[0], s);
     hipLaunchKernelGGL(k_score_table, dim3((waves + 3) / 4), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return a.L > 4 ? launch_w<true>(a, s) : launch_w<false>(a, s);
+    return a.L > 4 ? launch_w<true>(a, s, ev) : launch_w<false>(a, s, ev);
 }
 
 }  // namespace tcb

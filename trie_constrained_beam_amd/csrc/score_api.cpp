@@ -1,8 +1,10 @@
 // Host side of single-pass scoring of every valid SID (SPRINT summary, method and
 // inference paragraphs): argument checks, the leaf-code table, workspace layout and
 // launches. All arithmetic runs in score.hip.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -41,6 +43,19 @@ tcb_status build_codes(tcb_trie *t) {
     }
     return TCB_OK;
 }
+
+// Diagnostic kernel timing of tcb_score_catalog calls (process-wide).
+struct ScoreTiming {
+    std::mutex mu;
+    std::vector<hipEvent_t> ev;
+    int cap = 0, used = 0;
+    void release() {
+        for (auto e : ev) (void)hipEventDestroy(e);
+        ev.clear();
+        cap = used = 0;
+    }
+};
+ScoreTiming g_timing;
 
 }  // namespace
 
@@ -125,8 +140,55 @@ tcb_status tcb_score_catalog(const tcb_trie *t, int32_t n_users, const float *d_
     a.ug = tcb::score_ug(t->L);
     a.groups = (n_users + a.ug - 1) / a.ug;
     a.w = sid_term ? sid_weight : 0.0f;
-    const hipError_t e = tcb::launch_score(a, (hipStream_t)stream);
+    const hipEvent_t *ev = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_timing.mu);
+        if (g_timing.used < g_timing.cap) ev = g_timing.ev.data() + 4 * (g_timing.used++);
+    }
+    const hipError_t e = tcb::launch_score(a, (hipStream_t)stream, ev);
     if (e != hipSuccess) return hip_fail(e, "score_catalog launch");
+    return TCB_OK;
+}
+
+tcb_status tcb_score_enable_timing(int32_t capacity) {
+    if (capacity < 0 || capacity > 100000) return set_error(TCB_E_ARG, "score_enable_timing: capacity out of range");
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.release();
+    if (capacity == 0) return TCB_OK;
+    g_timing.ev.resize((size_t)capacity * 4);
+    for (auto &e : g_timing.ev) {
+        const hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) {
+            e = nullptr;
+            g_timing.ev.erase(std::remove(g_timing.ev.begin(), g_timing.ev.end(), nullptr), g_timing.ev.end());
+            g_timing.release();
+            return hip_fail(r, "score_enable_timing event");
+        }
+    }
+    g_timing.cap = capacity;
+    return TCB_OK;
+}
+
+tcb_status tcb_score_timing(double *table_ms, double *scan_ms, double *select_ms, int32_t *calls) {
+    if (!table_ms || !scan_ms || !select_ms || !calls) return set_error(TCB_E_ARG, "score_timing: null pointer");
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.cap == 0) return set_error(TCB_E_STATE, "score_timing: timing not enabled");
+    double acc[3] = {0.0, 0.0, 0.0};
+    for (int c = 0; c < g_timing.used; ++c) {
+        const hipEvent_t *e = g_timing.ev.data() + 4 * c;
+        hipError_t r = hipEventSynchronize(e[3]);
+        if (r != hipSuccess) return hip_fail(r, "score_timing sync");
+        for (int k = 0; k < 3; ++k) {
+            float ms = 0.0f;
+            r = hipEventElapsedTime(&ms, e[k], e[k + 1]);
+            if (r != hipSuccess) return hip_fail(r, "score_timing elapsed");
+            acc[k] += ms;
+        }
+    }
+    *table_ms = acc[0];
+    *scan_ms = acc[1];
+    *select_ms = acc[2];
+    *calls = g_timing.used;
     return TCB_OK;
 }
 

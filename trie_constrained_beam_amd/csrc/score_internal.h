@@ -49,6 +49,7 @@ struct ScoreLayout {
 };
 ScoreLayout score_layout(int L, int64_t n, int max_users);
 
-hipError_t launch_score(const ScoreDev &a, hipStream_t s);
+// ev: null, or 4 events recorded before the table, scan and select kernels and after
+hipError_t launch_score(const ScoreDev &a, hipStream_t s, const hipEvent_t *ev);
 
 }  // namespace tcb
