@@ -333,11 +333,11 @@ def score_leg(args, cat, dev):
     _lib.check(lib.tcb_score_enable_timing(n_ev))
     for d in range(n_ev):
         run(d)
-    t_ms, s_ms, x_ms, calls = C.c_double(), C.c_double(), C.c_double(), C.c_int32()
-    _lib.check(lib.tcb_score_timing(C.byref(t_ms), C.byref(s_ms), C.byref(x_ms), C.byref(calls)))
+    s_ms, x_ms, calls = C.c_double(), C.c_double(), C.c_int32()
+    _lib.check(lib.tcb_score_timing(C.byref(s_ms), C.byref(x_ms), C.byref(calls)))
     _lib.check(lib.tcb_score_enable_timing(0))
     k = max(1, calls.value)
-    scan_us, table_us, sel_us = s_ms.value * 1e3 / k, t_ms.value * 1e3 / k, x_ms.value * 1e3 / k
+    scan_us, sel_us = s_ms.value * 1e3 / k, x_ms.value * 1e3 / k
     code_bytes = 4 if trie.L <= 4 else 8
     unit_bytes = code_bytes + 2 * wl.dim                     # per SID and group of 32 users
     groups = -(-wl.users // 32)
@@ -346,7 +346,7 @@ def score_leg(args, cat, dev):
     traffic = recorded_traffic(SCORE_TRAFFIC_FILE, SCORE_SOURCES)
     value = wl.users * n * steps / elapsed
     log(f"[bench] scoring leg: {wl.users} users x {n} SIDs, top {wl.k}: {elapsed * 1e3 / steps:.3f} ms per call; "
-        f"scan {scan_us:.1f} us ({achieved:.0f} GB/s), table {table_us:.1f} us, select {sel_us:.1f} us")
+        f"scan {scan_us:.1f} us ({achieved:.0f} GB/s), select {sel_us:.1f} us")
     return {"workload": wl.name, "value": value, "unit": "user-SID scores/s", "steps": steps,
             "ms_per_step": elapsed * 1e3 / steps, "users": wl.users, "sids": n, "dim": wl.dim, "k": wl.k,
             "roofline": {"bound": "hbm", "kernel": "k_score_scan", "achieved": achieved, "peak": HBM_PEAK_GBPS,
@@ -355,7 +355,7 @@ def score_leg(args, cat, dev):
                          "traffic_bytes_per_launch": traffic,
                          "bytes_per_sid": unit_bytes, "bytes_per_launch": bytes_per_launch,
                          "avg_launch_us": scan_us},
-            "table_avg_us": table_us, "select_avg_us": sel_us,
+            "select_avg_us": sel_us,
             "kernel_source_sha": kernel_source_sha(SCORE_SOURCES)}
 
 

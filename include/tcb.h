@@ -305,6 +305,7 @@ void tcb_beams_destroy(tcb_beams *b);
  * (score desc, leaf asc).
  * ------------------------------------------------------------------------------ */
 #define TCB_SCORE_MAX_K 512
+#define TCB_SCORE_MAX_SIDS (1 << 25)
 enum { TCB_TABLE_LOGPROB = 0, TCB_TABLE_LOGITS = 1 };
 
 /* Device copy of every leaf's codes, needed by tcb_score_catalog: 4 bytes per leaf for
@@ -333,7 +334,8 @@ tcb_status tcb_score_workspace_bytes(const tcb_trie *t, int32_t max_users, size_
  *               may be NULL), d_lse float [n_users] (may be NULL: the log-normaliser
  *               is then not computed); rows past n_distinct get leaf -1, item -1 and
  *               score -inf
- * Inputs must be finite. Needs tcb_trie_upload and tcb_trie_upload_codes first and a
+ * Inputs must be finite; at most TCB_SCORE_MAX_SIDS valid SIDs. Needs tcb_trie_upload
+ * and tcb_trie_upload_codes first and a
  * workspace of tcb_score_workspace_bytes(t, n_users) (256-byte aligned). Asynchronous
  * on stream; no device memory is allocated. Errors: TCB_E_ARG, TCB_E_STATE (trie or
  * codes not uploaded), TCB_E_WORKSPACE, TCB_E_HIP. */
@@ -343,15 +345,15 @@ tcb_status tcb_score_catalog(const tcb_trie *t, int32_t n_users, const float *d_
                              int32_t *d_item, float *d_score, float *d_lse, void *d_ws,
                              size_t ws_bytes, void *stream);
 
-/* Diagnostics: record HIP events around the three kernels (table normalisation, scan,
- * selection) of each of the next `capacity` tcb_score_catalog calls in this process
- * (0..100000; 0 stops recording and releases the events). */
+/* Diagnostics: record HIP events around the two kernels (scan, selection) of each of
+ * the next `capacity` tcb_score_catalog calls in this process (0..100000; 0 stops
+ * recording and releases the events). */
 tcb_status tcb_score_enable_timing(int32_t capacity);
 
-/* Synchronise the recorded events and report the summed durations (ms) of the table,
- * scan and selection kernels over the calls recorded since tcb_score_enable_timing, and
- * their number. Errors: TCB_E_STATE (timing not enabled), TCB_E_HIP. */
-tcb_status tcb_score_timing(double *table_ms, double *scan_ms, double *select_ms, int32_t *calls);
+/* Synchronise the recorded events and report the summed durations (ms) of the scan and
+ * selection kernels over the calls recorded since tcb_score_enable_timing, and their
+ * number. Errors: TCB_E_STATE (timing not enabled), TCB_E_HIP. */
+tcb_status tcb_score_timing(double *scan_ms, double *select_ms, int32_t *calls);
 
 #ifdef __cplusplus
 }

@@ -77,8 +77,7 @@ SIGNATURES = {
     "tcb_score_workspace_bytes": (I32, [P, I32, C.POINTER(C.c_size_t)]),
     "tcb_score_catalog": (I32, [P, I32, P, I32, P, P, I32, C.c_float, I32, P, P, P, P, P, C.c_size_t, P]),
     "tcb_score_enable_timing": (I32, [I32]),
-    "tcb_score_timing": (I32, [C.POINTER(C.c_double), C.POINTER(C.c_double), C.POINTER(C.c_double),
-                               C.POINTER(I32)]),
+    "tcb_score_timing": (I32, [C.POINTER(C.c_double), C.POINTER(C.c_double), C.POINTER(I32)]),
 }
 
 _lib = None

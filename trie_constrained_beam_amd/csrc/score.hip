@@ -7,27 +7,30 @@
 // kept, and the softmax runs over the valid SIDs only:
 //   score(u, s) = sum_d T_u[d][c_d(s)] + w <v_u, e_s>,   lse(u) = log sum_s exp score(u, s)
 //
-// Three kernels:
-//   k_score_table   each user's table, normalised per position when it holds raw logits,
-//                   rewritten user-minor: [group][depth][code][user in group]
+// Two kernels:
 //   k_score_scan    one persistent 512-thread workgroup per CU and group of users (32 at
-//                   L <= 4). The group's tables sit in LDS; each wave streams blocks of
-//                   256 SIDs as 16 tiles of 16 (a tile is a group): token sums from LDS (a
-//                   16-byte read gives 4 users), similarities from v_mfma_f32_16x16x32_bf16
+//                   L <= 4). The group's tables, normalised per position when they hold
+//                   raw logits, sit in LDS user-minor ([depth][code][user], so a 16-byte
+//                   read gives 4 users); each wave streams blocks of
+//                   256 SIDs as 16 tiles of 16 (a tile is a group), several tiles of loads
+//                   in flight: token sums from LDS, similarities from v_mfma_f32_16x16x32_bf16
 //                   (16 users x 16 SIDs x 32 embedding elements per step, two user halves),
 //                   SID codes and embeddings read once with nontemporal loads. It writes
 //                   the best score of every group and of every block per user, and
 //                   per-workgroup (max, sum of exp) partials of the log-normaliser.
-//   k_score_select  one workgroup per user. Ranking is (score desc, SID asc) and groups
-//                   and blocks are runs of consecutive SIDs, so the best K SIDs lie in the
-//                   best K groups (ranked by their best score, then by position), and those
-//                   in the best K blocks: if K groups ranked above a SID's group, each
-//                   would hold a SID ranked above it. The kernel takes the exact top K of
-//                   the blocks, then of the groups inside them, rescores the SIDs of the
+//   k_score_select  one workgroup per user. Ranking is (score desc, SID asc) and groups,
+//                   blocks and superblocks (16 blocks) are runs of consecutive SIDs, so the
+//                   best K SIDs lie in the best K groups (ranked by their best score, then
+//                   by position), those in the best K blocks, and those in the best K
+//                   superblocks: if K groups ranked above a SID's group, each would hold a
+//                   SID ranked above it. The kernel takes the exact top K of the
+//                   superblocks, then of the blocks and groups inside them, rescores the SIDs of the
 //                   chosen groups with the very same arithmetic as the scan (same operands,
 //                   same MFMA, same order of additions), takes their exact top K and sorts
 //                   it. Every top-K is a radix selection on order-preserving keys with ties
 //                   taken in ascending position, so the result is deterministic.
+#include <type_traits>
+
 #include "score_internal.h"
 
 namespace tcb {
@@ -39,6 +42,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.6931471805599453f;
+// score of a lane past the last SID in the scan: below any real score, but finite, so
+// that it needs no special case in the running sums of exp
+constexpr float kPastEnd = -1.0e30f;
 
 __device__ __forceinline__ uint32_t f2ord(float f) {   // order-preserving, -0 == +0
     const uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
@@ -52,14 +59,6 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF,
                                                                  0xF, false));
-}
-// maximum over a row of 16 lanes, left in every lane of the row
-__device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, dpp_f<0xB1>(v));     // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp_f<0x4E>(v));     // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp_f<0x141>(v));    // row_half_mirror
-    v = fmaxf(v, dpp_f<0x140>(v));    // row_mirror
-    return v;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -78,11 +77,11 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2
 }
 
 template <bool WIDE>
-__device__ __forceinline__ uint64_t load_codes(const void *codes, int64_t leaf) {
-    if constexpr (WIDE)
-        return __builtin_nontemporal_load(static_cast<const uint64_t *>(codes) + leaf);
-    else
-        return __builtin_nontemporal_load(static_cast<const uint32_t *>(codes) + leaf);
+using CodeWord = typename std::conditional<WIDE, uint64_t, uint32_t>::type;
+
+template <bool WIDE>
+__device__ __forceinline__ CodeWord<WIDE> load_codes(const void *codes, int64_t leaf) {
+    return __builtin_nontemporal_load(static_cast<const CodeWord<WIDE> *>(codes) + leaf);
 }
 
 // MFMA operands of the similarity tile (v_mfma_f32_16x16x32_bf16). Lane (j = lane & 15,
@@ -118,14 +117,19 @@ __device__ __forceinline__ f32x4 sim_tile(const u32x4 (&av)[KS], const u32x4 (&b
 
 // Token sums of one SID for the lane's users: register 4 hh + e holds user row
 // 16 hh + 4 g + e (the MFMA output layout, one 16-user half per hh), added level by
-// level from 0.
-template <int UG, int NR>
-__device__ __forceinline__ void token_sums(const float *tbl, uint64_t cw, int L, int g, float (&s)[NR]) {
+// level from 0 over LP levels (levels past L hold zero rows and code 0). The LDS row of
+// (depth d, code c) starts at (256 d + c) * ST; row 256 LP holds kPastEnd, read at depth 0
+// by lanes past the last SID so that their scores come out below every real one without a
+// per-value select.
+template <int NR, int LP, int ST, class W>
+__device__ __forceinline__ void token_sums(const float *tbl, W cw, bool valid, int g, float (&s)[NR]) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) s[r] = 0.0f;
-    for (int d = 0; d < L; ++d) {
+#pragma unroll
+    for (int d = 0; d < LP; ++d) {
         const uint32_t c = (uint32_t)(cw >> (8 * d)) & 255u;
-        const f32x4 *row = reinterpret_cast<const f32x4 *>(tbl + (size_t)(d * 256 + (int)c) * UG + 4 * g);
+        const int rix = (d == 0 && !valid) ? LP * 256 : d * 256 + (int)c;   // past the end: the -inf row
+        const f32x4 *row = reinterpret_cast<const f32x4 *>(tbl + rix * ST + 4 * g);
 #pragma unroll
         for (int hh = 0; hh < NR / 4; ++hh) {
             const f32x4 v = row[4 * hh];
@@ -137,44 +141,96 @@ __device__ __forceinline__ void token_sums(const float *tbl, uint64_t cw, int L,
     }
 }
 
-// ---------------------------------------------------------------------- table
-// One wave per (padded user, depth): log-softmax over the V codes for raw logits;
-// codes >= V and users >= U get 0.
-__global__ __launch_bounds__(256) void k_score_table(ScoreDev a) {
-    const int lane = threadIdx.x & 63;
-    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int UG = a.ug, L = a.L, V = a.V;
-    if (wid >= a.groups * UG * L) return;
-    const int d = wid % L, uu = wid / L;
-    const int grp = uu / UG, row = uu % UG;
-    const bool user = uu < a.U;
-    float x[4];
+// Maximum over the 16 lanes of a DPP row for each of a lane's NR values (NR = 8 or 4,
+// one per user), by a transposed butterfly: each exchange halves the values a lane keeps,
+// so 8 values need 4 + 2 + 1 + 1 moves instead of 8 x 4. The pairings are xor 1, xor 2,
+// row_half_mirror (i <-> 7 - i) and row_mirror (i <-> 15 - i); the half a lane keeps is
+// chosen by c0 = b0^b2, c1 = b1^b2, c2 = b2^b3 (b = bits of its lane in the row), which
+// makes every partner hold the same users. Lane j ends with the maximum of register
+// reduced_reg(j); lanes j and 15 - j hold the same one.
+template <int NR>
+__device__ __forceinline__ int reduced_reg(int j) {
+    const int b0 = j & 1, b1 = (j >> 1) & 1, b2 = (j >> 2) & 1, b3 = (j >> 3) & 1;
+    if constexpr (NR == 8)
+        return 4 * (b0 ^ b2) + 2 * (b1 ^ b2) + (b2 ^ b3);
+    else
+        return 2 * (b0 ^ b2) + (b1 ^ b2);
+}
+
+template <int NR>
+__device__ __forceinline__ float transposed_max(const float (&v)[NR], int j) {
+    const bool c0 = ((j ^ (j >> 2)) & 1) != 0, c1 = (((j >> 1) ^ (j >> 2)) & 1) != 0;
+    constexpr int H = NR / 2;
+    float w[H];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int c = lane * 4 + e;
-        x[e] = (user && c < V) ? a.table_in[((size_t)uu * L + d) * V + c] : 0.0f;
+    for (int r = 0; r < H; ++r) {
+        const float keep = c0 ? v[r + H] : v[r], send = c0 ? v[r] : v[r + H];
+        w[r] = fmaxf(keep, dpp_f<0xB1>(send));                // xor 1
     }
-    if (a.kind == TCB_TABLE_LOGITS && user) {
-        float m = kNegInf;
+    constexpr int Q = H / 2;
+    float x[Q];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (lane * 4 + e < V) m = fmaxf(m, x[e]);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        float sum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (lane * 4 + e < V) sum += expf(x[e] - m);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
-        const float lse = m + logf(sum);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (lane * 4 + e < V) x[e] -= lse;
+    for (int r = 0; r < Q; ++r) {
+        const float keep = c1 ? w[r + Q] : w[r], send = c1 ? w[r] : w[r + Q];
+        x[r] = fmaxf(keep, dpp_f<0x4E>(send));                // xor 2
     }
-    float *out = a.table + ((size_t)grp * L + d) * 256 * UG + row;
+    float y;
+    if constexpr (NR == 8) {
+        const bool c2 = (((j >> 2) ^ (j >> 3)) & 1) != 0;
+        const float keep = c2 ? x[1] : x[0], send = c2 ? x[0] : x[1];
+        y = fmaxf(keep, dpp_f<0x141>(send));                  // row_half_mirror
+    } else {
+        y = fmaxf(x[0], dpp_f<0x141>(x[0]));
+    }
+    return fmaxf(y, dpp_f<0x140>(y));                         // row_mirror
+}
+
+
+// ---------------------------------------------------------------------- tables
+// The group's tables into LDS, normalised per position for raw logits (log-softmax over
+// the V codes); codes >= V and users >= U get 0. One wave per (user, depth) row. Every
+// workgroup computes the same values; with `store` it also writes them to the
+// workspace for the selection kernel.
+template <int UG, int LP, int ST>
+__device__ void load_tables(const ScoreDev &a, int grp, float *tbl, bool store) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int L = a.L, V = a.V;
+    float *gout = a.table + (size_t)grp * L * 256 * UG;
+    for (int rw = wave; rw < UG * LP; rw += kScanWaves) {
+        const int row = rw / LP, d = rw % LP, uu = grp * UG + row;
+        const bool user = uu < a.U && d < L;
+        float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[(size_t)(lane * 4 + e) * UG] = x[e];
+        for (int e = 0; e < 4; ++e) {
+            const int c = lane * 4 + e;
+            x[e] = (user && c < V) ? a.table_in[((size_t)uu * L + d) * V + c] : 0.0f;
+        }
+        if (a.kind == TCB_TABLE_LOGITS && user) {
+            float m = kNegInf;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (lane * 4 + e < V) m = fmaxf(m, x[e]);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+            float sum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (lane * 4 + e < V) sum += expf(x[e] - m);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+            const float lse = m + logf(sum);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (lane * 4 + e < V) x[e] -= lse;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = d * 256 + lane * 4 + e;
+            tbl[c * ST + row] = x[e];
+            if (store && d < L) gout[(size_t)c * UG + row] = x[e];
+        }
+    }
+    for (int i = threadIdx.x; i < ST; i += kScanThreads) tbl[LP * 256 * ST + i] = kPastEnd;
 }
 
 // ---------------------------------------------------------------------- scan
@@ -185,18 +241,18 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
     constexpr int NR = 4 * NH;                        // (user, SID) values per lane and tile
     constexpr int KA = KS > 0 ? KS : 1;
     constexpr int TPB = kScoreBlock / kScoreGroup;    // tiles (groups) per block
+    constexpr int PD = KS == 0 ? 8 : (KS <= 2 ? 4 : 2);   // tiles of loads in flight per wave
+    static_assert(TPB % PD == 0, "whole rounds of the load pipeline per block");
     __shared__ f32x4 tbl4[kScoreTableFloats / 4];
     __shared__ float2 part[kScanWaves][32];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 15, g = lane >> 4;
-    const int grp = blockIdx.y, L = a.L;
-    const int64_t n = a.n, NG = (n + kScoreGroup - 1) / kScoreGroup, NB = (n + kScoreBlock - 1) / kScoreBlock;
-    {
-        const int nf4 = UG * L * 64;
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.table) + (size_t)grp * nf4;
-        for (int i = tid; i < nf4; i += kScanThreads) tbl4[i] = src[i];
-    }
-    const float *tbl = reinterpret_cast<const float *>(tbl4);
+    constexpr int LP = WIDE ? 8 : 4;                  // levels, padded
+    constexpr int ST = WIDE ? kScoreStrideWide : kScoreStrideNarrow;
+    const int grp = blockIdx.y;
+    const int n = (int)a.n, NG = (n + kScoreGroup - 1) / kScoreGroup, NB = (n + kScoreBlock - 1) / kScoreBlock;
+    float *tbl = reinterpret_cast<float *>(tbl4);
+    load_tables<UG, LP, ST>(a, grp, tbl, blockIdx.x == 0);
     u32x4 av[NH][KA];
     if constexpr (KS > 0) {
 #pragma unroll
@@ -205,86 +261,94 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
             load_rows<KS>(a.user_vec, user, user < a.U, g, av[hh], false);
         }
     }
-    float lm[NR], ls[NR];
+    // log-normaliser partials: per lane and register a reference rl (in log2 units) and
+    // the sum ls of 2^(x log2 e - rl) over the scores x seen; the reference is the first
+    // score, raised (and the sum rescaled) when a score exceeds it by more than 2^64
+    float rl[NR], ls[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        lm[r] = kNegInf;
+        rl[r] = kNegInf;
         ls[r] = 0.0f;
     }
     __syncthreads();
     const float w = a.w;
     float *gmax = a.gmax + (size_t)grp * NG * UG;
-    float *bmax = a.bmax + (size_t)grp * NB * UG;
-    const int wr = 16 * (j >> 2) + 4 * g + (j & 3);   // the user row whose maxima lane j < NR stores
+    // after the transposed reduction lane j holds register ru of its row's users
+    const int ru = reduced_reg<NR>(j);
+    const int wr = 16 * (ru >> 2) + 4 * g + (ru & 3);        // ... i.e. this user row of the group
+    const bool writer = j < NR;                                // these lanes hold distinct users
+    float *bmax = a.bmax + ((size_t)grp * UG + wr) * NB;
 
-    for (int64_t blk = (int64_t)blockIdx.x * kScanWaves + wave; blk < NB; blk += (int64_t)gridDim.x * kScanWaves) {
-        float bm[NR];
+    // this wave's tiles: its blocks first, first + stride, ... taken 16 tiles each, as one
+    // sequence, so loads run PD tiles ahead across block ends; past the end they read the
+    // last SID again (a valid address) and the results are masked
+    const int first = (int)blockIdx.x * kScanWaves + wave, stride = (int)gridDim.x * kScanWaves;
+    const int ntile = first < NB ? ((NB - 1 - first) / stride + 1) * TPB : 0;
+    auto tile_first = [&](int q) { return (first + (q / TPB) * stride) * kScoreBlock + (q % TPB) * kScoreGroup; };
+    CodeWord<WIDE> cw[PD];
+    u32x4 bv[PD][KA];
+    auto load_tile = [&](int q, int slot) {
+        int leaf = tile_first(q) + j;
+        leaf = leaf < n ? leaf : n - 1;
+        cw[slot] = load_codes<WIDE>(a.codes, leaf);
+        if constexpr (KS > 0) load_rows<KS>(a.emb, leaf, true, g, bv[slot], true);
+    };
+    float bm = kNegInf;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) bm[r] = kNegInf;
-        uint64_t cw[2];
-        u32x4 bv[2][KA];
-        auto load_tile = [&](int t, int slot) {
-            const int64_t leaf = blk * kScoreBlock + t * kScoreGroup + j;
-            const bool valid = leaf < n;
-            cw[slot] = valid ? load_codes<WIDE>(a.codes, leaf) : 0ull;
-            if constexpr (KS > 0) load_rows<KS>(a.emb, leaf, valid, g, bv[slot], true);
-        };
-        auto tile = [&](int t, int slot) {
-            const int64_t grp_id = blk * TPB + t;
+    for (int q = 0; q < PD - 1; ++q) load_tile(q, q);
+#pragma unroll 1
+    for (int q0 = 0; q0 < ntile; q0 += PD) {
+#pragma unroll
+        for (int q = 0; q < PD; ++q) {
+            load_tile(q0 + q + PD - 1, (q + PD - 1) % PD);
+            const int f = tile_first(q0 + q);
             float s[NR];
-            token_sums<UG, NR>(tbl, cw[slot], L, g, s);
+            token_sums<NR, LP, ST>(tbl, cw[q], f + j < n, g, s);
             if constexpr (KS > 0) {
 #pragma unroll
                 for (int hh = 0; hh < NH; ++hh) {
-                    const f32x4 acc = sim_tile<KS>(av[hh], bv[slot]);
+                    const f32x4 acc = sim_tile<KS>(av[hh], bv[q]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) s[4 * hh + e] = fmaf(w, acc[e], s[4 * hh + e]);
                 }
             }
-            if (grp_id * kScoreGroup + j >= n) {
-#pragma unroll
-                for (int r = 0; r < NR; ++r) s[r] = kNegInf;
-            }
-            float gm[NR];
-#pragma unroll
-            for (int r = 0; r < NR; ++r) gm[r] = row16_max(s[r]);
-            float v = gm[0];
-#pragma unroll
-            for (int r = 1; r < NR; ++r) v = j == r ? gm[r] : v;
-            if (j < NR && grp_id < NG) gmax[grp_id * UG + wr] = v;
-#pragma unroll
-            for (int r = 0; r < NR; ++r) bm[r] = fmaxf(bm[r], gm[r]);
             if constexpr (LSE) {
+                float t[NR], mx = kNegInf;
 #pragma unroll
                 for (int r = 0; r < NR; ++r) {
-                    const float M = fmaxf(lm[r], gm[r]);
-                    if (M > lm[r]) {
-                        ls[r] *= exp2_fast(kLog2e * (lm[r] - M));
-                        lm[r] = M;
-                    }
-                    if (M != kNegInf) ls[r] += exp2_fast(kLog2e * (s[r] - M));
+                    t[r] = fmaf(s[r], kLog2e, -rl[r]);
+                    mx = fmaxf(mx, t[r]);
                 }
-            }
-        };
-        load_tile(0, 0);
-#pragma unroll 1
-        for (int t = 0; t < TPB; t += 2) {
-            load_tile(t + 1, 1);
-            tile(t, 0);
-            if (t + 2 < TPB) load_tile(t + 2, 0);
-            tile(t + 1, 1);
-        }
-        float v = bm[0];
+                if (mx > 64.0f) {                                // first scores, or a rare jump
 #pragma unroll
-        for (int r = 1; r < NR; ++r) v = j == r ? bm[r] : v;
-        if (j < NR) bmax[blk * UG + wr] = v;
+                    for (int r = 0; r < NR; ++r)
+                        if (t[r] > 0.0f) {
+                            ls[r] *= exp2_fast(-t[r]);
+                            rl[r] = s[r] * kLog2e;
+                            t[r] = 0.0f;
+                        }
+                }
+#pragma unroll
+                for (int r = 0; r < NR; ++r) ls[r] += exp2_fast(t[r]);
+            }
+            const float v = transposed_max<NR>(s, j);
+            const int gid = f / kScoreGroup;
+            if (writer && gid < NG) gmax[gid * UG + wr] = v;
+            bm = fmaxf(bm, v);
+            if (((q0 + q) % TPB) == TPB - 1) {                // block end
+                if (writer) bmax[f / kScoreBlock] = bm;
+                bm = kNegInf;
+            }
+        }
     }
 
     if constexpr (LSE) {
         // the 16 lanes of a DPP row hold the same users: butterfly over them, then the
         // waves in order
+        float lm[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
+            lm[r] = rl[r] * kLn2;                              // back to natural-log units
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) {
                 const float m2 = __shfl_xor(lm[r], o, 64), s2 = __shfl_xor(ls[r], o, 64);
@@ -312,6 +376,7 @@ constexpr int kSelWaves = kSelectThreads / 64;
 struct SelSmem {
     uint32_t hist[256];
     uint32_t wcount[kSelWaves];
+    uint32_t mn[kSelWaves], mx[kSelWaves];
     uint32_t st[4];
 };
 
@@ -335,18 +400,46 @@ __device__ __forceinline__ uint32_t block_count_before(bool f, SelSmem &S, uint3
 }
 
 // Exact top-k of n keys (a larger key is better; equal keys: the lower position first,
-// 1 <= k <= n): writes the chosen positions, ascending, to out[0 .. k).
+// 1 <= k <= n): writes the chosen positions, ascending, to out[0 .. k). Radix selection
+// of the k-th best key over d = key - (smallest key), 8 bits per pass from the highest
+// bit in which the keys differ (so the first pass spreads them over the bins), then one
+// ordered compaction.
 template <class Key>
 __device__ void select_top(int k, int n, const Key &key, uint32_t *out, SelSmem &S) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    uint32_t prefix = 0u, mask = 0u;
-    uint32_t rem = (uint32_t)k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int i = tid; i < n; i += kSelectThreads) {
+        const uint32_t kv = key(i);
+        lo = min(lo, kv);
+        hi = max(hi, kv);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+    }
+    if (lane == 0) {
+        S.mn[wave] = lo;
+        S.mx[wave] = hi;
+    }
+    __syncthreads();
+    lo = S.mn[0];
+    hi = S.mx[0];
+#pragma unroll
+    for (int w = 1; w < kSelWaves; ++w) {
+        lo = min(lo, S.mn[w]);
+        hi = max(hi, S.mx[w]);
+    }
+    __syncthreads();
+    uint32_t pref = 0u, rem = (uint32_t)k;
+    int remaining = hi > lo ? 32 - __clz((int)(hi - lo)) : 0;   // bits of d still undecided
+    while (remaining > 0) {
+        const int w = min(8, remaining), shift = remaining - w;
         for (int i = tid; i < 256; i += kSelectThreads) S.hist[i] = 0u;
         __syncthreads();
         for (int i = tid; i < n; i += kSelectThreads) {
-            const uint32_t kv = key(i);
-            if ((kv & mask) == prefix) atomicAdd(&S.hist[(kv >> shift) & 255u], 1u);
+            const uint32_t d = key(i) - lo;
+            if ((uint32_t)((uint64_t)d >> remaining) == pref) atomicAdd(&S.hist[(d >> shift) & ((1u << w) - 1u)], 1u);
         }
         __syncthreads();
         if (tid < 64) {
@@ -381,16 +474,16 @@ __device__ void select_top(int k, int n, const Key &key, uint32_t *out, SelSmem 
         __syncthreads();
         const uint32_t digit = S.st[0], above = S.st[1];
         rem -= above;
-        prefix |= digit << shift;
-        mask |= 255u << shift;
+        pref = (pref << w) | digit;
+        remaining = shift;
         __syncthreads();
     }
-    // prefix is the k-th best key; take every key above it and the first rem equal to it
+    const uint32_t T = lo + pref;     // the k-th best key; take all above it and the first rem equal
     uint32_t eq_seen = 0u, taken = 0u;
     for (int base = 0; base < n; base += kSelectThreads) {
         const int i = base + tid;
         const uint32_t kv = i < n ? key(i) : 0u;
-        const bool eq = i < n && kv == prefix, gt = i < n && kv > prefix;
+        const bool eq = i < n && kv == T, gt = i < n && kv > T;
         uint32_t eq_tot, take_tot;
         const uint32_t eq_rank = eq_seen + block_count_before(eq, S, eq_tot);
         const bool take = gt || (eq && eq_rank < rem);
@@ -407,7 +500,11 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_select(ScoreDev a) {
     constexpr int UG = WIDE ? kScoreUGWide : kScoreUGNarrow;
     constexpr int KA = KS > 0 ? KS : 1;
     constexpr int MK = TCB_SCORE_MAX_K;
+    constexpr int SUB = kScoreBlock / kScoreGroup;       // groups per block = blocks per superblock
+    constexpr int RB = KS >= 8 ? 2 : (KS >= 4 ? 4 : 8);   // groups a wave rescores at once, loads in flight
+    constexpr int LP = WIDE ? 8 : 4;
     __shared__ float val[kScoreCand];
+    __shared__ float sbm[kScoreCand];
     __shared__ uint32_t listA[MK], listB[MK];
     __shared__ uint64_t sortk[MK];
     __shared__ SelSmem S;
@@ -415,32 +512,58 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_select(ScoreDev a) {
     const int j = lane & 15, g = lane >> 4;
     const int u = blockIdx.x, grp = u / UG, row = u % UG, L = a.L;
     const int64_t n = a.n, NG = (n + kScoreGroup - 1) / kScoreGroup, NB = (n + kScoreBlock - 1) / kScoreBlock;
+    const int NS = (int)((NB + SUB - 1) / SUB);
     const int K = a.K;
 
-    // 1. the best K blocks by their best score
-    const float *bm = a.bmax + (size_t)grp * NB * UG + row;
-    const int nA = (int)NB, kA = min(K, nA);
-    select_top(kA, nA, [&](int i) { return f2ord(bm[(size_t)i * UG]); }, listA, S);
+    // 1. superblock maxima from this user's block maxima (contiguous), then the best K
+    const float *bm = a.bmax + ((size_t)grp * UG + row) * NB;
+    for (int sb = tid; sb < NS; sb += kSelectThreads) {
+        float m = kNegInf;
+#pragma unroll
+        for (int t = 0; t < SUB; ++t) {
+            const int64_t b = (int64_t)sb * SUB + t;
+            if (b < NB) m = fmaxf(m, bm[b]);
+        }
+        sbm[sb] = m;
+    }
+    __syncthreads();
+    const int kS = min(K, NS);
+    select_top(kS, NS, [&](int i) { return f2ord(sbm[i]); }, listA, S);
 
-    // 2. the best K groups inside them
+    // 2. the best K blocks inside them
+    const int nA = SUB * kS;
+    for (int p = tid; p < nA; p += kSelectThreads) {
+        const int64_t b = (int64_t)listA[p / SUB] * SUB + (p % SUB);
+        val[p] = b < NB ? bm[b] : kNegInf;
+    }
+    __syncthreads();
+    const int kA = min(K, nA);
+    select_top(kA, nA, [&](int i) { return f2ord(val[i]); }, listB, S);
+    for (int q = tid; q < kA; q += kSelectThreads) {
+        const uint32_t p = listB[q];
+        listB[q] = listA[p / SUB] * (uint32_t)SUB + (p % SUB);
+    }
+    __syncthreads();
+
+    // 3. the best K groups inside those blocks
     const float *gm = a.gmax + (size_t)grp * NG * UG + row;
-    const int nB = kScoreBlock / kScoreGroup * kA;
+    const int nB = SUB * kA;
     for (int p = tid; p < nB; p += kSelectThreads) {
-        const int64_t g = (int64_t)listA[p >> 4] * (kScoreBlock / kScoreGroup) + (p & 15);
-        val[p] = g < NG ? gm[(size_t)g * UG] : kNegInf;
+        const int64_t gi = (int64_t)listB[p / SUB] * SUB + (p % SUB);
+        val[p] = gi < NG ? gm[(size_t)gi * UG] : kNegInf;
     }
     __syncthreads();
     const int kB = min(K, nB);
-    select_top(kB, nB, [&](int i) { return f2ord(val[i]); }, listB, S);
+    select_top(kB, nB, [&](int i) { return f2ord(val[i]); }, listA, S);
     for (int q = tid; q < kB; q += kSelectThreads) {
-        const uint32_t p = listB[q];
-        listB[q] = listA[p >> 4] * (uint32_t)(kScoreBlock / kScoreGroup) + (p & 15u);
+        const uint32_t p = listA[q];
+        listA[q] = listB[p / SUB] * (uint32_t)SUB + (p % SUB);
     }
     __syncthreads();
 
-    // 3. rescore the SIDs of those groups: one 16-SID MFMA tile per group; only the
-    //    16-user half holding this user is multiplied (its result does not depend on
-    //    the other half)
+    // 4. rescore the SIDs of those groups: one 16-SID MFMA tile per group; only the
+    //    16-user half holding this user is multiplied (its result does not depend on the
+    //    other half). A wave takes RB groups at a time, all their loads in flight.
     const int hh_u = row >> 4, g_u = (row >> 2) & 3, e_u = row & 3;
     u32x4 av[KA];
     if constexpr (KS > 0) {
@@ -448,35 +571,55 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_select(ScoreDev a) {
         load_rows<KS>(a.user_vec, user, user < a.U, g, av, false);
     }
     const float *tg = a.table + (size_t)grp * L * 256 * UG + row;
-    for (int q = wave; q < kB; q += kSelWaves) {
-        const int64_t leaf = (int64_t)listB[q] * kScoreGroup + j;
-        const bool valid = leaf < n;
-        const uint64_t cw = valid ? load_codes<WIDE>(a.codes, leaf) : 0ull;
-        float s = 0.0f;
-        for (int d = 0; d < L; ++d) s += tg[(size_t)(d * 256 + (int)((cw >> (8 * d)) & 255u)) * UG];
-        if constexpr (KS > 0) {
-            u32x4 bv[KA];
-            load_rows<KS>(a.emb, leaf, valid, g, bv, false);
-            const f32x4 acc = sim_tile<KS>(av, bv);
-            const float x = e_u == 0 ? acc[0] : e_u == 1 ? acc[1] : e_u == 2 ? acc[2] : acc[3];
-            s = fmaf(a.w, x, s);
+    for (int q0 = wave; q0 < kB; q0 += kSelWaves * RB) {
+        CodeWord<WIDE> cw[RB];
+        u32x4 bv[RB][KA];
+        bool valid[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const int q = q0 + b * kSelWaves;
+            const int64_t leaf = q < kB ? (int64_t)listA[q] * kScoreGroup + j : n;
+            valid[b] = leaf < n;
+            cw[b] = valid[b] ? load_codes<WIDE>(a.codes, leaf) : (CodeWord<WIDE>)0;
+            if constexpr (KS > 0) load_rows<KS>(a.emb, leaf, valid[b], g, bv[b], false);
         }
-        if (!valid) s = kNegInf;
-        if (g == g_u) val[q * kScoreGroup + j] = s;
+        float s[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            s[b] = 0.0f;
+            // the scan's order of additions, zero rows past L included
+#pragma unroll
+            for (int d = 0; d < LP; ++d)
+                s[b] += d < L ? tg[(size_t)(d * 256 + (int)((cw[b] >> (8 * d)) & 255u)) * UG] : 0.0f;
+        }
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const int q = q0 + b * kSelWaves;
+            if constexpr (KS > 0) {
+                const f32x4 acc = sim_tile<KS>(av, bv[b]);
+                // register e_u by two bit selects: a chain of equality tests is lowered to
+                // branches, and a branch taken right after the MFMA was compiled without the
+                // wait states its result needs (wrong values seen on gfx950)
+                const float lo = (e_u & 1) ? acc[1] : acc[0], hi = (e_u & 1) ? acc[3] : acc[2];
+                s[b] = fmaf(a.w, (e_u & 2) ? hi : lo, s[b]);
+            }
+            if (!valid[b]) s[b] = kNegInf;
+            if (q < kB && g == g_u) val[q * kScoreGroup + j] = s[b];
+        }
     }
     __syncthreads();
 
-    // 4. the best K SIDs, then sorted by (score desc, SID asc)
+    // 5. the best K SIDs, then sorted by (score desc, SID asc)
     const int nC = kScoreGroup * kB;
     const int kC = (int)min((int64_t)K, n);
-    select_top(kC, nC, [&](int i) { return f2ord(val[i]); }, listA, S);
+    select_top(kC, nC, [&](int i) { return f2ord(val[i]); }, listB, S);
     int P2 = 1;
     while (P2 < kC) P2 <<= 1;
     for (int i = tid; i < P2; i += kSelectThreads) {
         uint64_t key = ~0ull;
         if (i < kC) {
-            const uint32_t p = listA[i];
-            const uint32_t leaf = listB[p >> 4] * (uint32_t)kScoreGroup + (p & 15u);
+            const uint32_t p = listB[i];
+            const uint32_t leaf = listA[p / kScoreGroup] * (uint32_t)kScoreGroup + (p % kScoreGroup);
             key = ((uint64_t)(~f2ord(val[p])) << 32) | leaf;
         }
         sortk[i] = key;
@@ -510,7 +653,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_select(ScoreDev a) {
         if (a.out_item) a.out_item[(size_t)u * K + i] = item;
     }
 
-    // 5. log-normaliser of the softmax over every valid SID: scan partials in order
+    // 6. log-normaliser of the softmax over every valid SID: the scan's partials in order
     if (a.out_lse && wave == 0) {
         const float *pp = a.lse_part + ((size_t)grp * kScanWGs * UG + row) * 2;
         float m = kNegInf, s = 0.0f;
@@ -527,14 +670,14 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_select(ScoreDev a) {
 template <bool WIDE, int KS>
 hipError_t launch_ks(const ScoreDev &a, hipStream_t s, const hipEvent_t *ev) {
     const dim3 scan_grid(kScanWGs, a.groups);
-    if (ev) (void)hipEventRecord(ev[1], s);
+    if (ev) (void)hipEventRecord(ev[0], s);
     if (a.out_lse)
         hipLaunchKernelGGL((k_score_scan<WIDE, KS, true>), scan_grid, dim3(kScanThreads), 0, s, a);
     else
         hipLaunchKernelGGL((k_score_scan<WIDE, KS, false>), scan_grid, dim3(kScanThreads), 0, s, a);
-    if (ev) (void)hipEventRecord(ev[2], s);
+    if (ev) (void)hipEventRecord(ev[1], s);
     hipLaunchKernelGGL((k_score_select<WIDE, KS>), dim3(a.U), dim3(kSelectThreads), 0, s, a);
-    if (ev) (void)hipEventRecord(ev[3], s);
+    if (ev) (void)hipEventRecord(ev[2], s);
     return hipGetLastError();
 }
 
@@ -567,11 +710,6 @@ ScoreLayout score_layout(int L, int64_t n, int max_users) {
 }
 
 hipError_t launch_score(const ScoreDev &a, hipStream_t s, const hipEvent_t *ev) {
-    const int waves = a.groups * a.ug * a.L;
-    if (ev) (void)hipEventRecord(ev[0], s);
-    hipLaunchKernelGGL(k_score_table, dim3((waves + 3) / 4), dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     return a.L > 4 ? launch_w<true>(a, s, ev) : launch_w<false>(a, s, ev);
 }
 

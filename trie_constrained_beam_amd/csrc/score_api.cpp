@@ -100,7 +100,7 @@ tcb_status tcb_score_catalog(const tcb_trie *t, int32_t n_users, const float *d_
     if (k < 1 || k > TCB_SCORE_MAX_K) return set_error(TCB_E_ARG, "score_catalog: k must be in 1..512");
     if (table_kind != TCB_TABLE_LOGPROB && table_kind != TCB_TABLE_LOGITS)
         return set_error(TCB_E_ARG, "score_catalog: bad table_kind");
-    if (t->n_distinct >= ((int64_t)1 << 31) - 256) return set_error(TCB_E_ARG, "score_catalog: too many SIDs");
+    if (t->n_distinct > TCB_SCORE_MAX_SIDS) return set_error(TCB_E_ARG, "score_catalog: more than 2^25 SIDs");
     const bool sid_term = d_user_vec || d_sid_emb;
     if (sid_term) {
         if (!d_user_vec || !d_sid_emb)
@@ -143,7 +143,7 @@ tcb_status tcb_score_catalog(const tcb_trie *t, int32_t n_users, const float *d_
     const hipEvent_t *ev = nullptr;
     {
         std::lock_guard<std::mutex> lk(g_timing.mu);
-        if (g_timing.used < g_timing.cap) ev = g_timing.ev.data() + 4 * (g_timing.used++);
+        if (g_timing.used < g_timing.cap) ev = g_timing.ev.data() + 3 * (g_timing.used++);
     }
     const hipError_t e = tcb::launch_score(a, (hipStream_t)stream, ev);
     if (e != hipSuccess) return hip_fail(e, "score_catalog launch");
@@ -155,7 +155,7 @@ tcb_status tcb_score_enable_timing(int32_t capacity) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     g_timing.release();
     if (capacity == 0) return TCB_OK;
-    g_timing.ev.resize((size_t)capacity * 4);
+    g_timing.ev.resize((size_t)capacity * 3);
     for (auto &e : g_timing.ev) {
         const hipError_t r = hipEventCreate(&e);
         if (r != hipSuccess) {
@@ -169,25 +169,24 @@ tcb_status tcb_score_enable_timing(int32_t capacity) {
     return TCB_OK;
 }
 
-tcb_status tcb_score_timing(double *table_ms, double *scan_ms, double *select_ms, int32_t *calls) {
-    if (!table_ms || !scan_ms || !select_ms || !calls) return set_error(TCB_E_ARG, "score_timing: null pointer");
+tcb_status tcb_score_timing(double *scan_ms, double *select_ms, int32_t *calls) {
+    if (!scan_ms || !select_ms || !calls) return set_error(TCB_E_ARG, "score_timing: null pointer");
     std::lock_guard<std::mutex> lk(g_timing.mu);
     if (g_timing.cap == 0) return set_error(TCB_E_STATE, "score_timing: timing not enabled");
-    double acc[3] = {0.0, 0.0, 0.0};
+    double acc[2] = {0.0, 0.0};
     for (int c = 0; c < g_timing.used; ++c) {
-        const hipEvent_t *e = g_timing.ev.data() + 4 * c;
-        hipError_t r = hipEventSynchronize(e[3]);
+        const hipEvent_t *e = g_timing.ev.data() + 3 * c;
+        hipError_t r = hipEventSynchronize(e[2]);
         if (r != hipSuccess) return hip_fail(r, "score_timing sync");
-        for (int k = 0; k < 3; ++k) {
+        for (int k = 0; k < 2; ++k) {
             float ms = 0.0f;
             r = hipEventElapsedTime(&ms, e[k], e[k + 1]);
             if (r != hipSuccess) return hip_fail(r, "score_timing elapsed");
             acc[k] += ms;
         }
     }
-    *table_ms = acc[0];
-    *scan_ms = acc[1];
-    *select_ms = acc[2];
+    *scan_ms = acc[0];
+    *select_ms = acc[1];
     *calls = g_timing.used;
     return TCB_OK;
 }

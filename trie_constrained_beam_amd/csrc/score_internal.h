@@ -14,7 +14,14 @@ namespace tcb {
 // v_mfma_f32_32x32x16_bf16 tile holds the group's 32 users x 32 SIDs.
 constexpr int kScoreUGNarrow = 32;            // L <= 4
 constexpr int kScoreUGWide = 16;              // 5 <= L <= 8
-constexpr int kScoreTableFloats = 32 * 4 * 256;
+// LDS for the tables: levels padded to 4 (L <= 4) or 8 with zero rows, so every SID
+// adds the same number of terms; a row of (depth, code) holds the group's users, padded
+// by 4 floats at L <= 4 (a row stride of an odd multiple of 16 bytes spreads the lanes'
+// random codes over the LDS banks)
+constexpr int kScoreStrideNarrow = kScoreUGNarrow + 4;    // 36 floats, 4 levels
+constexpr int kScoreStrideWide = kScoreUGWide;            // 16 floats, 8 levels
+constexpr int kScoreTableFloats = kScoreStrideNarrow * (4 * 256 + 1);   // + a row of -inf
+static_assert(kScoreStrideWide * (8 * 256 + 1) <= kScoreTableFloats, "wide tables fit the same LDS");
 constexpr int kScoreGroup = 16;               // SIDs per group (one DPP row)
 constexpr int kScoreBlock = 256;              // SIDs per block (8 MFMA tiles)
 constexpr int kScanWaves = 8;
@@ -29,11 +36,11 @@ struct ScoreDev {
     const void *codes;          // [n] leaf codes: u32 (L <= 4) or u64, byte d = code at depth d
     const int32_t *leaf_item;   // [n] lowest catalog row of each SID
     const float *table_in;      // [U][L][V] caller table
-    float *table;               // [groups][L][256][UG] normalised, user-minor
+    float *table;               // [groups][L][256][UG] normalised, user-minor (written by the scan)
     const uint16_t *user_vec;   // [U][D] bf16, or null
     const uint16_t *emb;        // [n][D] bf16 in leaf order, or null
     float *gmax;                // [groups][ceil(n / 16)][UG] best score of each 16-SID group
-    float *bmax;                // [groups][ceil(n / 256)][UG] best score of each 256-SID block
+    float *bmax;                // [groups][UG][ceil(n / 256)] best score of each 256-SID block
     float *lse_part;            // [groups][kScanWGs][UG][2] (max, sum of exp) per scan workgroup
     int32_t *out_leaf;          // [U][K]
     int32_t *out_item;          // [U][K] or null
@@ -49,7 +56,7 @@ struct ScoreLayout {
 };
 ScoreLayout score_layout(int L, int64_t n, int max_users);
 
-// ev: null, or 4 events recorded before the table, scan and select kernels and after
+// ev: null, or 3 events recorded before the scan kernel, before the select kernel and after
 hipError_t launch_score(const ScoreDev &a, hipStream_t s, const hipEvent_t *ev);
 
 }  // namespace tcb
