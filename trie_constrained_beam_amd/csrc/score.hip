@@ -61,6 +61,15 @@ __device__ __forceinline__ float dpp_f(float v) {
                                                                  0xF, false));
 }
 
+// maximum over a row of 16 lanes, left in every lane of the row
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));     // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_f<0x4E>(v));     // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_f<0x141>(v));    // row_half_mirror
+    v = fmaxf(v, dpp_f<0x140>(v));    // row_mirror
+    return v;
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // (m, s) represents sum exp(x - m) = s over a set of scores; merging two sets is
@@ -243,6 +252,7 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
     constexpr int TPB = kScoreBlock / kScoreGroup;    // tiles (groups) per block
     constexpr int PD = KS == 0 ? 8 : (KS <= 2 ? 4 : 2);   // tiles of loads in flight per wave
     static_assert(TPB % PD == 0, "whole rounds of the load pipeline per block");
+    static_assert(TPB % 4 == 0, "a block's group maxima are stored 4 at a time");
     __shared__ f32x4 tbl4[kScoreTableFloats / 4];
     __shared__ float2 part[kScanWaves][32];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -250,7 +260,7 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
     constexpr int LP = WIDE ? 8 : 4;                  // levels, padded
     constexpr int ST = WIDE ? kScoreStrideWide : kScoreStrideNarrow;
     const int grp = blockIdx.y;
-    const int n = (int)a.n, NG = (n + kScoreGroup - 1) / kScoreGroup, NB = (n + kScoreBlock - 1) / kScoreBlock;
+    const int n = (int)a.n, NB = (n + kScoreBlock - 1) / kScoreBlock;
     float *tbl = reinterpret_cast<float *>(tbl4);
     load_tables<UG, LP, ST>(a, grp, tbl, blockIdx.x == 0);
     u32x4 av[NH][KA];
@@ -272,7 +282,7 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
     }
     __syncthreads();
     const float w = a.w;
-    float *gmax = a.gmax + (size_t)grp * NG * UG;
+    float *gmax = a.gmax + (size_t)grp * NB * UG * (kScoreBlock / kScoreGroup);
     // after the transposed reduction lane j holds register ru of its row's users
     const int ru = reduced_reg<NR>(j);
     const int wr = 16 * (ru >> 2) + 4 * g + (ru & 3);        // ... i.e. this user row of the group
@@ -293,21 +303,23 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
         cw[slot] = load_codes<WIDE>(a.codes, leaf);
         if constexpr (KS > 0) load_rows<KS>(a.emb, leaf, true, g, bv[slot], true);
     };
-    float bm = kNegInf;
 #pragma unroll
     for (int q = 0; q < PD - 1; ++q) load_tile(q, q);
+    // one block (16 tiles) per round, unrolled, so that a lane keeps its user's 16 group
+    // maxima in registers and stores them as 64 contiguous bytes at the block end
 #pragma unroll 1
-    for (int q0 = 0; q0 < ntile; q0 += PD) {
+    for (int q0 = 0; q0 < ntile; q0 += TPB) {
+        float gv[TPB];
 #pragma unroll
-        for (int q = 0; q < PD; ++q) {
+        for (int q = 0; q < TPB; ++q) {
             load_tile(q0 + q + PD - 1, (q + PD - 1) % PD);
             const int f = tile_first(q0 + q);
             float s[NR];
-            token_sums<NR, LP, ST>(tbl, cw[q], f + j < n, g, s);
+            token_sums<NR, LP, ST>(tbl, cw[q % PD], f + j < n, g, s);
             if constexpr (KS > 0) {
 #pragma unroll
                 for (int hh = 0; hh < NH; ++hh) {
-                    const f32x4 acc = sim_tile<KS>(av[hh], bv[q]);
+                    const f32x4 acc = sim_tile<KS>(av[hh], bv[q % PD]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) s[4 * hh + e] = fmaf(w, acc[e], s[4 * hh + e]);
                 }
@@ -331,14 +343,18 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
 #pragma unroll
                 for (int r = 0; r < NR; ++r) ls[r] += exp2_fast(t[r]);
             }
-            const float v = transposed_max<NR>(s, j);
-            const int gid = f / kScoreGroup;
-            if (writer && gid < NG) gmax[gid * UG + wr] = v;
-            bm = fmaxf(bm, v);
-            if (((q0 + q) % TPB) == TPB - 1) {                // block end
-                if (writer) bmax[f / kScoreBlock] = bm;
-                bm = kNegInf;
-            }
+            gv[q] = transposed_max<NR>(s, j);
+        }
+        // block end: [block][user][group in block] and the block's maximum per user
+        const int blk = tile_first(q0) / kScoreBlock;
+        float bmx = gv[0];
+#pragma unroll
+        for (int q = 1; q < TPB; ++q) bmx = fmaxf(bmx, gv[q]);
+        if (writer) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(gmax + ((size_t)blk * UG + wr) * TPB);
+#pragma unroll
+            for (int c = 0; c < TPB / 4; ++c) dst[c] = f32x4{gv[4 * c], gv[4 * c + 1], gv[4 * c + 2], gv[4 * c + 3]};
+            bmax[blk] = bmx;
         }
     }
 
@@ -372,47 +388,56 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
 
 // ---------------------------------------------------------------------- select
 constexpr int kSelWaves = kSelectThreads / 64;
+constexpr int KPT = kScoreCand / kSelectThreads;      // keys per thread in a selection: 8
+static_assert(KPT * kSelectThreads == kScoreCand, "whole keys per thread");
 
 struct SelSmem {
     uint32_t hist[256];
-    uint32_t wcount[kSelWaves];
+    uint32_t wsum[kSelWaves];
     uint32_t mn[kSelWaves], mx[kSelWaves];
     uint32_t st[4];
 };
 
-// Exclusive count of set flags before this thread, over the workgroup; total in *total.
-__device__ __forceinline__ uint32_t block_count_before(bool f, SelSmem &S, uint32_t &total) {
+// Exclusive prefix sum of one value per thread over the workgroup, in thread order;
+// total in *total.
+__device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, SelSmem &S, uint32_t &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint64_t b = __ballot(f);
-    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-    if (lane == 0) S.wcount[wave] = (uint32_t)__popcll(b);
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) S.wsum[wave] = incl;
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) {
-        const uint32_t c = S.wcount[w];
+        const uint32_t c = S.wsum[w];
         before += w < wave ? c : 0u;
         tot += c;
     }
     __syncthreads();
     total = tot;
-    return before + below;
+    return before + incl - v;
 }
 
-// Exact top-k of n keys (a larger key is better; equal keys: the lower position first,
-// 1 <= k <= n): writes the chosen positions, ascending, to out[0 .. k). Radix selection
-// of the k-th best key over d = key - (smallest key), 8 bits per pass from the highest
-// bit in which the keys differ (so the first pass spreads them over the bins), then one
-// ordered compaction.
-template <class Key>
-__device__ void select_top(int k, int n, const Key &key, uint32_t *out, SelSmem &S) {
+// Exact top-k of n keys held in registers (thread t holds positions KPT t ... KPT t +
+// KPT - 1; a larger key is better, equal keys: the lower position first; 1 <= k <= n):
+// writes the chosen positions, ascending, to out[0 .. k). Radix selection of the k-th
+// best key over d = key - (smallest key), 8 bits per pass from the highest bit in which
+// the keys differ (so the first pass spreads them over the bins), then one ordered
+// compaction (threads own consecutive positions, so two prefix sums place everything).
+__device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *out, SelSmem &S) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int p0 = tid * KPT;
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int i = tid; i < n; i += kSelectThreads) {
-        const uint32_t kv = key(i);
-        lo = min(lo, kv);
-        hi = max(hi, kv);
-    }
+#pragma unroll
+    for (int e = 0; e < KPT; ++e)
+        if (p0 + e < n) {
+            lo = min(lo, kv[e]);
+            hi = max(hi, kv[e]);
+        }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
@@ -430,16 +455,17 @@ __device__ void select_top(int k, int n, const Key &key, uint32_t *out, SelSmem 
         lo = min(lo, S.mn[w]);
         hi = max(hi, S.mx[w]);
     }
-    __syncthreads();
     uint32_t pref = 0u, rem = (uint32_t)k;
     int remaining = hi > lo ? 32 - __clz((int)(hi - lo)) : 0;   // bits of d still undecided
     while (remaining > 0) {
         const int w = min(8, remaining), shift = remaining - w;
         for (int i = tid; i < 256; i += kSelectThreads) S.hist[i] = 0u;
         __syncthreads();
-        for (int i = tid; i < n; i += kSelectThreads) {
-            const uint32_t d = key(i) - lo;
-            if ((uint32_t)((uint64_t)d >> remaining) == pref) atomicAdd(&S.hist[(d >> shift) & ((1u << w) - 1u)], 1u);
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const uint32_t d = kv[e] - lo;
+            if (p0 + e < n && (uint32_t)((uint64_t)d >> remaining) == pref)
+                atomicAdd(&S.hist[(d >> shift) & ((1u << w) - 1u)], 1u);
         }
         __syncthreads();
         if (tid < 64) {
@@ -476,184 +502,244 @@ __device__ void select_top(int k, int n, const Key &key, uint32_t *out, SelSmem 
         rem -= above;
         pref = (pref << w) | digit;
         remaining = shift;
-        __syncthreads();
     }
     const uint32_t T = lo + pref;     // the k-th best key; take all above it and the first rem equal
-    uint32_t eq_seen = 0u, taken = 0u;
-    for (int base = 0; base < n; base += kSelectThreads) {
-        const int i = base + tid;
-        const uint32_t kv = i < n ? key(i) : 0u;
-        const bool eq = i < n && kv == T, gt = i < n && kv > T;
-        uint32_t eq_tot, take_tot;
-        const uint32_t eq_rank = eq_seen + block_count_before(eq, S, eq_tot);
-        const bool take = gt || (eq && eq_rank < rem);
-        const uint32_t pos = taken + block_count_before(take, S, take_tot);
-        if (take && pos < (uint32_t)k) out[pos] = (uint32_t)i;
-        eq_seen += eq_tot;
-        taken += take_tot;
+    uint32_t n_eq = 0u;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) n_eq += (p0 + e < n && kv[e] == T) ? 1u : 0u;
+    uint32_t tot;
+    uint32_t eq_rank = block_excl_sum(n_eq, S, tot);
+    bool take[KPT];
+    uint32_t n_take = 0u;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const bool valid = p0 + e < n;
+        const bool eq = valid && kv[e] == T;
+        take[e] = (valid && kv[e] > T) || (eq && eq_rank < rem);
+        eq_rank += eq ? 1u : 0u;
+        n_take += take[e] ? 1u : 0u;
     }
+    uint32_t pos = block_excl_sum(n_take, S, tot);
+#pragma unroll
+    for (int e = 0; e < KPT; ++e)
+        if (take[e]) {
+            if (pos < (uint32_t)k) out[pos] = (uint32_t)(p0 + e);
+            ++pos;
+        }
     __syncthreads();
 }
 
-template <bool WIDE, int KS>
-__global__ __launch_bounds__(kSelectThreads) void k_score_select(ScoreDev a) {
+// 1-3: the best K superblocks, then blocks, then groups of one user (one workgroup per
+// user); the chosen group ids, ascending, go to pick[u][0 .. npick[u]).
+template <bool WIDE>
+__global__ __launch_bounds__(kSelectThreads) void k_score_pick(ScoreDev a) {
     constexpr int UG = WIDE ? kScoreUGWide : kScoreUGNarrow;
-    constexpr int KA = KS > 0 ? KS : 1;
     constexpr int MK = TCB_SCORE_MAX_K;
     constexpr int SUB = kScoreBlock / kScoreGroup;       // groups per block = blocks per superblock
-    constexpr int RB = KS >= 8 ? 2 : (KS >= 4 ? 4 : 8);   // groups a wave rescores at once, loads in flight
-    constexpr int LP = WIDE ? 8 : 4;
-    __shared__ float val[kScoreCand];
+    static_assert(SUB % KPT == 0, "a thread's keys stay inside one parent");
     __shared__ float sbm[kScoreCand];
     __shared__ uint32_t listA[MK], listB[MK];
-    __shared__ uint64_t sortk[MK];
     __shared__ SelSmem S;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int j = lane & 15, g = lane >> 4;
-    const int u = blockIdx.x, grp = u / UG, row = u % UG, L = a.L;
-    const int64_t n = a.n, NG = (n + kScoreGroup - 1) / kScoreGroup, NB = (n + kScoreBlock - 1) / kScoreBlock;
-    const int NS = (int)((NB + SUB - 1) / SUB);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int u = blockIdx.x, grp = u / UG, row = u % UG;
+    const int n = (int)a.n, NG = (n + kScoreGroup - 1) / kScoreGroup, NB = (n + kScoreBlock - 1) / kScoreBlock;
+    const int NS = (NB + SUB - 1) / SUB;
     const int K = a.K;
+    const int p0 = tid * KPT;
+    uint32_t kv[KPT];
 
-    // 1. superblock maxima from this user's block maxima (contiguous), then the best K
+    // 1. superblock maxima: coalesced reads of this user's block maxima, a maximum over
+    //    each row of 16 lanes (16 consecutive blocks), then the best K superblocks
     const float *bm = a.bmax + ((size_t)grp * UG + row) * NB;
-    for (int sb = tid; sb < NS; sb += kSelectThreads) {
-        float m = kNegInf;
+    for (int c = 0; c < NB; c += kSelectThreads * 4) {
+        float x[4];
 #pragma unroll
-        for (int t = 0; t < SUB; ++t) {
-            const int64_t b = (int64_t)sb * SUB + t;
-            if (b < NB) m = fmaxf(m, bm[b]);
+        for (int e = 0; e < 4; ++e) {
+            const int b = c + e * kSelectThreads + tid;
+            x[e] = bm[b < NB ? b : NB - 1];
         }
-        sbm[sb] = m;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int b = c + e * kSelectThreads + tid;
+            const float m = row16_max(b < NB ? x[e] : kNegInf);
+            if ((lane & 15) == 0 && b < NB) sbm[b / SUB] = m;
+        }
     }
     __syncthreads();
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) kv[e] = f2ord(p0 + e < NS ? sbm[p0 + e] : kNegInf);
     const int kS = min(K, NS);
-    select_top(kS, NS, [&](int i) { return f2ord(sbm[i]); }, listA, S);
+    select_top(kS, NS, kv, listA, S);
 
     // 2. the best K blocks inside them
     const int nA = SUB * kS;
-    for (int p = tid; p < nA; p += kSelectThreads) {
-        const int64_t b = (int64_t)listA[p / SUB] * SUB + (p % SUB);
-        val[p] = b < NB ? bm[b] : kNegInf;
+    {
+        float x[KPT];
+        const int sb = (int)listA[min(p0 / SUB, kS - 1)];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int b = sb * SUB + (p0 + e) % SUB;
+            x[e] = bm[b < NB ? b : NB - 1];
+        }
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) kv[e] = f2ord(sb * SUB + (p0 + e) % SUB < NB ? x[e] : kNegInf);
     }
-    __syncthreads();
     const int kA = min(K, nA);
-    select_top(kA, nA, [&](int i) { return f2ord(val[i]); }, listB, S);
+    select_top(kA, nA, kv, listB, S);
     for (int q = tid; q < kA; q += kSelectThreads) {
         const uint32_t p = listB[q];
         listB[q] = listA[p / SUB] * (uint32_t)SUB + (p % SUB);
     }
     __syncthreads();
 
-    // 3. the best K groups inside those blocks
-    const float *gm = a.gmax + (size_t)grp * NG * UG + row;
+    // 3. the best K groups inside those blocks: a block's 16 group maxima of one user are
+    //    64 contiguous bytes
+    const float *gm = a.gmax + (size_t)grp * NB * UG * SUB + (size_t)row * SUB;
     const int nB = SUB * kA;
-    for (int p = tid; p < nB; p += kSelectThreads) {
-        const int64_t gi = (int64_t)listB[p / SUB] * SUB + (p % SUB);
-        val[p] = gi < NG ? gm[(size_t)gi * UG] : kNegInf;
+    {
+        const int blk = (int)listB[min(p0 / SUB, kA - 1)];
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(gm + (size_t)blk * UG * SUB + p0 % SUB);
+        const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const float v = e < 4 ? x0[e] : x1[e - 4];
+            kv[e] = f2ord(blk * SUB + (p0 + e) % SUB < NG && p0 + e < nB ? v : kNegInf);
+        }
     }
-    __syncthreads();
     const int kB = min(K, nB);
-    select_top(kB, nB, [&](int i) { return f2ord(val[i]); }, listA, S);
+    select_top(kB, nB, kv, listA, S);
     for (int q = tid; q < kB; q += kSelectThreads) {
         const uint32_t p = listA[q];
-        listA[q] = listB[p / SUB] * (uint32_t)SUB + (p % SUB);
+        a.pick[(size_t)u * MK + q] = (int32_t)(listB[p / SUB] * (uint32_t)SUB + (p % SUB));
     }
-    __syncthreads();
+    if (tid == 0) a.npick[u] = kB;
+}
 
-    // 4. rescore the SIDs of those groups: one 16-SID MFMA tile per group; only the
-    //    16-user half holding this user is multiplied (its result does not depend on the
-    //    other half). A wave takes RB groups at a time, all their loads in flight.
+// 4. rescore the SIDs of the picked groups of one user, spread over kRescoreWGs
+//    workgroups per user: one 16-SID MFMA tile per group; only the 16-user half holding
+//    this user is multiplied (its result does not depend on the other half), and the token
+//    sums add the same table values in the same order as the scan, so every score equals
+//    the scan's bit for bit.
+template <bool WIDE, int KS>
+__global__ __launch_bounds__(kRescoreThreads) void k_score_rescore(ScoreDev a) {
+    constexpr int UG = WIDE ? kScoreUGWide : kScoreUGNarrow;
+    constexpr int KA = KS > 0 ? KS : 1;
+    constexpr int MK = TCB_SCORE_MAX_K;
+    constexpr int LP = WIDE ? 8 : 4;
+    constexpr int NWV = kRescoreThreads / 64;
+    constexpr int RB = KS >= 8 ? 2 : (KS >= 4 ? 4 : 8);   // groups a wave rescores at once
+    __shared__ float tcol[LP * 256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 15, g = lane >> 4;
+    const int u = blockIdx.y, grp = u / UG, row = u % UG, L = a.L;
+    const int n = (int)a.n;
+    const int kB = a.npick[u];
+    const int *pick = a.pick + (size_t)u * MK;
+    float *cand = a.cand + (size_t)u * kScoreCand;
+    for (int i = tid; i < LP * 256; i += kRescoreThreads)
+        tcol[i] = i < L * 256 ? a.table[((size_t)grp * L * 256 + i) * UG + row] : 0.0f;
     const int hh_u = row >> 4, g_u = (row >> 2) & 3, e_u = row & 3;
     u32x4 av[KA];
     if constexpr (KS > 0) {
         const int user = grp * UG + 16 * hh_u + j;
         load_rows<KS>(a.user_vec, user, user < a.U, g, av, false);
     }
-    const float *tg = a.table + (size_t)grp * L * 256 * UG + row;
-    for (int q0 = wave; q0 < kB; q0 += kSelWaves * RB) {
+    __syncthreads();
+    const int step = (int)gridDim.x * NWV;
+    for (int q0 = (int)blockIdx.x * NWV + wave; q0 < kB; q0 += step * RB) {
         CodeWord<WIDE> cw[RB];
         u32x4 bv[RB][KA];
         bool valid[RB];
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-            const int q = q0 + b * kSelWaves;
-            const int64_t leaf = q < kB ? (int64_t)listA[q] * kScoreGroup + j : n;
-            valid[b] = leaf < n;
-            cw[b] = valid[b] ? load_codes<WIDE>(a.codes, leaf) : (CodeWord<WIDE>)0;
-            if constexpr (KS > 0) load_rows<KS>(a.emb, leaf, valid[b], g, bv[b], false);
-        }
-        float s[RB];
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            s[b] = 0.0f;
-            // the scan's order of additions, zero rows past L included
-#pragma unroll
-            for (int d = 0; d < LP; ++d)
-                s[b] += d < L ? tg[(size_t)(d * 256 + (int)((cw[b] >> (8 * d)) & 255u)) * UG] : 0.0f;
+            const int q = q0 + b * step;
+            const int leaf = pick[q < kB ? q : kB - 1] * kScoreGroup + j;
+            valid[b] = q < kB && leaf < n;
+            const int lc = leaf < n ? leaf : n - 1;
+            cw[b] = load_codes<WIDE>(a.codes, lc);
+            if constexpr (KS > 0) load_rows<KS>(a.emb, lc, true, g, bv[b], true);
         }
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-            const int q = q0 + b * kSelWaves;
+            float s = 0.0f;
+#pragma unroll
+            for (int d = 0; d < LP; ++d) s += tcol[d * 256 + (int)((cw[b] >> (8 * d)) & 255u)];
             if constexpr (KS > 0) {
                 const f32x4 acc = sim_tile<KS>(av, bv[b]);
                 // register e_u by two bit selects: a chain of equality tests is lowered to
-                // branches, and a branch taken right after the MFMA was compiled without the
-                // wait states its result needs (wrong values seen on gfx950)
+                // branches, and a branch taken right after the MFMA was compiled without
+                // the wait states its result needs (wrong values seen on gfx950)
                 const float lo = (e_u & 1) ? acc[1] : acc[0], hi = (e_u & 1) ? acc[3] : acc[2];
-                s[b] = fmaf(a.w, (e_u & 2) ? hi : lo, s[b]);
+                s = fmaf(a.w, (e_u & 2) ? hi : lo, s);
             }
-            if (!valid[b]) s[b] = kNegInf;
-            if (q < kB && g == g_u) val[q * kScoreGroup + j] = s[b];
+            const int q = q0 + b * step;
+            if (q < kB && g == g_u) cand[q * kScoreGroup + j] = valid[b] ? s : kNegInf;
         }
     }
-    __syncthreads();
+}
 
-    // 5. the best K SIDs, then sorted by (score desc, SID asc)
+// 5-6. the best K SIDs of one user, placed by rank under (score desc, SID asc), and the
+// log-normaliser of the softmax over every valid SID.
+template <bool WIDE>
+__global__ __launch_bounds__(kSelectThreads) void k_score_final(ScoreDev a) {
+    constexpr int UG = WIDE ? kScoreUGWide : kScoreUGNarrow;
+    constexpr int MK = TCB_SCORE_MAX_K;
+    __shared__ uint32_t listB[MK];
+    __shared__ uint64_t sortk[MK];
+    __shared__ SelSmem S;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int u = blockIdx.x, grp = u / UG, row = u % UG;
+    const int n = (int)a.n;
+    const int K = a.K;
+    const int p0 = tid * KPT;
+    const int kB = a.npick[u];
+    const int *pick = a.pick + (size_t)u * MK;
+    const float *cand = a.cand + (size_t)u * kScoreCand;
     const int nC = kScoreGroup * kB;
-    const int kC = (int)min((int64_t)K, n);
-    select_top(kC, nC, [&](int i) { return f2ord(val[i]); }, listB, S);
-    int P2 = 1;
-    while (P2 < kC) P2 <<= 1;
-    for (int i = tid; i < P2; i += kSelectThreads) {
-        uint64_t key = ~0ull;
-        if (i < kC) {
-            const uint32_t p = listB[i];
-            const uint32_t leaf = listA[p / kScoreGroup] * (uint32_t)kScoreGroup + (p % kScoreGroup);
-            key = ((uint64_t)(~f2ord(val[p])) << 32) | leaf;
-        }
-        sortk[i] = key;
+    const int kC = min(K, n);
+    uint32_t kv[KPT];
+    {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(cand + p0);
+        const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) kv[e] = f2ord(p0 + e < nC ? (e < 4 ? x0[e] : x1[e - 4]) : kNegInf);
+    }
+    select_top(kC, nC, kv, listB, S);
+    for (int i = tid; i < kC; i += kSelectThreads) {
+        const uint32_t p = listB[i];
+        const uint32_t leaf = (uint32_t)pick[p / kScoreGroup] * (uint32_t)kScoreGroup + (p % kScoreGroup);
+        sortk[i] = ((uint64_t)(~f2ord(cand[p])) << 32) | leaf;   // ascending = (score desc, SID asc)
     }
     __syncthreads();
-    for (int size = 2; size <= P2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < P2 / 2; i += kSelectThreads) {
-                const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
-                const bool up = (lo & size) == 0;
-                const uint64_t x = sortk[lo], y = sortk[hi];
-                if ((x > y) == up) {
-                    sortk[lo] = y;
-                    sortk[hi] = x;
-                }
-            }
-            __syncthreads();
-        }
-    }
-    for (int i = tid; i < K; i += kSelectThreads) {
-        int32_t leaf = -1, item = -1;
-        float sc = kNegInf;
+    // rank of each of the kC keys (distinct: they hold the SID) = keys below it; two
+    // threads per key count half each, two keys per LDS read
+    {
+        const int i = tid >> 1, half = tid & 1;
+        uint32_t below = 0u;
         if (i < kC) {
-            const uint64_t key = sortk[i];
-            leaf = (int32_t)(uint32_t)key;
-            sc = ord2f(~(uint32_t)(key >> 32));
-            item = (int64_t)leaf < n ? a.leaf_item[leaf] : -1;
+            const uint64_t me = sortk[i];
+            const int h0 = half ? (kC / 2) & ~1 : 0, h1 = half ? kC : (kC / 2) & ~1;
+            int jj = h0;
+            for (; jj + 8 <= h1; jj += 8) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) below += sortk[jj + t] < me ? 1u : 0u;
+            }
+            for (; jj < h1; ++jj) below += sortk[jj] < me ? 1u : 0u;
         }
-        a.out_leaf[(size_t)u * K + i] = leaf;
-        a.out_score[(size_t)u * K + i] = sc;
-        if (a.out_item) a.out_item[(size_t)u * K + i] = item;
+        below += (uint32_t)__shfl_xor((int)below, 1, 64);
+        if (i < kC && half == 0) {
+            const uint64_t key = sortk[i];
+            const int32_t leaf = (int32_t)(uint32_t)key;
+            a.out_leaf[(size_t)u * K + below] = leaf;
+            a.out_score[(size_t)u * K + below] = ord2f(~(uint32_t)(key >> 32));
+            if (a.out_item) a.out_item[(size_t)u * K + below] = leaf < n ? a.leaf_item[leaf] : -1;
+        }
     }
-
-    // 6. log-normaliser of the softmax over every valid SID: the scan's partials in order
+    for (int i = kC + tid; i < K; i += kSelectThreads) {
+        a.out_leaf[(size_t)u * K + i] = -1;
+        a.out_score[(size_t)u * K + i] = kNegInf;
+        if (a.out_item) a.out_item[(size_t)u * K + i] = -1;
+    }
     if (a.out_lse && wave == 0) {
         const float *pp = a.lse_part + ((size_t)grp * kScanWGs * UG + row) * 2;
         float m = kNegInf, s = 0.0f;
@@ -676,7 +762,9 @@ hipError_t launch_ks(const ScoreDev &a, hipStream_t s, const hipEvent_t *ev) {
     else
         hipLaunchKernelGGL((k_score_scan<WIDE, KS, false>), scan_grid, dim3(kScanThreads), 0, s, a);
     if (ev) (void)hipEventRecord(ev[1], s);
-    hipLaunchKernelGGL((k_score_select<WIDE, KS>), dim3(a.U), dim3(kSelectThreads), 0, s, a);
+    hipLaunchKernelGGL((k_score_pick<WIDE>), dim3(a.U), dim3(kSelectThreads), 0, s, a);
+    hipLaunchKernelGGL((k_score_rescore<WIDE, KS>), dim3(kRescoreWGs, a.U), dim3(kRescoreThreads), 0, s, a);
+    hipLaunchKernelGGL((k_score_final<WIDE>), dim3(a.U), dim3(kSelectThreads), 0, s, a);
     if (ev) (void)hipEventRecord(ev[2], s);
     return hipGetLastError();
 }
@@ -703,9 +791,13 @@ ScoreLayout score_layout(int L, int64_t n, int max_users) {
     ScoreLayout o;
     o.table = 0;
     o.gmax = al(o.table + groups * L * 256 * UG * 4);
-    o.bmax = al(o.gmax + groups * NG * UG * 4);
+    o.bmax = al(o.gmax + groups * NB * UG * (kScoreBlock / kScoreGroup) * 4);
     o.lse = al(o.bmax + groups * NB * UG * 4);
-    o.total = al(o.lse + groups * kScanWGs * UG * 8);
+    o.pick = al(o.lse + groups * kScanWGs * UG * 8);
+    o.npick = al(o.pick + (size_t)max_users * TCB_SCORE_MAX_K * 4);
+    o.cand = al(o.npick + (size_t)max_users * 4);
+    o.total = al(o.cand + (size_t)max_users * kScoreCand * 4);
+    (void)NG;
     return o;
 }
 

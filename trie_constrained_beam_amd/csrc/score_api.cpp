@@ -126,6 +126,9 @@ tcb_status tcb_score_catalog(const tcb_trie *t, int32_t n_users, const float *d_
     a.gmax = reinterpret_cast<float *>(ws + lay.gmax);
     a.bmax = reinterpret_cast<float *>(ws + lay.bmax);
     a.lse_part = reinterpret_cast<float *>(ws + lay.lse);
+    a.pick = reinterpret_cast<int32_t *>(ws + lay.pick);
+    a.npick = reinterpret_cast<int32_t *>(ws + lay.npick);
+    a.cand = reinterpret_cast<float *>(ws + lay.cand);
     a.out_leaf = d_leaf;
     a.out_item = d_item;
     a.out_score = d_score;

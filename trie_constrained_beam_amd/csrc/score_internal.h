@@ -28,6 +28,8 @@ constexpr int kScanWaves = 8;
 constexpr int kScanThreads = kScanWaves * 64;
 constexpr int kScanWGs = 256;                 // one persistent workgroup per CU and user group
 constexpr int kSelectThreads = 1024;
+constexpr int kRescoreThreads = 256;
+constexpr int kRescoreWGs = 16;                // workgroups per user that rescore its picked groups
 constexpr int kScoreCand = kScoreGroup * TCB_SCORE_MAX_K;   // candidates of one selection stage
 
 inline int score_ug(int L) { return L <= 4 ? kScoreUGNarrow : kScoreUGWide; }
@@ -39,9 +41,12 @@ struct ScoreDev {
     float *table;               // [groups][L][256][UG] normalised, user-minor (written by the scan)
     const uint16_t *user_vec;   // [U][D] bf16, or null
     const uint16_t *emb;        // [n][D] bf16 in leaf order, or null
-    float *gmax;                // [groups][ceil(n / 16)][UG] best score of each 16-SID group
+    float *gmax;                // [groups][ceil(n / 256)][UG][16] best score of each 16-SID group
     float *bmax;                // [groups][UG][ceil(n / 256)] best score of each 256-SID block
     float *lse_part;            // [groups][kScanWGs][UG][2] (max, sum of exp) per scan workgroup
+    int32_t *pick;              // [U][TCB_SCORE_MAX_K] group ids chosen for rescoring, ascending
+    int32_t *npick;             // [U] their number
+    float *cand;                // [U][kScoreCand] rescored scores of the picked groups' SIDs
     int32_t *out_leaf;          // [U][K]
     int32_t *out_item;          // [U][K] or null
     float *out_score;           // [U][K]
@@ -52,11 +57,11 @@ struct ScoreDev {
 };
 
 struct ScoreLayout {
-    size_t table = 0, gmax = 0, bmax = 0, lse = 0, total = 0;
+    size_t table = 0, gmax = 0, bmax = 0, lse = 0, pick = 0, npick = 0, cand = 0, total = 0;
 };
 ScoreLayout score_layout(int L, int64_t n, int max_users);
 
-// ev: null, or 3 events recorded before the scan kernel, before the select kernel and after
+// ev: null, or 3 events recorded before the scan kernel, before the selection kernels and after
 hipError_t launch_score(const ScoreDev &a, hipStream_t s, const hipEvent_t *ev);
 
 }  // namespace tcb
