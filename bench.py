@@ -214,7 +214,9 @@ def main_leg(args, wl, cat, dev):
             "dsize": 2 if wl.bf16 else 4, "V": V, "L": L, "R": R, "B": B}
 
 
-def lmhead_leg(args, dev):
+def lmhead_leg(args, dev, read_mode="dense"):
+    """The fused lm_head workload. read_mode "dense": the MFMA head at every level (its
+    roofline); "auto": children-only heads at the low-fanout levels."""
     import numpy as np
     import torch
     from trie_constrained_beam_amd import Beams, Trie, synth
@@ -224,6 +226,7 @@ def lmhead_leg(args, dev):
     widths = list(wl.widths)
     S, R, B, L, H = sum(widths), len(widths), max(widths), wl.L, wl.hidden
     beams = Beams(trie, S, R, B, device=dev)
+    beams.set_read_mode(read_mode)
     weights = np.stack([synth.lmhead_weight(wl.seed, lv, 256, H) for lv in range(L)])
     w_dev = torch.from_numpy(weights.view(np.int16)).to(dev).view(torch.bfloat16)
     host = [synth.hidden_states(wl.seed, t, S, H) for t in range(L)]
@@ -264,18 +267,23 @@ def lmhead_leg(args, dev):
     head_ms, tile_ms, merge_ms, n_timed = beams.timing()
     beams.enable_timing(0)
     rows_x_steps = sum(rows_per_step)
-    flop_per_decode = 2.0 * rows_x_steps * 256 * H
-    head_s = head_ms / 1e3 / n_timed                       # average lm_head launch
-    achieved = flop_per_decode / L / head_s / 1e12
-    log(f"[bench] lm_head leg: rows per step {rows_per_step}; lm_head avg {head_s * 1e6:.2f} us "
-        f"({achieved:.0f} TFLOP/s), tile {tile_ms * 1e3 / n_timed:.2f} us, merge {merge_ms * 1e3 / n_timed:.2f} us")
-    return {"workload": wl.name, "rows_per_step": rows_per_step,
-            "value": rows_x_steps * steps / elapsed, "unit": "beam-rows x steps/s",
-            "ms_per_step": elapsed * 1e3 / steps, "steps": steps,
-            "roofline": {"bound": "mfma", "kernel": "k_lmhead", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
-                         "flop_per_launch": flop_per_decode / L, "avg_launch_us": head_s * 1e6},
-            "tile_avg_us": tile_ms * 1e3 / n_timed, "merge_avg_us": merge_ms * 1e3 / n_timed}
+    head_s = head_ms / 1e3 / n_timed                       # average head launch(es) per step
+    res = {"workload": wl.name, "read_mode": read_mode, "rows_per_step": rows_per_step,
+           "value": rows_x_steps * steps / elapsed, "unit": "beam-rows x steps/s",
+           "ms_per_step": elapsed * 1e3 / steps, "steps": steps, "head_avg_us": head_s * 1e6,
+           "tile_avg_us": tile_ms * 1e3 / n_timed, "merge_avg_us": merge_ms * 1e3 / n_timed}
+    if read_mode == "dense":
+        flop_per_decode = 2.0 * rows_x_steps * 256 * H
+        achieved = flop_per_decode / L / head_s / 1e12
+        res["roofline"] = {"bound": "mfma", "kernel": "k_lmhead", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                           "flop_per_launch": flop_per_decode / L, "avg_launch_us": head_s * 1e6}
+        log(f"[bench] lm_head leg: rows per step {rows_per_step}; lm_head avg {head_s * 1e6:.2f} us "
+            f"({achieved:.0f} TFLOP/s), tile {res['tile_avg_us']:.2f} us, merge {res['merge_avg_us']:.2f} us")
+    else:
+        log(f"[bench] lm_head leg ({read_mode}): {elapsed * 1e3 / steps:.3f} ms per decode, head avg "
+            f"{head_s * 1e6:.2f} us per step")
+    return res
 
 
 def _score_inputs(wl, trie, dev):
@@ -407,7 +415,10 @@ def main():
     traffic = recorded_traffic()
     log(f"[bench] {args.steps} decodes in {m['elapsed'] * 1e3:.1f} ms; tile kernel avg {m['tile_us']:.2f} us "
         f"({achieved:.0f} GB/s), merge kernel avg {m['merge_us']:.2f} us")
-    lm = lmhead_leg(args, dev) if args.lmhead else None
+    lm = None
+    if args.lmhead:
+        lm = lmhead_leg(args, dev, "dense")
+        lm["children_only"] = lmhead_leg(args, dev, "auto")
     sc = None
     if args.score:
         swl = synth.SCORE_WORKLOADS["score_u32_k512_l4_4m_zipf_d64"]

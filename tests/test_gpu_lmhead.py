@@ -26,8 +26,8 @@ def _bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def _run_lmhead(cat, widths, H, seed, check_reqs=None):
-    run = gh.Run(cat, widths)
+def _run_lmhead(cat, widths, H, seed, check_reqs=None, read_mode="auto"):
+    run = gh.Run(cat, widths, read_mode=read_mode)
     L, S = run.L, run.max_slots
     weights = np.stack([synth.lmhead_weight(seed, lv, 256, H) for lv in range(L)])   # [L][256][H]
     w_dev = _bf16_dev(weights)
@@ -96,3 +96,34 @@ def test_lmhead_argument_errors():
         beams.step_lmhead(torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda"), w[:1])
     with pytest.raises(TcbError, match="ARG"):
         beams.step_lmhead(torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda"), w[:, :, :64].contiguous())
+
+
+@pytest.mark.parametrize("mode", ["dense", "gather"])
+def test_lmhead_head_modes_parity(mode):
+    """Dense head at every depth, or children-only pieces at every depth: both against the
+    float64 oracle (the deep levels of this catalog have one or two children per row)."""
+    cat = synth.catalog(40_000, 4, ("uniform",) * 4, [54, 1])
+    _run_lmhead(cat, [256, 70, 9], 1024, 54, read_mode=mode)
+
+
+def test_lmhead_children_only_wide_k_and_tail():
+    """Children-only head with H = 4096 (8 chunks per lane) and rows past a tile boundary."""
+    cat = synth.catalog(25_000, 3, ("zipf",) * 3, [55, 1])
+    _run_lmhead(cat, [300, 5], 4096, 55, read_mode="gather")
+
+
+def test_lmhead_children_only_deterministic():
+    cat = synth.catalog(30_000, 4, ("uniform",) * 4, [56, 1])
+    widths = [128, 64]
+    H = 512
+    weights = _bf16_dev(np.stack([synth.lmhead_weight(56, lv, 256, H) for lv in range(4)]))
+    states = []
+    for _ in range(2):
+        run = gh.Run(cat, widths, read_mode="gather")
+        for t in range(4):
+            run.beams.step_lmhead(_bf16_dev(synth.hidden_states(56, t, run.max_slots, H)), weights)
+        states.append(run.state())
+    for k in ("node", "score", "hist", "rows"):
+        a, b = states[0][k], states[1][k]
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b), k

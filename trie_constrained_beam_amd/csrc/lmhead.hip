@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     const int ql = gt / MT, rt = gt - ql * MT;
     if (ql >= R.n) return;
     const ReqArg ra = R.r[ql];
-    if (!ra.step()) return;
+    if (!ra.step() || ra.sparse_head()) return;
     const int r0 = rt * kGRows;
     if (r0 >= ra.rmax()) return;
     // operand loads are issued for every row the request can have; the live-row count
@@ -135,7 +135,77 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     }
 }
 
+// Children-only lm_head ([FR] Decoding: the dense or CSR-sparse choice, applied to the
+// head's flops). One wave per live row: the row's hidden state is read once into registers
+// (8 bf16 per lane per chunk of 512), its children are walked in ascending code order, and
+// for every 16-byte piece of the logit row (4 codes) that holds a child the 4 dot products
+// over H are summed per lane in fp32 and reduced across the wave in a fixed order. Pieces
+// holding no child are not written: the tile kernel then reads only the pieces that hold a
+// child (the request's gather flag is set with the sparse-head flag).
+constexpr int kSpWaves = 4;
+
+__global__ __launch_bounds__(64 * kSpWaves) void k_lmhead_sparse(TrieDev T, WaveDev W, int rp, StepReqs R,
+                                                               const uint16_t *__restrict__ hidden, int64_t ld, int H,
+                                                               const uint16_t *__restrict__ weight,
+                                                               float *__restrict__ out, int quads) {
+    const int ql = (int)blockIdx.x / quads, quad = (int)blockIdx.x - ql * quads;
+    if (ql >= R.n) return;
+    const ReqArg ra = R.r[ql];
+    if (!ra.step() || !ra.sparse_head()) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = quad * kSpWaves + wave;
+    const int rows = W.rec[rp][R.q0 + ql].rows;
+    if (r >= rows) return;
+    const int base = ra.base(), level = ra.level(), slot = base + r;
+    const uint32_t nd = (uint32_t)W.node[ra.par()][slot];
+    if (nd < T.off[level] || nd >= T.off[level + 1]) return;       // not a node of this depth: the tile kernel flags it
+    const uint32_t cb = T.child_begin[nd], ce = T.child_begin[nd + 1];
+    const int nch = H / 8;                                         // chunks of 8 bf16
+    const u32x4 *hp = reinterpret_cast<const u32x4 *>(hidden + (size_t)slot * (size_t)ld);
+    u32x4 hv[8];                                                   // H <= 4096: up to 8 chunks per lane
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hv[i] = (lane + 64 * i < nch) ? hp[lane + 64 * i] : u32x4{0u, 0u, 0u, 0u};
+    const uint16_t *wl = weight + (size_t)level * 256 * (size_t)H;
+    int last = -1;
+    for (uint32_t k = cb; k < ce; ++k) {
+        const int piece = T.child_code[k] >> 2;
+        if (piece == last) continue;                               // uniform: every lane walks the same list
+        last = piece;
+        float d[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 *wp = reinterpret_cast<const u32x4 *>(wl + (size_t)(4 * piece + c) * (size_t)H);
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (lane + 64 * i < nch) {
+                    const u32x4 wv = wp[lane + 64 * i];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc = fmaf(__uint_as_float(hv[i][q] << 16), __uint_as_float(wv[q] << 16), acc);
+                        acc = fmaf(__uint_as_float(hv[i][q] & 0xffff0000u), __uint_as_float(wv[q] & 0xffff0000u), acc);
+                    }
+                }
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+            d[c] = acc;
+        }
+        if (lane < 4) out[(size_t)slot * 256 + 4 * piece + lane] = lane == 0 ? d[0] : lane == 1 ? d[1] : lane == 2 ? d[2] : d[3];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_lmhead_sparse(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
+                                int64_t ld, int H, const void *weight, float *out, int max_rows, hipStream_t s) {
+    if (R.n <= 0 || max_rows <= 0) return hipSuccess;
+    if (H > 4096) return hipErrorInvalidValue;
+    const int quads = (max_rows + kSpWaves - 1) / kSpWaves;
+    hipLaunchKernelGGL(k_lmhead_sparse, dim3(R.n * quads), dim3(64 * kSpWaves), 0, s, t, w, rp, R,
+                       static_cast<const uint16_t *>(hidden), ld, H, static_cast<const uint16_t *>(weight), out, quads);
+    return hipGetLastError();
+}
 
 hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
                          int64_t ld, int H, const void *weight, float *out, hipStream_t s) {

@@ -254,6 +254,9 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
             const double sectors = k == 0 ? 16.0 : 8.0;
             if (1.0 - std::pow(1.0 - 1.0 / sectors, fan) < 0.5) b->gather_levels[k] |= 1u << d;
         }
+        // children-only lm_head where the pieces (4 codes) holding a child are expected to
+        // cover at most a quarter of the row, i.e. a quarter of the dense head's flops
+        if (4.0 * 64.0 * (1.0 - std::pow(1.0 - 1.0 / 64.0, fan)) <= 64.0) b->sparse_head_levels |= 1u << d;
     }
     const uint8_t *img = (const uint8_t *)t->d_image;
     b->tdev.child_begin = (const uint32_t *)(img + t->o_child_begin);
@@ -368,7 +371,7 @@ static void step_done(tcb_beams *b) {
 // kernel through `tile`, then the merge kernel. With timing on, HIP events bracket the
 // three launches separately.
 // The per-request kernel arguments of one step, in launches of up to tcb::kArgReqs ids.
-static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out, int dt_index) {
+static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out, int dt_index, bool head) {
     const int nr = n_req_hw(b);
     out.clear();
     for (int q0 = 0; q0 < nr; q0 += tcb::kArgReqs) {
@@ -391,7 +394,12 @@ static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out, int d
             const bool by_level = b->read_mode == TCB_READ_GATHER || (b->read_mode == TCB_READ_AUTO &&
                                                                       (b->gather_levels[dt_index] >> level & 1u));
             const bool gather = !open && b->w.norm == TCB_NORM_CHILDREN && step && dt_index < 2 && by_level;
-            R.r[i].base_flags = rq.base | (gather ? 1 << 24 : 0);
+            // an lm_head step computes only the children's pieces where rows have few children;
+            // its tile kernel then reads only those pieces
+            const bool sparse = head && !open && b->w.norm == TCB_NORM_CHILDREN && step &&
+                                (b->read_mode == TCB_READ_GATHER ||
+                                 (b->read_mode == TCB_READ_AUTO && (b->sparse_head_levels >> level & 1u)));
+            R.r[i].base_flags = rq.base | (gather || sparse ? 1 << 24 : 0) | (sparse ? 1 << 25 : 0);
             R.r[i].bits = width | rmax << 13 | level << 26 | pre << 29 | (step ? 1u : 0u) << 30 | (level & 1u) << 31;
         }
     }
@@ -406,9 +414,9 @@ static int gather_index(const void *logits, int64_t ld, int32_t dtype, int V) {
 
 template <class HeadLaunch, class TileLaunch>
 static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLaunch tile, int dt_index,
-                           double temperature = 0.0, uint64_t seed = 0) {
+                           double temperature = 0.0, uint64_t seed = 0, bool sparse_head = false) {
     static thread_local std::vector<tcb::StepReqs> args;
-    step_args(b, args, dt_index);
+    step_args(b, args, dt_index, sparse_head);
     for (auto &R : args) {
         R.inv_temp_d = temperature > 0.0 ? 1.0 / temperature : 0.0;
         R.inv_temp = (float)R.inv_temp_d;
@@ -486,10 +494,22 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
     return run_step(
         b, s,
         [&](const tcb::StepReqs &R) {
-            return tcb::launch_lmhead(b->tdev, b->w, b->rp, R, d_hidden, ld_hidden, H, d_weight, b->w.lmx, s);
+            bool dense = false;
+            int sparse_rows = 0;
+            for (int i = 0; i < R.n; ++i)
+                if (R.r[i].step()) {
+                    if (R.r[i].sparse_head()) sparse_rows = std::max(sparse_rows, R.r[i].rmax());
+                    else dense = true;
+                }
+            hipError_t e = hipSuccess;
+            if (dense) e = tcb::launch_lmhead(b->tdev, b->w, b->rp, R, d_hidden, ld_hidden, H, d_weight, b->w.lmx, s);
+            if (e == hipSuccess && sparse_rows > 0)
+                e = tcb::launch_lmhead_sparse(b->tdev, b->w, b->rp, R, d_hidden, ld_hidden, H, d_weight, b->w.lmx,
+                                              sparse_rows, s);
+            return e;
         },
         [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, b->w.lmx, 256, TCB_F32, false, s); },
-        2);
+        2, 0.0, 0, H <= 4096);
 }
 
 tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, float *d_phi, int32_t *d_parent_slot,

@@ -34,6 +34,7 @@ struct tcb_beams {
     uint32_t prefilter_levels = 0;         // bit d: the tile kernel prefilters rows at depth d
     uint32_t gather_levels[3] = {0, 0, 0}; // bit d: fp32 / bf16 rows at depth d read children's sectors only
     int32_t read_mode = TCB_READ_AUTO;
+    uint32_t sparse_head_levels = 0;       // bit d: the lm_head computes only children's pieces at depth d
     int64_t depth_nodes[TCB_MAX_L + 1] = {};   // trie nodes per depth: a bound on any request's rows
     int rp = 0;                            // which request-record buffer is current
     int64_t steps = 0;

@@ -89,10 +89,11 @@ struct WaveDev {
 // What the host knows of every request it steps, passed by value so a kernel's first
 // loads need no device-side lookup. Only the live-row count stays on the device.
 struct ReqArg {
-    int32_t base_flags;            // first slot (< 2^24) | gather << 24
+    int32_t base_flags;            // first slot (< 2^24) | gather << 24 | sparse head << 25
     uint32_t bits;                 // width | rmax << 13 | level << 26 | pre << 29 | step << 30 | par << 31
     __host__ __device__ int base() const { return base_flags & 0xFFFFFF; }
     __host__ __device__ bool gather() const { return (base_flags >> 24) & 1; }        // children's sectors only
+    __host__ __device__ bool sparse_head() const { return (base_flags >> 25) & 1; }   // lm_head: children's pieces only
     __host__ __device__ int width() const { return (int)(bits & 0x1FFFu); }
     __host__ __device__ int rmax() const { return (int)((bits >> 13) & 0x1FFFu); }   // bound on live rows
     __host__ __device__ int level() const { return (int)((bits >> 26) & 0x7u); }
@@ -136,6 +137,10 @@ hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s);
 // lm_head, the lm_head kernel first writes the logits to WaveDev::lmx.
 hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
                        int64_t ld, int dtype, bool sampled, hipStream_t s);
+// lm_head over only the 16-byte pieces (4 codes) of each row that hold a child, for the
+// requests whose argument carries the sparse-head flag; max_rows bounds their live rows.
+hipError_t launch_lmhead_sparse(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
+                                int64_t ld, int H, const void *weight, float *out, int max_rows, hipStream_t s);
 hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
                          int64_t ld, int H, const void *weight, float *out, hipStream_t s);
 hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, hipStream_t s);
