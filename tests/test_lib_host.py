@@ -113,3 +113,31 @@ def test_wave_errors_before_device_work():
     assert lib.tcb_trie_upload(t.handle, fake, 16, None) == -5
     assert lib.tcb_trie_upload(t.handle, C.c_void_p((1 << 20) + 8), 1 << 30, None) == -5
     assert lib.tcb_beam_step(None, fake, 256, 0, None) == -1
+
+
+@pytest.mark.parametrize("L,per", [(1, 4), (4, 4), (5, 8), (8, 8)])
+def test_score_host_sizes(L, per):
+    """Leaf codes take 4 bytes per distinct SID up to L = 4 and 8 above; the scoring
+    workspace grows with the number of users (one table and maxima set per user group)."""
+    cat = synth.catalog(200 if L == 1 else 3000, L, ("uniform",) * L, [90, L])
+    t = Trie(cat)
+    nb = C.c_size_t()
+    _lib.check(_lib.lib().tcb_trie_codes_bytes(t.handle, C.byref(nb)))
+    assert nb.value == t.n_distinct * per
+    sizes = []
+    for users in (1, 16, 32, 33, 200):
+        _lib.check(_lib.lib().tcb_score_workspace_bytes(t.handle, users, C.byref(nb)))
+        assert nb.value % 256 == 0
+        sizes.append(nb.value)
+    assert sizes == sorted(sizes) and sizes[-1] > sizes[0]
+    with pytest.raises(TcbError, match="ARG"):
+        _lib.check(_lib.lib().tcb_score_workspace_bytes(t.handle, 0, C.byref(nb)))
+
+
+def test_score_requires_uploaded_trie():
+    cat = synth.catalog(500, 3, ("uniform",) * 3, [91, 1])
+    t = Trie(cat)
+    with pytest.raises(TcbError, match="STATE"):
+        _lib.check(_lib.lib().tcb_score_catalog(t.handle, 1, C.c_void_p(16), 0, None, None, 0, 1.0, 4,
+                                                C.c_void_p(16), None, C.c_void_p(16), None,
+                                                C.c_void_p(256), 1 << 20, None))
