@@ -597,8 +597,8 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_pick(ScoreDev a) {
     const float *gm = a.gmax + (size_t)grp * NB * UG * SUB + (size_t)row * SUB;
     const int nB = SUB * kA;
     {
-        const int blk = (int)listB[min(p0 / SUB, kA - 1)];
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(gm + (size_t)blk * UG * SUB + p0 % SUB);
+        const int blk = (int)listB[min(p0 / SUB, kA - 1)];          // may lie past the last block
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(gm + (size_t)min(blk, NB - 1) * UG * SUB + p0 % SUB);
         const f32x4 x0 = src[0], x1 = src[1];
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
