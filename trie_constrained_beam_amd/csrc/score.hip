@@ -392,15 +392,15 @@ constexpr int KPT = kScoreCand / kSelectThreads;      // keys per thread in a se
 static_assert(KPT * kSelectThreads == kScoreCand, "whole keys per thread");
 
 struct SelSmem {
-    uint32_t hist[256];
-    uint32_t wsum[kSelWaves];
+    uint32_t hist[3][256];                  // radix passes rotate through three histograms
+    uint32_t wsum[2][kSelWaves];            // and the prefix sums through two wave-total rows
     uint32_t mn[kSelWaves], mx[kSelWaves];
-    uint32_t st[4];
 };
 
 // Exclusive prefix sum of one value per thread over the workgroup, in thread order;
-// total in *total.
-__device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, SelSmem &S, uint32_t &total) {
+// total in *total. One barrier: callers alternate `buf`, and consecutive uses of the same
+// row are separated by another barrier.
+__device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, SelSmem &S, int buf, uint32_t &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t incl = v;
 #pragma unroll
@@ -408,16 +408,15 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, SelSmem &S, uint3
         const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
         if (lane >= o) incl += y;
     }
-    if (lane == 63) S.wsum[wave] = incl;
+    if (lane == 63) S.wsum[buf][wave] = incl;
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) {
-        const uint32_t c = S.wsum[w];
+        const uint32_t c = S.wsum[buf][w];
         before += w < wave ? c : 0u;
         tot += c;
     }
-    __syncthreads();
     total = tot;
     return before + incl - v;
 }
@@ -428,9 +427,12 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, SelSmem &S, uint3
 // best key over d = key - (smallest key), 8 bits per pass from the highest bit in which
 // the keys differ (so the first pass spreads them over the bins), then one ordered
 // compaction (threads own consecutive positions, so two prefix sums place everything).
+// One barrier per radix pass: every wave finds the digit itself from the shared
+// histogram, and the histograms rotate so that clearing one never races with a read.
 __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *out, SelSmem &S) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p0 = tid * KPT;
+    for (int i = tid; i < 256; i += kSelectThreads) S.hist[0][i] = 0u;
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
     for (int e = 0; e < KPT; ++e)
@@ -457,48 +459,51 @@ __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *ou
     }
     uint32_t pref = 0u, rem = (uint32_t)k;
     int remaining = hi > lo ? 32 - __clz((int)(hi - lo)) : 0;   // bits of d still undecided
-    while (remaining > 0) {
+    for (int pass = 0; remaining > 0; ++pass) {
         const int w = min(8, remaining), shift = remaining - w;
-        for (int i = tid; i < 256; i += kSelectThreads) S.hist[i] = 0u;
-        __syncthreads();
+        uint32_t *H = S.hist[pass % 3];
+        // the next pass's histogram was last read two passes ago, before the previous
+        // pass's barrier; this pass's was cleared before it
+        for (int i = tid; i < 256; i += kSelectThreads) S.hist[(pass + 1) % 3][i] = 0u;
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const uint32_t d = kv[e] - lo;
             if (p0 + e < n && (uint32_t)((uint64_t)d >> remaining) == pref)
-                atomicAdd(&S.hist[(d >> shift) & ((1u << w) - 1u)], 1u);
+                atomicAdd(&H[(d >> shift) & ((1u << w) - 1u)], 1u);
         }
         __syncthreads();
-        if (tid < 64) {
-            // lane l owns digits 255 - 4l ... 252 - 4l: counts from the top digit down
-            uint32_t c[4], sum = 0u;
+        // every wave: lane l owns digits 255 - 4l ... 252 - 4l, counts from the top digit down
+        uint32_t c[4], sum = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            c[e] = H[255 - 4 * lane - e];
+            sum += c[e];
+        }
+        uint32_t incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        const uint32_t excl = incl - sum;
+        uint32_t digit = 0u, above = 0u;
+        if (excl < rem && incl >= rem) {
+            uint32_t cum = excl;
+            bool done = false;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                c[e] = S.hist[255 - 4 * lane - e];
-                sum += c[e];
-            }
-            uint32_t incl = sum;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
-                if (lane >= o) incl += y;
-            }
-            const uint32_t excl = incl - sum;
-            if (excl < rem && incl >= rem) {
-                uint32_t cum = excl;
-                bool done = false;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (!done && cum + c[e] >= rem) {
-                        S.st[0] = (uint32_t)(255 - 4 * lane - e);
-                        S.st[1] = cum;
-                        done = true;
-                    }
-                    if (!done) cum += c[e];
+                if (!done && cum + c[e] >= rem) {
+                    digit = (uint32_t)(255 - 4 * lane - e);
+                    above = cum;
+                    done = true;
                 }
+                if (!done) cum += c[e];
             }
         }
-        __syncthreads();
-        const uint32_t digit = S.st[0], above = S.st[1];
+        const uint64_t hit = __ballot(excl < rem && incl >= rem);
+        const int src = hit ? (int)__builtin_ctzll(hit) : 0;       // exactly one lane holds the digit
+        digit = (uint32_t)__shfl((int)digit, src, 64);
+        above = (uint32_t)__shfl((int)above, src, 64);
         rem -= above;
         pref = (pref << w) | digit;
         remaining = shift;
@@ -508,7 +513,7 @@ __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *ou
 #pragma unroll
     for (int e = 0; e < KPT; ++e) n_eq += (p0 + e < n && kv[e] == T) ? 1u : 0u;
     uint32_t tot;
-    uint32_t eq_rank = block_excl_sum(n_eq, S, tot);
+    uint32_t eq_rank = block_excl_sum(n_eq, S, 0, tot);
     bool take[KPT];
     uint32_t n_take = 0u;
 #pragma unroll
@@ -519,7 +524,7 @@ __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *ou
         eq_rank += eq ? 1u : 0u;
         n_take += take[e] ? 1u : 0u;
     }
-    uint32_t pos = block_excl_sum(n_take, S, tot);
+    uint32_t pos = block_excl_sum(n_take, S, 1, tot);
 #pragma unroll
     for (int e = 0; e < KPT; ++e)
         if (take[e]) {
@@ -529,8 +534,6 @@ __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *ou
     __syncthreads();
 }
 
-// 1-3: the best K superblocks, then blocks, then groups of one user (one workgroup per
-// user); the chosen group ids, ascending, go to pick[u][0 .. npick[u]).
 template <bool WIDE>
 __global__ __launch_bounds__(kSelectThreads) void k_score_pick(ScoreDev a) {
     constexpr int UG = WIDE ? kScoreUGWide : kScoreUGNarrow;
@@ -551,15 +554,15 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_pick(ScoreDev a) {
     // 1. superblock maxima: coalesced reads of this user's block maxima, a maximum over
     //    each row of 16 lanes (16 consecutive blocks), then the best K superblocks
     const float *bm = a.bmax + ((size_t)grp * UG + row) * NB;
-    for (int c = 0; c < NB; c += kSelectThreads * 4) {
-        float x[4];
+    for (int c = 0; c < NB; c += kSelectThreads * 16) {          // 16 loads in flight per thread
+        float x[16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 16; ++e) {
             const int b = c + e * kSelectThreads + tid;
             x[e] = bm[b < NB ? b : NB - 1];
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 16; ++e) {
             const int b = c + e * kSelectThreads + tid;
             const float m = row16_max(b < NB ? x[e] : kNegInf);
             if ((lane & 15) == 0 && b < NB) sbm[b / SUB] = m;
@@ -742,8 +745,16 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_final(ScoreDev a) {
     }
     if (a.out_lse && wave == 0) {
         const float *pp = a.lse_part + ((size_t)grp * kScanWGs * UG + row) * 2;
+        static_assert(kScanWGs % 64 == 0, "whole partials per lane");
+        float pm[kScanWGs / 64], ps[kScanWGs / 64];
+#pragma unroll
+        for (int i = 0; i < kScanWGs / 64; ++i) {                 // all loads first, then the merges
+            pm[i] = pp[(size_t)(lane + 64 * i) * UG * 2];
+            ps[i] = pp[(size_t)(lane + 64 * i) * UG * 2 + 1];
+        }
         float m = kNegInf, s = 0.0f;
-        for (int b = lane; b < kScanWGs; b += 64) lse_merge(m, s, pp[(size_t)b * UG * 2], pp[(size_t)b * UG * 2 + 1]);
+#pragma unroll
+        for (int i = 0; i < kScanWGs / 64; ++i) lse_merge(m, s, pm[i], ps[i]);
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
