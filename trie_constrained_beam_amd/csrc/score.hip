@@ -397,17 +397,34 @@ struct SelSmem {
     uint32_t mn[kSelWaves], mx[kSelWaves];
 };
 
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {    // lanes with no source, or in masked rows: 0
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
+}
+
+// inclusive prefix sum over the 64 lanes of a wave, in lane order, by DPP: shifts within
+// each row of 16 lanes, then the last lane of row 0 and 2 added to rows 1 and 3, and the
+// last lane of row 1 to rows 2 and 3
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+    x += dpp_u<0x111>(x);            // row_shr:1
+    x += dpp_u<0x112>(x);            // row_shr:2
+    x += dpp_u<0x114>(x);            // row_shr:4
+    x += dpp_u<0x118>(x);            // row_shr:8
+    x += dpp_u<0x142, 0xA>(x);       // row_bcast:15
+    x += dpp_u<0x143, 0xC>(x);       // row_bcast:31
+    return x;
+}
+
+__device__ __forceinline__ uint32_t lane_u(uint32_t v, int l) {   // l wave-uniform
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
 // Exclusive prefix sum of one value per thread over the workgroup, in thread order;
 // total in *total. One barrier: callers alternate `buf`, and consecutive uses of the same
 // row are separated by another barrier.
 __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, SelSmem &S, int buf, uint32_t &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
-        if (lane >= o) incl += y;
-    }
+    const uint32_t incl = wave_incl_sum(v);
     if (lane == 63) S.wsum[buf][wave] = incl;
     __syncthreads();
     uint32_t before = 0, tot = 0;
@@ -440,11 +457,18 @@ __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *ou
             lo = min(lo, kv[e]);
             hi = max(hi, kv[e]);
         }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
-        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
-    }
+    // within each row of 16 lanes (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
+    // row_mirror: every lane ends with its row's extremes), then over the four rows
+    lo = min(lo, dpp_u<0xB1>(lo));
+    hi = max(hi, dpp_u<0xB1>(hi));
+    lo = min(lo, dpp_u<0x4E>(lo));
+    hi = max(hi, dpp_u<0x4E>(hi));
+    lo = min(lo, dpp_u<0x141>(lo));
+    hi = max(hi, dpp_u<0x141>(hi));
+    lo = min(lo, dpp_u<0x140>(lo));
+    hi = max(hi, dpp_u<0x140>(hi));
+    lo = min(min(lane_u(lo, 0), lane_u(lo, 16)), min(lane_u(lo, 32), lane_u(lo, 48)));
+    hi = max(max(lane_u(hi, 0), lane_u(hi, 16)), max(lane_u(hi, 32), lane_u(hi, 48)));
     if (lane == 0) {
         S.mn[wave] = lo;
         S.mx[wave] = hi;
@@ -479,12 +503,7 @@ __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *ou
             c[e] = H[255 - 4 * lane - e];
             sum += c[e];
         }
-        uint32_t incl = sum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
-            if (lane >= o) incl += y;
-        }
+        const uint32_t incl = wave_incl_sum(sum);
         const uint32_t excl = incl - sum;
         uint32_t digit = 0u, above = 0u;
         if (excl < rem && incl >= rem) {
@@ -502,8 +521,8 @@ __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *ou
         }
         const uint64_t hit = __ballot(excl < rem && incl >= rem);
         const int src = hit ? (int)__builtin_ctzll(hit) : 0;       // exactly one lane holds the digit
-        digit = (uint32_t)__shfl((int)digit, src, 64);
-        above = (uint32_t)__shfl((int)above, src, 64);
+        digit = lane_u(digit, src);
+        above = lane_u(above, src);
         rem -= above;
         pref = (pref << w) | digit;
         remaining = shift;
@@ -689,6 +708,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_final(ScoreDev a) {
     constexpr int MK = TCB_SCORE_MAX_K;
     __shared__ uint32_t listB[MK];
     __shared__ uint64_t sortk[MK];
+    __shared__ uint32_t rank_hi[MK];
     __shared__ SelSmem S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int u = blockIdx.x, grp = u / UG, row = u % UG;
@@ -714,23 +734,27 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_final(ScoreDev a) {
         sortk[i] = ((uint64_t)(~f2ord(cand[p])) << 32) | leaf;   // ascending = (score desc, SID asc)
     }
     __syncthreads();
-    // rank of each of the kC keys (distinct: they hold the SID) = keys below it; two
-    // threads per key count half each, two keys per LDS read
+    // rank of each of the kC keys (distinct: they hold the SID) = keys below it. Waves w and
+    // w + 8 hold keys 64 (w mod 8) + lane and count the keys below them in alternate 64-key
+    // chunks of the list; a chunk is read once, one key per lane, and broadcast lane by lane
+    // from registers, so a comparison costs no LDS traffic.
     {
-        const int i = tid >> 1, half = tid & 1;
+        const int i = (wave & 7) * 64 + lane, half = wave >> 3;
         uint32_t below = 0u;
-        if (i < kC) {
-            const uint64_t me = sortk[i];
-            const int h0 = half ? (kC / 2) & ~1 : 0, h1 = half ? kC : (kC / 2) & ~1;
-            int jj = h0;
-            for (; jj + 8 <= h1; jj += 8) {
+        if ((wave & 7) * 64 < kC) {
+            const uint64_t me = i < kC ? sortk[i] : ~0ull;
+            for (int c = half; c * 64 < kC; c += 2) {
+                const uint64_t other = c * 64 + lane < kC ? sortk[c * 64 + lane] : ~0ull;
+                const uint32_t olo = (uint32_t)other, ohi = (uint32_t)(other >> 32);
 #pragma unroll
-                for (int t = 0; t < 8; ++t) below += sortk[jj + t] < me ? 1u : 0u;
+                for (int t = 0; t < 64; ++t)
+                    below += (((uint64_t)lane_u(ohi, t) << 32) | lane_u(olo, t)) < me ? 1u : 0u;
             }
-            for (; jj < h1; ++jj) below += sortk[jj] < me ? 1u : 0u;
+            if (half) rank_hi[i] = below;
         }
-        below += (uint32_t)__shfl_xor((int)below, 1, 64);
-        if (i < kC && half == 0) {
+        __syncthreads();
+        if (!half && i < kC) {
+            below += rank_hi[i];
             const uint64_t key = sortk[i];
             const int32_t leaf = (int32_t)(uint32_t)key;
             a.out_leaf[(size_t)u * K + below] = leaf;
