@@ -7,7 +7,7 @@
 // kept, and the softmax runs over the valid SIDs only:
 //   score(u, s) = sum_d T_u[d][c_d(s)] + w <v_u, e_s>,   lse(u) = log sum_s exp score(u, s)
 //
-// Two kernels:
+// Four kernels:
 //   k_score_scan    one persistent 512-thread workgroup per CU and group of users (32 at
 //                   L <= 4). The group's tables, normalised per position when they hold
 //                   raw logits, sit in LDS user-minor ([depth][code][user], so a 16-byte
@@ -18,17 +18,19 @@
 //                   SID codes and embeddings read once with nontemporal loads. It writes
 //                   the best score of every group and of every block per user, and
 //                   per-workgroup (max, sum of exp) partials of the log-normaliser.
-//   k_score_select  one workgroup per user. Ranking is (score desc, SID asc) and groups,
+//   k_score_pick    one workgroup per user. Ranking is (score desc, SID asc) and groups,
 //                   blocks and superblocks (16 blocks) are runs of consecutive SIDs, so the
 //                   best K SIDs lie in the best K groups (ranked by their best score, then
 //                   by position), those in the best K blocks, and those in the best K
 //                   superblocks: if K groups ranked above a SID's group, each would hold a
-//                   SID ranked above it. The kernel takes the exact top K of the
-//                   superblocks, then of the blocks and groups inside them, rescores the SIDs of the
-//                   chosen groups with the very same arithmetic as the scan (same operands,
-//                   same MFMA, same order of additions), takes their exact top K and sorts
-//                   it. Every top-K is a radix selection on order-preserving keys with ties
-//                   taken in ascending position, so the result is deterministic.
+//                   SID ranked above it. It takes the exact top K of the superblocks, then
+//                   of the blocks and of the groups inside them.
+//   k_score_rescore rescores the SIDs of the chosen groups with the very same arithmetic as
+//                   the scan (same operands, same MFMA, same order of additions).
+//   k_score_final   one workgroup per user: the exact top K of the rescored SIDs, sorted,
+//                   and the log-normaliser from the scan's partials.
+// Every top-K is a radix selection on order-preserving keys with ties taken in ascending
+// position, so the result is deterministic.
 #include <type_traits>
 
 #include "score_internal.h"
@@ -390,10 +392,11 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
 constexpr int kSelWaves = kSelectThreads / 64;
 constexpr int KPT = kScoreCand / kSelectThreads;      // keys per thread in a selection: 8
 static_assert(KPT * kSelectThreads == kScoreCand, "whole keys per thread");
+static_assert(kScoreCand < 65536, "16-bit halves in the compaction's prefix sum");
 
 struct SelSmem {
     uint32_t hist[3][256];                  // radix passes rotate through three histograms
-    uint32_t wsum[2][kSelWaves];            // and the prefix sums through two wave-total rows
+    uint32_t wsum[2][kSelWaves];            // and prefix sums through two wave-total rows
     uint32_t mn[kSelWaves], mx[kSelWaves];
 };
 
@@ -417,6 +420,54 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
 
 __device__ __forceinline__ uint32_t lane_u(uint32_t v, int l) {   // l wave-uniform
     return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// the value lane (lane ^ J) holds: DPP inside rows of 16 lanes (J = 1, 2, 4, 8), a swizzle
+// inside halves of 32 (J = 16), a permute (J = 32)
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+    if constexpr (J == 1) {
+        return dpp_u<0xB1>(v);                                  // quad_perm [1,0,3,2]
+    } else if constexpr (J == 2) {
+        return dpp_u<0x4E>(v);                                  // quad_perm [2,3,0,1]
+    } else if constexpr (J == 4) {
+        const uint32_t from_above = dpp_u<0x104>(v), from_below = dpp_u<0x114>(v);   // row_shl:4, row_shr:4
+        return (threadIdx.x & 4) ? from_below : from_above;
+    } else if constexpr (J == 8) {
+        return dpp_u<0x128>(v);                                 // row_ror:8
+    } else if constexpr (J == 16) {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);   // bitmask mode, xor 16
+    } else {
+        static_assert(J == 32, "lane distance");
+        return (uint32_t)__shfl_xor((int)v, 32, 64);
+    }
+}
+
+// one compare-exchange step of a bitonic sorting network over the wave's 64 lanes: blocks
+// of K lanes are ordered ascending where (lane & K) == 0, descending elsewhere; partners
+// are J apart
+template <int K, int J>
+__device__ __forceinline__ void bitonic_step(uint64_t &x) {
+    const uint32_t lo = xor_lane<J>((uint32_t)x), hi = xor_lane<J>((uint32_t)(x >> 32));
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    const int lane = threadIdx.x & 63;
+    const bool keep_min = ((lane & J) == 0) == ((lane & K) == 0);
+    x = keep_min ? (y < x ? y : x) : (y < x ? x : y);
+}
+template <int K, int J>
+__device__ __forceinline__ void bitonic_merge(uint64_t &x) {
+    bitonic_step<K, J>(x);
+    if constexpr (J > 1) bitonic_merge<K, J / 2>(x);
+}
+template <int K>
+__device__ __forceinline__ void bitonic_sort(uint64_t &x) {
+    if constexpr (K > 2) bitonic_sort<K / 2>(x);
+    bitonic_merge<K, K / 2>(x);
+}
+// the wave's 64 keys (one per lane), sorted ascending across the lanes
+__device__ __forceinline__ uint64_t wave_sort(uint64_t x) {
+    bitonic_sort<64>(x);
+    return x;
 }
 
 // Exclusive prefix sum of one value per thread over the workgroup, in thread order;
@@ -528,28 +579,30 @@ __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *ou
         remaining = shift;
     }
     const uint32_t T = lo + pref;     // the k-th best key; take all above it and the first rem equal
-    uint32_t n_eq = 0u;
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) n_eq += (p0 + e < n && kv[e] == T) ? 1u : 0u;
-    uint32_t tot;
-    uint32_t eq_rank = block_excl_sum(n_eq, S, 0, tot);
-    bool take[KPT];
-    uint32_t n_take = 0u;
+    // one prefix sum of (keys above T) | (keys equal to T) << 16 (n <= 8192 keeps the
+    // halves apart): a taken key's place is the keys above T before it plus the taken
+    // equal keys before it, min(equal keys before it, rem)
+    uint32_t n_gt = 0u, n_eq = 0u;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
         const bool valid = p0 + e < n;
-        const bool eq = valid && kv[e] == T;
-        take[e] = (valid && kv[e] > T) || (eq && eq_rank < rem);
-        eq_rank += eq ? 1u : 0u;
-        n_take += take[e] ? 1u : 0u;
+        n_gt += (valid && kv[e] > T) ? 1u : 0u;
+        n_eq += (valid && kv[e] == T) ? 1u : 0u;
     }
-    uint32_t pos = block_excl_sum(n_take, S, 1, tot);
+    uint32_t tot;
+    const uint32_t before = block_excl_sum(n_gt | (n_eq << 16), S, 0, tot);
+    uint32_t gt_before = before & 0xFFFFu, eq_before = before >> 16;
 #pragma unroll
-    for (int e = 0; e < KPT; ++e)
-        if (take[e]) {
+    for (int e = 0; e < KPT; ++e) {
+        const bool valid = p0 + e < n;
+        const bool gt = valid && kv[e] > T, eq = valid && kv[e] == T;
+        if (gt || (eq && eq_before < rem)) {
+            const uint32_t pos = gt_before + min(eq_before, rem);
             if (pos < (uint32_t)k) out[pos] = (uint32_t)(p0 + e);
-            ++pos;
         }
+        gt_before += gt ? 1u : 0u;
+        eq_before += eq ? 1u : 0u;
+    }
     __syncthreads();
 }
 
@@ -708,7 +761,6 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_final(ScoreDev a) {
     constexpr int MK = TCB_SCORE_MAX_K;
     __shared__ uint32_t listB[MK];
     __shared__ uint64_t sortk[MK];
-    __shared__ uint32_t rank_hi[MK];
     __shared__ SelSmem S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int u = blockIdx.x, grp = u / UG, row = u % UG;
@@ -734,32 +786,39 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_final(ScoreDev a) {
         sortk[i] = ((uint64_t)(~f2ord(cand[p])) << 32) | leaf;   // ascending = (score desc, SID asc)
     }
     __syncthreads();
-    // rank of each of the kC keys (distinct: they hold the SID) = keys below it. Waves w and
-    // w + 8 hold keys 64 (w mod 8) + lane and count the keys below them in alternate 64-key
-    // chunks of the list; a chunk is read once, one key per lane, and broadcast lane by lane
-    // from registers, so a comparison costs no LDS traffic.
+    // place each of the kC keys (distinct: they hold the SID) by its rank: waves 0 .. 7
+    // sort 64 keys each in registers, and a key's rank is the number of keys below it in
+    // every wave's sorted list (a binary search in LDS per list; in its own list that is
+    // its lane)
     {
-        const int i = (wave & 7) * 64 + lane, half = wave >> 3;
-        uint32_t below = 0u;
-        if ((wave & 7) * 64 < kC) {
-            const uint64_t me = i < kC ? sortk[i] : ~0ull;
-            for (int c = half; c * 64 < kC; c += 2) {
-                const uint64_t other = c * 64 + lane < kC ? sortk[c * 64 + lane] : ~0ull;
-                const uint32_t olo = (uint32_t)other, ohi = (uint32_t)(other >> 32);
-#pragma unroll
-                for (int t = 0; t < 64; ++t)
-                    below += (((uint64_t)lane_u(ohi, t) << 32) | lane_u(olo, t)) < me ? 1u : 0u;
-            }
-            if (half) rank_hi[i] = below;
+        const int nlist = (kC + 63) / 64;
+        uint64_t me = ~0ull;                          // no real key: the SID is below 2^25
+        if (wave < nlist) {
+            const int i = wave * 64 + lane;
+            me = wave_sort(i < kC ? sortk[i] : ~0ull);
+            sortk[i] = me;                            // a wave rewrites only the keys it read
         }
         __syncthreads();
-        if (!half && i < kC) {
-            below += rank_hi[i];
-            const uint64_t key = sortk[i];
-            const int32_t leaf = (int32_t)(uint32_t)key;
-            a.out_leaf[(size_t)u * K + below] = leaf;
-            a.out_score[(size_t)u * K + below] = ord2f(~(uint32_t)(key >> 32));
-            if (a.out_item) a.out_item[(size_t)u * K + below] = leaf < n ? a.leaf_item[leaf] : -1;
+        if (wave < nlist) {
+            constexpr int NL = MK / 64;
+            int pos[NL];
+#pragma unroll
+            for (int l = 0; l < NL; ++l) pos[l] = 0;
+#pragma unroll
+            for (int st = 32; st > 0; st >>= 1)
+#pragma unroll
+                for (int l = 0; l < NL; ++l)
+                    if (l < nlist && sortk[l * 64 + pos[l] + st - 1] < me) pos[l] += st;
+            uint32_t rank = 0u;
+#pragma unroll
+            for (int l = 0; l < NL; ++l)
+                if (l < nlist) rank += (uint32_t)pos[l] + (sortk[l * 64 + pos[l]] < me ? 1u : 0u);
+            if (me != ~0ull) {
+                const int32_t leaf = (int32_t)(uint32_t)me;
+                a.out_leaf[(size_t)u * K + rank] = leaf;
+                a.out_score[(size_t)u * K + rank] = ord2f(~(uint32_t)(me >> 32));
+                if (a.out_item) a.out_item[(size_t)u * K + rank] = leaf < n ? a.leaf_item[leaf] : -1;
+            }
         }
     }
     for (int i = kC + tid; i < K; i += kSelectThreads) {
