@@ -198,47 +198,106 @@ __device__ __forceinline__ float transposed_max(const float (&v)[NR], int j) {
 
 
 // ---------------------------------------------------------------------- tables
+// the value lane l holds (l wave-uniform)
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
 // The group's tables into LDS, normalised per position for raw logits (log-softmax over
-// the V codes); codes >= V and users >= U get 0. One wave per (user, depth) row. Every
-// workgroup computes the same values; with `store` it also writes them to the
-// workspace for the selection kernel.
+// the V codes); codes >= V and users >= U get 0. The rows (depth, user) are dealt to the
+// waves in chunks of 16 consecutive users of one depth (chunk k: depth k mod LP, users
+// 16 (k / LP) ...); a wave issues the loads of all its rows at once (lane l holds codes
+// l + 64 e), and after normalising writes, per code, each chunk's 16 values as four 16-byte
+// pieces of the code's user-minor row (lanes of consecutive codes land in distinct LDS
+// banks). Every workgroup computes the same values (the same operations in the same
+// order); with `store` it also writes them to the workspace for the selection kernels.
 template <int UG, int LP, int ST>
 __device__ void load_tables(const ScoreDev &a, int grp, float *tbl, bool store) {
+    constexpr int CPW = UG * LP / 16 / kScanWaves;        // chunks per wave
+    static_assert(CPW >= 1 && CPW * 16 * kScanWaves == UG * LP, "whole chunks per wave");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int L = a.L, V = a.V;
-    float *gout = a.table + (size_t)grp * L * 256 * UG;
-    for (int rw = wave; rw < UG * LP; rw += kScanWaves) {
-        const int row = rw / LP, d = rw % LP, uu = grp * UG + row;
-        const bool user = uu < a.U && d < L;
-        float x[4];
+    float x[CPW][16][4];
+#pragma unroll
+    for (int k = 0; k < CPW; ++k) {
+        const int ch = wave + kScanWaves * k, d = ch % LP, ub = (ch / LP) * 16;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int uu = grp * UG + ub + r;
+            const bool user = uu < a.U && d < L;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = lane + 64 * e;
+                x[k][r][e] = (user && c < V) ? a.table_in[((size_t)uu * L + d) * V + c] : 0.0f;
+            }
+        }
+    }
+    if (a.kind == TCB_TABLE_LOGITS) {
+        // each step runs over all 16 rows of a chunk, so that the rows' chains of cross-lane
+        // reductions overlap; rows past the last user or depth go through the steps (their
+        // values are all 0, so every step stays finite) and keep their zeros
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) {
+            const int ch = wave + kScanWaves * k, d = ch % LP, ub = (ch / LP) * 16;
+            float m[16], sum[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                m[r] = kNegInf;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (lane + 64 * e < V) m[r] = fmaxf(m[r], x[k][r][e]);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m[r] = fmaxf(m[r], dpp_f<0xB1>(m[r]));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m[r] = fmaxf(m[r], dpp_f<0x4E>(m[r]));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m[r] = fmaxf(m[r], dpp_f<0x141>(m[r]));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m[r] = fmaxf(m[r], dpp_f<0x140>(m[r]));
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                m[r] = fmaxf(fmaxf(lane_f(m[r], 0), lane_f(m[r], 16)), fmaxf(lane_f(m[r], 32), lane_f(m[r], 48)));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sum[r] = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (lane + 64 * e < V) sum[r] += exp2_fast((x[k][r][e] - m[r]) * kLog2e);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum[r] += dpp_f<0xB1>(sum[r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum[r] += dpp_f<0x4E>(sum[r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum[r] += dpp_f<0x141>(sum[r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum[r] += dpp_f<0x140>(sum[r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float t = (lane_f(sum[r], 0) + lane_f(sum[r], 16)) + (lane_f(sum[r], 32) + lane_f(sum[r], 48));
+                const bool live = grp * UG + ub + r < a.U && d < L;
+                const float lse = live ? m[r] + __builtin_amdgcn_logf(t) * kLn2 : 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (lane + 64 * e < V) x[k][r][e] -= lse;
+            }
+        }
+    }
+    f32x4 *t4 = reinterpret_cast<f32x4 *>(tbl);
+    f32x4 *g4 = reinterpret_cast<f32x4 *>(a.table + (size_t)grp * L * 256 * UG);
+#pragma unroll
+    for (int k = 0; k < CPW; ++k) {
+        const int ch = wave + kScanWaves * k, d = ch % LP, ub = (ch / LP) * 16;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int c = lane * 4 + e;
-            x[e] = (user && c < V) ? a.table_in[((size_t)uu * L + d) * V + c] : 0.0f;
-        }
-        if (a.kind == TCB_TABLE_LOGITS && user) {
-            float m = kNegInf;
+            const int c = d * 256 + lane + 64 * e;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (lane * 4 + e < V) m = fmaxf(m, x[e]);
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-            float sum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (lane * 4 + e < V) sum += expf(x[e] - m);
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
-            const float lse = m + logf(sum);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (lane * 4 + e < V) x[e] -= lse;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = d * 256 + lane * 4 + e;
-            tbl[c * ST + row] = x[e];
-            if (store && d < L) gout[(size_t)c * UG + row] = x[e];
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v = {x[k][4 * q][e], x[k][4 * q + 1][e], x[k][4 * q + 2][e], x[k][4 * q + 3][e]};
+                t4[(c * ST + ub) / 4 + q] = v;
+                if (store && d < L) g4[((size_t)c * UG + ub) / 4 + q] = v;
+            }
         }
     }
     for (int i = threadIdx.x; i < ST; i += kScanThreads) tbl[LP * 256 * ST + i] = kPastEnd;
@@ -264,7 +323,8 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
     const int grp = blockIdx.y;
     const int n = (int)a.n, NB = (n + kScoreBlock - 1) / kScoreBlock;
     float *tbl = reinterpret_cast<float *>(tbl4);
-    load_tables<UG, LP, ST>(a, grp, tbl, blockIdx.x == 0);
+    // the user vectors and the first tiles' loads do not depend on the tables: they are
+    // issued first and arrive while the tables are built
     u32x4 av[NH][KA];
     if constexpr (KS > 0) {
 #pragma unroll
@@ -273,6 +333,23 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
             load_rows<KS>(a.user_vec, user, user < a.U, g, av[hh], false);
         }
     }
+    // this wave's tiles: its blocks first, first + stride, ... taken 16 tiles each, as one
+    // sequence, so loads run PD tiles ahead across block ends; past the end they read the
+    // last SID again (a valid address) and the results are masked
+    const int first = (int)blockIdx.x * kScanWaves + wave, stride = (int)gridDim.x * kScanWaves;
+    const int ntile = first < NB ? ((NB - 1 - first) / stride + 1) * TPB : 0;
+    auto tile_first = [&](int q) { return (first + (q / TPB) * stride) * kScoreBlock + (q % TPB) * kScoreGroup; };
+    CodeWord<WIDE> cw[PD];
+    u32x4 bv[PD][KA];
+    auto load_tile = [&](int q, int slot) {
+        int leaf = tile_first(q) + j;
+        leaf = leaf < n ? leaf : n - 1;
+        cw[slot] = load_codes<WIDE>(a.codes, leaf);
+        if constexpr (KS > 0) load_rows<KS>(a.emb, leaf, true, g, bv[slot], true);
+    };
+#pragma unroll
+    for (int q = 0; q < PD - 1; ++q) load_tile(q, q);
+    load_tables<UG, LP, ST>(a, grp, tbl, blockIdx.x == 0);
     // log-normaliser partials: per lane and register a reference rl (in log2 units) and
     // the sum ls of 2^(x log2 e - rl) over the scores x seen; the reference is the first
     // score, raised (and the sum rescaled) when a score exceeds it by more than 2^64
@@ -291,22 +368,6 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
     const bool writer = j < NR;                                // these lanes hold distinct users
     float *bmax = a.bmax + ((size_t)grp * UG + wr) * NB;
 
-    // this wave's tiles: its blocks first, first + stride, ... taken 16 tiles each, as one
-    // sequence, so loads run PD tiles ahead across block ends; past the end they read the
-    // last SID again (a valid address) and the results are masked
-    const int first = (int)blockIdx.x * kScanWaves + wave, stride = (int)gridDim.x * kScanWaves;
-    const int ntile = first < NB ? ((NB - 1 - first) / stride + 1) * TPB : 0;
-    auto tile_first = [&](int q) { return (first + (q / TPB) * stride) * kScoreBlock + (q % TPB) * kScoreGroup; };
-    CodeWord<WIDE> cw[PD];
-    u32x4 bv[PD][KA];
-    auto load_tile = [&](int q, int slot) {
-        int leaf = tile_first(q) + j;
-        leaf = leaf < n ? leaf : n - 1;
-        cw[slot] = load_codes<WIDE>(a.codes, leaf);
-        if constexpr (KS > 0) load_rows<KS>(a.emb, leaf, true, g, bv[slot], true);
-    };
-#pragma unroll
-    for (int q = 0; q < PD - 1; ++q) load_tile(q, q);
     // one block (16 tiles) per round, unrolled, so that a lane keeps its user's 16 group
     // maxima in registers and stores them as 64 contiguous bytes at the block end
 #pragma unroll 1
@@ -361,17 +422,16 @@ __global__ __launch_bounds__(kScanThreads) void k_score_scan(ScoreDev a) {
     }
 
     if constexpr (LSE) {
-        // the 16 lanes of a DPP row hold the same users: butterfly over them, then the
-        // waves in order
+        // the 16 lanes of a DPP row hold the same users: butterfly over them by DPP (xor 1,
+        // xor 2, row_half_mirror, row_mirror), then the waves in order
         float lm[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             lm[r] = rl[r] * kLn2;                              // back to natural-log units
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) {
-                const float m2 = __shfl_xor(lm[r], o, 64), s2 = __shfl_xor(ls[r], o, 64);
-                lse_merge(lm[r], ls[r], m2, s2);
-            }
+            lse_merge(lm[r], ls[r], dpp_f<0xB1>(lm[r]), dpp_f<0xB1>(ls[r]));
+            lse_merge(lm[r], ls[r], dpp_f<0x4E>(lm[r]), dpp_f<0x4E>(ls[r]));
+            lse_merge(lm[r], ls[r], dpp_f<0x141>(lm[r]), dpp_f<0x141>(ls[r]));
+            lse_merge(lm[r], ls[r], dpp_f<0x140>(lm[r]), dpp_f<0x140>(ls[r]));
         }
         if (j == 0) {
 #pragma unroll
