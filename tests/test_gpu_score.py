@@ -129,6 +129,19 @@ def test_score_fullsize_sampled_users():
          users=[0, 17, 31], trie=trie)
 
 
+def test_score_superblock_path():
+    """More than 16384 blocks of 256 SIDs: the pick goes through superblocks. 16384 * 256 + 1
+    SIDs (every 4-byte code below that count), so the last superblock holds one block of
+    one SID; a SID-level term and a ragged user group."""
+    n = 16384 * 256 + 1
+    i = np.arange(n, dtype=np.uint32)
+    cat = np.stack([(i >> 24) & 255, (i >> 16) & 255, (i >> 8) & 255, i & 255], axis=1).astype(np.uint8)
+    trie = Trie(cat, device="cuda")
+    assert trie.n_distinct == n
+    _run(cat, 256, synth.score_logits(90, 3, 4), "logits", 300,
+         synth.user_vectors(90, 3, 32), synth.sid_embeddings(90, n, 32), 0.8, trie=trie)
+
+
 def test_score_argument_errors():
     cat = synth.catalog(2_000, 3, ("uniform",) * 3, [89, 1])
     trie = Trie(cat, device="cuda")

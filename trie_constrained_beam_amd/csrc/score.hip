@@ -24,7 +24,8 @@
 //                   by position), those in the best K blocks, and those in the best K
 //                   superblocks: if K groups ranked above a SID's group, each would hold a
 //                   SID ranked above it. It takes the exact top K of the superblocks, then
-//                   of the blocks and of the groups inside them.
+//                   of the blocks and of the groups inside them (at most 16384 blocks: the
+//                   top K of all blocks directly).
 //   k_score_rescore rescores the SIDs of the chosen groups with the very same arithmetic as
 //                   the scan (same operands, same MFMA, same order of additions).
 //   k_score_final   one workgroup per user: the exact top K of the rescored SIDs, sorted,
@@ -453,6 +454,8 @@ constexpr int kSelWaves = kSelectThreads / 64;
 constexpr int KPT = kScoreCand / kSelectThreads;      // keys per thread in a selection: 8
 static_assert(KPT * kSelectThreads == kScoreCand, "whole keys per thread");
 static_assert(kScoreCand < 65536, "16-bit halves in the compaction's prefix sum");
+constexpr int kDirectKeys = 16;   // block maxima per thread when the pick skips the superblocks
+static_assert(kSelectThreads * kDirectKeys < 65536, "16-bit halves in the compaction's prefix sum");
 
 struct SelSmem {
     uint32_t hist[3][256];                  // radix passes rotate through three histograms
@@ -549,21 +552,22 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, SelSmem &S, int b
     return before + incl - v;
 }
 
-// Exact top-k of n keys held in registers (thread t holds positions KPT t ... KPT t +
-// KPT - 1; a larger key is better, equal keys: the lower position first; 1 <= k <= n):
+// Exact top-k of n <= 65535 keys held in registers (thread t holds positions NK t ... NK t +
+// NK - 1; a larger key is better, equal keys: the lower position first; 1 <= k <= n):
 // writes the chosen positions, ascending, to out[0 .. k). Radix selection of the k-th
 // best key over d = key - (smallest key), 8 bits per pass from the highest bit in which
 // the keys differ (so the first pass spreads them over the bins), then one ordered
 // compaction (threads own consecutive positions, so two prefix sums place everything).
 // One barrier per radix pass: every wave finds the digit itself from the shared
 // histogram, and the histograms rotate so that clearing one never races with a read.
-__device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *out, SelSmem &S) {
+template <int NK>
+__device__ void select_top(int k, int n, const uint32_t (&kv)[NK], uint32_t *out, SelSmem &S) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int p0 = tid * KPT;
+    const int p0 = tid * NK;
     for (int i = tid; i < 256; i += kSelectThreads) S.hist[0][i] = 0u;
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int e = 0; e < KPT; ++e)
+    for (int e = 0; e < NK; ++e)
         if (p0 + e < n) {
             lo = min(lo, kv[e]);
             hi = max(hi, kv[e]);
@@ -601,7 +605,7 @@ __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *ou
         // pass's barrier; this pass's was cleared before it
         for (int i = tid; i < 256; i += kSelectThreads) S.hist[(pass + 1) % 3][i] = 0u;
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
+        for (int e = 0; e < NK; ++e) {
             const uint32_t d = kv[e] - lo;
             if (p0 + e < n && (uint32_t)((uint64_t)d >> remaining) == pref)
                 atomicAdd(&H[(d >> shift) & ((1u << w) - 1u)], 1u);
@@ -639,12 +643,12 @@ __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *ou
         remaining = shift;
     }
     const uint32_t T = lo + pref;     // the k-th best key; take all above it and the first rem equal
-    // one prefix sum of (keys above T) | (keys equal to T) << 16 (n <= 8192 keeps the
+    // one prefix sum of (keys above T) | (keys equal to T) << 16 (n < 2^16 keeps the
     // halves apart): a taken key's place is the keys above T before it plus the taken
     // equal keys before it, min(equal keys before it, rem)
     uint32_t n_gt = 0u, n_eq = 0u;
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
+    for (int e = 0; e < NK; ++e) {
         const bool valid = p0 + e < n;
         n_gt += (valid && kv[e] > T) ? 1u : 0u;
         n_eq += (valid && kv[e] == T) ? 1u : 0u;
@@ -653,7 +657,7 @@ __device__ void select_top(int k, int n, const uint32_t (&kv)[KPT], uint32_t *ou
     const uint32_t before = block_excl_sum(n_gt | (n_eq << 16), S, 0, tot);
     uint32_t gt_before = before & 0xFFFFu, eq_before = before >> 16;
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
+    for (int e = 0; e < NK; ++e) {
         const bool valid = p0 + e < n;
         const bool gt = valid && kv[e] > T, eq = valid && kv[e] == T;
         if (gt || (eq && eq_before < rem)) {
@@ -683,49 +687,64 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_pick(ScoreDev a) {
     const int p0 = tid * KPT;
     uint32_t kv[KPT];
 
-    // 1. superblock maxima: coalesced reads of this user's block maxima, a maximum over
-    //    each row of 16 lanes (16 consecutive blocks), then the best K superblocks
     const float *bm = a.bmax + ((size_t)grp * UG + row) * NB;
-    for (int c = 0; c < NB; c += kSelectThreads * 16) {          // 16 loads in flight per thread
-        float x[16];
+    int kA;
+    if (NB <= kSelectThreads * kDirectKeys) {
+        // 1-2. few blocks: the best K of all block maxima at once (thread t holds blocks
+        //      kDirectKeys t ...)
+        uint32_t kb[kDirectKeys];
+        const int b0 = tid * kDirectKeys;
+        float x[kDirectKeys];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int b = c + e * kSelectThreads + tid;
-            x[e] = bm[b < NB ? b : NB - 1];
+        for (int e = 0; e < kDirectKeys; ++e) x[e] = bm[b0 + e < NB ? b0 + e : NB - 1];
+#pragma unroll
+        for (int e = 0; e < kDirectKeys; ++e) kb[e] = f2ord(b0 + e < NB ? x[e] : kNegInf);
+        kA = min(K, NB);
+        select_top(kA, NB, kb, listB, S);
+    } else {
+        // 1. superblock maxima: coalesced reads of this user's block maxima, a maximum
+        //    over each row of 16 lanes (16 consecutive blocks), then the best K superblocks
+        for (int c = 0; c < NB; c += kSelectThreads * 16) {          // 16 loads in flight per thread
+            float x[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int b = c + e * kSelectThreads + tid;
+                x[e] = bm[b < NB ? b : NB - 1];
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int b = c + e * kSelectThreads + tid;
+                const float m = row16_max(b < NB ? x[e] : kNegInf);
+                if ((lane & 15) == 0 && b < NB) sbm[b / SUB] = m;
+            }
         }
+        __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int b = c + e * kSelectThreads + tid;
-            const float m = row16_max(b < NB ? x[e] : kNegInf);
-            if ((lane & 15) == 0 && b < NB) sbm[b / SUB] = m;
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) kv[e] = f2ord(p0 + e < NS ? sbm[p0 + e] : kNegInf);
-    const int kS = min(K, NS);
-    select_top(kS, NS, kv, listA, S);
+        for (int e = 0; e < KPT; ++e) kv[e] = f2ord(p0 + e < NS ? sbm[p0 + e] : kNegInf);
+        const int kS = min(K, NS);
+        select_top(kS, NS, kv, listA, S);
 
-    // 2. the best K blocks inside them
-    const int nA = SUB * kS;
-    {
-        float x[KPT];
-        const int sb = (int)listA[min(p0 / SUB, kS - 1)];
+        // 2. the best K blocks inside them
+        const int nA = SUB * kS;
+        {
+            float x[KPT];
+            const int sb = (int)listA[min(p0 / SUB, kS - 1)];
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const int b = sb * SUB + (p0 + e) % SUB;
-            x[e] = bm[b < NB ? b : NB - 1];
+            for (int e = 0; e < KPT; ++e) {
+                const int b = sb * SUB + (p0 + e) % SUB;
+                x[e] = bm[b < NB ? b : NB - 1];
+            }
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) kv[e] = f2ord(sb * SUB + (p0 + e) % SUB < NB ? x[e] : kNegInf);
         }
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) kv[e] = f2ord(sb * SUB + (p0 + e) % SUB < NB ? x[e] : kNegInf);
+        kA = min(K, nA);
+        select_top(kA, nA, kv, listB, S);
+        for (int q = tid; q < kA; q += kSelectThreads) {
+            const uint32_t p = listB[q];
+            listB[q] = listA[p / SUB] * (uint32_t)SUB + (p % SUB);
+        }
+        __syncthreads();
     }
-    const int kA = min(K, nA);
-    select_top(kA, nA, kv, listB, S);
-    for (int q = tid; q < kA; q += kSelectThreads) {
-        const uint32_t p = listB[q];
-        listB[q] = listA[p / SUB] * (uint32_t)SUB + (p % SUB);
-    }
-    __syncthreads();
 
     // 3. the best K groups inside those blocks: a block's 16 group maxima of one user are
     //    64 contiguous bytes
