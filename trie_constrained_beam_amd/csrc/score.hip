@@ -790,29 +790,36 @@ __global__ __launch_bounds__(kRescoreThreads) void k_score_rescore(ScoreDev a) {
     const int kB = a.npick[u];
     const int *pick = a.pick + (size_t)u * MK;
     float *cand = a.cand + (size_t)u * kScoreCand;
+    const int hh_u = row >> 4, g_u = (row >> 2) & 3, e_u = row & 3;
+    const int step = (int)gridDim.x * NWV;
+    CodeWord<WIDE> cw[RB];
+    u32x4 bv[RB][KA];
+    uint32_t leafv[RB];
+    // a round's loads need neither the table nor the count kB: entries of pick past kB
+    // (left from earlier calls) give SIDs that are clamped into the catalog and dropped
+    auto load_round = [&](int q0) {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const int q = q0 + b * step;
+            leafv[b] = (uint32_t)pick[q < MK ? q : MK - 1] * (uint32_t)kScoreGroup + (uint32_t)j;
+            const int lc = leafv[b] < (uint32_t)n ? (int)leafv[b] : n - 1;
+            cw[b] = load_codes<WIDE>(a.codes, lc);
+            if constexpr (KS > 0) load_rows<KS>(a.emb, lc, true, g, bv[b], true);
+        }
+    };
+    // the first round is issued before the table and the count arrive
+    const int qs = (int)blockIdx.x * NWV + wave;
+    load_round(qs);
     for (int i = tid; i < LP * 256; i += kRescoreThreads)
         tcol[i] = i < L * 256 ? a.table[((size_t)grp * L * 256 + i) * UG + row] : 0.0f;
-    const int hh_u = row >> 4, g_u = (row >> 2) & 3, e_u = row & 3;
     u32x4 av[KA];
     if constexpr (KS > 0) {
         const int user = grp * UG + 16 * hh_u + j;
         load_rows<KS>(a.user_vec, user, user < a.U, g, av, false);
     }
     __syncthreads();
-    const int step = (int)gridDim.x * NWV;
-    for (int q0 = (int)blockIdx.x * NWV + wave; q0 < kB; q0 += step * RB) {
-        CodeWord<WIDE> cw[RB];
-        u32x4 bv[RB][KA];
-        bool valid[RB];
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            const int q = q0 + b * step;
-            const int leaf = pick[q < kB ? q : kB - 1] * kScoreGroup + j;
-            valid[b] = q < kB && leaf < n;
-            const int lc = leaf < n ? leaf : n - 1;
-            cw[b] = load_codes<WIDE>(a.codes, lc);
-            if constexpr (KS > 0) load_rows<KS>(a.emb, lc, true, g, bv[b], true);
-        }
+    for (int q0 = qs; q0 < kB; q0 += step * RB) {
+        if (q0 != qs) load_round(q0);
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
             float s = 0.0f;
@@ -827,7 +834,7 @@ __global__ __launch_bounds__(kRescoreThreads) void k_score_rescore(ScoreDev a) {
                 s = fmaf(a.w, (e_u & 2) ? hi : lo, s);
             }
             const int q = q0 + b * step;
-            if (q < kB && g == g_u) cand[q * kScoreGroup + j] = valid[b] ? s : kNegInf;
+            if (q < kB && g == g_u) cand[q * kScoreGroup + j] = leafv[b] < (uint32_t)n ? s : kNegInf;
         }
     }
 }
