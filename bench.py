@@ -151,6 +151,14 @@ def timed(run, steps, warmup):
     return time.perf_counter() - t0
 
 
+def merge_steps(trie, widths, L):
+    """Steps of a decode that launch the merge kernel: a step whose requests all have at
+    most 64 possible rows (one tile; depth-t prefixes of the catalog, at most the beam
+    width) is merged inside the tile kernel."""
+    npd = trie.nodes_per_depth
+    return sum(1 for t in range(L) if max(min(w, 1 if t == 0 else npd[t]) for w in widths) > 64)
+
+
 def main_leg(args, wl, cat, dev):
     import numpy as np
     import torch
@@ -209,8 +217,9 @@ def main_leg(args, wl, cat, dev):
         decode(d % len(pool))
     _, tile_ms, merge_ms, n_timed = beams.timing()
     beams.enable_timing(0)
+    n_merge = n_timed // L * merge_steps(trie, widths, L)    # merge launches among the timed steps
     return {"elapsed": elapsed, "rows_x_steps": rows_x_steps, "rows_per_step": rows_per_step,
-            "tile_us": tile_ms * 1e3 / n_timed, "merge_us": merge_ms * 1e3 / n_timed, "pool": len(pool),
+            "tile_us": tile_ms * 1e3 / n_timed, "merge_us": merge_ms * 1e3 / max(1, n_merge), "pool": len(pool),
             "dsize": 2 if wl.bf16 else 4, "V": V, "L": L, "R": R, "B": B}
 
 
@@ -266,12 +275,13 @@ def lmhead_leg(args, dev, read_mode="dense"):
         decode(d % len(pool))
     head_ms, tile_ms, merge_ms, n_timed = beams.timing()
     beams.enable_timing(0)
+    n_merge = n_timed // L * merge_steps(trie, widths, L)
     rows_x_steps = sum(rows_per_step)
     head_s = head_ms / 1e3 / n_timed                       # average head launch(es) per step
     res = {"workload": wl.name, "read_mode": read_mode, "rows_per_step": rows_per_step,
            "value": rows_x_steps * steps / elapsed, "unit": "beam-rows x steps/s",
            "ms_per_step": elapsed * 1e3 / steps, "steps": steps, "head_avg_us": head_s * 1e6,
-           "tile_avg_us": tile_ms * 1e3 / n_timed, "merge_avg_us": merge_ms * 1e3 / n_timed}
+           "tile_avg_us": tile_ms * 1e3 / n_timed, "merge_avg_us": merge_ms * 1e3 / max(1, n_merge)}
     if read_mode == "dense":
         flop_per_decode = 2.0 * rows_x_steps * 256 * H
         achieved = flop_per_decode / L / head_s / 1e12

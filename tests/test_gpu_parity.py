@@ -34,6 +34,9 @@ CASES = {
     "csr_only": ((60_000, 4, ("zipf",) * 4, [35, 1]), [96, 512], 35, 2.0, False, 0, "children"),
     "mask_all_depths": ((60_000, 4, ("zipf",) * 4, [35, 1]), [96, 512], 35, 2.0, False, 4, "children"),
     "bf16_level": ((40_000, 3, ("uniform", "zipf", "zipf"), [36, 1]), [256, 45], 36, 3.0, True, None, "level"),
+    # every request at most 64 rows: every step merged inside the tile kernel
+    "zipf100k_l4_w64_in_tile": ((100_000, 4, ("zipf",) * 4, [37, 1]), [64, 1, 33, 50, 17, 64, 8], 37, 3.0, True,
+                                None, "children"),
 }
 
 
@@ -199,6 +202,46 @@ def test_determinism_bitwise():
         outs.append(run.beams.finalize(run.ids))
     for k in outs[0]:
         assert np.array_equal(outs[0][k], outs[1][k]), k
+
+
+def test_in_tile_merge_matches_merge_kernel():
+    """Requests of at most 64 rows are merged inside the tile kernel when the whole launch
+    has at most 64 rows per request; one wider request in the launch sends every request
+    through k_merge. The narrow requests' rows, back-pointers and final SIDs must be bitwise
+    the same either way (row-keyed logits give them the same inputs in both runs)."""
+    cat = synth.catalog(100_000, 4, ("zipf",) * 4, [46, 1])
+    narrow = [64, 33, 1, 50]
+    res = []
+    for widths in (narrow, narrow + [300]):
+        run = gh.Run(cat, widths)
+        states = []
+        for t in range(4):
+            x = gh.rowkeyed_logits(46, t, widths, 2.5, False)
+            host = np.zeros((run.max_slots, 256), dtype=np.float32)
+            for xi, base in zip(x, run.bases):
+                host[base:base + xi.shape[0]] = xi
+            run.beams.step(torch.from_numpy(host).cuda())
+            ex = {k: v.cpu().numpy() for k, v in run.beams.export().items()}
+            st = []
+            for i, (rid, base) in enumerate(zip(run.ids[:len(narrow)], run.bases)):
+                k = int(ex["rows"][rid])
+                st.append((k, ex["node"][base:base + k].copy(), ex["score"][base:base + k].view(np.int32).copy(),
+                           ex["hist"][t, base:base + k].copy()))
+            states.append(st)
+        fin = run.beams.finalize(run.ids)
+        res.append((states, {k: v[:len(narrow)] for k, v in fin.items()}))
+    for t in range(4):
+        for i in range(len(narrow)):
+            a, b = res[0][0][t][i], res[1][0][t][i]
+            assert a[0] == b[0], (t, i)
+            for u, v in zip(a[1:], b[1:]):
+                assert np.array_equal(u, v), (t, i)
+    fa, fb = res[0][1], res[1][1]
+    assert np.array_equal(fa["counts"], fb["counts"])
+    for i, c in enumerate(fa["counts"]):
+        for k in fa:
+            if k != "counts":
+                assert np.array_equal(fa[k][i][:int(c)], fb[k][i][:int(c)]), (k, i)
 
 
 def test_finalize_legality_items_and_device_variant():

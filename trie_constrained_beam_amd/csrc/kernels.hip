@@ -385,9 +385,58 @@ struct MergeSmem {
 };
 
 // ---------------------------------------------------------------------- merge
+// New row `rank` of request ra (in the request's other row buffers) and its back-pointer.
+__device__ __forceinline__ void write_new_row(const WaveDev &W, const ReqArg ra, uint32_t rank, float score,
+                                              uint32_t flat, int32_t node, float phi) {
+    if (rank >= (uint32_t)ra.width()) return;         // cannot happen; never write past the request
+    const int slot = ra.base() + (int)rank, np = ra.par() ^ 1;
+    W.node[np][slot] = node;
+    W.score[np][slot] = score;
+    W.phi[np][slot] = phi;
+    W.parent_slot[slot] = ra.base() + (int)(flat >> 8);
+    W.hist[(size_t)ra.level() * W.S + slot] = flat;   // (r << 8) | c
+}
+
+// The request's record for the next step: k rows one level deeper, in the other buffers.
+__device__ __forceinline__ void write_next_record(const WaveDev &W, int q, const ReqArg ra, int rp, uint32_t k) {
+    if (threadIdx.x == 0) {
+        ReqRec nr{};
+        nr.base = ra.base();
+        nr.width = ra.width();
+        nr.rows = (int32_t)k;
+        nr.level = ra.level() + 1;
+        nr.status = kReqActive;
+        nr.par = ra.par() ^ 1;
+        W.rec[rp ^ 1][q] = nr;
+    }
+}
+
+// Entries p < staged of M are grouped by bin (bin b at [G[b - 1], min(G[b], staged)),
+// G[-1] = 0): an entry's rank is the entries of better bins plus the better members of its
+// own bin; ranks below k become the request's new rows.
+__device__ __forceinline__ void rank_staged(const WaveDev &W, const ReqArg ra, const MergeSmem &M,
+                                            const uint32_t *G, uint32_t staged, uint32_t k, float sref) {
+    constexpr int U = kMergeCap / kThreads;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t p = (uint32_t)(threadIdx.x + u * kThreads);
+        if (p < staged) {
+            const float s = M.s[p];
+            const uint32_t o = f2ord(s), f = M.f[p];
+            const uint32_t b = score_bin(sref, s);
+            const uint32_t st = b ? G[b - 1] : 0u, en = min(G[b], staged);
+            uint32_t r = 0u;
+            for (uint32_t qq = st; qq < en; ++qq) r += key_better(f2ord(M.s[qq]), M.f[qq], o, f) ? 1u : 0u;
+            const uint32_t rank = st + r;
+            if (rank < k) write_new_row(W, ra, rank, s, f, M.n[p], M.phi[p]);
+        }
+    }
+}
+
 // One workgroup per request (k_merge). Every tile's kept candidates are in its region
 // of the candidate records grouped by bin, with its cumulative kept counts in tcum.
-__device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, MergeSmem &M, SelSmem &sel) {
+__device__ __forceinline__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, MergeSmem &M,
+                                              SelSmem &sel) {
     const int tid = threadIdx.x;
     const int MT = W.MT, CAPT = W.CAPT;
     const uint16_t *tc = W.tcum + (size_t)q * MT * kBins;
@@ -463,16 +512,6 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
         return reg0 + (size_t)jt * CAPT + (p - M.toff[jt]);
     };
 
-    const int level = ra.level(), np = ra.par() ^ 1, S = W.S, base = ra.base();
-    auto write_row = [&](uint32_t rank, float score, uint32_t flat, int32_t node, float phi) {
-        if (rank >= (uint32_t)ra.width()) return;     // cannot happen; never write past the request
-        const int slot = base + (int)rank;
-        W.node[np][slot] = node;
-        W.score[np][slot] = score;
-        W.phi[np][slot] = phi;
-        W.parent_slot[slot] = base + (int)(flat >> 8);
-        W.hist[(size_t)level * S + slot] = flat;      // (r << 8) | c
-    };
 
     if (staged <= (uint32_t)kMergeCap) {
         // 2. stage bins <= b* grouped by bin (each tile's first tcum_j[b*] entries)
@@ -509,20 +548,7 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
         }
         __syncthreads();
         // 3. rank = members of better bins + better members of the own bin
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t p = (uint32_t)(tid + u * kThreads);
-            if (p < staged) {
-                const float s = M.s[p];
-                const uint32_t o = f2ord(s), f = M.f[p];
-                const uint32_t b = score_bin(sref, s);
-                const uint32_t st = b ? M.G[b - 1] : 0u, en = min(M.G[b], staged);
-                uint32_t r = 0u;
-                for (uint32_t qq = st; qq < en; ++qq) r += key_better(f2ord(M.s[qq]), M.f[qq], o, f) ? 1u : 0u;
-                const uint32_t rank = st + r;
-                if (rank < k) write_row(rank, s, f, M.n[p], M.phi[p]);
-            }
-        }
+        rank_staged(W, ra, M, M.G, staged, k, sref);
     } else {
         // exact path (massive ties around b*): select the k-th key over the tiles'
         // buffers, gather exactly k survivors, rank them by counting
@@ -554,19 +580,10 @@ __device__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, 
             const uint32_t o = f2ord(M.s[p]), f = M.f[p];
             uint32_t r = 0u;
             for (uint32_t qq = 0; qq < n; ++qq) r += key_better(f2ord(M.s[qq]), M.f[qq], o, f) ? 1u : 0u;
-            write_row(r, M.s[p], f, M.n[p], M.phi[p]);
+            write_new_row(W, ra, r, M.s[p], f, M.n[p], M.phi[p]);
         }
     }
-    if (tid == 0) {
-        ReqRec nr{};
-        nr.base = base;
-        nr.width = ra.width();
-        nr.rows = (int32_t)k;
-        nr.level = level + 1;
-        nr.status = kReqActive;
-        nr.par = np;
-        W.rec[rp ^ 1][q] = nr;
-    }
+    write_next_record(W, q, ra, rp, k);
 }
 
 __global__ __launch_bounds__(kThreads) void k_merge(TrieDev T, WaveDev W, int rp, StepReqs R) {
@@ -670,27 +687,27 @@ __device__ __forceinline__ double row16_max_d(double v) {
     return v;
 }
 
-template <int DT, int NORM, bool VEC, bool SAMPLE>
-__global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp, StepReqs R,
-                                                   const void *__restrict__ logits, int64_t ld) {
+// The work of one tile (request ql of the launch, tile `tile`); it returns early where the
+// tile has nothing to do (every return is uniform over the workgroup). With MERGE (the
+// request's only tile) the kept candidates go to LDS and the tile ranks them and writes
+// the request's new rows itself, returning true; it returns false where k_merge's work
+// (from the records in memory) is still to do.
+template <int DT, int NORM, bool VEC, bool SAMPLE, bool MERGE>
+__device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, int rp, const StepReqs &R,
+                                          const void *__restrict__ logits, int64_t ld, int ql, int tile,
+                                          TileSmem &A, SelSmem &sel, MergeSmem *M) {
     constexpr int CH = Lay<DT>::CH, CW = Lay<DT>::CW, SPAN = 256 / CH;
     static_assert(CH * CW == kElems && (SPAN / CW) * 8 <= 256, "row layout");
-    __shared__ TileSmem A;
-    __shared__ SelSmem sel;
 
     const int tid = threadIdx.x;
     const int MT = W.MT;
-    const int i8 = (int)(blockIdx.x >> 3);
-    const int ql = (int)(blockIdx.x & 7u) + 8 * (i8 / MT);  // all tiles of a request on one XCD
-    const int tile = i8 % MT;
-    if (ql >= R.n) return;
     const int q = R.q0 + ql;
     const ReqArg ra = R.r[ql];
     if (!ra.step()) {
         if (tile == 0 && tid == 0) W.rec[rp ^ 1][q] = W.rec[rp][q];   // not stepped: carried over
-        return;
+        return false;
     }
-    if (tile * kTileRows >= ra.rmax()) return;          // past any row the request can have
+    if (tile * kTileRows >= ra.rmax()) return false;          // past any row the request can have
 
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, j = lane & 15;
     const int level = ra.level(), cp = ra.par(), base = ra.base();
@@ -726,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
         if constexpr (SAMPLE) pr = W.phi[cp][slot];
         if (!gather) load_row<DT, VEC>(logits, ld, slot, j, V, x);
     }
-    if (tile * kTileRows >= rows) return;              // a tile with no live row
+    if (tile * kTileRows >= rows) return false;              // a tile with no live row
     const bool live = r < rows;
     const bool wave_live = tile * kTileRows + wave * kRowsPerWave < rows;
 
@@ -984,6 +1001,32 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
             at[e] = 0u;
             if (bn[e] != 0u && bn[e] <= bt) at[e] = A.h2[bn[e] - 1];
         }
+        if constexpr (MERGE) {
+            // the request's only tile: its kept candidates are exactly what k_merge would
+            // stage (A.h2 holds the request's cumulative kept counts, b* = b_t), so they are
+            // staged in LDS, ranked and written here
+            static_assert(kTileCap <= kMergeCap, "a tile's kept candidates fit the merge's staging");
+#pragma unroll
+            for (int e = 0; e < kElems; ++e) {
+                if (bn[e] <= bt) {
+                    const uint32_t dst = at[e] + wb[e];
+                    if (dst < kept) {
+                        M->s[dst] = x[e];
+                        M->f[dst] = flat_of(e);
+                        M->n[dst] = node_of(e);
+                        if constexpr (SAMPLE) M->phi[dst] = ph[e];
+                        else M->phi[dst] = x[e];
+                    } else {
+                        atomicOr(W.err, kErrInternal);
+                    }
+                }
+            }
+            __syncthreads();
+            const uint32_t k = min(width, kept);
+            rank_staged(W, ra, *M, A.h2, kept, k, sref);
+            write_next_record(W, q, ra, rp, k);
+            return true;
+        }
         Cand *out = W.cand + reg;
 #pragma unroll
         for (int e = 0; e < kElems; ++e) {
@@ -1055,6 +1098,35 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
             }
         }
         W.tcum[((size_t)q * MT + tile) * kBins + tid] = (uint16_t)Cx;
+    }
+    return false;
+}
+
+// MERGE: every stepped request of the launch has at most kTileRows rows (one tile), so one
+// workgroup per request does its tile and then, after a barrier, its merge from the
+// records it has just written: no second kernel. Otherwise the tiles of a request are
+// dealt to one XCD (workgroup b -> XCD b mod 8) and k_merge follows.
+template <int DT, int NORM, bool VEC, bool SAMPLE, bool MERGE>
+__global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp, StepReqs R,
+                                                   const void *__restrict__ logits, int64_t ld) {
+    __shared__ TileSmem A;
+    __shared__ SelSmem sel;
+    if constexpr (MERGE) {
+        __shared__ MergeSmem M;
+        const int ql = (int)blockIdx.x;
+        if (ql >= R.n) return;
+        if (tile_work<DT, NORM, VEC, SAMPLE, true>(T, W, rp, R, logits, ld, ql, 0, A, sel, &M)) return;
+        const ReqArg ra = R.r[ql];
+        if (!ra.step()) return;                        // carried over by tile_work
+        __syncthreads();                               // the tile's records are visible to the workgroup
+        merge_request(W, R.q0 + ql, ra, rp, M, sel);   // a tile with no live row, or the exact path
+    } else {
+        const int MT = W.MT;
+        const int i8 = (int)(blockIdx.x >> 3);
+        const int ql = (int)(blockIdx.x & 7u) + 8 * (i8 / MT);  // all tiles of a request on one XCD
+        const int tile = i8 % MT;
+        if (ql >= R.n) return;
+        tile_work<DT, NORM, VEC, SAMPLE, false>(T, W, rp, R, logits, ld, ql, tile, A, sel, nullptr);
     }
 }
 
@@ -1165,27 +1237,38 @@ hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s) {
 
 template <int DT, int NORM, bool VEC, bool SAMPLE>
 static void launch_tile_t(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                          int64_t ld, hipStream_t s) {
-    const int groups = (R.n + 7) / 8;
-    hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE>), dim3(8 * groups * w.MT), dim3(kThreads), 0, s, t, w, rp,
-                       R, logits, ld);
+                          int64_t ld, bool merge, hipStream_t s) {
+    if (merge) {
+        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, true>), dim3(R.n), dim3(kThreads), 0, s, t, w, rp, R,
+                           logits, ld);
+    } else {
+        const int groups = (R.n + 7) / 8;
+        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, false>), dim3(8 * groups * w.MT), dim3(kThreads), 0, s, t,
+                           w, rp, R, logits, ld);
+    }
 }
 
 template <int DT, bool SAMPLE, bool VEC>
 static void launch_tile_v(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                          int64_t ld, hipStream_t s) {
+                          int64_t ld, bool merge, hipStream_t s) {
     switch (w.norm) {
-    case TCB_NORM_LEVEL: launch_tile_t<DT, TCB_NORM_LEVEL, VEC, SAMPLE>(t, w, rp, R, logits, ld, s); break;
-    case TCB_NORM_OPEN: launch_tile_t<DT, TCB_NORM_OPEN, VEC, SAMPLE>(t, w, rp, R, logits, ld, s); break;
-    default: launch_tile_t<DT, TCB_NORM_CHILDREN, VEC, SAMPLE>(t, w, rp, R, logits, ld, s); break;
+    case TCB_NORM_LEVEL: launch_tile_t<DT, TCB_NORM_LEVEL, VEC, SAMPLE>(t, w, rp, R, logits, ld, merge, s); break;
+    case TCB_NORM_OPEN: launch_tile_t<DT, TCB_NORM_OPEN, VEC, SAMPLE>(t, w, rp, R, logits, ld, merge, s); break;
+    default: launch_tile_t<DT, TCB_NORM_CHILDREN, VEC, SAMPLE>(t, w, rp, R, logits, ld, merge, s); break;
     }
 }
 
 template <int DT, bool SAMPLE>
 static void launch_tile_dt(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                           int64_t ld, bool vec, hipStream_t s) {
-    if (vec) launch_tile_v<DT, SAMPLE, true>(t, w, rp, R, logits, ld, s);
-    else launch_tile_v<DT, SAMPLE, false>(t, w, rp, R, logits, ld, s);
+                           int64_t ld, bool vec, bool merge, hipStream_t s) {
+    if (vec) launch_tile_v<DT, SAMPLE, true>(t, w, rp, R, logits, ld, merge, s);
+    else launch_tile_v<DT, SAMPLE, false>(t, w, rp, R, logits, ld, merge, s);
+}
+
+bool tile_merges(const StepReqs &R) {
+    for (int i = 0; i < R.n; ++i)
+        if (R.r[i].step() && R.r[i].rmax() > kTileRows) return false;
+    return true;
 }
 
 hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
@@ -1193,18 +1276,19 @@ hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReq
     if (R.n <= 0) return hipSuccess;
     // 16-byte row pieces: ld a multiple of 4 (fp32) or 8 (bf16) elements, 16-byte base
     const bool vec = t.V == 256 && (ld % (dtype == TCB_F32 ? 4 : 8)) == 0 && ((uintptr_t)logits % 16) == 0;
+    const bool merge = tile_merges(R);
     if (dtype == TCB_F32) {
-        if (sampled) launch_tile_dt<TCB_F32, true>(t, w, rp, R, logits, ld, vec, s);
-        else launch_tile_dt<TCB_F32, false>(t, w, rp, R, logits, ld, vec, s);
+        if (sampled) launch_tile_dt<TCB_F32, true>(t, w, rp, R, logits, ld, vec, merge, s);
+        else launch_tile_dt<TCB_F32, false>(t, w, rp, R, logits, ld, vec, merge, s);
     } else {
-        if (sampled) launch_tile_dt<TCB_BF16, true>(t, w, rp, R, logits, ld, vec, s);
-        else launch_tile_dt<TCB_BF16, false>(t, w, rp, R, logits, ld, vec, s);
+        if (sampled) launch_tile_dt<TCB_BF16, true>(t, w, rp, R, logits, ld, vec, merge, s);
+        else launch_tile_dt<TCB_BF16, false>(t, w, rp, R, logits, ld, vec, merge, s);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, hipStream_t s) {
-    if (R.n <= 0) return hipSuccess;
+    if (R.n <= 0 || tile_merges(R)) return hipSuccess;           // merged inside the tile kernel
     hipLaunchKernelGGL(k_merge, dim3(R.n), dim3(kThreads), 0, s, t, w, rp, R);
     return hipGetLastError();
 }

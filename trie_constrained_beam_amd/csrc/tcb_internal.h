@@ -143,6 +143,9 @@ hipError_t launch_lmhead_sparse(const TrieDev &t, const WaveDev &w, int rp, cons
                                 int64_t ld, int H, const void *weight, float *out, int max_rows, hipStream_t s);
 hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
                          int64_t ld, int H, const void *weight, float *out, hipStream_t s);
+// true when every stepped request of R has at most kTileRows rows: the tile kernel then
+// merges each request itself and launch_merge launches nothing
+bool tile_merges(const StepReqs &R);
 hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, hipStream_t s);
 hipError_t launch_finalize(const TrieDev &t, const WaveDev &w, int rp, const FinBatch &b,
                            uint8_t *sids, float *scores, int64_t *items, int32_t *counts,
