@@ -244,6 +244,53 @@ def test_in_tile_merge_matches_merge_kernel():
                 assert np.array_equal(fa[k][i][:int(c)], fb[k][i][:int(c)]), (k, i)
 
 
+def test_first_step_reads_no_initial_state():
+    """A request's first step starts from its known initial state without reading it (the
+    state is written only when something else reads it first). New requests admitted
+    mid-decode beside older ones, and into slots that held other requests' rows, with no
+    export in between, must decode bitwise as in a fresh wave."""
+    cat = synth.catalog(100_000, 4, ("zipf",) * 4, [47, 1])
+    trie = Trie(cat, device="cuda")
+    S = 1200
+
+    def run(plan):
+        """plan: list of ("init", [(key, width), ...]) / ("step",) / ("fin", [key, ...])."""
+        beams = Beams(trie, S, 8, 512)
+        live, out = {}, {}                              # key -> [req id, base, width, steps taken]
+        for op in plan:
+            if op[0] == "init":
+                ids, bases = beams.init(np.asarray([w for _, w in op[1]], dtype=np.int32))
+                for (key, w), rid, base in zip(op[1], ids, bases):
+                    live[key] = [int(rid), int(base), w, 0]
+            elif op[0] == "step":
+                host = np.zeros((S, 256), dtype=np.float32)
+                for key, (rid, base, w, t) in live.items():
+                    if t < 4:
+                        host[base:base + w] = synth.logits_rowkeyed(47, t, key, w, 2.0)
+                beams.step(torch.from_numpy(host).cuda())
+                for v in live.values():
+                    v[3] = min(v[3] + 1, 4)
+            else:
+                fin = beams.finalize(np.asarray([live[k][0] for k in op[1]], dtype=np.int32))
+                for i, k in enumerate(op[1]):
+                    c = int(fin["counts"][i])
+                    out[k] = (c, fin["sids"][i][:c].copy(), fin["scores"][i][:c].copy(), fin["items"][i][:c].copy())
+                    del live[k]
+        return out
+
+    W1, W2, W3 = [(1, 300), (2, 64)], [(3, 128), (4, 7), (5, 200)], [(6, 250), (7, 50)]
+    mixed = run([("init", W1), ("step",), ("step",), ("init", W2), ("step",), ("step",), ("fin", [1, 2]),
+                 ("init", W3), ("step",), ("step",), ("fin", [3, 4, 5]), ("step",), ("step",), ("fin", [6, 7])])
+    fresh = {}
+    for Wn in (W2, W3):
+        fresh.update(run([("init", Wn), ("step",), ("step",), ("step",), ("step",), ("fin", [k for k, _ in Wn])]))
+    for key in fresh:
+        a, b = mixed[key], fresh[key]
+        assert a[0] == b[0], key
+        for u, v in zip(a[1:], b[1:]):
+            assert np.array_equal(u, v), key
+
+
 def test_finalize_legality_items_and_device_variant():
     cat = synth.catalog(80_000, 4, ("zipf",) * 4, [45, 1])
     cat = np.concatenate([cat, cat[:5000]])               # duplicates map to the lowest row

@@ -444,8 +444,9 @@ __device__ __forceinline__ void merge_request(const WaveDev &W, int q, const Req
     // the live-row count (how many tiles wrote counts), the best row's score and the
     // tiles' counts are all loaded at once: the counts of every tile the request could
     // have are read and those past the live tiles are dropped
-    const int rows = W.rec[rp][q].rows;
-    const float sref = W.score[ra.par()][ra.base()];
+    const bool fresh = ra.level() == 0;                // the initial state: one row, the root, score 0
+    const int rows = fresh ? 1 : W.rec[rp][q].rows;
+    const float sref = fresh ? 0.0f : W.score[ra.par()][ra.base()];
     const int tmax = (ra.rmax() + kTileRows - 1) / kTileRows;
 
     // 1. request-wide cumulative kept counts and the boundary bin b*
@@ -724,9 +725,12 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
     }
 
     // 1. row state and logits, all issued at once: the live-row count arrives with the
-    //    rows, which are read for every row the request can have and dropped if dead
-    const int rows = W.rec[rp][q].rows;
-    const float sref = W.score[cp][base];              // best row of the request
+    //    rows, which are read for every row the request can have and dropped if dead. A
+    //    request's first step starts from its initial state (one row: the root, score 0),
+    //    which is not read back, so the step needs no earlier initialising kernel
+    const bool fresh = level == 0;
+    const int rows = fresh ? 1 : W.rec[rp][q].rows;
+    const float sref = fresh ? 0.0f : W.score[cp][base];   // best row of the request
     const bool in_range = r < ra.rmax();
     int32_t nd = -1;
     float sr = 0.0f, pr = 0.0f;                        // the row's key and (sampled) log-probability
@@ -738,9 +742,9 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
     const bool gather = VEC && ra.gather();
     if (in_range) {
         const int slot = base + r;
-        nd = W.node[cp][slot];
-        sr = W.score[cp][slot];
-        if constexpr (SAMPLE) pr = W.phi[cp][slot];
+        nd = fresh ? 0 : W.node[cp][slot];
+        sr = fresh ? 0.0f : W.score[cp][slot];
+        if constexpr (SAMPLE) pr = fresh ? 0.0f : W.phi[cp][slot];
         if (!gather) load_row<DT, VEC>(logits, ld, slot, j, V, x);
     }
     if (tile * kTileRows >= rows) return false;              // a tile with no live row

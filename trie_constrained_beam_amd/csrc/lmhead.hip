@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
             mfma_step(av, bv);
         }
     }
-    const int rows = W.rec[rp][R.q0 + ql].rows;
+    const int rows = level == 0 ? 1 : W.rec[rp][R.q0 + ql].rows;   // a first step: the root only
     // partial blocks of the four waves, added in a fixed order; wave w finishes row block w
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -154,10 +154,11 @@ __global__ __launch_bounds__(64 * kSpWaves) void k_lmhead_sparse(TrieDev T, Wave
     if (!ra.step() || !ra.sparse_head()) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = quad * kSpWaves + wave;
-    const int rows = W.rec[rp][R.q0 + ql].rows;
+    const int level = ra.level();
+    const int rows = level == 0 ? 1 : W.rec[rp][R.q0 + ql].rows;   // a first step: the root only
     if (r >= rows) return;
-    const int base = ra.base(), level = ra.level(), slot = base + r;
-    const uint32_t nd = (uint32_t)W.node[ra.par()][slot];
+    const int base = ra.base(), slot = base + r;
+    const uint32_t nd = level == 0 ? 0u : (uint32_t)W.node[ra.par()][slot];
     if (nd < T.off[level] || nd >= T.off[level + 1]) return;       // not a node of this depth: the tile kernel flags it
     const uint32_t cb = T.child_begin[nd], ce = T.child_begin[nd + 1];
     const int nch = H / 8;                                         // chunks of 8 bf16

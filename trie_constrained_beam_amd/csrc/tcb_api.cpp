@@ -140,8 +140,30 @@ tcb_status check_finalize_args(tcb_beams *b, int32_t n, const int32_t *req_ids) 
     return TCB_OK;
 }
 
+// Writes the initial device state of requests admitted since the last step: needed only
+// before something other than a step reads request state (a step starts a fresh request
+// from its known initial state without reading it).
+tcb_status flush_init(tcb_beams *b, hipStream_t s) {
+    const auto &p = b->pending_init;
+    for (size_t i0 = 0; i0 < p.size(); i0 += tcb::InitBatch::kMax) {
+        tcb::InitBatch ib{};
+        ib.n = (int32_t)std::min(p.size() - i0, (size_t)tcb::InitBatch::kMax);
+        for (int j = 0; j < ib.n; ++j) {
+            ib.req[j] = p[i0 + (size_t)j][0];
+            ib.base[j] = p[i0 + (size_t)j][1];
+            ib.width[j] = p[i0 + (size_t)j][2];
+        }
+        hipError_t e = tcb::launch_init(b->w, ib, s);
+        if (e != hipSuccess) return hip_fail(e, "beam_init launch");
+    }
+    b->pending_init.clear();
+    return TCB_OK;
+}
+
 tcb_status run_finalize(tcb_beams *b, int32_t n, const int32_t *req_ids, uint8_t *sids,
                         float *scores, int64_t *items, int32_t *counts, hipStream_t s) {
+    const tcb_status st = flush_init(b, s);
+    if (st) return st;
     for (int i0 = 0; i0 < n; i0 += tcb::FinBatch::kMax) {
         tcb::FinBatch fb{};
         fb.n = std::min(n - i0, tcb::FinBatch::kMax);
@@ -329,17 +351,8 @@ tcb_status tcb_beam_init(tcb_beams *b, int32_t n, const int32_t *widths, int32_t
         bases.push_back(base);
         ++next;
     }
-    for (int i0 = 0; i0 < n; i0 += tcb::InitBatch::kMax) {
-        tcb::InitBatch ib{};
-        ib.n = std::min(n - i0, tcb::InitBatch::kMax);
-        for (int j = 0; j < ib.n; ++j) {
-            ib.req[j] = ids[(size_t)(i0 + j)];
-            ib.base[j] = bases[(size_t)(i0 + j)];
-            ib.width[j] = widths[i0 + j];
-        }
-        hipError_t e = tcb::launch_init(b->w, ib, (hipStream_t)stream);
-        if (e != hipSuccess) return hip_fail(e, "beam_init launch");
-    }
+    (void)stream;                          // the initial state is written lazily (flush_init)
+    for (int i = 0; i < n; ++i) b->pending_init.push_back({ids[(size_t)i], bases[(size_t)i], widths[i]});
     b->free_ranges = fr;
     for (int i = 0; i < n; ++i) {
         auto &q = b->reqs[(size_t)ids[(size_t)i]];
@@ -360,6 +373,7 @@ static tcb_status step_common(tcb_beams *b) {
 }
 
 static void step_done(tcb_beams *b) {
+    b->pending_init.clear();               // every admitted request took its first step
     b->rp ^= 1;
     b->steps++;
     for (auto &q : b->reqs)
@@ -517,6 +531,8 @@ tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, float 
                            uint32_t *d_hist, int32_t *d_rows, int32_t *d_level, void *stream) {
     if (!b) return set_error(TCB_E_ARG, "beam_export: null wave");
     hipStream_t s = (hipStream_t)stream;
+    const tcb_status st = flush_init(b, s);
+    if (st) return st;
     const size_t S = (size_t)b->w.S;
     hipError_t e = hipSuccess;
     if (d_parent_slot && e == hipSuccess)

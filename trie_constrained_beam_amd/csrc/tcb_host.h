@@ -3,6 +3,7 @@
 
 #include <string>
 #include <utility>
+#include <array>
 #include <vector>
 
 #include "tcb_internal.h"
@@ -40,6 +41,10 @@ struct tcb_beams {
     int64_t steps = 0;
     std::vector<Req> reqs;
     std::vector<std::pair<int32_t, int32_t>> free_ranges;  // (start, length), sorted
+    // admitted requests whose initial device state (record, root row) is not written yet:
+    // their first step does not read it, so it is written only if something else would
+    // read it first (export, finalize); (request id, slot base, width)
+    std::vector<std::array<int32_t, 3>> pending_init;
     // finalize staging inside the workspace
     uint8_t *d_fin_sids = nullptr;
     float *d_fin_scores = nullptr;
