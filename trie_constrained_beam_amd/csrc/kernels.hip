@@ -1166,30 +1166,39 @@ __global__ void k_finalize(TrieDev T, WaveDev W, int rp, FinBatch fb, uint8_t *s
                            int64_t *items, int32_t *counts) {
     const int i = blockIdx.x;
     if (i >= fb.n) return;
-    const int req = fb.req[i];
+    const int req = fb.req[i], base = fb.base[i], width = fb.width[i], par = fb.par[i];
     const size_t orow = (size_t)fb.out_row[i];
-    const ReqRec rec = W.rec[rp][req];
-    const int L = T.L, par = rec.par;
+    const int L = T.L;
     const uint32_t leaf0 = T.off[L], leaf1 = T.off[L + 1];
+    // the live-row count, and each row's state and last back-pointer for every row the
+    // request can have, are loaded at once (rows past the count are dropped)
+    const int rows = W.rec[rp][req].rows;
     for (int j = threadIdx.x; j < W.Bmax; j += blockDim.x) {
         const size_t out = orow * (size_t)W.Bmax + (size_t)j;
-        if (j < rec.rows) {
-            const int slot = rec.base + j;
-            const uint32_t node = (uint32_t)W.node[par][slot];
+        uint32_t node = 0u, h = 0u;
+        float phi = 0.0f;
+        if (j < width) {
+            const int slot = base + j;
+            node = (uint32_t)W.node[par][slot];
+            phi = W.phi[par][slot];
+            h = W.hist[(size_t)(L - 1) * W.S + slot];
+        }
+        if (j < rows) {
             int64_t item = -1;
             if (node >= leaf0 && node < leaf1) item = T.leaf_item[node - leaf0];
             else if (!(W.norm == TCB_NORM_OPEN && (int32_t)node == -1)) atomicOr(W.err, kErrBadNode);
-            uint32_t r = (uint32_t)j;
-            for (int lv = L - 1; lv >= 0; --lv) {
-                if (r >= (uint32_t)rec.width) {      // corrupt back-pointer: never read past the request
+            sids[out * L + (L - 1)] = (uint8_t)(h & 255u);
+            uint32_t r = h >> 8;
+            for (int lv = L - 2; lv >= 0; --lv) {
+                if (r >= (uint32_t)width) {            // corrupt back-pointer: never read past the request
                     atomicOr(W.err, kErrBadNode);
                     break;
                 }
-                const uint32_t h = W.hist[(size_t)lv * W.S + rec.base + r];
-                sids[out * L + lv] = (uint8_t)(h & 255u);
-                r = h >> 8;
+                const uint32_t hl = W.hist[(size_t)lv * W.S + base + r];
+                sids[out * L + lv] = (uint8_t)(hl & 255u);
+                r = hl >> 8;
             }
-            scores[out] = W.phi[par][slot];          // summed log-probability
+            scores[out] = phi;                         // summed log-probability
             items[out] = item;
         } else {
             for (int lv = 0; lv < L; ++lv) sids[out * L + lv] = 0;
@@ -1197,11 +1206,16 @@ __global__ void k_finalize(TrieDev T, WaveDev W, int rp, FinBatch fb, uint8_t *s
             items[out] = -1;
         }
     }
-    __syncthreads();
+    __syncthreads();                                   // every wave has read the record
     if (threadIdx.x == 0) {
-        counts[orow] = rec.rows;
-        ReqRec fr = rec;
+        counts[orow] = rows;
+        ReqRec fr{};
+        fr.base = base;
+        fr.width = width;
+        fr.rows = rows;
+        fr.level = L;
         fr.status = kReqFree;
+        fr.par = par;
         W.rec[0][req] = fr;
         W.rec[1][req] = fr;
     }

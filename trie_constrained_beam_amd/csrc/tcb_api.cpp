@@ -168,8 +168,12 @@ tcb_status run_finalize(tcb_beams *b, int32_t n, const int32_t *req_ids, uint8_t
         tcb::FinBatch fb{};
         fb.n = std::min(n - i0, tcb::FinBatch::kMax);
         for (int j = 0; j < fb.n; ++j) {
+            const auto &rq = b->reqs[(size_t)req_ids[i0 + j]];
             fb.req[j] = req_ids[i0 + j];
             fb.out_row[j] = i0 + j;
+            fb.base[j] = rq.base;
+            fb.width[j] = rq.width;
+            fb.par[j] = rq.level & 1;      // a step at level t reads buffer t & 1 and writes the other
         }
         hipError_t e = tcb::launch_finalize(b->tdev, b->w, b->rp, fb, sids, scores, items, counts, s);
         if (e != hipSuccess) return hip_fail(e, "finalize launch");

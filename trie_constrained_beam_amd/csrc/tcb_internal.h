@@ -129,6 +129,7 @@ struct FinBatch {
     int32_t n;
     int32_t req[kMax];
     int32_t out_row[kMax];         // output row of each request in the caller arrays
+    int32_t base[kMax], width[kMax], par[kMax];   // host copies of the record's fixed fields
 };
 
 hipError_t launch_clear_wave(const WaveDev &w, hipStream_t s);
