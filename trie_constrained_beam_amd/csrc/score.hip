@@ -879,10 +879,13 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_final(ScoreDev a) {
     {
         const int nlist = (kC + 63) / 64;
         uint64_t me = ~0ull;                          // no real key: the SID is below 2^25
+        int32_t item = -1;
         if (wave < nlist) {
             const int i = wave * 64 + lane;
             me = wave_sort(i < kC ? sortk[i] : ~0ull);
             sortk[i] = me;                            // a wave rewrites only the keys it read
+            const int32_t leaf = (int32_t)(uint32_t)me;
+            if (me != ~0ull && a.out_item && leaf < n) item = a.leaf_item[leaf];   // arrives during the search
         }
         __syncthreads();
         if (wave < nlist) {
@@ -903,7 +906,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_score_final(ScoreDev a) {
                 const int32_t leaf = (int32_t)(uint32_t)me;
                 a.out_leaf[(size_t)u * K + rank] = leaf;
                 a.out_score[(size_t)u * K + rank] = ord2f(~(uint32_t)(me >> 32));
-                if (a.out_item) a.out_item[(size_t)u * K + rank] = leaf < n ? a.leaf_item[leaf] : -1;
+                if (a.out_item) a.out_item[(size_t)u * K + rank] = item;
             }
         }
     }
