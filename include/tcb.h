@@ -157,7 +157,10 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
  *                  [base_i, base_i + n_i); its live rows are the first rows_i of
  *                  them, best first. Logits / hidden rows are indexed by slot.
  * All or nothing: if the requests do not all fit in the free slots / ids the call
- * returns TCB_E_BUDGET and admits none. */
+ * returns TCB_E_BUDGET and admits none. Nothing is launched: a request's first step
+ * starts from this known state without reading it, and the device copy of the state is
+ * written on the stream of an export or finalize that would read it first (`stream`
+ * is unused). */
 tcb_status tcb_beam_init(tcb_beams *b, int32_t n, const int32_t *widths,
                          int32_t *out_req_ids, int32_t *out_slot_base, void *stream);
 
