@@ -408,7 +408,8 @@ static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out, int d
             const int64_t prefixes = rq.level == 0 ? 1 : open ? (int64_t)width : b->depth_nodes[rq.level < b->L ? rq.level : 0];
             const uint32_t rmax = (uint32_t)std::min<int64_t>(width, prefixes);
             const uint32_t level = step ? (uint32_t)rq.level : 0u;
-            const uint32_t pre = open ? 1u : (b->prefilter_levels >> level) & 1u;
+            // a first step has one row, at most V <= 256 candidates: nothing to prefilter
+            const uint32_t pre = level == 0 ? 0u : open ? 1u : (b->prefilter_levels >> level) & 1u;
             // gather only the logit sectors that hold a child where rows have few children
             const bool by_level = b->read_mode == TCB_READ_GATHER || (b->read_mode == TCB_READ_AUTO &&
                                                                       (b->gather_levels[dt_index] >> level & 1u));
