@@ -10,9 +10,12 @@
 // Tiling. A workgroup of 4 waves computes a 64-row x 64-code block with
 // v_mfma_f32_16x16x32_bf16. The block's K range is split across the waves: wave w
 // accumulates the whole 64 x 64 block (4 x 4 tiles of 16 x 16, 64 fp32 per lane) over
-// its quarter of K, reading its A and B operands straight from memory into registers
-// with many K-steps of loads in flight (one workgroup per CU leaves each wave a whole
-// SIMD and its register file). The four partial blocks are then added through LDS in a
+// its quarter of K with many K-steps of loads in flight (one workgroup per CU leaves each
+// wave a whole SIMD and its register file). The loads are row-contiguous (four lanes read
+// one row's 64 bytes of a K-step) and each step passes through the wave's own LDS stage
+// into the MFMA operand layout (lane = row): loading that layout straight from memory
+// touches 16 rows per instruction and runs at about a third of the per-CU load rate
+// (measured on gfx950). The four partial blocks are then added through LDS in a
 // fixed order (wave 0 + 1 + 2 + 3), so results are deterministic. The four code blocks
 // of one row tile are dealt to the same XCD, so the hidden rows they share are read
 // from HBM once and then hit that XCD's L2.
@@ -30,6 +33,9 @@ constexpr int kGRows = 64;                 // rows of a block
 constexpr int kGCodes = 64;                // codes of a block (4 blocks cover V = 256)
 constexpr int kGThreads = 256;             // 4 waves, each over a quarter of K
 constexpr int kKStep = 32;                 // K of one MFMA
+// a staged row (64 bytes of one K-step) padded to 80 bytes: the 16 rows one MFMA-layout
+// read instruction touches start in distinct 16-byte bank groups
+constexpr int kStageRow = 80;
 
 // NS = K-steps of 32 per wave (H = 4 * 32 * NS); NS = 0: any H % 128 == 0, one step
 // of loads in flight.
@@ -39,6 +45,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
                                                       const uint16_t *__restrict__ weight,
                                                       float *__restrict__ out) {
     __shared__ f32x4 red[4][4][4][64];                        // [wave][row blk][code blk][lane]
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][2][64 * kStageRow];   // [wave][A, B][row]
     const int MT = W.MT;
     const int xcd = (int)(blockIdx.x & 7u), i8 = (int)(blockIdx.x >> 3);
     const int cblk = i8 & 3;                                  // code block 0..3
@@ -54,22 +61,41 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     const int rows_bound = ra.rmax(), base = ra.base(), level = ra.level();
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, kq = lane >> 4;
+    const int l16 = lane & 15, kq = lane >> 4;                // MFMA layout: row l16, k chunk kq
+    const int lr = lane >> 2, lc = lane & 3;                  // loads: row lr (+16 i), 16-byte chunk lc
     const int nsteps = NS > 0 ? NS : H / (4 * kKStep);
-    const int k0 = wave * nsteps * kKStep + 8 * kq;           // this lane's first k
-    const uint16_t *ap[4], *bp[4];
+    const int kw0 = wave * nsteps * kKStep;                   // this wave's first k
+    const uint16_t *ag[4], *bg[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int ar = r0 + 16 * b + l16;                     // rows past the bound read row r0, never stored
-        ap[b] = hidden + (size_t)(base + (ar < rows_bound ? ar : r0)) * (size_t)ld + k0;
-        bp[b] = weight + ((size_t)level * 256 + (size_t)cblk * kGCodes + 16 * b + l16) * (size_t)H + k0;
+    for (int i = 0; i < 4; ++i) {
+        const int ar = r0 + 16 * i + lr;                      // rows past the bound read row r0, never stored
+        ag[i] = hidden + (size_t)(base + (ar < rows_bound ? ar : r0)) * (size_t)ld + kw0 + 8 * lc;
+        bg[i] = weight + ((size_t)level * 256 + (size_t)cblk * kGCodes + 16 * i + lr) * (size_t)H + kw0 + 8 * lc;
     }
+    uint8_t *sa = stage[wave][0], *sb = stage[wave][1];
     f32x4 acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    auto mfma_step = [&](const u32x4 (&av)[4], const u32x4 (&bv)[4]) {
+    // one K-step: the loaded pieces into the wave's stage, back out in the MFMA layout
+    // (the same k of each row as a direct load of that layout), 4 x 4 MFMAs. LDS operations
+    // of one wave complete in order, so the stage needs no barrier.
+    auto stage_step = [&](const u32x4 (&ra)[4], const u32x4 (&rb)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<u32x4 *>(sa + (16 * i + lr) * kStageRow + 16 * lc) = ra[i];
+            *reinterpret_cast<u32x4 *>(sb + (16 * i + lr) * kStageRow + 16 * lc) = rb[i];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        u32x4 av[4], bv[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            av[b] = *reinterpret_cast<const u32x4 *>(sa + (16 * b + l16) * kStageRow + 16 * kq);
+            bv[b] = *reinterpret_cast<const u32x4 *>(sb + (16 * b + l16) * kStageRow + 16 * kq);
+        }
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -77,40 +103,43 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[a]),
                                                                     __builtin_bit_cast(bf16x8, bv[b]), acc[a][b],
                                                                     0, 0, 0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
     if constexpr (NS > 0) {
-        // a ring of PD K-steps of operands in registers, refilled as each step is used
+        // a ring of PD K-steps of loads in registers, refilled as each step is used
         constexpr int PD = NS < 8 ? NS : 8;
         u32x4 ra[PD][4], rb[PD][4];
 #pragma unroll
         for (int s = 0; s < PD; ++s)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                ra[s][b] = *reinterpret_cast<const u32x4 *>(ap[b] + s * kKStep);
-                rb[s][b] = *reinterpret_cast<const u32x4 *>(bp[b] + s * kKStep);
+            for (int i = 0; i < 4; ++i) {
+                ra[s][i] = *reinterpret_cast<const u32x4 *>(ag[i] + s * kKStep);
+                rb[s][i] = *reinterpret_cast<const u32x4 *>(bg[i] + s * kKStep);
             }
         __builtin_amdgcn_sched_barrier(0);                    // keep the ring's loads issued up front
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            mfma_step(ra[s % PD], rb[s % PD]);
+            stage_step(ra[s % PD], rb[s % PD]);
             if (s + PD < NS) {
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    ra[s % PD][b] = *reinterpret_cast<const u32x4 *>(ap[b] + (s + PD) * kKStep);
-                    rb[s % PD][b] = *reinterpret_cast<const u32x4 *>(bp[b] + (s + PD) * kKStep);
+                for (int i = 0; i < 4; ++i) {
+                    ra[s % PD][i] = *reinterpret_cast<const u32x4 *>(ag[i] + (s + PD) * kKStep);
+                    rb[s % PD][i] = *reinterpret_cast<const u32x4 *>(bg[i] + (s + PD) * kKStep);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);                // the refill stays behind its step
         }
     } else {
         for (int s = 0; s < nsteps; ++s) {
-            u32x4 av[4], bv[4];
+            u32x4 ra[4], rb[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                av[b] = *reinterpret_cast<const u32x4 *>(ap[b] + s * kKStep);
-                bv[b] = *reinterpret_cast<const u32x4 *>(bp[b] + s * kKStep);
+            for (int i = 0; i < 4; ++i) {
+                ra[i] = *reinterpret_cast<const u32x4 *>(ag[i] + s * kKStep);
+                rb[i] = *reinterpret_cast<const u32x4 *>(bg[i] + s * kKStep);
             }
-            mfma_step(av, bv);
+            stage_step(ra, rb);
         }
     }
     const int rows = level == 0 ? 1 : W.rec[rp][R.q0 + ql].rows;   // a first step: the root only
