@@ -129,7 +129,6 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
                     rb[s % PD][i] = *reinterpret_cast<const u32x4 *>(bg[i] + (s + PD) * kKStep);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);                // the refill stays behind its step
         }
     } else {
         for (int s = 0; s < nsteps; ++s) {
