@@ -225,7 +225,8 @@ def main_leg(args, wl, cat, dev):
 
 def lmhead_leg(args, dev, read_mode="dense"):
     """The fused lm_head workload. read_mode "dense": the MFMA head at every level (its
-    roofline); "auto": children-only heads at the low-fanout levels."""
+    roofline); "auto": the library's per-level choice (the children-only head only where
+    rows touch at most one 4-code piece on average)."""
     import numpy as np
     import torch
     from trie_constrained_beam_amd import Beams, Trie, synth
@@ -428,7 +429,7 @@ def main():
     lm = None
     if args.lmhead:
         lm = lmhead_leg(args, dev, "dense")
-        lm["children_only"] = lmhead_leg(args, dev, "auto")
+        lm["auto"] = lmhead_leg(args, dev, "auto")
     sc = None
     if args.score:
         swl = synth.SCORE_WORKLOADS["score_u32_k512_l4_4m_zipf_d64"]

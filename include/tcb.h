@@ -251,7 +251,7 @@ tcb_status tcb_beams_set_validate(tcb_beams *b, int32_t on);
  * For tcb_beam_step_lmhead the same modes choose the head: DENSE computes every row's
  * 256 logits (MFMA); GATHER computes only the 16-byte pieces (4 codes) of each row that
  * hold a child, one dot product over H per code, and reads only those pieces; AUTO does
- * so at depths whose rows' children touch at most 2 of the row's 64 pieces on average
+ * so at depths whose rows' children touch at most one of the row's 64 pieces on average
  * (H <= 4096; otherwise dense). The two heads sum in different orders, so their logits
  * agree to fp32 rounding rather than bitwise. Errors: TCB_E_ARG. */
 enum { TCB_READ_AUTO = 0, TCB_READ_DENSE = 1, TCB_READ_GATHER = 2 };

@@ -280,10 +280,11 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
             const double sectors = k == 0 ? 16.0 : 8.0;
             if (1.0 - std::pow(1.0 - 1.0 / sectors, fan) < 0.5) b->gather_levels[k] |= 1u << d;
         }
-        // children-only lm_head where a row's children are expected to touch at most 2 of its
-        // 64 pieces (8 of 256 codes): its dot products run on the vector ALUs, about 30x
-        // dearer per flop than the dense head's matrix cores, so it pays only at fanouts near 1
-        if (64.0 * (1.0 - std::pow(1.0 - 1.0 / 64.0, fan)) <= 2.0) b->sparse_head_levels |= 1u << d;
+        // children-only lm_head where a row's children are expected to touch at most one of
+        // its 64 pieces (4 of 256 codes): its dot products run on the vector ALUs and re-read
+        // the weights per row, so against the LDS-staged matrix-core head it pays only at
+        // fanouts near 1 (measured: at about 2 pieces per row it is already slower)
+        if (64.0 * (1.0 - std::pow(1.0 - 1.0 / 64.0, fan)) <= 1.0) b->sparse_head_levels |= 1u << d;
     }
     const uint8_t *img = (const uint8_t *)t->d_image;
     b->tdev.child_begin = (const uint32_t *)(img + t->o_child_begin);
