@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     };
     if constexpr (NS > 0) {
         // a ring of PD K-steps of loads in registers, refilled as each step is used
-        constexpr int PD = NS < 8 ? NS : 8;
+        constexpr int PD = NS < 4 ? NS : 4;       // deeper rings spill past the 256 VGPRs
         u32x4 ra[PD][4], rb[PD][4];
 #pragma unroll
         for (int s = 0; s < PD; ++s)
