@@ -144,6 +144,23 @@ def test_constant_logits_exact_ties():
             assert abs(float(out["scores"][i, j]) - closed) < 1e-5
 
 
+def test_exact_path_inside_merged_tile():
+    """Requests of at most 64 rows merge inside the tile kernel. With every logit equal,
+    64 rows x 256 children give 16384 exactly tied candidates, more than a tile keeps, so
+    that tile takes its exact selection path and the merge then runs from memory in the
+    same kernel: GPU == oracle, ties by flat index."""
+    a, b, c = np.meshgrid(np.arange(256), np.arange(256), np.arange(4), indexing="ij")
+    cat = np.stack([a.ravel(), b.ravel(), c.ravel()], axis=1).astype(np.uint8)   # complete to depth 2
+    widths = [64, 17]
+    run = gh.Run(cat, widths)
+    for t in range(3):
+        rows = [np.zeros((w, 256), dtype=np.float32) for w in widths]
+        run.step_and_check(t, rows, "f32")
+    out = run.beams.finalize(run.ids)
+    for i, w in enumerate(widths):
+        assert int(out["counts"][i]) == w
+
+
 def test_single_child_chain_and_width_one():
     cat = np.array([[0, 5, 7, 1], [1, 2, 0, 0], [1, 2, 1, 0], [1, 2, 2, 0], [1, 3, 3, 3],
                     [2, 0, 0, 0]], dtype=np.uint8)
