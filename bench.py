@@ -3,7 +3,9 @@
 
 One bench step = one full decode of the workload's batch on the GPU: admit every
 request at the root, run L constrained beam steps (masked log-softmax, per-request
-top-n, parent-gather / trie-advance) and gather the ranked beams into device buffers.
+top-n, parent-gather / trie-advance); the last step also writes each request's ranked
+beams into device buffers (the wave's finish outputs), so a decode is L steps and no
+separate finalize pass.
 The default workload is 32 requests x beam 512, L = 4, a catalog of 4M Zipf(1.1) SIDs
 and bf16 logits N(0, 3^2). Inputs (trie image, per-step logits) are resident in HBM
 before the timed region; consecutive decodes rotate through a pool of input copies
@@ -181,17 +183,13 @@ def main_leg(args, wl, cat, dev):
         return [torch.from_numpy(h).to(dev) for h in host]
     per_decode = sum(h.nbytes for h in host)
     pool = make_pool(upload, per_decode, args.pool_gib)
-    out = {"sids": torch.empty((R, B, L), dtype=torch.uint8, device=dev),
-           "scores": torch.empty((R, B), dtype=torch.float32, device=dev),
-           "items": torch.empty((R, B), dtype=torch.int64, device=dev),
-           "counts": torch.empty(R, dtype=torch.int32, device=dev)}
+    beams.set_finish_outputs(True)       # the last step writes each request's beams (row = id)
     log(f"[bench] pool {len(pool)} x {per_decode / 2**20:.1f} MiB of logits")
     rows_per_step = []
     idx = torch.as_tensor(ids, device=dev).long()
     for t in range(L):
         rows_per_step.append(int(beams.export()["rows"][idx].sum().item()))
         beams.step(pool[0][t])
-    beams.finalize_device(ids, out)
     torch.cuda.synchronize()
     rows_x_steps = sum(rows_per_step)
     log(f"[bench] live rows per step {rows_per_step} -> {rows_x_steps} rows x steps per decode")
@@ -200,7 +198,6 @@ def main_leg(args, wl, cat, dev):
         rid, _ = beams.init(widths)
         for t in range(L):
             beams.step(pool[c][t])
-        beams.finalize_device(rid, out)
     graphs = capture(decode, len(pool)) if args.graph else None
 
     def run(d):
@@ -243,24 +240,19 @@ def lmhead_leg(args, dev, read_mode="dense"):
     per_decode = sum(h.nbytes for h in host)
     pool = make_pool(lambda: [torch.from_numpy(h.view(np.int16)).to(dev).view(torch.bfloat16) for h in host],
                      per_decode, args.pool_gib)
-    out = {"sids": torch.empty((R, B, L), dtype=torch.uint8, device=dev),
-           "scores": torch.empty((R, B), dtype=torch.float32, device=dev),
-           "items": torch.empty((R, B), dtype=torch.int64, device=dev),
-           "counts": torch.empty(R, dtype=torch.int32, device=dev)}
+    beams.set_finish_outputs(True)       # the last step writes each request's beams (row = id)
     ids, _ = beams.init(widths)
     rows_per_step = []
     idx = torch.as_tensor(ids, device=dev).long()
     for t in range(L):
         rows_per_step.append(int(beams.export()["rows"][idx].sum().item()))
         beams.step_lmhead(pool[0][t], w_dev)
-    beams.finalize_device(ids, out)
     torch.cuda.synchronize()
 
     def decode(c):
         rid, _ = beams.init(widths)
         for t in range(L):
             beams.step_lmhead(pool[c][t], w_dev)
-        beams.finalize_device(rid, out)
     graphs = capture(decode, len(pool)) if args.graph else None
 
     def run(d):

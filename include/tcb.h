@@ -282,6 +282,25 @@ tcb_status tcb_beam_finalize_device(tcb_beams *b, int32_t n, const int32_t *req_
                                     uint8_t *d_sids, float *d_scores, int64_t *d_items,
                                     int32_t *d_counts, void *stream);
 
+/* Finish requests inside the step that completes them ([FR] Quickstart: ranked choices
+ * with a sequence score; Features > Decoding, "CUDA graphs": the whole expansion step is
+ * one graph replay, and "Scheduling": slots are reused by requests admitted between steps).
+ * Once set, every step (of any kind) that brings a request to depth L also writes that
+ * request's beams into row `req_id` of these caller device buffers, with the content
+ * and layout tcb_beam_finalize gives a row:
+ *   d_sids     [max_requests][max_width][L] uint8
+ *   d_scores   [max_requests][max_width] float
+ *   d_items    [max_requests][max_width] int64
+ *   d_counts   [max_requests] int32
+ * and releases the request's id and slots at once (tcb_beam_finalize then no longer
+ * knows the id). The writes are made by the step's own kernels on its stream: a row is
+ * complete when the step's work on that stream is, and is overwritten when its id,
+ * re-admitted, finishes again. Requests already at depth L are not affected. The
+ * buffers must stay allocated while set; all four NULL turns the mode off.
+ * Errors: TCB_E_ARG (a null wave, or some but not all buffers NULL). */
+tcb_status tcb_beams_set_finish_outputs(tcb_beams *b, uint8_t *d_sids, float *d_scores,
+                                        int64_t *d_items, int32_t *d_counts);
+
 /* Diagnostics: record HIP events on `stream` around the kernels of each of the next
  * `capacity` steps (the lm_head kernel of tcb_beam_step_lmhead, the tile kernel, then the
  * per-request merge kernel); 0 stops recording and releases the events. While recording,

@@ -68,6 +68,7 @@ SIGNATURES = {
     "tcb_beam_check": (I32, [P, P]),
     "tcb_beam_finalize": (I32, [P, I32, P, P, P, P, P, P]),
     "tcb_beam_finalize_device": (I32, [P, I32, P, P, P, P, P, P]),
+    "tcb_beams_set_finish_outputs": (I32, [P, P, P, P, P]),
     "tcb_beams_enable_timing": (I32, [P, I32, I32]),
     "tcb_beams_timing": (I32, [P, C.POINTER(C.c_double), C.POINTER(C.c_double), C.POINTER(C.c_double),
                                C.POINTER(I32)]),

@@ -235,6 +235,36 @@ class Beams:
                                              _ptr(out["counts"]), _stream()))
         return out
 
+    def set_finish_outputs(self, out=True):
+        """Finish requests inside the step that completes them: from now on a step that
+        brings a request to depth L writes its beams (as ``finalize_device`` would) into row
+        ``req_id`` of the device tensors of ``out`` and releases its id and slots at once.
+        ``out``: a dict with ``sids`` [max_requests, max_width, L] uint8, ``scores`` and
+        ``items`` [max_requests, max_width] float32 / int64 and ``counts`` [max_requests]
+        int32 on the wave's device; ``True`` allocates one; ``None`` turns the mode off.
+        Returns the dict (kept referenced while set)."""
+        if out is None:
+            check(lib().tcb_beams_set_finish_outputs(self._h, None, None, None, None))
+            self._finish_out = None
+            return None
+        R, B, Lv = self.max_requests, self.max_width, self.trie.L
+        if out is True:
+            dev = self.device
+            out = {"sids": torch.zeros((R, B, Lv), dtype=torch.uint8, device=dev),
+                   "scores": torch.zeros((R, B), dtype=torch.float32, device=dev),
+                   "items": torch.zeros((R, B), dtype=torch.int64, device=dev),
+                   "counts": torch.zeros(R, dtype=torch.int32, device=dev)}
+        want = {"sids": ((R, B, Lv), torch.uint8), "scores": ((R, B), torch.float32),
+                "items": ((R, B), torch.int64), "counts": ((R,), torch.int32)}
+        for k, (shape, dt) in want.items():
+            t = out[k]
+            if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError(f"set_finish_outputs: {k} must be a contiguous {dt} {shape} device tensor")
+        check(lib().tcb_beams_set_finish_outputs(self._h, _ptr(out["sids"]), _ptr(out["scores"]),
+                                                 _ptr(out["items"]), _ptr(out["counts"])))
+        self._finish_out = out
+        return out
+
 
 def invalid_rate(out) -> float:
     """Share of returned beams that are not catalog SIDs (item < 0) in a finalize result:

@@ -413,9 +413,10 @@ __device__ __forceinline__ void write_next_record(const WaveDev &W, int q, const
 
 // Entries p < staged of M are grouped by bin (bin b at [G[b - 1], min(G[b], staged)),
 // G[-1] = 0): an entry's rank is the entries of better bins plus the better members of its
-// own bin; ranks below k become the request's new rows.
-__device__ __forceinline__ void rank_staged(const WaveDev &W, const ReqArg ra, const MergeSmem &M,
-                                            const uint32_t *G, uint32_t staged, uint32_t k, float sref) {
+// own bin. emit(rank, p, s, f) is called for every entry; ranks below k are the new rows.
+template <class Emit>
+__device__ __forceinline__ void rank_staged(const MergeSmem &M, const uint32_t *G, uint32_t staged, float sref,
+                                            Emit emit) {
     constexpr int U = kMergeCap / kThreads;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -427,16 +428,105 @@ __device__ __forceinline__ void rank_staged(const WaveDev &W, const ReqArg ra, c
             const uint32_t st = b ? G[b - 1] : 0u, en = min(G[b], staged);
             uint32_t r = 0u;
             for (uint32_t qq = st; qq < en; ++qq) r += key_better(f2ord(M.s[qq]), M.f[qq], o, f) ? 1u : 0u;
-            const uint32_t rank = st + r;
-            if (rank < k) write_new_row(W, ra, rank, s, f, M.n[p], M.phi[p]);
+            emit(st + r, p, s, f);
         }
+    }
+}
+
+// ---------------------------------------------------------------------- finishing requests
+// With StepFin set, the step that brings a request to depth L also does what k_finalize
+// does: the request's beams, best first, go to row q of the outputs and both of its
+// records become free.
+__device__ __forceinline__ bool finishes(const TrieDev &T, const StepFin &F, const ReqArg ra) {
+    return F.sids != nullptr && ra.level() + 1 == T.L;
+}
+
+// Whether `node` is a depth-L node (li: its leaf index); a node that is neither that nor
+// the unconstrained wave's off-catalog -1 sets kErrBadNode.
+__device__ __forceinline__ bool leaf_index(const TrieDev &T, const WaveDev &W, int32_t node, uint32_t &li) {
+    const uint32_t leaf0 = T.off[T.L], leaf1 = T.off[T.L + 1];
+    li = (uint32_t)node - leaf0;
+    if ((uint32_t)node >= leaf0 && (uint32_t)node < leaf1) return true;
+    if (!(W.norm == TCB_NORM_OPEN && node == -1)) atomicOr(W.err, kErrBadNode);
+    return false;
+}
+
+__device__ __forceinline__ int64_t item_of(const TrieDev &T, const WaveDev &W, int32_t node) {
+    uint32_t li;
+    return leaf_index(T, W, node, li) ? (int64_t)T.leaf_item[li] : (int64_t)-1;
+}
+
+// Output entry `rank` of finished request q: codes c_0 .. c_{L-2} from pfx (byte t holds
+// c_t), then c; the summed log-probability and the catalog item.
+__device__ __forceinline__ void write_final_row(const StepFin &F, int L, int Bmax, int q, uint32_t rank,
+                                                uint64_t pfx, uint32_t c, float phi, int64_t item) {
+    const size_t out = (size_t)q * (size_t)Bmax + rank;
+    uint8_t *sp = F.sids + out * (size_t)L;
+    for (int t = 0; t < L - 1; ++t) sp[t] = (uint8_t)(pfx >> (8 * t));
+    sp[L - 1] = (uint8_t)c;
+    F.scores[out] = phi;
+    F.items[out] = item;
+}
+
+// Codes of the request's row r at its current depth, walked back through the per-level
+// back-pointers in memory; a pointer past the request's width sets kErrBadNode.
+__device__ __forceinline__ uint64_t walk_prefix(const WaveDev &W, const ReqArg ra, uint32_t r) {
+    uint64_t pfx = 0;
+    for (int t = ra.level() - 1; t >= 0; --t) {
+        if (r >= (uint32_t)ra.width()) {
+            atomicOr(W.err, kErrBadNode);
+            break;
+        }
+        const uint32_t h = W.hist[(size_t)t * W.S + ra.base() + r];
+        pfx |= (uint64_t)(h & 255u) << (8 * t);
+        r = h >> 8;
+    }
+    return pfx;
+}
+
+// New row `rank` of a finishing request: its state as write_new_row, and its output entry.
+__device__ __forceinline__ void write_finished_row(const TrieDev &T, const WaveDev &W, const StepFin &F, int q,
+                                                   const ReqArg ra, uint32_t rank, float s, uint32_t f,
+                                                   int32_t node, float phi) {
+    write_new_row(W, ra, rank, s, f, node, phi);
+    if (rank < (uint32_t)ra.width())
+        write_final_row(F, T.L, W.Bmax, q, rank, walk_prefix(W, ra, f >> 8), f & 255u, phi, item_of(T, W, node));
+}
+
+// The output entries past the request's k beams, its count, and its free records (in
+// place of write_next_record). The record this step read keeps its row count (rows_in),
+// so a relaunch of the step's kernels reads the same input.
+__device__ __forceinline__ void finish_request(const TrieDev &T, const WaveDev &W, const StepFin &F, int q,
+                                               const ReqArg ra, int rp, int rows_in, uint32_t k) {
+    const int L = T.L;
+    for (int j = (int)k + (int)threadIdx.x; j < W.Bmax; j += (int)blockDim.x) {
+        const size_t out = (size_t)q * (size_t)W.Bmax + (size_t)j;
+        for (int t = 0; t < L; ++t) F.sids[out * L + t] = 0;
+        F.scores[out] = -INFINITY;
+        F.items[out] = -1;
+    }
+    if (threadIdx.x == 0) {
+        F.counts[q] = (int32_t)k;
+        ReqRec fr{};
+        fr.base = ra.base();
+        fr.width = ra.width();
+        fr.rows = (int32_t)k;
+        fr.level = L;
+        fr.status = kReqFree;
+        fr.par = ra.par() ^ 1;
+        W.rec[rp ^ 1][q] = fr;
+        fr.rows = rows_in;
+        W.rec[rp][q] = fr;
     }
 }
 
 // One workgroup per request (k_merge). Every tile's kept candidates are in its region
 // of the candidate records grouped by bin, with its cumulative kept counts in tcum.
-__device__ __forceinline__ void merge_request(const WaveDev &W, int q, const ReqArg ra, int rp, MergeSmem &M,
-                                              SelSmem &sel) {
+// Hs (or nullptr): LDS for the back-pointers of up to kThreads rows when the request finishes
+// in this step, so that its beams' codes are walked on chip.
+__device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W, const StepFin &F, int q,
+                                              const ReqArg ra, int rp, MergeSmem &M, SelSmem &sel,
+                                              uint32_t (*Hs)[kThreads]) {
     const int tid = threadIdx.x;
     const int MT = W.MT, CAPT = W.CAPT;
     const uint16_t *tc = W.tcum + (size_t)q * MT * kBins;
@@ -448,6 +538,17 @@ __device__ __forceinline__ void merge_request(const WaveDev &W, int q, const Req
     const int rows = fresh ? 1 : W.rec[rp][q].rows;
     const float sref = fresh ? 0.0f : W.score[ra.par()][ra.base()];
     const int tmax = (ra.rmax() + kTileRows - 1) / kTileRows;
+    const bool fin = finishes(T, F, ra);
+    // a finishing request: every row's back-pointers of all levels are loaded at once
+    // (ahead of the counts) and stored in LDS, where the beams' codes are walked later
+    const bool fin_lds = fin && Hs != nullptr && ra.rmax() <= kThreads;
+    constexpr int kH = TCB_MAX_L - 1;
+    uint32_t hh[kH];
+    if (fin_lds && tid < ra.rmax()) {
+#pragma unroll
+        for (int t = 0; t < kH; ++t)
+            if (t < ra.level()) hh[t] = W.hist[(size_t)t * W.S + ra.base() + tid];
+    }
 
     // 1. request-wide cumulative kept counts and the boundary bin b*
     const int ntile = (rows + kTileRows - 1) / kTileRows;
@@ -466,6 +567,11 @@ __device__ __forceinline__ void merge_request(const WaveDev &W, int q, const Req
     }
     M.G[tid] = g;
     M.cur[tid] = 0u;
+    if (fin_lds && tid < ra.rmax()) {
+#pragma unroll
+        for (int t = 0; t < kH; ++t)
+            if (t < ra.level()) Hs[t][tid] = hh[t];
+    }
     if (tid == 0) {
         M.bstar = kBins - 1;
         M.cnt = 0u;
@@ -518,11 +624,13 @@ __device__ __forceinline__ void merge_request(const WaveDev &W, int q, const Req
         // 2. stage bins <= b* grouped by bin (each tile's first tcum_j[b*] entries)
         constexpr int U = kMergeCap / kThreads;
         float sc[U], ph[U];
-        uint32_t fl[U];
+        uint32_t fl[U], pos[U];
         int32_t nd[U];
+        int32_t it[U];                                // finishing request: the candidates' catalog items
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t p = (uint32_t)(tid + u * kThreads);
+            nd[u] = 0;
             if (p < staged) {
                 const Cand c = W.cand[cand_index(p)];
                 sc[u] = c.s;
@@ -531,25 +639,83 @@ __device__ __forceinline__ void merge_request(const WaveDev &W, int q, const Req
                 ph[u] = c.phi;
             }
         }
+        uint32_t leafm = 0u;                          // bit u: entry u's node is a depth-L node
+        if (fin_lds) {
+            // issued now, used after the ranking; unconditional (a non-leaf reads item 0), so
+            // that no branch join makes the binning below wait for them
+            const uint32_t leaf0 = T.off[T.L], nleaf = T.off[T.L + 1] - leaf0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t p = (uint32_t)(tid + u * kThreads);
+                const uint32_t li = (uint32_t)nd[u] - leaf0;
+                const bool leaf = p < staged && li < nleaf;
+                leafm |= (leaf ? 1u : 0u) << u;
+                it[u] = T.leaf_item[leaf ? li : 0u];
+            }
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t p = (uint32_t)(tid + u * kThreads);
+            pos[u] = 0u;
             if (p < staged) {
                 const uint32_t b = score_bin(sref, sc[u]);
-                const uint32_t pos = (b ? M.G[b - 1] : 0u) + atomicAdd(&M.cur[b], 1u);
-                if (b <= bs && pos < staged) {        // holds by construction
-                    M.s[pos] = sc[u];
-                    M.f[pos] = fl[u];
-                    M.n[pos] = nd[u];
-                    M.phi[pos] = ph[u];
+                pos[u] = (b ? M.G[b - 1] : 0u) + atomicAdd(&M.cur[b], 1u);
+                if (b <= bs && pos[u] < staged) {     // holds by construction
+                    M.s[pos[u]] = sc[u];
+                    M.f[pos[u]] = fl[u];
+                    M.n[pos[u]] = nd[u];
+                    M.phi[pos[u]] = ph[u];
                 } else {
                     atomicOr(W.err, kErrInternal);
+                    pos[u] = staged;
                 }
             }
         }
         __syncthreads();
         // 3. rank = members of better bins + better members of the own bin
-        rank_staged(W, ra, M, M.G, staged, k, sref);
+        if (fin_lds) {
+            // each entry's rank goes to LDS (over its node id, which its staging thread
+            // holds), and the staging thread writes the row: it holds the item loaded above
+            rank_staged(M, M.G, staged, sref, [&](uint32_t rank, uint32_t p, float, uint32_t) {
+                M.n[p] = (int32_t)rank;
+            });
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t p = (uint32_t)(tid + u * kThreads);
+                if (p < staged && pos[u] < staged) {
+                    const uint32_t rank = (uint32_t)M.n[pos[u]];
+                    if (rank < k) {
+                        write_new_row(W, ra, rank, sc[u], fl[u], nd[u], ph[u]);
+                        uint64_t pfx = 0;
+                        uint32_t r = fl[u] >> 8;
+                        for (int t = ra.level() - 1; t >= 0; --t) {
+                            if (r >= (uint32_t)ra.rmax()) {   // rows of every depth are below rmax
+                                atomicOr(W.err, kErrBadNode);
+                                break;
+                            }
+                            const uint32_t h = Hs[t][r];
+                            pfx |= (uint64_t)(h & 255u) << (8 * t);
+                            r = h >> 8;
+                        }
+                        const bool leaf = (leafm >> u) & 1u;
+                        if (!leaf && !(W.norm == TCB_NORM_OPEN && nd[u] == -1)) atomicOr(W.err, kErrBadNode);
+                        int32_t item = it[u];
+                        asm volatile("" : "+v"(item));   // keeps its widening (and the wait) here
+                        write_final_row(F, T.L, W.Bmax, q, rank, pfx, fl[u] & 255u, ph[u],
+                                        leaf ? (int64_t)item : (int64_t)-1);
+                    }
+                }
+            }
+        } else if (fin) {
+            rank_staged(M, M.G, staged, sref, [&](uint32_t rank, uint32_t p, float s, uint32_t f) {
+                if (rank < k) write_finished_row(T, W, F, q, ra, rank, s, f, M.n[p], M.phi[p]);
+            });
+        } else {
+            rank_staged(M, M.G, staged, sref, [&](uint32_t rank, uint32_t p, float s, uint32_t f) {
+                if (rank < k) write_new_row(W, ra, rank, s, f, M.n[p], M.phi[p]);
+            });
+        }
     } else {
         // exact path (massive ties around b*): select the k-th key over the tiles'
         // buffers, gather exactly k survivors, rank them by counting
@@ -581,20 +747,23 @@ __device__ __forceinline__ void merge_request(const WaveDev &W, int q, const Req
             const uint32_t o = f2ord(M.s[p]), f = M.f[p];
             uint32_t r = 0u;
             for (uint32_t qq = 0; qq < n; ++qq) r += key_better(f2ord(M.s[qq]), M.f[qq], o, f) ? 1u : 0u;
-            write_new_row(W, ra, r, M.s[p], f, M.n[p], M.phi[p]);
+            if (fin) write_finished_row(T, W, F, q, ra, r, M.s[p], f, M.n[p], M.phi[p]);
+            else write_new_row(W, ra, r, M.s[p], f, M.n[p], M.phi[p]);
         }
     }
-    write_next_record(W, q, ra, rp, k);
+    if (fin) finish_request(T, W, F, q, ra, rp, rows, k);
+    else write_next_record(W, q, ra, rp, k);
 }
 
 __global__ __launch_bounds__(kThreads) void k_merge(TrieDev T, WaveDev W, int rp, StepReqs R) {
     __shared__ MergeSmem M;
     __shared__ SelSmem sel;
+    __shared__ uint32_t Hs[TCB_MAX_L - 1][kThreads];
     const int ql = blockIdx.x;
     if (ql >= R.n) return;
     const ReqArg ra = R.r[ql];
     if (!ra.step()) return;                            // carried over by k_tile
-    merge_request(W, R.q0 + ql, ra, rp, M, sel);
+    merge_request(T, W, R.fin, R.q0 + ql, ra, rp, M, sel, Hs);
 }
 
 // ---------------------------------------------------------------------- tile kernel
@@ -1027,8 +1196,17 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
             }
             __syncthreads();
             const uint32_t k = min(width, kept);
-            rank_staged(W, ra, *M, A.h2, kept, k, sref);
-            write_next_record(W, q, ra, rp, k);
+            if (finishes(T, R.fin, ra)) {
+                rank_staged(*M, A.h2, kept, sref, [&](uint32_t rank, uint32_t p, float s, uint32_t f) {
+                    if (rank < k) write_finished_row(T, W, R.fin, q, ra, rank, s, f, M->n[p], M->phi[p]);
+                });
+                finish_request(T, W, R.fin, q, ra, rp, rows, k);
+            } else {
+                rank_staged(*M, A.h2, kept, sref, [&](uint32_t rank, uint32_t p, float s, uint32_t f) {
+                    if (rank < k) write_new_row(W, ra, rank, s, f, M->n[p], M->phi[p]);
+                });
+                write_next_record(W, q, ra, rp, k);
+            }
             return true;
         }
         Cand *out = W.cand + reg;
@@ -1123,7 +1301,7 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
         const ReqArg ra = R.r[ql];
         if (!ra.step()) return;                        // carried over by tile_work
         __syncthreads();                               // the tile's records are visible to the workgroup
-        merge_request(W, R.q0 + ql, ra, rp, M, sel);   // a tile with no live row, or the exact path
+        merge_request(T, W, R.fin, R.q0 + ql, ra, rp, M, sel, nullptr);   // a tile with no live row, or the exact path
     } else {
         const int MT = W.MT;
         const int i8 = (int)(blockIdx.x >> 3);

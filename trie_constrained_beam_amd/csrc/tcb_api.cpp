@@ -382,7 +382,13 @@ static void step_done(tcb_beams *b) {
     b->rp ^= 1;
     b->steps++;
     for (auto &q : b->reqs)
-        if (q.used && q.level < b->L) q.level++;
+        if (q.used && q.level < b->L) {
+            q.level++;
+            if (q.level == b->L && b->fin.sids) {   // written out by the step itself: released
+                give_slots(b->free_ranges, q.base, q.width);
+                q = tcb_beams::Req{};
+            }
+        }
 }
 
 }  // extern "C"
@@ -399,6 +405,7 @@ static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out, int d
         tcb::StepReqs &R = out.back();
         R.q0 = q0;
         R.n = std::min(nr - q0, tcb::kArgReqs);
+        R.fin = b->fin;
         for (int i = 0; i < R.n; ++i) {
             const auto &rq = b->reqs[(size_t)(q0 + i)];
             const bool step = rq.used && rq.level < b->L;
@@ -548,6 +555,15 @@ tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, float 
     if ((d_node || d_score || d_phi || d_rows || d_level) && e == hipSuccess)
         e = tcb::launch_export(b->w, b->rp, d_node, d_score, d_phi, d_rows, d_level, s);
     if (e != hipSuccess) return hip_fail(e, "beam_export");
+    return TCB_OK;
+}
+
+tcb_status tcb_beams_set_finish_outputs(tcb_beams *b, uint8_t *d_sids, float *d_scores, int64_t *d_items,
+                                        int32_t *d_counts) {
+    if (!b) return set_error(TCB_E_ARG, "set_finish_outputs: null wave");
+    const int given = (d_sids != nullptr) + (d_scores != nullptr) + (d_items != nullptr) + (d_counts != nullptr);
+    if (given != 0 && given != 4) return set_error(TCB_E_ARG, "set_finish_outputs: give all four buffers or none");
+    b->fin = tcb::StepFin{d_sids, d_scores, d_items, d_counts};
     return TCB_OK;
 }
 

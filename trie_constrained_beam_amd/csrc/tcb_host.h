@@ -50,6 +50,8 @@ struct tcb_beams {
     float *d_fin_scores = nullptr;
     int64_t *d_fin_items = nullptr;
     int32_t *d_fin_counts = nullptr;
+    // where a step writes the requests it finishes (tcb_beams_set_finish_outputs); none if null
+    tcb::StepFin fin{};
     // optional kernel timing: 4 events per step (before the lm_head, before the tile kernel,
     // before the merge, after the merge)
     std::vector<hipEvent_t> events;

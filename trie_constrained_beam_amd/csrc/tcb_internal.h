@@ -107,6 +107,14 @@ static_assert(TCB_MAX_WIDTH < (1 << 13) && TCB_MAX_L <= 8, "ReqArg field widths"
 // depend on it).
 constexpr int kPrefilterFanout = 64;
 constexpr int kArgReqs = 400;      // requests per launch (the arguments stay under 4 KiB)
+// Where a step writes the requests it brings to depth L (row = request id), in the layouts
+// of the finalize outputs; sids == nullptr: nowhere (they wait for a finalize call).
+struct StepFin {
+    uint8_t *sids;                 // [R][Bmax][L]
+    float *scores;                 // [R][Bmax]
+    int64_t *items;                // [R][Bmax]
+    int32_t *counts;               // [R]
+};
 struct StepReqs {
     int32_t n;                     // request ids q0 .. q0 + n - 1
     int32_t q0;
@@ -114,8 +122,10 @@ struct StepReqs {
     int32_t pad;
     double inv_temp_d;             //                the same in float64
     uint64_t seed;                 //                noise seed
+    StepFin fin;
     ReqArg r[kArgReqs];
 };
+static_assert(sizeof(StepReqs) <= 4096 - 256, "kernel arguments stay under 4 KiB");
 
 // --------------------------------------------------------------------- launchers
 struct InitBatch {                 // admitted requests, passed by value
