@@ -153,12 +153,15 @@ def timed(run, steps, warmup):
     return time.perf_counter() - t0
 
 
-def merge_steps(trie, widths, L):
+def merge_steps(trie, widths, L, deferred=True):
     """Steps of a decode that launch the merge kernel: a step whose requests all have at
     most 64 possible rows (one tile; depth-t prefixes of the catalog, at most the beam
-    width) is merged inside the tile kernel."""
+    width) is merged inside the tile kernel; with back-to-back plain steps (deferred) every
+    other step's merge runs inside the next step's tile kernel, so only the last step's
+    merge is launched."""
     npd = trie.nodes_per_depth
-    return sum(1 for t in range(L) if max(min(w, 1 if t == 0 else npd[t]) for w in widths) > 64)
+    wide = [max(min(w, 1 if t == 0 else npd[t]) for w in widths) > 64 for t in range(L)]
+    return int(wide[L - 1]) if deferred else sum(wide)
 
 
 def main_leg(args, wl, cat, dev):
@@ -268,7 +271,7 @@ def lmhead_leg(args, dev, read_mode="dense"):
         decode(d % len(pool))
     head_ms, tile_ms, merge_ms, n_timed = beams.timing()
     beams.enable_timing(0)
-    n_merge = n_timed // L * merge_steps(trie, widths, L)
+    n_merge = n_timed // L * merge_steps(trie, widths, L, deferred=False)   # lm_head steps do not defer
     rows_x_steps = sum(rows_per_step)
     head_s = head_ms / 1e3 / n_timed                       # average head launch(es) per step
     res = {"workload": wl.name, "read_mode": read_mode, "rows_per_step": rows_per_step,

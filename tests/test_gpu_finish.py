@@ -227,3 +227,61 @@ def test_finish_under_timing_relaunches():
             beams.check()
         _same(res[0], res[1])
         assert int(res[0]["counts"][0]) == 512
+
+
+def _decode_exports(trie, widths, logits_fn, export_each, norm="children", temperature=0.0, bf16=False,
+                    repeat=0):
+    """A decode finalized at the end. Back-to-back steps leave each step's merge to the next
+    step's tile kernel; an export after every step (export_each) makes every merge run in
+    the merge kernel instead. Returns the finalize result and the state after every step."""
+    S = int(sum(widths))
+    beams = Beams(trie, S, len(widths), max(widths), norm=norm)
+    if repeat:
+        beams.enable_timing(trie.L, repeat)
+    ids, bases = beams.init(np.asarray(widths, dtype=np.int32))
+    states = []
+    for t in range(trie.L):
+        host = np.zeros((S, 256), dtype=np.float32)
+        for i, (w, b) in enumerate(zip(widths, bases)):
+            host[b:b + w] = logits_fn(t, i, w)
+        x = torch.from_numpy(host).cuda()
+        beams.step(x.to(torch.bfloat16) if bf16 else x, temperature=temperature, seed=1000 + t)
+        if export_each:
+            states.append({k: v.cpu().numpy() for k, v in beams.export().items()})
+    if not export_each:
+        states.append({k: v.cpu().numpy() for k, v in beams.export().items()})
+    res = beams.finalize(ids)
+    beams.check()
+    return res, states
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_deferred_merge_matches_merge_kernel(name):
+    """Each step's merge done by the next step's tile kernel (every tile of a request
+    merging it and keeping its own 64 rows) against the merge kernel: the final beams and
+    the final state (rows, keys, nodes, back-pointers) must be bitwise equal."""
+    cat_args, widths, seed, norm, temp, bf16 = CASES[name]
+    trie = Trie(synth.catalog(*cat_args), device="cuda")
+    fn = _rowkeyed(seed)
+    a, sa = _decode_exports(trie, widths, fn, False, norm=norm, temperature=temp, bf16=bf16)
+    b, sb = _decode_exports(trie, widths, fn, True, norm=norm, temperature=temp, bf16=bf16)
+    _same(a, b)
+    fa, fb = sa[-1], sb[-1]
+    assert np.array_equal(fa["rows"], fb["rows"]) and np.array_equal(fa["level"], fb["level"])
+    assert np.array_equal(fa["hist"], fb["hist"])
+    for rid, base in enumerate(np.cumsum([0] + widths[:-1])):
+        k = int(fa["rows"][rid])
+        for key in ("node", "score", "phi", "parent_slot"):
+            assert np.array_equal(fa[key][base:base + k], fb[key][base:base + k]), (rid, key)
+    if name == "merge_kernel_onchip_walk":
+        c, _ = _decode_exports(trie, widths, fn, False, repeat=3)   # relaunched kernels: the same beams
+        _same(a, c)
+
+
+def test_deferred_merge_under_exact_ties():
+    a_, b_, c_ = np.meshgrid(np.arange(256), np.arange(256), np.arange(4), indexing="ij")
+    trie = Trie(np.stack([a_.ravel(), b_.ravel(), c_.ravel()], axis=1).astype(np.uint8), device="cuda")
+    zero = lambda t, i, w: np.zeros((w, 256), dtype=np.float32)
+    a, _ = _decode_exports(trie, [300, 64, 7], zero, False)
+    b, _ = _decode_exports(trie, [300, 64, 7], zero, True)
+    _same(a, b)

@@ -524,12 +524,16 @@ __device__ __forceinline__ void finish_request(const TrieDev &T, const WaveDev &
 // of the candidate records grouped by bin, with its cumulative kept counts in tcum.
 // Hs (or nullptr): LDS for the back-pointers of up to kThreads rows when the request finishes
 // in this step, so that its beams' codes are walked on chip.
+// out.row(rank, s, f, node, phi) takes each new row (rank < k) and out.done(k) the count,
+// except for a finishing request, whose rows and records are written here.
+template <class Out>
 __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W, const StepFin &F, int q,
                                               const ReqArg ra, int rp, MergeSmem &M, SelSmem &sel,
-                                              uint32_t (*Hs)[kThreads]) {
+                                              uint32_t (*Hs)[kThreads], const Out &out) {
     const int tid = threadIdx.x;
     const int MT = W.MT, CAPT = W.CAPT;
-    const uint16_t *tc = W.tcum + (size_t)q * MT * kBins;
+    const int cpar = ra.level() & 1;                  // the buffers the step's tiles wrote
+    const uint16_t *tc = W.tcum[cpar] + (size_t)q * MT * kBins;
     const size_t reg0 = (size_t)q * MT * CAPT;
     // the live-row count (how many tiles wrote counts), the best row's score and the
     // tiles' counts are all loaded at once: the counts of every tile the request could
@@ -632,7 +636,7 @@ __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W
             const uint32_t p = (uint32_t)(tid + u * kThreads);
             nd[u] = 0;
             if (p < staged) {
-                const Cand c = W.cand[cand_index(p)];
+                const Cand c = W.cand[cpar][cand_index(p)];
                 sc[u] = c.s;
                 fl[u] = c.f;
                 nd[u] = c.n;
@@ -713,7 +717,7 @@ __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W
             });
         } else {
             rank_staged(M, M.G, staged, sref, [&](uint32_t rank, uint32_t p, float s, uint32_t f) {
-                if (rank < k) write_new_row(W, ra, rank, s, f, M.n[p], M.phi[p]);
+                if (rank < k) out.row(rank, s, f, M.n[p], M.phi[p]);
             });
         }
     } else {
@@ -722,14 +726,14 @@ __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W
         if (tid == 0) atomicOr(W.err, kInfoMergeSpill);
         auto each = [&](auto fn) {
             for (uint32_t p = tid; p < staged; p += kThreads) {
-                const Cand c = W.cand[cand_index(p)];
+                const Cand c = W.cand[cpar][cand_index(p)];
                 fn(f2ord(c.s), c.f);
             }
         };
         uint32_t o_star, f_star;
         block_select<kThreads>(each, k, sel, o_star, f_star, W.err);
         for (uint32_t p = tid; p < staged; p += kThreads) {
-            const Cand c = W.cand[cand_index(p)];
+            const Cand c = W.cand[cpar][cand_index(p)];
             if (key_le(f2ord(c.s), c.f, o_star, f_star)) {
                 const uint32_t pos = atomicAdd(&M.cnt, 1u);
                 if (pos < (uint32_t)kMergeCap) {
@@ -748,12 +752,55 @@ __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W
             uint32_t r = 0u;
             for (uint32_t qq = 0; qq < n; ++qq) r += key_better(f2ord(M.s[qq]), M.f[qq], o, f) ? 1u : 0u;
             if (fin) write_finished_row(T, W, F, q, ra, r, M.s[p], f, M.n[p], M.phi[p]);
-            else write_new_row(W, ra, r, M.s[p], f, M.n[p], M.phi[p]);
+            else out.row(r, M.s[p], f, M.n[p], M.phi[p]);
         }
     }
     if (fin) finish_request(T, W, F, q, ra, rp, rows, k);
-    else write_next_record(W, q, ra, rp, k);
+    else out.done(k);
 }
+
+// Where k_merge puts a request's new rows: the row buffers and the next record.
+struct RowsToMemory {
+    const WaveDev &W;
+    ReqArg ra;
+    int q, rp;
+    __device__ void row(uint32_t rank, float s, uint32_t f, int32_t n, float phi) const {
+        write_new_row(W, ra, rank, s, f, n, phi);
+    }
+    __device__ void done(uint32_t k) const { write_next_record(W, q, ra, rp, k); }
+};
+
+// Rows of one tile of the next step, taken from the previous step's merge (FuseRows).
+struct FuseRows {
+    int32_t node[kTileRows];
+    float score[kTileRows], phi[kTileRows];
+    float sref;                                       // the best new row's key
+};
+
+// The previous step's merge inside a tile of the next step: every tile of the request
+// merges, writes the rows of its own window [64 tile, 64 tile + 64) to the row buffers and
+// keeps them in LDS; tile 0 writes the record.
+struct RowsToTile {
+    const WaveDev &W;
+    ReqArg ra;                                        // the request at the merged step
+    int q, rp, tile;
+    FuseRows &Z;
+    uint32_t &k_out;
+    __device__ void row(uint32_t rank, float s, uint32_t f, int32_t n, float phi) const {
+        const uint32_t i = rank - (uint32_t)(tile * kTileRows);
+        if (i < (uint32_t)kTileRows) {
+            Z.node[i] = n;
+            Z.score[i] = s;
+            Z.phi[i] = phi;
+            write_new_row(W, ra, rank, s, f, n, phi);
+        }
+        if (rank == 0u) Z.sref = s;
+    }
+    __device__ void done(uint32_t k) const {
+        k_out = k;
+        if (tile == 0) write_next_record(W, q, ra, rp, k);
+    }
+};
 
 __global__ __launch_bounds__(kThreads) void k_merge(TrieDev T, WaveDev W, int rp, StepReqs R) {
     __shared__ MergeSmem M;
@@ -763,7 +810,7 @@ __global__ __launch_bounds__(kThreads) void k_merge(TrieDev T, WaveDev W, int rp
     if (ql >= R.n) return;
     const ReqArg ra = R.r[ql];
     if (!ra.step()) return;                            // carried over by k_tile
-    merge_request(T, W, R.fin, R.q0 + ql, ra, rp, M, sel, Hs);
+    merge_request(T, W, R.fin, R.q0 + ql, ra, rp, M, sel, Hs, RowsToMemory{W, ra, R.q0 + ql, rp});
 }
 
 // ---------------------------------------------------------------------- tile kernel
@@ -862,10 +909,12 @@ __device__ __forceinline__ double row16_max_d(double v) {
 // request's only tile) the kept candidates go to LDS and the tile ranks them and writes
 // the request's new rows itself, returning true; it returns false where k_merge's work
 // (from the records in memory) is still to do.
-template <int DT, int NORM, bool VEC, bool SAMPLE, bool MERGE>
+// With FUSE, a request whose previous step left its merge pending does that merge first
+// (M and Z: its staging and this tile's rows).
+template <int DT, int NORM, bool VEC, bool SAMPLE, bool MERGE, bool FUSE>
 __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, int rp, const StepReqs &R,
                                           const void *__restrict__ logits, int64_t ld, int ql, int tile,
-                                          TileSmem &A, SelSmem &sel, MergeSmem *M) {
+                                          TileSmem &A, SelSmem &sel, MergeSmem *M, FuseRows *Z) {
     constexpr int CH = Lay<DT>::CH, CW = Lay<DT>::CW, SPAN = 256 / CH;
     static_assert(CH * CW == kElems && (SPAN / CW) * 8 <= 256, "row layout");
 
@@ -898,8 +947,6 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
     //    request's first step starts from its initial state (one row: the root, score 0),
     //    which is not read back, so the step needs no earlier initialising kernel
     const bool fresh = level == 0;
-    const int rows = fresh ? 1 : W.rec[rp][q].rows;
-    const float sref = fresh ? 0.0f : W.score[cp][base];   // best row of the request
     const bool in_range = r < ra.rmax();
     int32_t nd = -1;
     float sr = 0.0f, pr = 0.0f;                        // the row's key and (sampled) log-probability
@@ -909,12 +956,33 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
     // at depths with few children per row the logits wait for the trie and only the
     // 16-byte pieces holding a child are read (the rest is masked off either way)
     const bool gather = VEC && ra.gather();
-    if (in_range) {
-        const int slot = base + r;
-        nd = fresh ? 0 : W.node[cp][slot];
-        sr = fresh ? 0.0f : W.score[cp][slot];
-        if constexpr (SAMPLE) pr = fresh ? 0.0f : W.phi[cp][slot];
-        if (!gather) load_row<DT, VEC>(logits, ld, slot, j, V, x);
+    int rows;
+    float sref;                                       // best row of the request
+    if (FUSE && ra.pending()) {
+        // the previous step's merge: a row's logits do not depend on it (they are indexed
+        // by slot), so they are issued first; the row state then comes from the merge
+        if (in_range && !gather) load_row<DT, VEC>(logits, ld, base + r, j, V, x);
+        uint32_t k = 0u;
+        const ReqArg pa = ra.prev_step();
+        merge_request(T, W, StepFin{}, q, pa, rp ^ 1, *M, sel, nullptr, RowsToTile{W, pa, q, rp ^ 1, tile, *Z, k});
+        __syncthreads();
+        rows = (int)k;
+        sref = Z->sref;
+        if (r < rows) {
+            nd = Z->node[rt];
+            sr = Z->score[rt];
+            if constexpr (SAMPLE) pr = Z->phi[rt];
+        }
+    } else {
+        rows = fresh ? 1 : W.rec[rp][q].rows;
+        sref = fresh ? 0.0f : W.score[cp][base];
+        if (in_range) {
+            const int slot = base + r;
+            nd = fresh ? 0 : W.node[cp][slot];
+            sr = fresh ? 0.0f : W.score[cp][slot];
+            if constexpr (SAMPLE) pr = fresh ? 0.0f : W.phi[cp][slot];
+            if (!gather) load_row<DT, VEC>(logits, ld, slot, j, V, x);
+        }
     }
     if (tile * kTileRows >= rows) return false;              // a tile with no live row
     const bool live = r < rows;
@@ -1209,7 +1277,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
             }
             return true;
         }
-        Cand *out = W.cand + reg;
+        Cand *out = W.cand[level & 1] + reg;
 #pragma unroll
         for (int e = 0; e < kElems; ++e) {
             if (bn[e] <= bt) {
@@ -1227,7 +1295,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
                 }
             }
         }
-        W.tcum[((size_t)q * MT + tile) * kBins + tid] = (uint16_t)min(C, kept);
+        W.tcum[level & 1][((size_t)q * MT + tile) * kBins + tid] = (uint16_t)min(C, kept);
     } else {
         // exact path: keep exactly the tile's top min(n, #candidates)
         if (tid == 0) atomicOr(W.err, kInfoTileExact);
@@ -1273,13 +1341,13 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
                     c.n = node_of(e);
                     if constexpr (SAMPLE) c.phi = ph[e];
                     else c.phi = s;
-                    W.cand[reg + dst] = c;
+                    W.cand[level & 1][reg + dst] = c;
                 } else {
                     atomicOr(W.err, kErrInternal);
                 }
             }
         }
-        W.tcum[((size_t)q * MT + tile) * kBins + tid] = (uint16_t)Cx;
+        W.tcum[level & 1][((size_t)q * MT + tile) * kBins + tid] = (uint16_t)Cx;
     }
     return false;
 }
@@ -1288,7 +1356,8 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
 // workgroup per request does its tile and then, after a barrier, its merge from the
 // records it has just written: no second kernel. Otherwise the tiles of a request are
 // dealt to one XCD (workgroup b -> XCD b mod 8) and k_merge follows.
-template <int DT, int NORM, bool VEC, bool SAMPLE, bool MERGE>
+// FUSE: requests whose previous merge is pending do it first, in every one of their tiles.
+template <int DT, int NORM, bool VEC, bool SAMPLE, bool MERGE, bool FUSE>
 __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp, StepReqs R,
                                                    const void *__restrict__ logits, int64_t ld) {
     __shared__ TileSmem A;
@@ -1297,18 +1366,25 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
         __shared__ MergeSmem M;
         const int ql = (int)blockIdx.x;
         if (ql >= R.n) return;
-        if (tile_work<DT, NORM, VEC, SAMPLE, true>(T, W, rp, R, logits, ld, ql, 0, A, sel, &M)) return;
+        if (tile_work<DT, NORM, VEC, SAMPLE, true, false>(T, W, rp, R, logits, ld, ql, 0, A, sel, &M, nullptr)) return;
         const ReqArg ra = R.r[ql];
         if (!ra.step()) return;                        // carried over by tile_work
         __syncthreads();                               // the tile's records are visible to the workgroup
-        merge_request(T, W, R.fin, R.q0 + ql, ra, rp, M, sel, nullptr);   // a tile with no live row, or the exact path
+        merge_request(T, W, R.fin, R.q0 + ql, ra, rp, M, sel, nullptr,     // a tile with no live row, or the exact path
+                      RowsToMemory{W, ra, R.q0 + ql, rp});
     } else {
         const int MT = W.MT;
         const int i8 = (int)(blockIdx.x >> 3);
         const int ql = (int)(blockIdx.x & 7u) + 8 * (i8 / MT);  // all tiles of a request on one XCD
         const int tile = i8 % MT;
         if (ql >= R.n) return;
-        tile_work<DT, NORM, VEC, SAMPLE, false>(T, W, rp, R, logits, ld, ql, tile, A, sel, nullptr);
+        if constexpr (FUSE) {
+            __shared__ MergeSmem M;
+            __shared__ FuseRows Z;
+            tile_work<DT, NORM, VEC, SAMPLE, false, true>(T, W, rp, R, logits, ld, ql, tile, A, sel, &M, &Z);
+        } else {
+            tile_work<DT, NORM, VEC, SAMPLE, false, false>(T, W, rp, R, logits, ld, ql, tile, A, sel, nullptr, nullptr);
+        }
     }
 }
 
@@ -1433,20 +1509,23 @@ hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s) {
 
 template <int DT, int NORM, bool VEC, bool SAMPLE>
 static void launch_tile_t(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                          int64_t ld, bool merge, hipStream_t s) {
-    if (merge) {
-        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, true>), dim3(R.n), dim3(kThreads), 0, s, t, w, rp, R,
-                           logits, ld);
+                          int64_t ld, int mode, hipStream_t s) {
+    const int groups = (R.n + 7) / 8;
+    if (mode == 1) {
+        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, true, false>), dim3(R.n), dim3(kThreads), 0, s, t, w, rp,
+                           R, logits, ld);
+    } else if (mode == 2) {
+        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, false, true>), dim3(8 * groups * w.MT), dim3(kThreads), 0,
+                           s, t, w, rp, R, logits, ld);
     } else {
-        const int groups = (R.n + 7) / 8;
-        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, false>), dim3(8 * groups * w.MT), dim3(kThreads), 0, s, t,
-                           w, rp, R, logits, ld);
+        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, false, false>), dim3(8 * groups * w.MT), dim3(kThreads), 0,
+                           s, t, w, rp, R, logits, ld);
     }
 }
 
 template <int DT, bool SAMPLE, bool VEC>
 static void launch_tile_v(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                          int64_t ld, bool merge, hipStream_t s) {
+                          int64_t ld, int merge, hipStream_t s) {
     switch (w.norm) {
     case TCB_NORM_LEVEL: launch_tile_t<DT, TCB_NORM_LEVEL, VEC, SAMPLE>(t, w, rp, R, logits, ld, merge, s); break;
     case TCB_NORM_OPEN: launch_tile_t<DT, TCB_NORM_OPEN, VEC, SAMPLE>(t, w, rp, R, logits, ld, merge, s); break;
@@ -1456,7 +1535,7 @@ static void launch_tile_v(const TrieDev &t, const WaveDev &w, int rp, const Step
 
 template <int DT, bool SAMPLE>
 static void launch_tile_dt(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                           int64_t ld, bool vec, bool merge, hipStream_t s) {
+                           int64_t ld, bool vec, int merge, hipStream_t s) {
     if (vec) launch_tile_v<DT, SAMPLE, true>(t, w, rp, R, logits, ld, merge, s);
     else launch_tile_v<DT, SAMPLE, false>(t, w, rp, R, logits, ld, merge, s);
 }
@@ -1468,11 +1547,12 @@ bool tile_merges(const StepReqs &R) {
 }
 
 hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                       int64_t ld, int dtype, bool sampled, hipStream_t s) {
+                       int64_t ld, int dtype, bool sampled, hipStream_t s, bool fuse) {
     if (R.n <= 0) return hipSuccess;
     // 16-byte row pieces: ld a multiple of 4 (fp32) or 8 (bf16) elements, 16-byte base
     const bool vec = t.V == 256 && (ld % (dtype == TCB_F32 ? 4 : 8)) == 0 && ((uintptr_t)logits % 16) == 0;
-    const bool merge = tile_merges(R);
+    // 1: every request merged inside its only tile; 2: pending merges first; 0: plain
+    const int merge = fuse ? 2 : tile_merges(R) ? 1 : 0;
     if (dtype == TCB_F32) {
         if (sampled) launch_tile_dt<TCB_F32, true>(t, w, rp, R, logits, ld, vec, merge, s);
         else launch_tile_dt<TCB_F32, false>(t, w, rp, R, logits, ld, vec, merge, s);

@@ -62,8 +62,8 @@ Layout make_layout(int L, int S, int R, int Bmax) {
     l.rec[0] = take(r * sizeof(tcb::ReqRec));
     l.rec[1] = take(r * sizeof(tcb::ReqRec));
     const size_t ncand = r * (size_t)l.MT * (size_t)l.CAPT;
-    l.cand = take(ncand * sizeof(tcb::Cand));
-    l.tcum = take(r * (size_t)l.MT * tcb::kBins * 2);
+    l.cand = take(2 * ncand * sizeof(tcb::Cand));
+    l.tcum = take(2 * r * (size_t)l.MT * tcb::kBins * 2);
     l.lmx = take(s * 256 * 4);
     l.err = take(256);
     l.fin_sids = take(r * (size_t)Bmax * (size_t)L);
@@ -160,9 +160,24 @@ tcb_status flush_init(tcb_beams *b, hipStream_t s) {
     return TCB_OK;
 }
 
+// Launches a merge left for the next step's tile kernel as k_merge (before anything other
+// than a step reads request state).
+tcb_status flush_merge(tcb_beams *b, hipStream_t s) {
+    if (!b->merge_pending) return TCB_OK;
+    for (const auto &R : b->deferred) {
+        hipError_t e = tcb::launch_merge(b->tdev, b->w, b->deferred_rp, R, s);
+        if (e != hipSuccess) return hip_fail(e, "merge launch");
+    }
+    for (auto &q : b->reqs) q.pending = false;
+    b->merge_pending = false;
+    return TCB_OK;
+}
+
 tcb_status run_finalize(tcb_beams *b, int32_t n, const int32_t *req_ids, uint8_t *sids,
                         float *scores, int64_t *items, int32_t *counts, hipStream_t s) {
-    const tcb_status st = flush_init(b, s);
+    tcb_status st = flush_merge(b, s);
+    if (st) return st;
+    st = flush_init(b, s);
     if (st) return st;
     for (int i0 = 0; i0 < n; i0 += tcb::FinBatch::kMax) {
         tcb::FinBatch fb{};
@@ -308,8 +323,14 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
     w.hist = (uint32_t *)(ws + l.hist);
     w.rec[0] = (tcb::ReqRec *)(ws + l.rec[0]);
     w.rec[1] = (tcb::ReqRec *)(ws + l.rec[1]);
-    w.cand = (tcb::Cand *)(ws + l.cand);
-    w.tcum = (uint16_t *)(ws + l.tcum);
+    {
+        const size_t ncand = (size_t)max_requests * (size_t)l.MT * (size_t)l.CAPT;
+        const size_t ntc = (size_t)max_requests * (size_t)l.MT * tcb::kBins;
+        w.cand[0] = (tcb::Cand *)(ws + l.cand);
+        w.cand[1] = w.cand[0] + ncand;
+        w.tcum[0] = (uint16_t *)(ws + l.tcum);
+        w.tcum[1] = w.tcum[0] + ntc;
+    }
     w.lmx = (float *)(ws + l.lmx);
     w.err = (uint32_t *)(ws + l.err);
     w.S = max_slots;
@@ -421,13 +442,16 @@ static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out, int d
             // gather only the logit sectors that hold a child where rows have few children
             const bool by_level = b->read_mode == TCB_READ_GATHER || (b->read_mode == TCB_READ_AUTO &&
                                                                       (b->gather_levels[dt_index] >> level & 1u));
-            const bool gather = !open && b->w.norm == TCB_NORM_CHILDREN && step && dt_index < 2 && by_level;
+            // a pending merge comes first in the tile kernel: rows are then read whole, issued
+            // before the merge, as their pieces would wait for the merged rows' nodes
+            const bool pend = step && rq.pending;
+            const bool gather = !open && b->w.norm == TCB_NORM_CHILDREN && step && dt_index < 2 && by_level && !pend;
             // an lm_head step computes only the children's pieces where rows have few children;
             // its tile kernel then reads only those pieces
             const bool sparse = head && !open && b->w.norm == TCB_NORM_CHILDREN && step &&
                                 (b->read_mode == TCB_READ_GATHER ||
                                  (b->read_mode == TCB_READ_AUTO && (b->sparse_head_levels >> level & 1u)));
-            R.r[i].base_flags = rq.base | (gather || sparse ? 1 << 24 : 0) | (sparse ? 1 << 25 : 0);
+            R.r[i].base_flags = rq.base | (gather || sparse ? 1 << 24 : 0) | (sparse ? 1 << 25 : 0) | (pend ? 1 << 26 : 0);
             R.r[i].bits = width | rmax << 13 | level << 26 | pre << 29 | (step ? 1u : 0u) << 30 | (level & 1u) << 31;
         }
     }
@@ -440,10 +464,18 @@ static int gather_index(const void *logits, int64_t ld, int32_t dtype, int V) {
     return vec ? (dtype == TCB_F32 ? 0 : 1) : 2;
 }
 
+// can_defer: a step whose tile kernel can take a pending merge (tcb_beam_step and
+// tcb_beam_step_sampled); it may leave its own merge to the next such step.
 template <class HeadLaunch, class TileLaunch>
 static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLaunch tile, int dt_index,
-                           double temperature = 0.0, uint64_t seed = 0, bool sparse_head = false) {
+                           double temperature = 0.0, uint64_t seed = 0, bool sparse_head = false,
+                           bool can_defer = false) {
     static thread_local std::vector<tcb::StepReqs> args;
+    if (!can_defer) {
+        const tcb_status st = flush_merge(b, s);
+        if (st) return st;
+    }
+    const bool fuse = b->merge_pending;                // this step's tile kernel does those merges
     step_args(b, args, dt_index, sparse_head);
     for (auto &R : args) {
         R.inv_temp_d = temperature > 0.0 ? 1.0 / temperature : 0.0;
@@ -461,12 +493,31 @@ static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLau
     if (e != hipSuccess) return hip_fail(e, "lm_head kernel launch");
     if (timed) e = hipEventRecord(ev[1], s);
     for (int i = 0; i < rep && e == hipSuccess; ++i)
-        for (size_t c = 0; c < args.size() && e == hipSuccess; ++c) e = tile(args[c]);
+        for (size_t c = 0; c < args.size() && e == hipSuccess; ++c) e = tile(args[c], fuse);
     if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
+    if (fuse) {
+        for (auto &q : b->reqs) q.pending = false;
+        b->merge_pending = false;
+    }
+    // defer this step's merge to the next step's tile kernel unless a request finishes now
+    // or the tile kernel merged every request itself
+    bool defer = can_defer;
+    for (const auto &q : b->reqs)
+        if (q.used && q.level < b->L && q.level + 1 >= b->L) defer = false;
+    for (const auto &R : args)
+        if (tcb::tile_merges(R)) defer = false;
     if (timed) e = hipEventRecord(ev[2], s);
-    for (int i = 0; i < rep && e == hipSuccess; ++i)
-        for (size_t c = 0; c < args.size() && e == hipSuccess; ++c)
-            e = tcb::launch_merge(b->tdev, b->w, b->rp, args[c], s);
+    if (defer) {
+        b->deferred = args;
+        b->deferred_rp = b->rp;
+        for (auto &q : b->reqs)
+            if (q.used && q.level < b->L) q.pending = true;
+        b->merge_pending = true;
+    } else {
+        for (int i = 0; i < rep && e == hipSuccess; ++i)
+            for (size_t c = 0; c < args.size() && e == hipSuccess; ++c)
+                e = tcb::launch_merge(b->tdev, b->w, b->rp, args[c], s);
+    }
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     if (timed) {
         e = hipEventRecord(ev[3], s);
@@ -488,8 +539,10 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
     hipStream_t s = (hipStream_t)stream;
     return run_step(
         b, s, [](const tcb::StepReqs &) { return hipSuccess; },
-        [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, false, s); },
-        gather_index(d_logits, ld, dtype, b->V));
+        [&](const tcb::StepReqs &R, bool fuse) {
+            return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, false, s, fuse);
+        },
+        gather_index(d_logits, ld, dtype, b->V), 0.0, 0, false, true);
 }
 
 tcb_status tcb_beam_step_sampled(tcb_beams *b, const void *d_logits, int64_t ld, int32_t dtype, float temperature,
@@ -504,8 +557,10 @@ tcb_status tcb_beam_step_sampled(tcb_beams *b, const void *d_logits, int64_t ld,
     hipStream_t s = (hipStream_t)stream;
     return run_step(
         b, s, [](const tcb::StepReqs &) { return hipSuccess; },
-        [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, true, s); },
-        gather_index(d_logits, ld, dtype, b->V), (double)temperature, seed);
+        [&](const tcb::StepReqs &R, bool fuse) {
+            return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, true, s, fuse);
+        },
+        gather_index(d_logits, ld, dtype, b->V), (double)temperature, seed, false, true);
 }
 
 tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_hidden, int32_t H,
@@ -536,7 +591,9 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
                                               sparse_rows, s);
             return e;
         },
-        [&](const tcb::StepReqs &R) { return tcb::launch_tile(b->tdev, b->w, b->rp, R, b->w.lmx, 256, TCB_F32, false, s); },
+        [&](const tcb::StepReqs &R, bool fuse) {
+            return tcb::launch_tile(b->tdev, b->w, b->rp, R, b->w.lmx, 256, TCB_F32, false, s, fuse);
+        },
         2, 0.0, 0, H <= 4096);
 }
 
@@ -544,7 +601,9 @@ tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, float 
                            uint32_t *d_hist, int32_t *d_rows, int32_t *d_level, void *stream) {
     if (!b) return set_error(TCB_E_ARG, "beam_export: null wave");
     hipStream_t s = (hipStream_t)stream;
-    const tcb_status st = flush_init(b, s);
+    tcb_status st = flush_merge(b, s);
+    if (st) return st;
+    st = flush_init(b, s);
     if (st) return st;
     const size_t S = (size_t)b->w.S;
     hipError_t e = hipSuccess;

@@ -27,6 +27,7 @@ struct tcb_trie {
 struct tcb_beams {
     struct Req {
         bool used = false;
+        bool pending = false;              // its last step's merge is deferred to its next step
         int32_t base = 0, width = 0, level = 0;
     };
     tcb::TrieDev tdev{};
@@ -52,6 +53,11 @@ struct tcb_beams {
     int32_t *d_fin_counts = nullptr;
     // where a step writes the requests it finishes (tcb_beams_set_finish_outputs); none if null
     tcb::StepFin fin{};
+    // a step's merge deferred into the next step's tile kernel: its launch arguments and
+    // request-record buffer, launched as k_merge instead if something else reads state first
+    bool merge_pending = false;
+    int deferred_rp = 0;
+    std::vector<tcb::StepReqs> deferred;
     // optional kernel timing: 4 events per step (before the lm_head, before the tile kernel,
     // before the merge, after the merge)
     std::vector<hipEvent_t> events;

@@ -78,8 +78,11 @@ struct WaveDev {
     int32_t *parent_slot;          // [S] parent slot at the request's last step
     uint32_t *hist;                // [L][S] back-pointer (r << 8) | c per level
     ReqRec *rec[2];                // [R] request records; a step reads one, writes the other
-    Cand *cand;                    // [R][MT][CAPT] kept candidates of every tile
-    uint16_t *tcum;                // [R][MT][kBins] cumulative kept count of each tile by bin
+    // kept candidates of every tile and their cumulative counts by bin, one buffer per step
+    // parity (level & 1 of the step that wrote them), so that a step's tiles can merge the
+    // previous step's candidates while writing their own
+    Cand *cand[2];                 // [R][MT][CAPT]
+    uint16_t *tcum[2];             // [R][MT][kBins]
     float *lmx;                    // [S][256] logits computed by the SID-range lm_head
     uint32_t *err;                 // sticky error / info bits
     int32_t S, R, MT, CAPT, Bmax, norm, validate, pad;
@@ -89,17 +92,25 @@ struct WaveDev {
 // What the host knows of every request it steps, passed by value so a kernel's first
 // loads need no device-side lookup. Only the live-row count stays on the device.
 struct ReqArg {
-    int32_t base_flags;            // first slot (< 2^24) | gather << 24 | sparse head << 25
+    int32_t base_flags;            // first slot (< 2^24) | gather << 24 | sparse head << 25 | merge pending << 26
     uint32_t bits;                 // width | rmax << 13 | level << 26 | pre << 29 | step << 30 | par << 31
     __host__ __device__ int base() const { return base_flags & 0xFFFFFF; }
     __host__ __device__ bool gather() const { return (base_flags >> 24) & 1; }        // children's sectors only
     __host__ __device__ bool sparse_head() const { return (base_flags >> 25) & 1; }   // lm_head: children's pieces only
+    // the request's previous step left its merge to this step's tile kernel
+    __host__ __device__ bool pending() const { return (base_flags >> 26) & 1; }
     __host__ __device__ int width() const { return (int)(bits & 0x1FFFu); }
     __host__ __device__ int rmax() const { return (int)((bits >> 13) & 0x1FFFu); }   // bound on live rows
     __host__ __device__ int level() const { return (int)((bits >> 26) & 0x7u); }
     __host__ __device__ bool prefilter() const { return (bits >> 29) & 1u; }        // sample-bound pruning
     __host__ __device__ bool step() const { return (bits >> 30) & 1u; }
     __host__ __device__ int par() const { return (int)(bits >> 31); }                // node/score buffer
+    // the same request as its previous step saw it (one level up, the other buffer)
+    __host__ __device__ ReqArg prev_step() const {
+        ReqArg p = *this;
+        p.bits = (bits & ~((7u << 26) | (1u << 31))) | ((uint32_t)(level() - 1) << 26) | ((uint32_t)(par() ^ 1) << 31);
+        return p;
+    }
 };
 static_assert(TCB_MAX_WIDTH < (1 << 13) && TCB_MAX_L <= 8, "ReqArg field widths");
 // The tile kernel's prefilter pays off only where rows have many children: it is used
@@ -146,8 +157,10 @@ hipError_t launch_clear_wave(const WaveDev &w, hipStream_t s);
 hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s);
 // A step is the tile kernel followed by the per-request merge kernel; with the SID-range
 // lm_head, the lm_head kernel first writes the logits to WaveDev::lmx.
+// fuse: some request of R has pending() set; the tile kernel then first does that request's
+// previous merge (redundantly in each of its tiles, each keeping its own 64 rows)
 hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                       int64_t ld, int dtype, bool sampled, hipStream_t s);
+                       int64_t ld, int dtype, bool sampled, hipStream_t s, bool fuse = false);
 // lm_head over only the 16-byte pieces (4 codes) of each row that hold a child, for the
 // requests whose argument carries the sparse-head flag; max_rows bounds their live rows.
 hipError_t launch_lmhead_sparse(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
