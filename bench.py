@@ -271,7 +271,7 @@ def lmhead_leg(args, dev, read_mode="dense"):
         decode(d % len(pool))
     head_ms, tile_ms, merge_ms, n_timed = beams.timing()
     beams.enable_timing(0)
-    n_merge = n_timed // L * merge_steps(trie, widths, L, deferred=False)   # lm_head steps do not defer
+    n_merge = n_timed // L * merge_steps(trie, widths, L)
     rows_x_steps = sum(rows_per_step)
     head_s = head_ms / 1e3 / n_timed                       # average head launch(es) per step
     res = {"workload": wl.name, "read_mode": read_mode, "rows_per_step": rows_per_step,

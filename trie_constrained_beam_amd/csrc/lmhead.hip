@@ -141,7 +141,9 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
             stage_step(ra, rb);
         }
     }
-    const int rows = level == 0 ? 1 : W.rec[rp][R.q0 + ql].rows;   // a first step: the root only
+    // a first step: the root only; a pending merge (done by the tile kernel that follows):
+    // every row the request can have
+    const int rows = level == 0 ? 1 : R.r[ql].pending() ? rows_bound : W.rec[rp][R.q0 + ql].rows;
     // partial blocks of the four waves, added in a fixed order; wave w finishes row block w
 #pragma unroll
     for (int a = 0; a < 4; ++a)

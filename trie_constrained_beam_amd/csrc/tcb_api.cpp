@@ -464,14 +464,16 @@ static int gather_index(const void *logits, int64_t ld, int32_t dtype, int V) {
     return vec ? (dtype == TCB_F32 ? 0 : 1) : 2;
 }
 
-// can_defer: a step whose tile kernel can take a pending merge (tcb_beam_step and
-// tcb_beam_step_sampled); it may leave its own merge to the next such step.
+// fuse_ok: this step's kernels can take a pending merge (its tile kernel does it first; no
+// kernel before it needs the merged rows); otherwise the pending merge is launched first. A
+// step may leave its own merge to the next step.
 template <class HeadLaunch, class TileLaunch>
 static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLaunch tile, int dt_index,
                            double temperature = 0.0, uint64_t seed = 0, bool sparse_head = false,
-                           bool can_defer = false) {
+                           bool fuse_ok = true) {
     static thread_local std::vector<tcb::StepReqs> args;
-    if (!can_defer) {
+    const bool can_defer = true;
+    if (!fuse_ok) {
         const tcb_status st = flush_merge(b, s);
         if (st) return st;
     }
@@ -542,7 +544,7 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
         [&](const tcb::StepReqs &R, bool fuse) {
             return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, false, s, fuse);
         },
-        gather_index(d_logits, ld, dtype, b->V), 0.0, 0, false, true);
+        gather_index(d_logits, ld, dtype, b->V));
 }
 
 tcb_status tcb_beam_step_sampled(tcb_beams *b, const void *d_logits, int64_t ld, int32_t dtype, float temperature,
@@ -560,7 +562,7 @@ tcb_status tcb_beam_step_sampled(tcb_beams *b, const void *d_logits, int64_t ld,
         [&](const tcb::StepReqs &R, bool fuse) {
             return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, true, s, fuse);
         },
-        gather_index(d_logits, ld, dtype, b->V), (double)temperature, seed, false, true);
+        gather_index(d_logits, ld, dtype, b->V), (double)temperature, seed);
 }
 
 tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_hidden, int32_t H,
@@ -574,6 +576,14 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
     tcb_status st = step_common(b);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
+    // the children-only head reads the rows' nodes: a pending merge is then launched first
+    bool any_sparse = false;
+    if (H <= 4096 && b->w.norm == TCB_NORM_CHILDREN)
+        for (const auto &q : b->reqs)
+            if (q.used && q.level < b->L &&
+                (b->read_mode == TCB_READ_GATHER ||
+                 (b->read_mode == TCB_READ_AUTO && (b->sparse_head_levels >> q.level & 1u))))
+                any_sparse = true;
     return run_step(
         b, s,
         [&](const tcb::StepReqs &R) {
@@ -594,7 +604,7 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
         [&](const tcb::StepReqs &R, bool fuse) {
             return tcb::launch_tile(b->tdev, b->w, b->rp, R, b->w.lmx, 256, TCB_F32, false, s, fuse);
         },
-        2, 0.0, 0, H <= 4096);
+        2, 0.0, 0, H <= 4096, !any_sparse);
 }
 
 tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, float *d_phi, int32_t *d_parent_slot,
