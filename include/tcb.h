@@ -37,6 +37,10 @@
  *   - A tcb_trie is immutable after tcb_trie_upload and may be shared by several
  *     tcb_beams. A tcb_beams object is used from one host thread and one stream.
  *   - Only tcb_beam_check and tcb_beam_finalize synchronise the stream.
+ *   - A step may leave its per-request merge (the ranking of the candidates into the
+ *     new rows) to the next step's kernels; tcb_beam_export, the finalize calls and a
+ *     step that needs the merged rows first launch it themselves. Results do not
+ *     depend on where the merge runs; a wave's steps therefore go to one stream.
  */
 #ifndef TCB_H
 #define TCB_H
