@@ -462,8 +462,14 @@ __device__ __forceinline__ void write_final_row(const StepFin &F, int L, int Bma
                                                 uint64_t pfx, uint32_t c, float phi, int64_t item) {
     const size_t out = (size_t)q * (size_t)Bmax + rank;
     uint8_t *sp = F.sids + out * (size_t)L;
-    for (int t = 0; t < L - 1; ++t) sp[t] = (uint8_t)(pfx >> (8 * t));
-    sp[L - 1] = (uint8_t)c;
+    const uint64_t codes = pfx | ((uint64_t)c << (8 * (L - 1)));
+    if (L == 4 && ((uintptr_t)sp & 3u) == 0) {          // one store where the row is aligned
+        *reinterpret_cast<uint32_t *>(sp) = (uint32_t)codes;
+    } else if (L == 8 && ((uintptr_t)sp & 7u) == 0) {
+        *reinterpret_cast<uint64_t *>(sp) = codes;
+    } else {
+        for (int t = 0; t < L; ++t) sp[t] = (uint8_t)(codes >> (8 * t));
+    }
     F.scores[out] = phi;
     F.items[out] = item;
 }
@@ -484,11 +490,12 @@ __device__ __forceinline__ uint64_t walk_prefix(const WaveDev &W, const ReqArg r
     return pfx;
 }
 
-// New row `rank` of a finishing request: its state as write_new_row, and its output entry.
+// New row `rank` of a finishing request: its output entry (the request is released, so no
+// row state is written).
 __device__ __forceinline__ void write_finished_row(const TrieDev &T, const WaveDev &W, const StepFin &F, int q,
                                                    const ReqArg ra, uint32_t rank, float s, uint32_t f,
                                                    int32_t node, float phi) {
-    write_new_row(W, ra, rank, s, f, node, phi);
+    (void)s;
     if (rank < (uint32_t)ra.width())
         write_final_row(F, T.L, W.Bmax, q, rank, walk_prefix(W, ra, f >> 8), f & 255u, phi, item_of(T, W, node));
 }
@@ -690,7 +697,6 @@ __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W
                 if (p < staged && pos[u] < staged) {
                     const uint32_t rank = (uint32_t)M.n[pos[u]];
                     if (rank < k) {
-                        write_new_row(W, ra, rank, sc[u], fl[u], nd[u], ph[u]);
                         uint64_t pfx = 0;
                         uint32_t r = fl[u] >> 8;
                         for (int t = ra.level() - 1; t >= 0; --t) {
