@@ -486,6 +486,32 @@ def pin_sampled_noise_moments(orc):
     assert abs(g.var() - math.pi ** 2 / 6) < 0.05
 
 
+def pin_splitmix64_known_answers(orc):
+    """Known answers of the sampled step's noise stream: SplitMix64 keyed by seed,
+    request, level, parent rank and code (flashrec 0.1.0, Features > Serving, "API"
+    names Gumbel top-k; the generator and key layout are this repository's reading).
+
+    * SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) seeded with 0 emits the published
+      reference stream e220a8397b1dcdaf, 6e789e6aa1b965f4, 06c45d188009454f,
+      f88bb8a8724c81ec, 1b39896a51a8749b; its i-th output is the mixer applied to
+      i times the golden-ratio increment, which is what ``splitmix64(i * gamma)`` is.
+    * The key layout is pinned through the first of those outputs: with seed 0 the
+      key is sm64(0) ^ req << 40 ^ level << 32 ^ rank << 8 ^ code, so the fields
+      req = 0xE220A8, level = 0x39, rank = 0x7B1DCD, code = 0xAF cancel sm64(0)
+      exactly, the hashed word is sm64(0) again and u = (0xE220A8 + 1/2) / 2^24.
+      A field at a wrong shift, or a wrong constant anywhere, moves u.
+    """
+    gamma = 0x9E3779B97F4A7C15
+    stream = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F,
+              0xF88BB8A8724C81EC, 0x1B39896A51A8749B]
+    for i, want in enumerate(stream):
+        assert orc.splitmix64((i * gamma) & ((1 << 64) - 1)) == want, i
+    u = orc.noise_uniform(0, 0xE220A8, 0x39, 0x7B1DCD, 0xAF)
+    assert u == (0xE220A8 + 0.5) / float(1 << 24)
+    # one bit of the code flipped: the hashed word is sm64(1), a different draw
+    assert orc.noise_uniform(0, 0xE220A8, 0x39, 0x7B1DCD, 0xAE) != u
+
+
 # --------------------------------------------------------------------------- single-pass scoring
 def _random_sids(rng, V, L, n):
     return [tuple(int(c) for c in rng.integers(0, V, L)) for _ in range(n)]
@@ -607,5 +633,5 @@ ALL_PINS = [pin_handworked, pin_trie_numbering, pin_dedupe_lowest_row,
             pin_full_catalog_unconstrained, pin_width_one_greedy, pin_wide_equals_bruteforce,
             pin_tiny_vs_replay, pin_legality, pin_lmhead_exact, pin_bf16_widening,
             pin_decode_api, pin_open_vocabulary, pin_sampled_plackett_luce, pin_sampled_key_invariants,
-            pin_sampled_noise_moments, pin_score_bruteforce, pin_score_equals_wide_beam,
+            pin_sampled_noise_moments, pin_splitmix64_known_answers, pin_score_bruteforce, pin_score_equals_wide_beam,
             pin_score_full_catalog, pin_score_sid_term_closed_form, pin_score_invariances]

@@ -206,11 +206,28 @@ def _score_mut(*, drop_level=False, reverse_levels=False, normalise=True, sid_si
     return score_catalog
 
 
+def _sm64_wrong_multiplier(x):
+    m = (1 << 64) - 1
+    z = (x + 0x9E3779B97F4A7C15) & m
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B5) & m     # last digit of the first multiplier
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & m
+    return z ^ (z >> 31)
+
+
+def _noise_with(sm64, level_shift=32):
+    def noise_uniform(seed, req, level, rank, code):
+        m = (1 << 64) - 1
+        key = sm64(seed & m) ^ (req << 40) ^ (level << level_shift) ^ (rank << 8) ^ code
+        return ((sm64(key & m) >> 40) + 0.5) / float(1 << 24)
+    return noise_uniform
+
+
 def _ns(**over):
     ns = dict(OracleTrie=oracle.OracleTrie, expand_request=oracle.expand_request,
               masked_log_softmax=oracle.masked_log_softmax, decode=oracle.decode,
               lmhead_logits=oracle.lmhead_logits, widen_logits=oracle.widen_logits,
               decode_sampled=oracle.decode_sampled, noise_uniform=oracle.noise_uniform,
+              splitmix64=oracle.splitmix64,
               gumbel=oracle.gumbel, score_catalog=oracle.score_catalog)
     ns.update(over)
     return types.SimpleNamespace(**ns)
@@ -248,6 +265,9 @@ MUTANTS = {
     "sampled_noise_shared_by_siblings": dict(decode_sampled=_decode_sampled_mut(shared_noise=True)),
     "sampled_parent_key_dropped": dict(decode_sampled=_decode_sampled_mut(parent_key=False)),
     "sampled_phi_not_accumulated": dict(decode_sampled=_decode_sampled_mut(accumulate=False)),
+    "splitmix_wrong_multiplier": dict(splitmix64=_sm64_wrong_multiplier,
+                                      noise_uniform=_noise_with(_sm64_wrong_multiplier)),
+    "noise_key_level_wrong_shift": dict(noise_uniform=_noise_with(oracle.splitmix64, level_shift=30)),
     "score_last_level_dropped": dict(score_catalog=_score_mut(drop_level=True)),
     "score_levels_reversed": dict(score_catalog=_score_mut(reverse_levels=True)),
     "score_logits_not_normalised": dict(score_catalog=_score_mut(normalise=False)),
