@@ -154,7 +154,11 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
                             int32_t max_width, int32_t norm, void *d_ws, size_t ws_bytes,
                             void *stream, tcb_beams **out);
 
-/* Admit n requests at the root (one row, score 0) before the next step.
+/* Admit n requests at the root (one row, score 0) before the next step ([FR]
+ * Decoding, "Scheduling": requests join decode waves between steps while their beam
+ * rows fit the slot budget, and then share every step with the requests already in
+ * flight. The pages give no start state; the plainest reading, taken here, is one
+ * row at the root, the empty prefix, with score 0).
  *   widths         host [n], beam width n_i of each request, 1..max_width
  *   out_req_ids    host [n] (may be NULL): request id of each admitted request
  *   out_slot_base  host [n] (may be NULL): request i owns slots
