@@ -223,6 +223,75 @@ def main_leg(args, wl, cat, dev):
             "dsize": 2 if wl.bf16 else 4, "V": V, "L": L, "R": R, "B": B}
 
 
+TRACE_ORDER = [1, 8, 9, 10, 2, 3, 4, 5, 6, 7]
+TRACE_NAMES = {1: "start", 8: "counts", 9: "staged", 10: "merged", 2: "prev-merge", 3: "softmax",
+               4: "prefilter", 5: "binned", 6: "in-tile-staged", 7: "done"}
+
+
+def phase_trace(args, wl, cat, dev):
+    """Phase marks of every workgroup of one decode of the workload, captured as a HIP graph
+    (the timed route) and replayed ``args.phase_trace`` times. Prints, per launch, the
+    start skew across workgroups, the span from the first start to the last mark, and the
+    median per-workgroup time between consecutive marks (100 MHz clock)."""
+    import numpy as np
+    import torch
+    from trie_constrained_beam_amd import Beams, Trie, synth
+    trie = Trie(cat, device=dev)
+    widths = list(wl.widths)
+    S, R, B, V, L = sum(widths), len(widths), max(widths), trie.V, trie.L
+    beams = Beams(trie, S, R, B, device=dev)
+    host = []
+    for t in range(L):
+        h = np.zeros((S, V), dtype=np.uint16 if wl.bf16 else np.float32)
+        for i, w in enumerate(widths):
+            base = sum(widths[:i])
+            h[base:base + w] = synth.logits_rowkeyed(wl.seed, t, i, w, wl.sigma, bf16=wl.bf16)
+        host.append(torch.from_numpy(h.view(np.int16) if wl.bf16 else h).to(dev))
+    xs = [x.view(torch.bfloat16) if wl.bf16 else x for x in host]
+    beams.set_finish_outputs(True)
+
+    def decode(_):
+        beams.init(widths)
+        for t in range(L):
+            beams.step(xs[t])
+    for d in range(3):
+        decode(d)
+    torch.cuda.synchronize()
+    beams.set_trace(64 * 2 ** 20 // 8)
+    (g,) = capture(decode, 1)
+    reps = []
+    for _ in range(args.phase_trace):
+        g.replay()
+        torch.cuda.synchronize()
+        reps.append(beams.trace())
+        torch.cuda.synchronize()
+    beams.set_trace(0)
+    lines = [f"# workload {wl.name}: {args.phase_trace} replays of one captured decode; times in us "
+             f"(median over replays; per-workgroup phases: median over workgroups)"]
+    for li, (kind, level, _) in enumerate(reps[0]):
+        recs = [r[li][2] for r in reps]
+        name = {1: "tile", 2: "merge"}.get(kind, str(kind))
+        skew, span, phases = [], [], {}
+        for rec in recs:
+            ran = rec[:, 0] > 0
+            rec = rec[ran]
+            st = rec[:, 1]
+            skew.append((st.max() - st.min()) / 100.0)
+            last = rec[:, 2:].max(axis=1)
+            span.append((np.maximum(last, st).max() - st.min()) / 100.0)
+            marks = [m for m in TRACE_ORDER if (rec[:, m] > 0).any()]
+            for a, b in zip(marks, marks[1:]):
+                both = (rec[:, a] > 0) & (rec[:, b] > 0)
+                if both.any():
+                    phases.setdefault(f"{TRACE_NAMES[a]}->{TRACE_NAMES[b]}", []).append(
+                        float(np.median(rec[both, b] - rec[both, a])) / 100.0)
+        xcd = np.bincount(recs[0][recs[0][:, 0] > 0, 0] - 1, minlength=8)
+        ph = ", ".join(f"{k} {np.median(v):.2f}" for k, v in phases.items())
+        lines.append(f"{name:5s} level {level} workgroups {recs[0].shape[0]:4d} (ran {int((recs[0][:, 0] > 0).sum())}, "
+                     f"per XCD {xcd.tolist()}): start skew {np.median(skew):.2f}, span {np.median(span):.2f}; {ph}")
+    print("\n".join(lines), flush=True)
+
+
 def lmhead_leg(args, dev, read_mode="dense"):
     """The fused lm_head workload. read_mode "dense": the MFMA head at every level (its
     roofline); "auto": the library's per-level choice (the children-only head only where
@@ -384,6 +453,8 @@ def main():
     ap.add_argument("--graph", type=int, default=1, help="replay each decode as a captured HIP graph")
     ap.add_argument("--lmhead", type=int, default=1, help="also run the SID-range lm_head leg")
     ap.add_argument("--score", type=int, default=1, help="also run the single-pass scoring leg")
+    ap.add_argument("--phase-trace", type=int, default=0,
+                    help="only print the phase trace of one decode replayed this many times (diagnostics)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -400,6 +471,11 @@ def main():
     t0 = time.perf_counter()
     cat = wl.catalog()
     log(f"[bench] catalog {cat.shape} in {time.perf_counter() - t0:.1f}s")
+    if args.phase_trace:
+        import torch
+        torch.cuda.set_device(0)
+        phase_trace(args, wl, cat, torch.device("cuda:0"))
+        return
     cpu = score_cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(wl, cat, args.cpu_seconds)

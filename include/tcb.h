@@ -325,6 +325,25 @@ tcb_status tcb_beams_enable_timing(tcb_beams *b, int32_t capacity, int32_t repea
 tcb_status tcb_beams_timing(tcb_beams *b, double *head_ms, double *tile_ms, double *merge_ms,
                             int32_t *steps);
 
+/* Phase trace (diagnostics). Arms a trace of the kernels this wave launches from now
+ * on: each tile or merge launch that still fits appends, per workgroup, TCB_TRACE_SLOTS
+ * 64-bit words to d_buf (caller-owned device memory of capacity_words words): word 0 =
+ * 1 + the XCD the workgroup ran on, word i > 0 = the 100 MHz real-time clock when the
+ * workgroup passed phase mark i (0 if it never did). Tile marks: 1 start, 2 the previous
+ * step's merge done (steps that merge it first), 3 rows loaded and log-softmaxed, 4
+ * prefilter bound, 5 candidates binned, 6 staged for an in-tile merge, 7 done; merge
+ * marks: 1 start, 8 counts read, 9 candidates staged, 10 done. capacity_words = 0 turns
+ * tracing off. Launches captured into a HIP graph keep the buffer they were captured
+ * with. Errors: TCB_E_ARG. */
+#define TCB_TRACE_SLOTS 16
+enum { TCB_TRACE_TILE = 1, TCB_TRACE_MERGE = 2 };
+tcb_status tcb_beams_set_trace(tcb_beams *b, uint64_t *d_buf, int64_t capacity_words);
+
+/* The traced launches since tcb_beams_set_trace: 4 int32 per launch (kind TCB_TRACE_*,
+ * the highest level it stepped, workgroups, word offset of its region in d_buf), at most
+ * max_launches of them written to out; *n = how many were traced. Errors: TCB_E_ARG. */
+tcb_status tcb_beams_trace_log(const tcb_beams *b, int32_t *out, int32_t max_launches, int32_t *n);
+
 void tcb_beams_destroy(tcb_beams *b);
 
 /* ------------------------------------------------------------------------------

@@ -318,3 +318,50 @@ def test_deferred_merge_lmhead(mode):
         k = int(res[0][1]["rows"][rid])
         assert k == int(res[1][1]["rows"][rid])
         assert np.array_equal(res[0][1]["hist"][-1, base:base + k], res[1][1]["hist"][-1, base:base + k]), rid
+
+
+def test_deferred_merge_with_second_launch_chunk():
+    """More request ids than one launch's arguments hold (400): the step is launched in
+    chunks. 400 requests of width 128 step back to back (each merge left to the next
+    step's tile kernel); then one more request is admitted, alone in the second chunk with
+    one row. Its first step runs in the kernel that does the pending merges, which leaves
+    its candidates to a merge like everyone else's. The beams and the final state must
+    equal those of the same decode with an export (hence the merge kernel) after every
+    step."""
+    cat = synth.catalog(100_000, 4, ("zipf",) * 4, [74, 1])
+    trie = Trie(cat, device="cuda")
+    n0, w = 400, 128
+    S = (n0 + 1) * w
+
+    def run(export_each):
+        beams = Beams(trie, S, n0 + 1, w)
+        ids, bases = beams.init(np.full(n0, w, dtype=np.int32))
+        ids, bases = list(ids), list(bases)
+        level = [0] * n0
+        for t in range(6):
+            if t == 2:
+                nid, nb = beams.init(np.asarray([w], dtype=np.int32))
+                assert int(nid[0]) == n0
+                ids.append(int(nid[0]))
+                bases.append(int(nb[0]))
+                level.append(0)
+            host = np.zeros((S, 256), dtype=np.float32)
+            for i, (b, lv) in enumerate(zip(bases, level)):
+                if lv < 4:
+                    host[b:b + w] = synth.logits_rowkeyed(74, lv, i, w, 2.0)
+            beams.step(torch.from_numpy(host).cuda())
+            level = [lv + 1 if lv < 4 else lv for lv in level]
+            if export_each:
+                beams.export()
+            if t == 3:                                  # the first 400 are at depth 4
+                first = beams.finalize(ids[:n0])
+            if t == 5:
+                last = beams.finalize(ids[n0:])
+        beams.check()
+        return first, last
+
+    a1, a2 = run(False)
+    b1, b2 = run(True)
+    _same(a1, b1)
+    _same(a2, b2)
+    assert int(a2["counts"][0]) == w

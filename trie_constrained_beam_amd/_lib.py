@@ -22,6 +22,8 @@ TCB_SCORE_MAX_K = 512
 TCB_MAX_L = 8
 TCB_MAX_WIDTH = 4096
 TCB_MASK_AUTO = -1
+TCB_TRACE_SLOTS = 16
+TCB_TRACE_TILE, TCB_TRACE_MERGE = 1, 2
 
 
 class TrieInfo(C.Structure):
@@ -72,6 +74,8 @@ SIGNATURES = {
     "tcb_beams_enable_timing": (I32, [P, I32, I32]),
     "tcb_beams_timing": (I32, [P, C.POINTER(C.c_double), C.POINTER(C.c_double), C.POINTER(C.c_double),
                                C.POINTER(I32)]),
+    "tcb_beams_set_trace": (I32, [P, P, I64]),
+    "tcb_beams_trace_log": (I32, [P, P, I32, C.POINTER(I32)]),
     "tcb_beams_destroy": (None, [P]),
     "tcb_trie_codes_bytes": (I32, [P, C.POINTER(C.c_size_t)]),
     "tcb_trie_upload_codes": (I32, [P, P, C.c_size_t, P]),

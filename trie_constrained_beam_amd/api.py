@@ -112,6 +112,7 @@ class Beams:
         self._h = h
         self._destroy = lib().tcb_beams_destroy
         self.device = device
+        self._trace = None
 
     def __del__(self):
         if getattr(self, "_h", None):
@@ -206,6 +207,26 @@ class Beams:
         h, a, b, n = C.c_double(), C.c_double(), C.c_double(), C.c_int32()
         check(lib().tcb_beams_timing(self._h, C.byref(h), C.byref(a), C.byref(b), C.byref(n)))
         return float(h.value), float(a.value), float(b.value), int(n.value)
+
+    def set_trace(self, capacity_words: int = 0):
+        """Arm a phase trace of the kernels launched from now on into a device buffer of
+        ``capacity_words`` 64-bit words (0: off). Diagnostics only."""
+        self._trace = (torch.zeros(int(capacity_words), dtype=torch.int64, device=self.device)
+                       if capacity_words > 0 else None)
+        check(lib().tcb_beams_set_trace(self._h, _ptr(self._trace), int(capacity_words)))
+
+    def trace(self):
+        """The traced launches: a list of (kind, level, records) with records an int64
+        array [workgroups, TCB_TRACE_SLOTS] (word 0 = 1 + XCD, then clock marks). Synchronises."""
+        n = C.c_int32()
+        check(lib().tcb_beams_trace_log(self._h, None, 0, C.byref(n)))
+        log = np.zeros((max(1, n.value), 4), dtype=np.int32)
+        check(lib().tcb_beams_trace_log(self._h, log.ctypes.data, n.value, C.byref(n)))
+        buf = self._trace.cpu().numpy() if self._trace is not None else np.zeros(0, dtype=np.int64)
+        out = []
+        for kind, level, grid, off in log[:n.value]:
+            out.append((int(kind), int(level), buf[off:off + grid * L.TCB_TRACE_SLOTS].reshape(grid, -1)))
+        return out
 
     def finalize(self, req_ids):
         """Ranked beams of finished requests (host arrays); releases their slots."""

@@ -109,6 +109,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     return x;
 }
 
+// Phase trace (diagnostics): thread 0 records the real-time clock (100 MHz) when its
+// workgroup passes mark i; mark 0 records the XCD. A uniform test of a kernel argument when
+// tracing is off.
+__device__ __forceinline__ void trace_mark(const WaveDev &W, int i) {
+    if (W.trace != nullptr && threadIdx.x == 0) {
+        uint64_t v;
+        if (i == 0) v = 1u + (__builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15u);  // HW_REG_XCC_ID
+        else v = wall_clock64();
+        W.trace[(size_t)blockIdx.x * kTraceSlots + i] = v;
+    }
+}
+
 // LDS ordering among the lanes of one wave (no workgroup barrier needed)
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -578,6 +590,7 @@ __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W
     }
     M.G[tid] = g;
     M.cur[tid] = 0u;
+    trace_mark(W, 8);                                 // the counts have arrived
     if (fin_lds && tid < ra.rmax()) {
 #pragma unroll
         for (int t = 0; t < kH; ++t)
@@ -683,6 +696,7 @@ __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W
             }
         }
         __syncthreads();
+        trace_mark(W, 9);                             // staged
         // 3. rank = members of better bins + better members of the own bin
         if (fin_lds) {
             // each entry's rank goes to LDS (over its node id, which its staging thread
@@ -763,6 +777,7 @@ __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W
     }
     if (fin) finish_request(T, W, F, q, ra, rp, rows, k);
     else out.done(k);
+    trace_mark(W, 10);                                // ranked, rows issued
 }
 
 // Where k_merge puts a request's new rows: the row buffers and the next record.
@@ -814,6 +829,8 @@ __global__ __launch_bounds__(kThreads) void k_merge(TrieDev T, WaveDev W, int rp
     __shared__ uint32_t Hs[TCB_MAX_L - 1][kThreads];
     const int ql = blockIdx.x;
     if (ql >= R.n) return;
+    trace_mark(W, 0);
+    trace_mark(W, 1);
     const ReqArg ra = R.r[ql];
     if (!ra.step()) return;                            // carried over by k_tile
     merge_request(T, W, R.fin, R.q0 + ql, ra, rp, M, sel, Hs, RowsToMemory{W, ra, R.q0 + ql, rp});
@@ -934,6 +951,8 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
     }
     if (tile * kTileRows >= ra.rmax()) return false;          // past any row the request can have
 
+    trace_mark(W, 0);
+    trace_mark(W, 1);                                 // started
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, j = lane & 15;
     const int level = ra.level(), cp = ra.par(), base = ra.base();
     const int rt = wave * kRowsPerWave + g;                   // row within the tile
@@ -972,6 +991,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
         const ReqArg pa = ra.prev_step();
         merge_request(T, W, StepFin{}, q, pa, rp ^ 1, *M, sel, nullptr, RowsToTile{W, pa, q, rp ^ 1, tile, *Z, k});
         __syncthreads();
+        trace_mark(W, 2);                             // previous merge done
         rows = (int)k;
         sref = Z->sref;
         if (r < rows) {
@@ -1155,6 +1175,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
     // 4. prefilter (at depths with many children per row): histogram of the lanes' best
     //    candidates, bin b_L where it reaches n. Elsewhere every candidate is binned exactly.
     __syncthreads();                                  // the zeroed histograms are visible
+    trace_mark(W, 3);                                 // rows loaded, trie read, log-softmax done
     uint32_t bL = kBins - 1;
     if (ra.prefilter()) {
         if (valid) atomicAdd(&A.h1[score_bin(sref, lbest)], 1u);
@@ -1167,6 +1188,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
         if (C >= width && C - h < width) A.bL = (uint32_t)tid;
         __syncthreads();
         bL = A.bL;
+        trace_mark(W, 4);                             // prefilter bound
     }
 
     // 5.-6. survivors and their exact bins. A candidate in a bin <= b_L scores above
@@ -1213,6 +1235,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
         A.h2[tid] = C;                                // this thread's bin only
     }
     __syncthreads();
+    trace_mark(W, 5);                                 // binned and scanned
     const uint32_t bt = A.bt;
     const uint32_t kept = A.h2[bt];
     const int CAPT = W.CAPT;
@@ -1269,6 +1292,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
                 }
             }
             __syncthreads();
+            trace_mark(W, 6);                         // staged for the in-tile merge
             const uint32_t k = min(width, kept);
             if (finishes(T, R.fin, ra)) {
                 rank_staged(*M, A.h2, kept, sref, [&](uint32_t rank, uint32_t p, float s, uint32_t f) {
@@ -1281,6 +1305,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
                 });
                 write_next_record(W, q, ra, rp, k);
             }
+            trace_mark(W, 7);                         // ranked, rows issued
             return true;
         }
         Cand *out = W.cand[level & 1] + reg;
@@ -1302,6 +1327,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
             }
         }
         W.tcum[level & 1][((size_t)q * MT + tile) * kBins + tid] = (uint16_t)min(C, kept);
+        trace_mark(W, 7);                             // candidates issued
     } else {
         // exact path: keep exactly the tile's top min(n, #candidates)
         if (tid == 0) atomicOr(W.err, kInfoTileExact);
@@ -1546,6 +1572,12 @@ static void launch_tile_dt(const TrieDev &t, const WaveDev &w, int rp, const Ste
     else launch_tile_v<DT, SAMPLE, false>(t, w, rp, R, logits, ld, merge, s);
 }
 
+int tile_grid(const WaveDev &w, const StepReqs &R, bool fuse) {
+    if (R.n <= 0) return 0;
+    if (!fuse && tile_merges(R)) return R.n;
+    return 8 * ((R.n + 7) / 8) * w.MT;
+}
+
 bool tile_merges(const StepReqs &R) {
     for (int i = 0; i < R.n; ++i)
         if (R.r[i].step() && R.r[i].rmax() > kTileRows) return false;
@@ -1569,8 +1601,11 @@ hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReq
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, hipStream_t s) {
-    if (R.n <= 0 || tile_merges(R)) return hipSuccess;           // merged inside the tile kernel
+bool merged_in_tile(const StepReqs &R, bool fuse) { return !fuse && tile_merges(R); }
+
+hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, bool in_tile,
+                        hipStream_t s) {
+    if (R.n <= 0 || in_tile) return hipSuccess;                   // merged inside the tile kernel
     hipLaunchKernelGGL(k_merge, dim3(R.n), dim3(kThreads), 0, s, t, w, rp, R);
     return hipGetLastError();
 }

@@ -160,12 +160,36 @@ tcb_status flush_init(tcb_beams *b, hipStream_t s) {
     return TCB_OK;
 }
 
+// Highest level among the requests a launch steps (the phase trace's label).
+int32_t launch_level(const tcb::StepReqs &R) {
+    int32_t lv = 0;
+    for (int i = 0; i < R.n; ++i)
+        if (R.r[i].step()) lv = std::max(lv, (int32_t)R.r[i].level());
+    return lv;
+}
+
+// The wave's device view for one launch: with a phase trace armed and room left, the
+// launch gets its own region of the trace buffer and an entry in the trace log.
+tcb::WaveDev traced(tcb_beams *b, int32_t kind, int32_t level, int32_t grid) {
+    tcb::WaveDev w = b->w;
+    w.trace = nullptr;
+    const int64_t words = (int64_t)grid * tcb::kTraceSlots;
+    if (b->trace_buf && grid > 0 && b->trace_used + words <= b->trace_cap) {
+        w.trace = b->trace_buf + b->trace_used;
+        b->trace_log.insert(b->trace_log.end(), {kind, level, grid, (int32_t)b->trace_used});
+        b->trace_used += words;
+    }
+    return w;
+}
+
 // Launches a merge left for the next step's tile kernel as k_merge (before anything other
 // than a step reads request state).
 tcb_status flush_merge(tcb_beams *b, hipStream_t s) {
     if (!b->merge_pending) return TCB_OK;
     for (const auto &R : b->deferred) {
-        hipError_t e = tcb::launch_merge(b->tdev, b->w, b->deferred_rp, R, s);
+        // a deferred step merged nothing inside its tile kernel
+        const tcb::WaveDev w = traced(b, TCB_TRACE_MERGE, launch_level(R), R.n);
+        hipError_t e = tcb::launch_merge(b->tdev, w, b->deferred_rp, R, false, s);
         if (e != hipSuccess) return hip_fail(e, "merge launch");
     }
     for (auto &q : b->reqs) q.pending = false;
@@ -495,7 +519,9 @@ static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLau
     if (e != hipSuccess) return hip_fail(e, "lm_head kernel launch");
     if (timed) e = hipEventRecord(ev[1], s);
     for (int i = 0; i < rep && e == hipSuccess; ++i)
-        for (size_t c = 0; c < args.size() && e == hipSuccess; ++c) e = tile(args[c], fuse);
+        for (size_t c = 0; c < args.size() && e == hipSuccess; ++c)
+            e = tile(traced(b, TCB_TRACE_TILE, launch_level(args[c]), tcb::tile_grid(b->w, args[c], fuse)), args[c],
+                     fuse);
     if (e != hipSuccess) return hip_fail(e, "tile kernel launch");
     if (fuse) {
         for (auto &q : b->reqs) q.pending = false;
@@ -507,7 +533,7 @@ static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLau
     for (const auto &q : b->reqs)
         if (q.used && q.level < b->L && q.level + 1 >= b->L) defer = false;
     for (const auto &R : args)
-        if (tcb::tile_merges(R)) defer = false;
+        if (tcb::merged_in_tile(R, fuse)) defer = false;
     if (timed) e = hipEventRecord(ev[2], s);
     if (defer) {
         b->deferred = args;
@@ -518,7 +544,11 @@ static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLau
     } else {
         for (int i = 0; i < rep && e == hipSuccess; ++i)
             for (size_t c = 0; c < args.size() && e == hipSuccess; ++c)
-                e = tcb::launch_merge(b->tdev, b->w, b->rp, args[c], s);
+                e = tcb::launch_merge(b->tdev,
+                                      tcb::merged_in_tile(args[c], fuse)
+                                          ? b->w
+                                          : traced(b, TCB_TRACE_MERGE, launch_level(args[c]), args[c].n),
+                                      b->rp, args[c], tcb::merged_in_tile(args[c], fuse), s);
     }
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     if (timed) {
@@ -541,8 +571,8 @@ tcb_status tcb_beam_step(tcb_beams *b, const void *d_logits, int64_t ld, int32_t
     hipStream_t s = (hipStream_t)stream;
     return run_step(
         b, s, [](const tcb::StepReqs &) { return hipSuccess; },
-        [&](const tcb::StepReqs &R, bool fuse) {
-            return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, false, s, fuse);
+        [&](const tcb::WaveDev &w, const tcb::StepReqs &R, bool fuse) {
+            return tcb::launch_tile(b->tdev, w, b->rp, R, d_logits, ld, dtype, false, s, fuse);
         },
         gather_index(d_logits, ld, dtype, b->V));
 }
@@ -559,8 +589,8 @@ tcb_status tcb_beam_step_sampled(tcb_beams *b, const void *d_logits, int64_t ld,
     hipStream_t s = (hipStream_t)stream;
     return run_step(
         b, s, [](const tcb::StepReqs &) { return hipSuccess; },
-        [&](const tcb::StepReqs &R, bool fuse) {
-            return tcb::launch_tile(b->tdev, b->w, b->rp, R, d_logits, ld, dtype, true, s, fuse);
+        [&](const tcb::WaveDev &w, const tcb::StepReqs &R, bool fuse) {
+            return tcb::launch_tile(b->tdev, w, b->rp, R, d_logits, ld, dtype, true, s, fuse);
         },
         gather_index(d_logits, ld, dtype, b->V), (double)temperature, seed);
 }
@@ -601,8 +631,8 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
                                               sparse_rows, s);
             return e;
         },
-        [&](const tcb::StepReqs &R, bool fuse) {
-            return tcb::launch_tile(b->tdev, b->w, b->rp, R, b->w.lmx, 256, TCB_F32, false, s, fuse);
+        [&](const tcb::WaveDev &w, const tcb::StepReqs &R, bool fuse) {
+            return tcb::launch_tile(b->tdev, w, b->rp, R, b->w.lmx, 256, TCB_F32, false, s, fuse);
         },
         2, 0.0, 0, H <= 4096, !any_sparse);
 }
@@ -755,6 +785,24 @@ tcb_status tcb_beams_timing(tcb_beams *b, double *head_ms, double *tile_ms, doub
     *tile_ms = ta;
     *merge_ms = tb;
     *steps = b->timing_used;
+    return TCB_OK;
+}
+
+tcb_status tcb_beams_set_trace(tcb_beams *b, uint64_t *d_buf, int64_t capacity_words) {
+    if (!b || capacity_words < 0 || (capacity_words > 0 && !d_buf)) return set_error(TCB_E_ARG, "set_trace: bad arguments");
+    b->trace_buf = capacity_words > 0 ? d_buf : nullptr;
+    b->trace_cap = capacity_words;
+    b->trace_used = 0;
+    b->trace_log.clear();
+    return TCB_OK;
+}
+
+tcb_status tcb_beams_trace_log(const tcb_beams *b, int32_t *out, int32_t max_launches, int32_t *n) {
+    if (!b || !n || max_launches < 0 || (max_launches > 0 && !out)) return set_error(TCB_E_ARG, "trace_log: bad arguments");
+    const int32_t have = (int32_t)(b->trace_log.size() / 4);
+    *n = have;
+    if (max_launches > 0 && have > 0)
+        std::memcpy(out, b->trace_log.data(), sizeof(int32_t) * 4 * (size_t)std::min(have, max_launches));
     return TCB_OK;
 }
 

@@ -62,6 +62,11 @@ struct tcb_beams {
     // before the merge, after the merge)
     std::vector<hipEvent_t> events;
     int32_t timing_cap = 0, timing_used = 0, timing_repeat = 1;
+    // optional phase trace (tcb_beams_set_trace): launches append kTraceSlots words per
+    // workgroup to trace_buf while they fit; trace_log holds (kind, level, grid, offset)
+    uint64_t *trace_buf = nullptr;
+    int64_t trace_cap = 0, trace_used = 0;
+    std::vector<int32_t> trace_log;
     ~tcb_beams() {
         for (auto e : events) (void)hipEventDestroy(e);
     }

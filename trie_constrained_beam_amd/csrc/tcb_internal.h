@@ -85,8 +85,13 @@ struct WaveDev {
     uint16_t *tcum[2];             // [R][MT][kBins]
     float *lmx;                    // [S][256] logits computed by the SID-range lm_head
     uint32_t *err;                 // sticky error / info bits
+    // phase trace of this launch (diagnostics; nullptr: off): kTraceSlots words per
+    // workgroup, word 0 = 1 + the XCD it ran on, word i > 0 = the real-time clock when the
+    // workgroup passed phase mark i (0 = never)
+    uint64_t *trace;
     int32_t S, R, MT, CAPT, Bmax, norm, validate, pad;
 };
+constexpr int kTraceSlots = TCB_TRACE_SLOTS;
 
 // --------------------------------------------------------------------- step arguments
 // What the host knows of every request it steps, passed by value so a kernel's first
@@ -153,6 +158,9 @@ struct FinBatch {
     int32_t base[kMax], width[kMax], par[kMax];   // host copies of the record's fixed fields
 };
 
+// workgroups of the tile kernel launch_tile would launch for R (phase-trace layout)
+int tile_grid(const WaveDev &w, const StepReqs &R, bool fuse);
+
 hipError_t launch_clear_wave(const WaveDev &w, hipStream_t s);
 hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s);
 // A step is the tile kernel followed by the per-request merge kernel; with the SID-range
@@ -167,10 +175,16 @@ hipError_t launch_lmhead_sparse(const TrieDev &t, const WaveDev &w, int rp, cons
                                 int64_t ld, int H, const void *weight, float *out, int max_rows, hipStream_t s);
 hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
                          int64_t ld, int H, const void *weight, float *out, hipStream_t s);
-// true when every stepped request of R has at most kTileRows rows: the tile kernel then
-// merges each request itself and launch_merge launches nothing
+// true when every stepped request of R has at most kTileRows rows: a tile kernel launched
+// without a pending merge (fuse false) then merges each request itself
 bool tile_merges(const StepReqs &R);
-hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, hipStream_t s);
+// whether launch_tile(..., fuse) merged the requests of R inside the tile kernel: only the
+// plain launch does; a launch that first does pending merges (fuse) leaves this step's
+// candidates in memory for k_merge or the next step, whatever the requests' widths
+bool merged_in_tile(const StepReqs &R, bool fuse);
+// k_merge over the requests of R, unless in_tile (the tile kernel merged them already)
+hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, bool in_tile,
+                        hipStream_t s);
 hipError_t launch_finalize(const TrieDev &t, const WaveDev &w, int rp, const FinBatch &b,
                            uint8_t *sids, float *scores, int64_t *items, int32_t *counts,
                            hipStream_t s);
