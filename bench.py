@@ -44,7 +44,8 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak, published
 STATE_BYTES = 8                 # node id + score read per live row
 TRIE_BYTES = 8                  # child range (or first child + mask word) per live row
 MERGE_WRITE_BYTES = 18          # node, score, parent slot, back-pointer (+ code) per survivor
-KERNEL_SOURCES = ["trie_constrained_beam_amd/csrc/kernels.hip", "trie_constrained_beam_amd/csrc/tcb_internal.h"]
+KERNEL_SOURCES = ["trie_constrained_beam_amd/csrc/" + f for f in (
+    "beam_device.h", "kernels.hip", "tile_bf16.hip", "tile_f32.hip", "tcb_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_tile_b512x32_l4_4m_zipf_bf16_traffic.txt")
 SCORE_SOURCES = ["trie_constrained_beam_amd/csrc/score.hip", "trie_constrained_beam_amd/csrc/score_internal.h"]
 SCORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_score_scan_score_u32_k512_l4_4m_zipf_d64_traffic.txt")
@@ -153,6 +154,29 @@ def timed(run, steps, warmup):
     return time.perf_counter() - t0
 
 
+def verify_replay(trie, widths, xs, fin, ids, dev):
+    """The last timed decode's outputs (every pool copy holds the same inputs) against a
+    decode of the same inputs with an export after every step, which runs each step's merge
+    in the merge kernel and finalizes separately: bitwise equal, or the bench fails."""
+    import numpy as np
+    import torch
+    from trie_constrained_beam_amd import Beams
+    torch.cuda.synchronize()
+    idx = np.asarray(ids)
+    got = {k: v.cpu().numpy()[idx] for k, v in fin.items()}
+    ref_beams = Beams(trie, sum(widths), len(widths), max(widths), device=dev)
+    rid, _ = ref_beams.init(widths)
+    for x in xs:
+        ref_beams.step(x)
+        ref_beams.export()
+    ref = ref_beams.finalize(rid)
+    ref_beams.check()
+    for k in ("counts", "sids", "scores", "items"):
+        if not np.array_equal(got[k], ref[k]):
+            raise SystemExit(f"bench: the timed decode's {k} differ from the step-by-step decode")
+    log(f"[bench] timed decode outputs equal a step-by-step decode of the same inputs (bitwise)")
+
+
 def merge_steps(trie, widths, L, deferred=True):
     """Steps of a decode that launch the merge kernel: a step whose requests all have at
     most 64 possible rows (one tile; depth-t prefixes of the catalog, at most the beam
@@ -186,7 +210,7 @@ def main_leg(args, wl, cat, dev):
         return [torch.from_numpy(h).to(dev) for h in host]
     per_decode = sum(h.nbytes for h in host)
     pool = make_pool(upload, per_decode, args.pool_gib)
-    beams.set_finish_outputs(True)       # the last step writes each request's beams (row = id)
+    fin = beams.set_finish_outputs(True)   # the last step writes each request's beams (row = id)
     log(f"[bench] pool {len(pool)} x {per_decode / 2**20:.1f} MiB of logits")
     rows_per_step = []
     idx = torch.as_tensor(ids, device=dev).long()
@@ -209,6 +233,7 @@ def main_leg(args, wl, cat, dev):
         else:
             decode(d % len(pool))
     elapsed = timed(run, args.steps, args.warmup)
+    verify_replay(trie, widths, pool[0], fin, ids, dev)
     # per-kernel durations: the same decodes again, eagerly, with events on the launch stream
     # around 10 back-to-back launches of each kernel (dispatch latency amortised)
     n_ev = min(args.steps, 100)

@@ -73,7 +73,7 @@ def _state(beams):
 @pytest.mark.parametrize("name,sample", [
     ("b50x1_l3_20k_f32", [0]),
     ("b128x64_l4_1m_zipf_f32", [0, 17, 42, 63]),
-    ("b512x32_l4_4m_zipf_bf16", [0, 13, 31]),
+    ("b512x32_l4_4m_zipf_bf16", list(range(32))),
 ])
 def test_fullsize_one_wave(name, sample):
     wl, cat, otrie, lowest = _workload(name)
@@ -101,6 +101,85 @@ def test_fullsize_one_wave(name, sample):
         c = int(out["counts"][i])
         assert c == w
         _check_legal(lowest, out["sids"][i, :c], out["scores"][i, :c], out["items"][i, :c], w, f"{name} req {i}")
+
+
+def _capture(decode, n):
+    """Each decode captured as a HIP graph on a side stream, as bench.py replays them."""
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in range(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                decode(c)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def test_fullsize_timed_route_graph_replay():
+    """The route bench.py times, at its size: 32 requests x 512 beams, 4M Zipf catalog, bf16
+    logits, steps back to back (each step's merge left to the next step's tile kernel), the
+    last step writing every request's beams to the finish outputs, each decode captured as a
+    HIP graph and replayed. Every replay's outputs must equal, bitwise, a decode of the same
+    inputs with an export after every step (each merge in the merge kernel, finalized
+    separately), which test_fullsize_one_wave checks against the oracle step by step for all
+    32 requests; the replays' beams must also be legal. Between replays the outputs are
+    overwritten by eager work, so each replay must write all of them again."""
+    wl, cat, otrie, lowest = _workload("b512x32_l4_4m_zipf_bf16")
+    widths = list(wl.widths)
+    S, R, B, L = sum(widths), len(widths), max(widths), wl.L
+    trie = Trie(cat, device="cuda")
+    bases = np.cumsum([0] + widths[:-1])
+    host = []
+    for t in range(L):
+        h = np.zeros((S, 256), dtype=np.uint16)
+        for i, (w, b) in enumerate(zip(widths, bases)):
+            h[b:b + w] = synth.logits_rowkeyed(wl.seed, t, i, w, wl.sigma, bf16=True)
+        host.append(h)
+    pool = [[torch.from_numpy(h.view(np.int16)).cuda().view(torch.bfloat16) for h in host] for _ in range(2)]
+
+    ref_beams = Beams(trie, S, R, B)
+    ids, got_bases = ref_beams.init(widths)
+    assert list(got_bases) == list(bases)
+    for t in range(L):
+        ref_beams.step(pool[0][t])
+        ref_beams.export()
+    ref = ref_beams.finalize(ids)
+    ref_beams.check()
+
+    beams = Beams(trie, S, R, B)
+    out = beams.set_finish_outputs(True)
+
+    def decode(c):
+        rid, _ = beams.init(widths)
+        assert list(rid) == list(ids)
+        for t in range(L):
+            beams.step(pool[c][t])
+    decode(0)                                          # one eager decode, as the bench's warm-up
+    torch.cuda.synchronize()
+    graphs = _capture(decode, 2)
+    idx = np.asarray(ids)
+    for rep in range(4):
+        out["sids"].fill_(0xAB)
+        out["scores"].fill_(12345.0)
+        out["items"].fill_(-7)
+        out["counts"].fill_(-7)
+        torch.cuda.synchronize()
+        graphs[rep % 2].replay()
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy()[idx] for k, v in out.items()}
+        for k in ("counts", "sids", "scores", "items"):
+            assert np.array_equal(got[k], ref[k]), (rep, k)
+        if rep == 0:
+            for i, w in enumerate(widths):
+                c = int(got["counts"][i])
+                assert c == w
+                _check_legal(lowest, got["sids"][i, :c], got["scores"][i, :c], got["items"][i, :c], w,
+                             f"replay req {i}")
+    beams.check()
 
 
 def test_fullsize_mixed_wave_fifo():

@@ -183,25 +183,52 @@ def test_single_level_catalog():
 
 
 def test_mask_vs_csr_bitwise():
-    """The dense-mask and CSR child paths give bit-identical states (many requests)."""
+    """The dense-mask and CSR child paths give bit-identical states: randomized waves
+    (catalog depth, size and code distributions, beam widths, logit scale and dtype, read
+    mode) stepped side by side with every depth masked and with none, at least 10,000
+    request-steps in all (the randomized dense-vs-sparse comparison of the SGLang
+    deployment write-up, applied to the two child-set forms)."""
     rng = np.random.default_rng(43)
-    cat = synth.catalog(120_000, 4, ("uniform", "zipf", "zipf", "zipf"), [43, 1])
-    widths = [int(w) for w in rng.choice([1, 7, 50, 128, 256, 512, 33], 600)]
-    runs = [gh.Run(cat, widths, mask_depths=md, max_slots=sum(widths)) for md in (0, 4)]
-    for t in range(4):
-        x = gh.rowkeyed_logits(43, t, widths, 2.0, False)
-        host = np.zeros((sum(widths), 256), dtype=np.float32)
-        for xi, base in zip(x, runs[0].bases):
-            host[base:base + xi.shape[0]] = xi
-        dev = torch.from_numpy(host).cuda()
-        states = []
+    request_steps = 0
+    case = 0
+    while request_steps < 10_000:
+        L = int(rng.integers(3, 6))
+        dists = tuple(str(x) for x in rng.choice(["uniform", "zipf"], L))
+        n = int(rng.integers(20_000, 150_000))
+        cat = synth.catalog(n, L, dists, [43, case])
+        widths = [int(w) for w in rng.choice([1, 7, 33, 50, 64, 100, 128, 256, 512], int(rng.integers(100, 500)))]
+        sigma = float(rng.choice([0.5, 2.0, 3.0]))
+        bf16 = bool(rng.integers(0, 2))
+        mode = str(rng.choice(["auto", "dense", "gather"]))
+        runs = [gh.Run(cat, widths, mask_depths=md, max_slots=sum(widths), read_mode=mode) for md in (0, L)]
+        for t in range(L):
+            x = gh.rowkeyed_logits(43 + case, t, widths, sigma, bf16)
+            host = np.zeros((sum(widths), 256), dtype=np.uint16 if bf16 else np.float32)
+            for xi, base in zip(x, runs[0].bases):
+                host[base:base + xi.shape[0]] = xi
+            dev = torch.from_numpy(host.view(np.int16) if bf16 else host).cuda()
+            states = []
+            for r in runs:
+                r.beams.step(dev.view(torch.bfloat16) if bf16 else dev)
+                states.append(r.state())
+            a, b = states
+            assert np.array_equal(a["rows"], b["rows"]) and np.array_equal(a["level"], b["level"]), (case, t)
+            # live rows and the level just written (the rest of the workspace is never read;
+            # earlier levels were compared at their own step)
+            for rid, base in zip(runs[0].ids, runs[0].bases):
+                k = int(a["rows"][rid])
+                sl = slice(int(base), int(base) + k)
+                for key in ("node", "parent_slot"):
+                    assert np.array_equal(a[key][sl], b[key][sl]), (case, t, rid, key)
+                assert np.array_equal(a["score"][sl].view(np.uint32), b["score"][sl].view(np.uint32)), (case, t, rid)
+                assert np.array_equal(a["hist"][t, sl], b["hist"][t, sl]), (case, t, rid)
+            request_steps += len(widths)
         for r in runs:
-            r.beams.step(dev)
-            states.append(r.state())
-        for k in ("node", "score", "hist", "rows", "parent_slot"):
-            a, b = states[0][k], states[1][k]
-            assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
-                                  b.view(np.uint32) if b.dtype == np.float32 else b), (t, k)
+            r.beams.check()
+        print(f"case {case}: L={L} {dists} {n} SIDs, {len(widths)} requests, sigma {sigma}, "
+              f"{'bf16' if bf16 else 'f32'}, {mode}; {request_steps} request-steps so far", flush=True)
+        case += 1
+    print(f"mask vs CSR: {request_steps} request-steps over {case} random waves", flush=True)
 
 
 def test_determinism_bitwise():

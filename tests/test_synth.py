@@ -50,3 +50,9 @@ def test_workload_table():
     assert w["b512x32_l4_4m_zipf_bf16"].widths == (512,) * 32
     mixed = w["mixed256_l5_8m_f32"]
     assert len(mixed.widths) == 256 and set(mixed.widths) <= {50, 128, 256, 512}
+
+
+def test_catalog_refuses_more_sids_than_exist():
+    import pytest
+    with pytest.raises(ValueError):
+        synth.catalog(70_000, 2, ("uniform", "uniform"), [1, 1])

@@ -158,6 +158,17 @@ struct FinBatch {
     int32_t base[kMax], width[kMax], par[kMax];   // host copies of the record's fixed fields
 };
 
+// The tile kernel of one logits type and sampling mode (compiled in its own translation
+// unit): mode 1 merges every request inside its only tile, 2 first does pending merges,
+// 0 plain; vec: rows read as 16-byte pieces.
+#define TCB_TILE_LAUNCHER(name)                                                                              \
+    hipError_t name(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits, int64_t ld, \
+                    bool vec, int mode, hipStream_t s)
+TCB_TILE_LAUNCHER(launch_tile_f32);
+TCB_TILE_LAUNCHER(launch_tile_bf16);
+TCB_TILE_LAUNCHER(launch_tile_f32_sampled);
+TCB_TILE_LAUNCHER(launch_tile_bf16_sampled);
+
 // workgroups of the tile kernel launch_tile would launch for R (phase-trace layout)
 int tile_grid(const WaveDev &w, const StepReqs &R, bool fuse);
 

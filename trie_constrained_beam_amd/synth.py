@@ -50,6 +50,8 @@ def catalog(n_distinct: int, L: int, level_dists, seed, V: int = V_DEFAULT) -> n
     distinct ones in draw order. Item id = row index of the result.
     """
     assert len(level_dists) == L
+    if n_distinct > V ** L:
+        raise ValueError(f"catalog: {n_distinct} distinct SIDs requested, only {V ** L} exist at L={L}, V={V}")
     rng = np.random.default_rng(seed)
     pz = zipf_probs(V)
     seen = np.zeros(0, dtype=np.uint64)          # sorted keys already kept
