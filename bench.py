@@ -248,9 +248,9 @@ def main_leg(args, wl, cat, dev):
             "dsize": 2 if wl.bf16 else 4, "V": V, "L": L, "R": R, "B": B}
 
 
-TRACE_ORDER = [1, 8, 9, 10, 2, 3, 4, 5, 6, 7]
-TRACE_NAMES = {1: "start", 8: "counts", 9: "staged", 10: "merged", 2: "prev-merge", 3: "softmax",
-               4: "prefilter", 5: "binned", 6: "in-tile-staged", 7: "done"}
+TRACE_ORDER = [1, 8, 11, 12, 13, 9, 10, 2, 3, 4, 5, 6, 7]
+TRACE_NAMES = {1: "start", 8: "counts", 11: "window", 12: "offsets", 13: "cand", 9: "staged", 10: "merged",
+               2: "prev-merge", 3: "softmax", 4: "prefilter", 5: "binned", 6: "in-tile-staged", 7: "done"}
 
 
 def phase_trace(args, wl, cat, dev):
@@ -293,6 +293,18 @@ def phase_trace(args, wl, cat, dev):
     beams.set_trace(0)
     lines = [f"# workload {wl.name}: {args.phase_trace} replays of one captured decode; times in us "
              f"(median over replays; per-workgroup phases: median over workgroups)"]
+    # timeline: each launch's first start and last mark, from the decode's first start
+    tl = []
+    for rep in reps:
+        t0 = min(int(r[2][r[2][:, 0] > 0, 1].min()) for r in rep)
+        row = []
+        for r in rep:
+            rec = r[2][r[2][:, 0] > 0]
+            row.append(((rec[:, 1].min() - t0) / 100.0, (rec[:, 1:].max() - t0) / 100.0))
+        tl.append(row)
+    tl = np.median(np.asarray(tl), axis=0)
+    lines.append("# timeline (first start .. last mark): " +
+                 ", ".join(f"{a:.2f}..{b:.2f}" for a, b in tl) + f"; decode span {tl[-1][1]:.2f}")
     for li, (kind, level, _) in enumerate(reps[0]):
         recs = [r[li][2] for r in reps]
         name = {1: "tile", 2: "merge"}.get(kind, str(kind))

@@ -358,6 +358,52 @@ __device__ __forceinline__ void load_row(const void *logits, int64_t ld, int slo
     }
 }
 
+// A row's logits as loaded (16-byte pieces), before widening to fp32: loading into these and
+// widening only where the values are used keeps a load issued early from being waited on
+// at once (a widening inside a branch would make the branch join wait for it).
+template <int DT>
+struct RawRow;
+template <>
+struct RawRow<TCB_F32> {
+    f32x4 v[4];
+};
+template <>
+struct RawRow<TCB_BF16> {
+    u32x4 v[2];
+};
+template <int DT>
+__device__ __forceinline__ void load_row_raw(const void *logits, int64_t ld, int slot, int j, RawRow<DT> &raw) {
+    if constexpr (DT == TCB_F32) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(static_cast<const float *>(logits) + (size_t)slot * (size_t)ld);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw.v[i] = __builtin_nontemporal_load(p + 16 * i + j);
+    } else {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(logits) + (size_t)slot * (size_t)ld);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) raw.v[i] = __builtin_nontemporal_load(p + 16 * i + j);
+    }
+}
+template <int DT>
+__device__ __forceinline__ void widen_row(const RawRow<DT> &raw, float (&x)[kElems]) {
+    if constexpr (DT == TCB_F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[4 * i + 0] = raw.v[i][0];
+            x[4 * i + 1] = raw.v[i][1];
+            x[4 * i + 2] = raw.v[i][2];
+            x[4 * i + 3] = raw.v[i][3];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                x[8 * i + 2 * w] = __uint_as_float(raw.v[i][w] << 16);
+                x[8 * i + 2 * w + 1] = __uint_as_float(raw.v[i][w] & 0xffff0000u);
+            }
+    }
+}
+
 // Only the chunks of a row whose bit in `chunks` is set (16-byte pieces, as load_row reads
 // them); the others stay 0. Used where a row's children touch few of its sectors.
 template <int DT>
@@ -390,7 +436,7 @@ __device__ __forceinline__ void load_row_chunks(const void *logits, int64_t ld, 
 }
 
 // ---------------------------------------------------------------------- shared memory
-struct MergeSmem {
+struct alignas(16) MergeSmem {
     float s[kMergeCap];
     uint32_t f[kMergeCap];
     int32_t n[kMergeCap];
@@ -563,8 +609,10 @@ __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W
     // tiles' counts are all loaded at once: the counts of every tile the request could
     // have are read and those past the live tiles are dropped
     const bool fresh = ra.level() == 0;                // the initial state: one row, the root, score 0
-    const int rows = fresh ? 1 : W.rec[rp][q].rows;
-    const float sref = fresh ? 0.0f : W.score[ra.par()][ra.base()];
+    const int rows_ld = W.rec[rp][q].rows;             // read unconditionally (no branch join waits)
+    const float sref_ld = W.score[ra.par()][ra.base()];
+    const int rows = fresh ? 1 : rows_ld;
+    const float sref = fresh ? 0.0f : sref_ld;
     const int tmax = (ra.rmax() + kTileRows - 1) / kTileRows;
     const bool fin = finishes(T, F, ra);
     // a finishing request: every row's back-pointers of all levels are loaded at once
@@ -796,11 +844,19 @@ struct RowsToMemory {
     __device__ void done(uint32_t k) const { write_next_record(W, q, ra, rp, k); }
 };
 
-// Rows of one tile of the next step, taken from the previous step's merge (FuseRows).
+// Rows of one tile of the next step, taken from the previous step's merge (FuseRows), with
+// their child sets when the window merge has loaded them (info true).
 struct FuseRows {
     int32_t node[kTileRows];
     float score[kTileRows], phi[kTileRows];
+    RowInfo ri[kTileRows];
     float sref;                                       // the best new row's key
+    uint32_t info;                                    // ri holds the rows' child sets
+    // window merge: per source tile, its first staged entry and the staged entries before it
+    // (window bins), its entries of the first bin and their offsets
+    uint32_t wst[kMaxTilesPerReq], woff[kMaxTilesPerReq + 1];
+    uint32_t wfirst[kMaxTilesPerReq], foff[kMaxTilesPerReq + 1];
+    uint32_t blo, bhi, bfirst, nfirst, glo, k;
 };
 
 // The previous step's merge inside a tile of the next step: every tile of the request
@@ -828,6 +884,200 @@ struct RowsToTile {
     }
 };
 
+
+// The child set of internal node `n` at depth `level` (RowInfo): its child range and, at
+// depths stored with masks, its mask (elsewhere the mask of row 0 is read and ignored: the
+// image always holds one). Unconditional loads only, so no branch join waits for them.
+__device__ __forceinline__ RowInfo load_row_info(const TrieDev &T, uint32_t n, int level) {
+    RowInfo ri;
+    ri.cb = T.child_begin[n];
+    ri.ce = T.child_begin[n + 1];
+    const bool dense = level < T.mask_depths;
+    const uint4 *m = reinterpret_cast<const uint4 *>(T.mask + (size_t)(dense ? n : 0u) * 8);
+    const uint4 a = m[0], b = m[1];
+    ri.mask[0] = a.x; ri.mask[1] = a.y; ri.mask[2] = a.z; ri.mask[3] = a.w;
+    ri.mask[4] = b.x; ri.mask[5] = b.y; ri.mask[6] = b.z; ri.mask[7] = b.w;
+    ri.pad[0] = ri.pad[1] = 0u;
+    return ri;
+}
+
+// The previous step's merge inside tile `tile` of the next step, for this tile's rows only:
+// the rows of ranks [64 tile, 64 tile + 64) lie in the score bins b_lo .. b_hi, so only the
+// candidates of those bins are staged (plus those of the request's first non-empty bin, for
+// the best row's key). Staged entries are grouped by bin in LDS (a bin's group starts at the
+// kept entries of the window's better bins), and an entry's rank is the kept entries of
+// better bins plus the better entries of its own bin. The child sets of the staged
+// candidates are loaded while they are ranked. Rows go to Z and to the row buffers; tile 0
+// writes the request's record. Returns false (nothing written) when the window would stage
+// more than kWinCap entries (massive ties); the caller then merges the whole request.
+// pa: the request as its previous step saw it; rpp: the record buffer that step read.
+// issue(): called once, right after the candidates' loads are issued (or before returning
+// false): the caller's own loads go there, behind the merge's, since a wait for a load also
+// waits for every load issued before it.
+template <class Issue>
+__device__ __forceinline__ bool window_merge(const TrieDev &T, const WaveDev &W, int q, const ReqArg pa, int rpp,
+                                             int tile, MergeSmem &M, FuseRows &Z, Issue issue) {
+    const int tid = threadIdx.x;
+    const int MT = W.MT, CAPT = W.CAPT;
+    const int cpar = pa.level() & 1;                  // the buffers the previous step's tiles wrote
+    const uint16_t *tc = W.tcum[cpar] + (size_t)q * MT * kBins;
+    const size_t reg0 = (size_t)q * MT * CAPT;
+    const bool fresh = pa.level() == 0;
+    const int tmax = (pa.rmax() + kTileRows - 1) / kTileRows;
+    // 1. request-wide cumulative counts (thread = bin); the first 8 tiles' own counts stay
+    //    in registers for the staging ranges. Every load of this phase is issued at once and
+    //    unconditionally (indices clamped to the request's tiles), values dropped after
+    const int rows_ld = W.rec[rpp][q].rows;
+    const float sref_ld = W.score[pa.par()][pa.base()];
+    uint32_t a8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a8[u] = tc[(size_t)min(u, tmax - 1) * kBins + tid];
+    if (tid == 0) Z.info = 0u;
+    const int rows = fresh ? 1 : rows_ld;
+    const float sref = fresh ? 0.0f : sref_ld;
+    const int ntile = min((rows + kTileRows - 1) / kTileRows, tmax);
+    uint32_t g = 0u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        a8[u] = u < ntile ? a8[u] : 0u;
+        g += a8[u];
+    }
+    for (int jt = 8; jt < ntile; ++jt) g += tc[(size_t)jt * kBins + tid];   // beams wider than 512
+    auto tile_count = [&](int jt) {                   // this bin's cumulative count in tile jt
+        return jt < 8 ? a8[jt & 7] : (uint32_t)tc[(size_t)jt * kBins + tid];
+    };
+    M.G[tid] = g;
+    M.cur[tid] = 0u;                                  // per-bin cursors of the grouping
+    trace_mark(W, 8);                                 // the counts have arrived
+    __syncthreads();
+    const uint32_t Ktot = M.G[kBins - 1];
+    const uint32_t k = min((uint32_t)pa.width(), Ktot);
+    const uint32_t lo = (uint32_t)(tile * kTileRows);
+    if (lo >= k) {                                    // no row of this tile survives (never tile 0: k >= 1)
+        if (tile == 0) write_next_record(W, q, pa, rpp, k);
+        if (tid == 0) Z.k = k;
+        return true;
+    }
+    const uint32_t hi = min(lo + (uint32_t)kTileRows, k) - 1u;
+    const uint32_t gprev = tid ? M.G[tid - 1] : 0u;
+    const uint32_t gnext = tid + 1 < kBins ? M.G[tid + 1] : 0xFFFFFFFFu;
+    // each bin's thread finds its roles at once: the bins holding ranks lo (b_lo) and hi
+    // (b_hi), the bin before b_lo, and the first non-empty bin; per source tile they record
+    // the tile's own cumulative counts there (the window is [count at b_lo - 1, count at
+    // b_hi) of each tile; the first bin's entries are the first ones of each tile)
+    if (gprev <= lo && lo < g) {
+        Z.blo = (uint32_t)tid;
+        Z.glo = gprev;
+    }
+    // (the first 8 tiles' counts from registers, unrolled; wider beams read the rest again)
+    auto put = [&](uint32_t *dst) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (u < ntile) dst[u] = a8[u];
+        for (int jt = 8; jt < ntile; ++jt) dst[jt] = tile_count(jt);
+    };
+    if (gprev <= hi && hi < g) {
+        Z.bhi = (uint32_t)tid;
+        put(Z.woff + 1);                              // end offsets, turned into lengths below
+    }
+    if (g <= lo && lo < gnext) put(Z.wst);
+    if (lo < M.G[0] && tid < ntile) Z.wst[tid] = 0u;  // b_lo = 0
+    if (gprev == 0u && g > 0u) {
+        Z.bfirst = (uint32_t)tid;
+        Z.nfirst = g;
+        put(Z.wfirst);
+    }
+    __syncthreads();
+    trace_mark(W, 11);                                // window bins found
+    const uint32_t blo = Z.blo, bfirst = Z.bfirst, glo = Z.glo;
+    if (tid < 64) {                                   // lengths -> exclusive offsets (one wave)
+        const uint32_t len = tid < ntile ? Z.woff[tid + 1] - Z.wst[tid] : 0u;
+        const uint32_t incl = wave_incl_scan(len);
+        const uint32_t flen = tid < ntile ? Z.wfirst[tid] : 0u;
+        const uint32_t fincl = wave_incl_scan(flen);
+        if (tid < ntile) {
+            Z.woff[tid + 1] = incl;
+            Z.foff[tid + 1] = fincl;
+        }
+        if (tid == 0) {
+            Z.woff[0] = 0u;
+            Z.foff[0] = 0u;
+        }
+    }
+    __syncthreads();
+    trace_mark(W, 12);                                // staging offsets
+    const uint32_t nwin = Z.woff[ntile];
+    const uint32_t nfirst = bfirst < blo ? Z.nfirst : 0u;   // first-bin entries staged after the window
+    const uint32_t nst = nwin + nfirst;               // >= 1: rank lo lies in the window
+    // 2. stage: entry p < nwin from the window, then the first bin's entries of every tile
+    //    (they lie at the start of each tile's region). The load is issued by every thread
+    //    (index clamped into the staged range), so the caller's loads follow it at one point
+    const bool staged = (uint32_t)tid < nst;
+    const uint32_t p = min((uint32_t)tid, nst - 1u);
+    const bool inwin = p < nwin;
+    const uint32_t pp = inwin ? p : p - nwin;
+    int jw = 0, jf = 0;                               // the source tile of entry p
+#pragma unroll
+    for (int u = 1; u < 8; ++u) {
+        jw += (u < ntile && Z.woff[u] <= pp) ? 1 : 0;
+        jf += (u < ntile && Z.foff[u] <= pp) ? 1 : 0;
+    }
+    for (int u = 8; u < ntile; ++u) {
+        jw += Z.woff[u] <= pp ? 1 : 0;
+        jf += Z.foff[u] <= pp ? 1 : 0;
+    }
+    const int jt = inwin ? jw : jf;
+    const uint32_t at = inwin ? Z.wst[jw] + (pp - Z.woff[jw]) : pp - Z.foff[jf];
+    const Cand c = W.cand[cpar][reg0 + (size_t)jt * CAPT + min(at, (uint32_t)CAPT - 1u)];
+    issue();
+    if (nst > (uint32_t)kWinCap) return false;
+    // the candidate's child set, loaded now and used only if the entry is one of this
+    // tile's rows; loaded unconditionally (another node of the depth stands in for a
+    // candidate off the depth), so that no branch join makes the staging below wait for it
+    const int level = pa.level() + 1;
+    const bool want = inwin && (uint32_t)c.n >= T.off[level] && (uint32_t)c.n < T.off[level + 1];
+    RowInfo ri = load_row_info(T, want ? (uint32_t)c.n : T.off[level], level);
+    const uint32_t b = score_bin(sref, c.s);
+    // grouped by bin: bin b's entries start after the window's entries of better bins
+    uint64_t *gk = reinterpret_cast<uint64_t *>(M.n);
+    const uint64_t key = ((uint64_t)f2ord(c.s) << 32) | (uint64_t)(~c.f);   // larger: better
+    const uint32_t gb = b ? M.G[b - 1] : 0u;          // kept entries of better bins
+    uint32_t st = 0u, en = 0u;
+    if (staged) {
+        st = inwin ? gb - glo : nwin;
+        en = inwin ? M.G[b] - glo : nwin + nfirst;
+        gk[st + atomicAdd(&M.cur[b], 1u)] = key;
+    }
+    trace_mark(W, 13);                                // thread 0's candidate arrived and grouped
+    __syncthreads();
+    trace_mark(W, 9);                                 // staged
+    // 3. ranks
+    if (staged) {
+        uint32_t r = gb;
+        uint32_t i = st;
+        for (; i + 4u <= en; i += 4u)
+            r += (gk[i] > key ? 1u : 0u) + (gk[i + 1] > key ? 1u : 0u) + (gk[i + 2] > key ? 1u : 0u) +
+                 (gk[i + 3] > key ? 1u : 0u);
+        for (; i < en; ++i) r += gk[i] > key ? 1u : 0u;
+        if (r == 0u) Z.sref = c.s;
+        if (inwin && r >= lo && r <= hi) {
+            const uint32_t w = r - lo;
+            Z.node[w] = c.n;
+            Z.score[w] = c.s;
+            Z.phi[w] = c.phi;
+            if (want) Z.ri[w] = ri;
+            else Z.ri[w] = RowInfo{};
+            write_new_row(W, pa, r, c.s, c.f, c.n, c.phi);
+        }
+    }
+    if (tile == 0) write_next_record(W, q, pa, rpp, k);
+    if (tid == 0) {
+        Z.k = k;
+        Z.info = 1u;
+    }
+    trace_mark(W, 10);                                // ranked, rows issued
+    return true;
+}
 
 // ---------------------------------------------------------------------- tile kernel
 // Per tile of 64 rows: masked log-softmax, then a superset of the tile's top-n.
@@ -920,6 +1170,93 @@ __device__ __forceinline__ double row16_max_d(double v) {
     return v;
 }
 
+// Masked log-softmax (sampled steps: of x / T) of one row held by a 16-lane group (lane j
+// holds the elements e of codes code_of(e, j)) and the keys of its candidates: codes
+// outside the support count as -inf. valid: this lane's candidates; ok: the row's node is
+// valid (the LEVEL support is every code of a valid row). On return x[e] is candidate e's
+// key (-inf off the candidates), ph[e] its log-probability (sampled steps) and lbest the
+// lane's best key. The 16 lanes of the group call it together (DPP reductions).
+template <int DT, int NORM, bool SAMPLE>
+__device__ __forceinline__ void score_row(const StepReqs &R, int q, int level, int r, int j, int V, bool ok,
+                                          uint32_t valid, float sr, float pr, float (&x)[kElems],
+                                          float (&ph)[SAMPLE ? kElems : 1], float &lbest) {
+    float lse = 0.0f;
+    uint32_t sup = valid;
+    if constexpr (NORM == TCB_NORM_LEVEL) {
+        sup = 0u;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) sup |= (ok && code_of<DT>(e, j) < V) ? (1u << e) : 0u;
+    }
+    if constexpr (!SAMPLE) {
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) x[e] = ((sup >> e) & 1u) ? x[e] : -INFINITY;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) mx = fmaxf(mx, x[e]);
+        float lm = mx;                            // this lane's best candidate logit
+        if constexpr (NORM == TCB_NORM_LEVEL) {
+            lm = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < kElems; ++e) lm = fmaxf(lm, ((valid >> e) & 1u) ? x[e] : -INFINITY);
+        }
+        mx = row16_max(mx);
+        const float mxl = mx * kLog2e;
+        float sum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) sum += __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -mxl));
+        sum = row16_sum(sum);
+        lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+        lbest = sr + (lm - lse);
+        // from here on x[e] is the candidate's score (-inf off the child set)
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) {
+            float sc = sr + (x[e] - lse);
+            if constexpr (NORM == TCB_NORM_LEVEL) sc = ((valid >> e) & 1u) ? sc : -INFINITY;
+            x[e] = sc;
+        }
+    } else {
+        // the same log-softmax of x / T, leaving x unscaled
+        const float it = R.inv_temp;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) mx = fmaxf(mx, ((sup >> e) & 1u) ? x[e] * it : -INFINITY);
+        mx = row16_max(mx);
+        const float mxl = mx * kLog2e;
+        float sum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e)
+            sum += __builtin_amdgcn_exp2f(fmaf(((sup >> e) & 1u) ? x[e] * it : -INFINITY, kLog2e, -mxl));
+        sum = row16_sum(sum);
+        lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+        // Gumbel top-k without replacement over SIDs (stochastic beam search): child c
+        // draws g_c = phi_c + Gumbel noise = (pr - lse) + t_c, t_c = x_c / T + Gumbel;
+        // its key is g_c conditioned on the siblings' maximum z equalling the row's key.
+        // t_c and the gap t* - t_c are formed in float64 from the unscaled logit.
+        // From here on x[e] is the child's key.
+        const uint64_t sh = splitmix64(R.seed);
+        auto t_of = [&](int e) -> double {
+            const double u = noise_uniform(sh, (uint32_t)q, (uint32_t)level, (uint32_t)r,
+                                           (uint32_t)code_of<DT>(e, j));
+            return (double)x[e] * R.inv_temp_d - log(-log(u));
+        };
+        double tmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) {
+            ph[e] = pr + (x[e] * it - lse);
+            if ((valid >> e) & 1u) tmax = fmax(tmax, t_of(e));
+        }
+        tmax = row16_max_d(tmax);
+        const float pz = (float)((double)sr - (double)pr + (double)lse - tmax);   // pk - z
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) {
+            float key = -INFINITY;
+            if ((valid >> e) & 1u) key = conditioned_key(sr, pz, (float)(tmax - t_of(e)));
+            x[e] = key;
+            lbest = fmaxf(lbest, key);
+        }
+    }
+}
+
 // The work of one tile (request ql of the launch, tile `tile`); it returns early where the
 // tile has nothing to do (every return is uniform over the workgroup). With MERGE (the
 // request's only tile) the kept candidates go to LDS and the tile ranks them and writes
@@ -974,33 +1311,83 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
     // at depths with few children per row the logits wait for the trie and only the
     // 16-byte pieces holding a child are read (the rest is masked off either way)
     const bool gather = VEC && ra.gather();
+    // the row's logits, unless they wait for the trie (gather): issued unconditionally with
+    // 16-byte pieces (a row past the request's bound reads its last possible row, dropped)
+    const int slot_c = base + min(r, ra.rmax() - 1);
+    RawRow<DT> raw;
+    auto issue_logits = [&]() {
+        if constexpr (VEC) {
+            // the empty asm pins the loads here: their address would otherwise let the
+            // compiler hoist them to the kernel's start, ahead of the merge's loads
+            int sl = slot_c;
+            asm volatile("" : "+v"(sl));
+            load_row_raw<DT>(logits, ld, sl, j, raw);
+        }
+    };
+    // a step that first does the previous merge issues them behind the merge's loads, with
+    // no branch around them (such a step never gathers: its rows' nodes come from the merge)
+    if (!(FUSE && ra.pending()) && !gather) issue_logits();
     int rows;
     float sref;                                       // best row of the request
+    // the row's child set, where it came with the row (from the previous step's merge in
+    // this kernel, or stored by a first step): this lane's mask words and the child range
+    const bool dense_depth = level < T.mask_depths;
+    bool have_info = false;
+    uint32_t mw[CH], icb = 0u, ice = 0u;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) mw[i] = 0u;
     if (FUSE && ra.pending()) {
         // the previous step's merge: a row's logits do not depend on it (they are indexed
-        // by slot), so they are issued first; the row state then comes from the merge
-        if (in_range && !gather) load_row<DT, VEC>(logits, ld, base + r, j, V, x);
-        uint32_t k = 0u;
+        // by slot), so they were issued first; the row state then comes from the merge
+        if (!VEC && in_range) load_row<DT, VEC>(logits, ld, base + r, j, V, x);
         const ReqArg pa = ra.prev_step();
-        merge_request(T, W, StepFin{}, q, pa, rp ^ 1, *M, sel, nullptr, RowsToTile{W, pa, q, rp ^ 1, tile, *Z, k});
+        if (!window_merge(T, W, q, pa, rp ^ 1, tile, *M, *Z, issue_logits)) {
+            uint32_t k = 0u;
+            merge_request(T, W, StepFin{}, q, pa, rp ^ 1, *M, sel, nullptr, RowsToTile{W, pa, q, rp ^ 1, tile, *Z, k});
+            if (tid == 0) Z->k = k;
+        }
         __syncthreads();
         trace_mark(W, 2);                             // previous merge done
-        rows = (int)k;
+        rows = (int)Z->k;
         sref = Z->sref;
+        have_info = Z->info != 0u;
         if (r < rows) {
             nd = Z->node[rt];
             sr = Z->score[rt];
             if constexpr (SAMPLE) pr = Z->phi[rt];
+            if (have_info) {
+#pragma unroll
+                for (int i = 0; i < CH; ++i) mw[i] = Z->ri[rt].mask[(i * SPAN + j * CW) >> 5];
+                icb = Z->ri[rt].cb;
+                ice = Z->ri[rt].ce;
+            }
         }
     } else {
-        rows = fresh ? 1 : W.rec[rp][q].rows;
-        sref = fresh ? 0.0f : W.score[cp][base];
+        // the row state, loaded unconditionally with the logits (a fresh request's first step
+        // uses its known initial state instead; rows past the bound are dropped)
+        const int rows_ld = W.rec[rp][q].rows;
+        const float sref_ld = W.score[cp][base];
+        const int32_t nd_ld = W.node[cp][slot_c];
+        const float sr_ld = W.score[cp][slot_c];
+        float pr_ld = 0.0f;
+        if constexpr (SAMPLE) pr_ld = W.phi[cp][slot_c];
+        have_info = ra.rows_info();
+        if (have_info) {
+            const RowInfo *ri = W.rinfo + slot_c;
+            if (dense_depth) {
+#pragma unroll
+                for (int i = 0; i < CH; ++i) mw[i] = ri->mask[(i * SPAN + j * CW) >> 5];
+            }
+            icb = ri->cb;
+            ice = ri->ce;
+        }
+        if (!VEC && in_range) load_row<DT, VEC>(logits, ld, slot_c, j, V, x);
+        rows = fresh ? 1 : rows_ld;
+        sref = fresh ? 0.0f : sref_ld;
         if (in_range) {
-            const int slot = base + r;
-            nd = fresh ? 0 : W.node[cp][slot];
-            sr = fresh ? 0.0f : W.score[cp][slot];
-            if constexpr (SAMPLE) pr = fresh ? 0.0f : W.phi[cp][slot];
-            if (!gather) load_row<DT, VEC>(logits, ld, slot, j, V, x);
+            nd = fresh ? 0 : nd_ld;
+            sr = fresh ? 0.0f : sr_ld;
+            if constexpr (SAMPLE) pr = fresh ? 0.0f : pr_ld;
         }
     }
     if (tile * kTileRows >= rows) return false;              // a tile with no live row
@@ -1008,8 +1395,8 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
     const bool wave_live = tile * kTileRows + wave * kRowsPerWave < rows;
 
     // 2. the row's node: first child id and this lane's child bits (chunk i holds the
-    //    CW codes i * SPAN + j * CW ...)
-    const bool dense_depth = level < T.mask_depths;
+    //    CW codes i * SPAN + j * CW ...), from the child set that came with the row or
+    //    from the trie
     const uint32_t lo_id = T.off[level], hi_id = T.off[level + 1];
     bool ok = false;
     uint32_t cb = 0u, ce = 0u;
@@ -1020,15 +1407,27 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
         const uint32_t n = (uint32_t)nd;
         if (n >= lo_id && n < hi_id) {
             ok = true;
-            cb = T.child_begin[n];
-            if (dense_depth) {
+            if (have_info) {
+                cb = icb;
+                ce = ice;
+                if (dense_depth) {
 #pragma unroll
-                for (int i = 0; i < CH; ++i) {
-                    const int c0 = i * SPAN + j * CW;
-                    bits[i] = (T.mask[(size_t)n * 8 + (c0 >> 5)] >> (c0 & 31)) & ((1u << CW) - 1u);
+                    for (int i = 0; i < CH; ++i) {
+                        const int c0 = i * SPAN + j * CW;
+                        bits[i] = (mw[i] >> (c0 & 31)) & ((1u << CW) - 1u);
+                    }
                 }
             } else {
-                ce = T.child_begin[n + 1];
+                cb = T.child_begin[n];
+                if (dense_depth) {
+#pragma unroll
+                    for (int i = 0; i < CH; ++i) {
+                        const int c0 = i * SPAN + j * CW;
+                        bits[i] = (T.mask[(size_t)n * 8 + (c0 >> 5)] >> (c0 & 31)) & ((1u << CW) - 1u);
+                    }
+                } else {
+                    ce = T.child_begin[n + 1];
+                }
             }
         } else if (j == 0 && !(NORM == TCB_NORM_OPEN && nd == -1)) {   // -1: off the catalog (open)
             atomicOr(W.err, kErrBadNode);
@@ -1059,6 +1458,9 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
             bits[i] = ok ? (cm[c0 >> 5] >> (c0 & 31)) & ((1u << CW) - 1u) : 0u;
         }
     }
+    if constexpr (VEC) {
+        if (!gather) widen_row<DT>(raw, x);           // the logits issued at the start
+    }
     if (gather && live) {
         uint32_t chunks = 0u;
 #pragma unroll
@@ -1082,84 +1484,11 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
         for (int e = 0; e < kElems; ++e) valid |= (live && code_of<DT>(e, j) < V) ? (1u << e) : 0u;
     }
 
-    // 3. masked log-softmax (sampled steps: of x / T); codes outside the support become -inf
-    float lse = 0.0f, lbest = -INFINITY;
+    // 3. masked log-softmax and the candidates' keys
+    float lbest = -INFINITY;
     float ph[SAMPLE ? kElems : 1];                    // sampled steps: the candidates' log-probabilities
     if (wave_live) {
-        uint32_t sup = valid;
-        if constexpr (NORM == TCB_NORM_LEVEL) {
-            sup = 0u;
-#pragma unroll
-            for (int e = 0; e < kElems; ++e) sup |= (ok && code_of<DT>(e, j) < V) ? (1u << e) : 0u;
-        }
-        if constexpr (!SAMPLE) {
-#pragma unroll
-            for (int e = 0; e < kElems; ++e) x[e] = ((sup >> e) & 1u) ? x[e] : -INFINITY;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < kElems; ++e) mx = fmaxf(mx, x[e]);
-            float lm = mx;                            // this lane's best candidate logit
-            if constexpr (NORM == TCB_NORM_LEVEL) {
-                lm = -INFINITY;
-#pragma unroll
-                for (int e = 0; e < kElems; ++e) lm = fmaxf(lm, ((valid >> e) & 1u) ? x[e] : -INFINITY);
-            }
-            mx = row16_max(mx);
-            const float mxl = mx * kLog2e;
-            float sum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < kElems; ++e) sum += __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -mxl));
-            sum = row16_sum(sum);
-            lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
-            lbest = sr + (lm - lse);
-            // from here on x[e] is the candidate's score (-inf off the child set)
-#pragma unroll
-            for (int e = 0; e < kElems; ++e) {
-                float sc = sr + (x[e] - lse);
-                if constexpr (NORM == TCB_NORM_LEVEL) sc = ((valid >> e) & 1u) ? sc : -INFINITY;
-                x[e] = sc;
-            }
-        } else {
-            // the same log-softmax of x / T, leaving x unscaled
-            const float it = R.inv_temp;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < kElems; ++e) mx = fmaxf(mx, ((sup >> e) & 1u) ? x[e] * it : -INFINITY);
-            mx = row16_max(mx);
-            const float mxl = mx * kLog2e;
-            float sum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < kElems; ++e)
-                sum += __builtin_amdgcn_exp2f(fmaf(((sup >> e) & 1u) ? x[e] * it : -INFINITY, kLog2e, -mxl));
-            sum = row16_sum(sum);
-            lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
-            // Gumbel top-k without replacement over SIDs (stochastic beam search): child c
-            // draws g_c = phi_c + Gumbel noise = (pr - lse) + t_c, t_c = x_c / T + Gumbel;
-            // its key is g_c conditioned on the siblings' maximum z equalling the row's key.
-            // t_c and the gap t* - t_c are formed in float64 from the unscaled logit.
-            // From here on x[e] is the child's key.
-            const uint64_t sh = splitmix64(R.seed);
-            auto t_of = [&](int e) -> double {
-                const double u = noise_uniform(sh, (uint32_t)q, (uint32_t)level, (uint32_t)r,
-                                               (uint32_t)code_of<DT>(e, j));
-                return (double)x[e] * R.inv_temp_d - log(-log(u));
-            };
-            double tmax = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < kElems; ++e) {
-                ph[e] = pr + (x[e] * it - lse);
-                if ((valid >> e) & 1u) tmax = fmax(tmax, t_of(e));
-            }
-            tmax = row16_max_d(tmax);
-            const float pz = (float)((double)sr - (double)pr + (double)lse - tmax);   // pk - z
-#pragma unroll
-            for (int e = 0; e < kElems; ++e) {
-                float key = -INFINITY;
-                if ((valid >> e) & 1u) key = conditioned_key(sr, pz, (float)(tmax - t_of(e)));
-                x[e] = key;
-                lbest = fmaxf(lbest, key);
-            }
-        }
+        score_row<DT, NORM, SAMPLE>(R, q, level, r, j, V, ok, valid, sr, pr, x, ph, lbest);
     } else {
 #pragma unroll
         for (int e = 0; e < kElems; ++e) x[e] = -INFINITY;
@@ -1413,15 +1742,201 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
     }
 }
 
+// ---------------------------------------------------------------------- first step
+// A launch whose stepped requests are all at their first step (one row: the root). One
+// workgroup of 256 threads per request: lanes 0..15 score the root's row exactly as a tile
+// does (same layout and arithmetic, so the rows equal the tile kernel's bit for bit);
+// every candidate (at most V <= 256 children) is then ranked by counting the better keys
+// in LDS, and the survivors are written in rank order. The root's children are the depth-1
+// nodes, so their child sets do not depend on the logits: they are loaded at the start and
+// stored with the new rows (WaveDev::rinfo), and the next step reads them with its rows
+// instead of waiting on the trie.
+struct alignas(16) FirstSmem {
+    uint64_t gk[256];                               // candidates' keys grouped by score bin
+    uint32_t ord[256];                              // key by code, order-preserving; 0: no candidate
+    float key[256], phi[256];
+    int32_t node[256];
+    RowInfo kid[256];                               // child sets of the depth-1 nodes
+    uint32_t bin0[kBins + 1];                       // bin counts, then each bin's first entry
+    uint32_t part[4];
+    uint32_t cm[8];                                 // the root's mask built from its child list
+};
+
+template <int DT, int NORM, bool VEC, bool SAMPLE>
+__global__ __launch_bounds__(256) void k_first(TrieDev T, WaveDev W, int rp, StepReqs R,
+                                               const void *__restrict__ logits, int64_t ld) {
+    constexpr int CH = Lay<DT>::CH, CW = Lay<DT>::CW, SPAN = 256 / CH;
+    __shared__ FirstSmem F;
+    const int ql = (int)blockIdx.x;
+    if (ql >= R.n) return;
+    const int q = R.q0 + ql;
+    const ReqArg ra = R.r[ql];
+    const int tid = threadIdx.x;
+    if (!ra.step()) {
+        if (tid == 0) W.rec[rp ^ 1][q] = W.rec[rp][q];   // not stepped: carried over
+        return;
+    }
+    trace_mark(W, 0);
+    trace_mark(W, 1);                                 // started
+    const int base = ra.base(), V = T.V, L = T.L;
+    const bool fin = finishes(T, R.fin, ra);
+    // the child sets of the depth-1 nodes, for the rows the next step will have
+    const uint32_t n1 = T.off[1], nk = T.off[2] - T.off[1];
+    const bool want_kids = !fin && L > 1 && (uint32_t)tid < nk;
+    // issued unconditionally (a stand-in internal node for the others: a depth-1 node, or the
+    // root when depth 1 holds the leaves), stored to LDS after the root's row
+    const RowInfo ki = load_row_info(T, L > 1 ? n1 + (want_kids ? (uint32_t)tid : 0u) : 0u, 1);
+    if (tid < 16) {
+        // the root's row, as a tile's 16-lane group holds it
+        const int j = tid;
+        float x[kElems];
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) x[e] = 0.0f;
+        load_row<DT, VEC>(logits, ld, base, j, V, x);
+        const uint32_t cb = T.child_begin[0];
+        uint32_t bits[CH];
+        if (0 < T.mask_depths) {
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int c0 = i * SPAN + j * CW;
+                bits[i] = (T.mask[c0 >> 5] >> (c0 & 31)) & ((1u << CW) - 1u);
+            }
+        } else {
+            const uint32_t ce = T.child_begin[1];
+            if (j < 8) F.cm[j] = 0u;
+            wave_lds_sync();
+            for (uint32_t a = (cb & ~3u) + 4u * (uint32_t)j; a < ce; a += 64u) {
+                const uint32_t wv = *reinterpret_cast<const uint32_t *>(T.child_code + a);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t idx = a + (uint32_t)k;
+                    if (idx >= cb && idx < ce) {
+                        const uint32_t c = (wv >> (8 * k)) & 255u;
+                        atomicOr(&F.cm[c >> 5], 1u << (c & 31));
+                    }
+                }
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int c0 = i * SPAN + j * CW;
+                bits[i] = (F.cm[c0 >> 5] >> (c0 & 31)) & ((1u << CW) - 1u);
+            }
+        }
+        if (W.validate) {
+            // as the tile kernel reads the row: with sector gathering only the 16-byte
+            // pieces that hold a child are read, hence checked
+            bool bad = false;
+#pragma unroll
+            for (int e = 0; e < kElems; ++e)
+                if (code_of<DT>(e, j) < V && !isfinite(x[e]) && (!(VEC && ra.gather()) || bits[e / CW] != 0u))
+                    bad = true;
+            if (bad) atomicOr(W.err, kErrNonFinite);
+        }
+        uint32_t tv = 0u;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) tv |= bits[i] << (i * CW);
+        uint32_t valid = tv;
+        if constexpr (NORM == TCB_NORM_OPEN) {
+            valid = 0u;
+#pragma unroll
+            for (int e = 0; e < kElems; ++e) valid |= code_of<DT>(e, j) < V ? (1u << e) : 0u;
+        }
+        float ph[SAMPLE ? kElems : 1];
+        float lbest = -INFINITY;
+        score_row<DT, NORM, SAMPLE>(R, q, 0, 0, j, V, true, valid, 0.0f, 0.0f, x, ph, lbest);
+        // child node ids as the tile kernel forms them
+        uint32_t pc = 0u;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) pc |= (uint32_t)__popc(bits[i]) << (8 * i);
+        const uint32_t rk = (row16_incl_scan(pc) - pc) + row16_sum_u(pc) * 0x01010100u;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) {
+            const int c = code_of<DT>(e, j);
+            const uint32_t below = tv & ((1u << e) - (1u << (e & ~(CW - 1))));
+            int32_t n = (int32_t)(cb + ((rk >> (8 * (e / CW))) & 255u) + (uint32_t)__popc(below));
+            if constexpr (NORM == TCB_NORM_OPEN) n = ((tv >> e) & 1u) ? n : -1;
+            F.ord[c] = ((valid >> e) & 1u) ? f2ord(x[e]) : 0u;   // every code 0..255 is one (e, j)
+            F.key[c] = x[e];
+            if constexpr (SAMPLE) F.phi[c] = ph[e];
+            else F.phi[c] = x[e];
+            F.node[c] = n;
+        }
+    }
+    if (want_kids) F.kid[tid] = ki;
+    // rank: candidates are grouped by score bin (1 / kBinRes nat below the root's score 0);
+    // a candidate's rank is the candidates of better bins plus the better ones of its own
+    // bin, by (score desc, code asc)
+    for (int i = tid; i <= kBins; i += 256) F.bin0[i] = 0u;
+    __syncthreads();
+    const uint32_t oo = F.ord[tid];
+    const bool cand = oo != 0u;
+    uint32_t b = 0u, within = 0u;
+    if (cand) {
+        b = score_bin(0.0f, F.key[tid]);
+        within = atomicAdd(&F.bin0[b], 1u);
+    }
+    __syncthreads();
+    // exclusive offsets of the 1024 bins, 4 per thread
+    {
+        const uint4 h = reinterpret_cast<const uint4 *>(F.bin0)[tid];
+        const uint32_t sum = h.x + h.y + h.z + h.w;
+        const uint32_t incl = wave_incl_scan(sum);
+        if ((tid & 63) == 63) F.part[tid >> 6] = incl;
+        __syncthreads();
+        uint32_t before = 0u;
+        for (int w = 0; w < (tid >> 6); ++w) before += F.part[w];
+        const uint32_t e0 = before + incl - sum;
+        reinterpret_cast<uint4 *>(F.bin0)[tid] = make_uint4(e0, e0 + h.x, e0 + h.x + h.y, e0 + h.x + h.y + h.z);
+        if (tid == 255) F.bin0[kBins] = before + incl;   // every candidate
+    }
+    __syncthreads();
+    const uint64_t key = ((uint64_t)oo << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)tid);   // larger: better
+    const uint32_t st = F.bin0[b];
+    if (cand) F.gk[st + within] = key;
+    const uint32_t nvalid = F.bin0[kBins];
+    __syncthreads();
+    trace_mark(W, 6);                                 // scored and grouped
+    const uint32_t k = min((uint32_t)ra.width(), nvalid);
+    if (cand) {
+        const uint32_t en = F.bin0[b + 1];
+        uint32_t rank = st;
+        for (uint32_t i = st; i < en; ++i) rank += F.gk[i] > key ? 1u : 0u;
+        if (rank < k) {
+            const int32_t node = F.node[tid];
+            if (fin) {
+                write_final_row(R.fin, L, W.Bmax, q, rank, 0ull, (uint32_t)tid, F.phi[tid], item_of(T, W, node));
+            } else {
+                write_new_row(W, ra, rank, F.key[tid], (uint32_t)tid, node, F.phi[tid]);
+                // the row's child set (zeros for an unconstrained row off the catalog)
+                const bool kid = (uint32_t)node - n1 < nk;
+                const uint4 *src = reinterpret_cast<const uint4 *>(&F.kid[kid ? (uint32_t)node - n1 : 0u]);
+                uint4 *dst = reinterpret_cast<uint4 *>(W.rinfo + base + (int)rank);
+#pragma unroll
+                for (int part = 0; part < 3; ++part) {
+                    const uint4 v = src[part];        // LDS read, then the choice on values
+                    const uint32_t keep = kid ? 0xFFFFFFFFu : 0u;
+                    dst[part] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+                }
+            }
+        }
+    }
+    if (fin) finish_request(T, W, R.fin, q, ra, rp, 1, k);
+    else write_next_record(W, q, ra, rp, k);
+    trace_mark(W, 7);                                 // ranked, rows issued
+}
+
 // ---------------------------------------------------------------------- tile launches
 template <int DT, int NORM, bool VEC, bool SAMPLE>
 void launch_tile_t(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
                           int64_t ld, int mode, hipStream_t s) {
     const int groups = (R.n + 7) / 8;
-    if (mode == 1) {
+    if (mode == kTileFirst) {
+        hipLaunchKernelGGL((k_first<DT, NORM, VEC, SAMPLE>), dim3(R.n), dim3(256), 0, s, t, w, rp, R, logits, ld);
+    } else if (mode == kTileMerge) {
         hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, true, false>), dim3(R.n), dim3(kThreads), 0, s, t, w, rp,
                            R, logits, ld);
-    } else if (mode == 2) {
+    } else if (mode == kTileFuse) {
         hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, false, true>), dim3(8 * groups * w.MT), dim3(kThreads), 0,
                            s, t, w, rp, R, logits, ld);
     } else {

@@ -138,9 +138,19 @@ hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s) {
     return hipGetLastError();
 }
 
+int tile_mode(const StepReqs &R, bool fuse) {
+    bool first = true;
+    for (int i = 0; i < R.n; ++i)
+        if (R.r[i].step() && R.r[i].level() != 0) first = false;
+    if (first) return kTileFirst;
+    if (fuse) return kTileFuse;
+    return tile_merges(R) ? kTileMerge : kTilePlain;
+}
+
 int tile_grid(const WaveDev &w, const StepReqs &R, bool fuse) {
     if (R.n <= 0) return 0;
-    if (!fuse && tile_merges(R)) return R.n;
+    const int mode = tile_mode(R, fuse);
+    if (mode == kTileFirst || mode == kTileMerge) return R.n;
     return 8 * ((R.n + 7) / 8) * w.MT;
 }
 
@@ -155,8 +165,7 @@ hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReq
     if (R.n <= 0) return hipSuccess;
     // 16-byte row pieces: ld a multiple of 4 (fp32) or 8 (bf16) elements, 16-byte base
     const bool vec = t.V == 256 && (ld % (dtype == TCB_F32 ? 4 : 8)) == 0 && ((uintptr_t)logits % 16) == 0;
-    // 1: every request merged inside its only tile; 2: pending merges first; 0: plain
-    const int merge = fuse ? 2 : tile_merges(R) ? 1 : 0;
+    const int merge = tile_mode(R, fuse);
     if (dtype == TCB_F32) {
         return sampled ? launch_tile_f32_sampled(t, w, rp, R, logits, ld, vec, merge, s)
                        : launch_tile_f32(t, w, rp, R, logits, ld, vec, merge, s);
@@ -166,7 +175,10 @@ hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReq
     }
 }
 
-bool merged_in_tile(const StepReqs &R, bool fuse) { return !fuse && tile_merges(R); }
+bool merged_in_tile(const StepReqs &R, bool fuse) {
+    const int mode = tile_mode(R, fuse);
+    return mode == kTileFirst || mode == kTileMerge;
+}
 
 hipError_t launch_merge(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, bool in_tile,
                         hipStream_t s) {

@@ -35,7 +35,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
     int32_t MT = 0, CAPT = 0;
-    size_t node[2]{}, score[2]{}, phi[2]{}, parent_slot = 0, hist = 0, rec[2]{};
+    size_t node[2]{}, score[2]{}, phi[2]{}, parent_slot = 0, hist = 0, rec[2]{}, rinfo = 0;
     size_t cand = 0, tcum = 0, lmx = 0, err = 0;
     size_t fin_sids = 0, fin_scores = 0, fin_items = 0, fin_counts = 0, total = 0;
 };
@@ -59,6 +59,7 @@ Layout make_layout(int L, int S, int R, int Bmax) {
     l.phi[1] = take(s * 4);
     l.parent_slot = take(s * 4);
     l.hist = take((size_t)L * s * 4);
+    l.rinfo = take(s * sizeof(tcb::RowInfo));
     l.rec[0] = take(r * sizeof(tcb::ReqRec));
     l.rec[1] = take(r * sizeof(tcb::ReqRec));
     const size_t ncand = r * (size_t)l.MT * (size_t)l.CAPT;
@@ -345,6 +346,7 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
     }
     w.parent_slot = (int32_t *)(ws + l.parent_slot);
     w.hist = (uint32_t *)(ws + l.hist);
+    w.rinfo = (tcb::RowInfo *)(ws + l.rinfo);
     w.rec[0] = (tcb::ReqRec *)(ws + l.rec[0]);
     w.rec[1] = (tcb::ReqRec *)(ws + l.rec[1]);
     {
@@ -475,7 +477,9 @@ static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out, int d
             const bool sparse = head && !open && b->w.norm == TCB_NORM_CHILDREN && step &&
                                 (b->read_mode == TCB_READ_GATHER ||
                                  (b->read_mode == TCB_READ_AUTO && (b->sparse_head_levels >> level & 1u)));
-            R.r[i].base_flags = rq.base | (gather || sparse ? 1 << 24 : 0) | (sparse ? 1 << 25 : 0) | (pend ? 1 << 26 : 0);
+            const bool rinfo = step && rq.rinfo;
+            R.r[i].base_flags = rq.base | (gather || sparse ? 1 << 24 : 0) | (sparse ? 1 << 25 : 0) | (pend ? 1 << 26 : 0) |
+                                (rinfo ? 1 << 27 : 0);
             R.r[i].bits = width | rmax << 13 | level << 26 | pre << 29 | (step ? 1u : 0u) << 30 | (level & 1u) << 31;
         }
     }
@@ -526,6 +530,12 @@ static tcb_status run_step(tcb_beams *b, hipStream_t s, HeadLaunch head, TileLau
     if (fuse) {
         for (auto &q : b->reqs) q.pending = false;
         b->merge_pending = false;
+    }
+    // rows made by a first-step kernel carry their child sets into the next step
+    for (const auto &R : args) {
+        const bool first = tcb::tile_mode(R, fuse) == tcb::kTileFirst;
+        for (int i = 0; i < R.n; ++i)
+            if (R.r[i].step()) b->reqs[(size_t)(R.q0 + i)].rinfo = first;
     }
     // defer this step's merge to the next step's tile kernel unless a request finishes now
     // or the tile kernel merged every request itself

@@ -28,6 +28,7 @@ struct tcb_beams {
     struct Req {
         bool used = false;
         bool pending = false;              // its last step's merge is deferred to its next step
+        bool rinfo = false;                // its rows carry their child sets (made by a first step)
         int32_t base = 0, width = 0, level = 0;
     };
     tcb::TrieDev tdev{};

@@ -28,6 +28,7 @@ constexpr float kBinRes = 32.0f;                      // bins per nat: 32 nats o
 static_assert(kBins == kThreads, "one bin per thread in the scans");
 constexpr int kTileCap = 4096;                        // candidates a tile keeps (its region)
 constexpr int kMergeCap = 4096;                       // candidates the merge stages in LDS
+constexpr int kWinCap = 1024;                         // candidates a tile's window merge stages
 static_assert(kTileCap >= TCB_MAX_WIDTH, "a tile's exact path keeps up to n_i candidates");
 static_assert(kMergeCap % kThreads == 0, "whole rounds of the workgroup");
 static_assert(kMergeCap >= TCB_MAX_WIDTH, "the exact merge path stages up to n_i survivors");
@@ -71,6 +72,14 @@ struct alignas(16) Cand {          // a tile's kept candidate, one 16-byte store
     float phi;                     // summed log-probability (equal to s at temperature 0)
 };
 
+// A row's child set as the next step reads it with the row (written where the row is made,
+// so the step needs no dependent trie load): the 256-bit child mask of the row's node (at
+// depths stored with masks), its first child id and the end of its child range.
+struct alignas(16) RowInfo {       // 48 bytes: three 16-byte pieces
+    uint32_t mask[8];
+    uint32_t cb, ce, pad[2];
+};
+
 struct WaveDev {
     int32_t *node[2];              // [S] trie node of each slot's row (ping-pong per request)
     float *score[2];               // [S] selection key of the row (ping-pong per request)
@@ -83,6 +92,7 @@ struct WaveDev {
     // previous step's candidates while writing their own
     Cand *cand[2];                 // [R][MT][CAPT]
     uint16_t *tcum[2];             // [R][MT][kBins]
+    RowInfo *rinfo;                // [S] child sets of rows made by a first step (ReqArg::rows_info)
     float *lmx;                    // [S][256] logits computed by the SID-range lm_head
     uint32_t *err;                 // sticky error / info bits
     // phase trace of this launch (diagnostics; nullptr: off): kTraceSlots words per
@@ -98,12 +108,16 @@ constexpr int kTraceSlots = TCB_TRACE_SLOTS;
 // loads need no device-side lookup. Only the live-row count stays on the device.
 struct ReqArg {
     int32_t base_flags;            // first slot (< 2^24) | gather << 24 | sparse head << 25 | merge pending << 26
+                                   // | rows carry their child sets << 27
     uint32_t bits;                 // width | rmax << 13 | level << 26 | pre << 29 | step << 30 | par << 31
     __host__ __device__ int base() const { return base_flags & 0xFFFFFF; }
     __host__ __device__ bool gather() const { return (base_flags >> 24) & 1; }        // children's sectors only
     __host__ __device__ bool sparse_head() const { return (base_flags >> 25) & 1; }   // lm_head: children's pieces only
     // the request's previous step left its merge to this step's tile kernel
     __host__ __device__ bool pending() const { return (base_flags >> 26) & 1; }
+    // the request's rows were made by a first-step kernel, which stored each row's child set
+    // in WaveDev::rinfo
+    __host__ __device__ bool rows_info() const { return (base_flags >> 27) & 1; }
     __host__ __device__ int width() const { return (int)(bits & 0x1FFFu); }
     __host__ __device__ int rmax() const { return (int)((bits >> 13) & 0x1FFFu); }   // bound on live rows
     __host__ __device__ int level() const { return (int)((bits >> 26) & 0x7u); }
@@ -159,8 +173,7 @@ struct FinBatch {
 };
 
 // The tile kernel of one logits type and sampling mode (compiled in its own translation
-// unit): mode 1 merges every request inside its only tile, 2 first does pending merges,
-// 0 plain; vec: rows read as 16-byte pieces.
+// unit) in one of the modes above; vec: rows read as 16-byte pieces.
 #define TCB_TILE_LAUNCHER(name)                                                                              \
     hipError_t name(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits, int64_t ld, \
                     bool vec, int mode, hipStream_t s)
@@ -169,6 +182,12 @@ TCB_TILE_LAUNCHER(launch_tile_bf16);
 TCB_TILE_LAUNCHER(launch_tile_f32_sampled);
 TCB_TILE_LAUNCHER(launch_tile_bf16_sampled);
 
+// The kernel launch_tile uses for one launch of R: kTileFirst when every stepped request
+// is at its first step (one row each; merged inside the kernel), else kTileFuse when
+// pending merges come first, kTileMerge when every request fits one tile (merged inside
+// the kernel), kTilePlain otherwise (k_merge or the next step merges).
+enum { kTilePlain = 0, kTileMerge = 1, kTileFuse = 2, kTileFirst = 3 };
+int tile_mode(const StepReqs &R, bool fuse);
 // workgroups of the tile kernel launch_tile would launch for R (phase-trace layout)
 int tile_grid(const WaveDev &w, const StepReqs &R, bool fuse);
 
@@ -189,8 +208,8 @@ hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepR
 // true when every stepped request of R has at most kTileRows rows: a tile kernel launched
 // without a pending merge (fuse false) then merges each request itself
 bool tile_merges(const StepReqs &R);
-// whether launch_tile(..., fuse) merged the requests of R inside the tile kernel: only the
-// plain launch does; a launch that first does pending merges (fuse) leaves this step's
+// whether launch_tile(..., fuse) merged the requests of R inside the tile kernel (first-step
+// and one-tile launches); a launch that first does pending merges (fuse) leaves this step's
 // candidates in memory for k_merge or the next step, whatever the requests' widths
 bool merged_in_tile(const StepReqs &R, bool fuse);
 // k_merge over the requests of R, unless in_tile (the tile kernel merged them already)
