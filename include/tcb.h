@@ -402,6 +402,19 @@ tcb_status tcb_score_catalog(const tcb_trie *t, int32_t n_users, const float *d_
                              int32_t *d_item, float *d_score, float *d_lse, void *d_ws,
                              size_t ws_bytes, void *stream);
 
+/* tcb_score_catalog for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same arguments and
+ * results without the workspace. The scratch is a static array of TCB_SCORE_STATIC_SCRATCH
+ * bytes per GPU, held until the process ends; calls on one GPU share it, so calls that
+ * overlap on one GPU (concurrent streams or threads) race. A call needing more scratch
+ * than that (tcb_score_workspace_bytes) returns TCB_E_WORKSPACE and launches nothing. No
+ * allocation happens. Errors as tcb_score_catalog. */
+#define TCB_SCORE_STATIC_SCRATCH (64u << 20)
+tcb_status tcb_score_catalog_static(const tcb_trie *t, int32_t n_users, const float *d_table,
+                                    int32_t table_kind, const void *d_user_vec, const void *d_sid_emb,
+                                    int32_t dim, float sid_weight, int32_t k, int32_t *d_leaf,
+                                    int32_t *d_item, float *d_score, float *d_lse, void *stream);
+
 /* Diagnostics: record HIP events around the two kernels (scan, selection) of each of
  * the next `capacity` tcb_score_catalog calls in this process (0..100000; 0 stops
  * recording and releases the events). */

@@ -19,6 +19,7 @@ TCB_NORM_CHILDREN, TCB_NORM_LEVEL, TCB_NORM_OPEN = 0, 1, 2
 TCB_READ_AUTO, TCB_READ_DENSE, TCB_READ_GATHER = 0, 1, 2
 TCB_TABLE_LOGPROB, TCB_TABLE_LOGITS = 0, 1
 TCB_SCORE_MAX_K = 512
+TCB_SCORE_STATIC_SCRATCH = 64 << 20
 TCB_MAX_L = 8
 TCB_MAX_WIDTH = 4096
 TCB_MASK_AUTO = -1
@@ -81,6 +82,7 @@ SIGNATURES = {
     "tcb_trie_upload_codes": (I32, [P, P, C.c_size_t, P]),
     "tcb_score_workspace_bytes": (I32, [P, I32, C.POINTER(C.c_size_t)]),
     "tcb_score_catalog": (I32, [P, I32, P, I32, P, P, I32, C.c_float, I32, P, P, P, P, P, C.c_size_t, P]),
+    "tcb_score_catalog_static": (I32, [P, I32, P, I32, P, P, I32, C.c_float, I32, P, P, P, P, P]),
     "tcb_score_enable_timing": (I32, [I32]),
     "tcb_score_timing": (I32, [C.POINTER(C.c_double), C.POINTER(C.c_double), C.POINTER(I32)]),
 }

@@ -308,8 +308,10 @@ def score_workspace_bytes(trie: Trie, max_users: int) -> int:
 
 
 def score_catalog(trie: Trie, table, k: int, table_kind: str = "logprob", user_vec=None,
-                  sid_emb=None, sid_weight: float = 1.0, want_lse: bool = True, workspace=None):
-    """Single-pass scoring of every valid SID for a batch of users (tcb_score_catalog).
+                  sid_emb=None, sid_weight: float = 1.0, want_lse: bool = True, workspace=None, out=None):
+    """Single-pass scoring of every valid SID for a batch of users (tcb_score_catalog;
+    ``workspace="static"``: tcb_score_catalog_static, the library's static scratch, with
+    ``out`` the caller's output tensors so that nothing is allocated).
 
     ``table``: float32 [U, L, V] on the device, per-position log-probabilities
     ("logprob") or raw logits ("logits"); ``user_vec`` bfloat16 [U, D] and ``sid_emb``
@@ -333,14 +335,18 @@ def score_catalog(trie: Trie, table, k: int, table_kind: str = "logprob", user_v
             raise ValueError("user_vec must be [U, D] and sid_emb [n_distinct, D]")
     kind = {"logprob": L.TCB_TABLE_LOGPROB, "logits": L.TCB_TABLE_LOGITS}[table_kind]
     dev = table.device
-    nb = score_workspace_bytes(trie, U)
-    if workspace is None or workspace.numel() < nb:
-        workspace = torch.empty(nb, dtype=torch.uint8, device=dev)
-    leaf = torch.empty((U, k), dtype=torch.int32, device=dev)
-    item = torch.empty((U, k), dtype=torch.int32, device=dev)
-    score = torch.empty((U, k), dtype=torch.float32, device=dev)
-    lse = torch.empty(U, dtype=torch.float32, device=dev) if want_lse else None
-    check(lib().tcb_score_catalog(trie.handle, U, _ptr(table), kind, _ptr(user_vec), _ptr(sid_emb), D,
-                                  float(sid_weight), int(k), _ptr(leaf), _ptr(item), _ptr(score), _ptr(lse),
-                                  _ptr(workspace), workspace.numel(), _stream()))
-    return {"leaf": leaf, "item": item, "score": score, "lse": lse}
+    if out is None:
+        out = {"leaf": torch.empty((U, k), dtype=torch.int32, device=dev),
+               "item": torch.empty((U, k), dtype=torch.int32, device=dev),
+               "score": torch.empty((U, k), dtype=torch.float32, device=dev),
+               "lse": torch.empty(U, dtype=torch.float32, device=dev) if want_lse else None}
+    args = (trie.handle, U, _ptr(table), kind, _ptr(user_vec), _ptr(sid_emb), D, float(sid_weight), int(k),
+            _ptr(out["leaf"]), _ptr(out["item"]), _ptr(out["score"]), _ptr(out["lse"]))
+    if workspace == "static":
+        check(lib().tcb_score_catalog_static(*args, _stream()))
+    else:
+        nb = score_workspace_bytes(trie, U)
+        if workspace is None or workspace.numel() < nb:
+            workspace = torch.empty(nb, dtype=torch.uint8, device=dev)
+        check(lib().tcb_score_catalog(*args, _ptr(workspace), workspace.numel(), _stream()))
+    return out

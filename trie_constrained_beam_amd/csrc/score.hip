@@ -32,6 +32,7 @@
 //                   and the log-normaliser from the scan's partials.
 // Every top-K is a radix selection on order-preserving keys with ties taken in ascending
 // position, so the result is deterministic.
+#include <mutex>
 #include <type_traits>
 
 #include "score_internal.h"
@@ -986,6 +987,30 @@ ScoreLayout score_layout(int L, int64_t n, int max_users) {
 
 hipError_t launch_score(const ScoreDev &a, hipStream_t s, const hipEvent_t *ev) {
     return a.L > 4 ? launch_w<true>(a, s, ev) : launch_w<false>(a, s, ev);
+}
+
+// The scratch of tcb_score_catalog_static, for callers that cannot allocate: one array per
+// GPU the library runs on, held until the process ends. Host code uses only the address
+// hipGetSymbolAddress gives for the current device, never the array's name.
+static __device__ __align__(256) uint8_t scratch[kStaticScoreScratch];
+
+hipError_t static_score_scratch(void **ptr, size_t *bytes) {
+    static std::mutex mu;
+    static void *dev_ptr[kMaxScratchDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (dev_ptr[dev] == nullptr) {                    // once per device, with it current
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        dev_ptr[dev] = p;
+    }
+    *ptr = dev_ptr[dev];
+    *bytes = kStaticScoreScratch;
+    return hipSuccess;
 }
 
 }  // namespace tcb

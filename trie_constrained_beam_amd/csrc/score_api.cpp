@@ -153,6 +153,26 @@ tcb_status tcb_score_catalog(const tcb_trie *t, int32_t n_users, const float *d_
     return TCB_OK;
 }
 
+tcb_status tcb_score_catalog_static(const tcb_trie *t, int32_t n_users, const float *d_table,
+                                    int32_t table_kind, const void *d_user_vec, const void *d_sid_emb,
+                                    int32_t dim, float sid_weight, int32_t k, int32_t *d_leaf,
+                                    int32_t *d_item, float *d_score, float *d_lse, void *stream) {
+    if (!t) return set_error(TCB_E_ARG, "score_catalog_static: null trie");
+    if (n_users <= 0) return set_error(TCB_E_ARG, "score_catalog_static: n_users must be > 0");
+    const size_t need = tcb::score_layout(t->L, t->n_distinct, n_users).total;
+    if (need > tcb::kStaticScoreScratch)
+        return set_error(TCB_E_WORKSPACE, "score_catalog_static: " + std::to_string(n_users) + " users x " +
+                                              std::to_string(t->n_distinct) + " SIDs need " + std::to_string(need) +
+                                              " bytes of scratch; the static scratch holds " +
+                                              std::to_string(tcb::kStaticScoreScratch));
+    void *ws = nullptr;
+    size_t cap = 0;
+    const hipError_t e = tcb::static_score_scratch(&ws, &cap);
+    if (e != hipSuccess) return hip_fail(e, "score_catalog_static: scratch address");
+    return tcb_score_catalog(t, n_users, d_table, table_kind, d_user_vec, d_sid_emb, dim, sid_weight, k, d_leaf,
+                             d_item, d_score, d_lse, ws, cap, stream);
+}
+
 tcb_status tcb_score_enable_timing(int32_t capacity) {
     if (capacity < 0 || capacity > 100000) return set_error(TCB_E_ARG, "score_enable_timing: capacity out of range");
     std::lock_guard<std::mutex> lk(g_timing.mu);

@@ -64,4 +64,11 @@ ScoreLayout score_layout(int L, int64_t n, int max_users);
 // ev: null, or 3 events recorded before the scan kernel, before the selection kernels and after
 hipError_t launch_score(const ScoreDev &a, hipStream_t s, const hipEvent_t *ev);
 
+// The static scratch of tcb_score_catalog_static on the current device: its address (taken
+// once per device) and size.
+constexpr size_t kStaticScoreScratch = TCB_SCORE_STATIC_SCRATCH;
+static_assert(TCB_SCORE_STATIC_SCRATCH == (64u << 20), "header and library agree");
+constexpr int kMaxScratchDevices = 64;
+hipError_t static_score_scratch(void **ptr, size_t *bytes);
+
 }  // namespace tcb
