@@ -13,13 +13,21 @@ larger than the 256 MB Infinity Cache, so every decode streams its logits from H
 Each decode is replayed as a captured HIP graph (``--graph 0``: eager launches).
 
 Also measured in the same run:
+  * the other workloads as legs of their own ("legs"): 1 request x beam 50 (L = 3, 20k
+    SIDs), 64 requests x beam 128 (L = 4, 1M Zipf SIDs, fp32), and the mixed decode wave
+    (256 requests of widths 50..512 admitted FIFO under 32,768 slots, L = 5, 8M SIDs; a
+    step there is one run of the whole workload), each with its tile kernel's roofline and
+    the oracle timed beside it;
+  * a 1 GiB device-to-device copy, the measured bandwidth beside the 8 TB/s spec;
   * per-kernel durations with HIP events on the launch stream (an eager pass);
   * the SID-range lm_head leg: 8 requests x beam 512, hidden 2048, its MFMA kernel
     against the bf16 dense peak;
   * the single-pass scoring leg: every SID of the same 4M catalog scored for 32 users
     (per-position logits plus a 64-dim SID-level term), top 512 kept per user; its scan
     kernel against the HBM peak;
-  * the CPU oracle on a bounded sample of the same workload (a baseline, not a target).
+  * the CPU oracle on a bounded sample of each workload, on every core (up to 16
+    processes) and on one core, with the CPU's model name (a baseline, not a target); for
+    the lm_head workload its fp64 product is timed apart from the steps.
 
 Prints one JSON line on stdout. Progress goes to stderr.
 """
@@ -82,41 +90,119 @@ def recorded_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
 _CPU = {}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
 def _oracle_request(i):
-    import oracle
-    wl, widths, xs = _CPU["wl"], _CPU["widths"], _CPU["xs"][i]
-    res = oracle.decode(_CPU["otrie"], widths[i],
-                        lambda t, pref: oracle.widen_logits(xs[t][:len(pref)], "bf16" if wl.bf16 else "f32"))
-    return sum(int(h["cand_parent"].max()) + 1 for h in res["history"])
-
-
-def cpu_baseline(wl, cat, seconds):
-    """The oracle decoding requests of this workload in a process pool (one request per
-    task) until ``seconds`` have passed; rows x steps per second of wall time."""
+    """One request of the workload decoded by the oracle (its logits drawn here, untimed
+    apart from the decode); returns (beam-rows x steps, seconds)."""
     import oracle
     from trie_constrained_beam_amd import synth
+    wl, w = _CPU["wl"], _CPU["widths"][i]
+    xs = [synth.logits_rowkeyed(wl.seed, t, i, w, wl.sigma, bf16=wl.bf16) for t in range(wl.L)]
+    t0 = time.perf_counter()
+    res = oracle.decode(_CPU["otrie"], w,
+                        lambda t, pref: oracle.widen_logits(xs[t][:len(pref)], "bf16" if wl.bf16 else "f32"))
+    el = time.perf_counter() - t0
+    return sum(int(h["cand_parent"].max()) + 1 for h in res["history"]), el
+
+
+def _oracle_lmhead_request(i):
+    """One request of the lm_head workload: per step the fp64 product of its live rows'
+    hidden states and the level's weights, then the step; returns (rows x steps, GEMM
+    seconds, step seconds)."""
+    import numpy as np
+    import oracle
+    wl, w, base = _CPU["wl"], _CPU["widths"][i], _CPU["bases"][i]
+    hid, wts = _CPU["hidden"], _CPU["weights"]
+    otrie = _CPU["otrie"]
+    prefixes = np.zeros(1, dtype=np.uint64)
+    scores = np.zeros(1)
+    rows, t_gemm, t_step = 0, 0.0, 0.0
+    for t in range(wl.L):
+        r = prefixes.size
+        rows += r
+        t0 = time.perf_counter()
+        x64 = oracle.lmhead_logits(hid[t][base:base + r], wts[t])
+        t1 = time.perf_counter()
+        h = oracle.expand_request(otrie, t, prefixes, scores, x64, w)
+        t2 = time.perf_counter()
+        t_gemm += t1 - t0
+        t_step += t2 - t1
+        prefixes, scores = h["prefix"], h["score"]
+    return rows, t_gemm, t_step
+
+
+def cpu_baseline(wl, cat, seconds, workers=None, lmhead=None):
+    """The oracle decoding requests of this workload (one request per task, round robin)
+    until ``seconds`` have passed, in ``workers`` processes (default: every core, at most
+    16) or in this process (workers = 1); rows x steps per second of wall time. lmhead:
+    (hidden [L] arrays, weights [L]) for the lm_head workload, whose fp64 GEMM is timed
+    separately from the steps."""
+    import oracle
     widths = list(wl.widths)
     _CPU.update(wl=wl, widths=widths, otrie=oracle.OracleTrie(cat),
-                xs=[[synth.logits_rowkeyed(wl.seed, t, i, w, wl.sigma, bf16=wl.bf16) for t in range(wl.L)]
-                    for i, w in enumerate(widths)])
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    workers = max(1, min(16, cores, len(widths)))
-    ctx = mp.get_context("fork")                 # before any GPU use in this process
-    done_rows, n_req = 0, 0
+                bases=[sum(widths[:i]) for i in range(len(widths))])
+    if lmhead is not None:
+        _CPU.update(hidden=lmhead[0], weights=lmhead[1])
+    fn = _oracle_lmhead_request if lmhead is not None else _oracle_request
+    cores = host_cores()
+    workers = workers or max(1, min(16, cores))
+    workers = min(workers, len(widths)) if lmhead is None else min(workers, len(widths))
+    done_rows, n_req, gemm_s, step_s = 0, 0, 0.0, 0.0
     t0 = time.perf_counter()
-    with ctx.Pool(workers) as pool:
+    if workers == 1:
         while time.perf_counter() - t0 < seconds:
-            batch = [(n_req + k) % len(widths) for k in range(workers)]
-            done_rows += sum(pool.map(_oracle_request, batch))
-            n_req += len(batch)
+            out = fn(n_req % len(widths))
+            done_rows += out[0]
+            if lmhead is not None:
+                gemm_s += out[1]
+                step_s += out[2]
+            n_req += 1
+    else:
+        ctx = mp.get_context("fork")             # before any GPU use in this process
+        with ctx.Pool(workers) as pool:
+            while time.perf_counter() - t0 < seconds:
+                batch = [(n_req + k) % len(widths) for k in range(workers)]
+                for out in pool.map(fn, batch):
+                    done_rows += out[0]
+                    if lmhead is not None:
+                        gemm_s += out[1]
+                        step_s += out[2]
+                n_req += len(batch)
     el = time.perf_counter() - t0
-    return {"value": done_rows / el, "unit": "beam-rows x steps/s", "cores": workers, "kind": "oracle",
-            "sample": f"{n_req} request decodes of this workload ({done_rows} beam-rows x steps) in "
-                      f"{el:.1f} s, {workers} worker processes (one request each, numpy float64) on "
-                      f"{platform.machine()} with {cores} cores available"}
+    res = {"value": done_rows / el, "unit": "beam-rows x steps/s", "cores": workers, "kind": "oracle",
+           "cpu": cpu_model(),
+           "sample": f"{n_req} request decodes of this workload ({done_rows} beam-rows x steps) in "
+                     f"{el:.1f} s, {workers} worker process{'es' if workers > 1 else ''} (one request each, "
+                     f"numpy float64) on {host_cores()} cores available"}
+    if lmhead is not None:
+        res["gemm_seconds"] = gemm_s
+        res["step_seconds"] = step_s
+        res["sample"] += f"; of the requests' CPU time {gemm_s:.1f} s in the fp64 lm_head product, {step_s:.1f} s in the steps"
+    return res
+
+
+def cpu_baselines(wl, cat, seconds, lmhead=None):
+    """The oracle on every core (up to 16 processes) and on one core."""
+    many = cpu_baseline(wl, cat, seconds, None, lmhead)
+    one = cpu_baseline(wl, cat, max(2.0, seconds / 3), 1, lmhead)
+    many["one_core"] = {k: one[k] for k in ("value", "cores", "sample")}
+    return many
 
 
 # ----------------------------------------------------------------------------- GPU legs
@@ -188,7 +274,9 @@ def merge_steps(trie, widths, L, deferred=True):
     return int(wide[L - 1]) if deferred else sum(wide)
 
 
-def main_leg(args, wl, cat, dev):
+def one_wave_leg(args, wl, cat, dev):
+    """A one-wave workload (every request admitted at once): its decode captured per input
+    copy and replayed, verified against a step-by-step decode, and its kernels timed."""
     import numpy as np
     import torch
     from trie_constrained_beam_amd import Beams, Trie, synth
@@ -327,6 +415,127 @@ def phase_trace(args, wl, cat, dev):
         lines.append(f"{name:5s} level {level} workgroups {recs[0].shape[0]:4d} (ran {int((recs[0][:, 0] > 0).sum())}, "
                      f"per XCD {xcd.tolist()}): start skew {np.median(skew):.2f}, span {np.median(span):.2f}; {ph}")
     print("\n".join(lines), flush=True)
+
+
+def leg_summary(m, steps):
+    """Throughput and the tile kernel's roofline of a measured leg."""
+    value = m["rows_x_steps"] * steps / m["elapsed"]
+    unit_bytes = m["V"] * m["dsize"] + STATE_BYTES + TRIE_BYTES          # per row-step, tile kernel
+    launches = m.get("launches", m["L"])
+    bytes_per_launch = m["rows_x_steps"] * unit_bytes / launches
+    achieved = bytes_per_launch / (m["tile_us"] * 1e-6) / 1e9
+    return value, unit_bytes, bytes_per_launch, achieved
+
+
+def mixed_leg(args, wl, cat, dev):
+    """The mixed decode wave: requests admitted FIFO under the slot budget between steps,
+    finished requests released by the step that completes them, so the whole run of the
+    workload (every request decoded) is one captured graph per input copy."""
+    import numpy as np
+    import torch
+    from trie_constrained_beam_amd import Beams, Trie, synth
+    trie = Trie(cat, device=dev)
+    widths = list(wl.widths)
+    L, S, V = wl.L, wl.slot_budget, trie.V
+    beams = Beams(trie, S, len(widths), max(widths), device=dev)
+    beams.set_finish_outputs(True)
+    # the FIFO schedule does not depend on the logits: record it once with zero logits
+    zero = torch.zeros((S, V), dtype=torch.float32, device=dev)
+    sched = []                       # per step: (widths admitted before it, live (index, base, level))
+    head, live = 0, []
+    while head < len(widths) or live:
+        st = beams.status()
+        free, free_ids, take = st["free_slots"], st["free_requests"], []
+        while head + len(take) < len(widths) and widths[head + len(take)] <= free and free_ids > 0:
+            free -= widths[head + len(take)]
+            free_ids -= 1
+            take.append(head + len(take))
+        admitted = []
+        while take:
+            try:
+                rids, bases = beams.init([widths[i] for i in take])
+                admitted = [(i, int(b)) for i, b in zip(take, bases)]
+                break
+            except Exception:                     # fragmented slots: admit fewer this time
+                take.pop()
+        head += len(admitted)
+        live += [[i, b, 0] for i, b in admitted]
+        sched.append(([widths[i] for i, _ in admitted], [tuple(e) for e in live]))
+        beams.step(zero)
+        for e in live:
+            e[2] += 1
+        live = [e for e in live if e[2] < L]
+    torch.cuda.synchronize()
+    host = []
+    for _, lv in sched:
+        h = np.zeros((S, V), dtype=np.float32)
+        for i, b, level in lv:
+            h[b:b + widths[i]] = synth.logits_rowkeyed(wl.seed, level, i, widths[i], wl.sigma)
+        host.append(h)
+    per_run = sum(h.nbytes for h in host)
+    pool = make_pool(lambda: [torch.from_numpy(h).to(dev) for h in host], per_run, args.pool_gib)
+    log(f"[bench] mixed wave: {len(widths)} requests in {len(sched)} steps; pool {len(pool)} x "
+        f"{per_run / 2**20:.0f} MiB of logits")
+
+    def run_once(c):
+        for s_i, (admit, _) in enumerate(sched):
+            if admit:
+                beams.init(admit)
+            beams.step(pool[c][s_i])
+
+    # rows x steps of one run: the live rows of every step, exported along an eager run
+    rows = []
+    id_of = {}
+    head2 = 0
+    for s_i, (admit, lv) in enumerate(sched):
+        if admit:
+            rids, _ = beams.init(admit)
+            for k, rid in enumerate(rids):
+                id_of[head2 + k] = int(rid)
+            head2 += len(admit)
+        ex = beams.export()["rows"].cpu().numpy()
+        rows.append(int(sum(ex[id_of[i]] for i, _, _ in lv)))
+        beams.step(pool[0][s_i])
+    torch.cuda.synchronize()
+    rows_x_steps = sum(rows)
+    graphs = capture(run_once, len(pool)) if args.graph else None
+
+    def run(d):
+        if graphs is not None:
+            graphs[d % len(pool)].replay()
+        else:
+            run_once(d % len(pool))
+    steps = max(5, args.steps // 4)
+    elapsed = timed(run, steps, max(2, args.warmup // 4))
+    n_ev = min(steps, 20)
+    beams.enable_timing(n_ev * len(sched), 10)
+    for d in range(n_ev):
+        run_once(d % len(pool))
+    _, tile_ms, merge_ms, n_timed = beams.timing()
+    beams.enable_timing(0)
+    return {"elapsed": elapsed, "steps": steps, "rows_x_steps": rows_x_steps, "rows_per_step": rows,
+            "tile_us": tile_ms * 1e3 / n_timed, "merge_ms_per_run": merge_ms / max(1, n_timed // len(sched)),
+            "pool": len(pool), "dsize": 4, "V": V, "L": L, "launches": len(sched), "R": len(widths),
+            "B": max(widths)}
+
+
+def copy_peak(dev, gib=1.0):
+    """A device-to-device copy of ``gib`` GiB: read + write bytes per second (GB/s)."""
+    import torch
+    n = int(gib * 2 ** 30)
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    reps = 20
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    return 2.0 * n * reps / el / 1e9
 
 
 def lmhead_leg(args, dev, read_mode="dense"):
@@ -479,6 +688,26 @@ def score_leg(args, cat, dev):
             "kernel_source_sha": kernel_source_sha(SCORE_SOURCES)}
 
 
+ONE_WAVE_LEGS = ["b50x1_l3_20k_f32", "b128x64_l4_1m_zipf_f32"]
+MIXED_LEG = "mixed256_l5_8m_f32"
+
+
+def leg_record(wl, m, steps, cat, cpu):
+    """The JSON record of a measured one-wave or mixed leg."""
+    value, unit_bytes, bpl, achieved = leg_summary(m, steps)
+    rec = {"workload": wl.name, "value": value, "unit": "beam-rows x steps/s", "steps": steps,
+           "ms_per_step": m["elapsed"] * 1e3 / steps, "requests": m["R"], "beam_width": m["B"], "L": m["L"],
+           "catalog": int(cat.shape[0]), "rows_per_step": m["rows_per_step"], "rows_x_steps_per_decode":
+           m["rows_x_steps"], "input_pool_copies": m["pool"],
+           "roofline": {"bound": "hbm", "kernel": "k_tile", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                        "bytes_per_row_step": unit_bytes, "bytes_per_launch": bpl, "avg_launch_us": m["tile_us"]},
+           "cpu_baseline": cpu}
+    if "merge_us" in m:
+        rec["merge_avg_us"] = m["merge_us"]
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -490,6 +719,7 @@ def main():
     ap.add_argument("--graph", type=int, default=1, help="replay each decode as a captured HIP graph")
     ap.add_argument("--lmhead", type=int, default=1, help="also run the SID-range lm_head leg")
     ap.add_argument("--score", type=int, default=1, help="also run the single-pass scoring leg")
+    ap.add_argument("--legs", type=int, default=1, help="also run the other workloads' legs")
     ap.add_argument("--phase-trace", type=int, default=0,
                     help="only print the phase trace of one decode replayed this many times (diagnostics)")
     args = ap.parse_args()
@@ -513,10 +743,27 @@ def main():
         torch.cuda.set_device(0)
         phase_trace(args, wl, cat, torch.device("cuda:0"))
         return
+    legs = [synth.WORKLOADS[n] for n in ONE_WAVE_LEGS + [MIXED_LEG] if args.legs and n != wl.name]
+    cats = {w.name: w.catalog() for w in legs}
+    lm_wl = synth.WORKLOADS["lmhead_b512x8_l4_1m_h2048"]
+    lm_cat = lm_wl.catalog() if args.lmhead else None
+    # the CPU oracle first: its worker processes are forked before this process touches the GPU
     cpu = score_cpu = None
+    leg_cpu, lm_cpu = {}, None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(wl, cat, args.cpu_seconds)
-        log(f"[bench] oracle {cpu['value']:.0f} rows x steps/s ({cpu['cores']} processes)")
+        cpu = cpu_baselines(wl, cat, args.cpu_seconds)
+        log(f"[bench] oracle {cpu['value']:.0f} rows x steps/s ({cpu['cores']} processes), "
+            f"{cpu['one_core']['value']:.0f} on one core; {cpu['cpu']}")
+        for w in legs:
+            leg_cpu[w.name] = cpu_baselines(w, cats[w.name], max(3.0, args.cpu_seconds / 3))
+            log(f"[bench] oracle {w.name}: {leg_cpu[w.name]['value']:.0f} rows x steps/s")
+        if args.lmhead:
+            import numpy as np
+            S = sum(lm_wl.widths)
+            hid = [synth.hidden_states(lm_wl.seed, t, S, lm_wl.hidden) for t in range(lm_wl.L)]
+            wts = [synth.lmhead_weight(lm_wl.seed, lv, 256, lm_wl.hidden) for lv in range(lm_wl.L)]
+            lm_cpu = cpu_baselines(lm_wl, lm_cat, max(3.0, args.cpu_seconds / 3), lmhead=(hid, wts))
+            log(f"[bench] oracle lm_head workload: {lm_cpu['value']:.0f} rows x steps/s")
         if args.score:
             swl = synth.SCORE_WORKLOADS["score_u32_k512_l4_4m_zipf_d64"]
             score_cpu = score_cpu_baseline(swl, cat if swl.catalog_of == wl.name else swl.catalog(),
@@ -526,18 +773,32 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    m = main_leg(args, wl, cat, dev)
-    value = m["rows_x_steps"] * args.steps / m["elapsed"]
-    unit_bytes = m["V"] * m["dsize"] + STATE_BYTES + TRIE_BYTES          # per row-step, tile kernel
-    bytes_per_launch = m["rows_x_steps"] * unit_bytes / m["L"]
-    achieved = bytes_per_launch / (m["tile_us"] * 1e-6) / 1e9
+    copy_gbps = copy_peak(dev)
+    log(f"[bench] 1 GiB device-to-device copy: {copy_gbps:.0f} GB/s (read + write)")
+    m = one_wave_leg(args, wl, cat, dev)
+    value, unit_bytes, bytes_per_launch, achieved = leg_summary(m, args.steps)
     traffic = recorded_traffic()
     log(f"[bench] {args.steps} decodes in {m['elapsed'] * 1e3:.1f} ms; tile kernel avg {m['tile_us']:.2f} us "
         f"({achieved:.0f} GB/s), merge kernel avg {m['merge_us']:.2f} us")
+    leg_out = {}
+    for w in legs:
+        if w.slot_budget:
+            lm_ = mixed_leg(args, w, cats[w.name], dev)
+            st = lm_["steps"]
+        else:
+            a2 = argparse.Namespace(**vars(args))
+            a2.steps = args.steps * (50 if w.name == "b50x1_l3_20k_f32" else 1)
+            lm_ = one_wave_leg(a2, w, cats[w.name], dev)
+            st = a2.steps
+        leg_out[w.name] = leg_record(w, lm_, st, cats[w.name], leg_cpu.get(w.name))
+        r = leg_out[w.name]
+        log(f"[bench] leg {w.name}: {r['value']:.4g} rows x steps/s, {r['ms_per_step'] * 1e3:.1f} us per decode; "
+            f"tile avg {r['roofline']['avg_launch_us']:.2f} us ({r['roofline']['achieved']:.0f} GB/s)")
     lm = None
     if args.lmhead:
         lm = lmhead_leg(args, dev, "dense")
         lm["auto"] = lmhead_leg(args, dev, "auto")
+        lm["cpu_baseline"] = lm_cpu
     sc = None
     if args.score:
         swl = synth.SCORE_WORKLOADS["score_u32_k512_l4_4m_zipf_d64"]
@@ -566,9 +827,10 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": None if traffic is None else traffic / (m["tile_us"] * 1e-6) / 1e9,
                      "traffic_bytes_per_launch": traffic, "bytes_per_row_step": unit_bytes, "bytes_per_launch": bytes_per_launch,
-                     "avg_launch_us": m["tile_us"]},
+                     "avg_launch_us": m["tile_us"], "measured_copy_GBps": copy_gbps},
         "hbm_GBps_wall": m["rows_x_steps"] * (unit_bytes + MERGE_WRITE_BYTES) * args.steps / m["elapsed"] / 1e9,
         "merge_avg_us": m["merge_us"],
+        "legs": leg_out,
         "lmhead": lm,
         "score": sc,
         "cpu_baseline": cpu,
