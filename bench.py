@@ -336,8 +336,9 @@ def one_wave_leg(args, wl, cat, dev):
             "dsize": 2 if wl.bf16 else 4, "V": V, "L": L, "R": R, "B": B}
 
 
-TRACE_ORDER = [1, 8, 11, 12, 13, 9, 10, 2, 3, 4, 5, 6, 7]
+TRACE_ORDER = [1, 8, 11, 12, 13, 9, 10, 2, 14, 15, 3, 4, 5, 6, 7]
 TRACE_NAMES = {1: "start", 8: "counts", 11: "window", 12: "offsets", 13: "cand", 9: "staged", 10: "merged",
+               14: "logits", 15: "keys",
                2: "prev-merge", 3: "softmax", 4: "prefilter", 5: "binned", 6: "in-tile-staged", 7: "done"}
 
 
@@ -396,12 +397,14 @@ def phase_trace(args, wl, cat, dev):
     for li, (kind, level, _) in enumerate(reps[0]):
         recs = [r[li][2] for r in reps]
         name = {1: "tile", 2: "merge"}.get(kind, str(kind))
-        skew, span, phases = [], [], {}
+        skew, span, phases, xst = [], [], {}, []
         for rec in recs:
             ran = rec[:, 0] > 0
             rec = rec[ran]
             st = rec[:, 1]
             skew.append((st.max() - st.min()) / 100.0)
+            xst.append([(st[rec[:, 0] == x + 1].min() - st.min()) / 100.0 if (rec[:, 0] == x + 1).any() else 0.0
+                        for x in range(8)])
             last = rec[:, 2:].max(axis=1)
             span.append((np.maximum(last, st).max() - st.min()) / 100.0)
             marks = [m for m in TRACE_ORDER if (rec[:, m] > 0).any()]
@@ -413,7 +416,8 @@ def phase_trace(args, wl, cat, dev):
         xcd = np.bincount(recs[0][recs[0][:, 0] > 0, 0] - 1, minlength=8)
         ph = ", ".join(f"{k} {np.median(v):.2f}" for k, v in phases.items())
         lines.append(f"{name:5s} level {level} workgroups {recs[0].shape[0]:4d} (ran {int((recs[0][:, 0] > 0).sum())}, "
-                     f"per XCD {xcd.tolist()}): start skew {np.median(skew):.2f}, span {np.median(span):.2f}; {ph}")
+                     f"per XCD {xcd.tolist()}): start skew {np.median(skew):.2f} (first start per XCD "
+                     f"{np.round(np.median(np.asarray(xst), axis=0), 2).tolist()}), span {np.median(span):.2f}; {ph}")
     print("\n".join(lines), flush=True)
 
 

@@ -330,7 +330,8 @@ tcb_status tcb_beams_timing(tcb_beams *b, double *head_ms, double *tile_ms, doub
  * 64-bit words to d_buf (caller-owned device memory of capacity_words words): word 0 =
  * 1 + the XCD the workgroup ran on, word i > 0 = the 100 MHz real-time clock when the
  * workgroup passed phase mark i (0 if it never did). Tile marks: 1 start, 2 the previous
- * step's merge done (steps that merge it first), 3 rows loaded and log-softmaxed, 4
+ * step's merge done (steps that merge it first), 14 logits and child bits in registers,
+ * 15 keys computed (the first wave), 3 every wave's rows loaded and log-softmaxed, 4
  * prefilter bound, 5 candidates binned, 6 staged for an in-tile merge, 7 done; merge
  * marks (also a tile's merge of the previous step): 1 start, 8 counts read, 11 window
  * bins found, 12 staging offsets, 13 thread 0's candidate staged, 9 candidates staged,

@@ -911,9 +911,10 @@ __device__ __forceinline__ RowInfo load_row_info(const TrieDev &T, uint32_t n, i
 // writes the request's record. Returns false (nothing written) when the window would stage
 // more than kWinCap entries (massive ties); the caller then merges the whole request.
 // pa: the request as its previous step saw it; rpp: the record buffer that step read.
-// issue(): called once, right after the candidates' loads are issued (or before returning
-// false): the caller's own loads go there, behind the merge's, since a wait for a load also
-// waits for every load issued before it.
+// issue(): called once where this tile has rows (right after the counts have arrived): the
+// caller's own loads go there, behind the counts and ahead of the candidates, since a wait
+// for a load also waits for every load issued before it (the candidates are waited on
+// about when the caller's loads would have arrived anyway).
 template <class Issue>
 __device__ __forceinline__ bool window_merge(const TrieDev &T, const WaveDev &W, int q, const ReqArg pa, int rpp,
                                              int tile, MergeSmem &M, FuseRows &Z, Issue issue) {
@@ -958,6 +959,7 @@ __device__ __forceinline__ bool window_merge(const TrieDev &T, const WaveDev &W,
         if (tid == 0) Z.k = k;
         return true;
     }
+    issue();
     const uint32_t hi = min(lo + (uint32_t)kTileRows, k) - 1u;
     const uint32_t gprev = tid ? M.G[tid - 1] : 0u;
     const uint32_t gnext = tid + 1 < kBins ? M.G[tid + 1] : 0xFFFFFFFFu;
@@ -1029,7 +1031,6 @@ __device__ __forceinline__ bool window_merge(const TrieDev &T, const WaveDev &W,
     const int jt = inwin ? jw : jf;
     const uint32_t at = inwin ? Z.wst[jw] + (pp - Z.woff[jw]) : pp - Z.foff[jf];
     const Cand c = W.cand[cpar][reg0 + (size_t)jt * CAPT + min(at, (uint32_t)CAPT - 1u)];
-    issue();
     if (nst > (uint32_t)kWinCap) return false;
     // the candidate's child set, loaded now and used only if the entry is one of this
     // tile's rows; loaded unconditionally (another node of the depth stands in for a
@@ -1170,6 +1171,11 @@ __device__ __forceinline__ double row16_max_d(double v) {
     return v;
 }
 
+// log-sum-exp of a row from its maximum and its sum of exp(x - max)
+__device__ __forceinline__ float row_lse(float mx, float sum) {
+    return mx + __builtin_amdgcn_logf(sum) * kLn2;
+}
+
 // Masked log-softmax (sampled steps: of x / T) of one row held by a 16-lane group (lane j
 // holds the elements e of codes code_of(e, j)) and the keys of its candidates: codes
 // outside the support count as -inf. valid: this lane's candidates; ok: the row's node is
@@ -1204,8 +1210,7 @@ __device__ __forceinline__ void score_row(const StepReqs &R, int q, int level, i
         float sum = 0.0f;
 #pragma unroll
         for (int e = 0; e < kElems; ++e) sum += __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -mxl));
-        sum = row16_sum(sum);
-        lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+        lse = row_lse(mx, row16_sum(sum));
         lbest = sr + (lm - lse);
         // from here on x[e] is the candidate's score (-inf off the child set)
 #pragma unroll
@@ -1485,6 +1490,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
     }
 
     // 3. masked log-softmax and the candidates' keys
+    trace_mark(W, 14);                                // logits in registers, child bits known
     float lbest = -INFINITY;
     float ph[SAMPLE ? kElems : 1];                    // sampled steps: the candidates' log-probabilities
     if (wave_live) {
@@ -1496,6 +1502,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
 
     // 4. prefilter (at depths with many children per row): histogram of the lanes' best
     //    candidates, bin b_L where it reaches n. Elsewhere every candidate is binned exactly.
+    trace_mark(W, 15);                                // keys computed (wave 0)
     __syncthreads();                                  // the zeroed histograms are visible
     trace_mark(W, 3);                                 // rows loaded, trie read, log-softmax done
     uint32_t bL = kBins - 1;
@@ -1584,6 +1591,12 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
         if constexpr (NORM == TCB_NORM_OPEN) return ((tv >> e) & 1u) ? n : -1;   // -1: off the catalog
         return n;
     };
+    // fn(e) for every kept element (one branch per element slot, skipped by a wave with none)
+    auto for_kept = [&](auto fn) {
+#pragma unroll
+        for (int e = 0; e < kElems; ++e)
+            if (bn[e] <= bt) fn(e);
+    };
 
     if (kept <= (uint32_t)CAPT) {
         // 7. write bins <= b_t grouped by bin (the bins' offsets are all read first)
@@ -1598,21 +1611,18 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
             // stage (A.h2 holds the request's cumulative kept counts, b* = b_t), so they are
             // staged in LDS, ranked and written here
             static_assert(kTileCap <= kMergeCap, "a tile's kept candidates fit the merge's staging");
-#pragma unroll
-            for (int e = 0; e < kElems; ++e) {
-                if (bn[e] <= bt) {
-                    const uint32_t dst = at[e] + wb[e];
-                    if (dst < kept) {
-                        M->s[dst] = x[e];
-                        M->f[dst] = flat_of(e);
-                        M->n[dst] = node_of(e);
-                        if constexpr (SAMPLE) M->phi[dst] = ph[e];
-                        else M->phi[dst] = x[e];
-                    } else {
-                        atomicOr(W.err, kErrInternal);
-                    }
+            for_kept([&](int e) {
+                const uint32_t dst = at[e] + wb[e];
+                if (dst < kept) {
+                    M->s[dst] = x[e];
+                    M->f[dst] = flat_of(e);
+                    M->n[dst] = node_of(e);
+                    if constexpr (SAMPLE) M->phi[dst] = ph[e];
+                    else M->phi[dst] = x[e];
+                } else {
+                    atomicOr(W.err, kErrInternal);
                 }
-            }
+            });
             __syncthreads();
             trace_mark(W, 6);                         // staged for the in-tile merge
             const uint32_t k = min(width, kept);
@@ -1631,23 +1641,20 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
             return true;
         }
         Cand *out = W.cand[level & 1] + reg;
-#pragma unroll
-        for (int e = 0; e < kElems; ++e) {
-            if (bn[e] <= bt) {
-                const uint32_t dst = at[e] + wb[e];
-                if (dst < kept) {
-                    Cand c;
-                    c.s = x[e];
-                    c.f = flat_of(e);
-                    c.n = node_of(e);
-                    if constexpr (SAMPLE) c.phi = ph[e];
-                    else c.phi = x[e];
-                    out[dst] = c;
-                } else {
-                    atomicOr(W.err, kErrInternal);
-                }
+        for_kept([&](int e) {
+            const uint32_t dst = at[e] + wb[e];
+            if (dst < kept) {
+                Cand c;
+                c.s = x[e];
+                c.f = flat_of(e);
+                c.n = node_of(e);
+                if constexpr (SAMPLE) c.phi = ph[e];
+                else c.phi = x[e];
+                out[dst] = c;
+            } else {
+                atomicOr(W.err, kErrInternal);
             }
-        }
+        });
         W.tcum[level & 1][((size_t)q * MT + tile) * kBins + tid] = (uint16_t)min(C, kept);
         trace_mark(W, 7);                             // candidates issued
     } else {
@@ -1658,10 +1665,16 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
         A.h2[tid] = 0u;                               // every thread has read kept
         __syncthreads();
         const uint32_t kt = min(width, A.tot);
-        auto each = [&](auto fn) {
+        // the selection gets copies (a reference to x or the lane's values would keep them
+        // in memory on every path when it is not inlined)
+        float xe[kElems];
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) xe[e] = x[e];
+        const uint32_t vc = valid, fc = flat0;
+        auto each = [xe, vc, fc](auto fn) {
 #pragma unroll
             for (int e = 0; e < kElems; ++e)
-                if ((valid >> e) & 1u) fn(f2ord(x[e]), flat_of(e));
+                if ((vc >> e) & 1u) fn(f2ord(xe[e]), fc + (uint32_t)((e / CW) * SPAN + e % CW));
         };
         uint32_t o_star, f_star;
         block_select<kThreads>(each, kt, sel, o_star, f_star, W.err);
