@@ -332,7 +332,8 @@ def one_wave_leg(args, wl, cat, dev):
     beams.enable_timing(0)
     n_merge = n_timed // L * merge_steps(trie, widths, L)    # merge launches among the timed steps
     return {"elapsed": elapsed, "rows_x_steps": rows_x_steps, "rows_per_step": rows_per_step,
-            "tile_us": tile_ms * 1e3 / n_timed, "merge_us": merge_ms * 1e3 / max(1, n_merge), "pool": len(pool),
+            "tile_us": tile_ms * 1e3 / n_timed, "merge_us": merge_ms * 1e3 / n_merge if n_merge else None,
+            "pool": len(pool),
             "dsize": 2 if wl.bf16 else 4, "V": V, "L": L, "R": R, "B": B}
 
 
@@ -344,9 +345,11 @@ TRACE_NAMES = {1: "start", 8: "counts", 11: "window", 12: "offsets", 13: "cand",
 
 def phase_trace(args, wl, cat, dev):
     """Phase marks of every workgroup of one decode of the workload, captured as a HIP graph
-    (the timed route) and replayed ``args.phase_trace`` times. Prints, per launch, the
-    start skew across workgroups, the span from the first start to the last mark, and the
-    median per-workgroup time between consecutive marks (100 MHz clock)."""
+    (the timed route) and replayed ``args.phase_trace`` times, each time right behind
+    ``args.trace_behind`` untraced decodes of other input copies replayed back to back (as
+    the timed loop runs them; 0: after an idle GPU). Prints, per launch, the start skew
+    across workgroups, the span from the first start to the last mark, and the median
+    per-workgroup time between consecutive marks (100 MHz clock)."""
     import numpy as np
     import torch
     from trie_constrained_beam_amd import Beams, Trie, synth
@@ -363,25 +366,31 @@ def phase_trace(args, wl, cat, dev):
         host.append(torch.from_numpy(h.view(np.int16) if wl.bf16 else h).to(dev))
     xs = [x.view(torch.bfloat16) if wl.bf16 else x for x in host]
     beams.set_finish_outputs(True)
+    nb = args.trace_behind
+    pool = [xs] + [[x.clone() for x in xs] for _ in range(nb)]
 
-    def decode(_):
+    def decode(c):
         beams.init(widths)
         for t in range(L):
-            beams.step(xs[t])
+            beams.step(pool[c][t])
     for d in range(3):
-        decode(d)
+        decode(d % len(pool))
     torch.cuda.synchronize()
+    others = capture(lambda c: decode(c + 1), nb) if nb else []
     beams.set_trace(64 * 2 ** 20 // 8)
     (g,) = capture(decode, 1)
     reps = []
     for _ in range(args.phase_trace):
+        for o in others:
+            o.replay()
         g.replay()
         torch.cuda.synchronize()
         reps.append(beams.trace())
         torch.cuda.synchronize()
     beams.set_trace(0)
-    lines = [f"# workload {wl.name}: {args.phase_trace} replays of one captured decode; times in us "
-             f"(median over replays; per-workgroup phases: median over workgroups)"]
+    lines = [f"# workload {wl.name}: {args.phase_trace} replays of one captured decode, each behind {nb} "
+             f"other decodes replayed back to back; times in us (median over replays; per-workgroup "
+             f"phases: median over workgroups)"]
     # timeline: each launch's first start and last mark, from the decode's first start
     tl = []
     for rep in reps:
@@ -414,9 +423,10 @@ def phase_trace(args, wl, cat, dev):
                     phases.setdefault(f"{TRACE_NAMES[a]}->{TRACE_NAMES[b]}", []).append(
                         float(np.median(rec[both, b] - rec[both, a])) / 100.0)
         xcd = np.bincount(recs[0][recs[0][:, 0] > 0, 0] - 1, minlength=8)
+        bx = [int(recs[0][b, 0]) - 1 for b in range(min(8, recs[0].shape[0]))]   # XCD of workgroups 0..7
         ph = ", ".join(f"{k} {np.median(v):.2f}" for k, v in phases.items())
         lines.append(f"{name:5s} level {level} workgroups {recs[0].shape[0]:4d} (ran {int((recs[0][:, 0] > 0).sum())}, "
-                     f"per XCD {xcd.tolist()}): start skew {np.median(skew):.2f} (first start per XCD "
+                     f"per XCD {xcd.tolist()}, workgroups 0..7 on XCDs {bx}): start skew {np.median(skew):.2f} (first start per XCD "
                      f"{np.round(np.median(np.asarray(xst), axis=0), 2).tolist()}), span {np.median(span):.2f}; {ph}")
     print("\n".join(lines), flush=True)
 
@@ -596,7 +606,7 @@ def lmhead_leg(args, dev, read_mode="dense"):
     res = {"workload": wl.name, "read_mode": read_mode, "rows_per_step": rows_per_step,
            "value": rows_x_steps * steps / elapsed, "unit": "beam-rows x steps/s",
            "ms_per_step": elapsed * 1e3 / steps, "steps": steps, "head_avg_us": head_s * 1e6,
-           "tile_avg_us": tile_ms * 1e3 / n_timed, "merge_avg_us": merge_ms * 1e3 / max(1, n_merge)}
+           "tile_avg_us": tile_ms * 1e3 / n_timed, "merge_avg_us": merge_ms * 1e3 / n_merge if n_merge else None}
     if read_mode == "dense":
         flop_per_decode = 2.0 * rows_x_steps * 256 * H
         achieved = flop_per_decode / L / head_s / 1e12
@@ -604,7 +614,8 @@ def lmhead_leg(args, dev, read_mode="dense"):
                            "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
                            "flop_per_launch": flop_per_decode / L, "avg_launch_us": head_s * 1e6}
         log(f"[bench] lm_head leg: rows per step {rows_per_step}; lm_head avg {head_s * 1e6:.2f} us "
-            f"({achieved:.0f} TFLOP/s), tile {res['tile_avg_us']:.2f} us, merge {res['merge_avg_us']:.2f} us")
+            f"({achieved:.0f} TFLOP/s), tile {res['tile_avg_us']:.2f} us"
+            + (f", merge {res['merge_avg_us']:.2f} us" if res["merge_avg_us"] is not None else ""))
     else:
         log(f"[bench] lm_head leg ({read_mode}): {elapsed * 1e3 / steps:.3f} ms per decode, head avg "
             f"{head_s * 1e6:.2f} us per step")
@@ -707,7 +718,7 @@ def leg_record(wl, m, steps, cat, cpu):
                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                         "bytes_per_row_step": unit_bytes, "bytes_per_launch": bpl, "avg_launch_us": m["tile_us"]},
            "cpu_baseline": cpu}
-    if "merge_us" in m:
+    if m.get("merge_us") is not None:
         rec["merge_avg_us"] = m["merge_us"]
     return rec
 
@@ -726,6 +737,8 @@ def main():
     ap.add_argument("--legs", type=int, default=1, help="also run the other workloads' legs")
     ap.add_argument("--phase-trace", type=int, default=0,
                     help="only print the phase trace of one decode replayed this many times (diagnostics)")
+    ap.add_argument("--trace-behind", type=int, default=16,
+                    help="phase trace: untraced decodes (other input copies) replayed before each traced one")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -783,7 +796,7 @@ def main():
     value, unit_bytes, bytes_per_launch, achieved = leg_summary(m, args.steps)
     traffic = recorded_traffic()
     log(f"[bench] {args.steps} decodes in {m['elapsed'] * 1e3:.1f} ms; tile kernel avg {m['tile_us']:.2f} us "
-        f"({achieved:.0f} GB/s), merge kernel avg {m['merge_us']:.2f} us")
+        f"({achieved:.0f} GB/s)" + (f", merge kernel avg {m['merge_us']:.2f} us" if m["merge_us"] is not None else ""))
     leg_out = {}
     for w in legs:
         if w.slot_budget:

@@ -1722,7 +1722,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
 // MERGE: every stepped request of the launch has at most kTileRows rows (one tile), so one
 // workgroup per request does its tile and then, after a barrier, its merge from the
 // records it has just written: no second kernel. Otherwise the tiles of a request are
-// dealt to one XCD (workgroup b -> XCD b mod 8) and k_merge follows.
+// dealt to one XCD (workgroups b with the same b mod 8 run on one XCD) and k_merge follows.
 // FUSE: requests whose previous merge is pending do it first, in every one of their tiles.
 template <int DT, int NORM, bool VEC, bool SAMPLE, bool MERGE, bool FUSE>
 __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp, StepReqs R,
@@ -1780,7 +1780,9 @@ __global__ __launch_bounds__(256) void k_first(TrieDev T, WaveDev W, int rp, Ste
                                                const void *__restrict__ logits, int64_t ld) {
     constexpr int CH = Lay<DT>::CH, CW = Lay<DT>::CW, SPAN = 256 / CH;
     __shared__ FirstSmem F;
-    const int ql = (int)blockIdx.x;
+    const int nx = first_xcds(R.n), xb = (int)((blockIdx.x + 7u) & 7u);
+    if (xb >= nx) return;                             // a workgroup of a later XCD: nothing to do
+    const int ql = (int)(blockIdx.x >> 3) * nx + xb;
     if (ql >= R.n) return;
     const int q = R.q0 + ql;
     const ReqArg ra = R.r[ql];
@@ -1945,7 +1947,9 @@ void launch_tile_t(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R
                           int64_t ld, int mode, hipStream_t s) {
     const int groups = (R.n + 7) / 8;
     if (mode == kTileFirst) {
-        hipLaunchKernelGGL((k_first<DT, NORM, VEC, SAMPLE>), dim3(R.n), dim3(256), 0, s, t, w, rp, R, logits, ld);
+        const int nx = first_xcds(R.n);
+        hipLaunchKernelGGL((k_first<DT, NORM, VEC, SAMPLE>), dim3(8 * ((R.n + nx - 1) / nx)), dim3(256), 0, s, t, w,
+                           rp, R, logits, ld);
     } else if (mode == kTileMerge) {
         hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, true, false>), dim3(R.n), dim3(kThreads), 0, s, t, w, rp,
                            R, logits, ld);

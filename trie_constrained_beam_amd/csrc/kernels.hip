@@ -150,7 +150,8 @@ int tile_mode(const StepReqs &R, bool fuse) {
 int tile_grid(const WaveDev &w, const StepReqs &R, bool fuse) {
     if (R.n <= 0) return 0;
     const int mode = tile_mode(R, fuse);
-    if (mode == kTileFirst || mode == kTileMerge) return R.n;
+    if (mode == kTileFirst) return 8 * ((R.n + first_xcds(R.n) - 1) / first_xcds(R.n));
+    if (mode == kTileMerge) return R.n;
     return 8 * ((R.n + 7) / 8) * w.MT;
 }
 

@@ -187,6 +187,16 @@ TCB_TILE_LAUNCHER(launch_tile_bf16_sampled);
 // pending merges come first, kTileMerge when every request fits one tile (merged inside
 // the kernel), kTilePlain otherwise (k_merge or the next step merges).
 enum { kTilePlain = 0, kTileMerge = 1, kTileFuse = 2, kTileFirst = 3 };
+// How many XCDs take the requests of a first-step launch of n requests (at most 16 per XCD
+// of 32 CUs): the requests go to the workgroups b with (b - 1) mod 8 < first_xcds(n). After
+// the GPU has been idle (a decode's first launch often follows such a gap) the XCDs start a
+// launch's workgroups up to about 4 us apart, XCDs 0 and 1 first, and workgroup b then runs
+// on XCD (b - 1) mod 8; behind other work the XCDs start together and the offset differs
+// (all measured with the phase trace). Only the time depends on this.
+__host__ __device__ inline int first_xcds(int n) {
+    const int x = (n + 15) / 16;
+    return x < 2 ? 2 : x > 8 ? 8 : x;
+}
 int tile_mode(const StepReqs &R, bool fuse);
 // workgroups of the tile kernel launch_tile would launch for R (phase-trace layout)
 int tile_grid(const WaveDev &w, const StepReqs &R, bool fuse);
