@@ -338,6 +338,7 @@ def one_wave_leg(args, wl, cat, dev):
 
 
 TRACE_ORDER = [1, 8, 11, 12, 13, 9, 10, 2, 14, 15, 3, 4, 5, 6, 7]
+MERGE_TRACE_ORDER = [1, 8, 9, 11, 10]                # k_merge (11: ranks written, finishing merge)
 TRACE_NAMES = {1: "start", 8: "counts", 11: "window", 12: "offsets", 13: "cand", 9: "staged", 10: "merged",
                14: "logits", 15: "keys",
                2: "prev-merge", 3: "softmax", 4: "prefilter", 5: "binned", 6: "in-tile-staged", 7: "done"}
@@ -416,11 +417,13 @@ def phase_trace(args, wl, cat, dev):
                         for x in range(8)])
             last = rec[:, 2:].max(axis=1)
             span.append((np.maximum(last, st).max() - st.min()) / 100.0)
-            marks = [m for m in TRACE_ORDER if (rec[:, m] > 0).any()]
+            order = MERGE_TRACE_ORDER if kind == 2 else TRACE_ORDER
+            names = {**TRACE_NAMES, **({11: "ranked"} if kind == 2 else {})}
+            marks = [m for m in order if (rec[:, m] > 0).any()]
             for a, b in zip(marks, marks[1:]):
                 both = (rec[:, a] > 0) & (rec[:, b] > 0)
                 if both.any():
-                    phases.setdefault(f"{TRACE_NAMES[a]}->{TRACE_NAMES[b]}", []).append(
+                    phases.setdefault(f"{names[a]}->{names[b]}", []).append(
                         float(np.median(rec[both, b] - rec[both, a])) / 100.0)
         xcd = np.bincount(recs[0][recs[0][:, 0] > 0, 0] - 1, minlength=8)
         bx = [int(recs[0][b, 0]) - 1 for b in range(min(8, recs[0].shape[0]))]   # XCD of workgroups 0..7

@@ -335,7 +335,7 @@ tcb_status tcb_beams_timing(tcb_beams *b, double *head_ms, double *tile_ms, doub
  * prefilter bound, 5 candidates binned, 6 staged for an in-tile merge, 7 done; merge
  * marks (also a tile's merge of the previous step): 1 start, 8 counts read, 11 window
  * bins found, 12 staging offsets, 13 thread 0's candidate staged, 9 candidates staged,
- * 10 done. capacity_words = 0 turns
+ * 10 done; in k_merge's finishing merge 11 marks the ranks written (after 9). capacity_words = 0 turns
  * tracing off. Launches captured into a HIP graph keep the buffer they were captured
  * with. Errors: TCB_E_ARG. */
 #define TCB_TRACE_SLOTS 16

@@ -437,6 +437,7 @@ __device__ __forceinline__ void load_row_chunks(const void *logits, int64_t ld, 
 
 // ---------------------------------------------------------------------- shared memory
 struct alignas(16) MergeSmem {
+    uint64_t key[kMergeCap];                       // staged entries' keys (merge_key): larger is better
     float s[kMergeCap];
     uint32_t f[kMergeCap];
     int32_t n[kMergeCap];
@@ -474,9 +475,16 @@ __device__ __forceinline__ void write_next_record(const WaveDev &W, int q, const
     }
 }
 
+// An entry's selection key as one 64-bit word, larger = better: the order-preserving score
+// above, the complemented flat index below (a lower flat index wins a tie).
+__device__ __forceinline__ uint64_t merge_key(float s, uint32_t f) {
+    return ((uint64_t)f2ord(s) << 32) | (uint64_t)(~f);
+}
+
 // Entries p < staged of M are grouped by bin (bin b at [G[b - 1], min(G[b], staged)),
-// G[-1] = 0): an entry's rank is the entries of better bins plus the better members of its
-// own bin. emit(rank, p, s, f) is called for every entry; ranks below k are the new rows.
+// G[-1] = 0), each with its merge_key in M.key: an entry's rank is the entries of better bins
+// plus the better members of its own bin. emit(rank, p, s, f) is called for every entry;
+// ranks below k are the new rows.
 template <class Emit>
 __device__ __forceinline__ void rank_staged(const MergeSmem &M, const uint32_t *G, uint32_t staged, float sref,
                                             Emit emit) {
@@ -486,11 +494,15 @@ __device__ __forceinline__ void rank_staged(const MergeSmem &M, const uint32_t *
         const uint32_t p = (uint32_t)(threadIdx.x + u * kThreads);
         if (p < staged) {
             const float s = M.s[p];
-            const uint32_t o = f2ord(s), f = M.f[p];
+            const uint32_t f = M.f[p];
+            const uint64_t key = M.key[p];
             const uint32_t b = score_bin(sref, s);
             const uint32_t st = b ? G[b - 1] : 0u, en = min(G[b], staged);
-            uint32_t r = 0u;
-            for (uint32_t qq = st; qq < en; ++qq) r += key_better(f2ord(M.s[qq]), M.f[qq], o, f) ? 1u : 0u;
+            uint32_t r = 0u, i = st;
+            for (; i + 4u <= en; i += 4u)
+                r += (M.key[i] > key ? 1u : 0u) + (M.key[i + 1] > key ? 1u : 0u) + (M.key[i + 2] > key ? 1u : 0u) +
+                     (M.key[i + 3] > key ? 1u : 0u);
+            for (; i < en; ++i) r += M.key[i] > key ? 1u : 0u;
             emit(st + r, p, s, f);
         }
     }
@@ -740,6 +752,7 @@ __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W
                 if (b <= bs && pos[u] < staged) {     // holds by construction
                     M.s[pos[u]] = sc[u];
                     M.f[pos[u]] = fl[u];
+                    M.key[pos[u]] = merge_key(sc[u], fl[u]);
                     M.n[pos[u]] = nd[u];
                     M.phi[pos[u]] = ph[u];
                 } else {
@@ -758,6 +771,7 @@ __device__ __forceinline__ void merge_request(const TrieDev &T, const WaveDev &W
                 M.n[p] = (int32_t)rank;
             });
             __syncthreads();
+            trace_mark(W, 11);                        // ranked (k_merge)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t p = (uint32_t)(tid + u * kThreads);
@@ -1616,6 +1630,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
                 if (dst < kept) {
                     M->s[dst] = x[e];
                     M->f[dst] = flat_of(e);
+                    M->key[dst] = merge_key(x[e], flat_of(e));
                     M->n[dst] = node_of(e);
                     if constexpr (SAMPLE) M->phi[dst] = ph[e];
                     else M->phi[dst] = x[e];
