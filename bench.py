@@ -197,12 +197,43 @@ def cpu_baseline(wl, cat, seconds, workers=None, lmhead=None):
     return res
 
 
-def cpu_baselines(wl, cat, seconds, lmhead=None):
-    """The oracle on every core (up to 16 processes) and on one core."""
+def cpu_baselines(wl, cat, seconds, lmhead=None, row_bytes=None):
+    """The oracle on every core (up to 16 processes) and on one core; with row_bytes (the
+    GPU roofline's algorithmic bytes per row-step) also its effective GB/s on those bytes."""
     many = cpu_baseline(wl, cat, seconds, None, lmhead)
     one = cpu_baseline(wl, cat, max(2.0, seconds / 3), 1, lmhead)
     many["one_core"] = {k: one[k] for k in ("value", "cores", "sample")}
+    if row_bytes:
+        many["effective_GBps"] = many["value"] * row_bytes / 1e9
+        many["one_core"]["effective_GBps"] = one["value"] * row_bytes / 1e9
     return many
+
+
+def row_bytes(wl):
+    """Algorithmic bytes per row-step of a workload's step kernels (the roofline's figure)."""
+    return 256 * (2 if wl.bf16 else 4) + STATE_BYTES + TRIE_BYTES
+
+
+def child_sector_bytes(trie, nodes_by_step, dsize):
+    """The child-sector lower bound of a decode: for every live row of every step, 64 bytes
+    for each 64-byte sector of its logit row that holds a child of its node."""
+    import numpy as np
+    cb, cc, _ = trie.host_arrays()
+    per = 64 // dsize                                  # codes per sector
+    total = 0
+    for nodes in nodes_by_step:
+        nodes = np.asarray(nodes, dtype=np.int64)
+        st, en = cb[nodes].astype(np.int64), cb[nodes + 1].astype(np.int64)
+        cnt = en - st
+        if cnt.sum() == 0:
+            continue
+        row = np.repeat(np.arange(nodes.size), cnt)
+        first = np.repeat(st - np.concatenate(([0], np.cumsum(cnt)[:-1])), cnt)
+        sec = cc[first + np.arange(cnt.sum())].astype(np.int64) // per
+        new = np.ones(sec.size, dtype=bool)                 # codes ascend within a row
+        new[1:] = (sec[1:] != sec[:-1]) | (row[1:] != row[:-1])
+        total += 64 * int(new.sum())
+    return total
 
 
 # ----------------------------------------------------------------------------- GPU legs
@@ -300,14 +331,20 @@ def one_wave_leg(args, wl, cat, dev):
     pool = make_pool(upload, per_decode, args.pool_gib)
     fin = beams.set_finish_outputs(True)   # the last step writes each request's beams (row = id)
     log(f"[bench] pool {len(pool)} x {per_decode / 2**20:.1f} MiB of logits")
-    rows_per_step = []
+    rows_per_step, nodes_by_step = [], []
     idx = torch.as_tensor(ids, device=dev).long()
     for t in range(L):
-        rows_per_step.append(int(beams.export()["rows"][idx].sum().item()))
+        ex = beams.export()
+        rows = ex["rows"][idx].cpu().numpy()
+        node = ex["node"].cpu().numpy()
+        rows_per_step.append(int(rows.sum()))
+        nodes_by_step.append(np.concatenate([node[b:b + int(k)] for b, k in zip(bases, rows)]))
         beams.step(pool[0][t])
     torch.cuda.synchronize()
     rows_x_steps = sum(rows_per_step)
-    log(f"[bench] live rows per step {rows_per_step} -> {rows_x_steps} rows x steps per decode")
+    sector_bytes = child_sector_bytes(trie, nodes_by_step, 2 if wl.bf16 else 4)
+    log(f"[bench] live rows per step {rows_per_step} -> {rows_x_steps} rows x steps per decode; "
+        f"child-sector bound {sector_bytes / rows_x_steps:.1f} B per row-step")
 
     def decode(c):
         rid, _ = beams.init(widths)
@@ -329,11 +366,17 @@ def one_wave_leg(args, wl, cat, dev):
     for d in range(n_ev):
         decode(d % len(pool))
     _, tile_ms, merge_ms, n_timed = beams.timing()
+    # cold: one launch per step, each decode on another input copy (logits from HBM)
+    beams.enable_timing(n_ev * L, 1)
+    for d in range(n_ev):
+        decode((d + 1) % len(pool))
+    _, tile_ms_c, _, n_timed_c = beams.timing()
     beams.enable_timing(0)
     n_merge = n_timed // L * merge_steps(trie, widths, L)    # merge launches among the timed steps
     return {"elapsed": elapsed, "rows_x_steps": rows_x_steps, "rows_per_step": rows_per_step,
-            "tile_us": tile_ms * 1e3 / n_timed, "merge_us": merge_ms * 1e3 / n_merge if n_merge else None,
-            "pool": len(pool),
+            "tile_us": tile_ms * 1e3 / n_timed, "tile_us_cold": tile_ms_c * 1e3 / n_timed_c,
+            "merge_us": merge_ms * 1e3 / n_merge if n_merge else None,
+            "pool": len(pool), "sector_bytes": sector_bytes,
             "dsize": 2 if wl.bf16 else 4, "V": V, "L": L, "R": R, "B": B}
 
 
@@ -602,20 +645,30 @@ def lmhead_leg(args, dev, read_mode="dense"):
     for d in range(n_ev):
         decode(d % len(pool))
     head_ms, tile_ms, merge_ms, n_timed = beams.timing()
+    # cold: one launch per step, each decode on another copy of the hidden states (from HBM)
+    beams.enable_timing(n_ev * L, 1)
+    for d in range(n_ev):
+        decode((d + 1) % len(pool))
+    head_ms_c, _, _, n_timed_c = beams.timing()
     beams.enable_timing(0)
     n_merge = n_timed // L * merge_steps(trie, widths, L)
     rows_x_steps = sum(rows_per_step)
     head_s = head_ms / 1e3 / n_timed                       # average head launch(es) per step
+    head_s_c = head_ms_c / 1e3 / n_timed_c
     res = {"workload": wl.name, "read_mode": read_mode, "rows_per_step": rows_per_step,
            "value": rows_x_steps * steps / elapsed, "unit": "beam-rows x steps/s",
            "ms_per_step": elapsed * 1e3 / steps, "steps": steps, "head_avg_us": head_s * 1e6,
+           "head_avg_us_cold": head_s_c * 1e6,
            "tile_avg_us": tile_ms * 1e3 / n_timed, "merge_avg_us": merge_ms * 1e3 / n_merge if n_merge else None}
     if read_mode == "dense":
         flop_per_decode = 2.0 * rows_x_steps * 256 * H
         achieved = flop_per_decode / L / head_s / 1e12
         res["roofline"] = {"bound": "mfma", "kernel": "k_lmhead", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
-                           "flop_per_launch": flop_per_decode / L, "avg_launch_us": head_s * 1e6}
+                           "flop_per_launch": flop_per_decode / L, "avg_launch_us": head_s * 1e6,
+                           "timing": "warm: 10 back-to-back launches on the same hidden states",
+                           "avg_launch_us_cold": head_s_c * 1e6,
+                           "achieved_cold": flop_per_decode / L / head_s_c / 1e12}
         log(f"[bench] lm_head leg: rows per step {rows_per_step}; lm_head avg {head_s * 1e6:.2f} us "
             f"({achieved:.0f} TFLOP/s), tile {res['tile_avg_us']:.2f} us"
             + (f", merge {res['merge_avg_us']:.2f} us" if res["merge_avg_us"] is not None else ""))
@@ -710,6 +763,18 @@ ONE_WAVE_LEGS = ["b50x1_l3_20k_f32", "b128x64_l4_1m_zipf_f32"]
 MIXED_LEG = "mixed256_l5_8m_f32"
 
 
+def roofline_extra(m, bytes_per_launch):
+    """The step kernels timed cold (one launch per step, inputs from another copy each
+    decode) and the decode's child-sector lower bound, beside the warm roofline."""
+    out = {"timing": "warm: 10 back-to-back launches of each step's kernel on the same inputs"}
+    if m.get("tile_us_cold"):
+        out["avg_launch_us_cold"] = m["tile_us_cold"]
+        out["achieved_cold"] = bytes_per_launch / (m["tile_us_cold"] * 1e-6) / 1e9
+    if m.get("sector_bytes"):
+        out["child_sector_bytes_per_row_step"] = m["sector_bytes"] / m["rows_x_steps"]
+    return out
+
+
 def leg_record(wl, m, steps, cat, cpu):
     """The JSON record of a measured one-wave or mixed leg."""
     value, unit_bytes, bpl, achieved = leg_summary(m, steps)
@@ -719,7 +784,8 @@ def leg_record(wl, m, steps, cat, cpu):
            m["rows_x_steps"], "input_pool_copies": m["pool"],
            "roofline": {"bound": "hbm", "kernel": "k_tile", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                        "bytes_per_row_step": unit_bytes, "bytes_per_launch": bpl, "avg_launch_us": m["tile_us"]},
+                        "bytes_per_row_step": unit_bytes, "bytes_per_launch": bpl, "avg_launch_us": m["tile_us"],
+                        **roofline_extra(m, bpl)},
            "cpu_baseline": cpu}
     if m.get("merge_us") is not None:
         rec["merge_avg_us"] = m["merge_us"]
@@ -771,11 +837,11 @@ def main():
     cpu = score_cpu = None
     leg_cpu, lm_cpu = {}, None
     if args.cpu_seconds > 0:
-        cpu = cpu_baselines(wl, cat, args.cpu_seconds)
+        cpu = cpu_baselines(wl, cat, args.cpu_seconds, row_bytes=row_bytes(wl))
         log(f"[bench] oracle {cpu['value']:.0f} rows x steps/s ({cpu['cores']} processes), "
             f"{cpu['one_core']['value']:.0f} on one core; {cpu['cpu']}")
         for w in legs:
-            leg_cpu[w.name] = cpu_baselines(w, cats[w.name], max(3.0, args.cpu_seconds / 3))
+            leg_cpu[w.name] = cpu_baselines(w, cats[w.name], max(3.0, args.cpu_seconds / 3), row_bytes=row_bytes(w))
             log(f"[bench] oracle {w.name}: {leg_cpu[w.name]['value']:.0f} rows x steps/s")
         if args.lmhead:
             import numpy as np
@@ -847,7 +913,8 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": None if traffic is None else traffic / (m["tile_us"] * 1e-6) / 1e9,
                      "traffic_bytes_per_launch": traffic, "bytes_per_row_step": unit_bytes, "bytes_per_launch": bytes_per_launch,
-                     "avg_launch_us": m["tile_us"], "measured_copy_GBps": copy_gbps},
+                     "avg_launch_us": m["tile_us"], "measured_copy_GBps": copy_gbps,
+                     **roofline_extra(m, bytes_per_launch)},
         "hbm_GBps_wall": m["rows_x_steps"] * (unit_bytes + MERGE_WRITE_BYTES) * args.steps / m["elapsed"] / 1e9,
         "merge_avg_us": m["merge_us"],
         "legs": leg_out,
