@@ -10,7 +10,9 @@ The default workload is 32 requests x beam 512, L = 4, a catalog of 4M Zipf(1.1)
 and bf16 logits N(0, 3^2). Inputs (trie image, per-step logits) are resident in HBM
 before the timed region; consecutive decodes rotate through a pool of input copies
 larger than the 256 MB Infinity Cache, so every decode streams its logits from HBM.
-Each decode is replayed as a captured HIP graph (``--graph 0``: eager launches).
+Decodes are replayed from captured HIP graphs, each holding ``--graph-decodes`` decodes of
+consecutive input copies (a graph launch costs about 4 us on the GPU before its first kernel,
+so it is paid once per group; ``--graph 0``: eager launches, one library call per step).
 
 Also measured in the same run:
   * the other workloads as legs of their own ("legs"): 1 request x beam 50 (L = 3, 20k
@@ -259,6 +261,18 @@ def capture(decode, n):
     return graphs
 
 
+def capture_groups(decode, n, group):
+    """Graphs of ``group`` decodes each: graph i runs decode(i * group + j), j < group, for
+    the n input copies (n a multiple of group)."""
+    return capture(lambda i: [decode(i * group + j) for j in range(group)], n // group)
+
+
+def decode_groups(steps, want, pool):
+    """Decodes per graph: the largest divisor of both ``steps`` and the pool size that is at
+    most ``want``, so that exactly ``steps`` decodes are timed and every copy is used."""
+    return max(g for g in range(1, max(1, want) + 1) if steps % g == 0 and pool % g == 0)
+
+
 def timed(run, steps, warmup):
     import torch
     for d in range(warmup):
@@ -350,14 +364,15 @@ def one_wave_leg(args, wl, cat, dev):
         rid, _ = beams.init(widths)
         for t in range(L):
             beams.step(pool[c][t])
-    graphs = capture(decode, len(pool)) if args.graph else None
+    group = decode_groups(args.steps, args.graph_decodes, len(pool)) if args.graph else 1
+    graphs = capture_groups(decode, len(pool), group) if args.graph else None
 
     def run(d):
         if graphs is not None:
-            graphs[d % len(pool)].replay()
+            graphs[d % len(graphs)].replay()
         else:
             decode(d % len(pool))
-    elapsed = timed(run, args.steps, args.warmup)
+    elapsed = timed(run, args.steps // group, -(-args.warmup // group))
     verify_replay(trie, widths, pool[0], fin, ids, dev)
     # per-kernel durations: the same decodes again, eagerly, with events on the launch stream
     # around 10 back-to-back launches of each kernel (dispatch latency amortised)
@@ -374,6 +389,7 @@ def one_wave_leg(args, wl, cat, dev):
     beams.enable_timing(0)
     n_merge = n_timed // L * merge_steps(trie, widths, L)    # merge launches among the timed steps
     return {"elapsed": elapsed, "rows_x_steps": rows_x_steps, "rows_per_step": rows_per_step,
+            "graph_decodes": group if args.graph else 0,
             "tile_us": tile_ms * 1e3 / n_timed, "tile_us_cold": tile_ms_c * 1e3 / n_timed_c,
             "merge_us": merge_ms * 1e3 / n_merge if n_merge else None,
             "pool": len(pool), "sector_bytes": sector_bytes,
@@ -389,9 +405,9 @@ TRACE_NAMES = {1: "start", 8: "counts", 11: "window", 12: "offsets", 13: "cand",
 
 def phase_trace(args, wl, cat, dev):
     """Phase marks of every workgroup of one decode of the workload, captured as a HIP graph
-    (the timed route) and replayed ``args.phase_trace`` times, each time right behind
-    ``args.trace_behind`` untraced decodes of other input copies replayed back to back (as
-    the timed loop runs them; 0: after an idle GPU). Prints, per launch, the start skew
+    (the timed route; ``--graph 0``: launched eagerly) and run ``args.phase_trace`` times, each
+    time right behind ``args.trace_behind`` untraced decodes of other input copies run back to
+    back (as the timed loop runs them; 0: after an idle GPU). Prints, per launch, the start skew
     across workgroups, the span from the first start to the last mark, and the median
     per-workgroup time between consecutive marks (100 MHz clock)."""
     import numpy as np
@@ -420,21 +436,33 @@ def phase_trace(args, wl, cat, dev):
     for d in range(3):
         decode(d % len(pool))
     torch.cuda.synchronize()
-    others = capture(lambda c: decode(c + 1), nb) if nb else []
-    beams.set_trace(64 * 2 ** 20 // 8)
-    (g,) = capture(decode, 1)
+    if args.graph:
+        others = [o.replay for o in capture(lambda c: decode(c + 1), nb)] if nb else []
+        beams.set_trace(64 * 2 ** 20 // 8)
+        run_traced = capture(decode, 1)[0].replay
+    else:                                             # eager launches, one call per step
+        beams.set_trace(64 * 2 ** 20 // 8)
+
+        def other(c):
+            beams.pause_trace(True)
+            decode(c + 1)
+        others = [lambda c=c: other(c) for c in range(nb)]
+
+        def run_traced():
+            beams.pause_trace(False)
+            decode(0)
     reps = []
     for _ in range(args.phase_trace):
         for o in others:
-            o.replay()
-        g.replay()
+            o()
+        run_traced()
         torch.cuda.synchronize()
         reps.append(beams.trace())
         torch.cuda.synchronize()
     beams.set_trace(0)
-    lines = [f"# workload {wl.name}: {args.phase_trace} replays of one captured decode, each behind {nb} "
-             f"other decodes replayed back to back; times in us (median over replays; per-workgroup "
-             f"phases: median over workgroups)"]
+    how = "replays of one captured decode" if args.graph else "eager decodes"
+    lines = [f"# workload {wl.name}: {args.phase_trace} {how}, each behind {nb} other decodes run back to "
+             f"back; times in us (median over runs; per-workgroup phases: median over workgroups)"]
     # timeline: each launch's first start and last mark, from the decode's first start
     tl = []
     for rep in reps:
@@ -631,15 +659,16 @@ def lmhead_leg(args, dev, read_mode="dense"):
         rid, _ = beams.init(widths)
         for t in range(L):
             beams.step_lmhead(pool[c][t], w_dev)
-    graphs = capture(decode, len(pool)) if args.graph else None
+    steps = max(10, args.steps // 5)
+    group = decode_groups(steps, args.graph_decodes, len(pool)) if args.graph else 1
+    graphs = capture_groups(decode, len(pool), group) if args.graph else None
 
     def run(d):
         if graphs is not None:
-            graphs[d % len(pool)].replay()
+            graphs[d % len(graphs)].replay()
         else:
             decode(d % len(pool))
-    steps = max(10, args.steps // 5)
-    elapsed = timed(run, steps, max(2, args.warmup // 5))
+    elapsed = timed(run, steps // group, -(-max(2, args.warmup // 5) // group))
     n_ev = min(steps, 50)
     beams.enable_timing(n_ev * L, 10)
     for d in range(n_ev):
@@ -657,7 +686,8 @@ def lmhead_leg(args, dev, read_mode="dense"):
     head_s_c = head_ms_c / 1e3 / n_timed_c
     res = {"workload": wl.name, "read_mode": read_mode, "rows_per_step": rows_per_step,
            "value": rows_x_steps * steps / elapsed, "unit": "beam-rows x steps/s",
-           "ms_per_step": elapsed * 1e3 / steps, "steps": steps, "head_avg_us": head_s * 1e6,
+           "ms_per_step": elapsed * 1e3 / steps, "steps": steps, "graph_decodes": group if args.graph else 0,
+           "head_avg_us": head_s * 1e6,
            "head_avg_us_cold": head_s_c * 1e6,
            "tile_avg_us": tile_ms * 1e3 / n_timed, "merge_avg_us": merge_ms * 1e3 / n_merge if n_merge else None}
     if read_mode == "dense":
@@ -781,7 +811,7 @@ def leg_record(wl, m, steps, cat, cpu):
     rec = {"workload": wl.name, "value": value, "unit": "beam-rows x steps/s", "steps": steps,
            "ms_per_step": m["elapsed"] * 1e3 / steps, "requests": m["R"], "beam_width": m["B"], "L": m["L"],
            "catalog": int(cat.shape[0]), "rows_per_step": m["rows_per_step"], "rows_x_steps_per_decode":
-           m["rows_x_steps"], "input_pool_copies": m["pool"],
+           m["rows_x_steps"], "input_pool_copies": m["pool"], "decodes_per_graph": m.get("graph_decodes"),
            "roofline": {"bound": "hbm", "kernel": "k_tile", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                         "bytes_per_row_step": unit_bytes, "bytes_per_launch": bpl, "avg_launch_us": m["tile_us"],
@@ -800,7 +830,9 @@ def main():
     ap.add_argument("--workload", default="b512x32_l4_4m_zipf_bf16")
     ap.add_argument("--pool-gib", type=float, default=1.0, help="size of each rotated input pool")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle baseline budget (0: skip)")
-    ap.add_argument("--graph", type=int, default=1, help="replay each decode as a captured HIP graph")
+    ap.add_argument("--graph", type=int, default=1, help="replay the decodes from captured HIP graphs")
+    ap.add_argument("--graph-decodes", type=int, default=8,
+                    help="decodes (of consecutive input copies) per captured graph, at most")
     ap.add_argument("--lmhead", type=int, default=1, help="also run the SID-range lm_head leg")
     ap.add_argument("--score", type=int, default=1, help="also run the single-pass scoring leg")
     ap.add_argument("--legs", type=int, default=1, help="also run the other workloads' legs")
@@ -864,7 +896,8 @@ def main():
     m = one_wave_leg(args, wl, cat, dev)
     value, unit_bytes, bytes_per_launch, achieved = leg_summary(m, args.steps)
     traffic = recorded_traffic()
-    log(f"[bench] {args.steps} decodes in {m['elapsed'] * 1e3:.1f} ms; tile kernel avg {m['tile_us']:.2f} us "
+    log(f"[bench] {args.steps} decodes ({m['graph_decodes']} per graph) in {m['elapsed'] * 1e3:.1f} ms; "
+        f"tile kernel avg {m['tile_us']:.2f} us "
         f"({achieved:.0f} GB/s)" + (f", merge kernel avg {m['merge_us']:.2f} us" if m["merge_us"] is not None else ""))
     leg_out = {}
     for w in legs:
@@ -908,7 +941,8 @@ def main():
                    "catalog": int(cat.shape[0]), "catalog_levels": "zipf(1.1) at every level",
                    "logits": ("bf16" if wl.bf16 else "f32") + f" N(0,{wl.sigma:g}^2), upcast to f32",
                    "rows_x_steps_per_decode": m["rows_x_steps"], "rows_per_step": m["rows_per_step"],
-                   "graph": bool(args.graph), "input_pool_copies": m["pool"]},
+                   "graph": bool(args.graph), "decodes_per_graph": m["graph_decodes"],
+                   "input_pool_copies": m["pool"]},
         "roofline": {"bound": "hbm", "kernel": "k_tile", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": None if traffic is None else traffic / (m["tile_us"] * 1e-6) / 1e9,

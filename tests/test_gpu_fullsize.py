@@ -104,7 +104,8 @@ def test_fullsize_one_wave(name, sample):
 
 
 def _capture(decode, n):
-    """Each decode captured as a HIP graph on a side stream, as bench.py replays them."""
+    """decode(c) for c < n, each captured as a HIP graph on a side stream, as bench.py
+    captures its groups of decodes."""
     graphs = []
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -122,10 +123,10 @@ def _capture(decode, n):
 def test_fullsize_timed_route_graph_replay():
     """The route bench.py times, at its size: 32 requests x 512 beams, 4M Zipf catalog, bf16
     logits, steps back to back (each step's merge left to the next step's tile kernel), the
-    last step writing every request's beams to the finish outputs, each decode captured as a
-    HIP graph and replayed. Every replay's outputs must equal, bitwise, a decode of the same
-    inputs with an export after every step (each merge in the merge kernel, finalized
-    separately), which test_fullsize_one_wave checks against the oracle step by step for all
+    last step writing every request's beams to the finish outputs, two decodes (of two input
+    copies) captured per HIP graph and replayed. Every replay's outputs must equal, bitwise, a
+    decode of the same inputs with an export after every step (each merge in the merge kernel,
+    finalized separately), which test_fullsize_one_wave checks against the oracle step by step for all
     32 requests; the replays' beams must also be legal. Between replays the outputs are
     overwritten by eager work, so each replay must write all of them again."""
     wl, cat, otrie, lowest = _workload("b512x32_l4_4m_zipf_bf16")
@@ -160,7 +161,7 @@ def test_fullsize_timed_route_graph_replay():
             beams.step(pool[c][t])
     decode(0)                                          # one eager decode, as the bench's warm-up
     torch.cuda.synchronize()
-    graphs = _capture(decode, 2)
+    graphs = _capture(lambda c: [decode(c), decode(1 - c)], 2)   # two decodes per graph
     idx = np.asarray(ids)
     for rep in range(4):
         out["sids"].fill_(0xAB)

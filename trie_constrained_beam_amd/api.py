@@ -215,6 +215,16 @@ class Beams:
                        if capacity_words > 0 else None)
         check(lib().tcb_beams_set_trace(self._h, _ptr(self._trace), int(capacity_words)))
 
+    def pause_trace(self, paused: bool):
+        """Stop recording into the armed trace buffer (True), or start again at its beginning
+        (False), without allocating. Diagnostics only."""
+        if self._trace is None:
+            return
+        if paused:
+            check(lib().tcb_beams_set_trace(self._h, None, 0))
+        else:
+            check(lib().tcb_beams_set_trace(self._h, _ptr(self._trace), int(self._trace.numel())))
+
     def trace(self):
         """The traced launches: a list of (kind, level, records) with records an int64
         array [workgroups, TCB_TRACE_SLOTS] (word 0 = 1 + XCD, then clock marks). Synchronises."""
