@@ -11,13 +11,16 @@
 // v_mfma_f32_16x16x32_bf16. The block's K range is split across the waves: wave w
 // accumulates the whole 64 x 64 block (4 x 4 tiles of 16 x 16, 64 fp32 per lane) over
 // its quarter of K with many K-steps of loads in flight (one workgroup per CU leaves each
-// wave a whole SIMD and its register file). The loads are row-contiguous (four lanes read
-// one row's 64 bytes of a K-step) and each step passes through the wave's own LDS stage
-// into the MFMA operand layout (lane = row): loading that layout straight from memory
-// touches 16 rows per instruction and runs at about a third of the per-CU load rate
-// (measured on gfx950). The four partial blocks are then added through LDS in a
-// fixed order (wave 0 + 1 + 2 + 3), so results are deterministic. The four code blocks
-// of one row tile are dealt to the same XCD, so the hidden rows they share are read
+// wave a whole SIMD and its register file). The loads are row-contiguous (eight lanes read
+// 128 bytes of one row: two K-steps, whole 128-byte lines, so each request to L2 carries a
+// whole line) and each pair of steps passes through the wave's own LDS stage into the MFMA
+// operand layout (lane = row): loading that layout straight from memory touches 16 rows
+// per instruction and runs at about a third of the per-CU load rate (measured on gfx950).
+// In the stage, 16-byte piece p of row r sits at piece p ^ (r mod 8) of the row, so that
+// neither the row-wise writes nor the MFMA-layout reads (8 lanes per LDS pass, 8
+// consecutive rows) meet a bank conflict. The four partial blocks are then added through
+// LDS in a fixed order (wave 0 + 1 + 2 + 3), so results are deterministic. The four code
+// blocks of one row tile are dealt to the same XCD, so the hidden rows they share are read
 // from HBM once and then hit that XCD's L2.
 //
 #include "tcb_internal.h"
@@ -33,9 +36,16 @@ constexpr int kGRows = 64;                 // rows of a block
 constexpr int kGCodes = 64;                // codes of a block (4 blocks cover V = 256)
 constexpr int kGThreads = 256;             // 4 waves, each over a quarter of K
 constexpr int kKStep = 32;                 // K of one MFMA
-// a staged row (64 bytes of one K-step) padded to 80 bytes: the 16 rows one MFMA-layout
-// read instruction touches start in distinct 16-byte bank groups
-constexpr int kStageRow = 80;
+
+// K-steps per load chunk: two (128 bytes of a row) where the wave's step count is even
+template <int NS>
+constexpr int lm_group() { return NS > 0 && NS % 2 == 0 ? 2 : 1; }
+// byte offset of 16-byte piece p of row r in a stage whose rows hold G K-steps (64 G bytes):
+// pieces are permuted within the row by the row's low bits (conflict-free writes and reads)
+template <int G>
+__device__ __forceinline__ int stage_at(int r, int p) {
+    return r * 64 * G + 16 * (p ^ (G == 2 ? (r & 7) : ((r >> 1) & 3)));
+}
 
 // NS = K-steps of 32 per wave (H = 4 * 32 * NS); NS = 0: any H % 128 == 0, one step
 // of loads in flight.
@@ -44,8 +54,12 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
                                                       const uint16_t *__restrict__ hidden, int64_t ld, int H,
                                                       const uint16_t *__restrict__ weight,
                                                       float *__restrict__ out) {
+    constexpr int G = lm_group<NS>();                        // K-steps per load chunk
+    constexpr int LPR = 4 * G;                                // lanes per row in a load (16 bytes each)
+    constexpr int RPI = 64 / LPR;                             // rows per load instruction
+    constexpr int NI = kGRows / RPI;                          // load instructions per operand and chunk
     __shared__ f32x4 red[4][4][4][64];                        // [wave][row blk][code blk][lane]
-    __shared__ __attribute__((aligned(16))) uint8_t stage[4][2][64 * kStageRow];   // [wave][A, B][row]
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][2][kGRows * 64 * G];   // [wave][A, B][row]
     const int MT = W.MT;
     const int xcd = (int)(blockIdx.x & 7u), i8 = (int)(blockIdx.x >> 3);
     const int cblk = i8 & 3;                                  // code block 0..3
@@ -62,15 +76,15 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kq = lane >> 4;                // MFMA layout: row l16, k chunk kq
-    const int lr = lane >> 2, lc = lane & 3;                  // loads: row lr (+16 i), 16-byte chunk lc
+    const int lr = lane / LPR, lc = lane % LPR;               // loads: row lr (+RPI i), 16-byte piece lc
     const int nsteps = NS > 0 ? NS : H / (4 * kKStep);
     const int kw0 = wave * nsteps * kKStep;                   // this wave's first k
-    const uint16_t *ag[4], *bg[4];
+    const uint16_t *ag[NI], *bg[NI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ar = r0 + 16 * i + lr;                      // rows past the bound read row r0, never stored
+    for (int i = 0; i < NI; ++i) {
+        const int ar = r0 + RPI * i + lr;                     // rows past the bound read row r0, never stored
         ag[i] = hidden + (size_t)(base + (ar < rows_bound ? ar : r0)) * (size_t)ld + kw0 + 8 * lc;
-        bg[i] = weight + ((size_t)level * 256 + (size_t)cblk * kGCodes + 16 * i + lr) * (size_t)H + kw0 + 8 * lc;
+        bg[i] = weight + ((size_t)level * 256 + (size_t)cblk * kGCodes + RPI * i + lr) * (size_t)H + kw0 + 8 * lc;
     }
     uint8_t *sa = stage[wave][0], *sb = stage[wave][1];
     f32x4 acc[4][4];
@@ -78,67 +92,72 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // one K-step: the loaded pieces into the wave's stage, back out in the MFMA layout
-    // (the same k of each row as a direct load of that layout), 4 x 4 MFMAs. LDS operations
-    // of one wave complete in order, so the stage needs no barrier.
-    auto stage_step = [&](const u32x4 (&ra)[4], const u32x4 (&rb)[4]) {
+    // one chunk of G K-steps: the loaded pieces into the wave's stage, back out in the MFMA
+    // layout (the same k of each row as a direct load of that layout), 4 x 4 MFMAs per
+    // K-step in K order. LDS operations of one wave complete in order, so the stage needs
+    // no barrier.
+    auto stage_chunk = [&](const u32x4 (&ra)[NI], const u32x4 (&rb)[NI]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<u32x4 *>(sa + (16 * i + lr) * kStageRow + 16 * lc) = ra[i];
-            *reinterpret_cast<u32x4 *>(sb + (16 * i + lr) * kStageRow + 16 * lc) = rb[i];
+        for (int i = 0; i < NI; ++i) {
+            *reinterpret_cast<u32x4 *>(sa + stage_at<G>(RPI * i + lr, lc)) = ra[i];
+            *reinterpret_cast<u32x4 *>(sb + stage_at<G>(RPI * i + lr, lc)) = rb[i];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        u32x4 av[4], bv[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            av[b] = *reinterpret_cast<const u32x4 *>(sa + (16 * b + l16) * kStageRow + 16 * kq);
-            bv[b] = *reinterpret_cast<const u32x4 *>(sb + (16 * b + l16) * kStageRow + 16 * kq);
+        for (int h = 0; h < G; ++h) {
+            u32x4 av[4], bv[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                av[b] = *reinterpret_cast<const u32x4 *>(sa + stage_at<G>(16 * b + l16, 4 * h + kq));
+                bv[b] = *reinterpret_cast<const u32x4 *>(sb + stage_at<G>(16 * b + l16, 4 * h + kq));
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[a]),
+                                                                        __builtin_bit_cast(bf16x8, bv[b]), acc[a][b],
+                                                                        0, 0, 0);
         }
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[a]),
-                                                                    __builtin_bit_cast(bf16x8, bv[b]), acc[a][b],
-                                                                    0, 0, 0);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
     if constexpr (NS > 0) {
-        // a ring of PD K-steps of loads in registers, refilled as each step is used
-        constexpr int PD = NS < 4 ? NS : 4;       // deeper rings spill past the 256 VGPRs
-        u32x4 ra[PD][4], rb[PD][4];
+        // a ring of PD chunks of loads in registers, refilled as each chunk is used
+        constexpr int NC = NS / G;                            // chunks per wave
+        constexpr int PD = NC < 4 / G ? NC : 4 / G;           // 4 K-steps of loads in flight
+        u32x4 ra[PD][NI], rb[PD][NI];
 #pragma unroll
         for (int s = 0; s < PD; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ra[s][i] = *reinterpret_cast<const u32x4 *>(ag[i] + s * kKStep);
-                rb[s][i] = *reinterpret_cast<const u32x4 *>(bg[i] + s * kKStep);
+            for (int i = 0; i < NI; ++i) {
+                ra[s][i] = *reinterpret_cast<const u32x4 *>(ag[i] + s * G * kKStep);
+                rb[s][i] = *reinterpret_cast<const u32x4 *>(bg[i] + s * G * kKStep);
             }
         __builtin_amdgcn_sched_barrier(0);                    // keep the ring's loads issued up front
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            stage_step(ra[s % PD], rb[s % PD]);
-            if (s + PD < NS) {
+        for (int s = 0; s < NC; ++s) {
+            stage_chunk(ra[s % PD], rb[s % PD]);
+            if (s + PD < NC) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ra[s % PD][i] = *reinterpret_cast<const u32x4 *>(ag[i] + (s + PD) * kKStep);
-                    rb[s % PD][i] = *reinterpret_cast<const u32x4 *>(bg[i] + (s + PD) * kKStep);
+                for (int i = 0; i < NI; ++i) {
+                    ra[s % PD][i] = *reinterpret_cast<const u32x4 *>(ag[i] + (s + PD) * G * kKStep);
+                    rb[s % PD][i] = *reinterpret_cast<const u32x4 *>(bg[i] + (s + PD) * G * kKStep);
                 }
             }
         }
     } else {
         for (int s = 0; s < nsteps; ++s) {
-            u32x4 ra[4], rb[4];
+            u32x4 ra[NI], rb[NI];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < NI; ++i) {
                 ra[i] = *reinterpret_cast<const u32x4 *>(ag[i] + s * kKStep);
                 rb[i] = *reinterpret_cast<const u32x4 *>(bg[i] + s * kKStep);
             }
-            stage_step(ra, rb);
+            stage_chunk(ra, rb);
         }
     }
     // a first step: the root only; a pending merge (done by the tile kernel that follows):
