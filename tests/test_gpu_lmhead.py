@@ -64,6 +64,14 @@ def test_lmhead_step_parity_wide_k():
     _run_lmhead(cat, [512, 200], 2048, 52)
 
 
+@pytest.mark.parametrize("H", [384, 1024])
+def test_lmhead_narrow_beams_16_row_tiles(H):
+    """Every request at most 16 beams wide: every level's head runs on 16-row tiles (the
+    first step's tiling), with the generic K loop (H = 384) and the two-step loads (1024)."""
+    cat = synth.catalog(20_000, 4, ("uniform",) * 4, [55, 1])
+    _run_lmhead(cat, [16, 5, 9, 1], H, 55)
+
+
 def test_lmhead_matches_stepping_with_torch_logits():
     """The lm_head step equals tcb_beam_step on logits from an fp32 torch matmul of the same
     inputs up to fp32 rounding: same survivors wherever no near-tie decides."""

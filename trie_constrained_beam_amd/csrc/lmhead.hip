@@ -48,8 +48,9 @@ __device__ __forceinline__ int stage_at(int r, int p) {
 }
 
 // NS = K-steps of 32 per wave (H = 4 * 32 * NS); NS = 0: any H % 128 == 0, one step
-// of loads in flight.
-template <int NS>
+// of loads in flight. RB = row blocks of 16 per tile: 4, or 1 where every request of the
+// launch has at most 16 rows (a first step), which then computes no dead row blocks.
+template <int NS, int RB>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_lmhead(TrieDev T, WaveDev W, int rp, StepReqs R,
                                                       const uint16_t *__restrict__ hidden, int64_t ld, int H,
                                                       const uint16_t *__restrict__ weight,
@@ -57,10 +58,12 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     constexpr int G = lm_group<NS>();                        // K-steps per load chunk
     constexpr int LPR = 4 * G;                                // lanes per row in a load (16 bytes each)
     constexpr int RPI = 64 / LPR;                             // rows per load instruction
-    constexpr int NI = kGRows / RPI;                          // load instructions per operand and chunk
-    __shared__ f32x4 red[4][4][4][64];                        // [wave][row blk][code blk][lane]
-    __shared__ __attribute__((aligned(16))) uint8_t stage[4][2][kGRows * 64 * G];   // [wave][A, B][row]
-    const int MT = W.MT;
+    constexpr int TR = 16 * RB;                               // rows of a tile
+    constexpr int NIA = TR / RPI, NIB = kGCodes / RPI;        // load instructions per chunk: rows, codes
+    __shared__ f32x4 red[4][RB][4][64];                       // [wave][row blk][code blk][lane]
+    __shared__ __attribute__((aligned(16))) uint8_t stage_a[4][TR * 64 * G];       // [wave][row]
+    __shared__ __attribute__((aligned(16))) uint8_t stage_b[4][kGCodes * 64 * G];  // [wave][code]
+    const int MT = RB == 4 ? W.MT : 1;                        // tiles per request
     const int xcd = (int)(blockIdx.x & 7u), i8 = (int)(blockIdx.x >> 3);
     const int cblk = i8 & 3;                                  // code block 0..3
     const int gt = (i8 >> 2) * 8 + xcd;                       // row tile over (request, tile)
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     if (ql >= R.n) return;
     const ReqArg ra = R.r[ql];
     if (!ra.step() || ra.sparse_head()) return;
-    const int r0 = rt * kGRows;
+    const int r0 = rt * TR;
     if (r0 >= ra.rmax()) return;
     // operand loads are issued for every row the request can have; the live-row count
     // arrives with them and decides which results are stored
@@ -79,42 +82,44 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     const int lr = lane / LPR, lc = lane % LPR;               // loads: row lr (+RPI i), 16-byte piece lc
     const int nsteps = NS > 0 ? NS : H / (4 * kKStep);
     const int kw0 = wave * nsteps * kKStep;                   // this wave's first k
-    const uint16_t *ag[NI], *bg[NI];
+    const uint16_t *ag[NIA], *bg[NIB];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int i = 0; i < NIA; ++i) {
         const int ar = r0 + RPI * i + lr;                     // rows past the bound read row r0, never stored
         ag[i] = hidden + (size_t)(base + (ar < rows_bound ? ar : r0)) * (size_t)ld + kw0 + 8 * lc;
-        bg[i] = weight + ((size_t)level * 256 + (size_t)cblk * kGCodes + RPI * i + lr) * (size_t)H + kw0 + 8 * lc;
     }
-    uint8_t *sa = stage[wave][0], *sb = stage[wave][1];
-    f32x4 acc[4][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int i = 0; i < NIB; ++i)
+        bg[i] = weight + ((size_t)level * 256 + (size_t)cblk * kGCodes + RPI * i + lr) * (size_t)H + kw0 + 8 * lc;
+    uint8_t *sa = stage_a[wave], *sb = stage_b[wave];
+    f32x4 acc[RB][4];
+#pragma unroll
+    for (int a = 0; a < RB; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     // one chunk of G K-steps: the loaded pieces into the wave's stage, back out in the MFMA
-    // layout (the same k of each row as a direct load of that layout), 4 x 4 MFMAs per
+    // layout (the same k of each row as a direct load of that layout), RB x 4 MFMAs per
     // K-step in K order. LDS operations of one wave complete in order, so the stage needs
     // no barrier.
-    auto stage_chunk = [&](const u32x4 (&ra)[NI], const u32x4 (&rb)[NI]) {
+    auto stage_chunk = [&](const u32x4 (&ra)[NIA], const u32x4 (&rb)[NIB]) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            *reinterpret_cast<u32x4 *>(sa + stage_at<G>(RPI * i + lr, lc)) = ra[i];
-            *reinterpret_cast<u32x4 *>(sb + stage_at<G>(RPI * i + lr, lc)) = rb[i];
-        }
+        for (int i = 0; i < NIA; ++i) *reinterpret_cast<u32x4 *>(sa + stage_at<G>(RPI * i + lr, lc)) = ra[i];
+#pragma unroll
+        for (int i = 0; i < NIB; ++i) *reinterpret_cast<u32x4 *>(sb + stage_at<G>(RPI * i + lr, lc)) = rb[i];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            u32x4 av[4], bv[4];
+            u32x4 av[RB], bv[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                av[b] = *reinterpret_cast<const u32x4 *>(sa + stage_at<G>(16 * b + l16, 4 * h + kq));
+            for (int a = 0; a < RB; ++a)
+                av[a] = *reinterpret_cast<const u32x4 *>(sa + stage_at<G>(16 * a + l16, 4 * h + kq));
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
                 bv[b] = *reinterpret_cast<const u32x4 *>(sb + stage_at<G>(16 * b + l16, 4 * h + kq));
-            }
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < RB; ++a)
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[a]),
@@ -129,56 +134,58 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
         // a ring of PD chunks of loads in registers, refilled as each chunk is used
         constexpr int NC = NS / G;                            // chunks per wave
         constexpr int PD = NC < 4 / G ? NC : 4 / G;           // 4 K-steps of loads in flight
-        u32x4 ra[PD][NI], rb[PD][NI];
+        u32x4 ra[PD][NIA], rb[PD][NIB];
 #pragma unroll
-        for (int s = 0; s < PD; ++s)
+        for (int s = 0; s < PD; ++s) {
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                ra[s][i] = *reinterpret_cast<const u32x4 *>(ag[i] + s * G * kKStep);
-                rb[s][i] = *reinterpret_cast<const u32x4 *>(bg[i] + s * G * kKStep);
-            }
+            for (int i = 0; i < NIA; ++i) ra[s][i] = *reinterpret_cast<const u32x4 *>(ag[i] + s * G * kKStep);
+#pragma unroll
+            for (int i = 0; i < NIB; ++i) rb[s][i] = *reinterpret_cast<const u32x4 *>(bg[i] + s * G * kKStep);
+        }
         __builtin_amdgcn_sched_barrier(0);                    // keep the ring's loads issued up front
 #pragma unroll
         for (int s = 0; s < NC; ++s) {
             stage_chunk(ra[s % PD], rb[s % PD]);
             if (s + PD < NC) {
 #pragma unroll
-                for (int i = 0; i < NI; ++i) {
+                for (int i = 0; i < NIA; ++i)
                     ra[s % PD][i] = *reinterpret_cast<const u32x4 *>(ag[i] + (s + PD) * G * kKStep);
+#pragma unroll
+                for (int i = 0; i < NIB; ++i)
                     rb[s % PD][i] = *reinterpret_cast<const u32x4 *>(bg[i] + (s + PD) * G * kKStep);
-                }
             }
         }
     } else {
         for (int s = 0; s < nsteps; ++s) {
-            u32x4 ra[NI], rb[NI];
+            u32x4 ra[NIA], rb[NIB];
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                ra[i] = *reinterpret_cast<const u32x4 *>(ag[i] + s * kKStep);
-                rb[i] = *reinterpret_cast<const u32x4 *>(bg[i] + s * kKStep);
-            }
+            for (int i = 0; i < NIA; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(ag[i] + s * kKStep);
+#pragma unroll
+            for (int i = 0; i < NIB; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(bg[i] + s * kKStep);
             stage_chunk(ra, rb);
         }
     }
     // a first step: the root only; a pending merge (done by the tile kernel that follows):
     // every row the request can have
     const int rows = level == 0 ? 1 : R.r[ql].pending() ? rows_bound : W.rec[rp][R.q0 + ql].rows;
-    // partial blocks of the four waves, added in a fixed order; wave w finishes row block w
+    // partial blocks of the four waves, added in a fixed order; wave w finishes the blocks
+    // (a, b) with a + b = w mod 4 (RB = 4), or block (0, w)
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < RB; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) red[wave][a][b][lane] = acc[a][b];
     __syncthreads();
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        f32x4 v = red[0][wave][b][lane];
-        v += red[1][wave][b][lane];
-        v += red[2][wave][b][lane];
-        v += red[3][wave][b][lane];
-        // D layout: rows 4 kq + i of row block `wave`, code 16 b + l16 of the block
+    for (int a = 0; a < RB; ++a) {
+        const int b = RB == 4 ? (wave - a) & 3 : wave;
+        f32x4 v = red[0][a][b][lane];
+        v += red[1][a][b][lane];
+        v += red[2][a][b][lane];
+        v += red[3][a][b][lane];
+        // D layout: rows 4 kq + i of row block a, code 16 b + l16 of the block
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = r0 + 16 * wave + 4 * kq + i;
+            const int row = r0 + 16 * a + 4 * kq + i;
             if (row < rows) out[(size_t)(base + row) * 256 + cblk * kGCodes + 16 * b + l16] = v[i];
         }
     }
@@ -257,20 +264,35 @@ hipError_t launch_lmhead_sparse(const TrieDev &t, const WaveDev &w, int rp, cons
     return hipGetLastError();
 }
 
+namespace {
+
+template <int RB>
+void launch_lmhead_rb(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const uint16_t *h, int64_t ld,
+                      int H, const uint16_t *wt, float *out, hipStream_t s) {
+    const int tiles = R.n * (RB == 4 ? w.MT : 1);             // row tiles over all requests
+    const int groups = (tiles + 7) / 8;
+    const dim3 grid(8 * groups * 4), block(kGThreads);
+    switch (H) {
+    case 512: hipLaunchKernelGGL((k_lmhead<4, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
+    case 1024: hipLaunchKernelGGL((k_lmhead<8, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
+    case 2048: hipLaunchKernelGGL((k_lmhead<16, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
+    case 4096: hipLaunchKernelGGL((k_lmhead<32, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
+    default: hipLaunchKernelGGL((k_lmhead<0, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
+    }
+}
+
+}  // namespace
+
 hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
                          int64_t ld, int H, const void *weight, float *out, hipStream_t s) {
     if (R.n <= 0) return hipSuccess;
-    const int tiles = R.n * w.MT;                             // row tiles over all requests
-    const int groups = (tiles + 7) / 8;
-    const dim3 grid(8 * groups * 4), block(kGThreads);
+    // 16-row tiles where no request of the launch can have more than 16 rows (a first step)
+    int rmax = 0;
+    for (int i = 0; i < R.n; ++i)
+        if (R.r[i].step() && !R.r[i].sparse_head()) rmax = std::max(rmax, R.r[i].rmax());
     const uint16_t *h = static_cast<const uint16_t *>(hidden), *wt = static_cast<const uint16_t *>(weight);
-    switch (H) {
-    case 512: hipLaunchKernelGGL(k_lmhead<4>, grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
-    case 1024: hipLaunchKernelGGL(k_lmhead<8>, grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
-    case 2048: hipLaunchKernelGGL(k_lmhead<16>, grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
-    case 4096: hipLaunchKernelGGL(k_lmhead<32>, grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
-    default: hipLaunchKernelGGL(k_lmhead<0>, grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
-    }
+    if (rmax <= 16) launch_lmhead_rb<1>(t, w, rp, R, h, ld, H, wt, out, s);
+    else launch_lmhead_rb<4>(t, w, rp, R, h, ld, H, wt, out, s);
     return hipGetLastError();
 }
 
