@@ -404,10 +404,10 @@ TRACE_NAMES = {1: "start", 8: "counts", 11: "window", 12: "offsets", 13: "cand",
 
 
 def phase_trace(args, wl, cat, dev):
-    """Phase marks of every workgroup of one decode of the workload, captured as a HIP graph
-    (the timed route; ``--graph 0``: launched eagerly) and run ``args.phase_trace`` times, each
-    time right behind ``args.trace_behind`` untraced decodes of other input copies run back to
-    back (as the timed loop runs them; 0: after an idle GPU). Prints, per launch, the start skew
+    """Phase marks of every workgroup of one decode of the workload, the last of a captured
+    graph of ``--graph-decodes`` decodes (the timed route; ``--graph 0``: launched eagerly), run
+    ``args.phase_trace`` times, each time right behind ``args.trace_behind`` untraced decodes of
+    other input copies run back to back (0: after an idle GPU). Prints, per launch, the start skew
     across workgroups, the span from the first start to the last mark, and the median
     per-workgroup time between consecutive marks (100 MHz clock)."""
     import numpy as np
@@ -436,10 +436,12 @@ def phase_trace(args, wl, cat, dev):
     for d in range(3):
         decode(d % len(pool))
     torch.cuda.synchronize()
+    group = max(1, args.graph_decodes) if args.graph else 1
     if args.graph:
         others = [o.replay for o in capture(lambda c: decode(c + 1), nb)] if nb else []
         beams.set_trace(64 * 2 ** 20 // 8)
-        run_traced = capture(decode, 1)[0].replay
+        # a graph of `group` decodes, as the timed loop captures them; the last one is read
+        run_traced = capture(lambda _: [decode(j % len(pool)) for j in range(group)], 1)[0].replay
     else:                                             # eager launches, one call per step
         beams.set_trace(64 * 2 ** 20 // 8)
 
@@ -457,10 +459,11 @@ def phase_trace(args, wl, cat, dev):
             o()
         run_traced()
         torch.cuda.synchronize()
-        reps.append(beams.trace())
+        tr = beams.trace()
+        reps.append(tr[len(tr) - len(tr) // group:])     # the last decode's launches
         torch.cuda.synchronize()
     beams.set_trace(0)
-    how = "replays of one captured decode" if args.graph else "eager decodes"
+    how = (f"replays of a graph of {group} decodes (the last one traced)" if args.graph else "eager decodes")
     lines = [f"# workload {wl.name}: {args.phase_trace} {how}, each behind {nb} other decodes run back to "
              f"back; times in us (median over runs; per-workgroup phases: median over workgroups)"]
     # timeline: each launch's first start and last mark, from the decode's first start
