@@ -48,13 +48,14 @@ __device__ __forceinline__ int stage_at(int r, int p) {
 }
 
 // NS = K-steps of 32 per wave (H = 4 * 32 * NS); NS = 0: any H % 128 == 0, one step
-// of loads in flight. RB = row blocks of 16 per tile: 4, or 1 where every request of the
-// launch has at most 16 rows (a first step), which then computes no dead row blocks.
+// of loads in flight. RB = row blocks of 16 per tile (4, 2 or 1) and mt = tiles per request:
+// smaller tiles where 64-row tiles would leave CUs idle (a first step, or few rows), so that
+// the launch fills the chip and computes fewer dead rows.
 template <int NS, int RB>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_lmhead(TrieDev T, WaveDev W, int rp, StepReqs R,
                                                       const uint16_t *__restrict__ hidden, int64_t ld, int H,
                                                       const uint16_t *__restrict__ weight,
-                                                      float *__restrict__ out) {
+                                                      float *__restrict__ out, int mt) {
     constexpr int G = lm_group<NS>();                        // K-steps per load chunk
     constexpr int LPR = 4 * G;                                // lanes per row in a load (16 bytes each)
     constexpr int RPI = 64 / LPR;                             // rows per load instruction
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     __shared__ f32x4 red[4][RB][4][64];                       // [wave][row blk][code blk][lane]
     __shared__ __attribute__((aligned(16))) uint8_t stage_a[4][TR * 64 * G];       // [wave][row]
     __shared__ __attribute__((aligned(16))) uint8_t stage_b[4][kGCodes * 64 * G];  // [wave][code]
-    const int MT = RB == 4 ? W.MT : 1;                        // tiles per request
+    const int MT = mt;
     const int xcd = (int)(blockIdx.x & 7u), i8 = (int)(blockIdx.x >> 3);
     const int cblk = i8 & 3;                                  // code block 0..3
     const int gt = (i8 >> 2) * 8 + xcd;                       // row tile over (request, tile)
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     // every row the request can have
     const int rows = level == 0 ? 1 : R.r[ql].pending() ? rows_bound : W.rec[rp][R.q0 + ql].rows;
     // partial blocks of the four waves, added in a fixed order; wave w finishes the blocks
-    // (a, b) with a + b = w mod 4 (RB = 4), or block (0, w)
+    // (a, b) with a + b = w mod 4
 #pragma unroll
     for (int a = 0; a < RB; ++a)
 #pragma unroll
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     __syncthreads();
 #pragma unroll
     for (int a = 0; a < RB; ++a) {
-        const int b = RB == 4 ? (wave - a) & 3 : wave;
+        const int b = (wave - a) & 3;
         f32x4 v = red[0][a][b][lane];
         v += red[1][a][b][lane];
         v += red[2][a][b][lane];
@@ -266,18 +267,31 @@ hipError_t launch_lmhead_sparse(const TrieDev &t, const WaveDev &w, int rp, cons
 
 namespace {
 
+// compute units of the current device (queried once per device)
+int cu_count() {
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] <= 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) return 256;
+        cache[dev] = c;
+    }
+    return cache[dev];
+}
+
 template <int RB>
 void launch_lmhead_rb(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const uint16_t *h, int64_t ld,
-                      int H, const uint16_t *wt, float *out, hipStream_t s) {
-    const int tiles = R.n * (RB == 4 ? w.MT : 1);             // row tiles over all requests
+                      int H, const uint16_t *wt, float *out, int mt, hipStream_t s) {
+    const int tiles = R.n * mt;                               // row tiles over all requests
     const int groups = (tiles + 7) / 8;
     const dim3 grid(8 * groups * 4), block(kGThreads);
     switch (H) {
-    case 512: hipLaunchKernelGGL((k_lmhead<4, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
-    case 1024: hipLaunchKernelGGL((k_lmhead<8, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
-    case 2048: hipLaunchKernelGGL((k_lmhead<16, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
-    case 4096: hipLaunchKernelGGL((k_lmhead<32, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
-    default: hipLaunchKernelGGL((k_lmhead<0, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out); break;
+    case 512: hipLaunchKernelGGL((k_lmhead<4, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out, mt); break;
+    case 1024: hipLaunchKernelGGL((k_lmhead<8, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out, mt); break;
+    case 2048: hipLaunchKernelGGL((k_lmhead<16, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out, mt); break;
+    case 4096: hipLaunchKernelGGL((k_lmhead<32, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out, mt); break;
+    default: hipLaunchKernelGGL((k_lmhead<0, RB>), grid, block, 0, s, t, w, rp, R, h, ld, H, wt, out, mt); break;
     }
 }
 
@@ -286,13 +300,17 @@ void launch_lmhead_rb(const TrieDev &t, const WaveDev &w, int rp, const StepReqs
 hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
                          int64_t ld, int H, const void *weight, float *out, hipStream_t s) {
     if (R.n <= 0) return hipSuccess;
-    // 16-row tiles where no request of the launch can have more than 16 rows (a first step)
-    int rmax = 0;
+    int rmax = 0;                                             // rows any request of the launch can have
     for (int i = 0; i < R.n; ++i)
         if (R.r[i].step() && !R.r[i].sparse_head()) rmax = std::max(rmax, R.r[i].rmax());
+    if (rmax <= 0) return hipSuccess;
+    // the tallest tiles whose 4 code blocks still give every CU a workgroup; else 16 rows
+    const int cus = cu_count();
+    auto tiles = [&](int rows) { return (rmax + rows - 1) / rows; };
     const uint16_t *h = static_cast<const uint16_t *>(hidden), *wt = static_cast<const uint16_t *>(weight);
-    if (rmax <= 16) launch_lmhead_rb<1>(t, w, rp, R, h, ld, H, wt, out, s);
-    else launch_lmhead_rb<4>(t, w, rp, R, h, ld, H, wt, out, s);
+    if (4 * R.n * tiles(64) >= cus) launch_lmhead_rb<4>(t, w, rp, R, h, ld, H, wt, out, tiles(64), s);
+    else if (4 * R.n * tiles(32) >= cus) launch_lmhead_rb<2>(t, w, rp, R, h, ld, H, wt, out, tiles(32), s);
+    else launch_lmhead_rb<1>(t, w, rp, R, h, ld, H, wt, out, tiles(16), s);
     return hipGetLastError();
 }
 
