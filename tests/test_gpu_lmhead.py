@@ -72,6 +72,15 @@ def test_lmhead_narrow_beams_16_row_tiles(H):
     _run_lmhead(cat, [16, 5, 9, 1], H, 55)
 
 
+def test_lmhead_generic_k_every_tile_height():
+    """H = 384 (the generic K loop, one K-step per load) with 8 requests of width 512 and the
+    dense head at every level: on the 256-CU MI355X the first step runs 16-row tiles, level 1
+    (2,048 rows) 32-row tiles and levels 2-3 64-row tiles; three requests checked against the
+    oracle at every step."""
+    cat = synth.catalog(300_000, 4, ("uniform",) * 4, [56, 1])
+    _run_lmhead(cat, [512] * 8, 384, 56, check_reqs=[0, 3, 7], read_mode="dense")
+
+
 def test_lmhead_matches_stepping_with_torch_logits():
     """The lm_head step equals tcb_beam_step on logits from an fp32 torch matmul of the same
     inputs up to fp32 rounding: same survivors wherever no near-tie decides."""
