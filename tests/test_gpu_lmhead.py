@@ -144,3 +144,23 @@ def test_lmhead_children_only_deterministic():
         a, b = states[0][k], states[1][k]
         assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                               b.view(np.uint32) if b.dtype == np.float32 else b), k
+
+
+def test_lmhead_dense_wide_k_deterministic():
+    """Dense head with H = 4096 (32 K-steps per wave, two per load) against the oracle, then
+    the same decode twice: bitwise equal states (the K split's partial sums are added in a
+    fixed order)."""
+    cat = synth.catalog(25_000, 3, ("zipf",) * 3, [57, 1])
+    _run_lmhead(cat, [128, 33], 4096, 57, read_mode="dense")
+    H = 4096
+    weights = _bf16_dev(np.stack([synth.lmhead_weight(57, lv, 256, H) for lv in range(3)]))
+    states = []
+    for _ in range(2):
+        run = gh.Run(cat, [128, 33], read_mode="dense")
+        for t in range(3):
+            run.beams.step_lmhead(_bf16_dev(synth.hidden_states(57, t, run.max_slots, H)), weights)
+        states.append(run.state())
+    for k in ("node", "score", "hist", "rows"):
+        a, b = states[0][k], states[1][k]
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b), k
