@@ -8,10 +8,11 @@
 // so the masked log-softmax and selection are the same code as for logits from memory.
 //
 // Tiling. A workgroup of 4 waves computes a 64-row x 64-code block with
-// v_mfma_f32_16x16x32_bf16. The block's K range is split across the waves: wave w
-// accumulates the whole 64 x 64 block (4 x 4 tiles of 16 x 16, 64 fp32 per lane) over
-// its quarter of K with many K-steps of loads in flight (one workgroup per CU leaves each
-// wave a whole SIMD and its register file). The loads are row-contiguous (eight lanes read
+// v_mfma_f32_16x16x32_bf16 (32 or 16 rows where 64-row blocks would leave CUs idle). The
+// block's K range is split across the waves: wave w accumulates the whole 64 x 64 block
+// (4 x 4 tiles of 16 x 16, 64 fp32 per lane) over its quarter of K with many K-steps of
+// loads in flight (one workgroup per CU leaves each wave a whole SIMD and its register
+// file). The loads are row-contiguous (eight lanes read
 // 128 bytes of one row: two K-steps, whole 128-byte lines, so each request to L2 carries a
 // whole line) and each pair of steps passes through the wave's own LDS stage into the MFMA
 // operand layout (lane = row): loading that layout straight from memory touches 16 rows
@@ -32,7 +33,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGRows = 64;                 // rows of a block
 constexpr int kGCodes = 64;                // codes of a block (4 blocks cover V = 256)
 constexpr int kGThreads = 256;             // 4 waves, each over a quarter of K
 constexpr int kKStep = 32;                 // K of one MFMA
