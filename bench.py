@@ -12,7 +12,8 @@ before the timed region; consecutive decodes rotate through a pool of input copi
 larger than the 256 MB Infinity Cache, so every decode streams its logits from HBM.
 Decodes are replayed from captured HIP graphs, each holding ``--graph-decodes`` decodes of
 consecutive input copies (a graph launch costs about 4 us on the GPU before its first kernel,
-so it is paid once per group; ``--graph 0``: eager launches, one library call per step).
+so it is paid once per group; ``--graph 0``: eager launches, one library call per step). The
+line also gives ``ms_per_step_eager``: the same decodes launched eagerly, timed right after.
 
 Also measured in the same run:
   * the other workloads as legs of their own ("legs"): 1 request x beam 50 (L = 3, 20k
@@ -373,6 +374,9 @@ def one_wave_leg(args, wl, cat, dev):
         else:
             decode(d % len(pool))
     elapsed = timed(run, args.steps // group, -(-args.warmup // group))
+    # the same decodes launched eagerly (one library call per step, no graph), for comparison
+    n_eager = max(1, args.steps // 5)
+    elapsed_eager = timed(lambda d: decode(d % len(pool)), n_eager, 5) / n_eager
     verify_replay(trie, widths, pool[0], fin, ids, dev)
     # per-kernel durations: the same decodes again, eagerly, with events on the launch stream
     # around 10 back-to-back launches of each kernel (dispatch latency amortised)
@@ -389,7 +393,7 @@ def one_wave_leg(args, wl, cat, dev):
     beams.enable_timing(0)
     n_merge = n_timed // L * merge_steps(trie, widths, L)    # merge launches among the timed steps
     return {"elapsed": elapsed, "rows_x_steps": rows_x_steps, "rows_per_step": rows_per_step,
-            "graph_decodes": group if args.graph else 0,
+            "graph_decodes": group if args.graph else 0, "eager_ms_per_decode": elapsed_eager * 1e3,
             "tile_us": tile_ms * 1e3 / n_timed, "tile_us_cold": tile_ms_c * 1e3 / n_timed_c,
             "merge_us": merge_ms * 1e3 / n_merge if n_merge else None,
             "pool": len(pool), "sector_bytes": sector_bytes,
@@ -935,6 +939,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": m["elapsed"] * 1e3 / args.steps,
+        "ms_per_step_eager": m["eager_ms_per_decode"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
