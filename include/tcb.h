@@ -210,7 +210,10 @@ tcb_status tcb_beam_step_sampled(tcb_beams *b, const void *d_logits, int64_t ld,
  *             H % 128 == 0, 16-byte aligned; row `slot` is that slot's hidden state
  *   d_weight  device bf16 [L][256][H] contiguous (one [256][H] matrix per level),
  *             16-byte aligned; the trie must have V = 256
- * The logits pass through an fp32 [max_slots][256] part of the workspace; the masked
+ * Where rows have many children the dense head (MFMA, its own launch) writes all 256
+ * logits of each row to an fp32 [max_slots][256] part of the workspace and the step
+ * kernel reads them; where they have about one (tcb_beams_set_read_mode), the step kernel
+ * computes only the children's logits itself and keeps them on chip. The masked
  * log-softmax and selection are those of tcb_beam_step.
  * Errors as tcb_beam_step; TCB_E_ARG for the shape and alignment conditions above. */
 tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_hidden,
@@ -257,11 +260,12 @@ tcb_status tcb_beams_set_validate(tcb_beams *b, int32_t on);
  * gathering applies to the children normaliser with 16-byte aligned rows (otherwise
  * rows are read whole).
  * For tcb_beam_step_lmhead the same modes choose the head: DENSE computes every row's
- * 256 logits (MFMA); GATHER computes only the 16-byte pieces (4 codes) of each row that
- * hold a child, one dot product over H per code, and reads only those pieces; AUTO does
- * so at depths whose rows' children touch at most one of the row's 64 pieces on average
- * (H <= 4096; otherwise dense). The two heads sum in different orders, so their logits
- * agree to fp32 rounding rather than bitwise. Errors: TCB_E_ARG. */
+ * 256 logits (MFMA, its own launch); GATHER computes, inside the step kernel and after
+ * the rows' nodes are known, only the logits of each row's children (one dot product
+ * over H per child), so no logits are written or read; AUTO does so at depths whose
+ * nodes have at most two children on average. A request's first step always uses the
+ * dense head. The two heads sum in different orders, so their logits agree to fp32
+ * rounding rather than bitwise. Errors: TCB_E_ARG. */
 enum { TCB_READ_AUTO = 0, TCB_READ_DENSE = 1, TCB_READ_GATHER = 2 };
 tcb_status tcb_beams_set_read_mode(tcb_beams *b, int32_t mode);
 

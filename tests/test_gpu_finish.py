@@ -291,8 +291,9 @@ def test_deferred_merge_under_exact_ties():
 @pytest.mark.parametrize("mode", ["dense", "gather"])
 def test_deferred_merge_lmhead(mode):
     """lm_head steps back to back (the dense head computes every row the request can have
-    while the merge is pending; the children-only head makes the pending merge launch
-    first) against an export after every step: bitwise equal beams and state."""
+    while the merge is pending; the children-only head runs in the tile kernel after the
+    merge it does first) against an export after every step: bitwise equal beams and
+    state."""
     cat = synth.catalog(60_000, 3, ("zipf",) * 3, [73, 1])
     trie = Trie(cat, device="cuda")
     widths, H = [512, 100, 20], 256

@@ -164,3 +164,31 @@ def test_lmhead_dense_wide_k_deterministic():
         a, b = states[0][k], states[1][k]
         assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                               b.view(np.uint32) if b.dtype == np.float32 else b), k
+
+
+@pytest.mark.parametrize("H", [640, 2048])
+def test_lmhead_in_tile_children_head_fused_route(H):
+    """The automatic head choice on a uniform 4-level catalog: dense head at levels 0-2,
+    and at level 3 (about one child per row) the children's logits computed inside the
+    tile kernel. H = 640: one batch of four 16-byte pieces per lane and a remainder piece;
+    H = 2048: four batches. Checked against the oracle step by step (export after every
+    step), then the same decode with the steps back to back (each merge done in the next
+    step's tile kernel, so level 3's head runs after that merge, in the same kernel) must
+    give bitwise the same finalized beams."""
+    cat = synth.catalog(200_000, 4, ("uniform",) * 4, [58, 1])
+    widths = [512, 512, 300, 9]
+    run, _ = _run_lmhead(cat, widths, H, 58, check_reqs=[0, 2, 3], read_mode="auto")
+    ref = run.beams.finalize(run.ids)
+    L, S = run.L, run.max_slots
+    w_dev = _bf16_dev(np.stack([synth.lmhead_weight(58, lv, 256, H) for lv in range(L)]))
+    hidden = [_bf16_dev(synth.hidden_states(58, t, S, H)) for t in range(L)]
+    beams = Beams(run.trie, S, len(widths), max(widths))
+    beams.set_read_mode("auto")
+    ids, _ = beams.init(np.asarray(widths, dtype=np.int32))
+    for t in range(L):
+        beams.step_lmhead(hidden[t], w_dev)
+    got = beams.finalize(ids)
+    beams.check()
+    for k in ("counts", "sids", "scores", "items"):
+        assert np.array_equal(got[k], ref[k]), k
+

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtcb.so")
 SOURCES = ["kernels.hip", "tile_f32.hip", "tile_bf16.hip", "tile_f32_sampled.hip", "tile_bf16_sampled.hip",
-           "lmhead.hip", "score.hip", "tcb_api.cpp", "score_api.cpp", "trie_builder.cpp"]
+           "tile_head.hip", "lmhead.hip", "score.hip", "tcb_api.cpp", "score_api.cpp", "trie_builder.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -114,6 +114,15 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     return x;
 }
 
+// smallest value over the 16 lanes of a row (in all 16 lanes)
+__device__ __forceinline__ uint32_t row16_min_u(uint32_t v) {
+    v = min(v, dpp_u<kQuadXor1, 0xF>(v));
+    v = min(v, dpp_u<kQuadXor2, 0xF>(v));
+    v = min(v, dpp_u<kHalfMirror, 0xF>(v));
+    v = min(v, dpp_u<kMirror, 0xF>(v));
+    return v;
+}
+
 // Phase trace (diagnostics): thread 0 records the real-time clock (100 MHz) when its
 // workgroup passes mark i; mark 0 records the XCD. A uniform test of a kernel argument when
 // tracing is off.
@@ -432,6 +441,77 @@ __device__ __forceinline__ void load_row_chunks(const void *logits, int64_t ld, 
                     x[8 * i + 2 * w + 1] = __uint_as_float(v[w] & 0xffff0000u);
                 }
             }
+    }
+}
+
+// ---------------------------------------------------------------------- children-only lm_head
+// flashrec 0.1.0, Features > Decoding: the head is evaluated only over the SID range, and
+// the trie is used dense or sparse by depth. Where a row has about one child, the logits
+// of its other codes are never used (they are masked off), so the tile computes only
+//     x[c] = sum_h hidden[slot][h] * W[level][c][h]      for each child code c of the row
+// (bf16 operands widened exactly, fp32 sums). A wave takes its 4 rows' (row, child) pairs
+// one at a time, rows in order and each row's children lowest code first, and all 64 lanes
+// share each pair: lane l sums the products of the rows' 16-byte pieces l, l + 64, ...
+// (8 elements each, in element order), then the 64 lane sums are added in a fixed order
+// (a DPP butterfly within each 16-lane row, then across rows), so a logit does not depend
+// on the launch and every lane holds the same value; the lane owning the code keeps it in
+// x. One pair's operand loads are all in flight at once (4 pieces of each operand per lane
+// at H = 2048). tv: the lane's codes that are children (bit e <-> code code_of(e, j)); g:
+// the lane's row in the wave; slot: the slot of the lane's row.
+__device__ __forceinline__ float dot8_bf16(const u32x4 &a, const u32x4 &b, float acc) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), acc);
+        acc = fmaf(__uint_as_float(a[w] & 0xffff0000u), __uint_as_float(b[w] & 0xffff0000u), acc);
+    }
+    return acc;
+}
+
+constexpr int kHeadBatch = 4;                               // pieces of each operand per lane per load round
+
+template <int DT>
+__device__ __forceinline__ void head_children(const StepHead &hd, int slot, int level, int g, int j, uint32_t tv,
+                                              float (&x)[kElems]) {
+    const int lane = (int)(threadIdx.x & 63u);
+    const uint16_t *wl = hd.weight + (size_t)level * 256 * (size_t)hd.H;
+    const int pieces = hd.H >> 3;                           // 16-byte pieces of a row
+    uint32_t rem = tv;
+#pragma unroll 1
+    for (int gg = 0; gg < 4; ++gg) {
+        const u32x4 *hp = reinterpret_cast<const u32x4 *>(
+            hd.hidden + (size_t)__builtin_amdgcn_readlane(slot, 16 * gg) * (size_t)hd.ld);
+#pragma unroll 1
+        while (true) {
+            const int e0 = rem ? __builtin_ctz(rem) : 0;
+            const uint32_t mine = rem ? (uint32_t)code_of<DT>(e0, j) : 256u;
+            // row gg's next child code (256: none left), the same in every lane
+            const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)row16_min_u(mine), 16 * gg);
+            if (c >= 256u) break;
+            const u32x4 *wp = reinterpret_cast<const u32x4 *>(wl + (size_t)c * (size_t)hd.H);
+            float acc = 0.0f;
+#pragma unroll 1
+            for (int p0 = 0; p0 < pieces; p0 += 64 * kHeadBatch) {
+                u32x4 hv[kHeadBatch], wv[kHeadBatch];
+#pragma unroll
+                for (int i = 0; i < kHeadBatch; ++i) {
+                    const int p = min(p0 + 64 * i + lane, pieces - 1);   // past the row: read, not summed
+                    hv[i] = __builtin_nontemporal_load(hp + p);
+                    wv[i] = wp[p];
+                }
+#pragma unroll
+                for (int i = 0; i < kHeadBatch; ++i)
+                    if (p0 + 64 * i + lane < pieces) acc = dot8_bf16(hv[i], wv[i], acc);
+            }
+            acc = row16_sum(acc);
+            acc += __shfl_xor(acc, 16, 64);
+            acc += __shfl_xor(acc, 32, 64);
+            if (g == gg && mine == c) {
+#pragma unroll
+                for (int e = 0; e < kElems; ++e)
+                    if (e == e0) x[e] = acc;
+                rem &= rem - 1u;
+            }
+        }
     }
 }
 
@@ -1283,12 +1363,15 @@ __device__ __forceinline__ void score_row(const StepReqs &R, int q, int level, i
 // (from the records in memory) is still to do.
 // With FUSE, a request whose previous step left its merge pending does that merge first
 // (M and Z: its staging and this tile's rows).
-template <int DT, int NORM, bool VEC, bool SAMPLE, bool MERGE, bool FUSE>
+// HEAD: an lm_head step; requests with the sparse-head flag get their rows' children's
+// logits from head_children (after the child sets are known) instead of from `logits`.
+template <int DT, int NORM, bool VEC, bool SAMPLE, bool MERGE, bool FUSE, bool HEAD = false>
 __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, int rp, const StepReqs &R,
                                           const void *__restrict__ logits, int64_t ld, int ql, int tile,
                                           TileSmem &A, SelSmem &sel, MergeSmem *M, FuseRows *Z) {
     constexpr int CH = Lay<DT>::CH, CW = Lay<DT>::CW, SPAN = 256 / CH;
     static_assert(CH * CW == kElems && (SPAN / CW) * 8 <= 256, "row layout");
+    static_assert(!HEAD || (VEC && !SAMPLE && NORM == TCB_NORM_CHILDREN), "in-tile head: children, 16-byte rows");
 
     const int tid = threadIdx.x;
     const int MT = W.MT;
@@ -1327,20 +1410,24 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
     float x[kElems];
 #pragma unroll
     for (int e = 0; e < kElems; ++e) x[e] = 0.0f;
+    // lm_head rows whose children's logits this tile computes (none are read)
+    const bool head_rows = HEAD && ra.sparse_head();
     // at depths with few children per row the logits wait for the trie and only the
     // 16-byte pieces holding a child are read (the rest is masked off either way)
-    const bool gather = VEC && ra.gather();
+    const bool gather = VEC && ra.gather() && !head_rows;
     // the row's logits, unless they wait for the trie (gather): issued unconditionally with
     // 16-byte pieces (a row past the request's bound reads its last possible row, dropped)
     const int slot_c = base + min(r, ra.rmax() - 1);
     RawRow<DT> raw;
     auto issue_logits = [&]() {
         if constexpr (VEC) {
-            // the empty asm pins the loads here: their address would otherwise let the
-            // compiler hoist them to the kernel's start, ahead of the merge's loads
-            int sl = slot_c;
-            asm volatile("" : "+v"(sl));
-            load_row_raw<DT>(logits, ld, sl, j, raw);
+            if (!head_rows) {
+                // the empty asm pins the loads here: their address would otherwise let the
+                // compiler hoist them to the kernel's start, ahead of the merge's loads
+                int sl = slot_c;
+                asm volatile("" : "+v"(sl));
+                load_row_raw<DT>(logits, ld, sl, j, raw);
+            }
         }
     };
     // a step that first does the previous merge issues them behind the merge's loads, with
@@ -1478,7 +1565,15 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
         }
     }
     if constexpr (VEC) {
-        if (!gather) widen_row<DT>(raw, x);           // the logits issued at the start
+        if (!gather && !head_rows) widen_row<DT>(raw, x);   // the logits issued at the start
+    }
+    if constexpr (HEAD) {
+        if (head_rows) {
+            uint32_t kids = 0u;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) kids |= bits[i] << (i * CW);
+            head_children<DT>(R.hd, slot_c, level, g, j, kids, x);
+        }
     }
     if (gather && live) {
         uint32_t chunks = 0u;
@@ -1739,7 +1834,7 @@ __device__ __forceinline__ bool tile_work(const TrieDev &T, const WaveDev &W, in
 // records it has just written: no second kernel. Otherwise the tiles of a request are
 // dealt to one XCD (workgroups b with the same b mod 8 run on one XCD) and k_merge follows.
 // FUSE: requests whose previous merge is pending do it first, in every one of their tiles.
-template <int DT, int NORM, bool VEC, bool SAMPLE, bool MERGE, bool FUSE>
+template <int DT, int NORM, bool VEC, bool SAMPLE, bool MERGE, bool FUSE, bool HEAD = false>
 __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp, StepReqs R,
                                                    const void *__restrict__ logits, int64_t ld) {
     __shared__ TileSmem A;
@@ -1748,7 +1843,8 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
         __shared__ MergeSmem M;
         const int ql = (int)blockIdx.x;
         if (ql >= R.n) return;
-        if (tile_work<DT, NORM, VEC, SAMPLE, true, false>(T, W, rp, R, logits, ld, ql, 0, A, sel, &M, nullptr)) return;
+        if (tile_work<DT, NORM, VEC, SAMPLE, true, false, HEAD>(T, W, rp, R, logits, ld, ql, 0, A, sel, &M, nullptr))
+            return;
         const ReqArg ra = R.r[ql];
         if (!ra.step()) return;                        // carried over by tile_work
         __syncthreads();                               // the tile's records are visible to the workgroup
@@ -1763,9 +1859,10 @@ __global__ __launch_bounds__(kThreads) void k_tile(TrieDev T, WaveDev W, int rp,
         if constexpr (FUSE) {
             __shared__ MergeSmem M;
             __shared__ FuseRows Z;
-            tile_work<DT, NORM, VEC, SAMPLE, false, true>(T, W, rp, R, logits, ld, ql, tile, A, sel, &M, &Z);
+            tile_work<DT, NORM, VEC, SAMPLE, false, true, HEAD>(T, W, rp, R, logits, ld, ql, tile, A, sel, &M, &Z);
         } else {
-            tile_work<DT, NORM, VEC, SAMPLE, false, false>(T, W, rp, R, logits, ld, ql, tile, A, sel, nullptr, nullptr);
+            tile_work<DT, NORM, VEC, SAMPLE, false, false, HEAD>(T, W, rp, R, logits, ld, ql, tile, A, sel, nullptr,
+                                                                 nullptr);
         }
     }
 }
@@ -1957,7 +2054,7 @@ __global__ __launch_bounds__(256) void k_first(TrieDev T, WaveDev W, int rp, Ste
 }
 
 // ---------------------------------------------------------------------- tile launches
-template <int DT, int NORM, bool VEC, bool SAMPLE>
+template <int DT, int NORM, bool VEC, bool SAMPLE, bool HEAD = false>
 void launch_tile_t(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
                           int64_t ld, int mode, hipStream_t s) {
     const int groups = (R.n + 7) / 8;
@@ -1966,13 +2063,13 @@ void launch_tile_t(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R
         hipLaunchKernelGGL((k_first<DT, NORM, VEC, SAMPLE>), dim3(8 * ((R.n + nx - 1) / nx)), dim3(256), 0, s, t, w,
                            rp, R, logits, ld);
     } else if (mode == kTileMerge) {
-        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, true, false>), dim3(R.n), dim3(kThreads), 0, s, t, w, rp,
+        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, true, false, HEAD>), dim3(R.n), dim3(kThreads), 0, s, t, w, rp,
                            R, logits, ld);
     } else if (mode == kTileFuse) {
-        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, false, true>), dim3(8 * groups * w.MT), dim3(kThreads), 0,
+        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, false, true, HEAD>), dim3(8 * groups * w.MT), dim3(kThreads), 0,
                            s, t, w, rp, R, logits, ld);
     } else {
-        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, false, false>), dim3(8 * groups * w.MT), dim3(kThreads), 0,
+        hipLaunchKernelGGL((k_tile<DT, NORM, VEC, SAMPLE, false, false, HEAD>), dim3(8 * groups * w.MT), dim3(kThreads), 0,
                            s, t, w, rp, R, logits, ld);
     }
 }

@@ -162,11 +162,22 @@ bool tile_merges(const StepReqs &R) {
 }
 
 hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                       int64_t ld, int dtype, bool sampled, hipStream_t s, bool fuse) {
+                       int64_t ld, int dtype, bool sampled, hipStream_t s, bool fuse, bool head) {
     if (R.n <= 0) return hipSuccess;
     // 16-byte row pieces: ld a multiple of 4 (fp32) or 8 (bf16) elements, 16-byte base
     const bool vec = t.V == 256 && (ld % (dtype == TCB_F32 ? 4 : 8)) == 0 && ((uintptr_t)logits % 16) == 0;
     const int merge = tile_mode(R, fuse);
+    bool head_rows = false;                        // some request's children's logits come from the tile
+    if (head)
+        for (int i = 0; i < R.n; ++i)
+            if (R.r[i].step() && R.r[i].sparse_head()) head_rows = true;
+    if (head_rows) {
+        // the host sets the flag only past a request's first step, on fp32 16-byte rows,
+        // with children normalisation and without sampling
+        if (merge == kTileFirst || dtype != TCB_F32 || sampled || !vec || R.hd.hidden == nullptr)
+            return hipErrorInvalidValue;
+        return launch_tile_f32_head(t, w, rp, R, logits, ld, vec, merge, s);
+    }
     if (dtype == TCB_F32) {
         return sampled ? launch_tile_f32_sampled(t, w, rp, R, logits, ld, vec, merge, s)
                        : launch_tile_f32(t, w, rp, R, logits, ld, vec, merge, s);

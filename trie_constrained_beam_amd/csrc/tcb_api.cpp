@@ -320,11 +320,11 @@ tcb_status tcb_beams_create(const tcb_trie *t, int32_t max_slots, int32_t max_re
             const double sectors = k == 0 ? 16.0 : 8.0;
             if (1.0 - std::pow(1.0 - 1.0 / sectors, fan) < 0.5) b->gather_levels[k] |= 1u << d;
         }
-        // children-only lm_head where a row's children are expected to touch at most one of
-        // its 64 pieces (4 of 256 codes): its dot products run on the vector ALUs and re-read
-        // the weights per row, so against the LDS-staged matrix-core head it pays only at
-        // fanouts near 1 (measured: at about 2 pieces per row it is already slower)
-        if (64.0 * (1.0 - std::pow(1.0 - 1.0 / 64.0, fan)) <= 1.0) b->sparse_head_levels |= 1u << d;
+        // children-only lm_head (in the tile kernel) where rows have at most two children on
+        // average: each child costs the tile one dot product over H on the vector ALUs and a
+        // weight row read from L2, so it pays only where the dense head's 256 codes per row
+        // are almost all masked off
+        if (fan <= 2.0) b->sparse_head_levels |= 1u << d;
     }
     const uint8_t *img = (const uint8_t *)t->d_image;
     b->tdev.child_begin = (const uint32_t *)(img + t->o_child_begin);
@@ -472,13 +472,13 @@ static void step_args(const tcb_beams *b, std::vector<tcb::StepReqs> &out, int d
             // before the merge, as their pieces would wait for the merged rows' nodes
             const bool pend = step && rq.pending;
             const bool gather = !open && b->w.norm == TCB_NORM_CHILDREN && step && dt_index < 2 && by_level && !pend;
-            // an lm_head step computes only the children's pieces where rows have few children;
-            // its tile kernel then reads only those pieces
-            const bool sparse = head && !open && b->w.norm == TCB_NORM_CHILDREN && step &&
+            // an lm_head step past the first computes only the children's logits where rows
+            // have few children, in the tile kernel (no head launch for the request)
+            const bool sparse = head && !open && b->w.norm == TCB_NORM_CHILDREN && step && level > 0 &&
                                 (b->read_mode == TCB_READ_GATHER ||
                                  (b->read_mode == TCB_READ_AUTO && (b->sparse_head_levels >> level & 1u)));
             const bool rinfo = step && rq.rinfo;
-            R.r[i].base_flags = rq.base | (gather || sparse ? 1 << 24 : 0) | (sparse ? 1 << 25 : 0) | (pend ? 1 << 26 : 0) |
+            R.r[i].base_flags = rq.base | (gather ? 1 << 24 : 0) | (sparse ? 1 << 25 : 0) | (pend ? 1 << 26 : 0) |
                                 (rinfo ? 1 << 27 : 0);
             R.r[i].bits = width | rmax << 13 | level << 26 | pre << 29 | (step ? 1u : 0u) << 30 | (level & 1u) << 31;
         }
@@ -616,35 +616,27 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
     tcb_status st = step_common(b);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    // the children-only head reads the rows' nodes: a pending merge is then launched first
-    bool any_sparse = false;
-    if (H <= 4096 && b->w.norm == TCB_NORM_CHILDREN)
-        for (const auto &q : b->reqs)
-            if (q.used && q.level < b->L &&
-                (b->read_mode == TCB_READ_GATHER ||
-                 (b->read_mode == TCB_READ_AUTO && (b->sparse_head_levels >> q.level & 1u))))
-                any_sparse = true;
+    // the dense head (its own launch) writes the logits of the requests without the
+    // sparse-head flag; the tile kernel computes the children's logits of the others itself,
+    // after any pending merge it does first, so no merge has to be launched ahead of the step
+    const tcb::StepHead hd{static_cast<const uint16_t *>(d_hidden), static_cast<const uint16_t *>(d_weight), ld_hidden,
+                           H, 0};
     return run_step(
         b, s,
         [&](const tcb::StepReqs &R) {
             bool dense = false;
-            int sparse_rows = 0;
             for (int i = 0; i < R.n; ++i)
-                if (R.r[i].step()) {
-                    if (R.r[i].sparse_head()) sparse_rows = std::max(sparse_rows, R.r[i].rmax());
-                    else dense = true;
-                }
-            hipError_t e = hipSuccess;
-            if (dense) e = tcb::launch_lmhead(b->tdev, b->w, b->rp, R, d_hidden, ld_hidden, H, d_weight, b->w.lmx, s);
-            if (e == hipSuccess && sparse_rows > 0)
-                e = tcb::launch_lmhead_sparse(b->tdev, b->w, b->rp, R, d_hidden, ld_hidden, H, d_weight, b->w.lmx,
-                                              sparse_rows, s);
-            return e;
+                if (R.r[i].step() && !R.r[i].sparse_head()) dense = true;
+            return dense ? tcb::launch_lmhead(b->tdev, b->w, b->rp, R, d_hidden, ld_hidden, H, d_weight, b->w.lmx, s)
+                         : hipSuccess;
         },
         [&](const tcb::WaveDev &w, const tcb::StepReqs &R, bool fuse) {
-            return tcb::launch_tile(b->tdev, w, b->rp, R, b->w.lmx, 256, TCB_F32, false, s, fuse);
+            static thread_local tcb::StepReqs Rh;
+            Rh = R;
+            Rh.hd = hd;
+            return tcb::launch_tile(b->tdev, w, b->rp, Rh, b->w.lmx, 256, TCB_F32, false, s, fuse, true);
         },
-        2, 0.0, 0, H <= 4096, !any_sparse);
+        2, 0.0, 0, true, true);
 }
 
 tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, float *d_phi, int32_t *d_parent_slot,

@@ -145,6 +145,15 @@ struct StepFin {
     int64_t *items;                // [R][Bmax]
     int32_t *counts;               // [R]
 };
+// The SID-range lm_head's operands, for requests whose argument carries the sparse-head flag:
+// the tile kernel computes their rows' logits itself, only for the rows' children.
+struct StepHead {
+    const uint16_t *hidden;        // bf16 [slots][ld], row = slot
+    const uint16_t *weight;        // bf16 [L][256][H]
+    int64_t ld;                    // elements between hidden rows (ld % 8 == 0)
+    int32_t H;                     // hidden size (H % 128 == 0)
+    int32_t pad;
+};
 struct StepReqs {
     int32_t n;                     // request ids q0 .. q0 + n - 1
     int32_t q0;
@@ -153,6 +162,7 @@ struct StepReqs {
     double inv_temp_d;             //                the same in float64
     uint64_t seed;                 //                noise seed
     StepFin fin;
+    StepHead hd;                   // lm_head steps: the children-only head's operands
     ReqArg r[kArgReqs];
 };
 static_assert(sizeof(StepReqs) <= 4096 - 256, "kernel arguments stay under 4 KiB");
@@ -181,6 +191,9 @@ TCB_TILE_LAUNCHER(launch_tile_f32);
 TCB_TILE_LAUNCHER(launch_tile_bf16);
 TCB_TILE_LAUNCHER(launch_tile_f32_sampled);
 TCB_TILE_LAUNCHER(launch_tile_bf16_sampled);
+// fp32 rows from the dense lm_head, and in-tile children-only logits for the requests with
+// the sparse-head flag (children normalisation, 16-byte pieces, no sampling)
+TCB_TILE_LAUNCHER(launch_tile_f32_head);
 
 // The kernel launch_tile uses for one launch of R: kTileFirst when every stepped request
 // is at its first step (one row each; merged inside the kernel), else kTileFuse when
@@ -207,12 +220,10 @@ hipError_t launch_init(const WaveDev &w, const InitBatch &b, hipStream_t s);
 // lm_head, the lm_head kernel first writes the logits to WaveDev::lmx.
 // fuse: some request of R has pending() set; the tile kernel then first does that request's
 // previous merge (redundantly in each of its tiles, each keeping its own 64 rows)
+// head: an lm_head step (R.hd set); requests with the sparse-head flag then get their
+// children's logits computed in the tile kernel, never at their first step
 hipError_t launch_tile(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *logits,
-                       int64_t ld, int dtype, bool sampled, hipStream_t s, bool fuse = false);
-// lm_head over only the 16-byte pieces (4 codes) of each row that hold a child, for the
-// requests whose argument carries the sparse-head flag; max_rows bounds their live rows.
-hipError_t launch_lmhead_sparse(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
-                                int64_t ld, int H, const void *weight, float *out, int max_rows, hipStream_t s);
+                       int64_t ld, int dtype, bool sampled, hipStream_t s, bool fuse = false, bool head = false);
 hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepReqs &R, const void *hidden,
                          int64_t ld, int H, const void *weight, float *out, hipStream_t s);
 // true when every stepped request of R has at most kTileRows rows: a tile kernel launched
