@@ -66,17 +66,18 @@ def test_lmhead_step_parity_wide_k():
 
 @pytest.mark.parametrize("H", [384, 1024])
 def test_lmhead_narrow_beams_16_row_tiles(H):
-    """Every request at most 16 beams wide: every level's head runs on 16-row tiles (the
-    first step's tiling), with the generic K loop (H = 384) and the two-step loads (1024)."""
+    """Every request at most 16 beams wide: every level after the first runs the head on
+    16-row tiles, with the generic K loop (H = 384) and the two-step loads (1024); the first
+    step runs the one-row kernel."""
     cat = synth.catalog(20_000, 4, ("uniform",) * 4, [55, 1])
     _run_lmhead(cat, [16, 5, 9, 1], H, 55)
 
 
 def test_lmhead_generic_k_every_tile_height():
     """H = 384 (the generic K loop, one K-step per load) with 8 requests of width 512 and the
-    dense head at every level: on the 256-CU MI355X the first step runs 16-row tiles, level 1
-    (2,048 rows) 32-row tiles and levels 2-3 64-row tiles; three requests checked against the
-    oracle at every step."""
+    dense head at every level: on the 256-CU MI355X the first step runs the one-row kernel
+    (48 pieces per row: a partial round of lanes), level 1 (2,048 rows) 32-row tiles and
+    levels 2-3 64-row tiles; three requests checked against the oracle at every step."""
     cat = synth.catalog(300_000, 4, ("uniform",) * 4, [56, 1])
     _run_lmhead(cat, [512] * 8, 384, 56, check_reqs=[0, 3, 7], read_mode="dense")
 

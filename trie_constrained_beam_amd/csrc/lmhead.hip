@@ -194,6 +194,69 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     }
 }
 
+// First steps: each request has one row (the root, in its first slot), so its head is a
+// matrix-vector product, 256 dot products over H. The 64-row MFMA tiles would stream the whole
+// weight matrix through a few workgroups for one live row; here a request's 256 codes are
+// spread over 32 workgroups of 4 waves, 2 codes per wave, so the matrix streams once through
+// every CU. All 64 lanes of a wave share a code: lane l sums the products of the 16-byte
+// pieces l, l + 64, ... of the hidden row and the weight row (8 elements each, in element
+// order), then the 64 lane sums are added by a fixed butterfly, so the logits are
+// deterministic (they differ from the MFMA head's only by the order of the fp32 sums).
+constexpr int kRootCodesPerWg = 8;
+constexpr int kRootBatch = 4;                             // 16-byte pieces of each operand per lane per round
+
+__device__ __forceinline__ float root_dot8(const u32x4 &a, const u32x4 &b, float acc) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), acc);
+        acc = fmaf(__uint_as_float(a[w] & 0xffff0000u), __uint_as_float(b[w] & 0xffff0000u), acc);
+    }
+    return acc;
+}
+
+__global__ __launch_bounds__(256) void k_lmhead_root(StepReqs R, const uint16_t *__restrict__ hidden, int64_t ld,
+                                                     int H, const uint16_t *__restrict__ weight,
+                                                     float *__restrict__ out) {
+    constexpr int G = 256 / kRootCodesPerWg;                  // workgroups per request
+    const int ql = (int)blockIdx.x / G, cg = (int)blockIdx.x - ql * G;
+    if (ql >= R.n) return;
+    const ReqArg ra = R.r[ql];
+    if (!ra.step() || ra.sparse_head() || ra.level() != 0) return;
+    const int lane = (int)(threadIdx.x & 63u), wave = (int)(threadIdx.x >> 6);
+    const int slot = ra.base();
+    const int pieces = H >> 3;                                // 16-byte pieces of a row
+    const int c0 = cg * kRootCodesPerWg + 2 * wave;           // this wave's codes c0, c0 + 1 (level 0)
+    const u32x4 *hp = reinterpret_cast<const u32x4 *>(hidden + (size_t)slot * (size_t)ld);
+    const u32x4 *w0 = reinterpret_cast<const u32x4 *>(weight + (size_t)c0 * (size_t)H);
+    const u32x4 *w1 = w0 + pieces;
+    float a0 = 0.0f, a1 = 0.0f;
+    for (int p0 = 0; p0 < pieces; p0 += 64 * kRootBatch) {
+        u32x4 hv[kRootBatch], x0[kRootBatch], x1[kRootBatch];
+#pragma unroll
+        for (int i = 0; i < kRootBatch; ++i) {
+            const int p = min(p0 + 64 * i + lane, pieces - 1);  // past the row: read, not summed
+            hv[i] = __builtin_nontemporal_load(hp + p);
+            x0[i] = w0[p];
+            x1[i] = w1[p];
+        }
+#pragma unroll
+        for (int i = 0; i < kRootBatch; ++i)
+            if (p0 + 64 * i + lane < pieces) {
+                a0 = root_dot8(hv[i], x0[i], a0);
+                a1 = root_dot8(hv[i], x1[i], a1);
+            }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        a0 += __shfl_xor(a0, o, 64);
+        a1 += __shfl_xor(a1, o, 64);
+    }
+    if (lane == 0) {
+        out[(size_t)slot * 256 + c0] = a0;
+        out[(size_t)slot * 256 + c0 + 1] = a1;
+    }
+}
+
 // compute units of the current device (queried once per device)
 int cu_count() {
     static int cache[64] = {};
@@ -231,10 +294,17 @@ hipError_t launch_lmhead(const TrieDev &t, const WaveDev &w, int rp, const StepR
     for (int i = 0; i < R.n; ++i)
         if (R.r[i].step() && !R.r[i].sparse_head()) rmax = std::max(rmax, R.r[i].rmax());
     if (rmax <= 0) return hipSuccess;
+    const uint16_t *h = static_cast<const uint16_t *>(hidden), *wt = static_cast<const uint16_t *>(weight);
+    bool first = true;                                        // every dense-head request at its first step
+    for (int i = 0; i < R.n; ++i)
+        if (R.r[i].step() && !R.r[i].sparse_head() && R.r[i].level() != 0) first = false;
+    if (first) {
+        hipLaunchKernelGGL(k_lmhead_root, dim3(R.n * (256 / kRootCodesPerWg)), dim3(256), 0, s, R, h, ld, H, wt, out);
+        return hipGetLastError();
+    }
     // the tallest tiles whose 4 code blocks still give every CU a workgroup; else 16 rows
     const int cus = cu_count();
     auto tiles = [&](int rows) { return (rmax + rows - 1) / rows; };
-    const uint16_t *h = static_cast<const uint16_t *>(hidden), *wt = static_cast<const uint16_t *>(weight);
     if (4 * R.n * tiles(64) >= cus) launch_lmhead_rb<4>(t, w, rp, R, h, ld, H, wt, out, tiles(64), s);
     else if (4 * R.n * tiles(32) >= cus) launch_lmhead_rb<2>(t, w, rp, R, h, ld, H, wt, out, tiles(32), s);
     else launch_lmhead_rb<1>(t, w, rp, R, h, ld, H, wt, out, tiles(16), s);
