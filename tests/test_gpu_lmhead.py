@@ -193,3 +193,61 @@ def test_lmhead_in_tile_children_head_fused_route(H):
     for k in ("counts", "sids", "scores", "items"):
         assert np.array_equal(got[k], ref[k]), k
 
+
+
+def test_lmhead_mixed_levels_in_one_launch():
+    """Requests admitted at different steps, so one lm_head launch holds requests at
+    different levels: in the same tile kernel, rows at a dense depth read the dense head's
+    logits while rows at the sparse last level get their children's logits computed in the
+    tile (automatic choice), and a request admitted mid-decode takes its first step beside
+    deeper ones (the MFMA head then computes its root row). First with an export around every
+    step (so each merge runs as its own kernel), every request checked against the oracle at
+    its own level; then the same schedule with the steps back to back (each merge done in the
+    next step's tile kernel, before the in-tile head), whose finalized beams must be bitwise
+    those of the checked run."""
+    cat = synth.catalog(200_000, 4, ("uniform",) * 4, [59, 1])
+    H, seed = 640, 59
+    trie = Trie(cat, device="cuda")
+    otrie = oracle.OracleTrie(cat.astype(np.int64))
+    L, S = 4, 2048
+    weights = np.stack([synth.lmhead_weight(seed, lv, 256, H) for lv in range(L)])
+    w_dev = _bf16_dev(weights)
+    admit = {0: [512, 100], 1: [256, 7], 2: [300]}           # step -> widths admitted before it
+    hidden = [synth.hidden_states(seed, t, S, H) for t in range(L + 2)]
+
+    def run(check):
+        beams = Beams(trie, S, 8, 512)
+        beams.set_read_mode("auto")
+        live = []                                           # (req id, base, width, level)
+        for t in range(L + 2):
+            if t in admit:
+                ids, bases = beams.init(np.asarray(admit[t], dtype=np.int32))
+                live += [[int(r), int(b), w, 0] for r, b, w in zip(ids, bases, admit[t])]
+            stepped = [q for q in live if q[3] < L]
+            if not stepped:
+                break
+            pre = {k: v.cpu().numpy() for k, v in beams.export().items()} if check else None
+            beams.step_lmhead(_bf16_dev(hidden[t]), w_dev)
+            if check:
+                post = {k: v.cpu().numpy() for k, v in beams.export().items()}
+                for rid, base, w, lv in stepped:
+                    assert int(pre["level"][rid]) == lv
+                    rows = int(pre["rows"][rid])
+                    pref = gh.walk_prefixes(pre["hist"], base, rows, lv)
+                    x64 = oracle.lmhead_logits(hidden[t][base:base + rows], weights[lv])
+                    ref = oracle.expand_request(otrie, lv, pref, pre["score"][base:base + rows].astype(np.float64),
+                                                x64, w)
+                    k = int(post["rows"][rid])
+                    h = post["hist"][lv, base:base + k].astype(np.int64)
+                    gh.compare_step(ref, h >> 8, h & 255, post["node"][base:base + k], post["score"][base:base + k],
+                                    ctx=f"request {rid} level {lv} step {t}")
+            for q in stepped:
+                q[3] += 1
+        res = beams.finalize(np.asarray([q[0] for q in live], dtype=np.int32))
+        beams.check()
+        return res
+
+    checked = run(True)
+    fused = run(False)
+    for k in ("counts", "sids", "scores", "items"):
+        assert np.array_equal(fused[k], checked[k]), k
