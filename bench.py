@@ -240,8 +240,11 @@ def child_sector_bytes(trie, nodes_by_step, dsize):
 
 
 # ----------------------------------------------------------------------------- GPU legs
-def make_pool(tensors_fn, per_decode_bytes, pool_gib):
+def make_pool(tensors_fn, per_decode_bytes, pool_gib, multiple=1):
+    """Copies of one decode's inputs filling at least ``pool_gib`` GiB, their count a multiple of
+    ``multiple`` (the decodes per captured graph), so that graphs of that many decodes divide it."""
     n = max(1, math.ceil(pool_gib * 2 ** 30 / per_decode_bytes))
+    n = -(-n // max(1, multiple)) * max(1, multiple)
     first = tensors_fn()
     return [first] + [[x.clone() for x in first] for _ in range(n - 1)]
 
@@ -343,7 +346,7 @@ def one_wave_leg(args, wl, cat, dev):
             return [torch.from_numpy(h.view(np.int16)).to(dev).view(torch.bfloat16) for h in host]
         return [torch.from_numpy(h).to(dev) for h in host]
     per_decode = sum(h.nbytes for h in host)
-    pool = make_pool(upload, per_decode, args.pool_gib)
+    pool = make_pool(upload, per_decode, args.pool_gib, args.graph_decodes)
     fin = beams.set_finish_outputs(True)   # the last step writes each request's beams (row = id)
     log(f"[bench] pool {len(pool)} x {per_decode / 2**20:.1f} MiB of logits")
     rows_per_step, nodes_by_step = [], []
@@ -652,7 +655,7 @@ def lmhead_leg(args, dev, read_mode="dense"):
     host = [synth.hidden_states(wl.seed, t, S, H) for t in range(L)]
     per_decode = sum(h.nbytes for h in host)
     pool = make_pool(lambda: [torch.from_numpy(h.view(np.int16)).to(dev).view(torch.bfloat16) for h in host],
-                     per_decode, args.pool_gib)
+                     per_decode, args.pool_gib, args.graph_decodes)
     beams.set_finish_outputs(True)       # the last step writes each request's beams (row = id)
     ids, _ = beams.init(widths)
     rows_per_step = []
