@@ -381,6 +381,29 @@ def one_wave_leg(args, wl, cat, dev):
     n_eager = max(1, args.steps // 5)
     elapsed_eager = timed(lambda d: decode(d % len(pool)), n_eager, 5) / n_eager
     verify_replay(trie, widths, pool[0], fin, ids, dev)
+    # the same decodes with the state brought up to date after every step but the last (each
+    # merge then runs as its own kernel, as for a caller whose next logits depend on the
+    # survivors), replayed from graphs of the same size; the outputs are verified again
+    def decode_unfused(c):
+        rid, _ = beams.init(widths)
+        for t in range(L):
+            beams.step(pool[c][t])
+            if t + 1 < L:
+                beams.flush()
+    if max(widths) > 64:                     # beams of at most 64 rows merge in their tile kernel
+        graphs_u = capture_groups(decode_unfused, len(pool), group) if args.graph else None
+        n_unfused = max(group, args.steps // 5 // group * group)
+
+        def run_u(d):
+            if graphs_u is not None:
+                graphs_u[d % len(graphs_u)].replay()
+            else:
+                decode_unfused(d % len(pool))
+        elapsed_unfused = timed(run_u, n_unfused // group, 2) / n_unfused
+        verify_replay(trie, widths, pool[0], fin, ids, dev)
+        del graphs_u
+    else:
+        elapsed_unfused = elapsed / args.steps
     # per-kernel durations: the same decodes again, eagerly, with events on the launch stream
     # around 10 back-to-back launches of each kernel (dispatch latency amortised)
     n_ev = min(args.steps, 100)
@@ -397,6 +420,7 @@ def one_wave_leg(args, wl, cat, dev):
     n_merge = n_timed // L * merge_steps(trie, widths, L)    # merge launches among the timed steps
     return {"elapsed": elapsed, "rows_x_steps": rows_x_steps, "rows_per_step": rows_per_step,
             "graph_decodes": group if args.graph else 0, "eager_ms_per_decode": elapsed_eager * 1e3,
+            "unfused_ms_per_decode": elapsed_unfused * 1e3,
             "tile_us": tile_ms * 1e3 / n_timed, "tile_us_cold": tile_ms_c * 1e3 / n_timed_c,
             "merge_us": merge_ms * 1e3 / n_merge if n_merge else None,
             "pool": len(pool), "sector_bytes": sector_bytes,
@@ -820,6 +844,7 @@ def leg_record(wl, m, steps, cat, cpu):
     value, unit_bytes, bpl, achieved = leg_summary(m, steps)
     rec = {"workload": wl.name, "value": value, "unit": "beam-rows x steps/s", "steps": steps,
            "ms_per_step": m["elapsed"] * 1e3 / steps, "requests": m["R"], "beam_width": m["B"], "L": m["L"],
+           "ms_per_step_unfused": m.get("unfused_ms_per_decode"),
            "catalog": int(cat.shape[0]), "rows_per_step": m["rows_per_step"], "rows_x_steps_per_decode":
            m["rows_x_steps"], "input_pool_copies": m["pool"], "decodes_per_graph": m.get("graph_decodes"),
            "roofline": {"bound": "hbm", "kernel": "k_tile", "achieved": achieved, "peak": HBM_PEAK_GBPS,
@@ -943,6 +968,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": m["elapsed"] * 1e3 / args.steps,
         "ms_per_step_eager": m["eager_ms_per_decode"],
+        "ms_per_step_unfused": m["unfused_ms_per_decode"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -226,7 +226,10 @@ tcb_status tcb_beam_step_lmhead(tcb_beams *b, const void *d_hidden, int64_t ld_h
  *   d_parent_slot         [max_slots]  slot of each row's parent at the last step
  *   d_hist                [L][max_slots] back-pointer of level t: (r << 8) | c
  *   d_rows, d_level       [max_requests] live rows and levels per request id
- * Rows beyond a request's live count hold stale values. Asynchronous. */
+ * Rows beyond a request's live count hold stale values. Asynchronous. With every
+ * buffer NULL nothing is copied: the call only launches a merge the last step left to
+ * the next step, so that the state is current (a caller whose next logits depend on
+ * this step's survivors reads them between steps, and the merge then runs on its own). */
 tcb_status tcb_beam_export(tcb_beams *b, int32_t *d_node, float *d_score, float *d_phi,
                            int32_t *d_parent_slot, uint32_t *d_hist, int32_t *d_rows,
                            int32_t *d_level, void *stream);

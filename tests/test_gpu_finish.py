@@ -366,3 +366,29 @@ def test_deferred_merge_with_second_launch_chunk():
     _same(a1, b1)
     _same(a2, b2)
     assert int(a2["counts"][0]) == w
+
+
+def test_flush_between_steps_matches_export():
+    """flush() (an export with every buffer NULL) after each step runs the step's merge on its
+    own, copying nothing: the beams equal those of a decode that exports after every step."""
+    cat = synth.catalog(100_000, 4, ("zipf",) * 4, [74, 1])
+    trie = Trie(cat, device="cuda")
+    widths = [512, 130, 64]
+    fn = _rowkeyed(74)
+    res = []
+    for mode in ("flush", "export"):
+        S = sum(widths)
+        beams = Beams(trie, S, len(widths), max(widths))
+        ids, bases = beams.init(np.asarray(widths, dtype=np.int32))
+        for t in range(trie.L):
+            host = np.zeros((S, 256), dtype=np.float32)
+            for i, (w, b) in enumerate(zip(widths, bases)):
+                host[b:b + w] = fn(t, i, w)
+            beams.step(torch.from_numpy(host).cuda())
+            if mode == "flush":
+                beams.flush()
+            else:
+                beams.export()
+        res.append(beams.finalize(ids))
+        beams.check()
+    _same(res[0], res[1])

@@ -176,6 +176,11 @@ class Beams:
                                     _ptr(out["rows"]), _ptr(out["level"]), _stream()))
         return out
 
+    def flush(self):
+        """Bring the wave state up to date without copying it: launches a merge the last step
+        left to the next step's tile kernel (tcb_beam_export with every buffer NULL)."""
+        check(lib().tcb_beam_export(self._h, None, None, None, None, None, None, None, _stream()))
+
     def set_read_mode(self, mode: str = "auto"):
         """'auto', 'dense' or 'gather': how rows' logits are read (results identical)."""
         m = {"auto": L.TCB_READ_AUTO, "dense": L.TCB_READ_DENSE, "gather": L.TCB_READ_GATHER}[mode]
