@@ -289,10 +289,12 @@ def timed(run, steps, warmup):
     return time.perf_counter() - t0
 
 
-def verify_replay(trie, widths, xs, fin, ids, dev):
+def verify_replay(trie, widths, xs, fin, ids, dev, step=None, read_mode="auto"):
     """The last timed decode's outputs (every pool copy holds the same inputs) against a
     decode of the same inputs with an export after every step, which runs each step's merge
-    in the merge kernel and finalizes separately: bitwise equal, or the bench fails."""
+    in the merge kernel and finalizes separately: bitwise equal, or the bench fails.
+    step(beams, x): one step on input x (default: beams.step(x)); read_mode: the head or
+    read mode of the timed decode."""
     import numpy as np
     import torch
     from trie_constrained_beam_amd import Beams
@@ -300,9 +302,13 @@ def verify_replay(trie, widths, xs, fin, ids, dev):
     idx = np.asarray(ids)
     got = {k: v.cpu().numpy()[idx] for k, v in fin.items()}
     ref_beams = Beams(trie, sum(widths), len(widths), max(widths), device=dev)
+    ref_beams.set_read_mode(read_mode)
     rid, _ = ref_beams.init(widths)
     for x in xs:
-        ref_beams.step(x)
+        if step is None:
+            ref_beams.step(x)
+        else:
+            step(ref_beams, x)
         ref_beams.export()
     ref = ref_beams.finalize(rid)
     ref_beams.check()
@@ -680,7 +686,7 @@ def lmhead_leg(args, dev, read_mode="dense"):
     per_decode = sum(h.nbytes for h in host)
     pool = make_pool(lambda: [torch.from_numpy(h.view(np.int16)).to(dev).view(torch.bfloat16) for h in host],
                      per_decode, args.pool_gib, args.graph_decodes)
-    beams.set_finish_outputs(True)       # the last step writes each request's beams (row = id)
+    fin = beams.set_finish_outputs(True)   # the last step writes each request's beams (row = id)
     ids, _ = beams.init(widths)
     rows_per_step = []
     idx = torch.as_tensor(ids, device=dev).long()
@@ -703,6 +709,8 @@ def lmhead_leg(args, dev, read_mode="dense"):
         else:
             decode(d % len(pool))
     elapsed = timed(run, steps // group, -(-max(2, args.warmup // 5) // group))
+    verify_replay(trie, widths, pool[0], fin, ids, dev,
+                  step=lambda b, x: b.step_lmhead(x, w_dev), read_mode=read_mode)
     n_ev = min(steps, 50)
     beams.enable_timing(n_ev * L, 10)
     for d in range(n_ev):
