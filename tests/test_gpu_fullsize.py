@@ -183,6 +183,65 @@ def test_fullsize_timed_route_graph_replay():
     beams.check()
 
 
+def test_fullsize_lmhead_route_graph_replay():
+    """The lm_head workload as bench.py times it with the automatic head choice: 8 requests x
+    512 beams, hidden 2048, 1M catalog; the dense MFMA head at levels 0-2 and the children's
+    logits computed in the tile kernel at level 3, steps back to back (each merge in the next
+    step's tile kernel, ahead of the in-tile head), finish outputs, two decodes per captured
+    HIP graph. Every replay's outputs must equal, bitwise, a decode of the same inputs with an
+    export after every step (test_fullsize_lmhead checks that route against the oracle), and
+    the beams must be legal."""
+    wl, cat, otrie, lowest = _workload("lmhead_b512x8_l4_1m_h2048")
+    widths = list(wl.widths)
+    S, R, B, L, H = sum(widths), len(widths), max(widths), wl.L, wl.hidden
+    trie = Trie(cat, device="cuda")
+    weights = np.stack([synth.lmhead_weight(wl.seed, lv, 256, H) for lv in range(L)])
+    w_dev = torch.from_numpy(weights.view(np.int16)).cuda().view(torch.bfloat16)
+    hid = [synth.hidden_states(wl.seed, t, S, H) for t in range(L)]
+    pool = [[torch.from_numpy(h.view(np.int16)).cuda().view(torch.bfloat16) for h in hid] for _ in range(2)]
+
+    ref_beams = Beams(trie, S, R, B)
+    ref_beams.set_read_mode("auto")
+    ids, _ = ref_beams.init(widths)
+    for t in range(L):
+        ref_beams.step_lmhead(pool[0][t], w_dev)
+        ref_beams.export()
+    ref = ref_beams.finalize(ids)
+    ref_beams.check()
+
+    beams = Beams(trie, S, R, B)
+    beams.set_read_mode("auto")
+    out = beams.set_finish_outputs(True)
+
+    def decode(c):
+        rid, _ = beams.init(widths)
+        assert list(rid) == list(ids)
+        for t in range(L):
+            beams.step_lmhead(pool[c][t], w_dev)
+    decode(0)
+    torch.cuda.synchronize()
+    graphs = _capture(lambda c: [decode(c), decode(1 - c)], 2)
+    idx = np.asarray(ids)
+    for rep in range(3):
+        out["sids"].fill_(0xAB)
+        out["scores"].fill_(12345.0)
+        out["items"].fill_(-7)
+        out["counts"].fill_(-7)
+        torch.cuda.synchronize()
+        graphs[rep % 2].replay()
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy()[idx] for k, v in out.items()}
+        for k in ("counts", "sids", "scores", "items"):
+            assert np.array_equal(got[k], ref[k]), (rep, k)
+        if rep == 0:
+            for i, w in enumerate(widths):
+                c = int(got["counts"][i])
+                assert c == w
+                _check_legal(lowest, got["sids"][i, :c], got["scores"][i, :c], got["items"][i, :c], w,
+                             f"lm_head replay req {i}")
+    beams.check()
+
+
 def test_fullsize_mixed_wave_fifo():
     """256 requests, widths from {50, 128, 256, 512}, FIFO admission under 32,768 slots, L=5."""
     wl, cat, otrie, lowest = _workload("mixed256_l5_8m_f32")
