@@ -167,12 +167,13 @@ def test_lmhead_dense_wide_k_deterministic():
                               b.view(np.uint32) if b.dtype == np.float32 else b), k
 
 
-@pytest.mark.parametrize("H", [640, 2048])
+@pytest.mark.parametrize("H", [640, 2048, 4096])
 def test_lmhead_in_tile_children_head_fused_route(H):
     """The automatic head choice on a uniform 4-level catalog: dense head at levels 0-2,
     and at level 3 (about one child per row) the children's logits computed inside the
-    tile kernel. H = 640: one batch of four 16-byte pieces per lane and a remainder piece;
-    H = 2048: four batches. Checked against the oracle step by step (export after every
+    tile kernel, all 64 lanes of a wave on one (row, child) pair. H = 640: one round of
+    loads in which lanes past the row's 80 pieces read and drop; H = 2048: one full round
+    (256 pieces); H = 4096: two rounds. Checked against the oracle step by step (export after every
     step), then the same decode with the steps back to back (each merge done in the next
     step's tile kernel, so level 3's head runs after that merge, in the same kernel) must
     give bitwise the same finalized beams."""
